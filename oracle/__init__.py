@@ -1,0 +1,31 @@
+"""Plain, slow, obviously-correct CPU oracle for the Gated DeltaNet chunked forward.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import anything from this package.  It
+shares no code with the HIP library (``gated_deltanet_chunked_fwd_amd``) and never
+imports it; the two meet only through the seeded input generators, which hold
+none of the method's arithmetic.
+
+Contents
+  token      -- Oracle A: fp64 token-by-token recurrence (plain C via ctypes, plus a
+                numpy twin used to check the C build on tiny inputs).
+  chunked    -- Oracle B: fp64 chunk-by-chunk WY form written from the pages' four
+                steps, its algebraic variants, the sequence-parallel correction
+                (wrong-start state S*, correction matrix M, merge) and the
+                window-lookback start.
+  gate       -- brute-force window-length decision for strongly decaying heads.
+  build      -- compiles the C part with gcc.
+
+Every function cites the passage of the pages it follows.  The pages are three
+web articles on FlashQLA; the primary one is the AICon talk transcript
+"Qwen系列模型线性注意力高性能优化实践" (tokendh.com).
+"""
+from .token import token_recurrence, token_recurrence_numpy  # noqa: F401
+from .chunked import (  # noqa: F401
+    chunk_inverse,
+    chunked_forward,
+    cp_forward,
+    window_forward,
+    segment_transition,
+)
+from .gate import window_chunks, window_chunks_all  # noqa: F401
