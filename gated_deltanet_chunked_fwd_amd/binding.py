@@ -1,0 +1,187 @@
+"""Thin ctypes binding over libgdn.so (the C ABI declared in include/gdn.h).
+
+Argument marshalling only: every step of the forward runs in the library's HIP
+kernels.  torch provides device memory (outputs, workspace) and the stream.  The
+library must have been built (``gated_deltanet_chunked_fwd_amd.build``); if it is
+missing, the first call raises -- there is no fallback.
+"""
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgdn.so")
+
+GDN_OK, GDN_ERR_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 0, -1, -2, -3, -4
+GDN_BF16, GDN_F32 = 1, 2
+
+# Symbols declared in include/gdn.h (checked by the CPU test of the boundary).
+EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_inverse",
+           "gdn_total_chunks", "gdn_status_str")
+
+
+class GdnShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("dk", ctypes.c_int64), ("dv", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("qkv_dtype", ctypes.c_int32), ("beta_dtype", ctypes.c_int32),
+                ("cu_seqlens_host", ctypes.POINTER(ctypes.c_int32))]
+
+
+class GdnOpts(ctypes.Structure):
+    _fields_ = [("auto_cp", ctypes.c_int32), ("force_segment_chunks", ctypes.c_int32),
+                ("force_start_mode", ctypes.c_int32), ("window_log_eps", ctypes.c_float),
+                ("window_max_chunks", ctypes.c_int32), ("lambda1_us", ctypes.c_float),
+                ("lambda2_us", ctypes.c_float)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__("%s: %s (status %d)" % (what, status_str(status), status))
+        self.status = status
+
+
+_LIB = None
+
+
+def lib():
+    """Loads libgdn.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libgdn.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        shp, opt = ctypes.POINTER(GdnShape), ctypes.POINTER(GdnOpts)
+        L.gdn_chunk_fwd_workspace_bytes.argtypes = [shp, opt, ctypes.POINTER(sz)]
+        L.gdn_chunk_fwd_workspace_bytes.restype = ctypes.c_int
+        L.gdn_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, shp, opt,
+                                    vp, sz, vp]
+        L.gdn_chunk_fwd.restype = ctypes.c_int
+        L.gdn_chunk_inverse.argtypes = [vp, vp, vp, vp, shp, vp, vp, sz, vp]
+        L.gdn_chunk_inverse.restype = ctypes.c_int
+        L.gdn_total_chunks.argtypes = [shp]
+        L.gdn_total_chunks.restype = ctypes.c_int64
+        L.gdn_status_str.argtypes = [ctypes.c_int]
+        L.gdn_status_str.restype = ctypes.c_char_p
+        _LIB = L
+    return _LIB
+
+
+def status_str(status: int) -> str:
+    return lib().gdn_status_str(int(status)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class _Shape:
+    """Builds a GdnShape and keeps the host cu_seqlens buffer alive."""
+
+    def __init__(self, q, v, beta, cu_seqlens, cu_seqlens_host):
+        B, T, H, dk = q.shape
+        dv = v.shape[-1]
+        self.cu_host = None
+        N = B
+        if cu_seqlens is not None:
+            host = cu_seqlens_host if cu_seqlens_host is not None else cu_seqlens.to("cpu")
+            self.cu_host = host.to(torch.int32).contiguous()
+            N = self.cu_host.numel() - 1
+        self.s = GdnShape(B, T, H, dk, dv, N, _dtype_code(q), _dtype_code(beta),
+                          None if self.cu_host is None else
+                          ctypes.cast(self.cu_host.data_ptr(), ctypes.POINTER(ctypes.c_int32)))
+        self.N = N
+
+    def ref(self):
+        return ctypes.byref(self.s)
+
+
+def make_opts(auto_cp=1, force_segment_chunks=0, force_start_mode=0, window_log_eps=0.0,
+              window_max_chunks=0, lambda1_us=0.0, lambda2_us=0.0) -> GdnOpts:
+    return GdnOpts(auto_cp, force_segment_chunks, force_start_mode, window_log_eps,
+                   window_max_chunks, lambda1_us, lambda2_us)
+
+
+def workspace_bytes(q, v, beta, cu_seqlens=None, cu_seqlens_host=None, opts=None) -> int:
+    sh = _Shape(q, v, beta, cu_seqlens, cu_seqlens_host)
+    n = ctypes.c_size_t(0)
+    rc = lib().gdn_chunk_fwd_workspace_bytes(sh.ref(), None if opts is None else ctypes.byref(opts),
+                                             ctypes.byref(n))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_chunk_fwd_workspace_bytes")
+    return int(n.value)
+
+
+def chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=None,
+              output_final_state=True, opts: Optional[GdnOpts] = None, cu_seqlens_host=None,
+              out=None, final_state_out=None, workspace=None):
+    """GDN chunked forward.  Returns ``(o, final_state)`` (final_state None if not requested).
+
+    Layouts follow include/gdn.h: q, k [B,T,H,dk]; v [B,T,H,dv]; g, beta [B,T,H];
+    initial_state / final_state [N,H,dk,dv] fp32; cu_seqlens int32 [N+1] on the device
+    (B == 1).  ``cu_seqlens_host`` avoids a device-to-host copy of cu_seqlens.
+    """
+    for t in (q, k, v, g, beta):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("inputs must be contiguous device tensors")
+    sh = _Shape(q, v, beta, cu_seqlens, cu_seqlens_host)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    o = out if out is not None else torch.empty_like(v)
+    fs = None
+    if output_final_state:
+        fs = final_state_out if final_state_out is not None else torch.empty(
+            (sh.N, H, dk, dv), dtype=torch.float32, device=q.device)
+    opts_ref = None if opts is None else ctypes.byref(opts)
+    n = ctypes.c_size_t(0)
+    rc = lib().gdn_chunk_fwd_workspace_bytes(sh.ref(), opts_ref, ctypes.byref(n))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_chunk_fwd_workspace_bytes")
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=q.device)
+    rc = lib().gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                             _ptr(cu_seqlens), ctypes.c_float(scale), _ptr(o), _ptr(fs), sh.ref(),
+                             opts_ref, _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                             _stream(q.device))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_chunk_fwd")
+    return o, fs
+
+
+def chunk_inverse(k, g, beta, cu_seqlens=None, cu_seqlens_host=None):
+    """Step 1 alone: returns T [total_chunks, H, 64, 64] in k's dtype."""
+    sh = _Shape(k, k, beta, cu_seqlens, cu_seqlens_host)
+    nch = lib().gdn_total_chunks(sh.ref())
+    if nch < 0:
+        raise GdnError(int(nch), "gdn_total_chunks")
+    H = k.shape[2]
+    t = torch.empty((nch, H, 64, 64), dtype=k.dtype, device=k.device)
+    ws = None
+    nbytes = 0
+    if cu_seqlens is not None:
+        n = ctypes.c_size_t(0)
+        lib().gdn_chunk_fwd_workspace_bytes(sh.ref(), None, ctypes.byref(n))
+        ws = torch.empty(int(n.value), dtype=torch.uint8, device=k.device)
+        nbytes = ws.numel()
+    rc = lib().gdn_chunk_inverse(_ptr(k), _ptr(g), _ptr(beta), _ptr(cu_seqlens), sh.ref(), _ptr(t),
+                                 _ptr(ws), ctypes.c_size_t(nbytes), _stream(k.device))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_chunk_inverse")
+    return t

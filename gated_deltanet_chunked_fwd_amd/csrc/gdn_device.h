@@ -1,0 +1,143 @@
+// Device building blocks for the gfx950 GDN kernels: MFMA wrappers, the
+// register-resident tile conventions, and small wave-level helpers.
+//
+// MFMA conventions (v_mfma_f32_16x16x32_bf16, and eight chained
+// v_mfma_f32_16x16x4_f32 for the fp32 path).  With lane l, r = l % 16, q = l / 16:
+//   * a 16x16 fp32 accumulator tile holds element (row 4q+i, col r) in slot i;
+//   * an A operand ("frag") holds row r of A and 8 values of the contraction
+//     index, element e; a B operand holds column r of B and 8 values, element e;
+//     A's (q, e) meets B's (q, e) in the product.
+// A 32-wide contraction step therefore pairs A[row][phys(q,e)] with
+// B[phys(q,e)][col] for any bijection phys; we always use phys(q,e) = 8q + e,
+// which makes every LDS fragment read 8 contiguous elements.
+//
+// Register-resident operands.  A result tile can feed the next product as its B
+// operand without leaving registers if the result's rows are numbered so that
+// (tile 2s+e/4, slot e%4) of lane group q is contraction index 32s + 8q + e.  So
+// every row dimension that is later contracted (chunk rows, key dimension)
+// lives in "tile order": slot i of lane group q in tile t is physical row
+//     prow(t, 4q+i),  prow(t, r) = 32*(t/2) + 8*(r/4) + 4*(t%2) + r%4.
+// An A operand that produces tile t must then supply, in lane row r, the
+// source row prow(t, r).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gdn_launch.h"
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__host__ __device__ constexpr int prow(int t, int r) {
+  return 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3);
+}
+
+template <typename E>
+struct Mma;
+
+template <>
+struct Mma<bf16> {
+  typedef bf16x8 frag;
+  static __device__ __forceinline__ f32x4 run(const frag& a, const frag& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // B operand of contraction step s from result tiles 2s (lo) and 2s+1 (hi)
+  static __device__ __forceinline__ frag pack(const f32x4& lo, const f32x4& hi) {
+    frag r;
+    r[0] = (bf16)lo[0]; r[1] = (bf16)lo[1]; r[2] = (bf16)lo[2]; r[3] = (bf16)lo[3];
+    r[4] = (bf16)hi[0]; r[5] = (bf16)hi[1]; r[6] = (bf16)hi[2]; r[7] = (bf16)hi[3];
+    return r;
+  }
+};
+
+template <>
+struct Mma<float> {
+  typedef f32x8 frag;
+  static __device__ __forceinline__ f32x4 run(const frag& a, const frag& b, f32x4 c) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+    return c;
+  }
+  static __device__ __forceinline__ frag pack(const f32x4& lo, const f32x4& hi) {
+    frag r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+  }
+};
+
+// Fragment read from a row-major LDS matrix: row `row`, columns kbase+8q .. +7.
+template <typename E>
+__device__ __forceinline__ typename Mma<E>::frag lds_frag(const E* base, int stride, int row,
+                                                          int kbase, int q) {
+  return *reinterpret_cast<const typename Mma<E>::frag*>(base + row * stride + kbase + 8 * q);
+}
+
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+template <typename E>
+__device__ __forceinline__ E from_f32(float x);
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+__device__ __forceinline__ float load_scalar(const void* p, int64_t i, bool is_bf16) {
+  return is_bf16 ? (float)reinterpret_cast<const bf16*>(p)[i] : reinterpret_cast<const float*>(p)[i];
+}
+
+__device__ __forceinline__ float fast_exp(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    float y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Sequence n's token range and first global chunk.
+struct SeqInfo {
+  int64_t tok0;    // first token (flattened over B*T)
+  int len;         // tokens in the sequence
+  int64_t chunk0;  // global index of its first chunk
+};
+
+__device__ __forceinline__ SeqInfo seq_info(int n, const int32_t* cu, const int32_t* chunk_off,
+                                            int64_t T) {
+  SeqInfo s;
+  if (cu) {
+    s.tok0 = cu[n];
+    s.len = cu[n + 1] - cu[n];
+    s.chunk0 = chunk_off[n];
+  } else {
+    s.tok0 = (int64_t)n * T;
+    s.len = (int)T;
+    s.chunk0 = (int64_t)n * ((T + kChunk - 1) / kChunk);
+  }
+  return s;
+}
+
+// Sequence owning global chunk `cg` (binary search over chunk offsets).
+__device__ __forceinline__ int seq_of_chunk(int64_t cg, const int32_t* chunk_off, int N,
+                                            int64_t T) {
+  if (!chunk_off) return (int)(cg / ((T + kChunk - 1) / kChunk));
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (chunk_off[mid] <= cg) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace gdn

@@ -1,0 +1,142 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) Gated DeltaNet chunked-prefill forward.
+ *
+ * Operation (FlashQLA talk transcript, "Qwen系列模型线性注意力高性能优化实践",
+ * tokendh.com: linear-attention, GDN and sliding-window sections; the API section
+ * says the library follows FLA's chunk_gated_delta_rule signature, with varlen
+ * support and an automatic intra-card sequence-parallel switch):
+ *
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   alpha_t = exp(g_t)
+ *     o_t = scale * S_t q_t
+ *
+ * evaluated chunk by chunk (C = 64) through the WY form (chunked-WY section:
+ * step 1 is the chunk's K K^T and its inverse, steps 2-4 the projections, the state
+ * recurrence and the output).  S_t is dv x dk; the state crossing this ABI is
+ * K-major, h = S^T, element [i][j] = S[j][i].
+ *
+ * Conventions for every entry point
+ *   * Pointers marked "device" are device memory on the current HIP device,
+ *     owned by the caller, contiguous, 16-byte aligned, and must stay valid until
+ *     the work enqueued on `stream` has finished.  Inputs are never written.
+ *     Outputs must not alias inputs or each other.
+ *   * Tensor layouts are token-major: q, k [B, T, H, dk]; v, o [B, T, H, dv];
+ *     g, beta [B, T, H]; states [N, H, dk, dv] fp32.  With packed sequences
+ *     (cu_seqlens != NULL) B must be 1 and the N sequences are the slices
+ *     [cu_seqlens[n], cu_seqlens[n+1]) of the T axis.
+ *   * Every call is asynchronous on `stream` (never synchronises, allocates
+ *     nothing) and returns a status code; all argument checks happen before
+ *     the first launch, so an error return means nothing was enqueued, except
+ *     GDN_ERR_HIP, which reports a failed launch.
+ *   * No exceptions cross this boundary.  The library holds no mutable global
+ *     state besides a per-device property cache filled once.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------------- */
+enum {
+  GDN_OK = 0,
+  GDN_ERR_ARG = -1,          /* null pointer, bad dimension, misalignment, bad cu_seqlens */
+  GDN_ERR_UNSUPPORTED = -2,  /* dk/dv not in {64,128}, dtype combination not built */
+  GDN_ERR_WORKSPACE = -3,    /* workspace missing or smaller than gdn_chunk_fwd_workspace_bytes */
+  GDN_ERR_HIP = -4           /* a kernel launch failed (hipGetLastError) */
+};
+
+/* ---- element types ----------------------------------------------------------- */
+enum { GDN_BF16 = 1, GDN_F32 = 2 };
+
+/* Problem description.  N = B without packing, or the number of packed sequences. */
+typedef struct gdn_shape {
+  int64_t B, T, H, dk, dv;
+  int64_t N;
+  int32_t qkv_dtype;   /* dtype of q, k, v and o: GDN_BF16 or GDN_F32 */
+  int32_t beta_dtype;  /* dtype of beta: GDN_BF16 or GDN_F32 */
+  /* Host copy of cu_seqlens (N+1 int32) when sequences are packed, else NULL.
+   * Used to size the launch grids without a device-to-host copy; it must hold
+   * the same values as the device array passed to the entry points. */
+  const int32_t* cu_seqlens_host;
+} gdn_shape;
+
+/* Planner options.  A zeroed struct (or NULL) selects the defaults. */
+typedef struct gdn_opts {
+  /* 0: one pass per (sequence, head) -- bitwise reproducible run to run and
+   *    independent of the planner.
+   * 1 (default when opts == NULL): the planner may split long sequences into
+   *    segments that run in parallel (the pages' automatic intra-card split).
+   *    Results then match the no-split path within rounding, not bitwise. */
+  int32_t auto_cp;
+  int32_t force_segment_chunks; /* >0: force this segment length in chunks (tests) */
+  int32_t force_start_mode;     /* 0: gate scan decides per (seq, head); 1: window starts
+                                   where the scan allows, else correction; 2: correction
+                                   (wrong-start state + matrix M) for every split head */
+  float window_log_eps;         /* log of the window tolerance; 0 -> log(2^-24) */
+  int32_t window_max_chunks;    /* longest lookback window in chunks; 0 -> 16 */
+  float lambda1_us;             /* planner: cost of one chunk step; 0 -> built in */
+  float lambda2_us;             /* planner: cost of one merge step; 0 -> built in */
+} gdn_opts;
+
+/* Workspace size in bytes that gdn_chunk_fwd needs for this problem and options.
+ * Returns GDN_OK and writes *bytes, or an error code for an invalid shape. */
+int gdn_chunk_fwd_workspace_bytes(const gdn_shape* shape, const gdn_opts* opts, size_t* bytes);
+
+/*
+ * The forward pass.
+ *   q, k           device, [B,T,H,dk], dtype shape->qkv_dtype; keys are expected
+ *                  L2-normalised per token (the GDN contract; not checked)
+ *   v              device, [B,T,H,dv], dtype shape->qkv_dtype
+ *   g              device, [B,T,H] fp32: log alpha per token (not cumulated), finite, <= 0
+ *   beta           device, [B,T,H], dtype shape->beta_dtype, in [0,1]
+ *   initial_state  device, [N,H,dk,dv] fp32, or NULL for a zero start
+ *   cu_seqlens     device, [N+1] int32 with cu_seqlens[0] = 0, non-decreasing,
+ *                  cu_seqlens[N] = T; or NULL (then N = B and each batch row
+ *                  is one sequence of length T)
+ *   scale          multiplies every output (typically dk^-1/2)
+ *   o              device, [B,T,H,dv], dtype shape->qkv_dtype, fully overwritten
+ *   final_state    device, [N,H,dk,dv] fp32, fully overwritten; or NULL (not written)
+ *   workspace      device scratch of at least gdn_chunk_fwd_workspace_bytes()
+ *   stream         HIP stream the work is enqueued on (0 = null stream)
+ */
+int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
+                  const void* beta, const float* initial_state, const int32_t* cu_seqlens,
+                  float scale, void* o, float* final_state, const gdn_shape* shape,
+                  const gdn_opts* opts, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream);
+
+/*
+ * Step 1 alone (chunked-WY section, first step; the pages cut the kernel after
+ * it so the sequence-parallel pass can reuse the inverse): for every chunk c
+ * (chunks restart at each sequence start; the last one may be partial) and head h,
+ *     A = strict_lower(diag(beta) K K^T * Gamma),  Gamma_rs = exp(G_r - G_s) (r >= s),
+ *     T = (I + A)^{-1},
+ * G the chunk-local cumulative sum of g.  Rows past a partial chunk's end are
+ * treated as k = 0, beta = 0, g = 0 (T is the identity there).
+ *   t_out  device, [total_chunks, H, 64, 64] in shape->qkv_dtype (bf16 or fp32),
+ *          chunk-major in sequence order; total_chunks = sum_n ceil(len_n / 64).
+ *   workspace  device scratch; only used with packed sequences, where it must hold
+ *          at least gdn_chunk_fwd_workspace_bytes() bytes (NULL allowed otherwise).
+ * Other arguments as in gdn_chunk_fwd.
+ */
+int gdn_chunk_inverse(const void* k, const float* g, const void* beta,
+                      const int32_t* cu_seqlens, const gdn_shape* shape, void* t_out,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Total number of chunks (sum over sequences of ceil(len/64)), or a negative status. */
+int64_t gdn_total_chunks(const gdn_shape* shape);
+
+/* Human-readable name of a status code (static string). */
+const char* gdn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

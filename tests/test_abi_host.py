@@ -1,0 +1,99 @@
+"""CPU-side checks of the C boundary: the library loads, exports every symbol
+include/gdn.h declares, and rejects bad arguments before any HIP call (no GPU is
+touched: every case here fails validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_deltanet_chunked_fwd_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[\w\s\*]+?\b(gdn_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.lib()
+    names = declared_symbols()
+    assert "gdn_chunk_fwd" in names and "gdn_chunk_fwd_workspace_bytes" in names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(B.EXPORTS) == set(names)
+
+
+def shape(**kw):
+    d = dict(B=1, T=128, H=2, dk=128, dv=128, N=1, qkv_dtype=B.GDN_BF16, beta_dtype=B.GDN_BF16,
+             cu_seqlens_host=None)
+    d.update(kw)
+    return B.GdnShape(**d)
+
+
+def ws_bytes(s):
+    n = ctypes.c_size_t(0)
+    rc = B.lib().gdn_chunk_fwd_workspace_bytes(ctypes.byref(s), None, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_query():
+    rc, n = ws_bytes(shape())
+    assert rc == B.GDN_OK
+    assert n >= 2 * 2 * 64 * 64 * 2  # two chunks x two heads of bf16 T
+    rc32, n32 = ws_bytes(shape(qkv_dtype=B.GDN_F32))
+    assert rc32 == B.GDN_OK and n32 > n
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dk=96), B.GDN_ERR_UNSUPPORTED),
+    (dict(dv=32), B.GDN_ERR_UNSUPPORTED),
+    (dict(qkv_dtype=7), B.GDN_ERR_UNSUPPORTED),
+    (dict(H=0), B.GDN_ERR_ARG),
+    (dict(T=-1), B.GDN_ERR_ARG),
+    (dict(N=2), B.GDN_ERR_ARG),          # dense layout needs N == B
+])
+def test_bad_shapes_rejected(kw, code):
+    rc, _ = ws_bytes(shape(**kw))
+    assert rc == code
+
+
+def test_bad_cu_seqlens_rejected():
+    for vals, N, T in [([0, 10, 5], 2, 5), ([1, 10], 1, 10), ([0, 10], 1, 11)]:
+        arr = (ctypes.c_int32 * len(vals))(*vals)
+        s = shape(T=T, N=N, cu_seqlens_host=ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)))
+        assert ws_bytes(s)[0] == B.GDN_ERR_ARG
+    arr = (ctypes.c_int32 * 3)(0, 10, 30)
+    s = shape(B=2, T=30, N=2, cu_seqlens_host=ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)))
+    assert ws_bytes(s)[0] == B.GDN_ERR_ARG   # packed needs B == 1
+
+
+def test_forward_rejects_before_launch():
+    lib = B.lib()
+    s = shape()
+    fake = ctypes.c_void_p(4096)        # never dereferenced: validation fails first
+    mis = ctypes.c_void_p(4096 + 2)
+    args = [fake] * 5 + [None, None, ctypes.c_float(0.1), fake, None, ctypes.byref(s), None]
+    # null q
+    a = list(args); a[0] = None
+    assert lib.gdn_chunk_fwd(*a, fake, ctypes.c_size_t(1 << 30), None) == B.GDN_ERR_ARG
+    # misaligned v
+    a = list(args); a[2] = mis
+    assert lib.gdn_chunk_fwd(*a, fake, ctypes.c_size_t(1 << 30), None) == B.GDN_ERR_ARG
+    # workspace too small
+    assert lib.gdn_chunk_fwd(*args, fake, ctypes.c_size_t(16), None) == B.GDN_ERR_WORKSPACE
+    # non-finite scale
+    a = list(args); a[7] = ctypes.c_float(float("nan"))
+    assert lib.gdn_chunk_fwd(*a, fake, ctypes.c_size_t(1 << 30), None) == B.GDN_ERR_ARG
+    # device cu_seqlens without the host copy
+    a = list(args); a[6] = fake
+    assert lib.gdn_chunk_fwd(*a, fake, ctypes.c_size_t(1 << 30), None) == B.GDN_ERR_ARG
+
+
+def test_status_strings():
+    assert B.status_str(0) == "ok"
+    assert "workspace" in B.status_str(B.GDN_ERR_WORKSPACE)
+    assert B.status_str(12345) == "unknown status"

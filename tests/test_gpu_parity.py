@@ -1,0 +1,167 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Element-by-element per (sequence, head) relative L2 on o and on the final state,
+at sizes the oracle finishes in seconds (several chunks, ragged tails, packed
+sequences, empty sequences), plus stage parity of the chunk inverse and the GPU
+side of the invariants.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_chunked_fwd_amd import binding, synth
+from oracle import chunked
+from tests.gpu_util import TOL, assert_parity, compare_pairs, run_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def spec(**kw):
+    base = dict(name="t", B=1, T=256, H=1, dk=64, dv=64, dtype="bf16", seed=0)
+    base.update(kw)
+    return synth.Spec(**base)
+
+
+CASES = [
+    # name, spec kwargs, opts
+    ("tiny_fp32_workload", dict(B=1, T=256, H=1, dk=64, dv=64, dtype="f32", seed=1)),
+    ("fp32_ragged_h0", dict(B=2, T=200, H=2, dk=64, dv=64, dtype="f32", h0_std=0.1, seed=21)),
+    ("fp32_dk128", dict(B=1, T=130, H=2, dk=128, dv=64, dtype="f32", seed=22)),
+    ("bf16_d128_ragged_h0", dict(B=2, T=300, H=3, dk=128, dv=128, h0_std=0.05, seed=23)),
+    ("bf16_d64", dict(B=2, T=257, H=2, dk=64, dv=64, seed=24)),
+    ("bf16_dk64_dv128", dict(B=1, T=190, H=2, dk=64, dv=128, seed=25)),
+    ("bf16_dk128_dv64", dict(B=1, T=190, H=2, dk=128, dv=64, seed=26)),
+    ("bf16_strong_gate", dict(B=1, T=700, H=2, dk=128, dv=128, gate="uniform", seed=27)),
+    ("bf16_no_decay", dict(B=1, T=700, H=2, dk=128, dv=128, gate="zero", seed=28)),
+]
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
+def test_parity_small(name, kw):
+    inp = synth.generate(spec(name=name, **kw))
+    o, hT = run_gpu(inp)
+    assert_parity(compare_pairs(inp, o, hT), TOL[inp["spec"].dtype], name)
+
+
+def _packed(lengths, H, dk, dv, dtype, h0_std, seed):
+    """Packed sequences with given lengths (built from one dense draw)."""
+    T = int(sum(lengths))
+    inp = synth.generate(spec(B=1, T=T, H=H, dk=dk, dv=dv, dtype=dtype, seed=seed))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    inp["cu_seqlens"] = torch.from_numpy(cu)
+    inp["N"] = len(lengths)
+    if h0_std:
+        g = torch.Generator().manual_seed(seed)
+        inp["h0"] = (torch.randn(len(lengths), H, dk, dv, generator=g) * h0_std).float()
+    return inp
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_parity_packed_with_empty_and_tiny(dtype):
+    inp = _packed([1, 64, 0, 65, 200, 130, 3], H=2, dk=64, dv=64, dtype=dtype, h0_std=0.05, seed=31)
+    o, hT = run_gpu(inp)
+    assert_parity(compare_pairs(inp, o, hT), TOL[dtype], "packed_" + dtype)
+
+
+def test_parity_packed_d128():
+    inp = _packed([512, 77, 1000, 64], H=3, dk=128, dv=128, dtype="bf16", h0_std=0.02, seed=32)
+    o, hT = run_gpu(inp)
+    assert_parity(compare_pairs(inp, o, hT), TOL["bf16"], "packed_d128")
+
+
+@pytest.mark.parametrize("dtype,dk", [("bf16", 128), ("f32", 64), ("bf16", 64)])
+def test_chunk_inverse_stage(dtype, dk):
+    """T from the HIP step-1 kernel against the oracle's T (same stored K, g, beta),
+    and the residual ||(I + A) T - I||_F / sqrt(C)."""
+    inp = synth.generate(spec(B=1, T=64 * 3 + 17, H=2, dk=dk, dv=64, dtype=dtype, seed=41,
+                              gate="uniform"))
+    d = to_dev(inp)
+    T = binding.chunk_inverse(d["k"], d["g"], d["beta"])
+    torch.cuda.synchronize()
+    Tg = T.to("cpu").to(torch.float64).numpy()
+    k64, g64, b64 = (synth.as_f64(inp[x]) for x in ("k", "g", "beta"))
+    tol = 1e-2 if dtype == "bf16" else 1e-5
+    worst = 0.0
+    for c in range(Tg.shape[0]):
+        s, e = 64 * c, min(64 * c + 64, inp["spec"].T)
+        for h in range(2):
+            Tref, A = chunked.chunk_inverse(k64[0, s:e, h], g64[0, s:e, h], b64[0, s:e, h])
+            n = e - s
+            Tgc = Tg[c, h]
+            # padded rows/cols are the identity
+            assert np.allclose(Tgc[n:, n:], np.eye(64 - n)) and np.all(Tgc[:n, n:] == 0)
+            assert np.all(np.triu(Tgc, 1) == 0) and np.all(np.diag(Tgc) == 1)
+            err = np.linalg.norm(Tgc[:n, :n] - Tref) / np.linalg.norm(Tref)
+            resid = np.linalg.norm((np.eye(n) + A) @ Tgc[:n, :n] - np.eye(n)) / np.sqrt(64)
+            worst = max(worst, err, resid)
+    print("chunk inverse worst rel err / residual %.3e (tol %.0e)" % (worst, tol))
+    assert worst <= tol
+
+
+def test_beta_zero_no_decay_keeps_state_bitwise():
+    inp = synth.generate(spec(B=1, T=300, H=2, dk=128, dv=128, gate="zero", h0_std=0.1, seed=51))
+    inp["beta"] = torch.zeros_like(inp["beta"])
+    o, hT = run_gpu(inp)
+    assert torch.equal(hT.cpu(), inp["h0"])
+    assert_parity(compare_pairs(inp, o, hT), TOL["bf16"], "beta0")
+
+
+def test_causality_bitwise():
+    inp = synth.generate(spec(B=1, T=400, H=2, dk=128, dv=128, seed=52))
+    o1, _ = run_gpu(inp)
+    t0 = 150
+    inp2 = dict(inp)
+    for key in ("q", "k", "v"):
+        x = inp[key].clone()
+        x[:, t0:] = torch.flip(x[:, t0:], dims=[1])
+        inp2[key] = x
+    b = inp["beta"].clone()
+    b[:, t0:] = 0.5
+    inp2["beta"] = b
+    o2, _ = run_gpu(inp2)
+    assert torch.equal(o1[:, :t0].cpu(), o2[:, :t0].cpu())
+    assert not torch.equal(o1[:, t0:].cpu(), o2[:, t0:].cpu())
+
+
+@pytest.mark.parametrize("t1", [128, 100])
+def test_state_carry(t1):
+    inp = synth.generate(spec(B=1, T=320, H=2, dk=128, dv=128, h0_std=0.05, seed=53))
+    o, hT = run_gpu(inp)
+    a = dict(inp); b = dict(inp)
+    for key in ("q", "k", "v", "g", "beta"):
+        a[key] = inp[key][:, :t1].contiguous()
+        b[key] = inp[key][:, t1:].contiguous()
+    a["spec"] = spec(B=1, T=t1, H=2, dk=128, dv=128)
+    oa, ha = run_gpu(a)
+    b["h0"] = ha.cpu()
+    b["spec"] = spec(B=1, T=320 - t1, H=2, dk=128, dv=128)
+    ob, hb = run_gpu(b)
+    oc = torch.cat([oa, ob], dim=1).float()
+    rel_o = (oc - o.float()).norm() / o.float().norm()
+    rel_h = (hb - hT).norm() / hT.norm()
+    assert rel_o < 1e-2 and rel_h < 1e-2, (rel_o, rel_h)
+
+
+def test_deterministic_repeat():
+    inp = synth.generate(spec(B=2, T=500, H=2, dk=128, dv=128, seed=54))
+    o1, h1 = run_gpu(inp)
+    o2, h2 = run_gpu(inp)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+def test_packed_equals_separate_runs_bitwise():
+    lengths = [200, 64, 129]
+    inp = _packed(lengths, H=2, dk=128, dv=128, dtype="bf16", h0_std=0.02, seed=55)
+    o, hT = run_gpu(inp)
+    cu = inp["cu_seqlens"].numpy()
+    for n in range(len(lengths)):
+        s, e = int(cu[n]), int(cu[n + 1])
+        one = dict(inp)
+        for key in ("q", "k", "v", "g", "beta"):
+            one[key] = inp[key][:, s:e].contiguous()
+        one["h0"] = inp["h0"][n:n + 1].contiguous()
+        one["cu_seqlens"] = None
+        one["spec"] = spec(B=1, T=e - s, H=2, dk=128, dv=128)
+        o1, h1 = run_gpu(one)
+        assert torch.equal(o1[0].cpu(), o[0, s:e].cpu())
+        assert torch.equal(h1[0].cpu(), hT[n].cpu())
