@@ -1,0 +1,252 @@
+"""Benchmark of the GDN chunked-prefill forward on one MI355X.
+
+One step = one gdn_chunk_fwd call (every stage of the forward) over one batch of
+seeded synthetic input, all inputs resident in HBM.  Default workload: the
+Qwen-like prefill (B=4, T=4096, H=16, dk=dv=128, bf16 q/k/v/o, fp32 g, bf16 beta,
+zero initial state, fp32 final state).
+
+Timing: W untimed warm-up steps; then K steps between two device synchronisations.
+Before each timed step a 512 MiB buffer is overwritten (evicts the 256 MB MALL and
+the L2s) outside the step's HIP events; ms_per_step is the mean of the per-step
+event times, so it never includes the flush.  Each stage of the call is also timed
+live with HIP events recorded by the library on the launch stream.
+
+Roofline (dominant kernel = the stage with the largest mean time):
+  achieved = algorithmic bytes of that kernel per launch / its mean duration,
+  bytes per token-head = 2*(dk+dv)*e_qkv + e_g + e_beta, plus the fp32 states it
+  reads/writes; peak = 8000 GB/s.
+traffic = HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE (from
+profiles/traffic_fused_forward.json) if those counters were taken on the current
+kernel source, else null.
+
+cpu_baseline: the fp64 oracle (plain C, OpenMP) on the host cores, rank 0 only.
+
+Prints ONE JSON line.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+F32_PEAK_TFLOPS = 157.3
+METRIC = "GDN fwd prefill ms & tokens/s at H=16,d=128,T=4k×4; % of MFMA/HBM roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="workload number (1-5)")
+    ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--auto-cp", type=int, default=1)
+    return ap.parse_args()
+
+
+class Hip:
+    """HIP events through the runtime torch already loaded (same soname)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            rc = self.lib.hipEventCreate(ctypes.addressof(arr) + i * ctypes.sizeof(ctypes.c_void_p))
+            if rc != 0:
+                raise RuntimeError("hipEventCreate failed: %d" % rc)
+        return arr
+
+    def record(self, ev, stream):
+        if self.lib.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed(self, a, b):
+        self.lib.hipEventSynchronize(b)
+        ms = ctypes.c_float(0.0)
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            return float("nan")
+        return float(ms.value)
+
+
+def algorithmic_bytes(spec, n_seqs, has_h0, has_hT):
+    e = 2 if spec.dtype == "bf16" else 4
+    eb = 2 if (spec.beta_dtype or spec.dtype) == "bf16" else 4
+    th = spec.B * spec.T * spec.H
+    per_th = 2 * (spec.dk + spec.dv) * e + 4 + eb
+    state = n_seqs * spec.H * spec.dk * spec.dv * 4
+    return th * per_th + state * (int(has_h0) + int(has_hT))
+
+
+def algorithmic_flops(spec):
+    """Per token-head: 6 dk dv (K h, Q h, K~^T U) + 4 C (dk + dv) (K K^T, Q K^T, T V', P U)
+    + C^2/3 (triangular inverse), C = 64, full C x C tiles."""
+    C = 64
+    th = spec.B * spec.T * spec.H
+    return th * (6 * spec.dk * spec.dv + 4 * C * (spec.dk + spec.dv) + C * C / 3.0)
+
+
+def source_sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def traffic_for(kernel_src, launches_per_step=1):
+    """HBM bytes per launch from committed rocprofv3 counters, if they were taken on
+    this exact kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_fused_forward.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != source_sha(kernel_src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, spec):
+    """The fp64 oracle on the host cores, on the whole workload (bounded: the oracle
+    needs ~1-3 s for the Qwen-like workload on 16 cores)."""
+    from gated_deltanet_chunked_fwd_amd import synth
+    from oracle import token
+
+    cores = len(os.sched_getaffinity(0))
+    args = [synth.as_f64(inp[k]) for k in ("q", "k", "v", "g", "beta")]
+    h0 = synth.as_f64(inp["h0"])
+    cu = None if inp["cu_seqlens"] is None else inp["cu_seqlens"].numpy()
+    t0 = time.perf_counter()
+    token.token_recurrence(*args, h0, cu_seqlens=cu, scale=inp["scale"], nthreads=cores)
+    dt = time.perf_counter() - t0
+    tokens = spec.B * spec.T
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "whole workload (%d tokens x %d heads), fp64 token recurrence, %.2f s"
+            % (tokens, spec.H, dt)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d, WORLD_SIZE %d requested)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gated_deltanet_chunked_fwd_amd import binding, synth
+
+    spec = synth.WORKLOADS[args.workload]
+    inp = synth.generate(spec)
+    dev = torch.device("cuda:0")
+    d = {k: (None if inp[k] is None else inp[k].to(dev).contiguous())
+         for k in ("q", "k", "v", "g", "beta", "h0", "cu_seqlens")}
+    N = inp["N"]
+    o = torch.empty_like(d["v"])
+    hT = torch.empty((N, spec.H, spec.dk, spec.dv), dtype=torch.float32, device=dev)
+    hip = Hip()
+    stage_ev = hip.events(2 * binding.GDN_NUM_STAGES)
+    opts = binding.make_opts(auto_cp=args.auto_cp,
+                             stage_events=ctypes.cast(stage_ev, ctypes.c_void_p))
+    ws = torch.empty(max(binding.workspace_bytes(d["q"], d["v"], d["beta"], d["cu_seqlens"],
+                                                 inp["cu_seqlens"], opts), 1),
+                     dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    step_ev = hip.events(2)
+
+    def step():
+        binding.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"],
+                          cu_seqlens=d["cu_seqlens"], scale=inp["scale"], opts=opts,
+                          cu_seqlens_host=inp["cu_seqlens"], out=o, final_state_out=hT,
+                          workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    step_ms, stage_ms = [], {i: [] for i in range(binding.GDN_NUM_STAGES)}
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush.fill_(i & 0xFF)
+        hip.record(step_ev[0], stream)
+        # stage events that a step does not record keep stale values: mark them
+        for s in range(binding.GDN_NUM_STAGES):
+            hip.record(stage_ev[2 * s], stream)
+            hip.record(stage_ev[2 * s + 1], stream)
+        step()
+        hip.record(step_ev[1], stream)
+        step_ms.append(hip.elapsed(step_ev[0], step_ev[1]))
+        for s in range(binding.GDN_NUM_STAGES):
+            stage_ms[s].append(hip.elapsed(stage_ev[2 * s], stage_ev[2 * s + 1]))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+
+    # a few back-to-back steps without flushes (hot caches), for context
+    torch.cuda.synchronize()
+    hip.record(step_ev[0], stream)
+    for _ in range(5):
+        step()
+    hip.record(step_ev[1], stream)
+    hot_ms = hip.elapsed(step_ev[0], step_ev[1]) / 5
+
+    ms = sum(step_ms) / len(step_ms)
+    tokens = spec.B * spec.T
+    st_mean = {binding.STAGE_NAMES[s]: sum(v) / len(v) for s, v in stage_ms.items()
+               if v and sum(v) / len(v) > 1e-4}
+    dom = max(st_mean, key=st_mean.get)
+    has_h0 = d["h0"] is not None
+    alg_bytes = algorithmic_bytes(spec, N, has_h0, True)
+    flops = algorithmic_flops(spec)
+    dom_ms = st_mean[dom]
+    achieved = alg_bytes / (dom_ms * 1e-3) / 1e9
+    ksrc = os.path.join(ROOT, "gated_deltanet_chunked_fwd_amd", "csrc", "fused_forward.hip")
+    traffic = traffic_for(ksrc) if dom == "fused_forward" else None
+    mfma_peak = BF16_PEAK_TFLOPS if spec.dtype == "bf16" else F32_PEAK_TFLOPS
+    rec = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded; q,k L2-normalised, g=log sigmoid(N(3,1)), beta=sigmoid(N(0,1)))",
+        "config": {"workload": spec.name, "B": spec.B, "T": spec.T, "H": spec.H, "dk": spec.dk,
+                   "dv": spec.dv, "chunk": 64, "initial_state": has_h0,
+                   "final_state": True, "auto_cp": args.auto_cp, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": alg_bytes, "kernel_ms": dom_ms},
+        "path": {"hbm_frac": alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "mfma_frac": flops / (ms * 1e-3) / 1e12 / mfma_peak,
+                 "algorithmic_flops": flops, "stage_ms": st_mean,
+                 "ms_per_step_hot_caches": hot_ms, "ms_min": min(step_ms),
+                 "wall_s_timed_loop_incl_flush": wall},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(inp, spec)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -34,7 +34,12 @@ class GdnOpts(ctypes.Structure):
     _fields_ = [("auto_cp", ctypes.c_int32), ("force_segment_chunks", ctypes.c_int32),
                 ("force_start_mode", ctypes.c_int32), ("window_log_eps", ctypes.c_float),
                 ("window_max_chunks", ctypes.c_int32), ("lambda1_us", ctypes.c_float),
-                ("lambda2_us", ctypes.c_float)]
+                ("lambda2_us", ctypes.c_float), ("stage_events", ctypes.c_void_p)]
+
+
+GDN_STAGE_INVERSE, GDN_STAGE_GATE_SCAN, GDN_STAGE_CP_PASS1, GDN_STAGE_CP_MERGE = 0, 1, 2, 3
+GDN_STAGE_FORWARD, GDN_NUM_STAGES = 4, 5
+STAGE_NAMES = ("chunk_inverse", "gate_scan", "cp_pass1", "cp_merge", "fused_forward")
 
 
 class GdnError(RuntimeError):
@@ -112,9 +117,9 @@ class _Shape:
 
 
 def make_opts(auto_cp=1, force_segment_chunks=0, force_start_mode=0, window_log_eps=0.0,
-              window_max_chunks=0, lambda1_us=0.0, lambda2_us=0.0) -> GdnOpts:
+              window_max_chunks=0, lambda1_us=0.0, lambda2_us=0.0, stage_events=None) -> GdnOpts:
     return GdnOpts(auto_cp, force_segment_chunks, force_start_mode, window_log_eps,
-                   window_max_chunks, lambda1_us, lambda2_us)
+                   window_max_chunks, lambda1_us, lambda2_us, stage_events)
 
 
 def workspace_bytes(q, v, beta, cu_seqlens=None, cu_seqlens_host=None, opts=None) -> int:

@@ -16,6 +16,20 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Records the caller's timing events around one stage (no-op without events).
+struct StageMark {
+  hipEvent_t* ev;
+  hipStream_t s;
+  int stage;
+  StageMark(const gdn_opts* o, int stage_, hipStream_t s_)
+      : ev(o ? o->stage_events : nullptr), s(s_), stage(stage_) {
+    if (ev) (void)hipEventRecord(ev[2 * stage], s);
+  }
+  ~StageMark() {
+    if (ev) (void)hipEventRecord(ev[2 * stage + 1], s);
+  }
+};
+
 int validate_shape(const gdn_shape* s) {
   if (!s) return GDN_ERR_ARG;
   if (s->B < 1 || s->T < 0 || s->H < 1 || s->N < 0) return GDN_ERR_ARG;
@@ -133,14 +147,20 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
       return GDN_ERR_HIP;
   }
   void* tmat = ws + L.tmat;
-  if (gdn::launch_chunk_inverse(p, tmat, stream) != hipSuccess) return GDN_ERR_HIP;
+  {
+    StageMark mark(opts, GDN_STAGE_INVERSE, stream);
+    if (gdn::launch_chunk_inverse(p, tmat, stream) != hipSuccess) return GDN_ERR_HIP;
+  }
 
   gdn::FwdPlan plan;
   plan.Tmat = tmat;
   plan.seg_chunks = INT_MAX / 2;
   plan.seg_off = nullptr;
   plan.units = (int64_t)p.N * p.H;
-  if (gdn::launch_fused_forward(p, plan, stream) != hipSuccess) return GDN_ERR_HIP;
+  {
+    StageMark mark(opts, GDN_STAGE_FORWARD, stream);
+    if (gdn::launch_fused_forward(p, plan, stream) != hipSuccess) return GDN_ERR_HIP;
+  }
   return GDN_OK;
 }
 

@@ -82,7 +82,23 @@ typedef struct gdn_opts {
   int32_t window_max_chunks;    /* longest lookback window in chunks; 0 -> 16 */
   float lambda1_us;             /* planner: cost of one chunk step; 0 -> built in */
   float lambda2_us;             /* planner: cost of one merge step; 0 -> built in */
+  /* Optional timing hook: NULL, or an array of 2 * GDN_NUM_STAGES events created by
+   * the caller (hipEventCreate).  For every stage that runs, the library records
+   * stage_events[2*s] on `stream` just before the stage's launch and
+   * stage_events[2*s+1] just after it; events of stages that do not run are left
+   * untouched.  Recording events is the only effect. */
+  hipEvent_t* stage_events;
 } gdn_opts;
+
+/* Stages of gdn_chunk_fwd, in launch order, for gdn_opts.stage_events. */
+enum {
+  GDN_STAGE_INVERSE = 0,    /* step 1: chunk-local gated Gram matrix and its inverse */
+  GDN_STAGE_GATE_SCAN = 1,  /* per-(sequence, head) window decision */
+  GDN_STAGE_CP_PASS1 = 2,   /* wrong-start states S* and correction matrices M */
+  GDN_STAGE_CP_MERGE = 3,   /* recurrence over segments: true segment starts */
+  GDN_STAGE_FORWARD = 4,    /* steps 2-4 fused: writes o and the final state */
+  GDN_NUM_STAGES = 5
+};
 
 /* Workspace size in bytes that gdn_chunk_fwd needs for this problem and options.
  * Returns GDN_OK and writes *bytes, or an error code for an invalid shape. */
