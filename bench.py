@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--auto-cp", type=int, default=1)
+    ap.add_argument("--value-block", type=int, default=0)
     return ap.parse_args()
 
 
@@ -159,7 +160,7 @@ def main():
     hT = torch.empty((N, spec.H, spec.dk, spec.dv), dtype=torch.float32, device=dev)
     hip = Hip()
     stage_ev = hip.events(2 * binding.GDN_NUM_STAGES)
-    opts = binding.make_opts(auto_cp=args.auto_cp,
+    opts = binding.make_opts(auto_cp=args.auto_cp, value_block=args.value_block,
                              stage_events=ctypes.cast(stage_ev, ctypes.c_void_p))
     ws = torch.empty(max(binding.workspace_bytes(d["q"], d["v"], d["beta"], d["cu_seqlens"],
                                                  inp["cu_seqlens"], opts), 1),

@@ -34,7 +34,8 @@ class GdnOpts(ctypes.Structure):
     _fields_ = [("auto_cp", ctypes.c_int32), ("force_segment_chunks", ctypes.c_int32),
                 ("force_start_mode", ctypes.c_int32), ("window_log_eps", ctypes.c_float),
                 ("window_max_chunks", ctypes.c_int32), ("lambda1_us", ctypes.c_float),
-                ("lambda2_us", ctypes.c_float), ("stage_events", ctypes.c_void_p)]
+                ("lambda2_us", ctypes.c_float), ("value_block", ctypes.c_int32),
+                ("stage_events", ctypes.c_void_p)]
 
 
 GDN_STAGE_INVERSE, GDN_STAGE_GATE_SCAN, GDN_STAGE_CP_PASS1, GDN_STAGE_CP_MERGE = 0, 1, 2, 3
@@ -117,9 +118,10 @@ class _Shape:
 
 
 def make_opts(auto_cp=1, force_segment_chunks=0, force_start_mode=0, window_log_eps=0.0,
-              window_max_chunks=0, lambda1_us=0.0, lambda2_us=0.0, stage_events=None) -> GdnOpts:
+              window_max_chunks=0, lambda1_us=0.0, lambda2_us=0.0, value_block=0,
+              stage_events=None) -> GdnOpts:
     return GdnOpts(auto_cp, force_segment_chunks, force_start_mode, window_log_eps,
-                   window_max_chunks, lambda1_us, lambda2_us, stage_events)
+                   window_max_chunks, lambda1_us, lambda2_us, value_block, stage_events)
 
 
 def workspace_bytes(q, v, beta, cu_seqlens=None, cu_seqlens_host=None, opts=None) -> int:

@@ -7,19 +7,23 @@
 // (W, U and S must not round-trip through HBM); algebraic-rewrites section
 // (forward merge: form "V minus S" first, then apply gamma).  With h = S^T the
 // state at chunk start, G the chunk-local cumsum of g, gamma = exp(G),
-// Gamma_rs = exp(G_r - G_s) (r >= s) and T from step 1:
+// Gamma_rs = exp(G_r - G_s) (r >= s), d = exp(G_last - G) and T from step 1:
 //
 //   V' = V - diag(gamma) K h                      (merged W/U form)
 //   U  = T diag(beta) V'
 //   O  = scale (diag(gamma) Q h + ((Q K^T) * Gamma) U)
-//   h <- gamma_last h + (diag(exp(G_last - G)) K)^T U
+//   h <- gamma_last h + K^T (diag(d) U)
 //
 // Mapping.  256 threads = 4 waves; each wave owns NCW value columns of h for
-// all dk rows, as 16x16 fp32 accumulator tiles in "tile order" (see
-// gdn_device.h), so h, V' and U feed the next MFMA directly from registers.
-// Each chunk's K, Q, K~^T (decay-scaled, transposed), T, P = (QK^T)*Gamma and
-// the wave's V columns are staged in LDS and read as MFMA A operands.  The
-// value columns are independent: only T and P are shared between them.
+// all dk rows, as 16x16 fp32 accumulator tiles in "tile order" (gdn_device.h),
+// so h, V' and U feed the next MFMA straight from registers.  Per chunk the
+// workgroup stages K, Q, T, the gates and its V columns in LDS (the global loads
+// of chunk c+1 are issued before chunk c is computed), computes P = (QK^T)*Gamma
+// once (tiles split over the waves), and each wave then runs its columns:
+// K^T for the state update and V in accumulator layout come from the row-major
+// tiles through LDS transpose reads; O is staged column-major per wave and
+// stored with 16-byte row writes.  Value columns are independent; only T and P
+// are shared between them.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -34,9 +38,90 @@ struct FwdCfg {
   static constexpr int NKS = DK / 32;       // contraction steps over dk
   static constexpr int PAD = sizeof(E) == 2 ? 8 : 4;
   static constexpr int KS = DK + PAD;       // row stride of sK, sQ
-  static constexpr int CS = kChunk + PAD;   // row stride of sKt, sT, sP
+  static constexpr int CS = kChunk + PAD;   // row stride of sT, sP, sO
   static constexpr int VS = BV + PAD;       // row stride of sV
+};
+
+// One chunk's inputs held in registers between the global loads and the LDS
+// stores, so the loads of chunk c+1 are in flight while chunk c is computed.
+// Nothing touches the loaded registers until store(): masking of rows past the
+// chunk end (zero there; beta = g = 0) and the beta conversion happen at store
+// time, so no wait for the loads is forced before the chunk's compute.
+template <typename E, int DK, int BV>
+struct ChunkRegs {
   static constexpr int EPV = 16 / (int)sizeof(E);
+  static constexpr int VPRK = DK / EPV, VPRV = BV / EPV, VPRT = kChunk / EPV;
+  static constexpr int NK = kChunk * VPRK / 256, NV = kChunk * VPRV / 256, NT = kChunk * VPRT / 256;
+  u32x4 k[NK], q[NK], v[NV], t[NT];
+  float g;
+  uint32_t b;   // raw beta bits (bf16 in the low half, or fp32)
+  int len;
+
+  // qb/kb/vb point at the chunk's first token (head and column offsets applied);
+  // row_* are element strides between consecutive tokens.
+  __device__ __forceinline__ void load(const E* qb, const E* kb, const E* vb, const E* ts,
+                                       const float* gb, const void* betab, bool beta_bf16,
+                                       int len_, int row_qk, int row_v, int row_g, int tid) {
+    len = len_;
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const int i = tid + 256 * j, r = i / VPRK, cv = i % VPRK;
+      const int off = min(r, len - 1) * row_qk + cv * EPV;
+      k[j] = *reinterpret_cast<const u32x4*>(kb + off);
+      q[j] = *reinterpret_cast<const u32x4*>(qb + off);
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int i = tid + 256 * j, r = i / VPRV, cv = i % VPRV;
+      v[j] = *reinterpret_cast<const u32x4*>(vb + min(r, len - 1) * row_v + cv * EPV);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) t[j] = reinterpret_cast<const u32x4*>(ts)[tid + 256 * j];
+    const int o = min(tid & (kChunk - 1), len - 1) * row_g;
+    g = gb[o];
+    if (beta_bf16) b = reinterpret_cast<const uint16_t*>(betab)[o];
+    else b = reinterpret_cast<const uint32_t*>(betab)[o];
+  }
+
+  template <int KS, int CS, int VS>
+  __device__ __forceinline__ void store(E* sK, E* sQ, E* sV, E* sT, float* sG, float* sB,
+                                        bool beta_bf16, int tid) const {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const int i = tid + 256 * j, r = i / VPRK, cv = i % VPRK;
+      const bool ok = r < len;
+      *reinterpret_cast<u32x4*>(sK + r * KS + cv * EPV) = ok ? k[j] : zero;
+      *reinterpret_cast<u32x4*>(sQ + r * KS + cv * EPV) = ok ? q[j] : zero;
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int i = tid + 256 * j, r = i / VPRV, cv = i % VPRV;
+      *reinterpret_cast<u32x4*>(sV + r * VS + cv * EPV) = r < len ? v[j] : zero;
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int i = tid + 256 * j, r = i / VPRT, cv = i % VPRT;
+      *reinterpret_cast<u32x4*>(sT + r * CS + cv * EPV) = t[j];
+    }
+    if (tid < kChunk) {
+      const bool ok = tid < len;
+      sG[tid] = ok ? g : 0.f;
+      const float bf = beta_bf16 ? __uint_as_float(b << 16) : __uint_as_float(b);
+      sB[tid] = ok ? bf : 0.f;
+    }
+  }
+};
+
+// P tiles (query tile, key tile) computed by each wave; -1 = none.  The ten
+// lower-triangular 16x16 tiles are split 3/3/2/2; tiles (0,1) and (2,3) lie
+// inside the contraction range of the P U product and are written as zeros
+// (by waves 2 and 3).
+__constant__ int kPTiles[4][3][2] = {
+    {{3, 0}, {3, 1}, {3, 2}},
+    {{3, 3}, {2, 0}, {2, 1}},
+    {{2, 2}, {1, 0}, {-1, -1}},
+    {{1, 1}, {0, 0}, {-1, -1}},
 };
 
 template <typename E, int DK, int NCW>
@@ -45,17 +130,19 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
   using M = Mma<E>;
   using frag = typename M::frag;
   constexpr int BV = Cfg::BV, NCT = Cfg::NCT, NKT = Cfg::NKT, NKS = Cfg::NKS;
-  constexpr int KS = Cfg::KS, CS = Cfg::CS, VS = Cfg::VS, EPV = Cfg::EPV;
+  constexpr int KS = Cfg::KS, CS = Cfg::CS, VS = Cfg::VS;
 
   __shared__ __align__(16) E sK[kChunk * KS];
   __shared__ __align__(16) E sQ[kChunk * KS];
-  __shared__ __align__(16) E sKt[DK * CS];
   __shared__ __align__(16) E sT[kChunk * CS];
   __shared__ __align__(16) E sP[kChunk * CS];
   __shared__ __align__(16) E sV[kChunk * VS];
-  __shared__ float sGraw[kChunk], sBraw[kChunk];
+  __shared__ __align__(16) E sO[4][NCW * CS];     // per wave, column-major [col][row]
+  __shared__ __align__(16) float sGraw[kChunk], sBraw[kChunk];
+  __shared__ __align__(16) float sGam[kChunk], sDec[kChunk], sBet[kChunk];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar table reads
   const int r16 = lane & 15, q = lane >> 4;
   const int H = p.H, dv = p.dv;
   const int col0 = blockIdx.y * BV;        // first value column of the workgroup
@@ -79,115 +166,93 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
   const int c_begin = seg * plan.seg_chunks;
   const int c_end = min(nch, c_begin + plan.seg_chunks);
 
-  const E* Q = reinterpret_cast<const E*>(p.q);
-  const E* K = reinterpret_cast<const E*>(p.k);
-  const E* V = reinterpret_cast<const E*>(p.v);
+  const int row_qk = H * DK, row_v = H * dv;   // element strides between tokens
+  const E* Qb = reinterpret_cast<const E*>(p.q) + si.tok0 * row_qk + (int64_t)h * DK;
+  const E* Kb = reinterpret_cast<const E*>(p.k) + si.tok0 * row_qk + (int64_t)h * DK;
+  const E* Vb = reinterpret_cast<const E*>(p.v) + si.tok0 * row_v + (int64_t)h * dv + col0;
+  E* Ob = reinterpret_cast<E*>(p.o) + si.tok0 * row_v + (int64_t)h * dv + col0 + wcol;
+  const float* Gb = p.g + si.tok0 * H + h;
+  const int bsz = p.beta_bf16 ? 2 : 4;
+  const char* Bb = reinterpret_cast<const char*>(p.beta) + (si.tok0 * H + h) * bsz;
   const E* Tm = reinterpret_cast<const E*>(plan.Tmat);
-  E* O = reinterpret_cast<E*>(p.o);
 
   // ---- initial state
   f32x4 hs[NKT][NCT];
-  const int64_t st_off = ((int64_t)n * H + h) * DK * dv;
+  const int64_t st_off = ((int64_t)n * H + h) * DK * dv + col0 + wcol + r16;
 #pragma unroll
   for (int t = 0; t < NKT; ++t)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        hs[t][ct][i] = (p.h0 && seg == 0)
-                           ? p.h0[st_off + (int64_t)prow(t, 4 * q + i) * dv + col0 + wcol + ct * 16 + r16]
-                           : 0.f;
+        hs[t][ct][i] = (p.h0 && seg == 0) ? p.h0[st_off + prow(t, 4 * q + i) * dv + ct * 16] : 0.f;
+
+  using Stage = ChunkRegs<E, DK, BV>;
+  Stage pf;
+  auto issue_loads = [&](int c) {
+    const int64_t t0 = (int64_t)c * kChunk;
+    const E* ts = Tm + ((si.chunk0 + c) * H + h) * (int64_t)(kChunk * kChunk);
+    pf.load(Qb + t0 * row_qk, Kb + t0 * row_qk, Vb + t0 * row_v, ts, Gb + t0 * H,
+            Bb + t0 * H * bsz, p.beta_bf16, min(kChunk, si.len - c * kChunk), row_qk, row_v, H,
+            tid);
+  };
+  if (c_begin < c_end) issue_loads(c_begin);
 
   for (int c = c_begin; c < c_end; ++c) {
-    const int64_t r0 = si.tok0 + (int64_t)c * kChunk;
     const int len = min(kChunk, si.len - c * kChunk);
 
-    // ---- stage the chunk in LDS (rows past the end are zero)
-    {
-      constexpr int VPR = DK / EPV;
-      for (int i = tid; i < kChunk * VPR; i += 256) {
-        const int r = i / VPR, cv = i % VPR;
-        u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
-        if (r < len) {
-          const int64_t off = ((r0 + r) * H + h) * DK + cv * EPV;
-          kv = *reinterpret_cast<const u32x4*>(K + off);
-          qv = *reinterpret_cast<const u32x4*>(Q + off);
-        }
-        *reinterpret_cast<u32x4*>(sK + r * KS + cv * EPV) = kv;
-        *reinterpret_cast<u32x4*>(sQ + r * KS + cv * EPV) = qv;
-      }
-      constexpr int VPRV = BV / EPV;
-      for (int i = tid; i < kChunk * VPRV; i += 256) {
-        const int r = i / VPRV, cv = i % VPRV;
-        u32x4 vv = {0u, 0u, 0u, 0u};
-        if (r < len) vv = *reinterpret_cast<const u32x4*>(V + ((r0 + r) * H + h) * dv + col0 + cv * EPV);
-        *reinterpret_cast<u32x4*>(sV + r * VS + cv * EPV) = vv;
-      }
-      constexpr int VPRT = kChunk / EPV;
-      const E* tsrc = Tm + ((si.chunk0 + c) * H + h) * (int64_t)(kChunk * kChunk);
-      for (int i = tid; i < kChunk * VPRT; i += 256) {
-        const int r = i / VPRT, cv = i % VPRT;
-        *reinterpret_cast<u32x4*>(sT + r * CS + cv * EPV) =
-            *reinterpret_cast<const u32x4*>(tsrc + r * kChunk + cv * EPV);
-      }
-      if (wave == 0) {
-        float gv = 0.f, bv = 0.f;
-        if (lane < len) {
-          gv = p.g[(r0 + lane) * H + h];
-          bv = load_scalar(p.beta, (r0 + lane) * H + h, p.beta_bf16);
-        }
-        sGraw[lane] = gv;
-        sBraw[lane] = bv;
-      }
-    }
+    // ---- stage chunk c in LDS, then start the loads of chunk c+1
+    pf.template store<KS, CS, VS>(sK, sQ, sV, sT, sGraw, sBraw, p.beta_bf16, tid);
     __syncthreads();
+    if (c + 1 < c_end) issue_loads(c + 1);
 
-    // ---- gates (every wave keeps its own copy; lane = chunk row)
+    // ---- gates: every wave scans (lane = chunk row); wave 0 publishes per-row values
     const float G = wave_inclusive_scan(sGraw[lane]);
     const float Glast = __shfl(G, 63, 64);
-    const float gam_l = fast_exp(G);
-    const float dec_l = fast_exp(Glast - G);
     const float gC = fast_exp(Glast);
-    const float bet_l = sBraw[lane];
-
-    // ---- K~^T: decay-scaled, transposed keys (wave w handles dk groups of 8)
-#pragma unroll
-    for (int jj = 0; jj < DK / 32; ++jj) {
-      const int j = wave * (DK / 32) + jj;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        sKt[(8 * j + e) * CS + lane] = from_f32<E>(to_f32(sK[lane * KS + 8 * j + e]) * dec_l);
+    if (wave == 0) {
+      sGam[lane] = fast_exp(G);
+      sDec[lane] = fast_exp(Glast - G);
+      sBet[lane] = sBraw[lane];
     }
-    // ---- P = (Q K^T) * Gamma, row tile = wave (natural row order)
+    // ---- P = (Q K^T) * Gamma as row-major [query][key]; computed as P^T = K Q^T so a
+    //      lane holds four consecutive keys of one query row
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if (v <= wave) {
+    for (int pt = 0; pt < 3; ++pt) {
+      const int qt = kPTiles[wave][pt][0], kt = kPTiles[wave][pt][1];
+      if (qt >= 0) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NKS; ++s)
-          acc = M::run(lds_frag(sQ, KS, 16 * wave + r16, 32 * s, q),
-                       lds_frag(sK, KS, 16 * v + r16, 32 * s, q), acc);
-      }
-      const int col = 16 * v + r16;
-      const float Gcol = __shfl(G, col, 64);
+          acc = M::run(lds_frag(sK, KS, 16 * kt + r16, 32 * s, q),
+                       lds_frag(sQ, KS, 16 * qt + r16, 32 * s, q), acc);
+        const int qrow = 16 * qt + r16;
+        const float Gq = __shfl(G, qrow, 64);
+        E* dst = sP + qrow * CS + 16 * kt + 4 * q;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * wave + 4 * q + i;
-        const float Grow = __shfl(G, row, 64);
-        const float val = (col <= row) ? acc[i] * fast_exp(Grow - Gcol) : 0.f;
-        sP[row * CS + col] = from_f32<E>(val);
+        for (int i = 0; i < 4; ++i) {
+          const int key = 16 * kt + 4 * q + i;
+          const float Gk = __shfl(G, key, 64);
+          dst[i] = from_f32<E>(key <= qrow ? acc[i] * fast_exp(Gq - Gk) : 0.f);
+        }
+      } else if (pt == 2) {
+        const int zq = wave == 2 ? 0 : 2, zk = zq + 1;
+        E* dst = sP + (16 * zq + r16) * CS + 16 * zk + 4 * q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = from_f32<E>(0.f);
       }
     }
-    // per-row gate values in tile order
-    float gam_r[4][4], bet_r[4][4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        gam_r[u][i] = __shfl(gam_l, prow(u, 4 * q + i), 64);
-        bet_r[u][i] = __shfl(bet_l, prow(u, 4 * q + i), 64);
-      }
     __syncthreads();
+
+    // ---- per-row gates in tile order (rows prow(u, 4q) .. +3 are consecutive)
+    f32x4 gam4[4], bet4[4], dec4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = prow(u, 4 * q);
+      gam4[u] = *reinterpret_cast<const f32x4*>(sGam + r);
+      bet4[u] = *reinterpret_cast<const f32x4*>(sBet + r);
+      dec4[u] = *reinterpret_cast<const f32x4*>(sDec + r);
+    }
 
     // ---- X = K h, Y = Q h
     f32x4 X[4][NCT], Y[4][NCT];
@@ -214,17 +279,15 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
         }
       }
     }
-    // ---- W = diag(beta) (V - diag(gamma) X), in place
+    // ---- W = diag(beta) (V - diag(gamma) X), in place; V read in accumulator layout
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = prow(u, 4 * q + i);
-          const float vv = to_f32(sV[row * VS + wcol + ct * 16 + r16]);
-          X[u][ct][i] = bet_r[u][i] * (vv - gam_r[u][i] * X[u][ct][i]);
-        }
+      for (int ct = 0; ct < NCT; ++ct) {
+        const int cb = wcol + 16 * ct;
+        const f32x4 vv = col_read4(sV, VS, prow(u, 4 * q), cb + r16, cb + 4 * (r16 & 3));
+        X[u][ct] = bet4[u] * (vv - gam4[u] * X[u][ct]);
+      }
     // ---- U = T W (T lower triangular: row tiles 0,1 need contraction step 0 only)
     frag wb[2][NCT];
 #pragma unroll
@@ -243,18 +306,20 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
         for (int ct = 0; ct < NCT; ++ct) U[u][ct] = M::run(aT, wb[s][ct], U[u][ct]);
       }
     }
-    frag ub[2][NCT];
+    frag ub[2][NCT], ubd[2][NCT];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) ub[s][ct] = M::pack(U[2 * s][ct], U[2 * s + 1][ct]);
-    // ---- O = scale (diag(gamma) Y + P U)
+      for (int ct = 0; ct < NCT; ++ct) {
+        ub[s][ct] = M::pack(U[2 * s][ct], U[2 * s + 1][ct]);
+        ubd[s][ct] = M::pack(U[2 * s][ct] * dec4[2 * s], U[2 * s + 1][ct] * dec4[2 * s + 1]);
+      }
+    // ---- O = scale (diag(gamma) Y + P U), staged column-major in this wave's sO
+    E* so = sO[wave];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Y[u][ct][i] *= gam_r[u][i];
+      for (int ct = 0; ct < NCT; ++ct) Y[u][ct] = Y[u][ct] * gam4[u];
 #pragma unroll
       for (int s = 0; s <= (u >> 1); ++s) {
         const frag aP = lds_frag(sP, CS, prow(u, r16), 32 * s, q);
@@ -262,25 +327,38 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
         for (int ct = 0; ct < NCT; ++ct) Y[u][ct] = M::run(aP, ub[s][ct], Y[u][ct]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = prow(u, 4 * q + i);
-        if (row < len) {
-          E* dst = O + ((r0 + row) * H + h) * dv + col0 + wcol + r16;
+      for (int ct = 0; ct < NCT; ++ct) {
+        E* dst = so + (16 * ct + r16) * CS + prow(u, 4 * q);
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) dst[ct * 16] = from_f32<E>(p.scale * Y[u][ct][i]);
-        }
+        for (int i = 0; i < 4; ++i) dst[i] = from_f32<E>(p.scale * Y[u][ct][i]);
       }
     }
-    // ---- h <- gamma_last h + K~^T U
+    // ---- h <- gamma_last h + K^T (diag(d) U); K^T via transpose reads of sK
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) hs[t][ct] *= gC;
+      const int own = prow(t, r16), supply = prow(t, 4 * (r16 & 3));
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const frag aKt = lds_frag(sKt, CS, prow(t, r16), 32 * s, q);
+        const frag aKt = col_frag(sK, KS, 32 * s + 8 * q, own, supply);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) hs[t][ct] = M::run(aKt, ub[s][ct], hs[t][ct]);
+        for (int ct = 0; ct < NCT; ++ct) hs[t][ct] = M::run(aKt, ubd[s][ct], hs[t][ct]);
+      }
+    }
+    // ---- O store: lane (j, q) writes 8 consecutive columns of token row 16*rb + j
+    {
+      constexpr int NG = NCW / 8;   // 8-column groups per wave
+      E* ob = Ob + (int64_t)c * kChunk * row_v;
+#pragma unroll
+      for (int rr = 0; rr < NG; ++rr) {
+        const int item = rr * 4 + q;
+        const int rb = item / NG, cg8 = item % NG;
+        const int row = 16 * rb + r16;
+        const int supply = 16 * rb + 4 * (r16 & 3);
+        const auto lo = col_read4_storage(so, CS, 8 * cg8, row, supply);
+        const auto hi = col_read4_storage(so, CS, 8 * cg8 + 4, row, supply);
+        if (row < len) store8(ob + row * row_v + 8 * cg8, lo, hi);
       }
     }
     __syncthreads();
@@ -292,15 +370,14 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          p.hT[st_off + (int64_t)prow(t, 4 * q + i) * dv + col0 + wcol + ct * 16 + r16] = hs[t][ct][i];
+        for (int i = 0; i < 4; ++i) p.hT[st_off + prow(t, 4 * q + i) * dv + ct * 16] = hs[t][ct][i];
   }
 }
 
 template <typename E, int DK>
 static void launch_dk(const Problem& p, const FwdPlan& plan, hipStream_t s) {
   if constexpr (sizeof(E) == 2) {  // fp32 tiles only fit LDS at 64 columns per workgroup
-    if (p.dv % 128 == 0) {
+    if (p.dv % 128 == 0 && plan.value_block != 64) {
       dim3 grid((unsigned)plan.units, (unsigned)(p.dv / 128));
       fused_forward_kernel<E, DK, 32><<<grid, 256, 0, s>>>(p, plan);
       return;

@@ -123,7 +123,6 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                   const float* initial_state, const int32_t* cu_seqlens, float scale, void* o,
                   float* final_state, const gdn_shape* shape, const gdn_opts* opts,
                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  (void)opts;
   int rc = validate_shape(shape);
   if (rc != GDN_OK) return rc;
   rc = check_inputs(k, g, beta, cu_seqlens, shape);
@@ -133,6 +132,8 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
       (initial_state && !aligned(initial_state, 16)) || (final_state && !aligned(final_state, 16)))
     return GDN_ERR_ARG;
   if (!std::isfinite(scale)) return GDN_ERR_ARG;
+  if (opts && opts->value_block != 0 && opts->value_block != 64 && opts->value_block != 128)
+    return GDN_ERR_ARG;
   const Layout L = layout(shape);
   if (workspace_bytes < L.total || (L.total > 0 && !workspace) || !aligned(workspace, kAlign))
     return GDN_ERR_WORKSPACE;
@@ -157,6 +158,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
   plan.seg_chunks = INT_MAX / 2;
   plan.seg_off = nullptr;
   plan.units = (int64_t)p.N * p.H;
+  plan.value_block = opts ? opts->value_block : 0;
   {
     StageMark mark(opts, GDN_STAGE_FORWARD, stream);
     if (gdn::launch_fused_forward(p, plan, stream) != hipSuccess) return GDN_ERR_HIP;

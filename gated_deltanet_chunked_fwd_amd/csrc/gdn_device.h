@@ -78,6 +78,95 @@ __device__ __forceinline__ typename Mma<E>::frag lds_frag(const E* base, int str
   return *reinterpret_cast<const typename Mma<E>::frag*>(base + row * stride + kbase + 8 * q);
 }
 
+// Column read of a row-major LDS matrix M: for the lane with index j inside its
+// 16-lane group, returns M[row0 + i][colmap(j)], i = 0..3, where the 16 columns
+// of a group form four runs of four, colmap(j) = base(j / 4) + j % 4, base()
+// 4-element aligned.  Every lane of a group passes the same row0.
+//   own_col    = colmap(j) of this lane (used by the fp32 form)
+//   supply_col = base(j % 4)  (used by the bf16 form)
+// bf16: one ds_read_b64_tr_b16.  Inside a 16-lane group, lane j receives element
+// j % 4 of the 8-byte chunks addressed by lanes 4i + j / 4 (i = 0..3), so lane j'
+// addresses M[row0 + j'/4][base(j'%4)].  fp32: four plain reads.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 col_read4(const bf16* M, int stride, int row0, int own_col,
+                                           int supply_col) {
+  (void)own_col;
+  const int j = threadIdx.x & 15;
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const bf16* addr = M + (row0 + (j >> 2)) * stride + supply_col;
+  const i16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(__attribute__((address_space(3))) void*)(addr));
+  f32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __uint_as_float(((uint32_t)(uint16_t)raw[i]) << 16);
+  return r;
+}
+
+__device__ __forceinline__ f32x4 col_read4(const float* M, int stride, int row0, int own_col,
+                                           int supply_col) {
+  (void)supply_col;
+  f32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = M[(row0 + i) * stride + own_col];
+  return r;
+}
+
+// Same column read returning the raw storage elements (to build MFMA operands).
+__device__ __forceinline__ i16x4 col_read4_raw(const bf16* M, int stride, int row0, int own_col,
+                                               int supply_col) {
+  (void)own_col;
+  const int j = threadIdx.x & 15;
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const bf16* addr = M + (row0 + (j >> 2)) * stride + supply_col;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(__attribute__((address_space(3))) void*)(addr));
+}
+
+// A/B operand of one 32-wide contraction step whose 8 elements are column reads
+// at rows row0 .. row0+3 (elements 0-3) and row0+4 .. row0+7 (elements 4-7).
+__device__ __forceinline__ bf16x8 col_frag(const bf16* M, int stride, int row0, int own_col,
+                                           int supply_col) {
+  const i16x4 lo = col_read4_raw(M, stride, row0, own_col, supply_col);
+  const i16x4 hi = col_read4_raw(M, stride, row0 + 4, own_col, supply_col);
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 v;
+  v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+  v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ f32x8 col_frag(const float* M, int stride, int row0, int own_col,
+                                          int supply_col) {
+  (void)supply_col;
+  f32x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = M[(row0 + i) * stride + own_col];
+  return r;
+}
+
+// Stores 8 consecutive elements: lo = elements 0..3, hi = 4..7 (raw storage).
+__device__ __forceinline__ void store8(bf16* dst, i16x4 lo, i16x4 hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 v;
+  v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+  v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+  *reinterpret_cast<i16x8*>(dst) = v;
+}
+__device__ __forceinline__ void store8(float* dst, f32x4 lo, f32x4 hi) {
+  reinterpret_cast<f32x4*>(dst)[0] = lo;
+  reinterpret_cast<f32x4*>(dst)[1] = hi;
+}
+__device__ __forceinline__ i16x4 col_read4_storage(const bf16* M, int stride, int row0, int own_col,
+                                                   int supply_col) {
+  return col_read4_raw(M, stride, row0, own_col, supply_col);
+}
+__device__ __forceinline__ f32x4 col_read4_storage(const float* M, int stride, int row0,
+                                                   int own_col, int supply_col) {
+  return col_read4(M, stride, row0, own_col, supply_col);
+}
+
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 template <typename E>

@@ -33,6 +33,7 @@ struct FwdPlan {
   int seg_chunks;            // chunks per segment (>= max chunks of any sequence: one segment)
   const int32_t* seg_off;    // device [N+1] segment offsets (packed + split) or null
   int64_t units;             // number of (sequence, head, segment) units
+  int value_block;           // value columns per workgroup: 64, 128, or 0 (widest that fits)
 };
 
 hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hipStream_t s);

@@ -43,6 +43,13 @@ def test_parity_small(name, kw):
     assert_parity(compare_pairs(inp, o, hT), TOL[inp["spec"].dtype], name)
 
 
+@pytest.mark.parametrize("vb", [64, 128])
+def test_parity_value_block(vb):
+    inp = synth.generate(spec(B=2, T=333, H=2, dk=128, dv=128, h0_std=0.05, seed=29))
+    o, hT = run_gpu(inp, opts=binding.make_opts(value_block=vb))
+    assert_parity(compare_pairs(inp, o, hT), TOL["bf16"], "value_block %d" % vb)
+
+
 def _packed(lengths, H, dk, dv, dtype, h0_std, seed):
     """Packed sequences with given lengths (built from one dense draw)."""
     T = int(sum(lengths))
