@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--workload", type=int, default=2, help="workload number (1-5)")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--auto-cp", type=int, default=1)
+    ap.add_argument("--no-split", type=int, default=0)
     ap.add_argument("--value-block", type=int, default=0)
     return ap.parse_args()
 
@@ -160,12 +160,13 @@ def main():
     hT = torch.empty((N, spec.H, spec.dk, spec.dv), dtype=torch.float32, device=dev)
     hip = Hip()
     stage_ev = hip.events(2 * binding.GDN_NUM_STAGES)
-    opts = binding.make_opts(auto_cp=args.auto_cp, value_block=args.value_block,
+    opts = binding.make_opts(no_split=args.no_split, value_block=args.value_block,
                              stage_events=ctypes.cast(stage_ev, ctypes.c_void_p))
     ws = torch.empty(max(binding.workspace_bytes(d["q"], d["v"], d["beta"], d["cu_seqlens"],
                                                  inp["cu_seqlens"], opts), 1),
                      dtype=torch.uint8, device=dev)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    seg_chunks = binding.plan_segment_chunks(d["q"], d["v"], d["beta"], inp["cu_seqlens"], opts)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     step_ev = hip.events(2)
 
@@ -234,7 +235,8 @@ def main():
         "data": "synthetic (seeded; q,k L2-normalised, g=log sigmoid(N(3,1)), beta=sigmoid(N(0,1)))",
         "config": {"workload": spec.name, "B": spec.B, "T": spec.T, "H": spec.H, "dk": spec.dk,
                    "dv": spec.dv, "chunk": 64, "initial_state": has_h0,
-                   "final_state": True, "auto_cp": args.auto_cp, "parallelism": "single GPU"},
+                   "final_state": True, "split_allowed": not args.no_split,
+                   "segment_chunks": seg_chunks, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": alg_bytes, "kernel_ms": dom_ms},

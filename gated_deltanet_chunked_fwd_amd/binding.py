@@ -20,6 +20,7 @@ GDN_BF16, GDN_F32 = 1, 2
 
 # Symbols declared in include/gdn.h (checked by the CPU test of the boundary).
 EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_inverse",
+           "gdn_gate_scan", "gdn_gate_scan_workspace_bytes", "gdn_plan_segment_chunks",
            "gdn_total_chunks", "gdn_status_str")
 
 
@@ -31,8 +32,8 @@ class GdnShape(ctypes.Structure):
 
 
 class GdnOpts(ctypes.Structure):
-    _fields_ = [("auto_cp", ctypes.c_int32), ("force_segment_chunks", ctypes.c_int32),
-                ("force_start_mode", ctypes.c_int32), ("window_log_eps", ctypes.c_float),
+    _fields_ = [("no_split", ctypes.c_int32), ("force_segment_chunks", ctypes.c_int32),
+                ("force_correction", ctypes.c_int32), ("window_log_eps", ctypes.c_float),
                 ("window_max_chunks", ctypes.c_int32), ("lambda1_us", ctypes.c_float),
                 ("lambda2_us", ctypes.c_float), ("value_block", ctypes.c_int32),
                 ("stage_events", ctypes.c_void_p)]
@@ -68,6 +69,12 @@ def lib():
         L.gdn_chunk_fwd.restype = ctypes.c_int
         L.gdn_chunk_inverse.argtypes = [vp, vp, vp, vp, shp, vp, vp, sz, vp]
         L.gdn_chunk_inverse.restype = ctypes.c_int
+        L.gdn_gate_scan.argtypes = [vp, vp, shp, opt, vp, vp, sz, vp]
+        L.gdn_gate_scan.restype = ctypes.c_int
+        L.gdn_gate_scan_workspace_bytes.argtypes = [shp, ctypes.POINTER(sz)]
+        L.gdn_gate_scan_workspace_bytes.restype = ctypes.c_int
+        L.gdn_plan_segment_chunks.argtypes = [shp, opt]
+        L.gdn_plan_segment_chunks.restype = ctypes.c_int64
         L.gdn_total_chunks.argtypes = [shp]
         L.gdn_total_chunks.restype = ctypes.c_int64
         L.gdn_status_str.argtypes = [ctypes.c_int]
@@ -117,10 +124,10 @@ class _Shape:
         return ctypes.byref(self.s)
 
 
-def make_opts(auto_cp=1, force_segment_chunks=0, force_start_mode=0, window_log_eps=0.0,
+def make_opts(no_split=0, force_segment_chunks=0, force_correction=0, window_log_eps=0.0,
               window_max_chunks=0, lambda1_us=0.0, lambda2_us=0.0, value_block=0,
               stage_events=None) -> GdnOpts:
-    return GdnOpts(auto_cp, force_segment_chunks, force_start_mode, window_log_eps,
+    return GdnOpts(no_split, force_segment_chunks, force_correction, window_log_eps,
                    window_max_chunks, lambda1_us, lambda2_us, value_block, stage_events)
 
 
@@ -192,3 +199,36 @@ def chunk_inverse(k, g, beta, cu_seqlens=None, cu_seqlens_host=None):
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_chunk_inverse")
     return t
+
+
+def gate_scan(g, cu_seqlens=None, cu_seqlens_host=None, opts: Optional[GdnOpts] = None):
+    """The gate scan alone: int32 [N, H] lookback windows (0 = none)."""
+    B, T, H = g.shape
+    fake_q = torch.empty((B, T, H, 64), dtype=torch.bfloat16, device="meta")
+    sh = _Shape(fake_q, fake_q, g, cu_seqlens, cu_seqlens_host)
+    sh.s.dk = 64
+    sh.s.dv = 64
+    sh.s.qkv_dtype = GDN_BF16
+    sh.s.beta_dtype = GDN_F32
+    n = ctypes.c_size_t(0)
+    rc = lib().gdn_gate_scan_workspace_bytes(sh.ref(), ctypes.byref(n))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_gate_scan_workspace_bytes")
+    ws = torch.empty(int(n.value), dtype=torch.uint8, device=g.device)
+    out = torch.empty((sh.N, H), dtype=torch.int32, device=g.device)
+    rc = lib().gdn_gate_scan(_ptr(g), _ptr(cu_seqlens), sh.ref(),
+                             None if opts is None else ctypes.byref(opts), _ptr(out), _ptr(ws),
+                             ctypes.c_size_t(ws.numel()), _stream(g.device))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_gate_scan")
+    return out
+
+
+def plan_segment_chunks(q, v, beta, cu_seqlens_host=None, opts: Optional[GdnOpts] = None) -> int:
+    """Segment length (chunks) the planner picks; >= the longest sequence's chunks = no split."""
+    cu = None if cu_seqlens_host is None else cu_seqlens_host
+    sh = _Shape(q, v, beta, cu, cu_seqlens_host)
+    r = lib().gdn_plan_segment_chunks(sh.ref(), None if opts is None else ctypes.byref(opts))
+    if r < 0:
+        raise GdnError(int(r), "gdn_plan_segment_chunks")
+    return int(r)

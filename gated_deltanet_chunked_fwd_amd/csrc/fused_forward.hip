@@ -61,7 +61,8 @@ struct ChunkRegs {
   // row_* are element strides between consecutive tokens.
   __device__ __forceinline__ void load(const E* qb, const E* kb, const E* vb, const E* ts,
                                        const float* gb, const void* betab, bool beta_bf16,
-                                       int len_, int row_qk, int row_v, int row_g, int tid) {
+                                       int len_, int row_qk, int row_v, int row_g, bool vzero,
+                                       int tid) {
     len = len_;
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
@@ -70,10 +71,12 @@ struct ChunkRegs {
       k[j] = *reinterpret_cast<const u32x4*>(kb + off);
       q[j] = *reinterpret_cast<const u32x4*>(qb + off);
     }
+    if (!vzero) {
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int i = tid + 256 * j, r = i / VPRV, cv = i % VPRV;
-      v[j] = *reinterpret_cast<const u32x4*>(vb + min(r, len - 1) * row_v + cv * EPV);
+      for (int j = 0; j < NV; ++j) {
+        const int i = tid + 256 * j, r = i / VPRV, cv = i % VPRV;
+        v[j] = *reinterpret_cast<const u32x4*>(vb + min(r, len - 1) * row_v + cv * EPV);
+      }
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j) t[j] = reinterpret_cast<const u32x4*>(ts)[tid + 256 * j];
@@ -85,7 +88,7 @@ struct ChunkRegs {
 
   template <int KS, int CS, int VS>
   __device__ __forceinline__ void store(E* sK, E* sQ, E* sV, E* sT, float* sG, float* sB,
-                                        bool beta_bf16, int tid) const {
+                                        bool beta_bf16, bool vzero, int tid) const {
     const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
@@ -97,7 +100,7 @@ struct ChunkRegs {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int i = tid + 256 * j, r = i / VPRV, cv = i % VPRV;
-      *reinterpret_cast<u32x4*>(sV + r * VS + cv * EPV) = r < len ? v[j] : zero;
+      *reinterpret_cast<u32x4*>(sV + r * VS + cv * EPV) = (r < len && !vzero) ? v[j] : zero;
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -157,35 +160,68 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
     seg = (int)(sg - plan.seg_off[n]);
   } else {
     const int64_t nch_all = (p.T + kChunk - 1) / kChunk;
-    const int64_t segs = (nch_all + plan.seg_chunks - 1) / plan.seg_chunks;
-    n = (int)(sg / (segs > 0 ? segs : 1));
+    const int64_t segs = max((int64_t)1, (nch_all + plan.seg_chunks - 1) / plan.seg_chunks);
+    n = (int)(sg / segs);
     seg = (int)(sg - (int64_t)n * segs);
   }
   const SeqInfo si = seq_info(n, p.cu, p.chunk_off, p.T);
   const int nch = (si.len + kChunk - 1) / kChunk;
   const int c_begin = seg * plan.seg_chunks;
   const int c_end = min(nch, c_begin + plan.seg_chunks);
+  const int nh = n * H + h;
+  const bool last_seg = c_end >= nch;
+  const int W = (plan.cp.best && !plan.cp.force_correction)
+                    ? window_of(plan.cp.best, nh, nch, plan.cp.wmax, plan.cp.thr) : 0;
+
+  // start state and the chunk range: [c_start, c_end) is run, O is written from c_out
+  enum { kZero, kH0, kBuf, kEye };
+  int init = kZero, c_start = c_begin, c_out = c_begin;
+  bool mcols = false;   // pass 1: this block carries the transition-matrix columns
+  if (plan.mode == kPass1) {
+    if (W > 0 || last_seg) return;     // window heads and last segments need no pass 1
+    mcols = col0 >= dv;
+    init = mcols ? kEye : kZero;
+    c_out = c_end;
+  } else if (seg == 0) {
+    init = p.h0 ? kH0 : kZero;
+  } else if (W > 0) {
+    c_start = c_begin - W;
+    if (c_start <= 0) { c_start = 0; init = p.h0 ? kH0 : kZero; }
+  } else {
+    init = kBuf;
+  }
+  const int vcol0 = mcols ? 0 : col0;  // value columns addressed by this block
 
   const int row_qk = H * DK, row_v = H * dv;   // element strides between tokens
   const E* Qb = reinterpret_cast<const E*>(p.q) + si.tok0 * row_qk + (int64_t)h * DK;
   const E* Kb = reinterpret_cast<const E*>(p.k) + si.tok0 * row_qk + (int64_t)h * DK;
-  const E* Vb = reinterpret_cast<const E*>(p.v) + si.tok0 * row_v + (int64_t)h * dv + col0;
-  E* Ob = reinterpret_cast<E*>(p.o) + si.tok0 * row_v + (int64_t)h * dv + col0 + wcol;
+  const E* Vb = reinterpret_cast<const E*>(p.v) + si.tok0 * row_v + (int64_t)h * dv + vcol0;
+  E* Ob = reinterpret_cast<E*>(p.o) + si.tok0 * row_v + (int64_t)h * dv + vcol0 + wcol;
   const float* Gb = p.g + si.tok0 * H + h;
   const int bsz = p.beta_bf16 ? 2 : 4;
   const char* Bb = reinterpret_cast<const char*>(p.beta) + (si.tok0 * H + h) * bsz;
   const E* Tm = reinterpret_cast<const E*>(plan.Tmat);
 
-  // ---- initial state
+  // ---- initial state (tile order: slot i of lane group q in tile t is dk row prow(t, 4q+i))
   f32x4 hs[NKT][NCT];
-  const int64_t st_off = ((int64_t)n * H + h) * DK * dv + col0 + wcol + r16;
+  {
+    const int64_t sg_slot = sg * H + h;
+    const float* src = init == kH0 ? p.h0 + (int64_t)nh * DK * dv
+                                   : (init == kBuf ? plan.cp.hstart + sg_slot * DK * dv : nullptr);
+    const int mc = col0 - dv + wcol + r16;   // identity column (pass-1 matrix block)
 #pragma unroll
-  for (int t = 0; t < NKT; ++t)
+    for (int t = 0; t < NKT; ++t)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
+      for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        hs[t][ct][i] = (p.h0 && seg == 0) ? p.h0[st_off + prow(t, 4 * q + i) * dv + ct * 16] : 0.f;
+        for (int i = 0; i < 4; ++i) {
+          const int r = prow(t, 4 * q + i);
+          float x = 0.f;
+          if (src) x = src[(int64_t)r * dv + col0 + wcol + ct * 16 + r16];
+          else if (init == kEye) x = (r == mc + ct * 16) ? 1.f : 0.f;
+          hs[t][ct][i] = x;
+        }
+  }
 
   using Stage = ChunkRegs<E, DK, BV>;
   Stage pf;
@@ -194,15 +230,16 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
     const E* ts = Tm + ((si.chunk0 + c) * H + h) * (int64_t)(kChunk * kChunk);
     pf.load(Qb + t0 * row_qk, Kb + t0 * row_qk, Vb + t0 * row_v, ts, Gb + t0 * H,
             Bb + t0 * H * bsz, p.beta_bf16, min(kChunk, si.len - c * kChunk), row_qk, row_v, H,
-            tid);
+            mcols, tid);
   };
-  if (c_begin < c_end) issue_loads(c_begin);
+  if (c_start < c_end) issue_loads(c_start);
 
-  for (int c = c_begin; c < c_end; ++c) {
+  for (int c = c_start; c < c_end; ++c) {
     const int len = min(kChunk, si.len - c * kChunk);
+    const bool emit = c >= c_out;   // uniform: lookback and pass-1 chunks write no O
 
     // ---- stage chunk c in LDS, then start the loads of chunk c+1
-    pf.template store<KS, CS, VS>(sK, sQ, sV, sT, sGraw, sBraw, p.beta_bf16, tid);
+    pf.template store<KS, CS, VS>(sK, sQ, sV, sT, sGraw, sBraw, p.beta_bf16, mcols, tid);
     __syncthreads();
     if (c + 1 < c_end) issue_loads(c + 1);
 
@@ -219,6 +256,7 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
     //      lane holds four consecutive keys of one query row
 #pragma unroll
     for (int pt = 0; pt < 3; ++pt) {
+      if (!emit) break;
       const int qt = kPTiles[wave][pt][0], kt = kPTiles[wave][pt][1];
       if (qt >= 0) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -271,11 +309,12 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const frag aK = lds_frag(sK, KS, prow(u, r16), 32 * s, q);
-        const frag aQ = lds_frag(sQ, KS, prow(u, r16), 32 * s, q);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          X[u][ct] = M::run(aK, hb[ct], X[u][ct]);
-          Y[u][ct] = M::run(aQ, hb[ct], Y[u][ct]);
+        for (int ct = 0; ct < NCT; ++ct) X[u][ct] = M::run(aK, hb[ct], X[u][ct]);
+        if (emit) {
+          const frag aQ = lds_frag(sQ, KS, prow(u, r16), 32 * s, q);
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) Y[u][ct] = M::run(aQ, hb[ct], Y[u][ct]);
         }
       }
     }
@@ -318,6 +357,7 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
     E* so = sO[wave];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
+      if (!emit) break;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) Y[u][ct] = Y[u][ct] * gam4[u];
 #pragma unroll
@@ -347,7 +387,7 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
       }
     }
     // ---- O store: lane (j, q) writes 8 consecutive columns of token row 16*rb + j
-    {
+    if (emit) {
       constexpr int NG = NCW / 8;   // 8-column groups per wave
       E* ob = Ob + (int64_t)c * kChunk * row_v;
 #pragma unroll
@@ -364,26 +404,47 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
     __syncthreads();
   }
 
-  if (p.hT) {
+  // ---- end state: final state (pass 3, last segment), or S* / M (pass 1)
+  float* dst = nullptr;
+  int64_t dst_off = 0;
+  int dst_row = dv;
+  if (plan.mode == kPass1) {
+    const int64_t slot = sg * H + h;
+    if (mcols) {
+      dst = plan.cp.mcorr;
+      dst_off = slot * DK * DK + (col0 - dv);
+      dst_row = DK;
+    } else {
+      dst = plan.cp.sstar;
+      dst_off = slot * DK * dv + col0;
+    }
+  } else if (last_seg && p.hT) {
+    dst = p.hT;
+    dst_off = (int64_t)nh * DK * dv + col0;
+  }
+  if (dst) {
 #pragma unroll
     for (int t = 0; t < NKT; ++t)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p.hT[st_off + prow(t, 4 * q + i) * dv + ct * 16] = hs[t][ct][i];
+        for (int i = 0; i < 4; ++i)
+          dst[dst_off + (int64_t)prow(t, 4 * q + i) * dst_row + wcol + ct * 16 + r16] = hs[t][ct][i];
   }
 }
 
 template <typename E, int DK>
 static void launch_dk(const Problem& p, const FwdPlan& plan, hipStream_t s) {
+  // pass 1 also runs dk transition-matrix columns after the dv value columns
+  const int cols = plan.mode == kPass1 ? p.dv + DK : p.dv;
   if constexpr (sizeof(E) == 2) {  // fp32 tiles only fit LDS at 64 columns per workgroup
-    if (p.dv % 128 == 0 && plan.value_block != 64) {
-      dim3 grid((unsigned)plan.units, (unsigned)(p.dv / 128));
+    if (p.dv % 128 == 0 && cols % 128 == 0 && plan.value_block != 64) {
+      dim3 grid((unsigned)plan.units, (unsigned)(cols / 128));
       fused_forward_kernel<E, DK, 32><<<grid, 256, 0, s>>>(p, plan);
       return;
     }
   }
-  dim3 grid((unsigned)plan.units, (unsigned)(p.dv / 64));
+  dim3 grid((unsigned)plan.units, (unsigned)(cols / 64));
   fused_forward_kernel<E, DK, 16><<<grid, 256, 0, s>>>(p, plan);
 }
 

@@ -1,0 +1,135 @@
+// Gate scan on gfx950: per (sequence, head), the largest gate sum over every run
+// of W consecutive chunks (W = 1..wmax), from which the window-lookback length
+// is decided.
+//
+// FlashQLA talk transcript (tokendh.com), sliding-window section: with alpha < 1
+// and ||I - beta k k^T|| <= 1 a state's influence decays by alpha per token, so a
+// head whose gate is not identically 1 has a window beyond which old state no
+// longer matters; a light kernel scans each head's gates (cost of about one gate
+// cumsum) to pick the heads that may start a segment from a lookback window.
+//
+// Decision: the error of starting W chunks early from a zero state is at most
+// ||S_old|| exp(sum of g over those chunks), so W is admissible iff every run of W
+// consecutive chunks has gate sum <= log_eps - margin (margin 1e-3 absorbs the
+// fp32 summation error).  The smallest admissible W <= wmax is used; 0 = none.
+//
+// Two kernels.  gate_window_max: grid (N*H, ceil(max chunks / 256)); each block
+// forms the chunk sums of its 256 chunks (plus a halo of wmax-1), the maximum
+// run sum per W over runs starting in its range, and merges them with an atomic
+// max into best[nh][W] (floats stored as order-preserving uints, reset to 0 =
+// "minus infinity" beforehand).  window_of() turns best[] into W wherever it is
+// needed; gate_window_finalize writes it out for the stand-alone entry point.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+__global__ __launch_bounds__(256) void gate_window_max_kernel(const float* __restrict__ g,
+                                                              const int32_t* __restrict__ cu,
+                                                              const int32_t* __restrict__ chunk_off,
+                                                              int64_t T, int N, int H, int wmax,
+                                                              uint32_t* __restrict__ best) {
+  __shared__ float sums[256 + kWindowMaxCap];
+  __shared__ float red[4][kWindowMaxCap];
+  const int nh = blockIdx.x, n = nh / H, h = nh % H;
+  const SeqInfo si = seq_info(n, cu, chunk_off, T);
+  const int nch = (si.len + kChunk - 1) / kChunk;
+  const int cs = blockIdx.y * 256;
+  if (cs >= nch) return;
+  const int tid = threadIdx.x;
+  // chunk sums for chunks cs + i, i < 256 + wmax - 1
+  for (int i = tid; i < 256 + wmax - 1; i += 256) {
+    const int c = cs + i;
+    float s = 0.f;
+    if (c < nch) {
+      const int r0 = c * kChunk, rl = min(kChunk, si.len - r0);
+      const float* gp = g + (si.tok0 + r0) * H + h;
+      for (int r = 0; r < rl; ++r) s += gp[(int64_t)r * H];
+    }
+    sums[i] = s;
+  }
+  __syncthreads();
+  float bestw[kWindowMaxCap];
+  float acc = 0.f;
+  const int c = cs + tid;
+#pragma unroll
+  for (int w = 1; w <= kWindowMaxCap; ++w) {
+    bestw[w - 1] = -INFINITY;
+    if (w <= wmax) {
+      acc += sums[tid + w - 1];
+      if (c + w <= nch) bestw[w - 1] = acc;
+    }
+  }
+  // block max per w: wave shuffles, then across the 4 waves
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int w = 0; w < kWindowMaxCap; ++w) {
+    float v = bestw[w];
+    for (int d = 32; d > 0; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
+    if (lane == 0) red[wave][w] = v;
+  }
+  __syncthreads();
+  if (tid < wmax) {
+    const float v = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+    if (v > -INFINITY) atomicMax(&best[nh * kWindowMaxCap + tid], ordered_bits(v));
+  }
+}
+
+// Resets best[] and (for packed input) builds the chunk / segment offset tables.
+__global__ void plan_tables_kernel(const int32_t* __restrict__ cu, int N, int seg_chunks,
+                                   int32_t* __restrict__ chunk_off, int32_t* __restrict__ seg_off,
+                                   uint32_t* __restrict__ best, int best_len) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < best_len; i += gridDim.x * blockDim.x)
+    best[i] = 0u;
+  if (cu && blockIdx.x == 0 && threadIdx.x == 0) {
+    int32_t acc = 0, sacc = 0;
+    chunk_off[0] = 0;
+    if (seg_off) seg_off[0] = 0;
+    for (int n = 0; n < N; ++n) {
+      const int nch = (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
+      acc += nch;
+      chunk_off[n + 1] = acc;
+      if (seg_off) {
+        sacc += max(1, (nch + seg_chunks - 1) / seg_chunks);  // empty sequences keep one unit
+        seg_off[n + 1] = sacc;
+      }
+    }
+  }
+}
+
+__global__ void gate_window_finalize_kernel(const uint32_t* __restrict__ best,
+                                            const int32_t* __restrict__ cu,
+                                            const int32_t* __restrict__ chunk_off, int64_t T,
+                                            int N, int H, int wmax, float thr,
+                                            int32_t* __restrict__ out) {
+  const int nh = blockIdx.x * blockDim.x + threadIdx.x;
+  if (nh >= N * H) return;
+  const SeqInfo si = seq_info(nh / H, cu, chunk_off, T);
+  out[nh] = window_of(best, nh, (si.len + kChunk - 1) / kChunk, wmax, thr);
+}
+
+hipError_t launch_plan_tables(const int32_t* cu, int N, int seg_chunks, int32_t* chunk_off,
+                              int32_t* seg_off, uint32_t* best, int best_len, hipStream_t s) {
+  const int blocks = best_len > 0 ? min(64, (best_len + 255) / 256) : 1;
+  plan_tables_kernel<<<blocks, 256, 0, s>>>(cu, N, seg_chunks, chunk_off, seg_off, best, best_len);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_scan(const Problem& p, int64_t max_chunks, int wmax, uint32_t* best,
+                            hipStream_t s) {
+  if (p.N == 0 || max_chunks == 0) return hipSuccess;
+  dim3 grid((unsigned)(p.N * p.H), (unsigned)((max_chunks + 255) / 256));
+  gate_window_max_kernel<<<grid, 256, 0, s>>>(p.g, p.cu, p.chunk_off, p.T, p.N, p.H, wmax, best);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_finalize(const Problem& p, const uint32_t* best, int wmax, float thr,
+                                int32_t* out, hipStream_t s) {
+  const int nh = p.N * p.H;
+  if (nh == 0) return hipSuccess;
+  gate_window_finalize_kernel<<<(nh + 255) / 256, 256, 0, s>>>(best, p.cu, p.chunk_off, p.T, p.N,
+                                                               p.H, wmax, thr, out);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

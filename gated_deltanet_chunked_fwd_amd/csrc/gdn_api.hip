@@ -1,5 +1,22 @@
-// C ABI of libgdn: argument validation, workspace carving and the launch
-// sequence.  Declarations and the full contract are in include/gdn.h.
+// C ABI of libgdn: argument validation, the split planner, workspace carving and
+// the launch sequence.  Declarations and the full contract are in include/gdn.h.
+//
+// Planner (FlashQLA talk transcript, tokendh.com, auto-CP section): the number of
+// splits per sequence is not fixed by the hardware the way inter-card parallelism
+// is; with L chunks per segment and N chunks per sequence the one-wave model is
+// T = lambda1 L + lambda2 N / L (the chunk-serial passes scale with L, the
+// recurrence over segments with N/L), minimised at L ~ sqrt(lambda2 N / lambda1);
+// splitting pays only when the grid does not fill the machine and the sequence is
+// long.  Here L is the larger of that optimum and the "fill" length: the chunk
+// steps per compute unit if all (sequence, head, column block) work were spread
+// evenly, L_fill = ceil(sum of chunks x heads x column blocks / CUs).  A split
+// happens only if the longest sequence holds more than 1.5 L chunks; an unsplit grid
+// that already keeps every CU busy for about as long as its longest sequence
+// has L_fill >= that length and stays unsplit, while one that is short of units
+// or unbalanced (packed sequences of very different lengths) gets its long
+// sequences cut.
+#include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstring>
@@ -10,11 +27,30 @@
 namespace {
 
 using gdn::kChunk;
+using gdn::kWindowMaxCap;
 
 constexpr size_t kAlign = 256;
-size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+constexpr float kLambda1Us = 1.0f;   // one chunk step of the fused kernel (MI355X)
+constexpr float kLambda2Us = 0.5f;   // one merge step
+constexpr int kMinSegmentChunks = 8;
+constexpr float kWindowMargin = 1e-3f;
 
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Compute units of the current device, queried once per device.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
 // Records the caller's timing events around one stage (no-op without events).
 struct StageMark {
@@ -33,13 +69,13 @@ struct StageMark {
 int validate_shape(const gdn_shape* s) {
   if (!s) return GDN_ERR_ARG;
   if (s->B < 1 || s->T < 0 || s->H < 1 || s->N < 0) return GDN_ERR_ARG;
-  if (s->T > INT_MAX / 2 || s->H > 65535) return GDN_ERR_ARG;
+  if (s->T > INT_MAX / 2 || s->H > 65535 || s->B * s->H > INT_MAX / 2) return GDN_ERR_ARG;
   if ((s->dk != 64 && s->dk != 128) || (s->dv != 64 && s->dv != 128)) return GDN_ERR_UNSUPPORTED;
   if ((s->qkv_dtype != GDN_BF16 && s->qkv_dtype != GDN_F32) ||
       (s->beta_dtype != GDN_BF16 && s->beta_dtype != GDN_F32))
     return GDN_ERR_UNSUPPORTED;
   if (s->cu_seqlens_host) {
-    if (s->B != 1 || s->N < 1) return GDN_ERR_ARG;
+    if (s->B != 1 || s->N < 1 || s->N * s->H > INT_MAX / 2) return GDN_ERR_ARG;
     const int32_t* cu = s->cu_seqlens_host;
     if (cu[0] != 0 || cu[s->N] != s->T) return GDN_ERR_ARG;
     for (int64_t n = 0; n < s->N; ++n)
@@ -50,38 +86,101 @@ int validate_shape(const gdn_shape* s) {
   return GDN_OK;
 }
 
-int64_t total_chunks(const gdn_shape* s) {
-  if (!s->cu_seqlens_host) return s->B * ((s->T + kChunk - 1) / kChunk);
-  int64_t c = 0;
-  for (int64_t n = 0; n < s->N; ++n)
-    c += (s->cu_seqlens_host[n + 1] - s->cu_seqlens_host[n] + kChunk - 1) / kChunk;
-  return c;
+int validate_opts(const gdn_opts* o) {
+  if (!o) return GDN_OK;
+  if (o->value_block != 0 && o->value_block != 64 && o->value_block != 128) return GDN_ERR_ARG;
+  if (o->force_segment_chunks < 0 || o->window_max_chunks < 0 ||
+      o->window_max_chunks > kWindowMaxCap)
+    return GDN_ERR_ARG;
+  if (!std::isfinite(o->window_log_eps) || o->window_log_eps > 0.f) return GDN_ERR_ARG;
+  if (!(o->lambda1_us >= 0.f) || !(o->lambda2_us >= 0.f)) return GDN_ERR_ARG;
+  return GDN_OK;
+}
+
+int64_t seq_chunks(const gdn_shape* s, int64_t n) {
+  const int64_t len = s->cu_seqlens_host ? s->cu_seqlens_host[n + 1] - s->cu_seqlens_host[n] : s->T;
+  return (len + kChunk - 1) / kChunk;
+}
+
+struct Plan {
+  int64_t total_chunks = 0, max_chunks = 0;
+  int seg_chunks = INT_MAX / 2;
+  bool split = false;
+  int64_t total_segs = 0;
+  int value_block = 128;
+  int wmax = kWindowMaxCap;
+  float log_eps = 0.f;
+};
+
+Plan make_plan(const gdn_shape* s, const gdn_opts* o) {
+  Plan P;
+  for (int64_t n = 0; n < s->N; ++n) {
+    const int64_t c = seq_chunks(s, n);
+    P.total_chunks += c;
+    P.max_chunks = std::max(P.max_chunks, c);
+  }
+  const int vb_req = o ? o->value_block : 0;
+  P.value_block = (s->qkv_dtype == GDN_BF16 && s->dv % 128 == 0 && vb_req != 64) ? 128 : 64;
+  P.wmax = (o && o->window_max_chunks > 0) ? o->window_max_chunks : kWindowMaxCap;
+  P.log_eps = (o && o->window_log_eps != 0.f) ? o->window_log_eps : (float)std::log(0x1p-24);
+  int64_t L = INT_MAX / 2;
+  if (!(o && o->no_split) && P.max_chunks > 1) {
+    if (o && o->force_segment_chunks > 0) {
+      L = o->force_segment_chunks;
+    } else {
+      const int64_t colblocks = s->dv / P.value_block;
+      const int64_t cus = device_cus();
+      const double l1 = (o && o->lambda1_us > 0.f) ? o->lambda1_us : kLambda1Us;
+      const double l2 = (o && o->lambda2_us > 0.f) ? o->lambda2_us : kLambda2Us;
+      const int64_t fill = (P.total_chunks * s->H * colblocks + cus - 1) / cus;
+      const int64_t opt = (int64_t)std::ceil(std::sqrt(l2 * (double)P.max_chunks / l1));
+      const int64_t cand = std::max<int64_t>({fill, opt, kMinSegmentChunks});
+      if (2 * P.max_chunks > 3 * cand) L = cand;
+    }
+  }
+  P.split = L < P.max_chunks;
+  P.seg_chunks = (int)std::min<int64_t>(L, INT_MAX / 2);
+  if (P.split) {
+    for (int64_t n = 0; n < s->N; ++n)  // an empty sequence still owns one unit (its final state)
+      P.total_segs += std::max<int64_t>(1, (seq_chunks(s, n) + L - 1) / L);
+  } else {
+    P.total_segs = s->N;
+  }
+  return P;
 }
 
 struct Layout {
-  size_t tmat = 0, chunk_off = 0, total = 0;
+  size_t tmat = 0, chunk_off = 0, seg_off = 0, best = 0, sstar = 0, mcorr = 0, hstart = 0;
+  size_t total = 0;
 };
 
-Layout layout(const gdn_shape* s) {
+Layout layout(const gdn_shape* s, const Plan& P) {
   Layout L;
   const size_t esz = s->qkv_dtype == GDN_BF16 ? 2 : 4;
   size_t off = 0;
-  L.tmat = off;
-  off += align_up((size_t)total_chunks(s) * (size_t)s->H * kChunk * kChunk * esz);
-  L.chunk_off = off;
-  off += align_up((size_t)(s->N + 1) * sizeof(int32_t));
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  L.tmat = take((size_t)P.total_chunks * s->H * kChunk * kChunk * esz);
+  L.chunk_off = take((size_t)(s->N + 1) * sizeof(int32_t));
+  L.seg_off = take((size_t)(s->N + 1) * sizeof(int32_t));
+  L.best = take((size_t)s->N * s->H * kWindowMaxCap * sizeof(uint32_t));
+  if (P.split) {
+    const size_t slots = (size_t)P.total_segs * s->H;
+    L.sstar = take(slots * s->dk * s->dv * sizeof(float));
+    L.mcorr = take(slots * s->dk * s->dk * sizeof(float));
+    L.hstart = take(slots * s->dk * s->dv * sizeof(float));
+  }
   L.total = off;
   return L;
 }
 
 gdn::Problem make_problem(const void* q, const void* k, const void* v, const float* g,
                           const void* beta, const float* h0, const int32_t* cu, float scale,
-                          void* o, float* hT, const gdn_shape* s) {
+                          void* o, float* hT, const gdn_shape* s, int64_t total_chunks) {
   gdn::Problem p;
   p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta; p.h0 = h0; p.cu = cu;
   p.chunk_off = nullptr; p.o = o; p.hT = hT;
   p.T = s->T;
-  p.total_chunks = total_chunks(s);
+  p.total_chunks = total_chunks;
   p.N = (int)s->N; p.H = (int)s->H; p.dk = (int)s->dk; p.dv = (int)s->dv;
   p.qkv_bf16 = s->qkv_dtype == GDN_BF16;
   p.beta_bf16 = s->beta_dtype == GDN_BF16;
@@ -107,15 +206,24 @@ extern "C" {
 int64_t gdn_total_chunks(const gdn_shape* shape) {
   int rc = validate_shape(shape);
   if (rc != GDN_OK) return rc;
-  return total_chunks(shape);
+  int64_t c = 0;
+  for (int64_t n = 0; n < shape->N; ++n) c += seq_chunks(shape, n);
+  return c;
+}
+
+int64_t gdn_plan_segment_chunks(const gdn_shape* shape, const gdn_opts* opts) {
+  int rc = validate_shape(shape);
+  if (rc == GDN_OK) rc = validate_opts(opts);
+  if (rc != GDN_OK) return rc;
+  return make_plan(shape, opts).seg_chunks;
 }
 
 int gdn_chunk_fwd_workspace_bytes(const gdn_shape* shape, const gdn_opts* opts, size_t* bytes) {
-  (void)opts;
   int rc = validate_shape(shape);
+  if (rc == GDN_OK) rc = validate_opts(opts);
   if (rc != GDN_OK) return rc;
   if (!bytes) return GDN_ERR_ARG;
-  *bytes = layout(shape).total;
+  *bytes = layout(shape, make_plan(shape, opts)).total;
   return GDN_OK;
 }
 
@@ -124,29 +232,34 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                   float* final_state, const gdn_shape* shape, const gdn_opts* opts,
                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int rc = validate_shape(shape);
-  if (rc != GDN_OK) return rc;
-  rc = check_inputs(k, g, beta, cu_seqlens, shape);
+  if (rc == GDN_OK) rc = validate_opts(opts);
+  if (rc == GDN_OK) rc = check_inputs(k, g, beta, cu_seqlens, shape);
   if (rc != GDN_OK) return rc;
   if (shape->T > 0 && (!q || !v || !o)) return GDN_ERR_ARG;
   if ((q && !aligned(q, 16)) || (v && !aligned(v, 16)) || (o && !aligned(o, 16)) ||
       (initial_state && !aligned(initial_state, 16)) || (final_state && !aligned(final_state, 16)))
     return GDN_ERR_ARG;
   if (!std::isfinite(scale)) return GDN_ERR_ARG;
-  if (opts && opts->value_block != 0 && opts->value_block != 64 && opts->value_block != 128)
-    return GDN_ERR_ARG;
-  const Layout L = layout(shape);
+  const Plan P = make_plan(shape, opts);
+  const Layout L = layout(shape, P);
   if (workspace_bytes < L.total || (L.total > 0 && !workspace) || !aligned(workspace, kAlign))
     return GDN_ERR_WORKSPACE;
 
   char* ws = static_cast<char*>(workspace);
   gdn::Problem p = make_problem(q, k, v, g, beta, initial_state, cu_seqlens, scale, o,
-                                final_state, shape);
-  if (cu_seqlens) {
-    p.chunk_off = reinterpret_cast<int32_t*>(ws + L.chunk_off);
-    if (gdn::launch_chunk_offsets(cu_seqlens, p.N, const_cast<int32_t*>(p.chunk_off), stream) !=
-        hipSuccess)
+                                final_state, shape, P.total_chunks);
+  int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + L.chunk_off);
+  int32_t* seg_off = reinterpret_cast<int32_t*>(ws + L.seg_off);
+  uint32_t* best = reinterpret_cast<uint32_t*>(ws + L.best);
+  const int best_len = P.split ? p.N * p.H * kWindowMaxCap : 0;
+  if (cu_seqlens || P.split) {
+    if (gdn::launch_plan_tables(cu_seqlens, p.N, P.seg_chunks, cu_seqlens ? chunk_off : nullptr,
+                                (cu_seqlens && P.split) ? seg_off : nullptr, best, best_len,
+                                stream) != hipSuccess)
       return GDN_ERR_HIP;
   }
+  if (cu_seqlens) p.chunk_off = chunk_off;
+
   void* tmat = ws + L.tmat;
   {
     StageMark mark(opts, GDN_STAGE_INVERSE, stream);
@@ -155,10 +268,36 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
 
   gdn::FwdPlan plan;
   plan.Tmat = tmat;
-  plan.seg_chunks = INT_MAX / 2;
-  plan.seg_off = nullptr;
-  plan.units = (int64_t)p.N * p.H;
-  plan.value_block = opts ? opts->value_block : 0;
+  plan.seg_chunks = P.seg_chunks;
+  plan.seg_off = (cu_seqlens && P.split) ? seg_off : nullptr;
+  plan.units = P.total_segs * p.H;
+  plan.value_block = P.value_block;
+  plan.mode = gdn::kPass3;
+  plan.cp = gdn::CpBuffers{};
+  if (P.split) {
+    plan.cp.best = best;
+    plan.cp.wmax = P.wmax;
+    plan.cp.thr = P.log_eps - kWindowMargin;
+    plan.cp.force_correction = opts ? opts->force_correction : 0;
+    plan.cp.sstar = reinterpret_cast<float*>(ws + L.sstar);
+    plan.cp.mcorr = reinterpret_cast<float*>(ws + L.mcorr);
+    plan.cp.hstart = reinterpret_cast<float*>(ws + L.hstart);
+    if (!plan.cp.force_correction) {
+      StageMark mark(opts, GDN_STAGE_GATE_SCAN, stream);
+      if (gdn::launch_gate_scan(p, P.max_chunks, P.wmax, best, stream) != hipSuccess)
+        return GDN_ERR_HIP;
+    }
+    {
+      StageMark mark(opts, GDN_STAGE_CP_PASS1, stream);
+      gdn::FwdPlan p1 = plan;
+      p1.mode = gdn::kPass1;
+      if (gdn::launch_fused_forward(p, p1, stream) != hipSuccess) return GDN_ERR_HIP;
+    }
+    {
+      StageMark mark(opts, GDN_STAGE_CP_MERGE, stream);
+      if (gdn::launch_cp_merge(p, plan, stream) != hipSuccess) return GDN_ERR_HIP;
+    }
+  }
   {
     StageMark mark(opts, GDN_STAGE_FORWARD, stream);
     if (gdn::launch_fused_forward(p, plan, stream) != hipSuccess) return GDN_ERR_HIP;
@@ -173,10 +312,10 @@ int gdn_chunk_inverse(const void* k, const float* g, const void* beta, const int
   if (rc != GDN_OK) return rc;
   rc = check_inputs(k, g, beta, cu_seqlens, shape);
   if (rc != GDN_OK) return rc;
-  const int64_t nch = total_chunks(shape);
+  const int64_t nch = gdn_total_chunks(shape);
   if (nch > 0 && (!t_out || !aligned(t_out, 16))) return GDN_ERR_ARG;
   gdn::Problem p = make_problem(nullptr, k, nullptr, g, beta, nullptr, cu_seqlens, 1.f, nullptr,
-                                nullptr, shape);
+                                nullptr, shape, nch);
   if (cu_seqlens) {
     const size_t need = align_up((size_t)(shape->N + 1) * sizeof(int32_t));
     if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)) return GDN_ERR_WORKSPACE;
@@ -186,6 +325,45 @@ int gdn_chunk_inverse(const void* k, const float* g, const void* beta, const int
       return GDN_ERR_HIP;
   }
   if (gdn::launch_chunk_inverse(p, t_out, stream) != hipSuccess) return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
+int gdn_gate_scan_workspace_bytes(const gdn_shape* shape, size_t* bytes) {
+  int rc = validate_shape(shape);
+  if (rc != GDN_OK) return rc;
+  if (!bytes) return GDN_ERR_ARG;
+  *bytes = align_up((size_t)(shape->N + 1) * sizeof(int32_t)) +
+           align_up((size_t)shape->N * shape->H * kWindowMaxCap * sizeof(uint32_t));
+  return GDN_OK;
+}
+
+int gdn_gate_scan(const float* g, const int32_t* cu_seqlens, const gdn_shape* shape,
+                  const gdn_opts* opts, int32_t* window_out, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  int rc = validate_shape(shape);
+  if (rc == GDN_OK) rc = validate_opts(opts);
+  if (rc != GDN_OK) return rc;
+  if ((cu_seqlens == nullptr) != (shape->cu_seqlens_host == nullptr)) return GDN_ERR_ARG;
+  if ((shape->T > 0 && !g) || (g && !aligned(g, 4)) || !window_out || !aligned(window_out, 4))
+    return GDN_ERR_ARG;
+  size_t need = 0;
+  gdn_gate_scan_workspace_bytes(shape, &need);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)) return GDN_ERR_WORKSPACE;
+  const Plan P = make_plan(shape, opts);
+  int32_t* chunk_off = static_cast<int32_t*>(workspace);
+  uint32_t* best = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
+                                               align_up((size_t)(shape->N + 1) * sizeof(int32_t)));
+  gdn::Problem p = make_problem(nullptr, nullptr, nullptr, g, nullptr, nullptr, cu_seqlens, 1.f,
+                                nullptr, nullptr, shape, P.total_chunks);
+  const int best_len = p.N * p.H * kWindowMaxCap;
+  if (gdn::launch_plan_tables(cu_seqlens, p.N, 1, cu_seqlens ? chunk_off : nullptr, nullptr, best,
+                              best_len, stream) != hipSuccess)
+    return GDN_ERR_HIP;
+  if (cu_seqlens) p.chunk_off = chunk_off;
+  if (gdn::launch_gate_scan(p, P.max_chunks, P.wmax, best, stream) != hipSuccess) return GDN_ERR_HIP;
+  if (gdn::launch_gate_finalize(p, best, P.wmax, P.log_eps - kWindowMargin, window_out, stream) !=
+      hipSuccess)
+    return GDN_ERR_HIP;
   return GDN_OK;
 }
 

@@ -195,6 +195,28 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
   return x;
 }
 
+// Order-preserving float <-> uint encoding (for atomic max of floats); 0 is
+// below every encoded float and marks "unset".
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float from_ordered_bits(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+// Smallest admissible lookback window (chunks) of (sequence, head) nh from the
+// gate-scan maxima; 0 if none.
+__device__ __forceinline__ int window_of(const uint32_t* best, int nh, int nch, int wmax,
+                                         float thr) {
+  const int lim = min(wmax, nch);
+  for (int w = 1; w <= lim; ++w) {
+    const uint32_t u = best[nh * kWindowMaxCap + (w - 1)];
+    if (u != 0u && from_ordered_bits(u) <= thr) return w;
+  }
+  return 0;
+}
+
 // Sequence n's token range and first global chunk.
 struct SeqInfo {
   int64_t tok0;    // first token (flattened over B*T)

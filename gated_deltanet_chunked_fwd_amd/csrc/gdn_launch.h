@@ -26,17 +26,46 @@ struct Problem {
   float scale;
 };
 
+constexpr int kWindowMaxCap = 16;  // longest lookback window the gate scan can return
+
+// Sequence-split state shared by the split passes (all null when no split).
+struct CpBuffers {
+  const uint32_t* best;     // [N*H][kWindowMaxCap] gate-scan maxima (order-preserving bits)
+  int wmax;                 // longest admissible window (chunks)
+  float thr;                // window threshold: log_eps - margin
+  int force_correction;     // 1: every split head uses the wrong-start correction
+  float* sstar;             // [total_segs, H, dk, dv] wrong-start (zero-start) segment end states
+  float* mcorr;             // [total_segs, H, dk, dk] segment transition matrices
+  float* hstart;            // [total_segs, H, dk, dv] true segment start states
+};
+
 // Work description for one launch of the fused forward kernel.  A work unit is
-// (sequence, head, segment); the kernel grid is (dv / BV, units).
+// (sequence, head, segment); the kernel grid is (units, column blocks).
+//   kPass3: steps 2-4 with O; a segment starts from h0 (first segment), from a
+//           zero state a window of chunks earlier (window heads) or from hstart
+//           (correction heads); the last segment writes the final state.
+//   kPass1: correction heads only, all but the last segment: run the segment from
+//           a zero state (value columns -> sstar) and, with V = 0, from the
+//           identity (extra dk columns -> mcorr); no O.
+enum { kPass3 = 0, kPass1 = 1 };
 struct FwdPlan {
   const void* Tmat;          // chunk inverses [total_chunks, H, 64, 64]
   int seg_chunks;            // chunks per segment (>= max chunks of any sequence: one segment)
   const int32_t* seg_off;    // device [N+1] segment offsets (packed + split) or null
   int64_t units;             // number of (sequence, head, segment) units
   int value_block;           // value columns per workgroup: 64, 128, or 0 (widest that fits)
+  int mode;                  // kPass3 or kPass1
+  CpBuffers cp;
 };
 
 hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hipStream_t s);
+hipError_t launch_plan_tables(const int32_t* cu, int N, int seg_chunks, int32_t* chunk_off,
+                              int32_t* seg_off, uint32_t* best, int best_len, hipStream_t s);
+hipError_t launch_gate_scan(const Problem& p, int64_t max_chunks, int wmax, uint32_t* best,
+                            hipStream_t s);
+hipError_t launch_gate_finalize(const Problem& p, const uint32_t* best, int wmax, float thr,
+                                int32_t* out, hipStream_t s);
+hipError_t launch_cp_merge(const Problem& p, const FwdPlan& plan, hipStream_t s);
 hipError_t launch_chunk_inverse(const Problem& p, void* t_out, hipStream_t s);
 hipError_t launch_fused_forward(const Problem& p, const FwdPlan& plan, hipStream_t s);
 

@@ -68,18 +68,17 @@ typedef struct gdn_shape {
 
 /* Planner options.  A zeroed struct (or NULL) selects the defaults. */
 typedef struct gdn_opts {
-  /* 0: one pass per (sequence, head) -- bitwise reproducible run to run and
-   *    independent of the planner.
-   * 1 (default when opts == NULL): the planner may split long sequences into
-   *    segments that run in parallel (the pages' automatic intra-card split).
-   *    Results then match the no-split path within rounding, not bitwise. */
-  int32_t auto_cp;
-  int32_t force_segment_chunks; /* >0: force this segment length in chunks (tests) */
-  int32_t force_start_mode;     /* 0: gate scan decides per (seq, head); 1: window starts
-                                   where the scan allows, else correction; 2: correction
-                                   (wrong-start state + matrix M) for every split head */
+  /* 1: never split a sequence: one chunk-serial pass per (sequence, head), bitwise
+   *    reproducible run to run and independent of the planner.
+   * 0 (default): the planner may cut long sequences into segments that run in
+   *    parallel (the pages' automatic intra-card sequence parallelism); results
+   *    then match the unsplit path within rounding, not bitwise. */
+  int32_t no_split;
+  int32_t force_segment_chunks; /* >0: split into segments of this many chunks; 0: planner */
+  int32_t force_correction;     /* 1: every split head uses the wrong-start correction
+                                   (S*, M and the merge) instead of window-lookback starts */
   float window_log_eps;         /* log of the window tolerance; 0 -> log(2^-24) */
-  int32_t window_max_chunks;    /* longest lookback window in chunks; 0 -> 16 */
+  int32_t window_max_chunks;    /* longest lookback window in chunks, 1..16; 0 -> 16 */
   float lambda1_us;             /* planner: cost of one chunk step; 0 -> built in */
   float lambda2_us;             /* planner: cost of one merge step; 0 -> built in */
   int32_t value_block;          /* value columns per workgroup of the fused kernel: 64 or
@@ -146,6 +145,28 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
 int gdn_chunk_inverse(const void* k, const float* g, const void* beta,
                       const int32_t* cu_seqlens, const gdn_shape* shape, void* t_out,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The gate scan alone (sliding-window section: a light kernel scans each head's
+ * gates to find the heads whose decay allows window-lookback starts).  For every
+ * (sequence n, head h) it writes the smallest W in 1..window_max_chunks such that
+ * every run of W consecutive chunks of that sequence (partial last chunk: its real
+ * tokens) has a gate sum <= window_log_eps - 1e-3, sums formed in fp32; or 0 if
+ * no such W exists.  Starting a segment from a zero state W chunks early then
+ * changes the state by at most exp(window_log_eps) times its norm (unit keys,
+ * beta in [0,1]).
+ *   window_out  device, [N, H] int32
+ *   workspace   device scratch of at least gdn_gate_scan_workspace_bytes()
+ * Other arguments as in gdn_chunk_fwd.
+ */
+int gdn_gate_scan(const float* g, const int32_t* cu_seqlens, const gdn_shape* shape,
+                  const gdn_opts* opts, int32_t* window_out, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream);
+int gdn_gate_scan_workspace_bytes(const gdn_shape* shape, size_t* bytes);
+
+/* Segment length (chunks) the planner picks for gdn_chunk_fwd, or a negative status;
+ * a value >= the longest sequence's chunk count means no sequence is split. */
+int64_t gdn_plan_segment_chunks(const gdn_shape* shape, const gdn_opts* opts);
 
 /* Total number of chunks (sum over sequences of ceil(len/64)), or a negative status. */
 int64_t gdn_total_chunks(const gdn_shape* shape);

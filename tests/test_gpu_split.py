@@ -1,0 +1,112 @@
+"""GPU parity of the sequence-split paths (gate scan, wrong-start correction with
+merge, window-lookback starts) against the fp64 token-recurrence oracle, and
+stage parity of the gate scan against its brute-force reference."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_chunked_fwd_amd import binding, synth
+from oracle import gate
+from tests.gpu_util import TOL, assert_parity, compare_pairs, run_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def spec(**kw):
+    base = dict(name="split", B=1, T=64 * 14 + 23, H=3, dk=128, dv=128, dtype="bf16", seed=0,
+                zero_gate_heads=(1,))
+    base.update(kw)
+    return synth.Spec(**base)
+
+
+@pytest.mark.parametrize("seg", [1, 2, 3, 7])
+@pytest.mark.parametrize("corr", [0, 1])
+def test_split_parity_forced_segments(seg, corr):
+    """Head 1 has g = 0 (correction path); heads 0 and 2 decay (window path unless
+    the correction is forced).  Any segment count must give the unsplit result."""
+    inp = synth.generate(spec(seed=60 + seg, h0_std=0.05))
+    o, hT = run_gpu(inp, opts=binding.make_opts(force_segment_chunks=seg, force_correction=corr))
+    assert_parity(compare_pairs(inp, o, hT), TOL["bf16"], "seg=%d corr=%d" % (seg, corr))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_split_parity_small_heads(dtype):
+    inp = synth.generate(spec(B=2, T=64 * 9 + 5, H=2, dk=64, dv=64, dtype=dtype, seed=71,
+                              zero_gate_heads=(0,), h0_std=0.1))
+    for corr in (0, 1):
+        o, hT = run_gpu(inp, opts=binding.make_opts(force_segment_chunks=2, force_correction=corr))
+        assert_parity(compare_pairs(inp, o, hT), TOL[dtype], "%s corr=%d" % (dtype, corr))
+
+
+def _packed(lengths, H, seed, dk=128, dv=128, zero_heads=(1,)):
+    T = int(sum(lengths))
+    inp = synth.generate(spec(B=1, T=T, H=H, dk=dk, dv=dv, seed=seed, zero_gate_heads=zero_heads))
+    inp["cu_seqlens"] = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
+    inp["N"] = len(lengths)
+    g = torch.Generator().manual_seed(seed)
+    inp["h0"] = (torch.randn(len(lengths), H, dk, dv, generator=g) * 0.03).float()
+    return inp
+
+
+@pytest.mark.parametrize("corr", [0, 1])
+def test_split_parity_packed(corr):
+    inp = _packed([64 * 9 + 7, 40, 0, 64 * 3, 64 * 6 + 1, 0], H=2, seed=72)
+    o, hT = run_gpu(inp, opts=binding.make_opts(force_segment_chunks=2, force_correction=corr))
+    assert_parity(compare_pairs(inp, o, hT), TOL["bf16"], "packed corr=%d" % corr)
+
+
+def test_split_value_block_64_and_dk64_dv128():
+    inp = synth.generate(spec(B=1, T=64 * 8, H=2, dk=64, dv=128, seed=73, zero_gate_heads=(0,)))
+    for vb in (64, 128):
+        o, hT = run_gpu(inp, opts=binding.make_opts(force_segment_chunks=3, value_block=vb))
+        assert_parity(compare_pairs(inp, o, hT), TOL["bf16"], "dk64 dv128 vb=%d" % vb)
+
+
+def test_planner_default_split_parity():
+    """A shape the planner splits by default (few heads, long sequence)."""
+    inp = synth.generate(spec(B=1, T=64 * 48, H=2, seed=74, zero_gate_heads=(1,)))
+    d = to_dev(inp)
+    L = binding.plan_segment_chunks(d["q"], d["v"], d["beta"])
+    assert L < 48, L
+    o, hT = run_gpu(inp)
+    assert_parity(compare_pairs(inp, o, hT), TOL["bf16"], "planner L=%d" % L)
+
+
+@pytest.mark.parametrize("kind", ["sigmoid", "uniform", "mixed", "packed"])
+def test_gate_scan_stage(kind):
+    """GPU window decision vs the fp64 brute force: the GPU's W must be admissible in
+    fp64 (every W-run sums to <= log eps) and minimal up to the 1e-3 margin band."""
+    if kind == "packed":
+        inp = _packed([64 * 30 + 5, 64 * 3, 17, 64 * 12], H=3, seed=81, zero_heads=(2,))
+    else:
+        gk = {"sigmoid": "sigmoid", "uniform": "uniform", "mixed": "sigmoid"}[kind]
+        inp = synth.generate(spec(B=2, T=64 * 40 + 9, H=4, gate=gk, seed=82,
+                                  zero_gate_heads=(3,) if kind == "mixed" else ()))
+    d = to_dev(inp)
+    win = binding.gate_scan(d["g"], d["cu_seqlens"], inp.get("cu_seqlens")).cpu().numpy()
+    g64 = synth.as_f64(inp["g"])
+    le = math.log(2.0 ** -24)
+    B, T, H = g64.shape
+    cu = (inp["cu_seqlens"].numpy() if inp.get("cu_seqlens") is not None
+          else np.arange(B + 1) * T)
+    gf = g64.reshape(-1, H)
+    checked = 0
+    for n in range(len(cu) - 1):
+        for h in range(H):
+            gs = gf[cu[n]:cu[n + 1], h]
+            sums = gate.chunk_sums(gs)
+            W = int(win[n, h])
+            if W > 0:
+                assert gate.max_window_sum(sums, W) <= le, (n, h, W)
+                if W > 1:
+                    assert gate.max_window_sum(sums, W - 1) > le - 2e-3, (n, h, W)
+            else:
+                for w in range(1, min(16, len(sums)) + 1):
+                    assert gate.max_window_sum(sums, w) > le - 2e-3, (n, h, w)
+            ref = gate.window_chunks(gs, log_eps=le - 1e-3)
+            assert W == ref or abs(gate.max_window_sum(sums, max(W, ref)) - (le - 1e-3)) < 1e-3
+            checked += 1
+    print("gate scan windows:", win.tolist())
+    assert checked > 0
