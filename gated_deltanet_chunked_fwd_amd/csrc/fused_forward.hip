@@ -14,8 +14,8 @@
 //   O  = scale (diag(gamma) Q h + ((Q K^T) * Gamma) U)
 //   h <- gamma_last h + K^T (diag(d) U)
 //
-// Mapping.  256 threads = 4 waves; each wave owns NCW value columns of h for
-// all dk rows, as 16x16 fp32 accumulator tiles in "tile order" (gdn_device.h),
+// Mapping.  4 or 8 waves (two per SIMD with 8); each wave owns NCW = 16 value
+// columns of h for all dk rows, as 16x16 fp32 accumulator tiles in "tile order" (gdn_device.h),
 // so h, V' and U feed the next MFMA straight from registers.  Per chunk the
 // workgroup stages K, Q, T, the gates and its V columns in LDS (the global loads
 // of chunk c+1 are issued before chunk c is computed), computes P = (QK^T)*Gamma
@@ -24,22 +24,29 @@
 // tiles through LDS transpose reads; O is staged column-major per wave and
 // stored with 16-byte row writes.  Value columns are independent; only T and P
 // are shared between them.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
 namespace gdn {
 
-template <typename E, int DK, int NCW>
+template <typename E, int DK, int NCW, int NW>
 struct FwdCfg {
-  static constexpr int NWAVES = 4;
+  static constexpr int NWAVES = NW;         // waves per workgroup (4 or 8)
+  static constexpr int NT = 64 * NW;        // threads per workgroup
   static constexpr int BV = NWAVES * NCW;   // value columns per workgroup
   static constexpr int NCT = NCW / 16;      // column tiles per wave
   static constexpr int NKT = DK / 16;       // dk tiles of the state
   static constexpr int NKS = DK / 32;       // contraction steps over dk
-  static constexpr int PAD = sizeof(E) == 2 ? 8 : 4;
-  static constexpr int KS = DK + PAD;       // row stride of sK, sQ
-  static constexpr int CS = kChunk + PAD;   // row stride of sT, sP, sO
-  static constexpr int VS = BV + PAD;       // row stride of sV
+  static constexpr bool BF = sizeof(E) == 2;
+  // Row strides (elements).  bf16 tiles that feed fragment reads are stored in tile
+  // order with a stride of 8 (mod 32) dwords: 16-byte fragment reads and 8-byte
+  // transpose reads are then free of bank conflicts on gfx950's LDS.
+  static constexpr int KS = BF ? DK + 16 : DK + 4;        // sK, sQ
+  static constexpr int CS = BF ? kChunk + 16 : kChunk + 4; // sT, sP, sKt, sO
+  static constexpr int VS = BF ? BV + 16 : BV + 4;        // sV
+  static constexpr bool KT_COPY = BF;  // stage K^T once per chunk instead of per wave
 };
 
 // One chunk's inputs held in registers between the global loads and the LDS
@@ -47,43 +54,65 @@ struct FwdCfg {
 // Nothing touches the loaded registers until store(): masking of rows past the
 // chunk end (zero there; beta = g = 0) and the beta conversion happen at store
 // time, so no wait for the loads is forced before the chunk's compute.
-template <typename E, int DK, int BV>
+template <typename E, int DK, int BV, int NTH>
 struct ChunkRegs {
   static constexpr int EPV = 16 / (int)sizeof(E);
   static constexpr int VPRK = DK / EPV, VPRV = BV / EPV, VPRT = kChunk / EPV;
-  static constexpr int NK = kChunk * VPRK / 256, NV = kChunk * VPRV / 256, NT = kChunk * VPRT / 256;
+  static constexpr int NK = kChunk * VPRK / NTH, NV = kChunk * VPRV / NTH, NT = kChunk * VPRT / NTH;
+  static_assert(NK * NTH == kChunk * VPRK && NV * NTH == kChunk * VPRV && NT * NTH == kChunk * VPRT,
+                "chunk tiles must split evenly over the threads");
   u32x4 k[NK], q[NK], v[NV], t[NT];
   float g;
   uint32_t b;   // raw beta bits (bf16 in the low half, or fp32)
   int len;
 
-  // qb/kb/vb point at the chunk's first token (head and column offsets applied);
-  // row_* are element strides between consecutive tokens.
+  // Per-thread element offsets inside a full chunk (fixed for the whole walk).
+  struct Offsets {
+    int k[NK], v[NV], g;
+    __device__ __forceinline__ void init(int row_qk, int row_v, int row_g, int tid) {
+#pragma unroll
+      for (int j = 0; j < NK; ++j) {
+        const int i = tid + NTH * j;
+        k[j] = (i / VPRK) * row_qk + (i % VPRK) * EPV;
+      }
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int i = tid + NTH * j;
+        v[j] = (i / VPRV) * row_v + (i % VPRV) * EPV;
+      }
+      g = (tid & (kChunk - 1)) * row_g;
+    }
+  };
+
+  // qb/kb/vb/gb/betab point at the chunk's first token (head and column offsets
+  // applied); rows past the chunk end read the chunk's first row instead (masked
+  // to zero in store()).
   __device__ __forceinline__ void load(const E* qb, const E* kb, const E* vb, const E* ts,
                                        const float* gb, const void* betab, bool beta_bf16,
-                                       int len_, int row_qk, int row_v, int row_g, bool vzero,
-                                       int tid) {
+                                       int len_, const Offsets& of, bool vzero, int tid) {
     len = len_;
+    const bool full = len == kChunk;
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
-      const int i = tid + 256 * j, r = i / VPRK, cv = i % VPRK;
-      const int off = min(r, len - 1) * row_qk + cv * EPV;
-      k[j] = *reinterpret_cast<const u32x4*>(kb + off);
-      q[j] = *reinterpret_cast<const u32x4*>(qb + off);
+      const int r = (tid + NTH * j) / VPRK;
+      const int o = (full || r < len) ? of.k[j] : (tid + NTH * j) % VPRK * EPV;
+      k[j] = *reinterpret_cast<const u32x4*>(kb + o);
+      q[j] = *reinterpret_cast<const u32x4*>(qb + o);
     }
     if (!vzero) {
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const int i = tid + 256 * j, r = i / VPRV, cv = i % VPRV;
-        v[j] = *reinterpret_cast<const u32x4*>(vb + min(r, len - 1) * row_v + cv * EPV);
+        const int r = (tid + NTH * j) / VPRV;
+        const int o = (full || r < len) ? of.v[j] : (tid + NTH * j) % VPRV * EPV;
+        v[j] = *reinterpret_cast<const u32x4*>(vb + o);
       }
     }
 #pragma unroll
-    for (int j = 0; j < NT; ++j) t[j] = reinterpret_cast<const u32x4*>(ts)[tid + 256 * j];
-    const int o = min(tid & (kChunk - 1), len - 1) * row_g;
-    g = gb[o];
-    if (beta_bf16) b = reinterpret_cast<const uint16_t*>(betab)[o];
-    else b = reinterpret_cast<const uint32_t*>(betab)[o];
+    for (int j = 0; j < NT; ++j) t[j] = reinterpret_cast<const u32x4*>(ts)[tid + NTH * j];
+    const int og = (full || (tid & (kChunk - 1)) < len) ? of.g : 0;
+    g = gb[og];
+    if (beta_bf16) b = reinterpret_cast<const uint16_t*>(betab)[og];
+    else b = reinterpret_cast<const uint32_t*>(betab)[og];
   }
 
   template <int KS, int CS, int VS>
@@ -92,20 +121,21 @@ struct ChunkRegs {
     const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
-      const int i = tid + 256 * j, r = i / VPRK, cv = i % VPRK;
+      const int i = tid + NTH * j, r = i / VPRK, cv = i % VPRK;
       const bool ok = r < len;
-      *reinterpret_cast<u32x4*>(sK + r * KS + cv * EPV) = ok ? k[j] : zero;
-      *reinterpret_cast<u32x4*>(sQ + r * KS + cv * EPV) = ok ? q[j] : zero;
+      const int lr = tord(r);
+      *reinterpret_cast<u32x4*>(sK + lr * KS + cv * EPV) = ok ? k[j] : zero;
+      *reinterpret_cast<u32x4*>(sQ + lr * KS + cv * EPV) = ok ? q[j] : zero;
     }
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int i = tid + 256 * j, r = i / VPRV, cv = i % VPRV;
+      const int i = tid + NTH * j, r = i / VPRV, cv = i % VPRV;
       *reinterpret_cast<u32x4*>(sV + r * VS + cv * EPV) = (r < len && !vzero) ? v[j] : zero;
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const int i = tid + 256 * j, r = i / VPRT, cv = i % VPRT;
-      *reinterpret_cast<u32x4*>(sT + r * CS + cv * EPV) = t[j];
+      const int i = tid + NTH * j, r = i / VPRT, cv = i % VPRT;
+      *reinterpret_cast<u32x4*>(sT + tord(r) * CS + cv * EPV) = t[j];
     }
     if (tid < kChunk) {
       const bool ok = tid < len;
@@ -116,33 +146,32 @@ struct ChunkRegs {
   }
 };
 
-// P tiles (query tile, key tile) computed by each wave; -1 = none.  The ten
-// lower-triangular 16x16 tiles are split 3/3/2/2; tiles (0,1) and (2,3) lie
-// inside the contraction range of the P U product and are written as zeros
-// (by waves 2 and 3).
-__constant__ int kPTiles[4][3][2] = {
-    {{3, 0}, {3, 1}, {3, 2}},
-    {{3, 3}, {2, 0}, {2, 1}},
-    {{2, 2}, {1, 0}, {-1, -1}},
-    {{1, 1}, {0, 0}, {-1, -1}},
-};
+// P tile pairs (query tile, key tile) in tile order: tiles 0 and 1 hold rows
+// 0..31 interleaved, tiles 2 and 3 rows 32..63, so the twelve pairs with some
+// key <= query are (0|1, 0|1) and (2|3, 0..3), dealt round-robin to the waves.
+__device__ __forceinline__ void p_pair(int i, int& qt, int& kt) {
+  if (i < 4) { qt = i >> 1; kt = i & 1; }
+  else { qt = 2 + ((i - 4) >> 2); kt = (i - 4) & 3; }
+}
 
-template <typename E, int DK, int NCW>
-__global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan plan) {
-  using Cfg = FwdCfg<E, DK, NCW>;
+template <typename E, int DK, int NCW, int NW>
+__global__ __launch_bounds__(64 * NW) void fused_forward_kernel(Problem p, FwdPlan plan) {
+  using Cfg = FwdCfg<E, DK, NCW, NW>;
   using M = Mma<E>;
   using frag = typename M::frag;
   constexpr int BV = Cfg::BV, NCT = Cfg::NCT, NKT = Cfg::NKT, NKS = Cfg::NKS;
   constexpr int KS = Cfg::KS, CS = Cfg::CS, VS = Cfg::VS;
 
-  __shared__ __align__(16) E sK[kChunk * KS];
-  __shared__ __align__(16) E sQ[kChunk * KS];
-  __shared__ __align__(16) E sT[kChunk * CS];
-  __shared__ __align__(16) E sP[kChunk * CS];
-  __shared__ __align__(16) E sV[kChunk * VS];
-  __shared__ __align__(16) E sO[4][NCW * CS];     // per wave, column-major [col][row]
+  constexpr bool KT_COPY = Cfg::KT_COPY;
+  __shared__ __align__(16) E sK[kChunk * KS];     // tile-order rows
+  __shared__ __align__(16) E sQ[kChunk * KS];     // tile-order rows
+  __shared__ __align__(16) E sKt[KT_COPY ? DK * CS : 8];  // K^T, tile-order dk rows
+  __shared__ __align__(16) E sT[kChunk * CS];     // tile-order rows
+  __shared__ __align__(16) E sP[kChunk * CS];     // tile-order query rows, natural keys
+  __shared__ __align__(16) E sV[kChunk * VS];     // natural rows
+  __shared__ __align__(16) E sO[NW][NCW * CS];    // per wave, column-major [col][row]
   __shared__ __align__(16) float sGraw[kChunk], sBraw[kChunk];
-  __shared__ __align__(16) float sGam[kChunk], sDec[kChunk], sBet[kChunk];
+  __shared__ __align__(16) float sGam[kChunk], sGamS[kChunk], sDec[kChunk], sBet[kChunk];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar table reads
@@ -223,84 +252,72 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
         }
   }
 
-  using Stage = ChunkRegs<E, DK, BV>;
+  using Stage = ChunkRegs<E, DK, BV, Cfg::NT>;
   Stage pf;
+  typename Stage::Offsets offs;
+  offs.init(row_qk, row_v, H, tid);
   auto issue_loads = [&](int c) {
     const int64_t t0 = (int64_t)c * kChunk;
     const E* ts = Tm + ((si.chunk0 + c) * H + h) * (int64_t)(kChunk * kChunk);
     pf.load(Qb + t0 * row_qk, Kb + t0 * row_qk, Vb + t0 * row_v, ts, Gb + t0 * H,
-            Bb + t0 * H * bsz, p.beta_bf16, min(kChunk, si.len - c * kChunk), row_qk, row_v, H,
-            mcols, tid);
+            Bb + t0 * H * bsz, p.beta_bf16, min(kChunk, si.len - c * kChunk), offs, mcols, tid);
   };
   if (c_start < c_end) issue_loads(c_start);
 
-  for (int c = c_start; c < c_end; ++c) {
-    const int len = min(kChunk, si.len - c * kChunk);
-    const bool emit = c >= c_out;   // uniform: lookback and pass-1 chunks write no O
+  // per-row gates in tile order: rows prow(u, 4q) .. +3 are consecutive, one 16-byte read
+  auto rows4 = [&](const float* v, int u) {
+    return *reinterpret_cast<const f32x4*>(v + prow(u, 4 * q));
+  };
 
-    // ---- stage chunk c in LDS, then start the loads of chunk c+1
-    pf.template store<KS, CS, VS>(sK, sQ, sV, sT, sGraw, sBraw, p.beta_bf16, mcols, tid);
-    __syncthreads();
-    if (c + 1 < c_end) issue_loads(c + 1);
-
-    // ---- gates: every wave scans (lane = chunk row); wave 0 publishes per-row values
-    const float G = wave_inclusive_scan(sGraw[lane]);
-    const float Glast = __shfl(G, 63, 64);
-    const float gC = fast_exp(Glast);
-    if (wave == 0) {
-      sGam[lane] = fast_exp(G);
-      sDec[lane] = fast_exp(Glast - G);
-      sBet[lane] = sBraw[lane];
-    }
-    // ---- P = (Q K^T) * Gamma as row-major [query][key]; computed as P^T = K Q^T so a
-    //      lane holds four consecutive keys of one query row
+  // One chunk after staging; EMIT (compile-time) selects whether O is produced, so
+  // each variant is straight-line code.
+  auto step = [&](auto emit_tag, int c, int len, float G, float gC) {
+    constexpr bool EMIT = decltype(emit_tag)::value;
+    // ---- P = scale (Q K^T) * Gamma: rows = queries in tile order, columns = keys in
+    //      natural order; computed as P^T = K Q^T so a lane holds four consecutive keys
+    if constexpr (EMIT) {
 #pragma unroll
-    for (int pt = 0; pt < 3; ++pt) {
-      if (!emit) break;
-      const int qt = kPTiles[wave][pt][0], kt = kPTiles[wave][pt][1];
-      if (qt >= 0) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int pt = 0; pt < (12 + NW - 1) / NW; ++pt) {
+        const int pi = wave + NW * pt;
+        if (pi < 12) {
+          int qt, kt;
+          p_pair(pi, qt, kt);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < NKS; ++s)
-          acc = M::run(lds_frag(sK, KS, 16 * kt + r16, 32 * s, q),
-                       lds_frag(sQ, KS, 16 * qt + r16, 32 * s, q), acc);
-        const int qrow = 16 * qt + r16;
-        const float Gq = __shfl(G, qrow, 64);
-        E* dst = sP + qrow * CS + 16 * kt + 4 * q;
+          for (int s = 0; s < NKS; ++s)
+            acc = M::run(lds_frag(sK, KS, 16 * kt + r16, 32 * s, q),
+                         lds_frag(sQ, KS, 16 * qt + r16, 32 * s, q), acc);
+          const int qrow = prow(qt, r16), key0 = prow(kt, 4 * q);
+          const float Gq = __shfl(G, qrow, 64);
+          E* dst = sP + (16 * qt + r16) * CS + key0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = 16 * kt + 4 * q + i;
-          const float Gk = __shfl(G, key, 64);
-          dst[i] = from_f32<E>(key <= qrow ? acc[i] * fast_exp(Gq - Gk) : 0.f);
+          for (int i = 0; i < 4; ++i) {
+            const float Gk = __shfl(G, key0 + i, 64);
+            dst[i] = from_f32<E>(key0 + i <= qrow ? p.scale * acc[i] * fast_exp(Gq - Gk) : 0.f);
+          }
         }
-      } else if (pt == 2) {
-        const int zq = wave == 2 ? 0 : 2, zk = zq + 1;
-        E* dst = sP + (16 * zq + r16) * CS + 16 * zk + 4 * q;
+      }
+    }
+    // ---- K^T for the state update, staged once: wave w transposes its dk tiles
+    if constexpr (KT_COPY) {
+      constexpr int TPW = (NKT + NW - 1) / NW;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = from_f32<E>(0.f);
+      for (int tt = 0; tt < TPW; ++tt) {
+        const int t = wave * TPW + tt;
+        if (t < NKT) {
+          const int own = prow(t, r16), supply = prow(t, 4 * (r16 & 3));
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+            *reinterpret_cast<frag*>(sKt + (16 * t + r16) * CS + 32 * s + 8 * q) =
+                col_frag(sK, KS, 32 * s + 4 * q, 32 * s + 16 + 4 * q, own, supply);
+        }
       }
     }
     __syncthreads();
 
-    // ---- per-row gates in tile order (rows prow(u, 4q) .. +3 are consecutive)
-    f32x4 gam4[4], bet4[4], dec4[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = prow(u, 4 * q);
-      gam4[u] = *reinterpret_cast<const f32x4*>(sGam + r);
-      bet4[u] = *reinterpret_cast<const f32x4*>(sBet + r);
-      dec4[u] = *reinterpret_cast<const f32x4*>(sDec + r);
-    }
-
-    // ---- X = K h, Y = Q h
+    // ---- X = K h, Y = Q h (first product of each chain starts from zero)
     f32x4 X[4][NCT], Y[4][NCT];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        X[u][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Y[u][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       frag hb[NCT];
@@ -308,13 +325,13 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
       for (int ct = 0; ct < NCT; ++ct) hb[ct] = M::pack(hs[2 * s][ct], hs[2 * s + 1][ct]);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const frag aK = lds_frag(sK, KS, prow(u, r16), 32 * s, q);
+        const frag aK = lds_frag(sK, KS, 16 * u + r16, 32 * s, q);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) X[u][ct] = M::run(aK, hb[ct], X[u][ct]);
-        if (emit) {
-          const frag aQ = lds_frag(sQ, KS, prow(u, r16), 32 * s, q);
+        for (int ct = 0; ct < NCT; ++ct) X[u][ct] = M::run(aK, hb[ct], s == 0 ? zero4 : X[u][ct]);
+        if constexpr (EMIT) {
+          const frag aQ = lds_frag(sQ, KS, 16 * u + r16, 32 * s, q);
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) Y[u][ct] = M::run(aQ, hb[ct], Y[u][ct]);
+          for (int ct = 0; ct < NCT; ++ct) Y[u][ct] = M::run(aQ, hb[ct], s == 0 ? zero4 : Y[u][ct]);
         }
       }
     }
@@ -325,7 +342,7 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
       for (int ct = 0; ct < NCT; ++ct) {
         const int cb = wcol + 16 * ct;
         const f32x4 vv = col_read4(sV, VS, prow(u, 4 * q), cb + r16, cb + 4 * (r16 & 3));
-        X[u][ct] = bet4[u] * (vv - gam4[u] * X[u][ct]);
+        X[u][ct] = rows4(sBet, u) * (vv - rows4(sGam, u) * X[u][ct]);
       }
     // ---- U = T W (T lower triangular: row tiles 0,1 need contraction step 0 only)
     frag wb[2][NCT];
@@ -337,12 +354,10 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) U[u][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
       for (int s = 0; s <= (u >> 1); ++s) {
-        const frag aT = lds_frag(sT, CS, prow(u, r16), 32 * s, q);
+        const frag aT = lds_frag(sT, CS, 16 * u + r16, 32 * s, q);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) U[u][ct] = M::run(aT, wb[s][ct], U[u][ct]);
+        for (int ct = 0; ct < NCT; ++ct) U[u][ct] = M::run(aT, wb[s][ct], s == 0 ? zero4 : U[u][ct]);
       }
     }
     frag ub[2][NCT], ubd[2][NCT];
@@ -350,30 +365,32 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        ub[s][ct] = M::pack(U[2 * s][ct], U[2 * s + 1][ct]);
-        ubd[s][ct] = M::pack(U[2 * s][ct] * dec4[2 * s], U[2 * s + 1][ct] * dec4[2 * s + 1]);
+        if constexpr (EMIT) ub[s][ct] = M::pack(U[2 * s][ct], U[2 * s + 1][ct]);
+        ubd[s][ct] = M::pack(U[2 * s][ct] * rows4(sDec, 2 * s), U[2 * s + 1][ct] * rows4(sDec, 2 * s + 1));
       }
     // ---- O = scale (diag(gamma) Y + P U), staged column-major in this wave's sO
     E* so = sO[wave];
+    if constexpr (EMIT) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (!emit) break;
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 gs4 = rows4(sGamS, u);
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) Y[u][ct] = Y[u][ct] * gam4[u];
+        for (int ct = 0; ct < NCT; ++ct) Y[u][ct] = Y[u][ct] * gs4;
 #pragma unroll
-      for (int s = 0; s <= (u >> 1); ++s) {
-        const frag aP = lds_frag(sP, CS, prow(u, r16), 32 * s, q);
+        for (int s = 0; s <= (u >> 1); ++s) {
+          const frag aP = lds_frag(sP, CS, 16 * u + r16, 32 * s, q);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) Y[u][ct] = M::run(aP, ub[s][ct], Y[u][ct]);
-      }
+          for (int ct = 0; ct < NCT; ++ct) Y[u][ct] = M::run(aP, ub[s][ct], Y[u][ct]);
+        }
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        E* dst = so + (16 * ct + r16) * CS + prow(u, 4 * q);
+        for (int ct = 0; ct < NCT; ++ct) {
+          E* dst = so + (16 * ct + r16) * CS + prow(u, 4 * q);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = from_f32<E>(p.scale * Y[u][ct][i]);
+          for (int i = 0; i < 4; ++i) dst[i] = from_f32<E>(Y[u][ct][i]);
+        }
       }
     }
-    // ---- h <- gamma_last h + K^T (diag(d) U); K^T via transpose reads of sK
+    // ---- h <- gamma_last h + K^T (diag(d) U)
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
 #pragma unroll
@@ -381,13 +398,15 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
       const int own = prow(t, r16), supply = prow(t, 4 * (r16 & 3));
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const frag aKt = col_frag(sK, KS, 32 * s + 8 * q, own, supply);
+        frag aKt;
+        if constexpr (KT_COPY) aKt = lds_frag(sKt, CS, 16 * t + r16, 32 * s, q);
+        else aKt = col_frag(sK, KS, 32 * s + 4 * q, 32 * s + 16 + 4 * q, own, supply);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) hs[t][ct] = M::run(aKt, ubd[s][ct], hs[t][ct]);
       }
     }
     // ---- O store: lane (j, q) writes 8 consecutive columns of token row 16*rb + j
-    if (emit) {
+    if constexpr (EMIT) {
       constexpr int NG = NCW / 8;   // 8-column groups per wave
       E* ob = Ob + (int64_t)c * kChunk * row_v;
 #pragma unroll
@@ -401,6 +420,29 @@ __global__ __launch_bounds__(256) void fused_forward_kernel(Problem p, FwdPlan p
         if (row < len) store8(ob + row * row_v + 8 * cg8, lo, hi);
       }
     }
+  };
+
+  for (int c = c_start; c < c_end; ++c) {
+    const int len = min(kChunk, si.len - c * kChunk);
+
+    // ---- stage chunk c in LDS, then start the loads of chunk c+1
+    pf.template store<KS, CS, VS>(sK, sQ, sV, sT, sGraw, sBraw, p.beta_bf16, mcols, tid);
+    __syncthreads();
+    if (c + 1 < c_end) issue_loads(c + 1);
+
+    // ---- gates: every wave scans (lane = chunk row); wave 0 publishes per-row values
+    const float G = wave_inclusive_scan(sGraw[lane]);
+    const float Glast = __shfl(G, 63, 64);
+    const float gC = fast_exp(Glast);
+    if (wave == 0) {
+      const float gam = fast_exp(G);
+      sGam[lane] = gam;
+      sGamS[lane] = gam * p.scale;
+      sDec[lane] = fast_exp(Glast - G);
+      sBet[lane] = sBraw[lane];
+    }
+    if (c >= c_out) step(std::true_type{}, c, len, G, gC);
+    else step(std::false_type{}, c, len, G, gC);
     __syncthreads();
   }
 
@@ -437,15 +479,17 @@ template <typename E, int DK>
 static void launch_dk(const Problem& p, const FwdPlan& plan, hipStream_t s) {
   // pass 1 also runs dk transition-matrix columns after the dv value columns
   const int cols = plan.mode == kPass1 ? p.dv + DK : p.dv;
-  if constexpr (sizeof(E) == 2) {  // fp32 tiles only fit LDS at 64 columns per workgroup
+  if constexpr (sizeof(E) == 2) {
+    // 128 columns per workgroup as 8 waves x 16 columns: two waves per SIMD
     if (p.dv % 128 == 0 && cols % 128 == 0 && plan.value_block != 64) {
       dim3 grid((unsigned)plan.units, (unsigned)(cols / 128));
-      fused_forward_kernel<E, DK, 32><<<grid, 256, 0, s>>>(p, plan);
+      fused_forward_kernel<E, DK, 16, 8><<<grid, 512, 0, s>>>(p, plan);
       return;
     }
   }
+  // 64 columns per workgroup as 4 waves x 16 columns (fp32 tiles only fit LDS this way)
   dim3 grid((unsigned)plan.units, (unsigned)(cols / 64));
-  fused_forward_kernel<E, DK, 16><<<grid, 256, 0, s>>>(p, plan);
+  fused_forward_kernel<E, DK, 16, 4><<<grid, 256, 0, s>>>(p, plan);
 }
 
 hipError_t launch_fused_forward(const Problem& p, const FwdPlan& plan, hipStream_t s) {

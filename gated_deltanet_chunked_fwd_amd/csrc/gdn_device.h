@@ -36,6 +36,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __host__ __device__ constexpr int prow(int t, int r) {
   return 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3);
 }
+// Inverse of prow: the tile-order slot 16 t + r that holds physical row R.  Tiles
+// staged in LDS in this order make every fragment read touch 16 consecutive LDS
+// rows, which (with a row stride of 8 mod 32 dwords) is free of bank conflicts.
+__host__ __device__ constexpr int tord(int R) {
+  return 16 * (2 * (R >> 5) + ((R >> 2) & 1)) + 4 * ((R & 31) >> 3) + (R & 3);
+}
 
 template <typename E>
 struct Mma;
@@ -125,11 +131,11 @@ __device__ __forceinline__ i16x4 col_read4_raw(const bf16* M, int stride, int ro
 }
 
 // A/B operand of one 32-wide contraction step whose 8 elements are column reads
-// at rows row0 .. row0+3 (elements 0-3) and row0+4 .. row0+7 (elements 4-7).
-__device__ __forceinline__ bf16x8 col_frag(const bf16* M, int stride, int row0, int own_col,
-                                           int supply_col) {
-  const i16x4 lo = col_read4_raw(M, stride, row0, own_col, supply_col);
-  const i16x4 hi = col_read4_raw(M, stride, row0 + 4, own_col, supply_col);
+// at rows row_lo .. row_lo+3 (elements 0-3) and row_hi .. row_hi+3 (elements 4-7).
+__device__ __forceinline__ bf16x8 col_frag(const bf16* M, int stride, int row_lo, int row_hi,
+                                           int own_col, int supply_col) {
+  const i16x4 lo = col_read4_raw(M, stride, row_lo, own_col, supply_col);
+  const i16x4 hi = col_read4_raw(M, stride, row_hi, own_col, supply_col);
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   i16x8 v;
   v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
@@ -137,12 +143,15 @@ __device__ __forceinline__ bf16x8 col_frag(const bf16* M, int stride, int row0, 
   return __builtin_bit_cast(bf16x8, v);
 }
 
-__device__ __forceinline__ f32x8 col_frag(const float* M, int stride, int row0, int own_col,
-                                          int supply_col) {
+__device__ __forceinline__ f32x8 col_frag(const float* M, int stride, int row_lo, int row_hi,
+                                          int own_col, int supply_col) {
   (void)supply_col;
   f32x8 r;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = M[(row0 + i) * stride + own_col];
+  for (int i = 0; i < 4; ++i) {
+    r[i] = M[(row_lo + i) * stride + own_col];
+    r[4 + i] = M[(row_hi + i) * stride + own_col];
+  }
   return r;
 }
 
