@@ -5,11 +5,14 @@ seeded synthetic input, all inputs resident in HBM.  Default workload: the
 Qwen-like prefill (B=4, T=4096, H=16, dk=dv=128, bf16 q/k/v/o, fp32 g, bf16 beta,
 zero initial state, fp32 final state).
 
-Timing: W untimed warm-up steps; then K steps between two device synchronisations.
-Before each timed step a 512 MiB buffer is overwritten (evicts the 256 MB MALL and
-the L2s) outside the step's HIP events; ms_per_step is the mean of the per-step
-event times, so it never includes the flush.  Each stage of the call is also timed
-live with HIP events recorded by the library on the launch stream.
+Timing: W untimed warm-up steps, then a short stage pass (3 steps with every
+stage bracketed by HIP events) that finds the dominant kernel.  Then K timed steps
+between two device synchronisations.  Before each timed step a 512 MiB buffer is
+overwritten (evicts the 256 MB MALL and the L2s) outside the step's HIP events, so
+ms_per_step (the mean of the per-step event times) never includes the flush.  In
+the timed steps only the dominant kernel's pair of events is recorded (by the
+library, on the launch stream, around that launch), which gives its live mean
+duration for the roofline at the cost of one event pair per step.
 
 Roofline (dominant kernel = the stage with the largest mean time):
   achieved = algorithmic bytes of that kernel per launch / its mean duration,
@@ -160,8 +163,9 @@ def main():
     hT = torch.empty((N, spec.H, spec.dk, spec.dv), dtype=torch.float32, device=dev)
     hip = Hip()
     stage_ev = hip.events(2 * binding.GDN_NUM_STAGES)
-    opts = binding.make_opts(no_split=args.no_split, value_block=args.value_block,
-                             stage_events=ctypes.cast(stage_ev, ctypes.c_void_p))
+    opts_all = binding.make_opts(no_split=args.no_split, value_block=args.value_block,
+                                 stage_events=ctypes.cast(stage_ev, ctypes.c_void_p))
+    opts = binding.make_opts(no_split=args.no_split, value_block=args.value_block)
     ws = torch.empty(max(binding.workspace_bytes(d["q"], d["v"], d["beta"], d["cu_seqlens"],
                                                  inp["cu_seqlens"], opts), 1),
                      dtype=torch.uint8, device=dev)
@@ -170,9 +174,9 @@ def main():
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     step_ev = hip.events(2)
 
-    def step():
+    def step(o_=None):
         binding.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"],
-                          cu_seqlens=d["cu_seqlens"], scale=inp["scale"], opts=opts,
+                          cu_seqlens=d["cu_seqlens"], scale=inp["scale"], opts=o_ or opts,
                           cu_seqlens_host=inp["cu_seqlens"], out=o, final_state_out=hT,
                           workspace=ws)
 
@@ -180,22 +184,42 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    step_ms, stage_ms = [], {i: [] for i in range(binding.GDN_NUM_STAGES)}
+    def stage_pass(steps):
+        """Per-stage mean ms over `steps` flushed steps, every stage timed."""
+        out = {i: [] for i in range(binding.GDN_NUM_STAGES)}
+        for i in range(steps):
+            if not args.no_flush:
+                flush.fill_(i & 0xFF)
+            # stages that a step does not run keep stale events: mark them first
+            for st in range(binding.GDN_NUM_STAGES):
+                hip.record(stage_ev[2 * st], stream)
+                hip.record(stage_ev[2 * st + 1], stream)
+            step(opts_all)
+            for st in range(binding.GDN_NUM_STAGES):
+                out[st].append(hip.elapsed(stage_ev[2 * st], stage_ev[2 * st + 1]))
+        return {binding.STAGE_NAMES[st]: sum(v) / len(v) for st, v in out.items()
+                if sum(v) / len(v) > 1e-4}
+
+    st_mean = stage_pass(3)
+    dom = max(st_mean, key=st_mean.get)
+    dom_idx = binding.STAGE_NAMES.index(dom)
+    dom_ev = (ctypes.c_void_p * (2 * binding.GDN_NUM_STAGES))()
+    dom_ev[2 * dom_idx] = stage_ev[2 * dom_idx]
+    dom_ev[2 * dom_idx + 1] = stage_ev[2 * dom_idx + 1]
+    opts_dom = binding.make_opts(no_split=args.no_split, value_block=args.value_block,
+                                 stage_events=ctypes.cast(dom_ev, ctypes.c_void_p))
+
+    step_ms, dom_ms_list = [], []
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     for i in range(args.steps):
         if not args.no_flush:
             flush.fill_(i & 0xFF)
         hip.record(step_ev[0], stream)
-        # stage events that a step does not record keep stale values: mark them
-        for s in range(binding.GDN_NUM_STAGES):
-            hip.record(stage_ev[2 * s], stream)
-            hip.record(stage_ev[2 * s + 1], stream)
-        step()
+        step(opts_dom)
         hip.record(step_ev[1], stream)
         step_ms.append(hip.elapsed(step_ev[0], step_ev[1]))
-        for s in range(binding.GDN_NUM_STAGES):
-            stage_ms[s].append(hip.elapsed(stage_ev[2 * s], stage_ev[2 * s + 1]))
+        dom_ms_list.append(hip.elapsed(stage_ev[2 * dom_idx], stage_ev[2 * dom_idx + 1]))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
 
@@ -208,14 +232,12 @@ def main():
     hot_ms = hip.elapsed(step_ev[0], step_ev[1]) / 5
 
     ms = sum(step_ms) / len(step_ms)
+    ms_median = sorted(step_ms)[len(step_ms) // 2]
     tokens = spec.B * spec.T
-    st_mean = {binding.STAGE_NAMES[s]: sum(v) / len(v) for s, v in stage_ms.items()
-               if v and sum(v) / len(v) > 1e-4}
-    dom = max(st_mean, key=st_mean.get)
+    dom_ms = sum(dom_ms_list) / len(dom_ms_list)
     has_h0 = d["h0"] is not None
     alg_bytes = algorithmic_bytes(spec, N, has_h0, True)
     flops = algorithmic_flops(spec)
-    dom_ms = st_mean[dom]
     achieved = alg_bytes / (dom_ms * 1e-3) / 1e9
     ksrc = os.path.join(ROOT, "gated_deltanet_chunked_fwd_amd", "csrc", "fused_forward.hip")
     traffic = traffic_for(ksrc) if dom == "fused_forward" else None
@@ -244,6 +266,7 @@ def main():
                  "mfma_frac": flops / (ms * 1e-3) / 1e12 / mfma_peak,
                  "algorithmic_flops": flops, "stage_ms": st_mean,
                  "ms_per_step_hot_caches": hot_ms, "ms_min": min(step_ms),
+                 "ms_median": ms_median,
                  "wall_s_timed_loop_incl_flush": wall},
     }
     if not args.no_cpu_baseline:

@@ -9,141 +9,246 @@
 //
 //   A = strict_lower(diag(beta) K K^T * Gamma),   T = (I + A)^{-1}
 //
-// Mapping: one 256-thread workgroup per (chunk, head).  The Gram matrix runs on
-// MFMA (wave w owns row tile w, bf16 or fp32 operands, fp32 accumulation).  The
-// inverse is computed in fp32 in LDS: the four 16x16 diagonal blocks by forward
-// substitution (one lane per column), then two doubling levels
-//     [D0 0; X D1]^-1 off-diagonal = -D1 A10 D0            (16 -> 32)
-//     [X0 0; Y X1]^-1 off-diagonal = -X1 A[32:,:32] X0     (32 -> 64)
-// and T is written in the storage dtype, row-major 64 x 64 per (chunk, head).
+// Mapping: one wave per (chunk, head), four heads of one chunk per workgroup, no
+// workgroup barriers (waves exchange data only through their own LDS slice).
+// The key rows go straight from HBM into MFMA operand registers; the Gram tiles
+// run on v_mfma_f32_16x16x32_bf16 (fp32 path: 16x16x4_f32).  With 16x16 blocks
+// A_ij, T_ij of A and T:
+//   * T_ii = (I + A_ii)^{-1} by forward substitution in fp32, lane = (block, column);
+//   * the rest by two doubling levels of 16x16x16 fp32 MFMA products,
+//       T_10 = -T_11 A_10 T_00,  T_32 = -T_33 A_32 T_22,
+//       [T_20 T_21; T_30 T_31] = -[T_22 0; T_32 T_33] A[32:, :32] [T_00 0; T_10 T_11].
+// Register-resident products.  In accumulator ("D") layout lane (r, q) holds
+// X[4q+i][r] in slot i.  Feeding slot e of X^T's D tile as the A operand and slot e
+// of Y's D tile as the B operand of four chained 16x16x4 MFMAs contracts index
+// 4q+e, so D(X^T), D(Y) -> D(XY), and with the operands swapped D(Y), D(X^T) ->
+// D((XY)^T).  Off-diagonal Gram tiles are therefore formed transposed (K_j K_i^T,
+// gated with the roles of rows and columns exchanged), and T's final blocks come
+// out transposed, i.e. with four consecutive columns of one row per lane, which is
+// what the row-major store wants.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
 namespace gdn {
 
-template <typename E, int DK>
-__global__ __launch_bounds__(256) void chunk_inverse_kernel(Problem p, E* __restrict__ tout) {
-  constexpr int PAD = sizeof(E) == 2 ? 8 : 4;
-  constexpr int KS = DK + PAD;       // padded row stride of the key tile (elements)
-  constexpr int AS = 65;             // fp32 stride of A and T
-  constexpr int VPR = DK * (int)sizeof(E) / 16;
-  constexpr int EPV = 16 / (int)sizeof(E);
-  __shared__ __align__(16) E sK[64 * KS];
-  __shared__ float sA[64 * AS];
-  __shared__ float sT[64 * AS];
-  __shared__ float sG[64], sB[64];
-  float* sR = reinterpret_cast<float*>(sK);  // scratch once the Gram matrix is done
-  static_assert(sizeof(sK) >= 32 * 33 * sizeof(float), "scratch alias too small");
+namespace {
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t cg = blockIdx.x;
-  const int h = blockIdx.y;
+template <typename E, int DK>
+struct InvCfg {
+  static constexpr int NS = DK / 32;                           // Gram contraction steps
+  static constexpr int OS = kChunk + (sizeof(E) == 2 ? 8 : 4);  // staged T row stride (elements)
+  static constexpr int ABS = 260;   // block stride of the staged diagonal A blocks (floats)
+  static constexpr int TCS = 20;    // column stride of the staged diagonal T blocks (floats)
+  static constexpr int TBS = 16 * TCS;
+  static constexpr int WORK = 4 * ABS + 4 * TBS;              // A and T diagonal blocks
+  static constexpr int OUT = kChunk * OS * (int)sizeof(E) / 4;  // staged T (aliases WORK)
+  static constexpr int UNION = WORK > OUT ? WORK : OUT;
+  static constexpr int PER_WAVE = 2 * kChunk + UNION;          // floats of LDS per wave
+};
+
+// D(X^T), D(Y), acc -> acc + D(X Y) for 16x16 blocks (see the header comment).
+__device__ __forceinline__ f32x4 mm16(const f32x4& xt, const f32x4& y, f32x4 acc) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[e], y[e], acc, 0, 0, 0);
+  return acc;
+}
+
+// Orders this wave's LDS accesses across lanes (LDS executes a wave's operations in
+// issue order; this keeps the compiler from moving them).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <typename E>
+__device__ __forceinline__ typename Mma<E>::frag load_frag(const E* src, bool ok) {
+  typename Mma<E>::frag f;
+  if (ok) {
+    f = *reinterpret_cast<const typename Mma<E>::frag*>(src);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (E)0.f;
+  }
+  return f;
+}
+
+// Four consecutive elements of one row: 8 bytes (bf16) or 16 bytes (fp32).
+__device__ __forceinline__ void store4(bf16* dst, const f32x4& v) {
+  bf16x4 b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = (bf16)v[i];
+  *reinterpret_cast<bf16x4*>(dst) = b;
+}
+__device__ __forceinline__ void store4(float* dst, const f32x4& v) {
+  *reinterpret_cast<f32x4*>(dst) = v;
+}
+
+}  // namespace
+
+template <typename E, int DK>
+__global__ __launch_bounds__(256) void chunk_inverse_kernel(Problem p, E* __restrict__ tout,
+                                                             float* __restrict__ csum) {
+  using Cfg = InvCfg<E, DK>;
+  using M = Mma<E>;
+  using frag = typename M::frag;
+  constexpr int NS = Cfg::NS, OS = Cfg::OS, ABS = Cfg::ABS, TCS = Cfg::TCS, TBS = Cfg::TBS;
+  __shared__ __align__(16) float lds[4 * Cfg::PER_WAVE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, q = lane >> 4;
+  const int HG = (p.H + 3) / 4;
+  const int64_t cg = blockIdx.x / HG;
+  const int h = (int)(blockIdx.x % HG) * 4 + wave;
+  if (h >= p.H) return;   // whole wave: no workgroup barrier follows
+
   const int n = seq_of_chunk(cg, p.chunk_off, p.N, p.T);
   const SeqInfo si = seq_info(n, p.cu, p.chunk_off, p.T);
   const int c = (int)(cg - si.chunk0);
   const int64_t r0 = si.tok0 + (int64_t)c * kChunk;
   const int len = min(kChunk, si.len - c * kChunk);
-  const E* K = reinterpret_cast<const E*>(p.k);
 
-  for (int i = tid; i < 64 * VPR; i += 256) {
-    const int r = i / VPR, cv = i % VPR;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (r < len) val = *reinterpret_cast<const u32x4*>(K + ((r0 + r) * p.H + h) * DK + cv * EPV);
-    *reinterpret_cast<u32x4*>(sK + r * KS + cv * EPV) = val;
-  }
-  if (wave == 0) {
+  float* sG = lds + wave * Cfg::PER_WAVE;   // chunk-local cumulative gate, per row
+  float* sB = sG + kChunk;                  // beta, per row
+  float* sAd = sB + kChunk;                 // diagonal A blocks, row-major, stride 16
+  float* sTd = sAd + 4 * ABS;               // diagonal T blocks, column-major, stride TCS
+  E* sOut = reinterpret_cast<E*>(sAd);      // staged T, row-major (after sAd/sTd are read)
+
+  // ---- key rows -> operand registers: tile a, step s, lane (r, q): row 16a+r, cols 32s+8q..+7
+  const E* K = reinterpret_cast<const E*>(p.k) + (r0 * p.H + h) * DK;
+  const int64_t krow = (int64_t)p.H * DK;
+  frag kf[4][NS];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      kf[a][s] = load_frag<E>(K + (16 * a + r) * krow + 32 * s + 8 * q, 16 * a + r < len);
+
+  {
     float gv = 0.f, bv = 0.f;
     if (lane < len) {
       gv = p.g[(r0 + lane) * p.H + h];
       bv = load_scalar(p.beta, (r0 + lane) * p.H + h, p.beta_bf16);
     }
-    sG[lane] = wave_inclusive_scan(gv);
+    const float G = wave_inclusive_scan(gv);
+    sG[lane] = G;
     sB[lane] = bv;
+    if (csum && lane == kChunk - 1) csum[cg * p.H + h] = G;   // chunk gate sum for the gate scan
   }
-  __syncthreads();
 
-  // Gram matrix, row tile = wave; mask before exp.
-  {
-    const int r = lane & 15, q = lane >> 4;
+  // ---- Gram tiles: diagonal (a, a) and transposed off-diagonal (b, a), b < a
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 gd[4], go[4][4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if (v <= wave) {
+  for (int a = 0; a < 4; ++a) {
+    gd[a] = zero4;
 #pragma unroll
-        for (int s = 0; s < DK / 32; ++s)
-          acc = Mma<E>::run(lds_frag(sK, KS, 16 * wave + r, 32 * s, q),
-                            lds_frag(sK, KS, 16 * v + r, 32 * s, q), acc);
-      }
+    for (int s = 0; s < NS; ++s) gd[a] = M::run(kf[a][s], kf[a][s], gd[a]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * wave + 4 * q + i, col = 16 * v + r;
-        float val = 0.f;
-        if (col < row) val = sB[row] * fast_exp(sG[row] - sG[col]) * acc[i];
-        sA[row * AS + col] = val;
-      }
+    for (int b = 0; b < a; ++b) {
+      go[a][b] = zero4;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) go[a][b] = M::run(kf[b][s], kf[a][s], go[a][b]);
     }
   }
-  __syncthreads();
+  wave_lds_sync();
 
-  // Diagonal blocks: lane = 16*b + column.
-  if (wave == 0) {
-    const int b = lane >> 4, cc = lane & 15;
+  // ---- gate and mask: A[m][k] = beta_m exp(G_m - G_k) (K K^T)[m][k], k < m
+  float Gc[4], Bc[4];
+  f32x4 Gr[4], Br[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    Gc[a] = sG[16 * a + r];
+    Bc[a] = sB[16 * a + r];
+    Gr[a] = *reinterpret_cast<const f32x4*>(sG + 16 * a + 4 * q);
+    Br[a] = *reinterpret_cast<const f32x4*>(sB + 16 * a + 4 * q);
+  }
+  f32x4 At[4][4];   // At[a][b] = D(A_ab^T), b < a
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * q + i;
+      sAd[a * ABS + m * 16 + r] = r < m ? Br[a][i] * fast_exp(Gr[a][i] - Gc[a]) * gd[a][i] : 0.f;
+    }
+#pragma unroll
+    for (int b = 0; b < a; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) At[a][b][i] = Bc[a] * fast_exp(Gc[a] - Gr[b][i]) * go[a][b][i];
+  }
+  wave_lds_sync();
+
+  // ---- T_bb = (I + A_bb)^{-1}: lane (r, q) solves column r of block q
+  {
+    const float* arow = sAd + q * ABS;
     float x[16];
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      float acc = (rr == cc) ? 1.f : 0.f;
-      const float* arow = sA + (16 * b + rr) * AS + 16 * b;
+    for (int m = 0; m < 16; ++m) {
+      float acc = (m == r) ? 1.f : 0.f;
 #pragma unroll
-      for (int s = 0; s < rr; ++s) acc -= arow[s] * x[s];
-      x[rr] = acc;
+      for (int j = 0; j < (m + 3) / 4; ++j) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(arow + m * 16 + 4 * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * j + e < m) acc -= a4[e] * x[4 * j + e];
+      }
+      x[m] = acc;
     }
+    float* tcol = sTd + q * TBS + r * TCS;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) sT[(16 * b + rr) * AS + 16 * b + cc] = x[rr];
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 v = {x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]};
+      *reinterpret_cast<f32x4*>(tcol + 4 * j) = v;
+    }
   }
-  __syncthreads();
+  wave_lds_sync();
+  f32x4 Td[4], TdT[4];   // D(T_aa), D(T_aa^T)
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    Td[a] = *reinterpret_cast<const f32x4*>(sTd + a * TBS + r * TCS + 4 * q);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) TdT[a][i] = sTd[a * TBS + (4 * q + i) * TCS + r];
+  }
+  wave_lds_sync();
 
-  // 16 -> 32: blocks (1,0) and (3,2):  T_i,i-1 = -D_i (A_i,i-1 D_i-1)
-  for (int idx = tid; idx < 512; idx += 256) {
-    const int which = idx >> 8, rr = (idx >> 4) & 15, cc = idx & 15;
-    const int i = which ? 3 : 1, j = i - 1;
-    const float* arow = sA + (16 * i + rr) * AS + 16 * j;
-    float acc = 0.f;
-    for (int s = cc; s < 16; ++s) acc += arow[s] * sT[(16 * j + s) * AS + 16 * j + cc];
-    sR[which * 256 + rr * 16 + cc] = acc;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < 512; idx += 256) {
-    const int which = idx >> 8, rr = (idx >> 4) & 15, cc = idx & 15;
-    const int i = which ? 3 : 1, j = i - 1;
-    const float* drow = sT + (16 * i + rr) * AS + 16 * i;
-    float acc = 0.f;
-    for (int s = 0; s <= rr; ++s) acc += drow[s] * sR[which * 256 + s * 16 + cc];
-    sT[(16 * i + rr) * AS + 16 * j + cc] = -acc;
-  }
-  __syncthreads();
+  // ---- doubling levels (D(.) of each block; "T" suffix = transposed block)
+  const f32x4 R10 = mm16(At[1][0], Td[0], zero4);
+  const f32x4 T10 = -mm16(TdT[1], R10, zero4);
+  const f32x4 T10T = -mm16(R10, TdT[1], zero4);
+  const f32x4 R32 = mm16(At[3][2], Td[2], zero4);
+  const f32x4 T32T = -mm16(R32, TdT[3], zero4);
+  const f32x4 R20 = mm16(At[2][1], T10, mm16(At[2][0], Td[0], zero4));
+  const f32x4 R21 = mm16(At[2][1], Td[1], zero4);
+  const f32x4 R30 = mm16(At[3][1], T10, mm16(At[3][0], Td[0], zero4));
+  const f32x4 R31 = mm16(At[3][1], Td[1], zero4);
+  const f32x4 T20T = -mm16(R20, TdT[2], zero4);
+  const f32x4 T21T = -mm16(R21, TdT[2], zero4);
+  const f32x4 T30T = -mm16(R30, TdT[3], mm16(R20, T32T, zero4));
+  const f32x4 T31T = -mm16(R31, TdT[3], mm16(R21, T32T, zero4));
 
-  // 32 -> 64: T[32:,:32] = -X1 (A[32:,:32] X0)
-  for (int idx = tid; idx < 1024; idx += 256) {
-    const int rr = idx >> 5, cc = idx & 31;
-    const float* arow = sA + (32 + rr) * AS;
-    float acc = 0.f;
-    for (int s = cc; s < 32; ++s) acc += arow[s] * sT[s * AS + cc];
-    sR[rr * 33 + cc] = acc;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < 1024; idx += 256) {
-    const int rr = idx >> 5, cc = idx & 31;
-    const float* xrow = sT + (32 + rr) * AS + 32;
-    float acc = 0.f;
-    for (int s = 0; s <= rr; ++s) acc += xrow[s] * sR[s * 33 + cc];
-    sT[(32 + rr) * AS + cc] = -acc;
-  }
-  __syncthreads();
+  // ---- stage T row-major (lane (r, q) of block (a, b): row 16a+r, cols 16b+4q..+3)
+  auto put = [&](int a, int b, const f32x4& v) { store4(sOut + (16 * a + r) * OS + 16 * b + 4 * q, v); };
+#pragma unroll
+  for (int a = 0; a < 4; ++a) put(a, a, TdT[a]);
+  put(1, 0, T10T);
+  put(2, 0, T20T);
+  put(2, 1, T21T);
+  put(3, 0, T30T);
+  put(3, 1, T31T);
+  put(3, 2, T32T);
+  wave_lds_sync();
 
+  // ---- coalesced 16-byte stores; blocks above the diagonal are zero
+  constexpr int EPV = 16 / (int)sizeof(E);
+  constexpr int SPR = kChunk / EPV;   // 16-byte segments per row
   E* dst = tout + ((int64_t)cg * p.H + h) * (kChunk * kChunk);
-  for (int idx = tid; idx < kChunk * kChunk; idx += 256) {
-    const int rr = idx >> 6, cc = idx & 63;
-    dst[idx] = from_f32<E>(cc <= rr ? sT[rr * AS + cc] : 0.f);
+#pragma unroll
+  for (int j = 0; j < kChunk * SPR / 64; ++j) {
+    const int idx = 64 * j + lane, row = idx / SPR, seg = idx % SPR;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (seg * EPV < 16 * (row / 16 + 1)) v = *reinterpret_cast<const u32x4*>(sOut + row * OS + seg * EPV);
+    *reinterpret_cast<u32x4*>(dst + row * kChunk + seg * EPV) = v;
   }
 }
 
@@ -163,15 +268,17 @@ hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hi
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_inverse(const Problem& p, void* t_out, hipStream_t s) {
+hipError_t launch_chunk_inverse(const Problem& p, void* t_out, float* csum, hipStream_t s) {
   if (p.total_chunks == 0) return hipSuccess;
-  dim3 grid((unsigned)p.total_chunks, (unsigned)p.H);
+  const int64_t blocks = p.total_chunks * ((p.H + 3) / 4);
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)blocks);
   if (p.qkv_bf16) {
-    if (p.dk == 128) chunk_inverse_kernel<bf16, 128><<<grid, 256, 0, s>>>(p, (bf16*)t_out);
-    else chunk_inverse_kernel<bf16, 64><<<grid, 256, 0, s>>>(p, (bf16*)t_out);
+    if (p.dk == 128) chunk_inverse_kernel<bf16, 128><<<grid, 256, 0, s>>>(p, (bf16*)t_out, csum);
+    else chunk_inverse_kernel<bf16, 64><<<grid, 256, 0, s>>>(p, (bf16*)t_out, csum);
   } else {
-    if (p.dk == 128) chunk_inverse_kernel<float, 128><<<grid, 256, 0, s>>>(p, (float*)t_out);
-    else chunk_inverse_kernel<float, 64><<<grid, 256, 0, s>>>(p, (float*)t_out);
+    if (p.dk == 128) chunk_inverse_kernel<float, 128><<<grid, 256, 0, s>>>(p, (float*)t_out, csum);
+    else chunk_inverse_kernel<float, 64><<<grid, 256, 0, s>>>(p, (float*)t_out, csum);
   }
   return hipGetLastError();
 }

@@ -13,18 +13,38 @@
 // consecutive chunks has gate sum <= log_eps - margin (margin 1e-3 absorbs the
 // fp32 summation error).  The smallest admissible W <= wmax is used; 0 = none.
 //
-// Two kernels.  gate_window_max: grid (N*H, ceil(max chunks / 256)); each block
-// forms the chunk sums of its 256 chunks (plus a halo of wmax-1), the maximum
-// run sum per W over runs starting in its range, and merges them with an atomic
-// max into best[nh][W] (floats stored as order-preserving uints, reset to 0 =
-// "minus infinity" beforehand).  window_of() turns best[] into W wherever it is
-// needed; gate_window_finalize writes it out for the stand-alone entry point.
+// The chunk gate sums come from the chunk-inverse kernel, which forms the chunk's
+// cumulative gate anyway (or, for the stand-alone entry point, from
+// chunk_gate_sums_kernel with the same wave scan, so both give identical sums).
+// gate_window_max: grid (N*H, ceil(max chunks / 256)); each block loads the sums
+// of its 256 chunks (plus a halo of wmax-1), forms the maximum run sum per W over
+// runs starting in its range, and merges them with an atomic max into
+// best[nh][W] (floats stored as order-preserving uints, reset to 0 = "minus
+// infinity" beforehand).  window_of() turns best[] into W wherever it is needed;
+// gate_window_finalize writes it out for the stand-alone entry point.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
 namespace gdn {
 
-__global__ __launch_bounds__(256) void gate_window_max_kernel(const float* __restrict__ g,
+// Per (chunk, head): the sum of the chunk's gates, as the last entry of the
+// chunk-local inclusive wave scan (one wave per chunk-head, lane = chunk row).
+__global__ __launch_bounds__(256) void chunk_gate_sums_kernel(Problem p, float* __restrict__ csum) {
+  const int lane = threadIdx.x & 63;
+  const int HG = (p.H + 3) / 4;
+  const int64_t cg = blockIdx.x / HG;
+  const int h = (int)(blockIdx.x % HG) * 4 + (threadIdx.x >> 6);
+  if (h >= p.H) return;
+  const int n = seq_of_chunk(cg, p.chunk_off, p.N, p.T);
+  const SeqInfo si = seq_info(n, p.cu, p.chunk_off, p.T);
+  const int c = (int)(cg - si.chunk0);
+  const int len = min(kChunk, si.len - c * kChunk);
+  const float gv = lane < len ? p.g[(si.tok0 + (int64_t)c * kChunk + lane) * p.H + h] : 0.f;
+  const float G = wave_inclusive_scan(gv);
+  if (lane == kChunk - 1) csum[cg * p.H + h] = G;
+}
+
+__global__ __launch_bounds__(256) void gate_window_max_kernel(const float* __restrict__ csum,
                                                               const int32_t* __restrict__ cu,
                                                               const int32_t* __restrict__ chunk_off,
                                                               int64_t T, int N, int H, int wmax,
@@ -37,16 +57,9 @@ __global__ __launch_bounds__(256) void gate_window_max_kernel(const float* __res
   const int cs = blockIdx.y * 256;
   if (cs >= nch) return;
   const int tid = threadIdx.x;
-  // chunk sums for chunks cs + i, i < 256 + wmax - 1
   for (int i = tid; i < 256 + wmax - 1; i += 256) {
     const int c = cs + i;
-    float s = 0.f;
-    if (c < nch) {
-      const int r0 = c * kChunk, rl = min(kChunk, si.len - r0);
-      const float* gp = g + (si.tok0 + r0) * H + h;
-      for (int r = 0; r < rl; ++r) s += gp[(int64_t)r * H];
-    }
-    sums[i] = s;
+    sums[i] = c < nch ? csum[(si.chunk0 + c) * H + h] : 0.f;
   }
   __syncthreads();
   float bestw[kWindowMaxCap];
@@ -115,11 +128,19 @@ hipError_t launch_plan_tables(const int32_t* cu, int N, int seg_chunks, int32_t*
   return hipGetLastError();
 }
 
-hipError_t launch_gate_scan(const Problem& p, int64_t max_chunks, int wmax, uint32_t* best,
-                            hipStream_t s) {
+hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s) {
+  if (p.total_chunks == 0) return hipSuccess;
+  const int64_t blocks = p.total_chunks * ((p.H + 3) / 4);
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  chunk_gate_sums_kernel<<<(unsigned)blocks, 256, 0, s>>>(p, csum);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_scan(const Problem& p, const float* csum, int64_t max_chunks, int wmax,
+                            uint32_t* best, hipStream_t s) {
   if (p.N == 0 || max_chunks == 0) return hipSuccess;
   dim3 grid((unsigned)(p.N * p.H), (unsigned)((max_chunks + 255) / 256));
-  gate_window_max_kernel<<<grid, 256, 0, s>>>(p.g, p.cu, p.chunk_off, p.T, p.N, p.H, wmax, best);
+  gate_window_max_kernel<<<grid, 256, 0, s>>>(csum, p.cu, p.chunk_off, p.T, p.N, p.H, wmax, best);
   return hipGetLastError();
 }
 

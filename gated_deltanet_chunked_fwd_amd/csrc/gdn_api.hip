@@ -59,10 +59,10 @@ struct StageMark {
   int stage;
   StageMark(const gdn_opts* o, int stage_, hipStream_t s_)
       : ev(o ? o->stage_events : nullptr), s(s_), stage(stage_) {
-    if (ev) (void)hipEventRecord(ev[2 * stage], s);
+    if (ev && ev[2 * stage]) (void)hipEventRecord(ev[2 * stage], s);
   }
   ~StageMark() {
-    if (ev) (void)hipEventRecord(ev[2 * stage + 1], s);
+    if (ev && ev[2 * stage + 1]) (void)hipEventRecord(ev[2 * stage + 1], s);
   }
 };
 
@@ -150,7 +150,7 @@ Plan make_plan(const gdn_shape* s, const gdn_opts* o) {
 }
 
 struct Layout {
-  size_t tmat = 0, chunk_off = 0, seg_off = 0, best = 0, sstar = 0, mcorr = 0, hstart = 0;
+  size_t tmat = 0, chunk_off = 0, seg_off = 0, best = 0, csum = 0, sstar = 0, mcorr = 0, hstart = 0;
   size_t total = 0;
 };
 
@@ -164,6 +164,7 @@ Layout layout(const gdn_shape* s, const Plan& P) {
   L.seg_off = take((size_t)(s->N + 1) * sizeof(int32_t));
   L.best = take((size_t)s->N * s->H * kWindowMaxCap * sizeof(uint32_t));
   if (P.split) {
+    L.csum = take((size_t)P.total_chunks * s->H * sizeof(float));
     const size_t slots = (size_t)P.total_segs * s->H;
     L.sstar = take(slots * s->dk * s->dv * sizeof(float));
     L.mcorr = take(slots * s->dk * s->dk * sizeof(float));
@@ -261,9 +262,10 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
   if (cu_seqlens) p.chunk_off = chunk_off;
 
   void* tmat = ws + L.tmat;
+  float* csum = P.split ? reinterpret_cast<float*>(ws + L.csum) : nullptr;
   {
     StageMark mark(opts, GDN_STAGE_INVERSE, stream);
-    if (gdn::launch_chunk_inverse(p, tmat, stream) != hipSuccess) return GDN_ERR_HIP;
+    if (gdn::launch_chunk_inverse(p, tmat, csum, stream) != hipSuccess) return GDN_ERR_HIP;
   }
 
   gdn::FwdPlan plan;
@@ -284,7 +286,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     plan.cp.hstart = reinterpret_cast<float*>(ws + L.hstart);
     if (!plan.cp.force_correction) {
       StageMark mark(opts, GDN_STAGE_GATE_SCAN, stream);
-      if (gdn::launch_gate_scan(p, P.max_chunks, P.wmax, best, stream) != hipSuccess)
+      if (gdn::launch_gate_scan(p, csum, P.max_chunks, P.wmax, best, stream) != hipSuccess)
         return GDN_ERR_HIP;
     }
     {
@@ -324,7 +326,7 @@ int gdn_chunk_inverse(const void* k, const float* g, const void* beta, const int
         hipSuccess)
       return GDN_ERR_HIP;
   }
-  if (gdn::launch_chunk_inverse(p, t_out, stream) != hipSuccess) return GDN_ERR_HIP;
+  if (gdn::launch_chunk_inverse(p, t_out, nullptr, stream) != hipSuccess) return GDN_ERR_HIP;
   return GDN_OK;
 }
 
@@ -332,8 +334,11 @@ int gdn_gate_scan_workspace_bytes(const gdn_shape* shape, size_t* bytes) {
   int rc = validate_shape(shape);
   if (rc != GDN_OK) return rc;
   if (!bytes) return GDN_ERR_ARG;
+  int64_t chunks = 0;
+  for (int64_t n = 0; n < shape->N; ++n) chunks += seq_chunks(shape, n);
   *bytes = align_up((size_t)(shape->N + 1) * sizeof(int32_t)) +
-           align_up((size_t)shape->N * shape->H * kWindowMaxCap * sizeof(uint32_t));
+           align_up((size_t)shape->N * shape->H * kWindowMaxCap * sizeof(uint32_t)) +
+           align_up((size_t)chunks * shape->H * sizeof(float));
   return GDN_OK;
 }
 
@@ -350,9 +355,13 @@ int gdn_gate_scan(const float* g, const int32_t* cu_seqlens, const gdn_shape* sh
   gdn_gate_scan_workspace_bytes(shape, &need);
   if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)) return GDN_ERR_WORKSPACE;
   const Plan P = make_plan(shape, opts);
-  int32_t* chunk_off = static_cast<int32_t*>(workspace);
-  uint32_t* best = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
-                                               align_up((size_t)(shape->N + 1) * sizeof(int32_t)));
+  char* ws = static_cast<char*>(workspace);
+  const size_t off_best = align_up((size_t)(shape->N + 1) * sizeof(int32_t));
+  const size_t off_csum = off_best + align_up((size_t)shape->N * shape->H * kWindowMaxCap *
+                                              sizeof(uint32_t));
+  int32_t* chunk_off = reinterpret_cast<int32_t*>(ws);
+  uint32_t* best = reinterpret_cast<uint32_t*>(ws + off_best);
+  float* csum = reinterpret_cast<float*>(ws + off_csum);
   gdn::Problem p = make_problem(nullptr, nullptr, nullptr, g, nullptr, nullptr, cu_seqlens, 1.f,
                                 nullptr, nullptr, shape, P.total_chunks);
   const int best_len = p.N * p.H * kWindowMaxCap;
@@ -360,7 +369,9 @@ int gdn_gate_scan(const float* g, const int32_t* cu_seqlens, const gdn_shape* sh
                               best_len, stream) != hipSuccess)
     return GDN_ERR_HIP;
   if (cu_seqlens) p.chunk_off = chunk_off;
-  if (gdn::launch_gate_scan(p, P.max_chunks, P.wmax, best, stream) != hipSuccess) return GDN_ERR_HIP;
+  if (gdn::launch_chunk_gate_sums(p, csum, stream) != hipSuccess) return GDN_ERR_HIP;
+  if (gdn::launch_gate_scan(p, csum, P.max_chunks, P.wmax, best, stream) != hipSuccess)
+    return GDN_ERR_HIP;
   if (gdn::launch_gate_finalize(p, best, P.wmax, P.log_eps - kWindowMargin, window_out, stream) !=
       hipSuccess)
     return GDN_ERR_HIP;

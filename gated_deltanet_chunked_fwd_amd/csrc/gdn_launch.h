@@ -61,12 +61,14 @@ struct FwdPlan {
 hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hipStream_t s);
 hipError_t launch_plan_tables(const int32_t* cu, int N, int seg_chunks, int32_t* chunk_off,
                               int32_t* seg_off, uint32_t* best, int best_len, hipStream_t s);
-hipError_t launch_gate_scan(const Problem& p, int64_t max_chunks, int wmax, uint32_t* best,
-                            hipStream_t s);
+hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s);
+hipError_t launch_gate_scan(const Problem& p, const float* csum, int64_t max_chunks, int wmax,
+                            uint32_t* best, hipStream_t s);
 hipError_t launch_gate_finalize(const Problem& p, const uint32_t* best, int wmax, float thr,
                                 int32_t* out, hipStream_t s);
 hipError_t launch_cp_merge(const Problem& p, const FwdPlan& plan, hipStream_t s);
-hipError_t launch_chunk_inverse(const Problem& p, void* t_out, hipStream_t s);
+// csum (nullable): [total_chunks, H] per-chunk gate sums, written on the side.
+hipError_t launch_chunk_inverse(const Problem& p, void* t_out, float* csum, hipStream_t s);
 hipError_t launch_fused_forward(const Problem& p, const FwdPlan& plan, hipStream_t s);
 
 }  // namespace gdn

@@ -87,7 +87,8 @@ typedef struct gdn_opts {
    * the caller (hipEventCreate).  For every stage that runs, the library records
    * stage_events[2*s] on `stream` just before the stage's launch and
    * stage_events[2*s+1] just after it; events of stages that do not run are left
-   * untouched.  Recording events is the only effect. */
+   * untouched, and NULL entries are skipped (so a caller can time one stage alone).
+   * Recording events is the only effect. */
   hipEvent_t* stage_events;
 } gdn_opts;
 
