@@ -73,17 +73,6 @@ __device__ __forceinline__ typename Mma<E>::frag load_frag(const E* src, bool ok
   return f;
 }
 
-// Four consecutive elements of one row: 8 bytes (bf16) or 16 bytes (fp32).
-__device__ __forceinline__ void store4(bf16* dst, const f32x4& v) {
-  bf16x4 b;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) b[i] = (bf16)v[i];
-  *reinterpret_cast<bf16x4*>(dst) = b;
-}
-__device__ __forceinline__ void store4(float* dst, const f32x4& v) {
-  *reinterpret_cast<f32x4*>(dst) = v;
-}
-
 }  // namespace
 
 template <typename E, int DK>

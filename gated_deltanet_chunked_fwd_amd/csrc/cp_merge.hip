@@ -10,9 +10,12 @@
 // Mapping: one workgroup per (sequence, head, 16 value columns); columns of h are
 // independent.  Wave w owns output rows [32w, 32w+32).  M_j h is one 128x128x16
 // product per step on MFMA; to keep fp32-level accuracy both factors are split
-// into bf16 high and low parts, M h ~= Mh hh + Mh hl + Ml hh.  The running state
-// lives in LDS as bf16 high/low, K-major by column, so a lane's B operand is one
-// 16-byte read.  Heads that take window-lookback starts skip the merge.
+// into bf16 high and low parts, M h ~= Mh hh + Mh hl + Ml hh.  Pass 1 stores M
+// already split (so the merge needs no conversion arithmetic), and the operands
+// of step j+1 (M_{j+1} fragments, S*_{j+1} tiles) are loaded while step j
+// computes: only the MFMA chain through h is serial.  The running state lives in
+// LDS as bf16 high/low, K-major by column, so a lane's B operand is one 16-byte
+// read.  Heads that take window-lookback starts skip the merge.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -52,37 +55,50 @@ __global__ __launch_bounds__(256) void cp_merge_kernel(Problem p, FwdPlan plan) 
   }
   __syncthreads();
 
-  for (int j = 0; j + 1 < segs; ++j) {
+  // operands of one step: M_j fragments (row-major hi / lo blocks) and S*_j tiles
+  struct Ops {
+    bf16x8 mh[RT][NKS], ml[RT][NKS];
+    f32x4 s[RT];
+  };
+  auto load = [&](Ops& o, int j) {
     const int64_t slot = (sg0 + j) * H + h;
-    const float* Mj = plan.cp.mcorr + slot * DK * DK;
+    const bf16* Mh = reinterpret_cast<const bf16*>(plan.cp.mcorr) + slot * 2 * DK * DK;
+    const bf16* Ml = Mh + DK * DK;
     const float* Sj = plan.cp.sstar + slot * DK * dv;
-    f32x4 acc[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int rb = 16 * (RT * wave + t);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[t][i] = Sj[(int64_t)(rb + 4 * q + i) * dv + col + r16];
+      for (int i = 0; i < 4; ++i) o.s[t][i] = Sj[(int64_t)(rb + 4 * q + i) * dv + col + r16];
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const int64_t at = (int64_t)(rb + r16) * DK + 32 * s + 8 * q;
+        o.mh[t][s] = *reinterpret_cast<const bf16x8*>(Mh + at);
+        o.ml[t][s] = *reinterpret_cast<const bf16x8*>(Ml + at);
+      }
     }
+  };
+
+  Ops cur, nxt;
+  load(cur, 0);
+  for (int j = 0; j + 1 < segs; ++j) {
+    if (j + 2 < segs) load(nxt, j + 1);   // in flight during this step
+    f32x4 acc[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[t] = cur.s[t];
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       const bf16x8 bh = lds_frag(sHi, HS, r16, 32 * s, q);
       const bf16x8 bl = lds_frag(sLo, HS, r16, 32 * s, q);
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
-        const int row = 16 * (RT * wave + t) + r16;
-        const f32x8 a = *reinterpret_cast<const f32x8*>(Mj + (int64_t)row * DK + 32 * s + 8 * q);
-        bf16x8 ah, al;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          ah[e] = (bf16)a[e];
-          al[e] = (bf16)(a[e] - (float)ah[e]);
-        }
-        acc[t] = Mma<bf16>::run(ah, bh, acc[t]);
-        acc[t] = Mma<bf16>::run(ah, bl, acc[t]);
-        acc[t] = Mma<bf16>::run(al, bh, acc[t]);
+        acc[t] = Mma<bf16>::run(cur.mh[t][s], bh, acc[t]);
+        acc[t] = Mma<bf16>::run(cur.mh[t][s], bl, acc[t]);
+        acc[t] = Mma<bf16>::run(cur.ml[t][s], bh, acc[t]);
       }
     }
     __syncthreads();  // every wave has read the old state
+    const int64_t slot = (sg0 + j) * H + h;
     float* Hn = plan.cp.hstart + (slot + H) * DK * dv;   // start of segment j+1
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
@@ -98,6 +114,7 @@ __global__ __launch_bounds__(256) void cp_merge_kernel(Problem p, FwdPlan plan) 
       }
     }
     __syncthreads();
+    cur = nxt;
   }
 }
 

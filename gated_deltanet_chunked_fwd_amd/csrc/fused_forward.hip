@@ -21,9 +21,10 @@
 // of chunk c+1 are issued before chunk c is computed), computes P = (QK^T)*Gamma
 // once (tiles split over the waves), and each wave then runs its columns:
 // K^T for the state update and V in accumulator layout come from the row-major
-// tiles through LDS transpose reads; O is staged column-major per wave and
-// stored with 16-byte row writes.  Value columns are independent; only T and P
-// are shared between them.
+// tiles through LDS transpose reads.  O is produced transposed (MFMA operands
+// swapped), so each lane ends with four consecutive value columns of one query
+// row and stores them to HBM directly.  Value columns are independent; only T and
+// P are shared between them.
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -44,7 +45,7 @@ struct FwdCfg {
   // order with a stride of 8 (mod 32) dwords: 16-byte fragment reads and 8-byte
   // transpose reads are then free of bank conflicts on gfx950's LDS.
   static constexpr int KS = BF ? DK + 16 : DK + 4;        // sK, sQ
-  static constexpr int CS = BF ? kChunk + 16 : kChunk + 4; // sT, sP, sKt, sO
+  static constexpr int CS = BF ? kChunk + 16 : kChunk + 4; // sT, sP, sKt
   static constexpr int VS = BF ? BV + 16 : BV + 4;        // sV
   static constexpr bool KT_COPY = BF;  // stage K^T once per chunk instead of per wave
 };
@@ -89,7 +90,7 @@ struct ChunkRegs {
   // to zero in store()).
   __device__ __forceinline__ void load(const E* qb, const E* kb, const E* vb, const E* ts,
                                        const float* gb, const void* betab, bool beta_bf16,
-                                       int len_, const Offsets& of, bool vzero, int tid) {
+                                       int len_, const Offsets& of, int tid) {
     len = len_;
     const bool full = len == kChunk;
 #pragma unroll
@@ -99,13 +100,14 @@ struct ChunkRegs {
       k[j] = *reinterpret_cast<const u32x4*>(kb + o);
       q[j] = *reinterpret_cast<const u32x4*>(qb + o);
     }
-    if (!vzero) {
+    // V is loaded even when it is not used (vzero: masked at store time), so every
+    // path issues the same loads and the compiler's memory-counter waits for older
+    // stores never have to drain these prefetches early.
 #pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const int r = (tid + NTH * j) / VPRV;
-        const int o = (full || r < len) ? of.v[j] : (tid + NTH * j) % VPRV * EPV;
-        v[j] = *reinterpret_cast<const u32x4*>(vb + o);
-      }
+    for (int j = 0; j < NV; ++j) {
+      const int r = (tid + NTH * j) / VPRV;
+      const int o = (full || r < len) ? of.v[j] : (tid + NTH * j) % VPRV * EPV;
+      v[j] = *reinterpret_cast<const u32x4*>(vb + o);
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j) t[j] = reinterpret_cast<const u32x4*>(ts)[tid + NTH * j];
@@ -169,7 +171,6 @@ __global__ __launch_bounds__(64 * NW) void fused_forward_kernel(Problem p, FwdPl
   __shared__ __align__(16) E sT[kChunk * CS];     // tile-order rows
   __shared__ __align__(16) E sP[kChunk * CS];     // tile-order query rows, natural keys
   __shared__ __align__(16) E sV[kChunk * VS];     // natural rows
-  __shared__ __align__(16) E sO[NW][NCW * CS];    // per wave, column-major [col][row]
   __shared__ __align__(16) float sGraw[kChunk], sBraw[kChunk];
   __shared__ __align__(16) float sGam[kChunk], sGamS[kChunk], sDec[kChunk], sBet[kChunk];
 
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(64 * NW) void fused_forward_kernel(Problem p, FwdPl
     const int64_t t0 = (int64_t)c * kChunk;
     const E* ts = Tm + ((si.chunk0 + c) * H + h) * (int64_t)(kChunk * kChunk);
     pf.load(Qb + t0 * row_qk, Kb + t0 * row_qk, Vb + t0 * row_v, ts, Gb + t0 * H,
-            Bb + t0 * H * bsz, p.beta_bf16, min(kChunk, si.len - c * kChunk), offs, mcols, tid);
+            Bb + t0 * H * bsz, p.beta_bf16, min(kChunk, si.len - c * kChunk), offs, tid);
   };
   if (c_start < c_end) issue_loads(c_start);
 
@@ -315,7 +316,8 @@ __global__ __launch_bounds__(64 * NW) void fused_forward_kernel(Problem p, FwdPl
     }
     __syncthreads();
 
-    // ---- X = K h, Y = Q h (first product of each chain starts from zero)
+    // ---- X = K h; Y^T = h^T Q^T (operands swapped: a lane holds four consecutive value
+    //      columns of one query row, the layout of the O store); first products start at zero
     f32x4 X[4][NCT], Y[4][NCT];
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -331,7 +333,7 @@ __global__ __launch_bounds__(64 * NW) void fused_forward_kernel(Problem p, FwdPl
         if constexpr (EMIT) {
           const frag aQ = lds_frag(sQ, KS, 16 * u + r16, 32 * s, q);
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) Y[u][ct] = M::run(aQ, hb[ct], s == 0 ? zero4 : Y[u][ct]);
+          for (int ct = 0; ct < NCT; ++ct) Y[u][ct] = M::run(hb[ct], aQ, s == 0 ? zero4 : Y[u][ct]);
         }
       }
     }
@@ -368,25 +370,25 @@ __global__ __launch_bounds__(64 * NW) void fused_forward_kernel(Problem p, FwdPl
         if constexpr (EMIT) ub[s][ct] = M::pack(U[2 * s][ct], U[2 * s + 1][ct]);
         ubd[s][ct] = M::pack(U[2 * s][ct] * rows4(sDec, 2 * s), U[2 * s + 1][ct] * rows4(sDec, 2 * s + 1));
       }
-    // ---- O = scale (diag(gamma) Y + P U), staged column-major in this wave's sO
-    E* so = sO[wave];
+    // ---- O^T = scale (Y^T diag(gamma) + U^T P^T), stored straight from registers: lane
+    //      (r, q) of tile (u, ct) holds query row prow(u, r), value columns 16 ct + 4q .. +3
     if constexpr (EMIT) {
+      E* ob = Ob + (int64_t)c * kChunk * row_v;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const f32x4 gs4 = rows4(sGamS, u);
+        const int row = prow(u, r16);
+        const float gs = sGamS[row];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) Y[u][ct] = Y[u][ct] * gs4;
+        for (int ct = 0; ct < NCT; ++ct) Y[u][ct] = Y[u][ct] * gs;
 #pragma unroll
         for (int s = 0; s <= (u >> 1); ++s) {
           const frag aP = lds_frag(sP, CS, 16 * u + r16, 32 * s, q);
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) Y[u][ct] = M::run(aP, ub[s][ct], Y[u][ct]);
+          for (int ct = 0; ct < NCT; ++ct) Y[u][ct] = M::run(ub[s][ct], aP, Y[u][ct]);
         }
+        if (row < len) {
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          E* dst = so + (16 * ct + r16) * CS + prow(u, 4 * q);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dst[i] = from_f32<E>(Y[u][ct][i]);
+          for (int ct = 0; ct < NCT; ++ct) store4(ob + row * row_v + 16 * ct + 4 * q, Y[u][ct]);
         }
       }
     }
@@ -405,21 +407,6 @@ __global__ __launch_bounds__(64 * NW) void fused_forward_kernel(Problem p, FwdPl
         for (int ct = 0; ct < NCT; ++ct) hs[t][ct] = M::run(aKt, ubd[s][ct], hs[t][ct]);
       }
     }
-    // ---- O store: lane (j, q) writes 8 consecutive columns of token row 16*rb + j
-    if constexpr (EMIT) {
-      constexpr int NG = NCW / 8;   // 8-column groups per wave
-      E* ob = Ob + (int64_t)c * kChunk * row_v;
-#pragma unroll
-      for (int rr = 0; rr < NG; ++rr) {
-        const int item = rr * 4 + q;
-        const int rb = item / NG, cg8 = item % NG;
-        const int row = 16 * rb + r16;
-        const int supply = 16 * rb + 4 * (r16 & 3);
-        const auto lo = col_read4_storage(so, CS, 8 * cg8, row, supply);
-        const auto hi = col_read4_storage(so, CS, 8 * cg8 + 4, row, supply);
-        if (row < len) store8(ob + row * row_v + 8 * cg8, lo, hi);
-      }
-    }
   };
 
   for (int c = c_start; c < c_end; ++c) {
@@ -428,7 +415,9 @@ __global__ __launch_bounds__(64 * NW) void fused_forward_kernel(Problem p, FwdPl
     // ---- stage chunk c in LDS, then start the loads of chunk c+1
     pf.template store<KS, CS, VS>(sK, sQ, sV, sT, sGraw, sBraw, p.beta_bf16, mcols, tid);
     __syncthreads();
-    if (c + 1 < c_end) issue_loads(c + 1);
+    // after the last chunk this reloads it (unused): the load count per step stays
+    // fixed, which keeps the step free of waits on these loads
+    issue_loads(min(c + 1, c_end - 1));
 
     // ---- gates: every wave scans (lane = chunk row); wave 0 publishes per-row values
     const float G = wave_inclusive_scan(sGraw[lane]);
@@ -446,20 +435,32 @@ __global__ __launch_bounds__(64 * NW) void fused_forward_kernel(Problem p, FwdPl
     __syncthreads();
   }
 
-  // ---- end state: final state (pass 3, last segment), or S* / M (pass 1)
+  // ---- end state: final state (pass 3, last segment), S* (pass 1 value columns), or
+  //      M (pass 1 identity columns) as bf16 high and low parts for the merge's MFMAs
+  if (plan.mode == kPass1 && mcols) {
+    const int64_t slot = sg * H + h;
+    bf16* mhi = reinterpret_cast<bf16*>(plan.cp.mcorr) + slot * 2 * DK * DK;
+    bf16* mlo = mhi + DK * DK;
+    const int mc = col0 - dv + wcol + r16;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = hs[t][ct][i];
+          const bf16 hi = (bf16)x;
+          const int64_t at = (int64_t)prow(t, 4 * q + i) * DK + mc + ct * 16;
+          mhi[at] = hi;
+          mlo[at] = (bf16)(x - (float)hi);
+        }
+    return;
+  }
   float* dst = nullptr;
   int64_t dst_off = 0;
-  int dst_row = dv;
   if (plan.mode == kPass1) {
-    const int64_t slot = sg * H + h;
-    if (mcols) {
-      dst = plan.cp.mcorr;
-      dst_off = slot * DK * DK + (col0 - dv);
-      dst_row = DK;
-    } else {
-      dst = plan.cp.sstar;
-      dst_off = slot * DK * dv + col0;
-    }
+    dst = plan.cp.sstar;
+    dst_off = (sg * H + h) * DK * dv + col0;
   } else if (last_seg && p.hT) {
     dst = p.hT;
     dst_off = (int64_t)nh * DK * dv + col0;
@@ -471,7 +472,7 @@ __global__ __launch_bounds__(64 * NW) void fused_forward_kernel(Problem p, FwdPl
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          dst[dst_off + (int64_t)prow(t, 4 * q + i) * dst_row + wcol + ct * 16 + r16] = hs[t][ct][i];
+          dst[dst_off + (int64_t)prow(t, 4 * q + i) * dv + wcol + ct * 16 + r16] = hs[t][ct][i];
   }
 }
 

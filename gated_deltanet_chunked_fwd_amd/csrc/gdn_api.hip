@@ -167,7 +167,7 @@ Layout layout(const gdn_shape* s, const Plan& P) {
     L.csum = take((size_t)P.total_chunks * s->H * sizeof(float));
     const size_t slots = (size_t)P.total_segs * s->H;
     L.sstar = take(slots * s->dk * s->dv * sizeof(float));
-    L.mcorr = take(slots * s->dk * s->dk * sizeof(float));
+    L.mcorr = take(slots * 2 * s->dk * s->dk * sizeof(uint16_t));   // bf16 hi + lo
     L.hstart = take(slots * s->dk * s->dv * sizeof(float));
   }
   L.total = off;
@@ -282,7 +282,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     plan.cp.thr = P.log_eps - kWindowMargin;
     plan.cp.force_correction = opts ? opts->force_correction : 0;
     plan.cp.sstar = reinterpret_cast<float*>(ws + L.sstar);
-    plan.cp.mcorr = reinterpret_cast<float*>(ws + L.mcorr);
+    plan.cp.mcorr = ws + L.mcorr;
     plan.cp.hstart = reinterpret_cast<float*>(ws + L.hstart);
     if (!plan.cp.force_correction) {
       StageMark mark(opts, GDN_STAGE_GATE_SCAN, stream);

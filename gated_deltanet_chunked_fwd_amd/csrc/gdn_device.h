@@ -176,6 +176,17 @@ __device__ __forceinline__ f32x4 col_read4_storage(const float* M, int stride, i
   return col_read4(M, stride, row0, own_col, supply_col);
 }
 
+// Four consecutive elements of one row from fp32: 8 bytes (bf16) or 16 bytes (fp32).
+__device__ __forceinline__ void store4(bf16* dst, const f32x4& v) {
+  bf16x4 b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = (bf16)v[i];
+  *reinterpret_cast<bf16x4*>(dst) = b;
+}
+__device__ __forceinline__ void store4(float* dst, const f32x4& v) {
+  *reinterpret_cast<f32x4*>(dst) = v;
+}
+
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 template <typename E>

@@ -35,7 +35,8 @@ struct CpBuffers {
   float thr;                // window threshold: log_eps - margin
   int force_correction;     // 1: every split head uses the wrong-start correction
   float* sstar;             // [total_segs, H, dk, dv] wrong-start (zero-start) segment end states
-  float* mcorr;             // [total_segs, H, dk, dk] segment transition matrices
+  void* mcorr;              // [total_segs, H] x {hi, lo} x [dk, dk] bf16: segment transition
+                            // matrices M split as M = hi + lo (row-major, hi block first)
   float* hstart;            // [total_segs, H, dk, dv] true segment start states
 };
 
