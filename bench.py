@@ -15,9 +15,9 @@ library, on the launch stream, around that launch), which gives its live mean
 duration for the roofline at the cost of one event pair per step.
 
 Roofline (dominant kernel = the stage with the largest mean time):
-  achieved = algorithmic bytes of that kernel per launch / its mean duration,
-  bytes per token-head = 2*(dk+dv)*e_qkv + e_g + e_beta, plus the fp32 states it
-  reads/writes; peak = 8000 GB/s.
+  achieved = algorithmic bytes of that kernel per launch (stage_bytes(): for the
+  pass that writes o, bytes per token-head = 2*(dk+dv)*e_qkv + e_g + e_beta plus
+  the fp32 states) / its live mean duration; peak = 8000 GB/s.
 traffic = HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE (from
 profiles/traffic_fused_forward.json) if those counters were taken on the current
 kernel source, else null.
@@ -90,12 +90,51 @@ class Hip:
 
 
 def algorithmic_bytes(spec, n_seqs, has_h0, has_hT):
+    """Compulsory HBM bytes of the whole path: q, k, v, g, beta in; o out; fp32
+    states in/out.  This is also the per-launch figure of the pass that writes o
+    (fused_forward), which reads and writes exactly these tensors."""
     e = 2 if spec.dtype == "bf16" else 4
     eb = 2 if (spec.beta_dtype or spec.dtype) == "bf16" else 4
     th = spec.B * spec.T * spec.H
     per_th = 2 * (spec.dk + spec.dv) * e + 4 + eb
     state = n_seqs * spec.H * spec.dk * spec.dv * 4
     return th * per_th + state * (int(has_h0) + int(has_hT))
+
+
+def stage_bytes(stage, spec, lengths, seg_chunks, windows, has_h0, has_hT):
+    """Algorithmic bytes one launch of `stage` must move, from the tensors it reads
+    and writes by definition (intermediates are counted where a stage's job is to
+    produce or consume them: T for the chunk inverse, S*/M/h_start for the split).
+      chunk_inverse: k, g, beta per token-head in; T (64 x 64) per chunk-head out.
+      cp_pass1 / cp_merge: only (sequence, head) pairs without a lookback window
+        (windows[n][h] == 0) and only their non-last segments.  Pass 1 reads k, v,
+        g, beta of those segments and writes S* (fp32) and M (2 x bf16) per segment;
+        the merge reads M and S* and writes h_start per segment boundary.
+      gate_scan: the chunk gate sums (fp32 per chunk-head).
+      fused_forward: the compulsory bytes of the path."""
+    C = 64
+    e = 2 if spec.dtype == "bf16" else 4
+    eb = 2 if (spec.beta_dtype or spec.dtype) == "bf16" else 4
+    H, dk, dv = spec.H, spec.dk, spec.dv
+    chunks = [(n + C - 1) // C for n in lengths]
+    if stage == "chunk_inverse":
+        return sum(lengths) * H * (dk * e + 4 + eb) + sum(chunks) * H * C * C * e
+    if stage == "gate_scan":
+        return sum(chunks) * H * 4
+    if stage in ("cp_pass1", "cp_merge"):
+        total = 0
+        for n, (ln, nch) in enumerate(zip(lengths, chunks)):
+            segs = max(1, -(-nch // seg_chunks))
+            for h in range(H):
+                if windows is None or windows[n][h] != 0 or segs < 2:
+                    continue
+                toks = min(ln, (segs - 1) * seg_chunks * C)
+                if stage == "cp_pass1":
+                    total += toks * ((dk + dv) * e + 4 + eb) + (segs - 1) * (dk * dv * 4 + 2 * dk * dk * 2)
+                else:
+                    total += (segs - 1) * (2 * dk * dk * 2 + 2 * dk * dv * 4)
+        return total
+    return algorithmic_bytes(spec, len(lengths), has_h0, has_hT)
 
 
 def algorithmic_flops(spec):
@@ -237,8 +276,15 @@ def main():
     dom_ms = sum(dom_ms_list) / len(dom_ms_list)
     has_h0 = d["h0"] is not None
     alg_bytes = algorithmic_bytes(spec, N, has_h0, True)
+    cu_host = inp["cu_seqlens"]
+    lengths = ([spec.T] * spec.B if cu_host is None
+               else [int(cu_host[i + 1] - cu_host[i]) for i in range(N)])
+    windows = None
+    if seg_chunks < max((n + 63) // 64 for n in lengths):
+        windows = binding.gate_scan(d["g"], d["cu_seqlens"], cu_host).cpu().tolist()
+    dom_bytes = stage_bytes(dom, spec, lengths, seg_chunks, windows, has_h0, True)
     flops = algorithmic_flops(spec)
-    achieved = alg_bytes / (dom_ms * 1e-3) / 1e9
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     ksrc = os.path.join(ROOT, "gated_deltanet_chunked_fwd_amd", "csrc", "fused_forward.hip")
     traffic = traffic_for(ksrc) if dom == "fused_forward" else None
     mfma_peak = BF16_PEAK_TFLOPS if spec.dtype == "bf16" else F32_PEAK_TFLOPS
@@ -261,7 +307,7 @@ def main():
                    "segment_chunks": seg_chunks, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes": alg_bytes, "kernel_ms": dom_ms},
+                     "algorithmic_bytes": dom_bytes, "kernel_ms": dom_ms},
         "path": {"hbm_frac": alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                  "mfma_frac": flops / (ms * 1e-3) / 1e12 / mfma_peak,
                  "algorithmic_flops": flops, "stage_ms": st_mean,

@@ -156,7 +156,9 @@ __device__ __forceinline__ void p_pair(int i, int& qt, int& kt) {
   else { qt = 2 + ((i - 4) >> 2); kt = (i - 4) & 3; }
 }
 
-template <typename E, int DK, int NCW, int NW>
+// PASS (kPass3 / kPass1) is a template parameter so that each pass compiles to
+// its own straight-line code and shows up as its own kernel in profiles.
+template <typename E, int DK, int NCW, int NW, int PASS>
 __global__ __launch_bounds__(64 * NW) void fused_forward_kernel(Problem p, FwdPlan plan) {
   using Cfg = FwdCfg<E, DK, NCW, NW>;
   using M = Mma<E>;
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(64 * NW) void fused_forward_kernel(Problem p, FwdPl
   enum { kZero, kH0, kBuf, kEye };
   int init = kZero, c_start = c_begin, c_out = c_begin;
   bool mcols = false;   // pass 1: this block carries the transition-matrix columns
-  if (plan.mode == kPass1) {
+  if constexpr (PASS == kPass1) {
     if (W > 0 || last_seg) return;     // window heads and last segments need no pass 1
     mcols = col0 >= dv;
     init = mcols ? kEye : kZero;
@@ -437,7 +439,7 @@ __global__ __launch_bounds__(64 * NW) void fused_forward_kernel(Problem p, FwdPl
 
   // ---- end state: final state (pass 3, last segment), S* (pass 1 value columns), or
   //      M (pass 1 identity columns) as bf16 high and low parts for the merge's MFMAs
-  if (plan.mode == kPass1 && mcols) {
+  if (PASS == kPass1 && mcols) {
     const int64_t slot = sg * H + h;
     bf16* mhi = reinterpret_cast<bf16*>(plan.cp.mcorr) + slot * 2 * DK * DK;
     bf16* mlo = mhi + DK * DK;
@@ -458,7 +460,7 @@ __global__ __launch_bounds__(64 * NW) void fused_forward_kernel(Problem p, FwdPl
   }
   float* dst = nullptr;
   int64_t dst_off = 0;
-  if (plan.mode == kPass1) {
+  if constexpr (PASS == kPass1) {
     dst = plan.cp.sstar;
     dst_off = (sg * H + h) * DK * dv + col0;
   } else if (last_seg && p.hT) {
@@ -476,31 +478,37 @@ __global__ __launch_bounds__(64 * NW) void fused_forward_kernel(Problem p, FwdPl
   }
 }
 
-template <typename E, int DK>
+template <typename E, int DK, int PASS>
 static void launch_dk(const Problem& p, const FwdPlan& plan, hipStream_t s) {
   // pass 1 also runs dk transition-matrix columns after the dv value columns
-  const int cols = plan.mode == kPass1 ? p.dv + DK : p.dv;
+  const int cols = PASS == kPass1 ? p.dv + DK : p.dv;
   if constexpr (sizeof(E) == 2) {
     // 128 columns per workgroup as 8 waves x 16 columns: two waves per SIMD
     if (p.dv % 128 == 0 && cols % 128 == 0 && plan.value_block != 64) {
       dim3 grid((unsigned)plan.units, (unsigned)(cols / 128));
-      fused_forward_kernel<E, DK, 16, 8><<<grid, 512, 0, s>>>(p, plan);
+      fused_forward_kernel<E, DK, 16, 8, PASS><<<grid, 512, 0, s>>>(p, plan);
       return;
     }
   }
   // 64 columns per workgroup as 4 waves x 16 columns (fp32 tiles only fit LDS this way)
   dim3 grid((unsigned)plan.units, (unsigned)(cols / 64));
-  fused_forward_kernel<E, DK, 16, 4><<<grid, 256, 0, s>>>(p, plan);
+  fused_forward_kernel<E, DK, 16, 4, PASS><<<grid, 256, 0, s>>>(p, plan);
+}
+
+template <typename E, int DK>
+static void launch_pass(const Problem& p, const FwdPlan& plan, hipStream_t s) {
+  if (plan.mode == kPass1) launch_dk<E, DK, kPass1>(p, plan, s);
+  else launch_dk<E, DK, kPass3>(p, plan, s);
 }
 
 hipError_t launch_fused_forward(const Problem& p, const FwdPlan& plan, hipStream_t s) {
   if (plan.units == 0) return hipSuccess;
   if (p.qkv_bf16) {
-    if (p.dk == 128) launch_dk<bf16, 128>(p, plan, s);
-    else launch_dk<bf16, 64>(p, plan, s);
+    if (p.dk == 128) launch_pass<bf16, 128>(p, plan, s);
+    else launch_pass<bf16, 64>(p, plan, s);
   } else {
-    if (p.dk == 128) launch_dk<float, 128>(p, plan, s);
-    else launch_dk<float, 64>(p, plan, s);
+    if (p.dk == 128) launch_pass<float, 128>(p, plan, s);
+    else launch_pass<float, 64>(p, plan, s);
   }
   return hipGetLastError();
 }
