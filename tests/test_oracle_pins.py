@@ -8,6 +8,7 @@ sliding-window sections) is S_t = alpha_t S_{t-1}(I - beta_t k_t k_t^T) + beta_t
 o_t = scale S_t q_t, alpha = exp(g), state exchanged K-major (h = S^T).
 """
 import math
+import os
 from fractions import Fraction as Fr
 
 import numpy as np
@@ -345,3 +346,36 @@ def test_window_decision_hand_cases():
     assert gate.window_chunks(g, log_eps=le) == 2
     # w_max caps the answer
     assert gate.window_chunks(np.full(64 * 40, -0.01), log_eps=le, w_max=16) == 0
+
+
+def _load_worked_example():
+    path = os.path.join(os.path.dirname(__file__), "golden", "worked_example_dk2.txt")
+    toks, final = [], None
+    for line in open(path):
+        f = line.split()
+        if not f or f[0].startswith("#"):
+            continue
+        if f[0] == "token":
+            toks.append([float(x) for x in f[1:]])
+        elif f[0] == "final":
+            final = np.array([float(x) for x in f[1:]]).reshape(2, 2)
+    return np.array(toks), final
+
+
+def test_golden_worked_example():
+    """Both oracles reproduce the hand-worked 3-token example in tests/golden."""
+    toks, final = _load_worked_example()
+    T = len(toks)
+    k = toks[:, 1:3].reshape(1, T, 1, 2)
+    v = toks[:, 3:5].reshape(1, T, 1, 2)
+    q = toks[:, 5:7].reshape(1, T, 1, 2)
+    beta = toks[:, 7].reshape(1, T, 1)
+    g = np.log(toks[:, 8]).reshape(1, T, 1)
+    o_ref = toks[:, 9:11]
+    for fn in (token.token_recurrence, token.token_recurrence_numpy):
+        o, hT = fn(q, k, v, g, beta, None, scale=1.0)
+        assert np.allclose(o[0, :, 0], o_ref, rtol=0, atol=1e-12), o
+        assert np.allclose(hT[0, 0], final, rtol=0, atol=1e-12), hT
+    o, hT = chunked.chunked_forward(q, k, v, g, beta, None, scale=1.0)
+    assert np.allclose(o[0, :, 0], o_ref, rtol=0, atol=1e-12)
+    assert np.allclose(hT[0, 0], final, rtol=0, atol=1e-12)
