@@ -54,6 +54,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-split", type=int, default=0)
     ap.add_argument("--value-block", type=int, default=0)
+    ap.add_argument("--segment-chunks", type=int, default=0, help="force the split length (0: planner)")
     return ap.parse_args()
 
 
@@ -203,8 +204,10 @@ def main():
     hip = Hip()
     stage_ev = hip.events(2 * binding.GDN_NUM_STAGES)
     opts_all = binding.make_opts(no_split=args.no_split, value_block=args.value_block,
+                                 force_segment_chunks=args.segment_chunks,
                                  stage_events=ctypes.cast(stage_ev, ctypes.c_void_p))
-    opts = binding.make_opts(no_split=args.no_split, value_block=args.value_block)
+    opts = binding.make_opts(no_split=args.no_split, value_block=args.value_block,
+                             force_segment_chunks=args.segment_chunks)
     ws = torch.empty(max(binding.workspace_bytes(d["q"], d["v"], d["beta"], d["cu_seqlens"],
                                                  inp["cu_seqlens"], opts), 1),
                      dtype=torch.uint8, device=dev)
@@ -246,6 +249,7 @@ def main():
     dom_ev[2 * dom_idx] = stage_ev[2 * dom_idx]
     dom_ev[2 * dom_idx + 1] = stage_ev[2 * dom_idx + 1]
     opts_dom = binding.make_opts(no_split=args.no_split, value_block=args.value_block,
+                                 force_segment_chunks=args.segment_chunks,
                                  stage_events=ctypes.cast(dom_ev, ctypes.c_void_p))
 
     step_ms, dom_ms_list = [], []

@@ -47,7 +47,7 @@ struct FwdCfg {
   static constexpr int KS = BF ? DK + 16 : DK + 4;        // sK, sQ
   static constexpr int CS = BF ? kChunk + 16 : kChunk + 4; // sT, sP, sKt
   static constexpr int VS = BF ? BV + 16 : BV + 4;        // sV
-  static constexpr bool KT_COPY = BF;  // stage K^T once per chunk instead of per wave
+  static constexpr bool KT_COPY = BF && NW == 8;  // stage K^T once per chunk instead of per wave
 };
 
 // One chunk's inputs held in registers between the global loads and the LDS
@@ -55,7 +55,8 @@ struct FwdCfg {
 // Nothing touches the loaded registers until store(): masking of rows past the
 // chunk end (zero there; beta = g = 0) and the beta conversion happen at store
 // time, so no wait for the loads is forced before the chunk's compute.
-template <typename E, int DK, int BV, int NTH>
+// WITH_Q: pass 1 produces no output, so it neither loads nor stages Q.
+template <typename E, int DK, int BV, int NTH, bool WITH_Q>
 struct ChunkRegs {
   static constexpr int EPV = 16 / (int)sizeof(E);
   static constexpr int VPRK = DK / EPV, VPRV = BV / EPV, VPRT = kChunk / EPV;
@@ -98,7 +99,7 @@ struct ChunkRegs {
       const int r = (tid + NTH * j) / VPRK;
       const int o = (full || r < len) ? of.k[j] : (tid + NTH * j) % VPRK * EPV;
       k[j] = *reinterpret_cast<const u32x4*>(kb + o);
-      q[j] = *reinterpret_cast<const u32x4*>(qb + o);
+      if constexpr (WITH_Q) q[j] = *reinterpret_cast<const u32x4*>(qb + o);
     }
     // V is loaded even when it is not used (vzero: masked at store time), so every
     // path issues the same loads and the compiler's memory-counter waits for older
@@ -127,7 +128,7 @@ struct ChunkRegs {
       const bool ok = r < len;
       const int lr = tord(r);
       *reinterpret_cast<u32x4*>(sK + lr * KS + cv * EPV) = ok ? k[j] : zero;
-      *reinterpret_cast<u32x4*>(sQ + lr * KS + cv * EPV) = ok ? q[j] : zero;
+      if constexpr (WITH_Q) *reinterpret_cast<u32x4*>(sQ + lr * KS + cv * EPV) = ok ? q[j] : zero;
     }
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
@@ -159,7 +160,7 @@ __device__ __forceinline__ void p_pair(int i, int& qt, int& kt) {
 // PASS (kPass3 / kPass1) is a template parameter so that each pass compiles to
 // its own straight-line code and shows up as its own kernel in profiles.
 template <typename E, int DK, int NCW, int NW, int PASS>
-__global__ __launch_bounds__(64 * NW) void fused_forward_kernel(Problem p, FwdPlan plan) {
+__global__ __launch_bounds__(64 * NW, 2) void fused_forward_kernel(Problem p, FwdPlan plan) {
   using Cfg = FwdCfg<E, DK, NCW, NW>;
   using M = Mma<E>;
   using frag = typename M::frag;
@@ -180,10 +181,19 @@ __global__ __launch_bounds__(64 * NW) void fused_forward_kernel(Problem p, FwdPl
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar table reads
   const int r16 = lane & 15, q = lane >> 4;
   const int H = p.H, dv = p.dv;
-  const int col0 = blockIdx.y * BV;        // first value column of the workgroup
+  // XCD-aware decode of the 1-D grid: workgroups are dealt to the 8 XCDs round-robin
+  // by id, so every column block of one unit gets id = unit (mod 8) and the unit's
+  // K, T (and shared V) reads are served by one XCD's L2.  Padding ids past the last
+  // unit exit at once.
+  const int64_t bid = blockIdx.x;
+  const int ncb = ((PASS == kPass1) ? dv + DK : dv) / BV;   // column blocks per unit
+  const int64_t rest = bid >> 3;
+  const int cb = (int)(rest % ncb);
+  const int64_t unit = (rest / ncb) * 8 + (bid & 7);
+  if (unit >= plan.units) return;
+  const int col0 = cb * BV;                // first value column of the workgroup
   const int wcol = wave * NCW;             // wave's first column inside the block
 
-  const int64_t unit = blockIdx.x;
   const int h = (int)(unit % H);
   const int64_t sg = unit / H;             // global segment index
   int n, seg;
@@ -255,7 +265,7 @@ __global__ __launch_bounds__(64 * NW) void fused_forward_kernel(Problem p, FwdPl
         }
   }
 
-  using Stage = ChunkRegs<E, DK, BV, Cfg::NT>;
+  using Stage = ChunkRegs<E, DK, BV, Cfg::NT, PASS == kPass3>;
   Stage pf;
   typename Stage::Offsets offs;
   offs.init(row_qk, row_v, H, tid);
@@ -478,21 +488,26 @@ __global__ __launch_bounds__(64 * NW) void fused_forward_kernel(Problem p, FwdPl
   }
 }
 
+// 1-D grid of ceil(units / 8) * 8 * column blocks (see the decode in the kernel).
 template <typename E, int DK, int PASS>
 static void launch_dk(const Problem& p, const FwdPlan& plan, hipStream_t s) {
   // pass 1 also runs dk transition-matrix columns after the dv value columns
   const int cols = PASS == kPass1 ? p.dv + DK : p.dv;
+  const int64_t groups = (plan.units + 7) / 8;
   if constexpr (sizeof(E) == 2) {
-    // 128 columns per workgroup as 8 waves x 16 columns: two waves per SIMD
-    if (p.dv % 128 == 0 && cols % 128 == 0 && plan.value_block != 64) {
-      dim3 grid((unsigned)plan.units, (unsigned)(cols / 128));
-      fused_forward_kernel<E, DK, 16, 8, PASS><<<grid, 512, 0, s>>>(p, plan);
+    // 128 columns per workgroup as 8 waves x 16 columns: two waves per SIMD.  Pass 1
+    // always takes 64-column workgroups: both shapes reach the same throughput per CU,
+    // and pass 1 usually runs few (sequence, head) pairs, so the narrower blocks
+    // spread its units over twice as many CUs.
+    if (PASS == kPass3 && p.dv % 128 == 0 && cols % 128 == 0 && plan.value_block != 64) {
+      const int ncb = cols / 128;
+      fused_forward_kernel<E, DK, 16, 8, PASS><<<(unsigned)(groups * 8 * ncb), 512, 0, s>>>(p, plan);
       return;
     }
   }
   // 64 columns per workgroup as 4 waves x 16 columns (fp32 tiles only fit LDS this way)
-  dim3 grid((unsigned)plan.units, (unsigned)(cols / 64));
-  fused_forward_kernel<E, DK, 16, 4, PASS><<<grid, 256, 0, s>>>(p, plan);
+  const int ncb = cols / 64;
+  fused_forward_kernel<E, DK, 16, 4, PASS><<<(unsigned)(groups * 8 * ncb), 256, 0, s>>>(p, plan);
 }
 
 template <typename E, int DK>
