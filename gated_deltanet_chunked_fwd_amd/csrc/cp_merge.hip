@@ -11,9 +11,10 @@
 // independent.  Wave w owns output rows [32w, 32w+32).  M_j h is one 128x128x16
 // product per step on MFMA; to keep fp32-level accuracy both factors are split
 // into bf16 high and low parts, M h ~= Mh hh + Mh hl + Ml hh.  Pass 1 stores M
-// already split (so the merge needs no conversion arithmetic), and the operands
-// of step j+1 (M_{j+1} fragments, S*_{j+1} tiles) are loaded while step j
-// computes: only the MFMA chain through h is serial.  The running state lives in
+// already split, in operand order (mfrag_offset: one 1 KB contiguous block per
+// wave and fragment, so the loads coalesce fully), and the operands
+// of step j+2 (M fragments, S* tiles) are loaded while step j computes: only the
+// MFMA chain through h is serial.  The running state lives in
 // LDS as bf16 high/low, K-major by column, so a lane's B operand is one 16-byte
 // read.  Heads that take window-lookback starts skip the merge.
 #include "gdn_device.h"
@@ -72,17 +73,19 @@ __global__ __launch_bounds__(256) void cp_merge_kernel(Problem p, FwdPlan plan) 
       for (int i = 0; i < 4; ++i) o.s[t][i] = Sj[(int64_t)(rb + 4 * q + i) * dv + col + r16];
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        const int64_t at = (int64_t)(rb + r16) * DK + 32 * s + 8 * q;
+        const int64_t at = ((int64_t)((RT * wave + t) * NKS + s) * 64 + lane) * 8;   // mfrag_offset order
         o.mh[t][s] = *reinterpret_cast<const bf16x8*>(Mh + at);
         o.ml[t][s] = *reinterpret_cast<const bf16x8*>(Ml + at);
       }
     }
   };
 
-  Ops cur, nxt;
-  load(cur, 0);
-  for (int j = 0; j + 1 < segs; ++j) {
-    if (j + 2 < segs) load(nxt, j + 1);   // in flight during this step
+  // three operand sets in flight: step j computes with set j % 3 while the loads of
+  // step j + 2 land in the set step j - 1 used (load counts are the same every step,
+  // the index is clamped at the end, so no step waits on loads it does not need)
+  const int steps = segs - 1;
+  auto body = [&](const Ops& cur, Ops& far, int j) {
+    load(far, min(j + 2, steps - 1));
     f32x4 acc[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) acc[t] = cur.s[t];
@@ -114,8 +117,18 @@ __global__ __launch_bounds__(256) void cp_merge_kernel(Problem p, FwdPlan plan) 
       }
     }
     __syncthreads();
-    cur = nxt;
+  };
+  Ops o0, o1, o2;
+  load(o0, 0);
+  load(o1, min(1, steps - 1));
+  int j = 0;
+  for (; j + 3 <= steps; j += 3) {   // no conditions inside: every path issues the same loads
+    body(o0, o2, j);
+    body(o1, o0, j + 1);
+    body(o2, o1, j + 2);
   }
+  if (j < steps) body(o0, o2, j);
+  if (j + 1 < steps) body(o1, o0, j + 1);
 }
 
 hipError_t launch_cp_merge(const Problem& p, const FwdPlan& plan, hipStream_t s) {

@@ -27,6 +27,13 @@
 // P are shared between them.
 #include <type_traits>
 
+#ifndef GDN_KT_COPY
+#define GDN_KT_COPY 0
+#endif
+#ifndef GDN_P_FIRST
+#define GDN_P_FIRST 1
+#endif
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -45,9 +52,8 @@ struct FwdCfg {
   // order with a stride of 8 (mod 32) dwords: 16-byte fragment reads and 8-byte
   // transpose reads are then free of bank conflicts on gfx950's LDS.
   static constexpr int KS = BF ? DK + 16 : DK + 4;        // sK, sQ
-  static constexpr int CS = BF ? kChunk + 16 : kChunk + 4; // sT, sP, sKt
+  static constexpr int CS = BF ? kChunk + 16 : kChunk + 4; // sT, sP
   static constexpr int VS = BF ? BV + 16 : BV + 4;        // sV
-  static constexpr bool KT_COPY = BF && NW == 8;  // stage K^T once per chunk instead of per wave
 };
 
 // One chunk's inputs held in registers between the global loads and the LDS
@@ -119,8 +125,8 @@ struct ChunkRegs {
   }
 
   template <int KS, int CS, int VS>
-  __device__ __forceinline__ void store(E* sK, E* sQ, E* sV, E* sT, float* sG, float* sB,
-                                        bool beta_bf16, bool vzero, int tid) const {
+  __device__ __forceinline__ void store(E* sK, E* sQ, E* sV, E* sT, float* sB, bool beta_bf16,
+                                        bool vzero, int tid) const {
     const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
@@ -141,10 +147,8 @@ struct ChunkRegs {
       *reinterpret_cast<u32x4*>(sT + tord(r) * CS + cv * EPV) = t[j];
     }
     if (tid < kChunk) {
-      const bool ok = tid < len;
-      sG[tid] = ok ? g : 0.f;
       const float bf = beta_bf16 ? __uint_as_float(b << 16) : __uint_as_float(b);
-      sB[tid] = ok ? bf : 0.f;
+      sB[tid] = tid < len ? bf : 0.f;
     }
   }
 };
@@ -160,22 +164,25 @@ __device__ __forceinline__ void p_pair(int i, int& qt, int& kt) {
 // PASS (kPass3 / kPass1) is a template parameter so that each pass compiles to
 // its own straight-line code and shows up as its own kernel in profiles.
 template <typename E, int DK, int NCW, int NW, int PASS>
-__global__ __launch_bounds__(64 * NW, 2) void fused_forward_kernel(Problem p, FwdPlan plan) {
+__global__ __launch_bounds__(64 * NW, (NW == 4 && PASS == kPass3) ? 1 : 2) void fused_forward_kernel(Problem p,
+                                                                                      FwdPlan plan) {
   using Cfg = FwdCfg<E, DK, NCW, NW>;
   using M = Mma<E>;
   using frag = typename M::frag;
   constexpr int BV = Cfg::BV, NCT = Cfg::NCT, NKT = Cfg::NKT, NKS = Cfg::NKS;
   constexpr int KS = Cfg::KS, CS = Cfg::CS, VS = Cfg::VS;
 
-  constexpr bool KT_COPY = Cfg::KT_COPY;
+  constexpr bool OUT = PASS == kPass3;
   __shared__ __align__(16) E sK[kChunk * KS];     // tile-order rows
-  __shared__ __align__(16) E sQ[kChunk * KS];     // tile-order rows
-  __shared__ __align__(16) E sKt[KT_COPY ? DK * CS : 8];  // K^T, tile-order dk rows
+  __shared__ __align__(16) E sQ[OUT ? kChunk * KS : 8];  // tile-order rows
   __shared__ __align__(16) E sT[kChunk * CS];     // tile-order rows
-  __shared__ __align__(16) E sP[kChunk * CS];     // tile-order query rows, natural keys
+  // P of chunks c and c-1 (O of a chunk is formed during the next chunk): tile-order
+  // query rows, natural keys
+  __shared__ __align__(16) E sP[OUT ? 2 : 1][OUT ? kChunk * CS : 8];
   __shared__ __align__(16) E sV[kChunk * VS];     // natural rows
-  __shared__ __align__(16) float sGraw[kChunk], sBraw[kChunk];
-  __shared__ __align__(16) float sGam[kChunk], sGamS[kChunk], sDec[kChunk], sBet[kChunk];
+  constexpr bool KT_COPY = GDN_KT_COPY && sizeof(E) == 2 && NW == 8 && OUT;
+  __shared__ __align__(16) E sKt[KT_COPY ? DK * CS : 8];
+  __shared__ __align__(16) float sG[kChunk], sGam[kChunk], sGamS[kChunk], sDec[kChunk], sBet[kChunk];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar table reads
@@ -282,36 +289,65 @@ __global__ __launch_bounds__(64 * NW, 2) void fused_forward_kernel(Problem p, Fw
     return *reinterpret_cast<const f32x4*>(v + prow(u, 4 * q));
   };
 
-  // One chunk after staging; EMIT (compile-time) selects whether O is produced, so
-  // each variant is straight-line code.
-  auto step = [&](auto emit_tag, int c, int len, float G, float gC) {
-    constexpr bool EMIT = decltype(emit_tag)::value;
-    // ---- P = scale (Q K^T) * Gamma: rows = queries in tile order, columns = keys in
-    //      natural order; computed as P^T = K Q^T so a lane holds four consecutive keys
-    if constexpr (EMIT) {
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  // O of a chunk is completed during the next chunk (after its first barrier), from
+  // these registers and that chunk's P: Yp = scale diag(gamma) Q h (transposed
+  // tiles), ubp = U packed as MFMA operands.
+  f32x4 Yp[4][NCT];
+  frag ubp[2][NCT];
+  auto emit_o = [&](int c, int len) {
+    E* ob = Ob + (int64_t)c * kChunk * row_v;
+    const E* sp = sP[c & 1];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int s = 0; s <= (u >> 1); ++s) {
+        const frag aP = lds_frag(sp, CS, 16 * u + r16, 32 * s, q);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) Yp[u][ct] = M::run(ubp[s][ct], aP, Yp[u][ct]);
+      }
+      const int row = prow(u, r16);
+      if (row < len) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) store4(ob + row * row_v + 16 * ct + 4 * q, Yp[u][ct]);
+      }
+    }
+  };
+
+  auto pstep = [&](int c) {
+    // ---- P = scale (Q K^T) * Gamma for this chunk's O (formed during the next chunk):
+    //      rows = queries in tile order, columns = keys in natural order; computed as
+    //      P^T = K Q^T so a lane holds four consecutive keys
+    {
+      E* sp = sP[c & 1];
 #pragma unroll
       for (int pt = 0; pt < (12 + NW - 1) / NW; ++pt) {
         const int pi = wave + NW * pt;
         if (pi < 12) {
           int qt, kt;
           p_pair(pi, qt, kt);
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          f32x4 acc = zero4;
 #pragma unroll
           for (int s = 0; s < NKS; ++s)
             acc = M::run(lds_frag(sK, KS, 16 * kt + r16, 32 * s, q),
                          lds_frag(sQ, KS, 16 * qt + r16, 32 * s, q), acc);
           const int qrow = prow(qt, r16), key0 = prow(kt, 4 * q);
-          const float Gq = __shfl(G, qrow, 64);
-          E* dst = sP + (16 * qt + r16) * CS + key0;
+          const float Gq = sG[qrow];
+          const f32x4 Gk = *reinterpret_cast<const f32x4*>(sG + key0);
+          E* dst = sp + (16 * qt + r16) * CS + key0;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float Gk = __shfl(G, key0 + i, 64);
-            dst[i] = from_f32<E>(key0 + i <= qrow ? p.scale * acc[i] * fast_exp(Gq - Gk) : 0.f);
-          }
+          for (int i = 0; i < 4; ++i)
+            dst[i] = from_f32<E>(key0 + i <= qrow ? p.scale * acc[i] * fast_exp(Gq - Gk[i]) : 0.f);
         }
       }
     }
-    // ---- K^T for the state update, staged once: wave w transposes its dk tiles
+  };
+
+  // One chunk after staging; EMIT (compile-time) selects whether O is produced, so
+  // each variant is straight-line code.
+  auto step = [&](auto emit_tag, int c, float gC) {
+    constexpr bool EMIT = decltype(emit_tag)::value;
+    if constexpr (EMIT && GDN_P_FIRST) pstep(c);
     if constexpr (KT_COPY) {
       constexpr int TPW = (NKT + NW - 1) / NW;
 #pragma unroll
@@ -325,13 +361,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fused_forward_kernel(Problem p, Fw
                 col_frag(sK, KS, 32 * s + 4 * q, 32 * s + 16 + 4 * q, own, supply);
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
-
     // ---- X = K h; Y^T = h^T Q^T (operands swapped: a lane holds four consecutive value
     //      columns of one query row, the layout of the O store); first products start at zero
-    f32x4 X[4][NCT], Y[4][NCT];
-    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 X[4][NCT];
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       frag hb[NCT];
@@ -345,8 +379,16 @@ __global__ __launch_bounds__(64 * NW, 2) void fused_forward_kernel(Problem p, Fw
         if constexpr (EMIT) {
           const frag aQ = lds_frag(sQ, KS, 16 * u + r16, 32 * s, q);
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) Y[u][ct] = M::run(hb[ct], aQ, s == 0 ? zero4 : Y[u][ct]);
+          for (int ct = 0; ct < NCT; ++ct) Yp[u][ct] = M::run(hb[ct], aQ, s == 0 ? zero4 : Yp[u][ct]);
         }
+      }
+    }
+    if constexpr (EMIT) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float gs = sGamS[prow(u, r16)];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) Yp[u][ct] = Yp[u][ct] * gs;
       }
     }
     // ---- W = diag(beta) (V - diag(gamma) X), in place; V read in accumulator layout
@@ -374,37 +416,15 @@ __global__ __launch_bounds__(64 * NW, 2) void fused_forward_kernel(Problem p, Fw
         for (int ct = 0; ct < NCT; ++ct) U[u][ct] = M::run(aT, wb[s][ct], s == 0 ? zero4 : U[u][ct]);
       }
     }
-    frag ub[2][NCT], ubd[2][NCT];
+    frag ubd[2][NCT];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        if constexpr (EMIT) ub[s][ct] = M::pack(U[2 * s][ct], U[2 * s + 1][ct]);
+        if constexpr (EMIT) ubp[s][ct] = M::pack(U[2 * s][ct], U[2 * s + 1][ct]);
         ubd[s][ct] = M::pack(U[2 * s][ct] * rows4(sDec, 2 * s), U[2 * s + 1][ct] * rows4(sDec, 2 * s + 1));
       }
-    // ---- O^T = scale (Y^T diag(gamma) + U^T P^T), stored straight from registers: lane
-    //      (r, q) of tile (u, ct) holds query row prow(u, r), value columns 16 ct + 4q .. +3
-    if constexpr (EMIT) {
-      E* ob = Ob + (int64_t)c * kChunk * row_v;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int row = prow(u, r16);
-        const float gs = sGamS[row];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) Y[u][ct] = Y[u][ct] * gs;
-#pragma unroll
-        for (int s = 0; s <= (u >> 1); ++s) {
-          const frag aP = lds_frag(sP, CS, 16 * u + r16, 32 * s, q);
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) Y[u][ct] = M::run(ub[s][ct], aP, Y[u][ct]);
-        }
-        if (row < len) {
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) store4(ob + row * row_v + 16 * ct + 4 * q, Y[u][ct]);
-        }
-      }
-    }
-    // ---- h <- gamma_last h + K^T (diag(d) U)
+    // ---- h <- gamma_last h + K^T (diag(d) U); K^T fragments by LDS transpose reads
 #pragma unroll
     for (int t = 0; t < NKT; ++t) {
 #pragma unroll
@@ -419,36 +439,49 @@ __global__ __launch_bounds__(64 * NW, 2) void fused_forward_kernel(Problem p, Fw
         for (int ct = 0; ct < NCT; ++ct) hs[t][ct] = M::run(aKt, ubd[s][ct], hs[t][ct]);
       }
     }
+    if constexpr (EMIT && !GDN_P_FIRST) pstep(c);
   };
 
+  int len_prev = 0;
   for (int c = c_start; c < c_end; ++c) {
     const int len = min(kChunk, si.len - c * kChunk);
 
-    // ---- stage chunk c in LDS, then start the loads of chunk c+1
-    pf.template store<KS, CS, VS>(sK, sQ, sV, sT, sGraw, sBraw, p.beta_bf16, mcols, tid);
+    // ---- gates of chunk c from the prefetched registers (every wave holds all rows:
+    //      lane = chunk row), then stage chunk c in LDS and start the loads of chunk c+1
+    const float G = wave_inclusive_scan_dpp(lane < len ? pf.g : 0.f);
+    const float gC = fast_exp(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), kChunk - 1)));
+    pf.template store<KS, CS, VS>(sK, sQ, sV, sT, sBet, p.beta_bf16, mcols, tid);
+    if (wave == 0) {
+      const float gam = fast_exp(G);
+      sG[lane] = G;
+      sGam[lane] = gam;
+      sGamS[lane] = gam * p.scale;
+      sDec[lane] = fast_exp(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), kChunk - 1)) - G);
+    }
     __syncthreads();
     // after the last chunk this reloads it (unused): the load count per step stays
     // fixed, which keeps the step free of waits on these loads
     issue_loads(min(c + 1, c_end - 1));
 
-    // ---- gates: every wave scans (lane = chunk row); wave 0 publishes per-row values
-    const float G = wave_inclusive_scan(sGraw[lane]);
-    const float Glast = __shfl(G, 63, 64);
-    const float gC = fast_exp(Glast);
-    if (wave == 0) {
-      const float gam = fast_exp(G);
-      sGam[lane] = gam;
-      sGamS[lane] = gam * p.scale;
-      sDec[lane] = fast_exp(Glast - G);
-      sBet[lane] = sBraw[lane];
+    if constexpr (OUT) {
+      if (c - 1 >= c_out && c - 1 >= c_start) emit_o(c - 1, len_prev);
     }
-    if (c >= c_out) step(std::true_type{}, c, len, G, gC);
-    else step(std::false_type{}, c, len, G, gC);
+    if constexpr (OUT) {
+      if (c >= c_out) step(std::true_type{}, c, gC);
+      else step(std::false_type{}, c, gC);
+    } else {
+      step(std::false_type{}, c, gC);
+    }
+    len_prev = len;
     __syncthreads();
+  }
+  if constexpr (OUT) {
+    if (c_end - 1 >= c_out && c_end - 1 >= c_start) emit_o(c_end - 1, len_prev);
   }
 
   // ---- end state: final state (pass 3, last segment), S* (pass 1 value columns), or
-  //      M (pass 1 identity columns) as bf16 high and low parts for the merge's MFMAs
+  //      M (pass 1 identity columns) as bf16 high and low parts for the merge's MFMAs,
+  //      in the merge's operand order (mfrag_offset)
   if (PASS == kPass1 && mcols) {
     const int64_t slot = sg * H + h;
     bf16* mhi = reinterpret_cast<bf16*>(plan.cp.mcorr) + slot * 2 * DK * DK;
@@ -462,7 +495,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fused_forward_kernel(Problem p, Fw
         for (int i = 0; i < 4; ++i) {
           const float x = hs[t][ct][i];
           const bf16 hi = (bf16)x;
-          const int64_t at = (int64_t)prow(t, 4 * q + i) * DK + mc + ct * 16;
+          const int64_t at = mfrag_offset<DK>(prow(t, 4 * q + i), mc + ct * 16);
           mhi[at] = hi;
           mlo[at] = (bf16)(x - (float)hi);
         }

@@ -215,6 +215,33 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
   return x;
 }
 
+// Fragment-ordered storage of a DK x DK bf16 matrix used as MFMA A operands (the
+// merge's M): the 16-byte operand of lane l = 16 q + r for row tile rt and
+// contraction step s (row 16 rt + r, columns 32 s + 8 q .. +7) sits at element
+// ((rt * DK/32 + s) * 64 + l) * 8, so one wave's operand load is 1 KB contiguous.
+template <int DK>
+__device__ __forceinline__ int64_t mfrag_offset(int row, int col) {
+  return ((int64_t)((row >> 4) * (DK / 32) + (col >> 5)) * 64 + 16 * ((col & 31) >> 3) + (row & 15)) * 8 +
+         (col & 7);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave without LDS traffic: DPP row
+// shifts scan each 16-lane row (lanes without a source add 0), then the row totals
+// are carried with v_readlane.
+__device__ __forceinline__ float wave_inclusive_scan_dpp(float x) {
+  const int lane = threadIdx.x & 63;
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xF, 0xF, true));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 15));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 47));
+  const int row = lane >> 4;
+  const float c1 = r0, c2 = r0 + r1, c3 = r0 + r1 + r2;
+  return x + (row == 0 ? 0.f : row == 1 ? c1 : row == 2 ? c2 : c3);
+}
+
 // Order-preserving float <-> uint encoding (for atomic max of floats); 0 is
 // below every encoded float and marks "unset".
 __device__ __forceinline__ uint32_t ordered_bits(float f) {

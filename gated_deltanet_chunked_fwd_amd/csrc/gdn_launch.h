@@ -36,7 +36,8 @@ struct CpBuffers {
   int force_correction;     // 1: every split head uses the wrong-start correction
   float* sstar;             // [total_segs, H, dk, dv] wrong-start (zero-start) segment end states
   void* mcorr;              // [total_segs, H] x {hi, lo} x [dk, dk] bf16: segment transition
-                            // matrices M split as M = hi + lo (row-major, hi block first)
+                            // matrices M split as M = hi + lo (hi block first), each block
+                            // in MFMA operand order (mfrag_offset in gdn_device.h)
   float* hstart;            // [total_segs, H, dk, dv] true segment start states
 };
 
