@@ -7,12 +7,15 @@ zero initial state, fp32 final state).
 
 Timing: W untimed warm-up steps, then a short stage pass (3 steps with every
 stage bracketed by HIP events) that finds the dominant kernel.  Then K timed steps
-between two device synchronisations.  Before each timed step a 512 MiB buffer is
-overwritten (evicts the 256 MB MALL and the L2s) outside the step's HIP events, so
-ms_per_step (the mean of the per-step event times) never includes the flush.  In
-the timed steps only the dominant kernel's pair of events is recorded (by the
-library, on the launch stream, around that launch), which gives its live mean
-duration for the roofline at the cost of one event pair per step.
+between two device synchronisations.  Before each timed step, outside the step's
+HIP events, a 512 MiB buffer is written and another 512 MiB buffer is read: this
+evicts the 256 MB MALL and the L2s, and the read also drains the written lines, so
+the step starts from HBM with clean caches (a write-only flush leaves up to ~0.3
+GB of dirty lines whose write-back would be billed to the step's first kernel).
+ms_per_step is the mean of the per-step event times.  In the timed steps only the
+dominant kernel's pair of events is recorded (by the library, on the launch
+stream, around that launch), which gives its live mean duration for the roofline
+at the cost of one event pair per step.
 
 Roofline (dominant kernel = the stage with the largest mean time):
   achieved = algorithmic bytes of that kernel per launch (stage_bytes(): for the
@@ -212,6 +215,14 @@ def main():
                                                  inp["cu_seqlens"], opts), 1),
                      dtype=torch.uint8, device=dev)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush_rd = torch.ones(128 << 20, dtype=torch.int32, device=dev)   # 512 MiB
+
+    def evict(i):
+        # write 512 MiB, then read another 512 MiB: the read pushes the written (dirty)
+        # lines out of the L2s and the MALL here, so their write-back is not billed to
+        # the next step (a write-only flush halves the next kernel's HBM read rate)
+        flush.fill_(i & 0xFF)
+        flush_rd.sum()
     seg_chunks = binding.plan_segment_chunks(d["q"], d["v"], d["beta"], inp["cu_seqlens"], opts)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     step_ev = hip.events(2)
@@ -231,7 +242,7 @@ def main():
         out = {i: [] for i in range(binding.GDN_NUM_STAGES)}
         for i in range(steps):
             if not args.no_flush:
-                flush.fill_(i & 0xFF)
+                evict(i)
             # stages that a step does not run keep stale events: mark them first
             for st in range(binding.GDN_NUM_STAGES):
                 hip.record(stage_ev[2 * st], stream)
@@ -257,7 +268,7 @@ def main():
     t_wall0 = time.perf_counter()
     for i in range(args.steps):
         if not args.no_flush:
-            flush.fill_(i & 0xFF)
+            evict(i)
         hip.record(step_ev[0], stream)
         step(opts_dom)
         hip.record(step_ev[1], stream)
