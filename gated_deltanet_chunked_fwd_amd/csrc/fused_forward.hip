@@ -366,20 +366,28 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && PASS == kPass3) ? 1 : 2) void 
     // ---- X = K h; Y^T = h^T Q^T (operands swapped: a lane holds four consecutive value
     //      columns of one query row, the layout of the O store); first products start at zero
     f32x4 X[4][NCT];
+    // the step's operand fragments are read as one batch ahead of their MFMAs (the
+    // scheduling barrier keeps the compiler from trading the reads in flight for
+    // registers, which would expose one LDS round trip per MFMA)
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
+      frag aK[4], aQ[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        aK[u] = lds_frag(sK, KS, 16 * u + r16, 32 * s, q);
+        if constexpr (EMIT) aQ[u] = lds_frag(sQ, KS, 16 * u + r16, 32 * s, q);
+      }
       frag hb[NCT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) hb[ct] = M::pack(hs[2 * s][ct], hs[2 * s + 1][ct]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const frag aK = lds_frag(sK, KS, 16 * u + r16, 32 * s, q);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) X[u][ct] = M::run(aK, hb[ct], s == 0 ? zero4 : X[u][ct]);
+        for (int ct = 0; ct < NCT; ++ct) X[u][ct] = M::run(aK[u], hb[ct], s == 0 ? zero4 : X[u][ct]);
         if constexpr (EMIT) {
-          const frag aQ = lds_frag(sQ, KS, 16 * u + r16, 32 * s, q);
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) Yp[u][ct] = M::run(hb[ct], aQ, s == 0 ? zero4 : Yp[u][ct]);
+          for (int ct = 0; ct < NCT; ++ct) Yp[u][ct] = M::run(hb[ct], aQ[u], s == 0 ? zero4 : Yp[u][ct]);
         }
       }
     }
