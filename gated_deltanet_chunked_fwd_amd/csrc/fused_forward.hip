@@ -298,13 +298,18 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && PASS == kPass3) ? 1 : 2) void 
   auto emit_o = [&](int c, int len) {
     E* ob = Ob + (int64_t)c * kChunk * row_v;
     const E* sp = sP[c & 1];
+    frag aP[6];   // P fragments (u, s), ordered as the T fragments of the U product
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int s = 0; s <= (u >> 1); ++s) aP[u < 2 ? u : 2 * u - 2 + s] = lds_frag(sp, CS, 16 * u + r16, 32 * s, q);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
 #pragma unroll
       for (int s = 0; s <= (u >> 1); ++s) {
-        const frag aP = lds_frag(sp, CS, 16 * u + r16, 32 * s, q);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) Yp[u][ct] = M::run(ubp[s][ct], aP, Yp[u][ct]);
+        for (int ct = 0; ct < NCT; ++ct) Yp[u][ct] = M::run(ubp[s][ct], aP[u < 2 ? u : 2 * u - 2 + s], Yp[u][ct]);
       }
       const int row = prow(u, r16);
       if (row < len) {
@@ -415,14 +420,20 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && PASS == kPass3) ? 1 : 2) void 
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) wb[s][ct] = M::pack(X[2 * s][ct], X[2 * s + 1][ct]);
     f32x4 U[4][NCT];
+    {
+      frag aT[6];   // T fragments (u, s): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int s = 0; s <= (u >> 1); ++s) {
-        const frag aT = lds_frag(sT, CS, 16 * u + r16, 32 * s, q);
+        for (int s = 0; s <= (u >> 1); ++s) aT[u < 2 ? u : 2 * u - 2 + s] = lds_frag(sT, CS, 16 * u + r16, 32 * s, q);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) U[u][ct] = M::run(aT, wb[s][ct], s == 0 ? zero4 : U[u][ct]);
-      }
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int s = 0; s <= (u >> 1); ++s)
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+            U[u][ct] = M::run(aT[u < 2 ? u : 2 * u - 2 + s], wb[s][ct], s == 0 ? zero4 : U[u][ct]);
     }
     frag ubd[2][NCT];
 #pragma unroll
@@ -432,20 +443,32 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && PASS == kPass3) ? 1 : 2) void 
         if constexpr (EMIT) ubp[s][ct] = M::pack(U[2 * s][ct], U[2 * s + 1][ct]);
         ubd[s][ct] = M::pack(U[2 * s][ct] * rows4(sDec, 2 * s), U[2 * s + 1][ct] * rows4(sDec, 2 * s + 1));
       }
-    // ---- h <- gamma_last h + K^T (diag(d) U); K^T fragments by LDS transpose reads
+    // ---- h <- gamma_last h + K^T (diag(d) U); K^T fragments by LDS transpose reads,
+    //      two dk tiles' fragments read as a batch ahead of their MFMAs
 #pragma unroll
-    for (int t = 0; t < NKT; ++t) {
+    for (int t0 = 0; t0 < NKT; t0 += 2) {
+      frag aKt[2][2];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) hs[t][ct] *= gC;
-      const int own = prow(t, r16), supply = prow(t, 4 * (r16 & 3));
+      for (int dt = 0; dt < 2; ++dt) {
+        const int t = t0 + dt;
+        const int own = prow(t, r16), supply = prow(t, 4 * (r16 & 3));
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        frag aKt;
-        if constexpr (KT_COPY) aKt = lds_frag(sKt, CS, 16 * t + r16, 32 * s, q);
-        else aKt = col_frag(sK, KS, 32 * s + 4 * q, 32 * s + 16 + 4 * q, own, supply);
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) hs[t][ct] = M::run(aKt, ubd[s][ct], hs[t][ct]);
+        for (int s = 0; s < 2; ++s) {
+          if constexpr (KT_COPY) aKt[dt][s] = lds_frag(sKt, CS, 16 * t + r16, 32 * s, q);
+          else aKt[dt][s] = col_frag(sK, KS, 32 * s + 4 * q, 32 * s + 16 + 4 * q, own, supply);
+        }
       }
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) hs[t0 + dt][ct] *= gC;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) hs[t0 + dt][ct] = M::run(aKt[dt][s], ubd[s][ct], hs[t0 + dt][ct]);
     }
     if constexpr (EMIT && !GDN_P_FIRST) pstep(c);
   };
