@@ -94,34 +94,45 @@ struct ChunkRegs {
 
   // qb/kb/vb/gb/betab point at the chunk's first token (head and column offsets
   // applied); rows past the chunk end read the chunk's first row instead (masked
-  // to zero in store()).
+  // to zero in store()).  The loads go out in four parts spread over the step
+  // (PART 0: g, beta, K; 1: Q; 2: V; 3: T): issuing a whole chunk at once fills the
+  // CU's vector-memory queue and stalls the waves that issue last.
+  template <int PART>
   __device__ __forceinline__ void load(const E* qb, const E* kb, const E* vb, const E* ts,
                                        const float* gb, const void* betab, bool beta_bf16,
                                        int len_, const Offsets& of, int tid) {
-    len = len_;
-    const bool full = len == kChunk;
+    const bool full = len_ == kChunk;
+    if constexpr (PART == 0) {
+      len = len_;
+      const int og = (full || (tid & (kChunk - 1)) < len_) ? of.g : 0;
+      g = gb[og];
+      if (beta_bf16) b = reinterpret_cast<const uint16_t*>(betab)[og];
+      else b = reinterpret_cast<const uint32_t*>(betab)[og];
+    }
+    if constexpr (PART == 0 || (PART == 1 && WITH_Q)) {
 #pragma unroll
-    for (int j = 0; j < NK; ++j) {
-      const int r = (tid + NTH * j) / VPRK;
-      const int o = (full || r < len) ? of.k[j] : (tid + NTH * j) % VPRK * EPV;
-      k[j] = *reinterpret_cast<const u32x4*>(kb + o);
-      if constexpr (WITH_Q) q[j] = *reinterpret_cast<const u32x4*>(qb + o);
+      for (int j = 0; j < NK; ++j) {
+        const int r = (tid + NTH * j) / VPRK;
+        const int o = (full || r < len_) ? of.k[j] : (tid + NTH * j) % VPRK * EPV;
+        if constexpr (PART == 0) k[j] = *reinterpret_cast<const u32x4*>(kb + o);
+        else q[j] = *reinterpret_cast<const u32x4*>(qb + o);
+      }
     }
     // V is loaded even when it is not used (vzero: masked at store time), so every
     // path issues the same loads and the compiler's memory-counter waits for older
     // stores never have to drain these prefetches early.
+    if constexpr (PART == 2) {
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int r = (tid + NTH * j) / VPRV;
-      const int o = (full || r < len) ? of.v[j] : (tid + NTH * j) % VPRV * EPV;
-      v[j] = *reinterpret_cast<const u32x4*>(vb + o);
+      for (int j = 0; j < NV; ++j) {
+        const int r = (tid + NTH * j) / VPRV;
+        const int o = (full || r < len_) ? of.v[j] : (tid + NTH * j) % VPRV * EPV;
+        v[j] = *reinterpret_cast<const u32x4*>(vb + o);
+      }
     }
+    if constexpr (PART == 3) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) t[j] = reinterpret_cast<const u32x4*>(ts)[tid + NTH * j];
-    const int og = (full || (tid & (kChunk - 1)) < len) ? of.g : 0;
-    g = gb[og];
-    if (beta_bf16) b = reinterpret_cast<const uint16_t*>(betab)[og];
-    else b = reinterpret_cast<const uint32_t*>(betab)[og];
+      for (int j = 0; j < NT; ++j) t[j] = reinterpret_cast<const u32x4*>(ts)[tid + NTH * j];
+    }
   }
 
   template <int KS, int CS, int VS>
@@ -272,17 +283,36 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && PASS == kPass3) ? 1 : 2) void 
         }
   }
 
+  // Prefetch depth: the global loads of chunk c + PF are issued while chunk c is
+  // computed, from PF register sets used in turn.  Pass 1 has the registers for two.
+  constexpr int PF = (PASS == kPass1) ? 2 : 1;
   using Stage = ChunkRegs<E, DK, BV, Cfg::NT, PASS == kPass3>;
-  Stage pf;
+  Stage pf[PF];
   typename Stage::Offsets offs;
   offs.init(row_qk, row_v, H, tid);
-  auto issue_loads = [&](int c) {
+  auto issue_part = [&](auto part_tag, Stage& st, int c) {
+    constexpr int PART = decltype(part_tag)::value;
     const int64_t t0 = (int64_t)c * kChunk;
     const E* ts = Tm + ((si.chunk0 + c) * H + h) * (int64_t)(kChunk * kChunk);
-    pf.load(Qb + t0 * row_qk, Kb + t0 * row_qk, Vb + t0 * row_v, ts, Gb + t0 * H,
-            Bb + t0 * H * bsz, p.beta_bf16, min(kChunk, si.len - c * kChunk), offs, tid);
+    __builtin_amdgcn_sched_barrier(0);
+    st.template load<PART>(Qb + t0 * row_qk, Kb + t0 * row_qk, Vb + t0 * row_v, ts, Gb + t0 * H,
+                           Bb + t0 * H * bsz, p.beta_bf16, min(kChunk, si.len - c * kChunk), offs, tid);
+    __builtin_amdgcn_sched_barrier(0);
   };
-  if (c_start < c_end) issue_loads(c_start);
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using P2 = std::integral_constant<int, 2>;
+  using P3 = std::integral_constant<int, 3>;
+  if (c_start < c_end) {
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+      const int cc = min(c_start + k, c_end - 1);
+      issue_part(P0{}, pf[k], cc);
+      issue_part(P1{}, pf[k], cc);
+      issue_part(P2{}, pf[k], cc);
+      issue_part(P3{}, pf[k], cc);
+    }
+  }
 
   // per-row gates in tile order: rows prow(u, 4q) .. +3 are consecutive, one 16-byte read
   auto rows4 = [&](const float* v, int u) {
@@ -350,9 +380,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && PASS == kPass3) ? 1 : 2) void 
 
   // One chunk after staging; EMIT (compile-time) selects whether O is produced, so
   // each variant is straight-line code.
-  auto step = [&](auto emit_tag, int c, float gC) {
+  auto step = [&](auto emit_tag, int c, float gC, auto&& load_part) {
     constexpr bool EMIT = decltype(emit_tag)::value;
     if constexpr (EMIT && GDN_P_FIRST) pstep(c);
+    load_part(P1{});
     if constexpr (KT_COPY) {
       constexpr int TPW = (NKT + NW - 1) / NW;
 #pragma unroll
@@ -404,6 +435,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && PASS == kPass3) ? 1 : 2) void 
         for (int ct = 0; ct < NCT; ++ct) Yp[u][ct] = Yp[u][ct] * gs;
       }
     }
+    load_part(P2{});
     // ---- W = diag(beta) (V - diag(gamma) X), in place; V read in accumulator layout
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -435,6 +467,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && PASS == kPass3) ? 1 : 2) void 
           for (int ct = 0; ct < NCT; ++ct)
             U[u][ct] = M::run(aT[u < 2 ? u : 2 * u - 2 + s], wb[s][ct], s == 0 ? zero4 : U[u][ct]);
     }
+    load_part(P3{});
     frag ubd[2][NCT];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
@@ -474,37 +507,51 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && PASS == kPass3) ? 1 : 2) void 
   };
 
   int len_prev = 0;
-  for (int c = c_start; c < c_end; ++c) {
+  auto chunk = [&](Stage& st, int c) {
     const int len = min(kChunk, si.len - c * kChunk);
 
     // ---- gates of chunk c from the prefetched registers (every wave holds all rows:
-    //      lane = chunk row), then stage chunk c in LDS and start the loads of chunk c+1
-    const float G = wave_inclusive_scan_dpp(lane < len ? pf.g : 0.f);
-    const float gC = fast_exp(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), kChunk - 1)));
-    pf.template store<KS, CS, VS>(sK, sQ, sV, sT, sBet, p.beta_bf16, mcols, tid);
+    //      lane = chunk row), then stage chunk c in LDS and start the loads of chunk c+PF
+    const float G = wave_inclusive_scan_dpp(lane < len ? st.g : 0.f);
+    const float Glast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), kChunk - 1));
+    const float gC = fast_exp(Glast);
+    st.template store<KS, CS, VS>(sK, sQ, sV, sT, sBet, p.beta_bf16, mcols, tid);
     if (wave == 0) {
       const float gam = fast_exp(G);
       sG[lane] = G;
       sGam[lane] = gam;
       sGamS[lane] = gam * p.scale;
-      sDec[lane] = fast_exp(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), kChunk - 1)) - G);
+      sDec[lane] = fast_exp(Glast - G);
     }
     __syncthreads();
-    // after the last chunk this reloads it (unused): the load count per step stays
-    // fixed, which keeps the step free of waits on these loads
-    issue_loads(min(c + 1, c_end - 1));
+    // loads of chunk c+PF (past the last chunk this reloads it, unused: the load
+    // count per step stays fixed, which keeps the step free of waits on them); part 0
+    // now, the others from inside the step
+    const int cn = min(c + PF, c_end - 1);
+    issue_part(P0{}, st, cn);
+    auto load_part = [&](auto part) { issue_part(part, st, cn); };
 
     if constexpr (OUT) {
       if (c - 1 >= c_out && c - 1 >= c_start) emit_o(c - 1, len_prev);
     }
     if constexpr (OUT) {
-      if (c >= c_out) step(std::true_type{}, c, gC);
-      else step(std::false_type{}, c, gC);
+      if (c >= c_out) step(std::true_type{}, c, gC, load_part);
+      else step(std::false_type{}, c, gC, load_part);
     } else {
-      step(std::false_type{}, c, gC);
+      step(std::false_type{}, c, gC, load_part);
     }
     len_prev = len;
     __syncthreads();
+  };
+  int c = c_start;
+  if constexpr (PF == 1) {
+    for (; c < c_end; ++c) chunk(pf[0], c);
+  } else {
+    for (; c + 2 <= c_end; c += 2) {   // no conditions inside: fixed load counts
+      chunk(pf[0], c);
+      chunk(pf[1], c + 1);
+    }
+    if (c < c_end) chunk(pf[0], c);
   }
   if constexpr (OUT) {
     if (c_end - 1 >= c_out && c_end - 1 >= c_start) emit_o(c_end - 1, len_prev);
@@ -563,7 +610,8 @@ static void launch_dk(const Problem& p, const FwdPlan& plan, hipStream_t s) {
     // always takes 64-column workgroups: both shapes reach the same throughput per CU,
     // and pass 1 usually runs few (sequence, head) pairs, so the narrower blocks
     // spread its units over twice as many CUs.
-    if (PASS == kPass3 && p.dv % 128 == 0 && cols % 128 == 0 && plan.value_block != 64) {
+    if (p.dv % 128 == 0 && cols % 128 == 0 &&
+        (PASS == kPass3 ? plan.value_block != 64 : plan.pass1_block == 128)) {
       const int ncb = cols / 128;
       fused_forward_kernel<E, DK, 16, 8, PASS><<<(unsigned)(groups * 8 * ncb), 512, 0, s>>>(p, plan);
       return;

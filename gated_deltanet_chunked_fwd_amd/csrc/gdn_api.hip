@@ -108,6 +108,7 @@ struct Plan {
   bool split = false;
   int64_t total_segs = 0;
   int value_block = 128;
+  int pass1_block = 64;
   int wmax = kWindowMaxCap;
   float log_eps = 0.f;
 };
@@ -121,6 +122,7 @@ Plan make_plan(const gdn_shape* s, const gdn_opts* o) {
   }
   const int vb_req = o ? o->value_block : 0;
   P.value_block = (s->qkv_dtype == GDN_BF16 && s->dv % 128 == 0 && vb_req != 64) ? 128 : 64;
+  P.pass1_block = vb_req == 128 ? 128 : 64;
   P.wmax = (o && o->window_max_chunks > 0) ? o->window_max_chunks : kWindowMaxCap;
   P.log_eps = (o && o->window_log_eps != 0.f) ? o->window_log_eps : (float)std::log(0x1p-24);
   int64_t L = INT_MAX / 2;
@@ -274,6 +276,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
   plan.seg_off = (cu_seqlens && P.split) ? seg_off : nullptr;
   plan.units = P.total_segs * p.H;
   plan.value_block = P.value_block;
+  plan.pass1_block = P.pass1_block;
   plan.mode = gdn::kPass3;
   plan.cp = gdn::CpBuffers{};
   if (P.split) {

@@ -56,6 +56,7 @@ struct FwdPlan {
   const int32_t* seg_off;    // device [N+1] segment offsets (packed + split) or null
   int64_t units;             // number of (sequence, head, segment) units
   int value_block;           // value columns per workgroup: 64, 128, or 0 (widest that fits)
+  int pass1_block;           // pass-1 columns per workgroup: 128 (if requested), else 64
   int mode;                  // kPass3 or kPass1
   CpBuffers cp;
 };
