@@ -526,14 +526,15 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && PASS == kPass3) ? 1 : 2) void 
     __syncthreads();
     // loads of chunk c+PF (past the last chunk this reloads it, unused: the load
     // count per step stays fixed, which keeps the step free of waits on them); part 0
-    // now, the others from inside the step
+    // after the O stores below, the others from inside the step
     const int cn = min(c + PF, c_end - 1);
-    issue_part(P0{}, st, cn);
     auto load_part = [&](auto part) { issue_part(part, st, cn); };
 
+    // the previous chunk's O stores go out before this step's first loads
     if constexpr (OUT) {
       if (c - 1 >= c_out && c - 1 >= c_start) emit_o(c - 1, len_prev);
     }
+    issue_part(P0{}, st, cn);
     if constexpr (OUT) {
       if (c >= c_out) step(std::true_type{}, c, gC, load_part);
       else step(std::false_type{}, c, gC, load_part);
