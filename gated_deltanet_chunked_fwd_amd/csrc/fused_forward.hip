@@ -212,8 +212,19 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && PASS == kPass3) ? 1 : 2) void 
   const int col0 = cb * BV;                // first value column of the workgroup
   const int wcol = wave * NCW;             // wave's first column inside the block
 
-  const int h = (int)(unit % H);
-  const int64_t sg = unit / H;             // global segment index
+  // Pass 1 numbers its units head-major, so the few heads that need it (all of
+  // their units run full segments) still spread over all XCDs; pass 3 numbers them
+  // segment-major, so units dispatched together have similar lengths.
+  const int64_t nseg = plan.units / H;     // segments over all sequences
+  int h;
+  int64_t sg;                              // global segment index
+  if constexpr (PASS == kPass1) {
+    h = (int)(unit / nseg);
+    sg = unit - (int64_t)h * nseg;
+  } else {
+    h = (int)(unit % H);
+    sg = unit / H;
+  }
   int n, seg;
   if (plan.seg_off) {
     n = seq_of_chunk(sg, plan.seg_off, p.N, 0);

@@ -42,7 +42,7 @@ struct CpBuffers {
 };
 
 // Work description for one launch of the fused forward kernel.  A work unit is
-// (sequence, head, segment); the kernel grid is (units, column blocks).
+// (sequence, head, segment); the kernel grid covers units x column blocks.
 //   kPass3: steps 2-4 with O; a segment starts from h0 (first segment), from a
 //           zero state a window of chunks earlier (window heads) or from hstart
 //           (correction heads); the last segment writes the final state.
