@@ -16,12 +16,11 @@
 // The chunk gate sums come from the chunk-inverse kernel, which forms the chunk's
 // cumulative gate anyway (or, for the stand-alone entry point, from
 // chunk_gate_sums_kernel with the same wave scan, so both give identical sums).
-// gate_window_max: grid (N*H, ceil(max chunks / 256)); each block loads the sums
-// of its 256 chunks (plus a halo of wmax-1), forms the maximum run sum per W over
-// runs starting in its range, and merges them with an atomic max into
-// best[nh][W] (floats stored as order-preserving uints, reset to 0 = "minus
-// infinity" beforehand).  window_of() turns best[] into W wherever it is needed;
-// gate_window_finalize writes it out for the stand-alone entry point.
+// gate_window_max: one block per (sequence, head) forms
+// the maximum run sum per W (block_run_max) and stores it in best[nh][W] (floats as
+// order-preserving uints; 0 = no such run, so no reset is needed).  window_of()
+// turns best[] into W wherever it is needed; gate_window_finalize writes it out for
+// the stand-alone entry point.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -44,57 +43,29 @@ __global__ __launch_bounds__(256) void chunk_gate_sums_kernel(Problem p, float* 
   if (lane == kChunk - 1) csum[cg * p.H + h] = G;
 }
 
-__global__ __launch_bounds__(256) void gate_window_max_kernel(const float* __restrict__ csum,
-                                                              const int32_t* __restrict__ cu,
-                                                              const int32_t* __restrict__ chunk_off,
-                                                              int64_t T, int N, int H, int wmax,
-                                                              uint32_t* __restrict__ best) {
-  __shared__ float sums[256 + kWindowMaxCap];
-  __shared__ float red[4][kWindowMaxCap];
+constexpr int kScanThreads = 1024;   // run starts per pass of the gate-window scan
+
+__global__ __launch_bounds__(kScanThreads) void gate_window_max_kernel(const float* __restrict__ csum,
+                                                                       const int32_t* __restrict__ cu,
+                                                                       const int32_t* __restrict__ chunk_off,
+                                                                       int64_t T, int N, int H, int wmax,
+                                                                       uint32_t* __restrict__ best) {
+  __shared__ float sums[kScanThreads + kWindowMaxCap];
+  __shared__ float red[kScanThreads / 64 * kWindowMaxCap];
   const int nh = blockIdx.x, n = nh / H, h = nh % H;
   const SeqInfo si = seq_info(n, cu, chunk_off, T);
   const int nch = (si.len + kChunk - 1) / kChunk;
-  const int cs = blockIdx.y * 256;
-  if (cs >= nch) return;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < 256 + wmax - 1; i += 256) {
-    const int c = cs + i;
-    sums[i] = c < nch ? csum[(si.chunk0 + c) * H + h] : 0.f;
-  }
-  __syncthreads();
-  float bestw[kWindowMaxCap];
-  float acc = 0.f;
-  const int c = cs + tid;
-#pragma unroll
-  for (int w = 1; w <= kWindowMaxCap; ++w) {
-    bestw[w - 1] = -INFINITY;
-    if (w <= wmax) {
-      acc += sums[tid + w - 1];
-      if (c + w <= nch) bestw[w - 1] = acc;
-    }
-  }
-  // block max per w: wave shuffles, then across the 4 waves
-  const int lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-  for (int w = 0; w < kWindowMaxCap; ++w) {
-    float v = bestw[w];
-    for (int d = 32; d > 0; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
-    if (lane == 0) red[wave][w] = v;
-  }
-  __syncthreads();
-  if (tid < wmax) {
-    const float v = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
-    if (v > -INFINITY) atomicMax(&best[nh * kWindowMaxCap + tid], ordered_bits(v));
-  }
+  const float v = block_run_max<kScanThreads>(csum, si.chunk0, nch, H, h, wmax, sums,
+                                              kScanThreads + kWindowMaxCap, red);
+  const int w = threadIdx.x;   // thread w holds the maximum for runs of w + 1 chunks
+  if (w < kWindowMaxCap)       // 0 = no run of that length
+    best[nh * kWindowMaxCap + w] = (w < wmax && v > -INFINITY) ? ordered_bits(v) : 0u;
 }
 
-// Resets best[] and (for packed input) builds the chunk / segment offset tables.
+// Packed input: the chunk / segment offset tables.
 __global__ void plan_tables_kernel(const int32_t* __restrict__ cu, int N, int seg_chunks,
-                                   int32_t* __restrict__ chunk_off, int32_t* __restrict__ seg_off,
-                                   uint32_t* __restrict__ best, int best_len) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < best_len; i += gridDim.x * blockDim.x)
-    best[i] = 0u;
-  if (cu && blockIdx.x == 0 && threadIdx.x == 0) {
+                                   int32_t* __restrict__ chunk_off, int32_t* __restrict__ seg_off) {
+  if (threadIdx.x == 0) {
     int32_t acc = 0, sacc = 0;
     chunk_off[0] = 0;
     if (seg_off) seg_off[0] = 0;
@@ -122,9 +93,8 @@ __global__ void gate_window_finalize_kernel(const uint32_t* __restrict__ best,
 }
 
 hipError_t launch_plan_tables(const int32_t* cu, int N, int seg_chunks, int32_t* chunk_off,
-                              int32_t* seg_off, uint32_t* best, int best_len, hipStream_t s) {
-  const int blocks = best_len > 0 ? min(64, (best_len + 255) / 256) : 1;
-  plan_tables_kernel<<<blocks, 256, 0, s>>>(cu, N, seg_chunks, chunk_off, seg_off, best, best_len);
+                              int32_t* seg_off, hipStream_t s) {
+  plan_tables_kernel<<<1, 64, 0, s>>>(cu, N, seg_chunks, chunk_off, seg_off);
   return hipGetLastError();
 }
 
@@ -138,9 +108,10 @@ hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s) 
 
 hipError_t launch_gate_scan(const Problem& p, const float* csum, int64_t max_chunks, int wmax,
                             uint32_t* best, hipStream_t s) {
-  if (p.N == 0 || max_chunks == 0) return hipSuccess;
-  dim3 grid((unsigned)(p.N * p.H), (unsigned)((max_chunks + 255) / 256));
-  gate_window_max_kernel<<<grid, 256, 0, s>>>(csum, p.cu, p.chunk_off, p.T, p.N, p.H, wmax, best);
+  (void)max_chunks;
+  if (p.N == 0) return hipSuccess;
+  gate_window_max_kernel<<<(unsigned)(p.N * p.H), kScanThreads, 0, s>>>(csum, p.cu, p.chunk_off, p.T,
+                                                                          p.N, p.H, wmax, best);
   return hipGetLastError();
 }
 

@@ -254,11 +254,9 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
   int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + L.chunk_off);
   int32_t* seg_off = reinterpret_cast<int32_t*>(ws + L.seg_off);
   uint32_t* best = reinterpret_cast<uint32_t*>(ws + L.best);
-  const int best_len = P.split ? p.N * p.H * kWindowMaxCap : 0;
-  if (cu_seqlens || P.split) {
-    if (gdn::launch_plan_tables(cu_seqlens, p.N, P.seg_chunks, cu_seqlens ? chunk_off : nullptr,
-                                (cu_seqlens && P.split) ? seg_off : nullptr, best, best_len,
-                                stream) != hipSuccess)
+  if (cu_seqlens) {
+    if (gdn::launch_plan_tables(cu_seqlens, p.N, P.seg_chunks, chunk_off,
+                                P.split ? seg_off : nullptr, stream) != hipSuccess)
       return GDN_ERR_HIP;
   }
   if (cu_seqlens) p.chunk_off = chunk_off;
@@ -367,9 +365,8 @@ int gdn_gate_scan(const float* g, const int32_t* cu_seqlens, const gdn_shape* sh
   float* csum = reinterpret_cast<float*>(ws + off_csum);
   gdn::Problem p = make_problem(nullptr, nullptr, nullptr, g, nullptr, nullptr, cu_seqlens, 1.f,
                                 nullptr, nullptr, shape, P.total_chunks);
-  const int best_len = p.N * p.H * kWindowMaxCap;
-  if (gdn::launch_plan_tables(cu_seqlens, p.N, 1, cu_seqlens ? chunk_off : nullptr, nullptr, best,
-                              best_len, stream) != hipSuccess)
+  if (cu_seqlens &&
+      gdn::launch_plan_tables(cu_seqlens, p.N, 1, chunk_off, nullptr, stream) != hipSuccess)
     return GDN_ERR_HIP;
   if (cu_seqlens) p.chunk_off = chunk_off;
   if (gdn::launch_chunk_gate_sums(p, csum, stream) != hipSuccess) return GDN_ERR_HIP;

@@ -264,6 +264,55 @@ __device__ __forceinline__ int window_of(const uint32_t* best, int nh, int nch, 
   return 0;
 }
 
+// Largest gate sum over every run of w consecutive chunks (w = 1..wmax) of one
+// (sequence, head), from its chunk gate sums csum[(chunk0 + c) * H + h], computed by a
+// whole workgroup of NT threads (every thread must call it).  sums: LDS scratch of
+// cap floats (cap > kWindowMaxCap); red: LDS scratch of NT / 64 * kWindowMaxCap
+// floats.  Thread t < kWindowMaxCap returns the maximum for w = t + 1 (-inf: no run
+// of that length); the other threads return -inf.
+template <int NT>
+__device__ float block_run_max(const float* csum, int64_t chunk0, int nch, int H, int h, int wmax,
+                               float* sums, int cap, float* red) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int pass = cap - kWindowMaxCap;   // run starts per pass
+  float mx[kWindowMaxCap];
+#pragma unroll
+  for (int w = 0; w < kWindowMaxCap; ++w) mx[w] = -INFINITY;
+  for (int cs = 0; cs < nch; cs += pass) {
+    __syncthreads();   // the previous pass (or the caller) is done with sums[]
+    for (int i = tid; i < pass + wmax - 1; i += NT) {
+      const int c = cs + i;
+      sums[i] = c < nch ? csum[(chunk0 + c) * H + h] : 0.f;
+    }
+    __syncthreads();
+    for (int i = tid; i < pass; i += NT) {
+      const int c = cs + i;
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 1; w <= kWindowMaxCap; ++w) {
+        if (w <= wmax) {
+          acc += sums[i + w - 1];
+          if (c + w <= nch) mx[w - 1] = fmaxf(mx[w - 1], acc);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int w = 0; w < kWindowMaxCap; ++w) {
+    float v = mx[w];
+    for (int d = 32; d > 0; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
+    if (lane == 0) red[wave * kWindowMaxCap + w] = v;
+  }
+  __syncthreads();
+  float v = -INFINITY;
+  if (tid < kWindowMaxCap) {
+    v = red[tid];
+#pragma unroll
+    for (int k = 1; k < NT / 64; ++k) v = fmaxf(v, red[k * kWindowMaxCap + tid]);
+  }
+  return v;
+}
+
 // Sequence n's token range and first global chunk.
 struct SeqInfo {
   int64_t tok0;    // first token (flattened over B*T)

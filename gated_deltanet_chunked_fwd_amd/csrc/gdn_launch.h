@@ -63,7 +63,7 @@ struct FwdPlan {
 
 hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hipStream_t s);
 hipError_t launch_plan_tables(const int32_t* cu, int N, int seg_chunks, int32_t* chunk_off,
-                              int32_t* seg_off, uint32_t* best, int best_len, hipStream_t s);
+                              int32_t* seg_off, hipStream_t s);
 hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s);
 hipError_t launch_gate_scan(const Problem& p, const float* csum, int64_t max_chunks, int wmax,
                             uint32_t* best, hipStream_t s);
