@@ -352,10 +352,31 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && PASS == kPass3) ? 1 : 2) void 
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) Yp[u][ct] = M::run(ubp[s][ct], aP[u < 2 ? u : 2 * u - 2 + s], Yp[u][ct]);
       }
-      const int row = prow(u, r16);
-      if (row < len) {
+    }
+    if constexpr (sizeof(E) == 2) {
+      // 16-byte stores: for the tile pair (u, u+1), v_permlane16_swap hands lane group
+      // q^1 the other group's four columns, so an even group holds eight consecutive
+      // columns of tile u's row and an odd group those of tile u+1's row
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) store4(ob + row * row_v + 16 * ct + 4 * q, Yp[u][ct]);
+      for (int u = 0; u < 4; u += 2) {
+        const int row = (q & 1) ? prow(u + 1, r16) : prow(u, r16);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const uint2 a = pack_bf16x4(Yp[u][ct]), b = pack_bf16x4(Yp[u + 1][ct]);
+          const auto sx = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
+          const auto sy = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
+          const u32x4 v = {sx[0], sy[0], sx[1], sy[1]};
+          if (row < len) *reinterpret_cast<u32x4*>(ob + row * row_v + 16 * ct + 8 * (q >> 1)) = v;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = prow(u, r16);
+        if (row < len) {
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) store4(ob + row * row_v + 16 * ct + 4 * q, Yp[u][ct]);
+        }
       }
     }
   };

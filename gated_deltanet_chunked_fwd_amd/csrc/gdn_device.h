@@ -176,6 +176,14 @@ __device__ __forceinline__ f32x4 col_read4_storage(const float* M, int stride, i
   return col_read4(M, stride, row0, own_col, supply_col);
 }
 
+// Four fp32 values as four bf16 (round to nearest even) in two dwords.
+__device__ __forceinline__ uint2 pack_bf16x4(const f32x4& v) {
+  bf16x4 b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = (bf16)v[i];
+  return __builtin_bit_cast(uint2, b);
+}
+
 // Four consecutive elements of one row from fp32: 8 bytes (bf16) or 16 bytes (fp32).
 __device__ __forceinline__ void store4(bf16* dst, const f32x4& v) {
   bf16x4 b;
