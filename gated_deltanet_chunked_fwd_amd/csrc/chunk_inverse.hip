@@ -15,7 +15,8 @@
 // run on v_mfma_f32_16x16x32_bf16 (fp32 path: 16x16x4_f32).  With 16x16 blocks
 // A_ij, T_ij of A and T:
 //   * T_ii = (I + A_ii)^{-1} by forward substitution in fp32, lane = (block, column);
-//   * the rest by two doubling levels of 16x16x16 fp32 MFMA products,
+//   * the rest by two doubling levels of 16x16x16 MFMA products (fp32 inputs: fp32
+//     MFMA; bf16 inputs: bf16 MFMA, fp32 accumulation),
 //       T_10 = -T_11 A_10 T_00,  T_32 = -T_33 A_32 T_22,
 //       [T_20 T_21; T_30 T_31] = -[T_22 0; T_32 T_33] A[32:, :32] [T_00 0; T_10 T_11].
 // Register-resident products.  In accumulator ("D") layout lane (r, q) holds
@@ -46,11 +47,23 @@ struct InvCfg {
   static constexpr int PER_WAVE = 2 * kChunk + UNION;          // floats of LDS per wave
 };
 
-// D(X^T), D(Y), acc -> acc + D(X Y) for 16x16 blocks (see the header comment).
+// D(X^T), D(Y), acc -> acc + D(X Y) for 16x16 blocks (see the header comment).  fp32
+// inputs: four chained v_mfma_f32_16x16x4_f32 (fp32 products, the fp32 path's 1e-5
+// accuracy).  bf16 inputs: one v_mfma_f32_16x16x16_bf16 on the operands rounded to
+// bf16 (the four slots of a D tile are exactly that MFMA's four contraction
+// elements); T leaves this kernel in bf16, whose rounding is of the same size.
+template <typename E>
 __device__ __forceinline__ f32x4 mm16(const f32x4& xt, const f32x4& y, f32x4 acc) {
+  if constexpr (sizeof(E) == 2) {
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    const i16x4 a = __builtin_bit_cast(i16x4, pack_bf16x4(xt));
+    const i16x4 b = __builtin_bit_cast(i16x4, pack_bf16x4(y));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+  } else {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[e], y[e], acc, 0, 0, 0);
-  return acc;
+    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xt[e], y[e], acc, 0, 0, 0);
+    return acc;
+  }
 }
 
 // Orders this wave's LDS accesses across lanes (LDS executes a wave's operations in
@@ -202,19 +215,19 @@ __global__ __launch_bounds__(256) void chunk_inverse_kernel(Problem p, E* __rest
   wave_lds_sync();
 
   // ---- doubling levels (D(.) of each block; "T" suffix = transposed block)
-  const f32x4 R10 = mm16(At[1][0], Td[0], zero4);
-  const f32x4 T10 = -mm16(TdT[1], R10, zero4);
-  const f32x4 T10T = -mm16(R10, TdT[1], zero4);
-  const f32x4 R32 = mm16(At[3][2], Td[2], zero4);
-  const f32x4 T32T = -mm16(R32, TdT[3], zero4);
-  const f32x4 R20 = mm16(At[2][1], T10, mm16(At[2][0], Td[0], zero4));
-  const f32x4 R21 = mm16(At[2][1], Td[1], zero4);
-  const f32x4 R30 = mm16(At[3][1], T10, mm16(At[3][0], Td[0], zero4));
-  const f32x4 R31 = mm16(At[3][1], Td[1], zero4);
-  const f32x4 T20T = -mm16(R20, TdT[2], zero4);
-  const f32x4 T21T = -mm16(R21, TdT[2], zero4);
-  const f32x4 T30T = -mm16(R30, TdT[3], mm16(R20, T32T, zero4));
-  const f32x4 T31T = -mm16(R31, TdT[3], mm16(R21, T32T, zero4));
+  const f32x4 R10 = mm16<E>(At[1][0], Td[0], zero4);
+  const f32x4 T10 = -mm16<E>(TdT[1], R10, zero4);
+  const f32x4 T10T = -mm16<E>(R10, TdT[1], zero4);
+  const f32x4 R32 = mm16<E>(At[3][2], Td[2], zero4);
+  const f32x4 T32T = -mm16<E>(R32, TdT[3], zero4);
+  const f32x4 R20 = mm16<E>(At[2][1], T10, mm16<E>(At[2][0], Td[0], zero4));
+  const f32x4 R21 = mm16<E>(At[2][1], Td[1], zero4);
+  const f32x4 R30 = mm16<E>(At[3][1], T10, mm16<E>(At[3][0], Td[0], zero4));
+  const f32x4 R31 = mm16<E>(At[3][1], Td[1], zero4);
+  const f32x4 T20T = -mm16<E>(R20, TdT[2], zero4);
+  const f32x4 T21T = -mm16<E>(R21, TdT[2], zero4);
+  const f32x4 T30T = -mm16<E>(R30, TdT[3], mm16<E>(R20, T32T, zero4));
+  const f32x4 T31T = -mm16<E>(R31, TdT[3], mm16<E>(R21, T32T, zero4));
 
   // ---- stage T row-major (lane (r, q) of block (a, b): row 16a+r, cols 16b+4q..+3)
   auto put = [&](int a, int b, const f32x4& v) { store4(sOut + (16 * a + r) * OS + 16 * b + 4 * q, v); };
