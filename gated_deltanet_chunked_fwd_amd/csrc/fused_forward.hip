@@ -175,7 +175,7 @@ __device__ __forceinline__ void p_pair(int i, int& qt, int& kt) {
 // PASS (kPass3 / kPass1) is a template parameter so that each pass compiles to
 // its own straight-line code and shows up as its own kernel in profiles.
 template <typename E, int DK, int NCW, int NW, int PASS>
-__global__ __launch_bounds__(64 * NW, (NW == 4 && PASS == kPass3) ? 1 : 2) void fused_forward_kernel(Problem p,
+__global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) == 4)) ? 1 : 2) void fused_forward_kernel(Problem p,
                                                                                       FwdPlan plan) {
   using Cfg = FwdCfg<E, DK, NCW, NW>;
   using M = Mma<E>;
@@ -184,16 +184,27 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && PASS == kPass3) ? 1 : 2) void 
   constexpr int KS = Cfg::KS, CS = Cfg::CS, VS = Cfg::VS;
 
   constexpr bool OUT = PASS == kPass3;
-  __shared__ __align__(16) E sK[kChunk * KS];     // tile-order rows
-  __shared__ __align__(16) E sQ[OUT ? kChunk * KS : 8];  // tile-order rows
-  __shared__ __align__(16) E sT[kChunk * CS];     // tile-order rows
+  // Staging buffers: bf16 chunks are double-buffered (chunk c+1 is staged at the end
+  // of chunk c's step, so one barrier per chunk suffices); fp32 tiles only fit once.
+  constexpr int NB = sizeof(E) == 2 ? 2 : 1;
+  __shared__ __align__(16) E sKb[NB][kChunk * KS];     // tile-order rows
+  __shared__ __align__(16) E sQb[NB][OUT ? kChunk * KS : 8];  // tile-order rows
+  __shared__ __align__(16) E sTb[NB][kChunk * CS];     // tile-order rows
   // P of chunks c and c-1 (O of a chunk is formed during the next chunk): tile-order
   // query rows, natural keys
   __shared__ __align__(16) E sP[OUT ? 2 : 1][OUT ? kChunk * CS : 8];
-  __shared__ __align__(16) E sV[kChunk * VS];     // natural rows
+  __shared__ __align__(16) E sVb[NB][kChunk * VS];     // natural rows
   constexpr bool KT_COPY = GDN_KT_COPY && sizeof(E) == 2 && NW == 8 && OUT;
   __shared__ __align__(16) E sKt[KT_COPY ? DK * CS : 8];
-  __shared__ __align__(16) float sG[kChunk], sGam[kChunk], sGamS[kChunk], sDec[kChunk], sBet[kChunk];
+  __shared__ __align__(16) float sGb[NB][kChunk], sGamb[NB][kChunk], sGamSb[NB][kChunk],
+      sDecb[NB][kChunk], sBetb[NB][kChunk];
+  // the buffer set of the chunk being computed (the step lambdas read through these)
+  E *sK = sKb[0], *sQ = sQb[0], *sT = sTb[0], *sV = sVb[0];
+  float *sG = sGb[0], *sGam = sGamb[0], *sGamS = sGamSb[0], *sDec = sDecb[0], *sBet = sBetb[0];
+  auto use_buffers = [&](int b) {
+    sK = sKb[b]; sQ = sQb[b]; sT = sTb[b]; sV = sVb[b];
+    sG = sGb[b]; sGam = sGamb[b]; sGamS = sGamSb[b]; sDec = sDecb[b]; sBet = sBetb[b];
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar table reads
@@ -538,35 +549,43 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && PASS == kPass3) ? 1 : 2) void 
     if constexpr (EMIT && !GDN_P_FIRST) pstep(c);
   };
 
-  int len_prev = 0;
-  auto chunk = [&](Stage& st, int c) {
-    const int len = min(kChunk, si.len - c * kChunk);
-
-    // ---- gates of chunk c from the prefetched registers (every wave holds all rows:
-    //      lane = chunk row), then stage chunk c in LDS and start the loads of chunk c+PF
+  // Stages chunk cs (registers of st) in buffer b: the gates of chunk cs are scanned in
+  // registers (every wave holds all rows: lane = chunk row); returns gamma_last.
+  auto stage = [&](Stage& st, int cs, int b) {
+    const int len = min(kChunk, si.len - cs * kChunk);
     const float G = wave_inclusive_scan_dpp(lane < len ? st.g : 0.f);
     const float Glast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), kChunk - 1));
-    const float gC = fast_exp(Glast);
-    st.template store<KS, CS, VS>(sK, sQ, sV, sT, sBet, p.beta_bf16, mcols, tid);
+    st.template store<KS, CS, VS>(sKb[b], sQb[b], sVb[b], sTb[b], sBetb[b], p.beta_bf16, mcols, tid);
     if (wave == 0) {
       const float gam = fast_exp(G);
-      sG[lane] = G;
-      sGam[lane] = gam;
-      sGamS[lane] = gam * p.scale;
-      sDec[lane] = fast_exp(Glast - G);
+      sGb[b][lane] = G;
+      sGamb[b][lane] = gam;
+      sGamSb[b][lane] = gam * p.scale;
+      sDecb[b][lane] = fast_exp(Glast - G);
     }
-    __syncthreads();
-    // loads of chunk c+PF (past the last chunk this reloads it, unused: the load
-    // count per step stays fixed, which keeps the step free of waits on them); part 0
-    // after the O stores below, the others from inside the step
-    const int cn = min(c + PF, c_end - 1);
-    auto load_part = [&](auto part) { issue_part(part, st, cn); };
+    return fast_exp(Glast);
+  };
 
-    // the previous chunk's O stores go out before this step's first loads
+  // One chunk: ld receives the loads of chunk c+PF (past the last chunk this reloads
+  // it, unused: the load count per step stays fixed, which keeps the step free of
+  // waits on them); part 0 goes out after the previous chunk's O stores, the others
+  // from inside the step.  With two buffers, sg (holding chunk c+1) is staged at the
+  // end of the step, so the next chunk starts right after the one barrier.
+  int len_prev = 0;
+  float gC = 0.f;
+  auto chunk = [&](Stage& ld, Stage& sg, int c) {
+    const int len = min(kChunk, si.len - c * kChunk);
+    if constexpr (NB == 1) {
+      gC = stage(ld, c, 0);
+      __syncthreads();
+    }
+    use_buffers(c % NB);
+    const int cn = min(c + PF, c_end - 1);
+    auto load_part = [&](auto part) { issue_part(part, ld, cn); };
     if constexpr (OUT) {
       if (c - 1 >= c_out && c - 1 >= c_start) emit_o(c - 1, len_prev);
     }
-    issue_part(P0{}, st, cn);
+    issue_part(P0{}, ld, cn);
     if constexpr (OUT) {
       if (c >= c_out) step(std::true_type{}, c, gC, load_part);
       else step(std::false_type{}, c, gC, load_part);
@@ -574,17 +593,24 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && PASS == kPass3) ? 1 : 2) void 
       step(std::false_type{}, c, gC, load_part);
     }
     len_prev = len;
+    if constexpr (NB == 2) gC = stage(sg, min(c + 1, c_end - 1), (c + 1) % NB);
     __syncthreads();
   };
   int c = c_start;
-  if constexpr (PF == 1) {
-    for (; c < c_end; ++c) chunk(pf[0], c);
-  } else {
-    for (; c + 2 <= c_end; c += 2) {   // no conditions inside: fixed load counts
-      chunk(pf[0], c);
-      chunk(pf[1], c + 1);
+  if (c_start < c_end) {
+    if constexpr (NB == 2) {
+      gC = stage(pf[0], c_start, c_start % NB);
+      __syncthreads();
     }
-    if (c < c_end) chunk(pf[0], c);
+    if constexpr (PF == 1) {
+      for (; c < c_end; ++c) chunk(pf[0], pf[0], c);
+    } else {
+      for (; c + 2 <= c_end; c += 2) {   // no conditions inside: fixed load counts
+        chunk(pf[0], pf[1], c);
+        chunk(pf[1], pf[0], c + 1);
+      }
+      if (c < c_end) chunk(pf[0], pf[1], c);
+    }
   }
   if constexpr (OUT) {
     if (c_end - 1 >= c_out && c_end - 1 >= c_start) emit_o(c_end - 1, len_prev);
