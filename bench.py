@@ -58,7 +58,23 @@ def parse():
     ap.add_argument("--no-split", type=int, default=0)
     ap.add_argument("--value-block", type=int, default=0)
     ap.add_argument("--segment-chunks", type=int, default=0, help="force the split length (0: planner)")
+    ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
+                    help="only run 3 plain device copies of MIB MiB (the known-size kernel that "
+                         "scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings) and exit")
     return ap.parse_args()
+
+
+def copy_reference(mib):
+    """Three torch copies of a known size: each moves mib MiB in and mib MiB out."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_reference_bytes_each_way": n * 4, "copies": 3}), flush=True)
 
 
 class Hip:
@@ -186,6 +202,9 @@ def cpu_baseline(inp, spec):
 
 def main():
     args = parse()
+    if args.copy_reference:
+        copy_reference(args.copy_reference)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
