@@ -8,30 +8,47 @@
 //     h_start(0) = h0 (or 0),   h_start(j+1) = M_j h_start(j) + S*_j
 //
 // Mapping: one workgroup per (sequence, head, 16 value columns); columns of h are
-// independent.  Wave w owns output rows [32w, 32w+32).  M_j h is one 128x128x16
-// product per step on MFMA; to keep fp32-level accuracy both factors are split
-// into bf16 high and low parts, M h ~= Mh hh + Mh hl + Ml hh.  Pass 1 stores M
-// already split, in operand order (mfrag_offset: one 1 KB contiguous block per
-// wave and fragment, so the loads coalesce fully), and the operands
-// of step j+2 (M fragments, S* tiles) are loaded while step j computes: only the
-// MFMA chain through h is serial.  The running state lives in
-// LDS as bf16 high/low, K-major by column, so a lane's B operand is one 16-byte
-// read.  Heads that take window-lookback starts skip the merge.
+// independent.  DK/16 waves, wave w owns output rows [16w, 16w+16).  M_j h is one
+// DKxDKx16 product per step on MFMA; to keep fp32-level accuracy both factors are
+// split into bf16 high and low parts, M h ~= Mh hh + Mh hl + Ml hh (three
+// independent accumulator chains, summed at the end).  Pass 1 stores M already
+// split and S* as accumulator tiles, both in operand order (one 1 KB contiguous
+// block per wave and operand, so the loads coalesce fully).  The step is bound by
+// the latency of those loads, not by its few MFMAs, so a ring of NSET operand sets
+// keeps the loads of steps j+1 .. j+NSET-1 in flight while step j computes: only
+// the MFMA chain through h is serial.  The running state lives in LDS as bf16
+// high/low, K-major by column (a lane's B operand is one 16-byte read), in two
+// copies used alternately, so each step needs a single barrier.  The column blocks
+// of one (sequence, head) run on one XCD and share M through its L2.  Heads that
+// take window-lookback starts skip the merge.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
 namespace gdn {
 
 template <int DK>
-__global__ __launch_bounds__(256) void cp_merge_kernel(Problem p, FwdPlan plan) {
-  constexpr int HS = DK + 8;                 // row stride of the bf16 state copies
-  constexpr int NKS = DK / 32;
-  constexpr int RT = DK / 64;                // row tiles per wave (4 waves x RT x 16 = DK)
-  __shared__ __align__(16) bf16 sHi[16 * HS];
-  __shared__ __align__(16) bf16 sLo[16 * HS];
+struct MergeCfg {
+  static constexpr int NW = DK / 16;     // waves, one 16-row tile each
+  static constexpr int NKS = DK / 32;    // contraction steps
+  static constexpr int HS = DK + 8;      // row stride of the bf16 state copies
+  static constexpr int NSET = DK == 128 ? 4 : 6;   // operand sets in flight (registers permitting)
+};
 
-  const int nh = blockIdx.x, H = p.H, n = nh / H, h = nh % H;
-  const int dv = p.dv, col = 16 * blockIdx.y;
+template <int DK>
+__global__ __launch_bounds__(64 * MergeCfg<DK>::NW) void cp_merge_kernel(Problem p, FwdPlan plan) {
+  using C = MergeCfg<DK>;
+  constexpr int NKS = C::NKS, HS = C::HS, NSET = C::NSET;
+  __shared__ __align__(16) bf16 sHi[2][16 * HS];
+  __shared__ __align__(16) bf16 sLo[2][16 * HS];
+
+  // XCD-aware decode of the 1-D grid: workgroup b runs on XCD b % 8; the column
+  // blocks of unit u all go to XCD u % 8
+  const int ncb = p.dv / 16;
+  const int bid = blockIdx.x, xcd = bid & 7, k = bid >> 3;
+  const int nh = (k / ncb) * 8 + xcd, cb = k % ncb;
+  if (nh >= p.N * p.H) return;
+  const int H = p.H, n = nh / H, h = nh % H;
+  const int dv = p.dv, col = 16 * cb;
   const SeqInfo si = seq_info(n, p.cu, p.chunk_off, p.T);
   const int nch = (si.len + kChunk - 1) / kChunk;
   const int L = plan.seg_chunks;
@@ -46,96 +63,110 @@ __global__ __launch_bounds__(256) void cp_merge_kernel(Problem p, FwdPlan plan) 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, q = lane >> 4;
 
-  // start state columns [col, col+16) -> LDS (hi/lo), K-major per column
-  for (int i = tid; i < DK * 16; i += 256) {
+  // start state columns [col, col+16) -> LDS copy 0 (hi/lo), K-major per column
+  for (int i = tid; i < DK * 16; i += 64 * C::NW) {
     const int r = i >> 4, cc = i & 15;
     const float x = p.h0 ? p.h0[((int64_t)nh * DK + r) * dv + col + cc] : 0.f;
     const bf16 hi = (bf16)x;
-    sHi[cc * HS + r] = hi;
-    sLo[cc * HS + r] = (bf16)(x - (float)hi);
+    sHi[0][cc * HS + r] = hi;
+    sLo[0][cc * HS + r] = (bf16)(x - (float)hi);
   }
   __syncthreads();
 
-  // operands of one step: M_j fragments (row-major hi / lo blocks) and S*_j tiles
+  // operands of one step: this wave's M_j fragments (hi / lo) and S*_j tile
   struct Ops {
-    bf16x8 mh[RT][NKS], ml[RT][NKS];
-    f32x4 s[RT];
+    bf16x8 mh[NKS], ml[NKS];
+    f32x4 s;
   };
   auto load = [&](Ops& o, int j) {
     const int64_t slot = (sg0 + j) * H + h;
     const bf16* Mh = reinterpret_cast<const bf16*>(plan.cp.mcorr) + slot * 2 * DK * DK;
     const bf16* Ml = Mh + DK * DK;
     const float* Sj = plan.cp.sstar + slot * DK * dv;
+    o.s = *reinterpret_cast<const f32x4*>(Sj + ((int64_t)(cb * (DK / 16) + wave) * 64 + lane) * 4);
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const int rb = 16 * (RT * wave + t);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o.s[t][i] = Sj[(int64_t)(rb + 4 * q + i) * dv + col + r16];
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const int64_t at = ((int64_t)((RT * wave + t) * NKS + s) * 64 + lane) * 8;   // mfrag_offset order
-        o.mh[t][s] = *reinterpret_cast<const bf16x8*>(Mh + at);
-        o.ml[t][s] = *reinterpret_cast<const bf16x8*>(Ml + at);
-      }
+    for (int s = 0; s < NKS; ++s) {
+      const int64_t at = ((int64_t)(wave * NKS + s) * 64 + lane) * 8;   // mfrag_offset order
+      o.mh[s] = *reinterpret_cast<const bf16x8*>(Mh + at);
+      o.ml[s] = *reinterpret_cast<const bf16x8*>(Ml + at);
     }
   };
 
-  // three operand sets in flight: step j computes with set j % 3 while the loads of
-  // step j + 2 land in the set step j - 1 used (load counts are the same every step,
-  // the index is clamped at the end, so no step waits on loads it does not need)
+  // Step j computes with set j % NSET and then refills it with the operands of step
+  // j + NSET (clamped at the end: load counts are the same every step, so no step
+  // waits on loads it does not need).  State copy j % 2 is read, copy (j+1) % 2
+  // written: a wave can only write a copy again after the next barrier, which every
+  // wave reaches after its reads of that copy.
   const int steps = segs - 1;
-  auto body = [&](const Ops& cur, Ops& far, int j) {
-    load(far, min(j + 2, steps - 1));
-    f32x4 acc[RT];
+  auto store_state = [&](int64_t seg_slot, const f32x4& x) {
+    float* Hs = plan.cp.hstart + seg_slot * DK * dv;
 #pragma unroll
-    for (int t = 0; t < RT; ++t) acc[t] = cur.s[t];
+    for (int i = 0; i < 4; ++i) Hs[(int64_t)(16 * wave + 4 * q + i) * dv + col + r16] = x[i];
+  };
+  auto body = [&](Ops& cur, int j) {
+    const bf16* hHi = sHi[j & 1];
+    const bf16* hLo = sLo[j & 1];
+    bf16x8 bh[NKS], bl[NKS];
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      const bf16x8 bh = lds_frag(sHi, HS, r16, 32 * s, q);
-      const bf16x8 bl = lds_frag(sLo, HS, r16, 32 * s, q);
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        acc[t] = Mma<bf16>::run(cur.mh[t][s], bh, acc[t]);
-        acc[t] = Mma<bf16>::run(cur.mh[t][s], bl, acc[t]);
-        acc[t] = Mma<bf16>::run(cur.ml[t][s], bh, acc[t]);
-      }
+      bh[s] = lds_frag(hHi, HS, r16, 32 * s, q);
+      bl[s] = lds_frag(hLo, HS, r16, 32 * s, q);
     }
-    __syncthreads();  // every wave has read the old state
-    const int64_t slot = (sg0 + j) * H + h;
-    float* Hn = plan.cp.hstart + (slot + H) * DK * dv;   // start of segment j+1
+    f32x4 a0 = cur.s, a1 = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const int rb = 16 * (RT * wave + t);
+    for (int s = 0; s < NKS; ++s) {
+      a0 = Mma<bf16>::run(cur.mh[s], bh[s], a0);
+      a1 = Mma<bf16>::run(cur.mh[s], bl[s], a1);
+      a2 = Mma<bf16>::run(cur.ml[s], bh[s], a2);
+    }
+    load(cur, min(j + NSET, steps - 1));
+    const f32x4 x = a0 + a1 + a2;
+    store_state((sg0 + j + 1) * H + h, x);   // start of segment j+1
+    bf16* nHi = sHi[(j + 1) & 1];
+    bf16* nLo = sLo[(j + 1) & 1];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = rb + 4 * q + i;
-        const float x = acc[t][i];
-        Hn[(int64_t)r * dv + col + r16] = x;
-        const bf16 hi = (bf16)x;
-        sHi[r16 * HS + r] = hi;
-        sLo[r16 * HS + r] = (bf16)(x - (float)hi);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * wave + 4 * q + i;
+      const bf16 hi = (bf16)x[i];
+      nHi[r16 * HS + r] = hi;
+      nLo[r16 * HS + r] = (bf16)(x[i] - (float)hi);
     }
     __syncthreads();
   };
-  Ops o0, o1, o2;
-  load(o0, 0);
-  load(o1, min(1, steps - 1));
-  int j = 0;
-  for (; j + 3 <= steps; j += 3) {   // no conditions inside: every path issues the same loads
-    body(o0, o2, j);
-    body(o1, o0, j + 1);
-    body(o2, o1, j + 2);
+  // Prologue: the compiler sizes each wait in the loop for the worst path into it,
+  // so the prologue issues the same memory operations in the same order as a step
+  // (a set's loads, then four state stores; here the start state of segment 0, which
+  // is its true start); loads issued back to back would make every wait of the
+  // loop wait for loads issued one step earlier.
+  f32x4 x0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * wave + 4 * q + i;
+    x0[i] = p.h0 ? p.h0[((int64_t)nh * DK + r) * dv + col + r16] : 0.f;
   }
-  if (j < steps) body(o0, o2, j);
-  if (j + 1 < steps) body(o1, o0, j + 1);
+  Ops o[NSET];
+#pragma unroll
+  for (int i = 0; i < NSET; ++i) {
+    load(o[i], min(i, steps - 1));
+    store_state(sg0 * H + h, x0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  int j = 0;
+  for (; j + NSET <= steps; j += NSET) {   // no conditions inside: every path issues the same loads
+#pragma unroll
+    for (int i = 0; i < NSET; ++i) body(o[i], j + i);
+  }
+#pragma unroll
+  for (int i = 0; i < NSET - 1; ++i)
+    if (j + i < steps) body(o[i], j + i);
 }
 
 hipError_t launch_cp_merge(const Problem& p, const FwdPlan& plan, hipStream_t s) {
   if (p.N == 0) return hipSuccess;
-  dim3 grid((unsigned)(p.N * p.H), (unsigned)(p.dv / 16));
-  if (p.dk == 128) cp_merge_kernel<128><<<grid, 256, 0, s>>>(p, plan);
-  else cp_merge_kernel<64><<<grid, 256, 0, s>>>(p, plan);
+  const int64_t units = (int64_t)p.N * p.H;
+  const unsigned grid = (unsigned)((units + 7) / 8 * 8 * (p.dv / 16));
+  if (p.dk == 128) cp_merge_kernel<128><<<grid, 64 * MergeCfg<128>::NW, 0, s>>>(p, plan);
+  else cp_merge_kernel<64><<<grid, 64 * MergeCfg<64>::NW, 0, s>>>(p, plan);
   return hipGetLastError();
 }
 

@@ -135,7 +135,8 @@ struct ChunkRegs {
     }
   }
 
-  template <int KS, int CS, int VS>
+  // SQ = false: the chunk produces no output (a lookback chunk), Q is not staged
+  template <int KS, int CS, int VS, bool SQ = WITH_Q>
   __device__ __forceinline__ void store(E* sK, E* sQ, E* sV, E* sT, float* sB, bool beta_bf16,
                                         bool vzero, int tid) const {
     const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -145,7 +146,7 @@ struct ChunkRegs {
       const bool ok = r < len;
       const int lr = tord(r);
       *reinterpret_cast<u32x4*>(sK + lr * KS + cv * EPV) = ok ? k[j] : zero;
-      if constexpr (WITH_Q) *reinterpret_cast<u32x4*>(sQ + lr * KS + cv * EPV) = ok ? q[j] : zero;
+      if constexpr (WITH_Q && SQ) *reinterpret_cast<u32x4*>(sQ + lr * KS + cv * EPV) = ok ? q[j] : zero;
     }
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
@@ -551,11 +552,13 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
 
   // Stages chunk cs (registers of st) in buffer b: the gates of chunk cs are scanned in
   // registers (every wave holds all rows: lane = chunk row); returns gamma_last.
-  auto stage = [&](Stage& st, int cs, int b) {
+  // q_tag (compile-time): whether Q is staged (a lookback chunk has no output).
+  auto stage = [&](auto q_tag, Stage& st, int cs, int b) {
     const int len = min(kChunk, si.len - cs * kChunk);
     const float G = wave_inclusive_scan_dpp(lane < len ? st.g : 0.f);
     const float Glast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), kChunk - 1));
-    st.template store<KS, CS, VS>(sKb[b], sQb[b], sVb[b], sTb[b], sBetb[b], p.beta_bf16, mcols, tid);
+    st.template store<KS, CS, VS, decltype(q_tag)::value>(sKb[b], sQb[b], sVb[b], sTb[b], sBetb[b],
+                                                          p.beta_bf16, mcols, tid);
     if (wave == 0) {
       const float gam = fast_exp(G);
       sGb[b][lane] = G;
@@ -573,15 +576,20 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
   // end of the step, so the next chunk starts right after the one barrier.
   int len_prev = 0;
   float gC = 0.f;
-  auto chunk = [&](Stage& ld, Stage& sg, int c) {
+  // q_tag (compile-time): whether chunk c + PF is loaded with its Q (false while it is
+  // still a lookback chunk: no output, so no Q traffic).
+  auto chunk = [&](auto q_tag, Stage& ld, Stage& sg, int c) {
+    constexpr bool LOADQ = decltype(q_tag)::value;
     const int len = min(kChunk, si.len - c * kChunk);
     if constexpr (NB == 1) {
-      gC = stage(ld, c, 0);
+      gC = stage(std::true_type{}, ld, c, 0);
       __syncthreads();
     }
     use_buffers(c % NB);
     const int cn = min(c + PF, c_end - 1);
-    auto load_part = [&](auto part) { issue_part(part, ld, cn); };
+    auto load_part = [&](auto part) {
+      if constexpr (LOADQ || decltype(part)::value != 1) issue_part(part, ld, cn);
+    };
     if constexpr (OUT) {
       if (c - 1 >= c_out && c - 1 >= c_start) emit_o(c - 1, len_prev);
     }
@@ -593,23 +601,26 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
       step(std::false_type{}, c, gC, load_part);
     }
     len_prev = len;
-    if constexpr (NB == 2) gC = stage(sg, min(c + 1, c_end - 1), (c + 1) % NB);
+    if constexpr (NB == 2) gC = stage(q_tag, sg, min(c + 1, c_end - 1), (c + 1) % NB);
     __syncthreads();
   };
   int c = c_start;
   if (c_start < c_end) {
     if constexpr (NB == 2) {
-      gC = stage(pf[0], c_start, c_start % NB);
+      gC = stage(std::true_type{}, pf[0], c_start, c_start % NB);
       __syncthreads();
     }
     if constexpr (PF == 1) {
-      for (; c < c_end; ++c) chunk(pf[0], pf[0], c);
+      if constexpr (OUT) {   // lookback chunks followed by another lookback chunk: no Q
+        for (; c + 1 < c_out && c < c_end; ++c) chunk(std::false_type{}, pf[0], pf[0], c);
+      }
+      for (; c < c_end; ++c) chunk(std::true_type{}, pf[0], pf[0], c);
     } else {
       for (; c + 2 <= c_end; c += 2) {   // no conditions inside: fixed load counts
-        chunk(pf[0], pf[1], c);
-        chunk(pf[1], pf[0], c + 1);
+        chunk(std::true_type{}, pf[0], pf[1], c);
+        chunk(std::true_type{}, pf[1], pf[0], c + 1);
       }
-      if (c < c_end) chunk(pf[0], pf[1], c);
+      if (c < c_end) chunk(std::true_type{}, pf[0], pf[1], c);
     }
   }
   if constexpr (OUT) {
@@ -638,23 +649,26 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
         }
     return;
   }
-  float* dst = nullptr;
-  int64_t dst_off = 0;
   if constexpr (PASS == kPass1) {
-    dst = plan.cp.sstar;
-    dst_off = (sg * H + h) * DK * dv + col0;
+    // S* as the merge's accumulator tiles (sfrag_offset): the four rows a lane holds
+    // in a tile are consecutive (prow(t, 4q + i) = prow(t, 4q) + i), so each tile
+    // leaves as one 16-byte store per lane
+    float* dst = plan.cp.sstar + (sg * H + h) * DK * dv;
+#pragma unroll
+    for (int t = 0; t < NKT; ++t)
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+        *reinterpret_cast<f32x4*>(dst + sfrag_offset<DK>(prow(t, 4 * q), col0 + wcol + ct * 16 + r16)) =
+            hs[t][ct];
   } else if (last_seg && p.hT) {
-    dst = p.hT;
-    dst_off = (int64_t)nh * DK * dv + col0;
-  }
-  if (dst) {
+    float* dst = p.hT + (int64_t)nh * DK * dv + col0;
 #pragma unroll
     for (int t = 0; t < NKT; ++t)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          dst[dst_off + (int64_t)prow(t, 4 * q + i) * dv + wcol + ct * 16 + r16] = hs[t][ct][i];
+          dst[(int64_t)prow(t, 4 * q + i) * dv + wcol + ct * 16 + r16] = hs[t][ct][i];
   }
 }
 

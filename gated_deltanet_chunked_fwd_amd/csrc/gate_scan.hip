@@ -16,7 +16,7 @@
 // The chunk gate sums come from the chunk-inverse kernel, which forms the chunk's
 // cumulative gate anyway (or, for the stand-alone entry point, from
 // chunk_gate_sums_kernel with the same wave scan, so both give identical sums).
-// gate_window_max: one block per (sequence, head) forms
+// gate_window_max: one 256-thread block per (sequence, head) forms
 // the maximum run sum per W (block_run_max) and stores it in best[nh][W] (floats as
 // order-preserving uints; 0 = no such run, so no reset is needed).  window_of()
 // turns best[] into W wherever it is needed; gate_window_finalize writes it out for
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void chunk_gate_sums_kernel(Problem p, float* 
   if (lane == kChunk - 1) csum[cg * p.H + h] = G;
 }
 
-constexpr int kScanThreads = 1024;   // run starts per pass of the gate-window scan
+constexpr int kScanThreads = 256;   // run starts per pass of the gate-window scan
 
 __global__ __launch_bounds__(kScanThreads) void gate_window_max_kernel(const float* __restrict__ csum,
                                                                        const int32_t* __restrict__ cu,

@@ -233,6 +233,16 @@ __device__ __forceinline__ int64_t mfrag_offset(int row, int col) {
          (col & 7);
 }
 
+// Accumulator-ordered storage of a DK x dv fp32 matrix read as 16x16 MFMA D tiles
+// (the merge's S*): lane l = 16 q + r of row tile rt, column tile ct holds rows
+// 16 rt + 4 q + i (i = 0..3) of column 16 ct + r, at float ((ct * DK/16 + rt) * 64
+// + l) * 4 + i, so one tile is a 1 KB contiguous 16-byte-per-lane load.
+template <int DK>
+__device__ __forceinline__ int64_t sfrag_offset(int row, int col) {
+  return ((int64_t)((col >> 4) * (DK / 16) + (row >> 4)) * 64 + 16 * ((row & 15) >> 2) + (col & 15)) * 4 +
+         (row & 3);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave without LDS traffic: DPP row
 // shifts scan each 16-lane row (lanes without a source add 0), then the row totals
 // are carried with v_readlane.
@@ -278,6 +288,12 @@ __device__ __forceinline__ int window_of(const uint32_t* best, int nh, int nch, 
 // cap floats (cap > kWindowMaxCap); red: LDS scratch of NT / 64 * kWindowMaxCap
 // floats.  Thread t < kWindowMaxCap returns the maximum for w = t + 1 (-inf: no run
 // of that length); the other threads return -inf.
+//
+// The 16 per-lane maxima are reduced over the wave by a halving butterfly: at the
+// exchange with lane ^ d (d = 32, 16, 8, 4) a lane keeps half of its windows (the
+// upper half if bit d of its lane is set) and sends the other half, so the wave
+// needs 8 + 4 + 2 + 1 + 2 shuffles instead of 16 x 6; afterwards lanes 4w .. 4w+3
+// hold window w + 1.
 template <int NT>
 __device__ float block_run_max(const float* csum, int64_t chunk0, int nch, int H, int h, int wmax,
                                float* sums, int cap, float* red) {
@@ -305,14 +321,23 @@ __device__ float block_run_max(const float* csum, int64_t chunk0, int nch, int H
       }
     }
   }
+  // halving butterfly over the wave (see above)
 #pragma unroll
-  for (int w = 0; w < kWindowMaxCap; ++w) {
-    float v = mx[w];
-    for (int d = 32; d > 0; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
-    if (lane == 0) red[wave * kWindowMaxCap + w] = v;
+  for (int half = kWindowMaxCap / 2, d = 32; half >= 1; half >>= 1, d >>= 1) {
+    const bool upper = (lane & d) != 0;
+#pragma unroll
+    for (int k = 0; k < half; ++k) {
+      const float send = upper ? mx[k] : mx[k + half];
+      const float keep = upper ? mx[k + half] : mx[k];
+      mx[k] = fmaxf(keep, __shfl_xor(send, d, 64));
+    }
   }
+  float v = mx[0];
+  v = fmaxf(v, __shfl_xor(v, 2, 64));
+  v = fmaxf(v, __shfl_xor(v, 1, 64));
+  if ((lane & 3) == 0) red[wave * kWindowMaxCap + (lane >> 2)] = v;
   __syncthreads();
-  float v = -INFINITY;
+  v = -INFINITY;
   if (tid < kWindowMaxCap) {
     v = red[tid];
 #pragma unroll

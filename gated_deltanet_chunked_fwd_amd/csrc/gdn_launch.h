@@ -34,7 +34,8 @@ struct CpBuffers {
   int wmax;                 // longest admissible window (chunks)
   float thr;                // window threshold: log_eps - margin
   int force_correction;     // 1: every split head uses the wrong-start correction
-  float* sstar;             // [total_segs, H, dk, dv] wrong-start (zero-start) segment end states
+  float* sstar;             // [total_segs, H] x [dk x dv] fp32 wrong-start (zero-start) segment
+                            // end states, each in accumulator-tile order (sfrag_offset)
   void* mcorr;              // [total_segs, H] x {hi, lo} x [dk, dk] bf16: segment transition
                             // matrices M split as M = hi + lo (hi block first), each block
                             // in MFMA operand order (mfrag_offset in gdn_device.h)
