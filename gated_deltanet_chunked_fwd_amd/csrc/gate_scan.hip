@@ -16,7 +16,7 @@
 // The chunk gate sums come from the chunk-inverse kernel, which forms the chunk's
 // cumulative gate anyway (or, for the stand-alone entry point, from
 // chunk_gate_sums_kernel with the same wave scan, so both give identical sums).
-// gate_window_max: one 256-thread block per (sequence, head) forms
+// gate_window_max: one block per (sequence, head) forms
 // the maximum run sum per W (block_run_max) and stores it in best[nh][W] (floats as
 // order-preserving uints; 0 = no such run, so no reset is needed).  window_of()
 // turns best[] into W wherever it is needed; gate_window_finalize writes it out for
@@ -43,20 +43,20 @@ __global__ __launch_bounds__(256) void chunk_gate_sums_kernel(Problem p, float* 
   if (lane == kChunk - 1) csum[cg * p.H + h] = G;
 }
 
-constexpr int kScanThreads = 256;   // run starts per pass of the gate-window scan
-
-__global__ __launch_bounds__(kScanThreads) void gate_window_max_kernel(const float* __restrict__ csum,
+// NT threads = run starts per pass of the gate-window scan: 256 for sequences of up
+// to 512 chunks, 1024 for longer ones (fewer serial passes when there are few blocks).
+template <int NT>
+__global__ __launch_bounds__(NT) void gate_window_max_kernel(const float* __restrict__ csum,
                                                                        const int32_t* __restrict__ cu,
                                                                        const int32_t* __restrict__ chunk_off,
                                                                        int64_t T, int N, int H, int wmax,
                                                                        uint32_t* __restrict__ best) {
-  __shared__ float sums[kScanThreads + kWindowMaxCap];
-  __shared__ float red[kScanThreads / 64 * kWindowMaxCap];
+  __shared__ float sums[NT + kWindowMaxCap];
+  __shared__ float red[NT / 64 * kWindowMaxCap];
   const int nh = blockIdx.x, n = nh / H, h = nh % H;
   const SeqInfo si = seq_info(n, cu, chunk_off, T);
   const int nch = (si.len + kChunk - 1) / kChunk;
-  const float v = block_run_max<kScanThreads>(csum, si.chunk0, nch, H, h, wmax, sums,
-                                              kScanThreads + kWindowMaxCap, red);
+  const float v = block_run_max<NT>(csum, si.chunk0, nch, H, h, wmax, sums, NT + kWindowMaxCap, red);
   const int w = threadIdx.x;   // thread w holds the maximum for runs of w + 1 chunks
   if (w < kWindowMaxCap)       // 0 = no run of that length
     best[nh * kWindowMaxCap + w] = (w < wmax && v > -INFINITY) ? ordered_bits(v) : 0u;
@@ -108,10 +108,13 @@ hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s) 
 
 hipError_t launch_gate_scan(const Problem& p, const float* csum, int64_t max_chunks, int wmax,
                             uint32_t* best, hipStream_t s) {
-  (void)max_chunks;
   if (p.N == 0) return hipSuccess;
-  gate_window_max_kernel<<<(unsigned)(p.N * p.H), kScanThreads, 0, s>>>(csum, p.cu, p.chunk_off, p.T,
-                                                                          p.N, p.H, wmax, best);
+  if (max_chunks > 512)
+    gate_window_max_kernel<1024><<<(unsigned)(p.N * p.H), 1024, 0, s>>>(csum, p.cu, p.chunk_off, p.T, p.N,
+                                                                        p.H, wmax, best);
+  else
+    gate_window_max_kernel<256><<<(unsigned)(p.N * p.H), 256, 0, s>>>(csum, p.cu, p.chunk_off, p.T, p.N,
+                                                                      p.H, wmax, best);
   return hipGetLastError();
 }
 

@@ -153,6 +153,7 @@ Plan make_plan(const gdn_shape* s, const gdn_opts* o) {
 
 struct Layout {
   size_t tmat = 0, chunk_off = 0, seg_off = 0, best = 0, csum = 0, sstar = 0, mcorr = 0, hstart = 0;
+  size_t gmat = 0, gvec = 0;
   size_t total = 0;
 };
 
@@ -171,6 +172,11 @@ Layout layout(const gdn_shape* s, const Plan& P) {
     L.sstar = take(slots * s->dk * s->dv * sizeof(float));
     L.mcorr = take(slots * 2 * s->dk * s->dk * sizeof(uint16_t));   // bf16 hi + lo
     L.hstart = take(slots * s->dk * s->dv * sizeof(float));
+    const int64_t max_steps = (P.max_chunks + P.seg_chunks - 1) / P.seg_chunks - 1;
+    if (max_steps > gdn::kMergeTreeMinSteps) {   // group maps of the tree merge
+      L.gmat = take(slots * 2 * s->dk * s->dk * sizeof(uint16_t));
+      L.gvec = take(slots * s->dk * s->dv * sizeof(float));
+    }
   }
   L.total = off;
   return L;
@@ -285,6 +291,8 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     plan.cp.sstar = reinterpret_cast<float*>(ws + L.sstar);
     plan.cp.mcorr = ws + L.mcorr;
     plan.cp.hstart = reinterpret_cast<float*>(ws + L.hstart);
+    plan.cp.gmat = L.gmat ? ws + L.gmat : nullptr;
+    plan.cp.gvec = L.gvec ? reinterpret_cast<float*>(ws + L.gvec) : nullptr;
     if (!plan.cp.force_correction) {
       StageMark mark(opts, GDN_STAGE_GATE_SCAN, stream);
       if (gdn::launch_gate_scan(p, csum, P.max_chunks, P.wmax, best, stream) != hipSuccess)
@@ -298,7 +306,8 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     }
     {
       StageMark mark(opts, GDN_STAGE_CP_MERGE, stream);
-      if (gdn::launch_cp_merge(p, plan, stream) != hipSuccess) return GDN_ERR_HIP;
+      const int max_steps = (int)((P.max_chunks + P.seg_chunks - 1) / P.seg_chunks - 1);
+      if (gdn::launch_cp_merge(p, plan, max_steps, stream) != hipSuccess) return GDN_ERR_HIP;
     }
   }
   {

@@ -271,15 +271,25 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t u) {
 }
 
 // Smallest admissible lookback window (chunks) of (sequence, head) nh from the
-// gate-scan maxima; 0 if none.
+// gate-scan maxima; 0 if none.  The 16 maxima are loaded at once (64 bytes, 16-byte
+// aligned) and searched in registers: a load per candidate behind the early exit
+// would cost one memory latency per window length tried.
 __device__ __forceinline__ int window_of(const uint32_t* best, int nh, int nch, int wmax,
                                          float thr) {
-  const int lim = min(wmax, nch);
-  for (int w = 1; w <= lim; ++w) {
-    const uint32_t u = best[nh * kWindowMaxCap + (w - 1)];
-    if (u != 0u && from_ordered_bits(u) <= thr) return w;
+  static_assert(kWindowMaxCap == 16, "one 64-byte row of maxima per (sequence, head)");
+  const uint4* row = reinterpret_cast<const uint4*>(best + (int64_t)nh * kWindowMaxCap);
+  uint32_t u[kWindowMaxCap];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 x = row[i];
+    u[4 * i] = x.x; u[4 * i + 1] = x.y; u[4 * i + 2] = x.z; u[4 * i + 3] = x.w;
   }
-  return 0;
+  const int lim = min(wmax, nch);
+  int found = 0;
+#pragma unroll
+  for (int w = kWindowMaxCap; w >= 1; --w)   // the smallest admissible w wins
+    if (w <= lim && u[w - 1] != 0u && from_ordered_bits(u[w - 1]) <= thr) found = w;
+  return found;
 }
 
 // Largest gate sum over every run of w consecutive chunks (w = 1..wmax) of one

@@ -40,7 +40,12 @@ struct CpBuffers {
                             // matrices M split as M = hi + lo (hi block first), each block
                             // in MFMA operand order (mfrag_offset in gdn_device.h)
   float* hstart;            // [total_segs, H, dk, dv] true segment start states
+  void* gmat;               // long merge chains, per group of steps (slot of the group's first
+  float* gvec;              // segment): composed map A (as mcorr) and offset b (as sstar)
 };
+
+// Merge chains of more steps than this run as a two-level tree (cp_merge.hip).
+constexpr int kMergeTreeMinSteps = 16;
 
 // Work description for one launch of the fused forward kernel.  A work unit is
 // (sequence, head, segment); the kernel grid covers units x column blocks.
@@ -70,7 +75,8 @@ hipError_t launch_gate_scan(const Problem& p, const float* csum, int64_t max_chu
                             uint32_t* best, hipStream_t s);
 hipError_t launch_gate_finalize(const Problem& p, const uint32_t* best, int wmax, float thr,
                                 int32_t* out, hipStream_t s);
-hipError_t launch_cp_merge(const Problem& p, const FwdPlan& plan, hipStream_t s);
+// max_steps: the most segment boundaries of any sequence (segments - 1).
+hipError_t launch_cp_merge(const Problem& p, const FwdPlan& plan, int max_steps, hipStream_t s);
 // csum (nullable): [total_chunks, H] per-chunk gate sums, written on the side.
 hipError_t launch_chunk_inverse(const Problem& p, void* t_out, float* csum, hipStream_t s);
 hipError_t launch_fused_forward(const Problem& p, const FwdPlan& plan, hipStream_t s);

@@ -57,6 +57,25 @@ def test_split_parity_packed(corr):
     assert_parity(compare_pairs(inp, o, hT), TOL["bf16"], "packed corr=%d" % corr)
 
 
+@pytest.mark.parametrize("seg", [1, 2])
+def test_split_tree_merge(seg):
+    """Merge chains longer than 16 steps run as a two-level tree (group maps
+    composed in parallel, a chain over groups, then each group's own steps): 40 and
+    20 steps, with an uneven last group for seg=1."""
+    inp = synth.generate(spec(B=1, T=64 * 40 + 9, H=2, seed=75 + seg, zero_gate_heads=(0,),
+                              h0_std=0.05))
+    o, hT = run_gpu(inp, opts=binding.make_opts(force_segment_chunks=seg, force_correction=1))
+    assert_parity(compare_pairs(inp, o, hT), TOL["bf16"], "tree merge seg=%d" % seg)
+
+
+def test_split_tree_merge_packed():
+    """Tree merge with sequences of different step counts (29, 16, 2, 0 steps, and
+    an empty sequence): every sequence uses the same group length."""
+    inp = _packed([64 * 30, 64 * 17 - 5, 64 * 3, 0, 50], H=2, seed=78, zero_heads=(0, 1))
+    o, hT = run_gpu(inp, opts=binding.make_opts(force_segment_chunks=1))
+    assert_parity(compare_pairs(inp, o, hT), TOL["bf16"], "tree merge packed")
+
+
 def test_split_value_block_64_and_dk64_dv128():
     inp = synth.generate(spec(B=1, T=64 * 8, H=2, dk=64, dv=128, seed=73, zero_gate_heads=(0,)))
     for vb in (64, 128):
