@@ -74,19 +74,22 @@ struct ChunkRegs {
   uint32_t b;   // raw beta bits (bf16 in the low half, or fp32)
   int len;
 
-  // Per-thread element offsets inside a full chunk (fixed for the whole walk).
+  // Per-thread offsets inside a full chunk (fixed for the whole walk): k, v in bytes
+  // (32-bit, added to the chunk's uniform base pointer, so a load needs no 64-bit
+  // address arithmetic), g in elements.
   struct Offsets {
-    int k[NK], v[NV], g;
+    uint32_t k[NK], v[NV];
+    int g;
     __device__ __forceinline__ void init(int row_qk, int row_v, int row_g, int tid) {
 #pragma unroll
       for (int j = 0; j < NK; ++j) {
         const int i = tid + NTH * j;
-        k[j] = (i / VPRK) * row_qk + (i % VPRK) * EPV;
+        k[j] = (uint32_t)((i / VPRK) * row_qk + (i % VPRK) * EPV) * (uint32_t)sizeof(E);
       }
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
         const int i = tid + NTH * j;
-        v[j] = (i / VPRV) * row_v + (i % VPRV) * EPV;
+        v[j] = (uint32_t)((i / VPRV) * row_v + (i % VPRV) * EPV) * (uint32_t)sizeof(E);
       }
       g = (tid & (kChunk - 1)) * row_g;
     }
@@ -113,9 +116,9 @@ struct ChunkRegs {
 #pragma unroll
       for (int j = 0; j < NK; ++j) {
         const int r = (tid + NTH * j) / VPRK;
-        const int o = (full || r < len_) ? of.k[j] : (tid + NTH * j) % VPRK * EPV;
-        if constexpr (PART == 0) k[j] = *reinterpret_cast<const u32x4*>(kb + o);
-        else q[j] = *reinterpret_cast<const u32x4*>(qb + o);
+        const uint32_t o = (full || r < len_) ? of.k[j] : (uint32_t)((tid + NTH * j) % VPRK) * 16u;
+        if constexpr (PART == 0) k[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(kb) + o);
+        else q[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(qb) + o);
       }
     }
     // V is loaded even when it is not used (vzero: masked at store time), so every
@@ -125,13 +128,15 @@ struct ChunkRegs {
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
         const int r = (tid + NTH * j) / VPRV;
-        const int o = (full || r < len_) ? of.v[j] : (tid + NTH * j) % VPRV * EPV;
-        v[j] = *reinterpret_cast<const u32x4*>(vb + o);
+        const uint32_t o = (full || r < len_) ? of.v[j] : (uint32_t)((tid + NTH * j) % VPRV) * 16u;
+        v[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(vb) + o);
       }
     }
     if constexpr (PART == 3) {
 #pragma unroll
-      for (int j = 0; j < NT; ++j) t[j] = reinterpret_cast<const u32x4*>(ts)[tid + NTH * j];
+      for (int j = 0; j < NT; ++j)
+        t[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(ts) +
+                                                (uint32_t)(tid + NTH * j) * 16u);
     }
   }
 
@@ -140,18 +145,33 @@ struct ChunkRegs {
   __device__ __forceinline__ void store(E* sK, E* sQ, E* sV, E* sT, float* sB, bool beta_bf16,
                                         bool vzero, int tid) const {
     const u32x4 zero = {0u, 0u, 0u, 0u};
+    if (len == kChunk && !vzero) {   // full chunk: no masking
 #pragma unroll
-    for (int j = 0; j < NK; ++j) {
-      const int i = tid + NTH * j, r = i / VPRK, cv = i % VPRK;
-      const bool ok = r < len;
-      const int lr = tord(r);
-      *reinterpret_cast<u32x4*>(sK + lr * KS + cv * EPV) = ok ? k[j] : zero;
-      if constexpr (WITH_Q && SQ) *reinterpret_cast<u32x4*>(sQ + lr * KS + cv * EPV) = ok ? q[j] : zero;
-    }
+      for (int j = 0; j < NK; ++j) {
+        const int i = tid + NTH * j, r = i / VPRK, cv = i % VPRK;
+        const int lr = tord(r);
+        *reinterpret_cast<u32x4*>(sK + lr * KS + cv * EPV) = k[j];
+        if constexpr (WITH_Q && SQ) *reinterpret_cast<u32x4*>(sQ + lr * KS + cv * EPV) = q[j];
+      }
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int i = tid + NTH * j, r = i / VPRV, cv = i % VPRV;
-      *reinterpret_cast<u32x4*>(sV + r * VS + cv * EPV) = (r < len && !vzero) ? v[j] : zero;
+      for (int j = 0; j < NV; ++j) {
+        const int i = tid + NTH * j, r = i / VPRV, cv = i % VPRV;
+        *reinterpret_cast<u32x4*>(sV + r * VS + cv * EPV) = v[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NK; ++j) {
+        const int i = tid + NTH * j, r = i / VPRK, cv = i % VPRK;
+        const bool ok = r < len;
+        const int lr = tord(r);
+        *reinterpret_cast<u32x4*>(sK + lr * KS + cv * EPV) = ok ? k[j] : zero;
+        if constexpr (WITH_Q && SQ) *reinterpret_cast<u32x4*>(sQ + lr * KS + cv * EPV) = ok ? q[j] : zero;
+      }
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int i = tid + NTH * j, r = i / VPRV, cv = i % VPRV;
+        *reinterpret_cast<u32x4*>(sV + r * VS + cv * EPV) = (r < len && !vzero) ? v[j] : zero;
+      }
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {

@@ -93,8 +93,9 @@ def test_planner_default_split_parity():
     assert_parity(compare_pairs(inp, o, hT), TOL["bf16"], "planner L=%d" % L)
 
 
+@pytest.mark.parametrize("eps_bits", [24, 16])
 @pytest.mark.parametrize("kind", ["sigmoid", "uniform", "mixed", "packed"])
-def test_gate_scan_stage(kind):
+def test_gate_scan_stage(kind, eps_bits):
     """GPU window decision vs the fp64 brute force: the GPU's W must be admissible in
     fp64 (every W-run sums to <= log eps) and minimal up to the 1e-3 margin band."""
     if kind == "packed":
@@ -104,9 +105,13 @@ def test_gate_scan_stage(kind):
         inp = synth.generate(spec(B=2, T=64 * 40 + 9, H=4, gate=gk, seed=82,
                                   zero_gate_heads=(3,) if kind == "mixed" else ()))
     d = to_dev(inp)
-    win = binding.gate_scan(d["g"], d["cu_seqlens"], inp.get("cu_seqlens")).cpu().numpy()
+    le = math.log(2.0 ** -eps_bits)
+    win = binding.gate_scan(d["g"], d["cu_seqlens"], inp.get("cu_seqlens"),
+                            opts=binding.make_opts(window_log_eps=le)).cpu().numpy()
+    if eps_bits == 24:   # the default
+        win_default = binding.gate_scan(d["g"], d["cu_seqlens"], inp.get("cu_seqlens")).cpu().numpy()
+        assert (win_default == win).all()
     g64 = synth.as_f64(inp["g"])
-    le = math.log(2.0 ** -24)
     B, T, H = g64.shape
     cu = (inp["cu_seqlens"].numpy() if inp.get("cu_seqlens") is not None
           else np.arange(B + 1) * T)
