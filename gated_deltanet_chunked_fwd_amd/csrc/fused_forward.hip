@@ -34,6 +34,7 @@
 #define GDN_P_FIRST 1
 #endif
 
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -434,9 +435,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
           const float Gq = sG[qrow];
           const f32x4 Gk = *reinterpret_cast<const f32x4*>(sG + key0);
           E* dst = sp + (16 * qt + r16) * CS + key0;
+          f32x4 pv;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            dst[i] = from_f32<E>(key0 + i <= qrow ? p.scale * acc[i] * fast_exp(Gq - Gk[i]) : 0.f);
+          for (int i = 0; i < 4; ++i) pv[i] = key0 + i <= qrow ? p.scale * acc[i] * fast_exp(Gq - Gk[i]) : 0.f;
+          store4(dst, pv);   // four adjacent keys: one 8-byte (bf16) or 16-byte store
         }
       }
     }
