@@ -25,6 +25,9 @@ traffic = HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE (fr
 profiles/traffic_fused_forward.json) if those counters were taken on the current
 kernel source, else null.
 
+path.copy_gbs_context: read + write GB/s of a plain 512 MiB device copy on the same
+stream, as context for what the HBM roofline allows in practice.
+
 cpu_baseline: the fp64 oracle (plain C, OpenMP) on the host cores, rank 0 only.
 
 Prints ONE JSON line.
@@ -157,12 +160,29 @@ def stage_bytes(stage, spec, lengths, seg_chunks, windows, has_h0, has_hT):
     return algorithmic_bytes(spec, len(lengths), has_h0, has_hT)
 
 
-def algorithmic_flops(spec):
+def algorithmic_flops(spec, triangular=False):
     """Per token-head: 6 dk dv (K h, Q h, K~^T U) + 4 C (dk + dv) (K K^T, Q K^T, T V', P U)
-    + C^2/3 (triangular inverse), C = 64, full C x C tiles."""
+    + C^2/3 (triangular inverse), C = 64, full C x C tiles; triangular=True counts only
+    the lower triangles of the four C x C products (2 C (dk + dv))."""
     C = 64
     th = spec.B * spec.T * spec.H
-    return th * (6 * spec.dk * spec.dv + 4 * C * (spec.dk + spec.dv) + C * C / 3.0)
+    tiles = (2 if triangular else 4) * C * (spec.dk + spec.dv)
+    return th * (6 * spec.dk * spec.dv + tiles + C * C / 3.0)
+
+
+def copy_bandwidth(hip, stream, torch, mib=512, reps=5):
+    """Context for the HBM roofline: GB/s (read + write) of a plain device copy of
+    mib MiB, timed with HIP events on the bench stream."""
+    src = torch.ones(mib << 18, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ev = hip.events(2)
+    hip.record(ev[0], stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    hip.record(ev[1], stream)
+    ms = hip.elapsed(ev[0], ev[1]) / reps
+    return 2 * (mib << 20) / (ms * 1e-3) / 1e9
 
 
 def source_sha(path):
@@ -318,6 +338,7 @@ def main():
         windows = binding.gate_scan(d["g"], d["cu_seqlens"], cu_host).cpu().tolist()
     dom_bytes = stage_bytes(dom, spec, lengths, seg_chunks, windows, has_h0, True)
     flops = algorithmic_flops(spec)
+    copy_gbs = copy_bandwidth(hip, stream, torch)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     ksrc = os.path.join(ROOT, "gated_deltanet_chunked_fwd_amd", "csrc", "fused_forward.hip")
     traffic = traffic_for(ksrc) if dom == "fused_forward" else None
@@ -344,7 +365,9 @@ def main():
                      "algorithmic_bytes": dom_bytes, "kernel_ms": dom_ms},
         "path": {"hbm_frac": alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                  "mfma_frac": flops / (ms * 1e-3) / 1e12 / mfma_peak,
-                 "algorithmic_flops": flops, "stage_ms": st_mean,
+                 "algorithmic_flops": flops,
+                 "algorithmic_flops_triangular": algorithmic_flops(spec, triangular=True),
+                 "copy_gbs_context": copy_gbs, "stage_ms": st_mean,
                  "ms_per_step_hot_caches": hot_ms, "ms_min": min(step_ms),
                  "ms_median": ms_median,
                  "wall_s_timed_loop_incl_flush": wall},

@@ -172,3 +172,60 @@ def test_packed_equals_separate_runs_bitwise():
         o1, h1 = run_gpu(one)
         assert torch.equal(o1[0].cpu(), o[0, s:e].cpu())
         assert torch.equal(h1[0].cpu(), hT[n].cpu())
+
+
+def _basis_inputs(T, H, dk, dv, m, seed, dtype):
+    """k_t = q_t = e_{t mod m} (m < 64: keys repeat inside a chunk), beta = 1, g = 0,
+    zero initial state, scale 1/8 (a power of two); v = integers in [-64, 64] / 16, so
+    every sum or difference of two values is an integer of at most 8 bits over 16,
+    exact in bf16."""
+    g = torch.Generator().manual_seed(seed)
+    idx = torch.arange(T) % m
+    kq = torch.zeros(1, T, H, dk)
+    kq[0, torch.arange(T), :, idx] = 1.0
+    v = (torch.randint(-64, 65, (1, T, H, dv), generator=g).float() / 16).to(dtype)
+    return dict(q=kq.to(dtype), k=kq.to(dtype).clone(), v=v, g=torch.zeros(1, T, H),
+                beta=torch.ones(1, T, H).to(dtype), h0=None, cu_seqlens=None, scale=0.125)
+
+
+@pytest.mark.parametrize("m,dk,dv", [(5, 128, 128), (17, 64, 128), (63, 128, 64)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_basis_keys_with_repeats(m, dk, dv, dtype):
+    """Closed form: with k_t = q_t = e_{t mod m}, beta = 1, g = 0 and S_0 = 0, the
+    delta rule replaces column t mod m of S by v_t, so o_t = scale v_t, and row j < m
+    of the final state is v of the last token with key e_j.  Every intermediate of the
+    chunked form is then exact in both precisions (T has entries in {-1, 0, 1}, the
+    gates are exp(0) = 1, V' = v - h and U are differences of two values, all integers
+    of at most 8 bits over 16, and the bf16 MFMA operands hold them exactly), so the
+    GPU must match to the bit."""
+    T, H = 300, 2
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    inp = _basis_inputs(T, H, dk, dv, m, seed=60 + m, dtype=tdt)
+    o, hT = run_gpu(inp)
+    want_h = torch.zeros(1, H, dk, dv)
+    for j in range(m):
+        last = max(t for t in range(T) if t % m == j)
+        want_h[0, :, j, :] = inp["v"][0, last].float()
+    want_o = inp["v"] * 0.125
+    bad = (o.cpu().float() != want_o.float()).sum().item()
+    print("basis keys m=%d %s: %d of %d outputs differ, max |diff| %.3e" % (
+        m, dtype, bad, o.numel(), (o.cpu().float() - want_o.float()).abs().max().item()))
+    assert torch.equal(o.cpu(), want_o)
+    assert torch.equal(hT.cpu(), want_h)
+
+
+def test_beta_one_last_token_closed_form():
+    """Closed form: a delta-rule update with beta = 1 and a unit key makes the new state
+    map that key to its value exactly, whatever alpha and the prior state: with beta = 1
+    on the last token, sum_i hT[i, j] k_T[i] = v_T[j] (up to the bf16/fp32 rounding of
+    the chunked products)."""
+    inp = synth.generate(spec(B=2, T=333, H=3, dk=128, dv=128, h0_std=0.05, seed=61))
+    beta = inp["beta"].clone()
+    beta[:, -1] = 1.0
+    inp["beta"] = beta
+    o, hT = run_gpu(inp)
+    k_last = inp["k"][:, -1].float()              # [B, H, dk]
+    v_last = inp["v"][:, -1].float()              # [B, H, dv]
+    got = torch.einsum("bhij,bhi->bhj", hT.cpu().float(), k_last)
+    rel = (got - v_last).norm() / v_last.norm()
+    assert rel < 1e-2, rel
