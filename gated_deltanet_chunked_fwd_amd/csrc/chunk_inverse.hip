@@ -88,9 +88,11 @@ __device__ __forceinline__ typename Mma<E>::frag load_frag(const E* src, bool ok
 
 }  // namespace
 
+// full = 0: the upper-right 32 x 32 quadrant of T (zero) is not written; the fused
+// forward never reads it.
 template <typename E, int DK>
 __global__ __launch_bounds__(256) void chunk_inverse_kernel(Problem p, E* __restrict__ tout,
-                                                             float* __restrict__ csum) {
+                                                             float* __restrict__ csum, int full) {
   using Cfg = InvCfg<E, DK>;
   using M = Mma<E>;
   using frag = typename M::frag;
@@ -250,7 +252,8 @@ __global__ __launch_bounds__(256) void chunk_inverse_kernel(Problem p, E* __rest
     const int idx = 64 * j + lane, row = idx / SPR, seg = idx % SPR;
     u32x4 v = {0u, 0u, 0u, 0u};
     if (seg * EPV < 16 * (row / 16 + 1)) v = *reinterpret_cast<const u32x4*>(sOut + row * OS + seg * EPV);
-    *reinterpret_cast<u32x4*>(dst + row * kChunk + seg * EPV) = v;
+    if (full || row >= kChunk / 2 || seg * EPV < kChunk / 2)
+      *reinterpret_cast<u32x4*>(dst + row * kChunk + seg * EPV) = v;
   }
 }
 
@@ -270,17 +273,17 @@ hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hi
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_inverse(const Problem& p, void* t_out, float* csum, hipStream_t s) {
+hipError_t launch_chunk_inverse(const Problem& p, void* t_out, float* csum, bool full, hipStream_t s) {
   if (p.total_chunks == 0) return hipSuccess;
   const int64_t blocks = p.total_chunks * ((p.H + 3) / 4);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks);
   if (p.qkv_bf16) {
-    if (p.dk == 128) chunk_inverse_kernel<bf16, 128><<<grid, 256, 0, s>>>(p, (bf16*)t_out, csum);
-    else chunk_inverse_kernel<bf16, 64><<<grid, 256, 0, s>>>(p, (bf16*)t_out, csum);
+    if (p.dk == 128) chunk_inverse_kernel<bf16, 128><<<grid, 256, 0, s>>>(p, (bf16*)t_out, csum, full ? 1 : 0);
+    else chunk_inverse_kernel<bf16, 64><<<grid, 256, 0, s>>>(p, (bf16*)t_out, csum, full ? 1 : 0);
   } else {
-    if (p.dk == 128) chunk_inverse_kernel<float, 128><<<grid, 256, 0, s>>>(p, (float*)t_out, csum);
-    else chunk_inverse_kernel<float, 64><<<grid, 256, 0, s>>>(p, (float*)t_out, csum);
+    if (p.dk == 128) chunk_inverse_kernel<float, 128><<<grid, 256, 0, s>>>(p, (float*)t_out, csum, full ? 1 : 0);
+    else chunk_inverse_kernel<float, 64><<<grid, 256, 0, s>>>(p, (float*)t_out, csum, full ? 1 : 0);
   }
   return hipGetLastError();
 }

@@ -71,6 +71,10 @@ struct ChunkRegs {
   static_assert(NK * NTH == kChunk * VPRK && NV * NTH == kChunk * VPRV && NT * NTH == kChunk * VPRT,
                 "chunk tiles must split evenly over the threads");
   u32x4 k[NK], q[NK], v[NV], t[NT];
+  // 16-byte piece i of a chunk's T lies in the upper-right 32 x 32 quadrant
+  static __device__ __forceinline__ bool t_quadrant(int i) {
+    return i / VPRT < kChunk / 2 && (i % VPRT) * EPV >= kChunk / 2;
+  }
   float g;
   uint32_t b;   // raw beta bits (bf16 in the low half, or fp32)
   int len;
@@ -134,10 +138,16 @@ struct ChunkRegs {
       }
     }
     if constexpr (PART == 3) {
+      // T's upper-right 32 x 32 quadrant is zero and never read (the U product's
+      // 32-column steps stay at or below the diagonal): not loaded
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
-        t[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(ts) +
-                                                (uint32_t)(tid + NTH * j) * 16u);
+      for (int j = 0; j < NT; ++j) {
+        const int i = tid + NTH * j;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        t[j] = zero;
+        if (!t_quadrant(i))
+          t[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(ts) + (uint32_t)i * 16u);
+      }
     }
   }
 
@@ -177,7 +187,7 @@ struct ChunkRegs {
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const int i = tid + NTH * j, r = i / VPRT, cv = i % VPRT;
-      *reinterpret_cast<u32x4*>(sT + tord(r) * CS + cv * EPV) = t[j];
+      if (!t_quadrant(i)) *reinterpret_cast<u32x4*>(sT + tord(r) * CS + cv * EPV) = t[j];
     }
     if (tid < kChunk) {
       const float bf = beta_bf16 ? __uint_as_float(b << 16) : __uint_as_float(b);

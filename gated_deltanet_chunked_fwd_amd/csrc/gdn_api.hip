@@ -271,7 +271,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
   float* csum = P.split ? reinterpret_cast<float*>(ws + L.csum) : nullptr;
   {
     StageMark mark(opts, GDN_STAGE_INVERSE, stream);
-    if (gdn::launch_chunk_inverse(p, tmat, csum, stream) != hipSuccess) return GDN_ERR_HIP;
+    if (gdn::launch_chunk_inverse(p, tmat, csum, false, stream) != hipSuccess) return GDN_ERR_HIP;
   }
 
   gdn::FwdPlan plan;
@@ -336,7 +336,7 @@ int gdn_chunk_inverse(const void* k, const float* g, const void* beta, const int
         hipSuccess)
       return GDN_ERR_HIP;
   }
-  if (gdn::launch_chunk_inverse(p, t_out, nullptr, stream) != hipSuccess) return GDN_ERR_HIP;
+  if (gdn::launch_chunk_inverse(p, t_out, nullptr, true, stream) != hipSuccess) return GDN_ERR_HIP;
   return GDN_OK;
 }
 

@@ -78,7 +78,10 @@ hipError_t launch_gate_finalize(const Problem& p, const uint32_t* best, int wmax
 // max_steps: the most segment boundaries of any sequence (segments - 1).
 hipError_t launch_cp_merge(const Problem& p, const FwdPlan& plan, int max_steps, hipStream_t s);
 // csum (nullable): [total_chunks, H] per-chunk gate sums, written on the side.
-hipError_t launch_chunk_inverse(const Problem& p, void* t_out, float* csum, hipStream_t s);
+// full = false: T's zero upper-right 32 x 32 quadrant is left unwritten (the fused
+// forward never reads it).
+hipError_t launch_chunk_inverse(const Problem& p, void* t_out, float* csum, bool full,
+                                hipStream_t s);
 hipError_t launch_fused_forward(const Problem& p, const FwdPlan& plan, hipStream_t s);
 
 }  // namespace gdn
