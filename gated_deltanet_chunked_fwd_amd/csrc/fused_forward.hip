@@ -27,12 +27,6 @@
 // P are shared between them.
 #include <type_traits>
 
-#ifndef GDN_KT_COPY
-#define GDN_KT_COPY 0
-#endif
-#ifndef GDN_P_FIRST
-#define GDN_P_FIRST 1
-#endif
 
 
 #include "gdn_device.h"
@@ -226,8 +220,6 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
   // query rows, natural keys
   __shared__ __align__(16) E sP[OUT ? 2 : 1][OUT ? kChunk * CS : 8];
   __shared__ __align__(16) E sVb[NB][kChunk * VS];     // natural rows
-  constexpr bool KT_COPY = GDN_KT_COPY && sizeof(E) == 2 && NW == 8 && OUT;
-  __shared__ __align__(16) E sKt[KT_COPY ? DK * CS : 8];
   __shared__ __align__(16) float sGb[NB][kChunk], sGamb[NB][kChunk], sGamSb[NB][kChunk],
       sDecb[NB][kChunk], sBetb[NB][kChunk];
   // the buffer set of the chunk being computed (the step lambdas read through these)
@@ -458,23 +450,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
   // each variant is straight-line code.
   auto step = [&](auto emit_tag, int c, float gC, auto&& load_part) {
     constexpr bool EMIT = decltype(emit_tag)::value;
-    if constexpr (EMIT && GDN_P_FIRST) pstep(c);
+    if constexpr (EMIT) pstep(c);
     load_part(P1{});
-    if constexpr (KT_COPY) {
-      constexpr int TPW = (NKT + NW - 1) / NW;
-#pragma unroll
-      for (int tt = 0; tt < TPW; ++tt) {
-        const int t = wave * TPW + tt;
-        if (t < NKT) {
-          const int own = prow(t, r16), supply = prow(t, 4 * (r16 & 3));
-#pragma unroll
-          for (int s = 0; s < 2; ++s)
-            *reinterpret_cast<frag*>(sKt + (16 * t + r16) * CS + 32 * s + 8 * q) =
-                col_frag(sK, KS, 32 * s + 4 * q, 32 * s + 16 + 4 * q, own, supply);
-        }
-      }
-      __syncthreads();
-    }
     // ---- X = K h; Y^T = h^T Q^T (operands swapped: a lane holds four consecutive value
     //      columns of one query row, the layout of the O store); first products start at zero
     f32x4 X[4][NCT];
@@ -562,10 +539,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
         const int t = t0 + dt;
         const int own = prow(t, r16), supply = prow(t, 4 * (r16 & 3));
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          if constexpr (KT_COPY) aKt[dt][s] = lds_frag(sKt, CS, 16 * t + r16, 32 * s, q);
-          else aKt[dt][s] = col_frag(sK, KS, 32 * s + 4 * q, 32 * s + 16 + 4 * q, own, supply);
-        }
+        for (int s = 0; s < 2; ++s)
+          aKt[dt][s] = col_frag(sK, KS, 32 * s + 4 * q, 32 * s + 16 + 4 * q, own, supply);
       }
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
@@ -579,7 +554,6 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) hs[t0 + dt][ct] = M::run(aKt[dt][s], ubd[s][ct], hs[t0 + dt][ct]);
     }
-    if constexpr (EMIT && !GDN_P_FIRST) pstep(c);
   };
 
   // Stages chunk cs (registers of st) in buffer b: the gates of chunk cs are scanned in
