@@ -5,17 +5,19 @@ seeded synthetic input, all inputs resident in HBM.  Default workload: the
 Qwen-like prefill (B=4, T=4096, H=16, dk=dv=128, bf16 q/k/v/o, fp32 g, bf16 beta,
 zero initial state, fp32 final state).
 
-Timing: W untimed warm-up steps, then a short stage pass (3 steps with every
-stage bracketed by HIP events) that finds the dominant kernel.  Then K timed steps
-between two device synchronisations.  Before each timed step, outside the step's
-HIP events, a 512 MiB buffer is written and another 512 MiB buffer is read: this
-evicts the 256 MB MALL and the L2s, and the read also drains the written lines, so
-the step starts from HBM with clean caches (a write-only flush leaves up to ~0.3
-GB of dirty lines whose write-back would be billed to the step's first kernel).
-ms_per_step is the mean of the per-step event times.  In the timed steps only the
-dominant kernel's pair of events is recorded (by the library, on the launch
-stream, around that launch), which gives its live mean duration for the roofline
-at the cost of one event pair per step.
+Timing: W untimed warm-up steps, then a short stage pass (3 calls, each after a
+cache eviction, every stage timed) that finds the dominant kernel.  The timed region
+is exactly K back-to-back calls, after one cache eviction (512 MiB written, then
+another 512 MiB read: this evicts the 256 MB MALL and the L2s and drains the dirty
+lines), bracketed by device synchronisations and one pair of HIP events:
+ms_per_step = region time / K.  Inside the region the dominant kernel is timed live
+in every call, on the launch stream, by stop-only events that the library records
+from kernel dispatches: from the end of the kernel launched before it to its own end
+(a stop event adds nothing to the stream, while a start marker, like any separately
+recorded event, idles the GPU for a few microseconds).  All events are created with
+hipEventDisableSystemFence (no cache writeback when they complete).  For context,
+path.ms_per_step_evicted_caches_median is the median of up to 10 calls that each
+start after a cache eviction (each includes one start marker, a few microseconds).
 
 Roofline (dominant kernel = the stage with the largest mean time):
   achieved = algorithmic bytes of that kernel per launch (stage_bytes(): for the
@@ -81,11 +83,18 @@ def copy_reference(mib):
 
 
 class Hip:
-    """HIP events through the runtime torch already loaded (same soname)."""
+    """HIP events through the runtime torch already loaded (same soname).  Timing
+    events are created with hipEventDisableSystemFence: a default event performs a
+    system-scope release (cache writeback and invalidation) when it completes, which
+    idles the GPU for several microseconds after every event and slows the work that
+    follows; these events only time work (every read of them follows a device
+    synchronisation)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
 
     def __init__(self):
         self.lib = ctypes.CDLL("libamdhip64.so.7")
-        self.lib.hipEventCreate.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.c_void_p, ctypes.c_uint]
         self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
@@ -95,7 +104,8 @@ class Hip:
     def events(self, n):
         arr = (ctypes.c_void_p * n)()
         for i in range(n):
-            rc = self.lib.hipEventCreate(ctypes.addressof(arr) + i * ctypes.sizeof(ctypes.c_void_p))
+            rc = self.lib.hipEventCreateWithFlags(ctypes.addressof(arr) + i * ctypes.sizeof(ctypes.c_void_p),
+                                                  self.DISABLE_SYSTEM_FENCE)
             if rc != 0:
                 raise RuntimeError("hipEventCreate failed: %d" % rc)
         return arr
@@ -264,7 +274,6 @@ def main():
         flush_rd.sum()
     seg_chunks = binding.plan_segment_chunks(d["q"], d["v"], d["beta"], inp["cu_seqlens"], opts)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    step_ev = hip.events(2)
 
     def step(o_=None):
         binding.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"],
@@ -295,37 +304,62 @@ def main():
     st_mean = stage_pass(3)
     dom = max(st_mean, key=st_mean.get)
     dom_idx = binding.STAGE_NAMES.index(dom)
-    dom_ev = (ctypes.c_void_p * (2 * binding.GDN_NUM_STAGES))()
-    dom_ev[2 * dom_idx] = stage_ev[2 * dom_idx]
-    dom_ev[2 * dom_idx + 1] = stage_ev[2 * dom_idx + 1]
-    opts_dom = binding.make_opts(no_split=args.no_split, value_block=args.value_block,
-                                 force_segment_chunks=args.segment_chunks,
-                                 stage_events=ctypes.cast(dom_ev, ctypes.c_void_p))
+    NS = binding.GDN_NUM_STAGES
+    # the stage whose last kernel runs right before the dominant one
+    lengths_h = ([spec.T] * spec.B if inp["cu_seqlens"] is None
+                 else [int(inp["cu_seqlens"][i + 1] - inp["cu_seqlens"][i]) for i in range(N)])
+    split = seg_chunks < max((n + 63) // 64 for n in lengths_h)
+    launched = [0] + ([1, 2, 3] if split else []) + [4]
+    prev_idx = launched[launched.index(dom_idx) - 1] if launched.index(dom_idx) > 0 else None
 
-    step_ms, dom_ms_list = [], []
+    def timing_opts(ev_prev_stop, ev_dom_stop, ev_dom_start=None):
+        arr = (ctypes.c_void_p * (2 * NS))()
+        arr[2 * dom_idx + 1] = ev_dom_stop
+        if prev_idx is not None:
+            arr[2 * prev_idx + 1] = ev_prev_stop
+        else:
+            arr[2 * dom_idx] = ev_dom_start
+        o_ = binding.make_opts(no_split=args.no_split, value_block=args.value_block,
+                               force_segment_chunks=args.segment_chunks,
+                               stage_events=ctypes.cast(arr, ctypes.c_void_p))
+        o_._keep = arr
+        return o_
+
+    # ---- the timed region: exactly K back-to-back calls (after one cache eviction),
+    #      bracketed by device synchronisations and one event pair.  Inside it, the
+    #      dominant kernel is timed live in every call by stop-only events recorded
+    #      from kernel dispatches: the end of the kernel launched before it to its own
+    #      end (a stop event adds nothing to the stream; a start event would idle the
+    #      GPU for a few microseconds before the kernel).
+    K = args.steps
+    kev = hip.events(2 * K)
+    call_opts = [timing_opts(kev[2 * i], kev[2 * i + 1], kev[2 * i]) for i in range(K)]
+    region_ev = hip.events(2)
+    if not args.no_flush:
+        evict(0)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
-    for i in range(args.steps):
-        if not args.no_flush:
-            evict(i)
-        hip.record(step_ev[0], stream)
-        step(opts_dom)
-        hip.record(step_ev[1], stream)
-        step_ms.append(hip.elapsed(step_ev[0], step_ev[1]))
-        dom_ms_list.append(hip.elapsed(stage_ev[2 * dom_idx], stage_ev[2 * dom_idx + 1]))
+    hip.record(region_ev[0], stream)
+    for i in range(K):
+        step(call_opts[i])
+    hip.record(region_ev[1], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
+    ms = hip.elapsed(region_ev[0], region_ev[1]) / K
+    dom_ms_list = [hip.elapsed(kev[2 * i], kev[2 * i + 1]) for i in range(K)]
 
-    # a few back-to-back steps without flushes (hot caches), for context
-    torch.cuda.synchronize()
-    hip.record(step_ev[0], stream)
-    for _ in range(5):
-        step()
-    hip.record(step_ev[1], stream)
-    hot_ms = hip.elapsed(step_ev[0], step_ev[1]) / 5
+    # context, outside the timed region: calls that each start from evicted caches
+    # (one start marker per call, which adds a few microseconds of idle GPU)
+    cold_ms = []
+    if not args.no_flush:
+        cev = hip.events(2)
+        cold_opts = timing_opts(None, cev[1], None)   # the call's end: the dominant kernel's stop
+        for i in range(min(K, 10)):
+            evict(i + 1)
+            hip.record(cev[0], stream)
+            step(cold_opts)
+            cold_ms.append(hip.elapsed(cev[0], cev[1]))
 
-    ms = sum(step_ms) / len(step_ms)
-    ms_median = sorted(step_ms)[len(step_ms) // 2]
     tokens = spec.B * spec.T
     dom_ms = sum(dom_ms_list) / len(dom_ms_list)
     has_h0 = d["h0"] is not None
@@ -368,9 +402,10 @@ def main():
                  "algorithmic_flops": flops,
                  "algorithmic_flops_triangular": algorithmic_flops(spec, triangular=True),
                  "copy_gbs_context": copy_gbs, "stage_ms": st_mean,
-                 "ms_per_step_hot_caches": hot_ms, "ms_min": min(step_ms),
-                 "ms_median": ms_median,
-                 "wall_s_timed_loop_incl_flush": wall},
+                 "ms_per_step_evicted_caches_median":
+                     sorted(cold_ms)[len(cold_ms) // 2] if cold_ms else None,
+                 "dominant_ms_min": min(dom_ms_list),
+                 "wall_s_timed_region": wall},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, spec)

@@ -273,17 +273,29 @@ hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hi
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_inverse(const Problem& p, void* t_out, float* csum, bool full, hipStream_t s) {
-  if (p.total_chunks == 0) return hipSuccess;
+hipError_t launch_chunk_inverse(const Problem& p, void* t_out, float* csum, bool full, hipStream_t s,
+                                KernelEvents ev) {
+  if (p.total_chunks == 0) {
+    ev.record_empty(s);
+    return hipSuccess;
+  }
   const int64_t blocks = p.total_chunks * ((p.H + 3) / 4);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks);
   if (p.qkv_bf16) {
-    if (p.dk == 128) chunk_inverse_kernel<bf16, 128><<<grid, 256, 0, s>>>(p, (bf16*)t_out, csum, full ? 1 : 0);
-    else chunk_inverse_kernel<bf16, 64><<<grid, 256, 0, s>>>(p, (bf16*)t_out, csum, full ? 1 : 0);
+    if (p.dk == 128)
+      hipExtLaunchKernelGGL(chunk_inverse_kernel<bf16, 128>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, p,
+                            (bf16*)t_out, csum, full ? 1 : 0);
+    else
+      hipExtLaunchKernelGGL(chunk_inverse_kernel<bf16, 64>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, p,
+                            (bf16*)t_out, csum, full ? 1 : 0);
   } else {
-    if (p.dk == 128) chunk_inverse_kernel<float, 128><<<grid, 256, 0, s>>>(p, (float*)t_out, csum, full ? 1 : 0);
-    else chunk_inverse_kernel<float, 64><<<grid, 256, 0, s>>>(p, (float*)t_out, csum, full ? 1 : 0);
+    if (p.dk == 128)
+      hipExtLaunchKernelGGL(chunk_inverse_kernel<float, 128>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, p,
+                            (float*)t_out, csum, full ? 1 : 0);
+    else
+      hipExtLaunchKernelGGL(chunk_inverse_kernel<float, 64>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, p,
+                            (float*)t_out, csum, full ? 1 : 0);
   }
   return hipGetLastError();
 }

@@ -239,28 +239,38 @@ __global__ __launch_bounds__(64 * MergeCfg<DK>::NW) void cp_merge_kernel(Problem
   }
 }
 
+// ev: start recorded from the first kernel's dispatch, stop from the last one's.
 template <int DK>
-static void launch_merge_dk(const Problem& p, const FwdPlan& plan, int max_steps, hipStream_t s) {
-  constexpr int NT = 64 * MergeCfg<DK>::NW;
+static void launch_merge_dk(const Problem& p, const FwdPlan& plan, int max_steps, hipStream_t s,
+                            KernelEvents ev) {
+  const dim3 nt(64 * MergeCfg<DK>::NW);
   const int64_t nh = (int64_t)p.N * p.H;
   const int ncb = p.dv / 16;
-  auto grid = [&](int64_t units, int cbs) { return (unsigned)((units + 7) / 8 * 8 * cbs); };
+  auto grid = [&](int64_t units, int cbs) { return dim3((unsigned)((units + 7) / 8 * 8 * cbs)); };
   if (max_steps <= kMergeTreeMinSteps) {
-    cp_merge_kernel<DK, kRun><<<grid(nh, ncb), NT, 0, s>>>(p, plan, max(max_steps, 1), 1, 0);
+    hipExtLaunchKernelGGL(cp_merge_kernel<DK, kRun>, grid(nh, ncb), nt, 0, s, ev.start, ev.stop, 0, p, plan,
+                          max(max_steps, 1), 1, 0);
     return;
   }
   int G = 1;
   while ((int64_t)G * G < max_steps) ++G;   // G = ceil(sqrt(steps))
   const int maxg = (max_steps + G - 1) / G;
-  cp_merge_kernel<DK, kCompose><<<grid(nh * maxg, (DK + p.dv) / 16), NT, 0, s>>>(p, plan, G, maxg, 1);
-  cp_merge_kernel<DK, kGroups><<<grid(nh, ncb), NT, 0, s>>>(p, plan, G, 1, 1);
-  cp_merge_kernel<DK, kRun><<<grid(nh * maxg, ncb), NT, 0, s>>>(p, plan, G, maxg, 1);
+  hipExtLaunchKernelGGL(cp_merge_kernel<DK, kCompose>, grid(nh * maxg, (DK + p.dv) / 16), nt, 0, s, ev.start,
+                        nullptr, 0, p, plan, G, maxg, 1);
+  hipExtLaunchKernelGGL(cp_merge_kernel<DK, kGroups>, grid(nh, ncb), nt, 0, s, nullptr, nullptr, 0, p, plan,
+                        G, 1, 1);
+  hipExtLaunchKernelGGL(cp_merge_kernel<DK, kRun>, grid(nh * maxg, ncb), nt, 0, s, nullptr, ev.stop, 0, p,
+                        plan, G, maxg, 1);
 }
 
-hipError_t launch_cp_merge(const Problem& p, const FwdPlan& plan, int max_steps, hipStream_t s) {
-  if (p.N == 0 || max_steps < 1) return hipSuccess;
-  if (p.dk == 128) launch_merge_dk<128>(p, plan, max_steps, s);
-  else launch_merge_dk<64>(p, plan, max_steps, s);
+hipError_t launch_cp_merge(const Problem& p, const FwdPlan& plan, int max_steps, hipStream_t s,
+                           KernelEvents ev) {
+  if (p.N == 0 || max_steps < 1) {
+    ev.record_empty(s);
+    return hipSuccess;
+  }
+  if (p.dk == 128) launch_merge_dk<128>(p, plan, max_steps, s, ev);
+  else launch_merge_dk<64>(p, plan, max_steps, s, ev);
   return hipGetLastError();
 }
 

@@ -680,7 +680,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
 
 // 1-D grid of ceil(units / 8) * 8 * column blocks (see the decode in the kernel).
 template <typename E, int DK, int PASS>
-static void launch_dk(const Problem& p, const FwdPlan& plan, hipStream_t s) {
+static void launch_dk(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev) {
   // pass 1 also runs dk transition-matrix columns after the dv value columns
   const int cols = PASS == kPass1 ? p.dv + DK : p.dv;
   const int64_t groups = (plan.units + 7) / 8;
@@ -692,29 +692,34 @@ static void launch_dk(const Problem& p, const FwdPlan& plan, hipStream_t s) {
     if (p.dv % 128 == 0 && cols % 128 == 0 &&
         (PASS == kPass3 ? plan.value_block != 64 : plan.pass1_block == 128)) {
       const int ncb = cols / 128;
-      fused_forward_kernel<E, DK, 16, 8, PASS><<<(unsigned)(groups * 8 * ncb), 512, 0, s>>>(p, plan);
+      hipExtLaunchKernelGGL(fused_forward_kernel<E, DK, 16, 8, PASS>, dim3((unsigned)(groups * 8 * ncb)),
+                            dim3(512), 0, s, ev.start, ev.stop, 0, p, plan);
       return;
     }
   }
   // 64 columns per workgroup as 4 waves x 16 columns (fp32 tiles only fit LDS this way)
   const int ncb = cols / 64;
-  fused_forward_kernel<E, DK, 16, 4, PASS><<<(unsigned)(groups * 8 * ncb), 256, 0, s>>>(p, plan);
+  hipExtLaunchKernelGGL(fused_forward_kernel<E, DK, 16, 4, PASS>, dim3((unsigned)(groups * 8 * ncb)),
+                        dim3(256), 0, s, ev.start, ev.stop, 0, p, plan);
 }
 
 template <typename E, int DK>
-static void launch_pass(const Problem& p, const FwdPlan& plan, hipStream_t s) {
-  if (plan.mode == kPass1) launch_dk<E, DK, kPass1>(p, plan, s);
-  else launch_dk<E, DK, kPass3>(p, plan, s);
+static void launch_pass(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev) {
+  if (plan.mode == kPass1) launch_dk<E, DK, kPass1>(p, plan, s, ev);
+  else launch_dk<E, DK, kPass3>(p, plan, s, ev);
 }
 
-hipError_t launch_fused_forward(const Problem& p, const FwdPlan& plan, hipStream_t s) {
-  if (plan.units == 0) return hipSuccess;
+hipError_t launch_fused_forward(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev) {
+  if (plan.units == 0) {
+    ev.record_empty(s);
+    return hipSuccess;
+  }
   if (p.qkv_bf16) {
-    if (p.dk == 128) launch_pass<bf16, 128>(p, plan, s);
-    else launch_pass<bf16, 64>(p, plan, s);
+    if (p.dk == 128) launch_pass<bf16, 128>(p, plan, s, ev);
+    else launch_pass<bf16, 64>(p, plan, s, ev);
   } else {
-    if (p.dk == 128) launch_pass<float, 128>(p, plan, s);
-    else launch_pass<float, 64>(p, plan, s);
+    if (p.dk == 128) launch_pass<float, 128>(p, plan, s, ev);
+    else launch_pass<float, 64>(p, plan, s, ev);
   }
   return hipGetLastError();
 }

@@ -107,14 +107,18 @@ hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s) 
 }
 
 hipError_t launch_gate_scan(const Problem& p, const float* csum, int64_t max_chunks, int wmax,
-                            uint32_t* best, hipStream_t s) {
-  if (p.N == 0) return hipSuccess;
+                            uint32_t* best, hipStream_t s, KernelEvents ev) {
+  if (p.N == 0) {
+    ev.record_empty(s);
+    return hipSuccess;
+  }
+  const dim3 grid((unsigned)(p.N * p.H));
   if (max_chunks > 512)
-    gate_window_max_kernel<1024><<<(unsigned)(p.N * p.H), 1024, 0, s>>>(csum, p.cu, p.chunk_off, p.T, p.N,
-                                                                        p.H, wmax, best);
+    hipExtLaunchKernelGGL(gate_window_max_kernel<1024>, grid, dim3(1024), 0, s, ev.start, ev.stop, 0, csum,
+                          p.cu, p.chunk_off, p.T, p.N, p.H, wmax, best);
   else
-    gate_window_max_kernel<256><<<(unsigned)(p.N * p.H), 256, 0, s>>>(csum, p.cu, p.chunk_off, p.T, p.N,
-                                                                      p.H, wmax, best);
+    hipExtLaunchKernelGGL(gate_window_max_kernel<256>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, csum,
+                          p.cu, p.chunk_off, p.T, p.N, p.H, wmax, best);
   return hipGetLastError();
 }
 

@@ -52,19 +52,18 @@ int device_cus() {
   return cus;
 }
 
-// Records the caller's timing events around one stage (no-op without events).
-struct StageMark {
-  hipEvent_t* ev;
-  hipStream_t s;
-  int stage;
-  StageMark(const gdn_opts* o, int stage_, hipStream_t s_)
-      : ev(o ? o->stage_events : nullptr), s(s_), stage(stage_) {
-    if (ev && ev[2 * stage]) (void)hipEventRecord(ev[2 * stage], s);
+// The caller's timing events of a stage, handed to its launcher, which records them
+// from the dispatch of the stage's first (start) and last (stop) kernel; null entries
+// are skipped.
+gdn::KernelEvents stage_events(const gdn_opts* o, int stage) {
+  gdn::KernelEvents e;
+  if (o && o->stage_events) {
+    e.start = o->stage_events[2 * stage];
+    e.stop = o->stage_events[2 * stage + 1];
   }
-  ~StageMark() {
-    if (ev && ev[2 * stage + 1]) (void)hipEventRecord(ev[2 * stage + 1], s);
-  }
-};
+  return e;
+}
+
 
 int validate_shape(const gdn_shape* s) {
   if (!s) return GDN_ERR_ARG;
@@ -270,8 +269,9 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
   void* tmat = ws + L.tmat;
   float* csum = P.split ? reinterpret_cast<float*>(ws + L.csum) : nullptr;
   {
-    StageMark mark(opts, GDN_STAGE_INVERSE, stream);
-    if (gdn::launch_chunk_inverse(p, tmat, csum, false, stream) != hipSuccess) return GDN_ERR_HIP;
+    if (gdn::launch_chunk_inverse(p, tmat, csum, false, stream,
+                                  stage_events(opts, GDN_STAGE_INVERSE)) != hipSuccess)
+      return GDN_ERR_HIP;
   }
 
   gdn::FwdPlan plan;
@@ -294,25 +294,28 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
     plan.cp.gmat = L.gmat ? ws + L.gmat : nullptr;
     plan.cp.gvec = L.gvec ? reinterpret_cast<float*>(ws + L.gvec) : nullptr;
     if (!plan.cp.force_correction) {
-      StageMark mark(opts, GDN_STAGE_GATE_SCAN, stream);
-      if (gdn::launch_gate_scan(p, csum, P.max_chunks, P.wmax, best, stream) != hipSuccess)
+      if (gdn::launch_gate_scan(p, csum, P.max_chunks, P.wmax, best, stream,
+                                stage_events(opts, GDN_STAGE_GATE_SCAN)) != hipSuccess)
         return GDN_ERR_HIP;
     }
     {
-      StageMark mark(opts, GDN_STAGE_CP_PASS1, stream);
       gdn::FwdPlan p1 = plan;
       p1.mode = gdn::kPass1;
-      if (gdn::launch_fused_forward(p, p1, stream) != hipSuccess) return GDN_ERR_HIP;
+      if (gdn::launch_fused_forward(p, p1, stream, stage_events(opts, GDN_STAGE_CP_PASS1)) !=
+          hipSuccess)
+        return GDN_ERR_HIP;
     }
     {
-      StageMark mark(opts, GDN_STAGE_CP_MERGE, stream);
       const int max_steps = (int)((P.max_chunks + P.seg_chunks - 1) / P.seg_chunks - 1);
-      if (gdn::launch_cp_merge(p, plan, max_steps, stream) != hipSuccess) return GDN_ERR_HIP;
+      if (gdn::launch_cp_merge(p, plan, max_steps, stream, stage_events(opts, GDN_STAGE_CP_MERGE)) !=
+          hipSuccess)
+        return GDN_ERR_HIP;
     }
   }
   {
-    StageMark mark(opts, GDN_STAGE_FORWARD, stream);
-    if (gdn::launch_fused_forward(p, plan, stream) != hipSuccess) return GDN_ERR_HIP;
+    if (gdn::launch_fused_forward(p, plan, stream, stage_events(opts, GDN_STAGE_FORWARD)) !=
+        hipSuccess)
+      return GDN_ERR_HIP;
   }
   return GDN_OK;
 }

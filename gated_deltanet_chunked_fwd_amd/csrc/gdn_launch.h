@@ -1,5 +1,6 @@
 // Internal host-side launch interface between the ABI layer and the kernels.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -71,17 +72,30 @@ hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hi
 hipError_t launch_plan_tables(const int32_t* cu, int N, int seg_chunks, int32_t* chunk_off,
                               int32_t* seg_off, hipStream_t s);
 hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s);
+// Optional start / stop events of a single-kernel launch, recorded from the kernel's
+// own dispatch (hipExtLaunchKernel): timing a stage this way adds no packets to the
+// stream, where a separate event record costs a few microseconds of idle GPU.
+struct KernelEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  // a launcher that has nothing to launch still marks the (empty) interval
+  void record_empty(hipStream_t s) const {
+    if (start) (void)hipEventRecord(start, s);
+    if (stop) (void)hipEventRecord(stop, s);
+  }
+};
 hipError_t launch_gate_scan(const Problem& p, const float* csum, int64_t max_chunks, int wmax,
-                            uint32_t* best, hipStream_t s);
+                            uint32_t* best, hipStream_t s, KernelEvents ev = {});
 hipError_t launch_gate_finalize(const Problem& p, const uint32_t* best, int wmax, float thr,
                                 int32_t* out, hipStream_t s);
 // max_steps: the most segment boundaries of any sequence (segments - 1).
-hipError_t launch_cp_merge(const Problem& p, const FwdPlan& plan, int max_steps, hipStream_t s);
+hipError_t launch_cp_merge(const Problem& p, const FwdPlan& plan, int max_steps, hipStream_t s,
+                           KernelEvents ev = {});
 // csum (nullable): [total_chunks, H] per-chunk gate sums, written on the side.
 // full = false: T's zero upper-right 32 x 32 quadrant is left unwritten (the fused
 // forward never reads it).
 hipError_t launch_chunk_inverse(const Problem& p, void* t_out, float* csum, bool full,
-                                hipStream_t s);
-hipError_t launch_fused_forward(const Problem& p, const FwdPlan& plan, hipStream_t s);
+                                hipStream_t s, KernelEvents ev = {});
+hipError_t launch_fused_forward(const Problem& p, const FwdPlan& plan, hipStream_t s,
+                                KernelEvents ev = {});
 
 }  // namespace gdn

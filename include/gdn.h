@@ -84,11 +84,14 @@ typedef struct gdn_opts {
   int32_t value_block;          /* value columns per workgroup of the fused kernel: 64 or
                                    128; 0 -> planner's choice */
   /* Optional timing hook: NULL, or an array of 2 * GDN_NUM_STAGES events created by
-   * the caller (hipEventCreate).  For every stage that runs, the library records
-   * stage_events[2*s] on `stream` just before the stage's launch and
-   * stage_events[2*s+1] just after it; events of stages that do not run are left
-   * untouched, and NULL entries are skipped (so a caller can time one stage alone).
-   * Recording events is the only effect. */
+   * the caller (hipEventCreate).  For every stage that runs, stage_events[2*s] and
+   * stage_events[2*s+1] are recorded on `stream` from the dispatch of the stage's
+   * first and last kernel (hipExtLaunchKernel: that kernel's start and end; a stage
+   * with nothing to launch records both at once).  Events of stages that do not run
+   * are left untouched, and NULL entries are skipped (so a caller can time one stage
+   * alone).  A stop event alone adds nothing to the stream; a start event makes the
+   * runtime insert a marker before the kernel, which idles the GPU for a few
+   * microseconds.  Recording events is the only effect. */
   hipEvent_t* stage_events;
 } gdn_opts;
 
