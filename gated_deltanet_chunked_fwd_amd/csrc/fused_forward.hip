@@ -18,13 +18,16 @@
 // columns of h for all dk rows, as 16x16 fp32 accumulator tiles in "tile order" (gdn_device.h),
 // so h, V' and U feed the next MFMA straight from registers.  Per chunk the
 // workgroup stages K, Q, T, the gates and its V columns in LDS (the global loads
-// of chunk c+1 are issued before chunk c is computed), computes P = (QK^T)*Gamma
-// once (tiles split over the waves), and each wave then runs its columns:
-// K^T for the state update and V in accumulator layout come from the row-major
-// tiles through LDS transpose reads.  O is produced transposed (MFMA operands
-// swapped), so each lane ends with four consecutive value columns of one query
-// row and stores them to HBM directly.  Value columns are independent; only T and
-// P are shared between them.
+// of chunk c+1 go out in four parts while chunk c is computed, and bf16 chunks are
+// double-buffered, so chunk c+1 is staged at the end of chunk c's step), computes
+// P = (QK^T)*Gamma once (tiles split over the waves), and each wave then runs its
+// columns: K^T for the state update and V in accumulator layout come from the
+// row-major tiles through LDS transpose reads.  O is produced transposed (MFMA
+// operands swapped), so each lane ends with four consecutive value columns of one
+// query row; it is finished and stored at the start of the next chunk's step.
+// Lookback chunks (window starts) produce no O and skip Q; T's zero upper-right
+// 32 x 32 quadrant is never loaded.  Value columns are independent; only T and P
+// are shared between them.
 #include <type_traits>
 
 
