@@ -229,3 +229,18 @@ def test_beta_one_last_token_closed_form():
     got = torch.einsum("bhij,bhi->bhj", hT.cpu().float(), k_last)
     rel = (got - v_last).norm() / v_last.norm()
     assert rel < 1e-2, rel
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_no_tokens_passes_state_through(packed):
+    """Degenerate input: no tokens at all (dense T = 0, or packed sequences that are
+    all empty).  The output is empty and the final state equals the initial state,
+    bit for bit (no recurrence step touches it)."""
+    H, dk, dv = 2, 128, 128
+    if packed:
+        inp = _packed([0, 0, 0], H=H, dk=dk, dv=dv, dtype="bf16", h0_std=0.1, seed=71)
+    else:
+        inp = synth.generate(spec(B=2, T=0, H=H, dk=dk, dv=dv, h0_std=0.1, seed=71))
+    o, hT = run_gpu(inp)
+    assert o.numel() == 0
+    assert torch.equal(hT.cpu(), inp["h0"])
