@@ -5,21 +5,23 @@
 // splits per sequence is not fixed by the hardware the way inter-card parallelism
 // is; with L chunks per segment and N chunks per sequence the one-wave model is
 // T = lambda1 L + lambda2 N / L (the chunk-serial passes scale with L, the
-// recurrence over segments with N/L), minimised at L ~ sqrt(lambda2 N / lambda1);
-// splitting pays only when the grid does not fill the machine and the sequence is
-// long.  Here L is the larger of that optimum and the "fill" length: the chunk
-// steps per compute unit if all (sequence, head, column block) work were spread
-// evenly, L_fill = ceil(sum of chunks x heads x column blocks / CUs).  A split
-// happens only if the longest sequence holds more than 1.5 L chunks; an unsplit grid
-// that already keeps every CU busy for about as long as its longest sequence
-// has L_fill >= that length and stays unsplit, while one that is short of units
-// or unbalanced (packed sequences of very different lengths) gets its long
-// sequences cut.
+// recurrence over segments with N / L).  On a GPU with 256 CUs and one fused
+// workgroup per CU the first term is really the makespan of the fused pass: its
+// units (sequence, segment, head, column block) run in dispatch order on the
+// earliest free CU of their XCD, and with packed sequences of different lengths the
+// tail of that schedule, not the average, decides.  So the planner simulates that
+// schedule for a ladder of candidate lengths (pass3_makespan) and takes
+// argmin lambda1 * makespan(L) + lambda2 * (N_longest / L - 1), with "no split"
+// competing as one more candidate.  lambda1, lambda2 and the model's start-up and
+// lookback costs are MI355X measurements; the choice is a performance decision only
+// (every plan computes the same result within rounding).
 #include <algorithm>
 #include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstring>
+#include <queue>
+#include <vector>
 
 #include "gdn.h"
 #include "gdn_launch.h"
@@ -30,9 +32,15 @@ using gdn::kChunk;
 using gdn::kWindowMaxCap;
 
 constexpr size_t kAlign = 256;
-constexpr float kLambda1Us = 1.0f;   // one chunk step of the fused kernel (MI355X)
-constexpr float kLambda2Us = 0.5f;   // one merge step
+// Planner costs, measured on MI355X (workload timestamps): one chunk step of the fused
+// kernel per workgroup, one merge step, and in chunk steps a workgroup's start-up and
+// the lookback a segment after the first usually walks (about 4.5 chunks of 0.7 step).
+constexpr float kLambda1Us = 3.8f;
+constexpr float kLambda2Us = 0.75f;
+constexpr double kStartSteps = 2.0;
+constexpr double kLookbackSteps = 3.2;
 constexpr int kMinSegmentChunks = 8;
+constexpr int64_t kPlanModelMaxUnits = 1 << 16;   // larger plans use the closed form
 constexpr float kWindowMargin = 1e-3f;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -112,6 +120,54 @@ struct Plan {
   float log_eps = 0.f;
 };
 
+// Pass-3 makespan, in chunk steps, of segment length L: the kernel's units (sequence,
+// segment, head, column block) in dispatch order, dealt to the 8 XCDs round robin
+// (workgroup id mod 8), each XCD placing a unit on its earliest free CU (one
+// workgroup per CU).  A unit costs its chunks, plus the lookback for segments after
+// the first, plus the start-up.  Plans too large to simulate cheaply use the closed
+// form max(average work per CU, longest unit).
+double pass3_makespan(const gdn_shape* s, int64_t L, int64_t cus, int ncb) {
+  const int64_t per_xcd = std::max<int64_t>(1, cus / 8);
+  int64_t units = 0;
+  double work = 0, longest = 0;
+  for (int64_t n = 0; n < s->N; ++n) {
+    const int64_t nch = seq_chunks(s, n);
+    const int64_t segs = std::max<int64_t>(1, (nch + L - 1) / L);
+    units += segs * s->H * ncb;
+    for (int64_t j = 0; j < segs; ++j) {
+      const double c = (double)std::min(L, std::max<int64_t>(0, nch - j * L)) +
+                       (j > 0 ? kLookbackSteps : 0.0) + kStartSteps;
+      work += c * s->H * ncb;
+      longest = std::max(longest, c);
+    }
+  }
+  if (units > kPlanModelMaxUnits) return std::max(work / (double)cus, longest);
+  std::vector<std::priority_queue<double, std::vector<double>, std::greater<double>>> xcd(8);
+  for (auto& q : xcd)
+    for (int64_t i = 0; i < per_xcd; ++i) q.push(0.0);
+  int64_t u = 0;
+  for (int64_t n = 0; n < s->N; ++n) {
+    const int64_t nch = seq_chunks(s, n);
+    const int64_t segs = std::max<int64_t>(1, (nch + L - 1) / L);
+    for (int64_t j = 0; j < segs; ++j) {
+      const double c = (double)std::min(L, std::max<int64_t>(0, nch - j * L)) +
+                       (j > 0 ? kLookbackSteps : 0.0) + kStartSteps;
+      for (int64_t k = 0; k < s->H * ncb; ++k, ++u) {
+        auto& q = xcd[u % 8];
+        const double t = q.top();
+        q.pop();
+        q.push(t + c);
+      }
+    }
+  }
+  double m = 0;   // latest finishing CU: the last element left in each min-heap
+  for (auto& q : xcd) {
+    while (q.size() > 1) q.pop();
+    m = std::max(m, q.top());
+  }
+  return m;
+}
+
 Plan make_plan(const gdn_shape* s, const gdn_opts* o) {
   Plan P;
   for (int64_t n = 0; n < s->N; ++n) {
@@ -129,14 +185,37 @@ Plan make_plan(const gdn_shape* s, const gdn_opts* o) {
     if (o && o->force_segment_chunks > 0) {
       L = o->force_segment_chunks;
     } else {
-      const int64_t colblocks = s->dv / P.value_block;
+      // T auto-CP: cost(L) = lambda1 * (pass-3 makespan in chunk steps) + lambda2 *
+      // (merge steps of the longest sequence); the makespan is simulated (see
+      // pass3_makespan), so unequal sequence lengths are scheduled as they will run.
+      // Candidates from kMinSegmentChunks up; no split (L = max_chunks) competes too.
+      const int ncb = (int)(s->dv / P.value_block);
       const int64_t cus = device_cus();
       const double l1 = (o && o->lambda1_us > 0.f) ? o->lambda1_us : kLambda1Us;
       const double l2 = (o && o->lambda2_us > 0.f) ? o->lambda2_us : kLambda2Us;
-      const int64_t fill = (P.total_chunks * s->H * colblocks + cus - 1) / cus;
-      const int64_t opt = (int64_t)std::ceil(std::sqrt(l2 * (double)P.max_chunks / l1));
-      const int64_t cand = std::max<int64_t>({fill, opt, kMinSegmentChunks});
-      if (2 * P.max_chunks > 3 * cand) L = cand;
+      auto cost = [&](int64_t cand) {
+        const int64_t steps = (P.max_chunks + cand - 1) / cand - 1;
+        return l1 * pass3_makespan(s, cand, cus, ncb) + l2 * (double)steps;
+      };
+      // candidates: a ladder of round lengths (ratio about 1.25 to 1.5) and the lengths
+      // that cut the longest sequence into 2..8 equal segments
+      std::vector<int64_t> cands;
+      for (int64_t c = kMinSegmentChunks; c < P.max_chunks;) {
+        cands.push_back(c);
+        c = c < 16 ? c + 4 : (c < 32 ? c + 8 : (c < 64 ? c + 16 : c + c / 2));
+      }
+      for (int64_t k = 2; k <= 8; ++k) {
+        const int64_t c = (P.max_chunks + k - 1) / k;
+        if (c >= kMinSegmentChunks && c < P.max_chunks) cands.push_back(c);
+      }
+      double best = cost(P.max_chunks);
+      for (int64_t cand : cands) {
+        const double c = cost(cand);
+        if (c < best || (c == best && cand > L && L < INT_MAX / 2)) {
+          best = c;
+          L = cand;
+        }
+      }
     }
   }
   P.split = L < P.max_chunks;
