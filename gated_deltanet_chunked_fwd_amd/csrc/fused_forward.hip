@@ -252,7 +252,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
 
   // Pass 1 numbers its units head-major, so the few heads that need it (all of
   // their units run full segments) still spread over all XCDs; pass 3 numbers them
-  // segment-major, so units dispatched together have similar lengths.
+  // segment-major, in the plan's segment order when there is one (packed input:
+  // longest segments first), so units dispatched together have similar lengths.
   const int64_t nseg = plan.units / H;     // segments over all sequences
   int h;
   int64_t sg;                              // global segment index
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
     sg = unit - (int64_t)h * nseg;
   } else {
     h = (int)(unit % H);
-    sg = unit / H;
+    sg = plan.seg_order ? plan.seg_order[unit / H] : unit / H;   // longest segments first
   }
   int n, seg;
   if (plan.seg_off) {

@@ -63,8 +63,16 @@ __global__ __launch_bounds__(NT) void gate_window_max_kernel(const float* __rest
 }
 
 // Packed input: the chunk / segment offset tables.
-__global__ void plan_tables_kernel(const int32_t* __restrict__ cu, int N, int seg_chunks,
-                                   int32_t* __restrict__ chunk_off, int32_t* __restrict__ seg_off) {
+// Packed input: the chunk / segment offset tables, and (split plans) the order in
+// which pass 3 takes the segments: longest first (list scheduling: the long units
+// start early and the short ones fill the tail).  Every full segment (seg_chunks
+// chunks) comes first, in sequence order; then the last segment of every sequence,
+// ranked by its length (longest first, ties in sequence order), the rank of each
+// counted by its own thread.
+__global__ __launch_bounds__(256) void plan_tables_kernel(const int32_t* __restrict__ cu, int N,
+                                                          int seg_chunks, int32_t* __restrict__ chunk_off,
+                                                          int32_t* __restrict__ seg_off,
+                                                          int32_t* __restrict__ seg_order) {
   if (threadIdx.x == 0) {
     int32_t acc = 0, sacc = 0;
     chunk_off[0] = 0;
@@ -78,6 +86,24 @@ __global__ void plan_tables_kernel(const int32_t* __restrict__ cu, int N, int se
         seg_off[n + 1] = sacc;
       }
     }
+  }
+  if (!seg_order) return;
+  __syncthreads();
+  auto last_len = [&](int n) {   // chunks of sequence n's last segment (0: empty sequence)
+    const int nch = (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
+    return nch - (max(1, (nch + seg_chunks - 1) / seg_chunks) - 1) * seg_chunks;
+  };
+  const int full = seg_off[N] - N;   // full segments over all sequences
+  for (int n = threadIdx.x; n < N; n += blockDim.x) {
+    const int s0 = seg_off[n], segs = seg_off[n + 1] - s0;
+    for (int j = 0; j + 1 < segs; ++j) seg_order[s0 - n + j] = s0 + j;
+    const int len = last_len(n);
+    int rank = 0;
+    for (int m = 0; m < N; ++m) {
+      const int lm = last_len(m);
+      rank += (lm > len || (lm == len && m < n)) ? 1 : 0;
+    }
+    seg_order[full + rank] = s0 + segs - 1;
   }
 }
 
@@ -93,8 +119,8 @@ __global__ void gate_window_finalize_kernel(const uint32_t* __restrict__ best,
 }
 
 hipError_t launch_plan_tables(const int32_t* cu, int N, int seg_chunks, int32_t* chunk_off,
-                              int32_t* seg_off, hipStream_t s) {
-  plan_tables_kernel<<<1, 64, 0, s>>>(cu, N, seg_chunks, chunk_off, seg_off);
+                              int32_t* seg_off, int32_t* seg_order, hipStream_t s) {
+  plan_tables_kernel<<<1, 256, 0, s>>>(cu, N, seg_chunks, chunk_off, seg_off, seg_order);
   return hipGetLastError();
 }
 

@@ -120,44 +120,59 @@ struct Plan {
   float log_eps = 0.f;
 };
 
-// Pass-3 makespan, in chunk steps, of segment length L: the kernel's units (sequence,
-// segment, head, column block) in dispatch order, dealt to the 8 XCDs round robin
-// (workgroup id mod 8), each XCD placing a unit on its earliest free CU (one
-// workgroup per CU).  A unit costs its chunks, plus the lookback for segments after
-// the first, plus the start-up.  Plans too large to simulate cheaply use the closed
-// form max(average work per CU, longest unit).
+// Pass-3 makespan, in chunk steps, of segment length L: the kernel's units (segment,
+// head, column block) in dispatch order, dealt to the 8 XCDs round robin (workgroup
+// id mod 8), each XCD placing a unit on its earliest free CU (one workgroup per CU).
+// The segment order is the kernel's: packed input (split, at most kSegOrderMaxSeqs
+// sequences) takes full segments first and then the last segments longest first;
+// otherwise sequence order.  A unit costs its chunks, plus the lookback for segments
+// after the first, plus the start-up.  Plans too large to simulate cheaply use the
+// closed form max(average work per CU, longest unit).
 double pass3_makespan(const gdn_shape* s, int64_t L, int64_t cus, int ncb) {
   const int64_t per_xcd = std::max<int64_t>(1, cus / 8);
-  int64_t units = 0;
-  double work = 0, longest = 0;
+  std::vector<double> full, last;
   for (int64_t n = 0; n < s->N; ++n) {
     const int64_t nch = seq_chunks(s, n);
     const int64_t segs = std::max<int64_t>(1, (nch + L - 1) / L);
-    units += segs * s->H * ncb;
     for (int64_t j = 0; j < segs; ++j) {
       const double c = (double)std::min(L, std::max<int64_t>(0, nch - j * L)) +
                        (j > 0 ? kLookbackSteps : 0.0) + kStartSteps;
-      work += c * s->H * ncb;
-      longest = std::max(longest, c);
+      (j + 1 < segs ? full : last).push_back(c);
     }
   }
+  const int64_t per_seg = s->H * ncb;
+  const int64_t units = (int64_t)(full.size() + last.size()) * per_seg;
+  double work = 0, longest = 0;
+  for (double c : full) work += c, longest = std::max(longest, c);
+  for (double c : last) work += c, longest = std::max(longest, c);
+  work *= (double)per_seg;
   if (units > kPlanModelMaxUnits) return std::max(work / (double)cus, longest);
+  std::vector<double> order;
+  const bool lpt = s->cu_seqlens_host && s->N <= gdn::kSegOrderMaxSeqs && !full.empty();
+  if (lpt) {
+    order = full;
+    std::stable_sort(last.begin(), last.end(), std::greater<double>());
+    order.insert(order.end(), last.begin(), last.end());
+  } else {
+    // sequence order: rebuild it (full and last were separated above)
+    for (int64_t n = 0; n < s->N; ++n) {
+      const int64_t nch = seq_chunks(s, n);
+      const int64_t segs = std::max<int64_t>(1, (nch + L - 1) / L);
+      for (int64_t j = 0; j < segs; ++j)
+        order.push_back((double)std::min(L, std::max<int64_t>(0, nch - j * L)) +
+                        (j > 0 ? kLookbackSteps : 0.0) + kStartSteps);
+    }
+  }
   std::vector<std::priority_queue<double, std::vector<double>, std::greater<double>>> xcd(8);
   for (auto& q : xcd)
     for (int64_t i = 0; i < per_xcd; ++i) q.push(0.0);
   int64_t u = 0;
-  for (int64_t n = 0; n < s->N; ++n) {
-    const int64_t nch = seq_chunks(s, n);
-    const int64_t segs = std::max<int64_t>(1, (nch + L - 1) / L);
-    for (int64_t j = 0; j < segs; ++j) {
-      const double c = (double)std::min(L, std::max<int64_t>(0, nch - j * L)) +
-                       (j > 0 ? kLookbackSteps : 0.0) + kStartSteps;
-      for (int64_t k = 0; k < s->H * ncb; ++k, ++u) {
-        auto& q = xcd[u % 8];
-        const double t = q.top();
-        q.pop();
-        q.push(t + c);
-      }
+  for (double c : order) {
+    for (int64_t k = 0; k < per_seg; ++k, ++u) {
+      auto& q = xcd[u % 8];
+      const double t = q.top();
+      q.pop();
+      q.push(t + c);
     }
   }
   double m = 0;   // latest finishing CU: the last element left in each min-heap
@@ -230,8 +245,10 @@ Plan make_plan(const gdn_shape* s, const gdn_opts* o) {
 }
 
 struct Layout {
-  size_t tmat = 0, chunk_off = 0, seg_off = 0, best = 0, csum = 0, sstar = 0, mcorr = 0, hstart = 0;
+  size_t tmat = 0, chunk_off = 0, seg_off = 0, seg_order = 0, best = 0, csum = 0, sstar = 0, mcorr = 0,
+         hstart = 0;
   size_t gmat = 0, gvec = 0;
+  bool has_seg_order = false;
   size_t total = 0;
 };
 
@@ -243,6 +260,10 @@ Layout layout(const gdn_shape* s, const Plan& P) {
   L.tmat = take((size_t)P.total_chunks * s->H * kChunk * kChunk * esz);
   L.chunk_off = take((size_t)(s->N + 1) * sizeof(int32_t));
   L.seg_off = take((size_t)(s->N + 1) * sizeof(int32_t));
+  if (s->cu_seqlens_host && P.split && s->N <= gdn::kSegOrderMaxSeqs) {
+    L.seg_order = take((size_t)P.total_segs * sizeof(int32_t));
+    L.has_seg_order = true;
+  }
   L.best = take((size_t)s->N * s->H * kWindowMaxCap * sizeof(uint32_t));
   if (P.split) {
     L.csum = take((size_t)P.total_chunks * s->H * sizeof(float));
@@ -337,10 +358,12 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                                 final_state, shape, P.total_chunks);
   int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + L.chunk_off);
   int32_t* seg_off = reinterpret_cast<int32_t*>(ws + L.seg_off);
+  int32_t* seg_order = reinterpret_cast<int32_t*>(ws + L.seg_order);
   uint32_t* best = reinterpret_cast<uint32_t*>(ws + L.best);
   if (cu_seqlens) {
     if (gdn::launch_plan_tables(cu_seqlens, p.N, P.seg_chunks, chunk_off,
-                                P.split ? seg_off : nullptr, stream) != hipSuccess)
+                                P.split ? seg_off : nullptr, L.has_seg_order ? seg_order : nullptr,
+                                stream) != hipSuccess)
       return GDN_ERR_HIP;
   }
   if (cu_seqlens) p.chunk_off = chunk_off;
@@ -357,6 +380,7 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
   plan.Tmat = tmat;
   plan.seg_chunks = P.seg_chunks;
   plan.seg_off = (cu_seqlens && P.split) ? seg_off : nullptr;
+  plan.seg_order = (cu_seqlens && L.has_seg_order) ? seg_order : nullptr;
   plan.units = P.total_segs * p.H;
   plan.value_block = P.value_block;
   plan.pass1_block = P.pass1_block;
@@ -457,7 +481,7 @@ int gdn_gate_scan(const float* g, const int32_t* cu_seqlens, const gdn_shape* sh
   gdn::Problem p = make_problem(nullptr, nullptr, nullptr, g, nullptr, nullptr, cu_seqlens, 1.f,
                                 nullptr, nullptr, shape, P.total_chunks);
   if (cu_seqlens &&
-      gdn::launch_plan_tables(cu_seqlens, p.N, 1, chunk_off, nullptr, stream) != hipSuccess)
+      gdn::launch_plan_tables(cu_seqlens, p.N, 1, chunk_off, nullptr, nullptr, stream) != hipSuccess)
     return GDN_ERR_HIP;
   if (cu_seqlens) p.chunk_off = chunk_off;
   if (gdn::launch_chunk_gate_sums(p, csum, stream) != hipSuccess) return GDN_ERR_HIP;

@@ -61,6 +61,7 @@ struct FwdPlan {
   const void* Tmat;          // chunk inverses [total_chunks, H, 64, 64]
   int seg_chunks;            // chunks per segment (>= max chunks of any sequence: one segment)
   const int32_t* seg_off;    // device [N+1] segment offsets (packed + split) or null
+  const int32_t* seg_order;  // device [total_segs] pass 3's segment order (longest first) or null
   int64_t units;             // number of (sequence, head, segment) units
   int value_block;           // value columns per workgroup: 64, 128, or 0 (widest that fits)
   int pass1_block;           // pass-1 columns per workgroup: 128 (if requested), else 64
@@ -69,8 +70,11 @@ struct FwdPlan {
 };
 
 hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hipStream_t s);
+// seg_order (nullable, needs seg_off): pass 3's segment order, longest first.
 hipError_t launch_plan_tables(const int32_t* cu, int N, int seg_chunks, int32_t* chunk_off,
-                              int32_t* seg_off, hipStream_t s);
+                              int32_t* seg_off, int32_t* seg_order, hipStream_t s);
+// Packed inputs of at most this many sequences get a longest-first segment order.
+constexpr int kSegOrderMaxSeqs = 4096;
 hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s);
 // Optional start / stop events of a single-kernel launch, recorded from the kernel's
 // own dispatch (hipExtLaunchKernel): timing a stage this way adds no packets to the
