@@ -62,7 +62,6 @@ __global__ __launch_bounds__(NT) void gate_window_max_kernel(const float* __rest
     best[nh * kWindowMaxCap + w] = (w < wmax && v > -INFINITY) ? ordered_bits(v) : 0u;
 }
 
-// Packed input: the chunk / segment offset tables.
 // Packed input: the chunk / segment offset tables, and (split plans) the order in
 // which pass 3 takes the segments: longest first (list scheduling: the long units
 // start early and the short ones fill the tail).  Every full segment (seg_chunks
@@ -87,22 +86,20 @@ __global__ __launch_bounds__(256) void plan_tables_kernel(const int32_t* __restr
       }
     }
   }
-  if (!seg_order) return;
-  __syncthreads();
-  auto last_len = [&](int n) {   // chunks of sequence n's last segment (0: empty sequence)
+  if (!seg_order) return;   // (N <= kSegOrderMaxSeqs when the table is requested)
+  __shared__ int last[kSegOrderMaxSeqs];   // chunks of each sequence's last segment
+  for (int n = threadIdx.x; n < N; n += blockDim.x) {
     const int nch = (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
-    return nch - (max(1, (nch + seg_chunks - 1) / seg_chunks) - 1) * seg_chunks;
-  };
+    last[n] = nch - (max(1, (nch + seg_chunks - 1) / seg_chunks) - 1) * seg_chunks;
+  }
+  __syncthreads();   // also publishes thread 0's seg_off to the workgroup
   const int full = seg_off[N] - N;   // full segments over all sequences
   for (int n = threadIdx.x; n < N; n += blockDim.x) {
     const int s0 = seg_off[n], segs = seg_off[n + 1] - s0;
     for (int j = 0; j + 1 < segs; ++j) seg_order[s0 - n + j] = s0 + j;
-    const int len = last_len(n);
+    const int len = last[n];
     int rank = 0;
-    for (int m = 0; m < N; ++m) {
-      const int lm = last_len(m);
-      rank += (lm > len || (lm == len && m < n)) ? 1 : 0;
-    }
+    for (int m = 0; m < N; ++m) rank += (last[m] > len || (last[m] == len && m < n)) ? 1 : 0;
     seg_order[full + rank] = s0 + segs - 1;
   }
 }

@@ -74,7 +74,7 @@ hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hi
 hipError_t launch_plan_tables(const int32_t* cu, int N, int seg_chunks, int32_t* chunk_off,
                               int32_t* seg_off, int32_t* seg_order, hipStream_t s);
 // Packed inputs of at most this many sequences get a longest-first segment order.
-constexpr int kSegOrderMaxSeqs = 4096;
+constexpr int kSegOrderMaxSeqs = 1024;
 hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s);
 // Optional start / stop events of a single-kernel launch, recorded from the kernel's
 // own dispatch (hipExtLaunchKernel): timing a stage this way adds no packets to the

@@ -76,6 +76,20 @@ def test_split_tree_merge_packed():
     assert_parity(compare_pairs(inp, o, hT), TOL["bf16"], "tree merge packed")
 
 
+@pytest.mark.parametrize("N", [300, 1030])
+def test_split_many_sequences(N):
+    """Many short packed sequences (0 to 4 chunks, empty ones included), split into
+    one-chunk segments: 300 sequences take the longest-first segment order table,
+    1030 exceed its size limit and keep sequence order.  Both must give the unsplit
+    result."""
+    rng = np.random.default_rng(90 + N)
+    lengths = rng.integers(0, 64 * 4 + 1, size=N)
+    lengths[rng.integers(0, N, size=N // 10)] = 0
+    inp = _packed(list(lengths), H=2, seed=91 + N, dk=64, dv=64, zero_heads=(0,))
+    o, hT = run_gpu(inp, opts=binding.make_opts(force_segment_chunks=1))
+    assert_parity(compare_pairs(inp, o, hT), TOL["bf16"], "N=%d" % N)
+
+
 def test_split_value_block_64_and_dk64_dv128():
     inp = synth.generate(spec(B=1, T=64 * 8, H=2, dk=64, dv=128, seed=73, zero_gate_heads=(0,)))
     for vb in (64, 128):
