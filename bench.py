@@ -199,14 +199,16 @@ def source_sha(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
 
-def traffic_for(kernel_src, launches_per_step=1):
+def traffic_for(kernel_src, workload, seg_chunks):
     """HBM bytes per launch from committed rocprofv3 counters, if they were taken on
-    this exact kernel source; else None."""
+    this exact kernel source, workload and segment length; else None."""
     path = os.path.join(ROOT, "profiles", "traffic_fused_forward.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     if rec.get("source_sha256") != source_sha(kernel_src):
+        return None
+    if rec.get("workload_name") != workload or rec.get("segment_chunks") != seg_chunks:
         return None
     return rec.get("bytes_per_launch")
 
@@ -375,7 +377,7 @@ def main():
     copy_gbs = copy_bandwidth(hip, stream, torch)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     ksrc = os.path.join(ROOT, "gated_deltanet_chunked_fwd_amd", "csrc", "fused_forward.hip")
-    traffic = traffic_for(ksrc) if dom == "fused_forward" else None
+    traffic = traffic_for(ksrc, spec.name, seg_chunks) if dom == "fused_forward" else None
     mfma_peak = BF16_PEAK_TFLOPS if spec.dtype == "bf16" else F32_PEAK_TFLOPS
     rec = {
         "metric": METRIC,
