@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--no-split", type=int, default=0)
     ap.add_argument("--value-block", type=int, default=0)
     ap.add_argument("--segment-chunks", type=int, default=0, help="force the split length (0: planner)")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="override the workload's batch size B (dense workloads; occupancy sweeps)")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB (the known-size kernel that "
                          "scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings) and exit")
@@ -248,6 +250,12 @@ def main():
     from gated_deltanet_chunked_fwd_amd import binding, synth
 
     spec = synth.WORKLOADS[args.workload]
+    if args.batch:
+        if spec.packed:
+            print("--batch applies to dense workloads only", file=sys.stderr)
+            sys.exit(2)
+        spec = synth.workload(args.workload, B=args.batch,
+                              name="%s_batch%d" % (spec.name, args.batch))
     inp = synth.generate(spec)
     dev = torch.device("cuda:0")
     d = {k: (None if inp[k] is None else inp[k].to(dev).contiguous())
