@@ -352,9 +352,11 @@ def main():
     hip.record(region_ev[0], stream)
     for i in range(K):
         step(call_opts[i])
+    t_enqueued = time.perf_counter()
     hip.record(region_ev[1], stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
+    host_ms = (t_enqueued - t_wall0) / K * 1e3   # host time to enqueue one call
     ms = hip.elapsed(region_ev[0], region_ev[1]) / K
     dom_ms_list = [hip.elapsed(kev[2 * i], kev[2 * i + 1]) for i in range(K)]
 
@@ -415,7 +417,8 @@ def main():
                  "ms_per_step_evicted_caches_median":
                      sorted(cold_ms)[len(cold_ms) // 2] if cold_ms else None,
                  "dominant_ms_min": min(dom_ms_list),
-                 "wall_s_timed_region": wall},
+                 "wall_s_timed_region": wall,
+                 "host_ms_per_call": host_ms},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(inp, spec)

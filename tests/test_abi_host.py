@@ -97,3 +97,35 @@ def test_status_strings():
     assert B.status_str(0) == "ok"
     assert "workspace" in B.status_str(B.GDN_ERR_WORKSPACE)
     assert B.status_str(12345) == "unknown status"
+
+
+def plan_L(s, opts=None):
+    return B.lib().gdn_plan_segment_chunks(ctypes.byref(s), None if opts is None else ctypes.byref(opts))
+
+
+def test_plan_cache_follows_packed_lengths_and_options():
+    """Plans are memoised per thread; a changed packed length (same buffer, same N and
+    T), a different option or a sixth shape must never return a stale plan."""
+    T = 8192 * 64
+    a = (ctypes.c_int32 * 3)(0, T // 2, T)            # two equal sequences
+    b_vals = (0, 64 * 16, T)                           # one short, one long
+    b = (ctypes.c_int32 * 3)(*b_vals)
+    sa = shape(T=T, N=2, H=4, cu_seqlens_host=ctypes.cast(a, ctypes.POINTER(ctypes.c_int32)))
+    sb = shape(T=T, N=2, H=4, cu_seqlens_host=ctypes.cast(b, ctypes.POINTER(ctypes.c_int32)))
+    la, lb = plan_L(sa), plan_L(sb)
+    assert la > 0 and lb > 0 and la != lb
+    n_a = ws_bytes(sa)[1]
+    for i, v in enumerate(b_vals):   # same pointer, new contents
+        a[i] = v
+    assert plan_L(sa) == lb and ws_bytes(sa)[1] == ws_bytes(sb)[1]
+    a[1] = T // 2
+    assert plan_L(sa) == la and ws_bytes(sa)[1] == n_a
+    forced = B.make_opts(force_segment_chunks=7)
+    assert plan_L(sa, forced) == 7 and plan_L(sa) == la
+    assert plan_L(sa, B.make_opts(no_split=1)) > 8192 and plan_L(sa) == la
+    # more distinct shapes than cache entries, twice round: answers stay the same
+    shapes = [shape(T=64 * n, H=h) for n, h in [(300, 1), (700, 2), (1500, 1), (4000, 1), (9000, 1),
+                                                 (20000, 1)]]
+    first = [plan_L(s) for s in shapes]
+    assert [plan_L(s) for s in shapes] == first
+    assert [plan_L(s) for s in reversed(shapes)] == list(reversed(first))
