@@ -7,6 +7,7 @@ whole output is checked for properties that hold at any size (finite everywhere,
 padded/untouched regions absent).  Tolerance: relative L2 per (sequence, head),
 1e-2 for bf16 storage, 1e-5 for fp32.
 """
+import math
 import time
 
 import numpy as np
@@ -72,3 +73,47 @@ def test_full_size_parity(w):
     tol = TOL[spec.dtype]
     print("  worst %.3e (tol %.0e), %.1f s" % (worst, tol, time.time() - t0), flush=True)
     assert worst <= tol
+
+
+def test_tensors_beyond_2pow31_elements():
+    """Every input tensor holds more than 2^31 elements (T = 2^20 + 37 tokens, 16 heads,
+    d = 128, bf16; a ragged last chunk), so any 32-bit element offset would wrap.  The
+    inputs are drawn on the GPU from a seeded generator (q, k L2-normalised, v normal,
+    g = log sigmoid(N(3, 1)) with the last head ungated, beta = sigmoid(N(0, 1))) and
+    the oracle runs on the first and the last head; the last head sits at the largest
+    offsets and takes the S*/M correction path."""
+    T, H, D = (1 << 20) + 37, 16, 128
+    assert T * H * D > 1 << 31
+    t0 = time.time()
+    gen = torch.Generator(device="cuda").manual_seed(31)
+
+    def unit_rows():
+        x = torch.randn((1, T, H, D), generator=gen, device="cuda")
+        x /= x.norm(dim=-1, keepdim=True)
+        return x.to(torch.bfloat16)
+
+    q, k = unit_rows(), unit_rows()
+    v = torch.randn((1, T, H, D), generator=gen, device="cuda").to(torch.bfloat16)
+    x = torch.randn((1, T, H), generator=gen, device="cuda", dtype=torch.float64) + 3.0
+    g = (-torch.log1p(torch.exp(-x))).to(torch.float32)
+    g[:, :, H - 1] = 0.0
+    beta = torch.sigmoid(torch.randn((1, T, H), generator=gen, device="cuda")).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(D)
+    print("inputs ready (%.1f s); planner segment chunks %d" % (
+        time.time() - t0, binding.plan_segment_chunks(q, v, beta)), flush=True)
+    o, hT = binding.chunk_fwd(q, k, v, g, beta, None, scale=scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(hT).all())
+    heads = torch.tensor([0, H - 1], device="cuda")
+    pick = lambda t: synth.as_f64(t.index_select(2, heads).cpu())  # noqa: E731
+    o_ref, h_ref = token.token_recurrence(pick(q), pick(k), pick(v), pick(g), pick(beta), None,
+                                          scale=scale)
+    og = o.index_select(2, heads).cpu().to(torch.float64).numpy()
+    hg = hT.index_select(1, heads).cpu().to(torch.float64).numpy()
+    worst = 0.0
+    for j, h in enumerate([0, H - 1]):
+        eo, eh = rel_l2(og[0, :, j], o_ref[0, :, j]), rel_l2(hg[0, j], h_ref[0, j])
+        print("  head %2d: o %.3e state %.3e" % (h, eo, eh), flush=True)
+        worst = max(worst, eo, eh)
+    print("  worst %.3e, %.1f s" % (worst, time.time() - t0), flush=True)
+    assert worst <= TOL["bf16"]
