@@ -19,7 +19,8 @@ GDN_OK, GDN_ERR_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 0, -1
 GDN_BF16, GDN_F32 = 1, 2
 
 # Symbols declared in include/gdn.h (checked by the CPU test of the boundary).
-EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_inverse",
+EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_stage",
+           "gdn_chunk_fwd_workspace_region", "gdn_chunk_inverse",
            "gdn_gate_scan", "gdn_gate_scan_workspace_bytes", "gdn_plan_segment_chunks",
            "gdn_total_chunks", "gdn_status_str")
 
@@ -41,6 +42,8 @@ class GdnOpts(ctypes.Structure):
 
 GDN_STAGE_INVERSE, GDN_STAGE_GATE_SCAN, GDN_STAGE_CP_PASS1, GDN_STAGE_CP_MERGE = 0, 1, 2, 3
 GDN_STAGE_FORWARD, GDN_NUM_STAGES = 4, 5
+GDN_REGION_CHUNK_INVERSE, GDN_REGION_WINDOWS, GDN_REGION_SEGMENT_MAPS = 0, 1, 2
+GDN_REGION_SEGMENT_STARTS, GDN_NUM_REGIONS = 3, 4
 STAGE_NAMES = ("chunk_inverse", "gate_scan", "cp_pass1", "cp_merge", "fused_forward")
 
 
@@ -67,6 +70,11 @@ def lib():
         L.gdn_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, shp, opt,
                                     vp, sz, vp]
         L.gdn_chunk_fwd.restype = ctypes.c_int
+        L.gdn_chunk_fwd_stage.argtypes = [ctypes.c_int] + L.gdn_chunk_fwd.argtypes
+        L.gdn_chunk_fwd_stage.restype = ctypes.c_int
+        L.gdn_chunk_fwd_workspace_region.argtypes = [shp, opt, ctypes.c_int, ctypes.POINTER(sz),
+                                                     ctypes.POINTER(sz)]
+        L.gdn_chunk_fwd_workspace_region.restype = ctypes.c_int
         L.gdn_chunk_inverse.argtypes = [vp, vp, vp, vp, shp, vp, vp, sz, vp]
         L.gdn_chunk_inverse.restype = ctypes.c_int
         L.gdn_gate_scan.argtypes = [vp, vp, shp, opt, vp, vp, sz, vp]
@@ -143,7 +151,7 @@ def workspace_bytes(q, v, beta, cu_seqlens=None, cu_seqlens_host=None, opts=None
 
 def chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=None,
               output_final_state=True, opts: Optional[GdnOpts] = None, cu_seqlens_host=None,
-              out=None, final_state_out=None, workspace=None):
+              out=None, final_state_out=None, workspace=None, stage=None):
     """GDN chunked forward.  Returns ``(o, final_state)`` (final_state None if not requested).
 
     Layouts follow include/gdn.h: q, k [B,T,H,dk]; v [B,T,H,dv]; g, beta [B,T,H];
@@ -169,14 +177,43 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=None,
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_chunk_fwd_workspace_bytes")
     if workspace is None or workspace.numel() < n.value:
+        if stage is not None:
+            raise ValueError("a stage call needs the caller's workspace (workspace_bytes())")
         workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=q.device)
-    rc = lib().gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
-                             _ptr(cu_seqlens), ctypes.c_float(scale), _ptr(o), _ptr(fs), sh.ref(),
-                             opts_ref, _ptr(workspace), ctypes.c_size_t(workspace.numel()),
-                             _stream(q.device))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+            ctypes.c_float(scale), _ptr(o), _ptr(fs), sh.ref(), opts_ref, _ptr(workspace),
+            ctypes.c_size_t(workspace.numel()), _stream(q.device))
+    if stage is None:
+        rc = lib().gdn_chunk_fwd(*args)
+    else:
+        rc = lib().gdn_chunk_fwd_stage(ctypes.c_int(stage), *args)
     if rc != GDN_OK:
-        raise GdnError(rc, "gdn_chunk_fwd")
+        raise GdnError(rc, "gdn_chunk_fwd" if stage is None else "gdn_chunk_fwd_stage")
     return o, fs
+
+
+def chunk_fwd_stage(stage, q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=None,
+                    opts: Optional[GdnOpts] = None, cu_seqlens_host=None, out=None,
+                    final_state_out=None, workspace=None):
+    """One stage (GDN_STAGE_*) of chunk_fwd on the caller's workspace and outputs; the
+    stages run in order give chunk_fwd's result (include/gdn.h, gdn_chunk_fwd_stage)."""
+    if out is None or workspace is None:
+        raise ValueError("chunk_fwd_stage needs out= and workspace= (shared by all stages)")
+    return chunk_fwd(q, k, v, g, beta, initial_state, cu_seqlens, scale,
+                     output_final_state=final_state_out is not None, opts=opts,
+                     cu_seqlens_host=cu_seqlens_host, out=out, final_state_out=final_state_out,
+                     workspace=workspace, stage=stage)
+
+
+def workspace_region(q, v, beta, region, cu_seqlens=None, cu_seqlens_host=None, opts=None):
+    """(offset, bytes) of a GDN_REGION_* inside chunk_fwd's workspace."""
+    sh = _Shape(q, v, beta, cu_seqlens, cu_seqlens_host)
+    off, n = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    rc = lib().gdn_chunk_fwd_workspace_region(sh.ref(), None if opts is None else ctypes.byref(opts),
+                                              ctypes.c_int(region), ctypes.byref(off), ctypes.byref(n))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_chunk_fwd_workspace_region")
+    return int(off.value), int(n.value)
 
 
 def chunk_inverse(k, g, beta, cu_seqlens=None, cu_seqlens_host=None):

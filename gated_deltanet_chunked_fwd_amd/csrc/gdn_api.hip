@@ -373,6 +373,104 @@ int check_inputs(const void* k, const float* g, const void* beta, const int32_t*
   return GDN_OK;
 }
 
+
+// Runs stages [first, last] of the forward pass (GDN_STAGE_*, launch order) on one
+// workspace; gdn_chunk_fwd is all of them.  Every call validates all arguments and
+// plans the same way, so a caller that runs the stages one by one, in order, on one
+// stream and workspace, gets the result of gdn_chunk_fwd bit for bit.  Stages the
+// plan does not need (the split stages of an unsplit plan, the gate scan when the
+// correction is forced) enqueue nothing.
+int run_stages(int first, int last, const void* q, const void* k, const void* v, const float* g,
+               const void* beta, const float* initial_state, const int32_t* cu_seqlens,
+               float scale, void* o, float* final_state, const gdn_shape* shape,
+               const gdn_opts* opts, void* workspace, size_t workspace_bytes,
+               hipStream_t stream) {
+  auto runs = [&](int st) { return first <= st && st <= last; };
+  int rc = validate_shape(shape);
+  if (rc == GDN_OK) rc = validate_opts(opts);
+  if (rc == GDN_OK) rc = check_inputs(k, g, beta, cu_seqlens, shape);
+  if (rc != GDN_OK) return rc;
+  if (shape->T > 0 && (!q || !v || !o)) return GDN_ERR_ARG;
+  if ((q && !aligned(q, 16)) || (v && !aligned(v, 16)) || (o && !aligned(o, 16)) ||
+      (initial_state && !aligned(initial_state, 16)) || (final_state && !aligned(final_state, 16)))
+    return GDN_ERR_ARG;
+  if (!std::isfinite(scale)) return GDN_ERR_ARG;
+  const Plan P = make_plan(shape, opts);
+  const Layout L = layout(shape, P);
+  if (workspace_bytes < L.total || (L.total > 0 && !workspace) || !aligned(workspace, kAlign))
+    return GDN_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  gdn::Problem p = make_problem(q, k, v, g, beta, initial_state, cu_seqlens, scale, o,
+                                final_state, shape, P.total_chunks);
+  int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + L.chunk_off);
+  int32_t* seg_off = reinterpret_cast<int32_t*>(ws + L.seg_off);
+  int32_t* seg_order = reinterpret_cast<int32_t*>(ws + L.seg_order);
+  uint32_t* best = reinterpret_cast<uint32_t*>(ws + L.best);
+  // the packed-sequence tables live in the workspace: built with step 1, read by every stage
+  if (cu_seqlens && runs(GDN_STAGE_INVERSE)) {
+    if (gdn::launch_plan_tables(cu_seqlens, p.N, P.seg_chunks, chunk_off,
+                                P.split ? seg_off : nullptr, L.has_seg_order ? seg_order : nullptr,
+                                stream) != hipSuccess)
+      return GDN_ERR_HIP;
+  }
+  if (cu_seqlens) p.chunk_off = chunk_off;
+
+  void* tmat = ws + L.tmat;
+  float* csum = P.split ? reinterpret_cast<float*>(ws + L.csum) : nullptr;
+  if (runs(GDN_STAGE_INVERSE)) {
+    if (gdn::launch_chunk_inverse(p, tmat, csum, false, stream,
+                                  stage_events(opts, GDN_STAGE_INVERSE)) != hipSuccess)
+      return GDN_ERR_HIP;
+  }
+
+  gdn::FwdPlan plan;
+  plan.Tmat = tmat;
+  plan.seg_chunks = P.seg_chunks;
+  plan.seg_off = (cu_seqlens && P.split) ? seg_off : nullptr;
+  plan.seg_order = (cu_seqlens && L.has_seg_order) ? seg_order : nullptr;
+  plan.units = P.total_segs * p.H;
+  plan.value_block = P.value_block;
+  plan.pass1_block = P.pass1_block;
+  plan.mode = gdn::kPass3;
+  plan.cp = gdn::CpBuffers{};
+  if (P.split) {
+    plan.cp.best = best;
+    plan.cp.wmax = P.wmax;
+    plan.cp.thr = P.log_eps - kWindowMargin;
+    plan.cp.force_correction = opts ? opts->force_correction : 0;
+    plan.cp.sstar = reinterpret_cast<float*>(ws + L.sstar);
+    plan.cp.mcorr = ws + L.mcorr;
+    plan.cp.hstart = reinterpret_cast<float*>(ws + L.hstart);
+    plan.cp.gmat = L.gmat ? ws + L.gmat : nullptr;
+    plan.cp.gvec = L.gvec ? reinterpret_cast<float*>(ws + L.gvec) : nullptr;
+    if (!plan.cp.force_correction && runs(GDN_STAGE_GATE_SCAN)) {
+      if (gdn::launch_gate_scan(p, csum, P.max_chunks, P.wmax, best, stream,
+                                stage_events(opts, GDN_STAGE_GATE_SCAN)) != hipSuccess)
+        return GDN_ERR_HIP;
+    }
+    if (runs(GDN_STAGE_CP_PASS1)) {
+      gdn::FwdPlan p1 = plan;
+      p1.mode = gdn::kPass1;
+      if (gdn::launch_fused_forward(p, p1, stream, stage_events(opts, GDN_STAGE_CP_PASS1)) !=
+          hipSuccess)
+        return GDN_ERR_HIP;
+    }
+    if (runs(GDN_STAGE_CP_MERGE)) {
+      const int max_steps = (int)((P.max_chunks + P.seg_chunks - 1) / P.seg_chunks - 1);
+      if (gdn::launch_cp_merge(p, plan, max_steps, stream, stage_events(opts, GDN_STAGE_CP_MERGE)) !=
+          hipSuccess)
+        return GDN_ERR_HIP;
+    }
+  }
+  if (runs(GDN_STAGE_FORWARD)) {
+    if (gdn::launch_fused_forward(p, plan, stream, stage_events(opts, GDN_STAGE_FORWARD)) !=
+        hipSuccess)
+      return GDN_ERR_HIP;
+  }
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -405,86 +503,53 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                   const float* initial_state, const int32_t* cu_seqlens, float scale, void* o,
                   float* final_state, const gdn_shape* shape, const gdn_opts* opts,
                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run_stages(0, GDN_NUM_STAGES - 1, q, k, v, g, beta, initial_state, cu_seqlens, scale, o,
+                    final_state, shape, opts, workspace, workspace_bytes, stream);
+}
+
+int gdn_chunk_fwd_stage(int stage, const void* q, const void* k, const void* v, const float* g,
+                        const void* beta, const float* initial_state, const int32_t* cu_seqlens,
+                        float scale, void* o, float* final_state, const gdn_shape* shape,
+                        const gdn_opts* opts, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  if (stage < 0 || stage >= GDN_NUM_STAGES) return GDN_ERR_ARG;
+  return run_stages(stage, stage, q, k, v, g, beta, initial_state, cu_seqlens, scale, o,
+                    final_state, shape, opts, workspace, workspace_bytes, stream);
+}
+
+int gdn_chunk_fwd_workspace_region(const gdn_shape* shape, const gdn_opts* opts, int region,
+                                   size_t* offset, size_t* bytes) {
   int rc = validate_shape(shape);
   if (rc == GDN_OK) rc = validate_opts(opts);
-  if (rc == GDN_OK) rc = check_inputs(k, g, beta, cu_seqlens, shape);
   if (rc != GDN_OK) return rc;
-  if (shape->T > 0 && (!q || !v || !o)) return GDN_ERR_ARG;
-  if ((q && !aligned(q, 16)) || (v && !aligned(v, 16)) || (o && !aligned(o, 16)) ||
-      (initial_state && !aligned(initial_state, 16)) || (final_state && !aligned(final_state, 16)))
-    return GDN_ERR_ARG;
-  if (!std::isfinite(scale)) return GDN_ERR_ARG;
+  if (!offset || !bytes || region < 0 || region >= GDN_NUM_REGIONS) return GDN_ERR_ARG;
   const Plan P = make_plan(shape, opts);
   const Layout L = layout(shape, P);
-  if (workspace_bytes < L.total || (L.total > 0 && !workspace) || !aligned(workspace, kAlign))
-    return GDN_ERR_WORKSPACE;
-
-  char* ws = static_cast<char*>(workspace);
-  gdn::Problem p = make_problem(q, k, v, g, beta, initial_state, cu_seqlens, scale, o,
-                                final_state, shape, P.total_chunks);
-  int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + L.chunk_off);
-  int32_t* seg_off = reinterpret_cast<int32_t*>(ws + L.seg_off);
-  int32_t* seg_order = reinterpret_cast<int32_t*>(ws + L.seg_order);
-  uint32_t* best = reinterpret_cast<uint32_t*>(ws + L.best);
-  if (cu_seqlens) {
-    if (gdn::launch_plan_tables(cu_seqlens, p.N, P.seg_chunks, chunk_off,
-                                P.split ? seg_off : nullptr, L.has_seg_order ? seg_order : nullptr,
-                                stream) != hipSuccess)
-      return GDN_ERR_HIP;
-  }
-  if (cu_seqlens) p.chunk_off = chunk_off;
-
-  void* tmat = ws + L.tmat;
-  float* csum = P.split ? reinterpret_cast<float*>(ws + L.csum) : nullptr;
-  {
-    if (gdn::launch_chunk_inverse(p, tmat, csum, false, stream,
-                                  stage_events(opts, GDN_STAGE_INVERSE)) != hipSuccess)
-      return GDN_ERR_HIP;
-  }
-
-  gdn::FwdPlan plan;
-  plan.Tmat = tmat;
-  plan.seg_chunks = P.seg_chunks;
-  plan.seg_off = (cu_seqlens && P.split) ? seg_off : nullptr;
-  plan.seg_order = (cu_seqlens && L.has_seg_order) ? seg_order : nullptr;
-  plan.units = P.total_segs * p.H;
-  plan.value_block = P.value_block;
-  plan.pass1_block = P.pass1_block;
-  plan.mode = gdn::kPass3;
-  plan.cp = gdn::CpBuffers{};
-  if (P.split) {
-    plan.cp.best = best;
-    plan.cp.wmax = P.wmax;
-    plan.cp.thr = P.log_eps - kWindowMargin;
-    plan.cp.force_correction = opts ? opts->force_correction : 0;
-    plan.cp.sstar = reinterpret_cast<float*>(ws + L.sstar);
-    plan.cp.mcorr = ws + L.mcorr;
-    plan.cp.hstart = reinterpret_cast<float*>(ws + L.hstart);
-    plan.cp.gmat = L.gmat ? ws + L.gmat : nullptr;
-    plan.cp.gvec = L.gvec ? reinterpret_cast<float*>(ws + L.gvec) : nullptr;
-    if (!plan.cp.force_correction) {
-      if (gdn::launch_gate_scan(p, csum, P.max_chunks, P.wmax, best, stream,
-                                stage_events(opts, GDN_STAGE_GATE_SCAN)) != hipSuccess)
-        return GDN_ERR_HIP;
-    }
-    {
-      gdn::FwdPlan p1 = plan;
-      p1.mode = gdn::kPass1;
-      if (gdn::launch_fused_forward(p, p1, stream, stage_events(opts, GDN_STAGE_CP_PASS1)) !=
-          hipSuccess)
-        return GDN_ERR_HIP;
-    }
-    {
-      const int max_steps = (int)((P.max_chunks + P.seg_chunks - 1) / P.seg_chunks - 1);
-      if (gdn::launch_cp_merge(p, plan, max_steps, stream, stage_events(opts, GDN_STAGE_CP_MERGE)) !=
-          hipSuccess)
-        return GDN_ERR_HIP;
-    }
-  }
-  {
-    if (gdn::launch_fused_forward(p, plan, stream, stage_events(opts, GDN_STAGE_FORWARD)) !=
-        hipSuccess)
-      return GDN_ERR_HIP;
+  const size_t esz = shape->qkv_dtype == GDN_BF16 ? 2 : 4;
+  const size_t slots = (size_t)P.total_segs * shape->H;
+  *offset = 0;
+  *bytes = 0;
+  switch (region) {
+    case GDN_REGION_CHUNK_INVERSE:
+      *offset = L.tmat;
+      *bytes = (size_t)P.total_chunks * shape->H * kChunk * kChunk * esz;
+      break;
+    case GDN_REGION_WINDOWS:
+      *offset = L.best;
+      *bytes = (size_t)shape->N * shape->H * kWindowMaxCap * sizeof(uint32_t);
+      break;
+    case GDN_REGION_SEGMENT_MAPS:
+      if (P.split) {
+        *offset = L.sstar;
+        *bytes = L.mcorr - L.sstar + slots * 2 * shape->dk * shape->dk * sizeof(uint16_t);
+      }
+      break;
+    default:   // GDN_REGION_SEGMENT_STARTS
+      if (P.split) {
+        *offset = L.hstart;
+        *bytes = slots * shape->dk * shape->dv * sizeof(float);
+      }
+      break;
   }
   return GDN_OK;
 }

@@ -28,7 +28,8 @@
  *     the first launch, so an error return means nothing was enqueued, except
  *     GDN_ERR_HIP, which reports a failed launch.
  *   * No exceptions cross this boundary.  The library holds no mutable global
- *     state besides a per-device property cache filled once.
+ *     state besides a per-device property cache filled once and, per host
+ *     thread, the last few plans (keyed by everything a plan depends on).
  */
 #ifndef GDN_H
 #define GDN_H
@@ -131,6 +132,58 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                   float scale, void* o, float* final_state, const gdn_shape* shape,
                   const gdn_opts* opts, void* workspace, size_t workspace_bytes,
                   hipStream_t stream);
+
+/*
+ * One stage of gdn_chunk_fwd (the two-level API of the pages: the API section
+ * describes a high-level call and a split, lower-level one for frameworks that
+ * schedule the pieces themselves).  `stage` is a GDN_STAGE_* value; every other
+ * argument has the meaning it has for gdn_chunk_fwd and must be the same in every
+ * stage call of one forward pass.  Running stages 0 .. GDN_NUM_STAGES-1 in order on
+ * one stream and one workspace gives gdn_chunk_fwd's result bit for bit; between
+ * two stages a caller may read, or replace with bytes produced by the same stage
+ * elsewhere, the workspace regions below (gdn_chunk_fwd_workspace_region).  A
+ * stage that the plan does not need (the split stages when no sequence is split,
+ * the gate scan under force_correction) enqueues nothing and returns GDN_OK.
+ * GDN_STAGE_INVERSE also builds the packed-sequence tables the later stages read.
+ * Errors as gdn_chunk_fwd; an unknown stage is GDN_ERR_ARG.
+ */
+int gdn_chunk_fwd_stage(int stage, const void* q, const void* k, const void* v, const float* g,
+                        const void* beta, const float* initial_state,
+                        const int32_t* cu_seqlens, float scale, void* o, float* final_state,
+                        const gdn_shape* shape, const gdn_opts* opts, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace regions that connect the stages.  Segments are numbered over all
+ * sequences in order (segment j of sequence n is seg_base(n) + j, where seg_base
+ * counts the segments of the earlier sequences; a sequence that is not split, or
+ * is empty, has one), and (segment s, head h) is slot s * H + h. */
+enum {
+  GDN_REGION_CHUNK_INVERSE = 0,  /* T of every chunk-head: [total_chunks, H, 64, 64] in
+                                    shape->qkv_dtype, as gdn_chunk_inverse writes it, except
+                                    that the (zero) upper-right 32 x 32 quadrant is not
+                                    written (written by GDN_STAGE_INVERSE) */
+  GDN_REGION_WINDOWS = 1,        /* per (sequence, head): 16 uint32, the largest gate sum
+                                    over runs of 1..16 chunks in an order-preserving encoding
+                                    (GDN_STAGE_GATE_SCAN) */
+  GDN_REGION_SEGMENT_MAPS = 2,   /* per slot the affine map of its segment: the wrong-start
+                                    end state S* (dk * dv fp32 per slot, all slots), then,
+                                    at a 256-byte aligned offset, the transition M (2 * dk *
+                                    dk bf16 per slot, a high and a low part); element order
+                                    inside a slot is the kernels' own (GDN_STAGE_CP_PASS1;
+                                    read by GDN_STAGE_CP_MERGE).  Slots of a sequence's last
+                                    segment, and of heads that take lookback windows, are
+                                    not written */
+  GDN_REGION_SEGMENT_STARTS = 3, /* per slot the true start state, [slots, dk, dv] fp32,
+                                    K-major like initial_state (GDN_STAGE_CP_MERGE; read by
+                                    GDN_STAGE_FORWARD for corrected heads) */
+  GDN_NUM_REGIONS = 4
+};
+
+/* Byte offset and size of a workspace region for this problem and options (both
+ * 0 when the plan does not split, for the two segment regions).  Returns GDN_OK,
+ * or an error code for an invalid shape, option or region. */
+int gdn_chunk_fwd_workspace_region(const gdn_shape* shape, const gdn_opts* opts, int region,
+                                   size_t* offset, size_t* bytes);
 
 /*
  * Step 1 alone (chunked-WY section, first step; the pages cut the kernel after

@@ -129,3 +129,47 @@ def test_plan_cache_follows_packed_lengths_and_options():
     first = [plan_L(s) for s in shapes]
     assert [plan_L(s) for s in shapes] == first
     assert [plan_L(s) for s in reversed(shapes)] == list(reversed(first))
+
+
+def region(s, r, opts=None):
+    off, n = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    rc = B.lib().gdn_chunk_fwd_workspace_region(ctypes.byref(s), None if opts is None else ctypes.byref(opts),
+                                                r, ctypes.byref(off), ctypes.byref(n))
+    return rc, off.value, n.value
+
+
+def test_workspace_regions():
+    """The stage-connecting regions lie inside the workspace, 256-byte aligned and
+    disjoint, with the sizes their layouts imply; the segment regions are empty when
+    nothing is split; unknown regions and stages are rejected before any launch."""
+    T, H, d = 64 * 14 + 23, 3, 128
+    s = shape(T=T, H=H, dk=d, dv=d)
+    split = B.make_opts(force_segment_chunks=3)
+    total = ctypes.c_size_t(0)
+    assert B.lib().gdn_chunk_fwd_workspace_bytes(ctypes.byref(s), ctypes.byref(split), ctypes.byref(total)) == 0
+    chunks, segs = 15, 5
+    want = {B.GDN_REGION_CHUNK_INVERSE: chunks * H * 64 * 64 * 2, B.GDN_REGION_WINDOWS: H * 16 * 4,
+            B.GDN_REGION_SEGMENT_STARTS: segs * H * d * d * 4}
+    spans = []
+    for r in range(B.GDN_NUM_REGIONS):
+        rc, off, n = region(s, r, split)
+        assert rc == B.GDN_OK and off % 256 == 0 and 0 < n and off + n <= total.value
+        if r in want:
+            assert n == want[r], r
+        spans.append((off, off + n))
+    rc, off, n = region(s, B.GDN_REGION_SEGMENT_MAPS, split)
+    # S* (fp32) then M (2 x bf16) per slot, M at the next 256-byte boundary
+    smap = segs * H * d * d * 4
+    assert n == -(-smap // 256) * 256 + segs * H * 2 * d * d * 2
+    spans.sort()
+    assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+    unsplit = B.make_opts(no_split=1)
+    for r in (B.GDN_REGION_SEGMENT_MAPS, B.GDN_REGION_SEGMENT_STARTS):
+        assert region(s, r, unsplit) == (B.GDN_OK, 0, 0)
+    assert region(s, B.GDN_NUM_REGIONS)[0] == B.GDN_ERR_ARG
+    assert region(s, -1)[0] == B.GDN_ERR_ARG
+    fake = ctypes.c_void_p(4096)
+    args = [fake] * 5 + [None, None, ctypes.c_float(0.1), fake, None, ctypes.byref(s), None,
+            fake, ctypes.c_size_t(1 << 40), None]
+    for bad in (-1, B.GDN_NUM_STAGES):
+        assert B.lib().gdn_chunk_fwd_stage(bad, *args) == B.GDN_ERR_ARG

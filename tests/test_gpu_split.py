@@ -148,3 +148,83 @@ def test_gate_scan_stage(kind, eps_bits):
             checked += 1
     print("gate scan windows:", win.tolist())
     assert checked > 0
+
+
+def _stage_setup(inp, opts):
+    d = to_dev(inp)
+    spec = inp["spec"]
+    N = inp.get("N", spec.B)
+    nbytes = binding.workspace_bytes(d["q"], d["v"], d["beta"], d["cu_seqlens"], d["cu_host"], opts)
+    new_ws = lambda: torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")  # noqa: E731
+    outs = lambda: (torch.empty_like(d["v"]),  # noqa: E731
+                    torch.empty((N, spec.H, spec.dk, spec.dv), dtype=torch.float32, device="cuda"))
+
+    def run(stages, ws, o, hT):
+        for st in stages:
+            binding.chunk_fwd_stage(st, d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"],
+                                    cu_seqlens=d["cu_seqlens"], scale=inp["scale"], opts=opts,
+                                    cu_seqlens_host=d["cu_host"], out=o, final_state_out=hT,
+                                    workspace=ws)
+        torch.cuda.synchronize()
+
+    def region(r):
+        return binding.workspace_region(d["q"], d["v"], d["beta"], r, d["cu_seqlens"], d["cu_host"], opts)
+    return d, new_ws, outs, run, region
+
+
+STAGE_CASES = {
+    "dense_split": (lambda: synth.generate(spec(seed=81, h0_std=0.05)),
+                    dict(force_segment_chunks=3)),
+    "dense_tree": (lambda: synth.generate(spec(T=64 * 40 + 9, seed=82)), dict(force_segment_chunks=2)),
+    "packed_split": (lambda: _packed([64 * 9 + 7, 40, 0, 64 * 3, 64 * 6 + 1, 0], H=2, seed=83),
+                     dict(force_segment_chunks=2)),
+    "unsplit_f32": (lambda: synth.generate(spec(H=2, dk=64, dv=64, dtype="f32", seed=84)), dict(no_split=1)),
+    "planner": (lambda: synth.generate(spec(T=64 * 64, seed=85)), dict()),
+}
+
+
+@pytest.mark.parametrize("case", sorted(STAGE_CASES))
+def test_stages_one_by_one_equal_whole_call(case):
+    """gdn_chunk_fwd_stage run for every stage in order reproduces gdn_chunk_fwd bit
+    for bit (split with correction and window heads, tree merge, packed, unsplit)."""
+    make, kw = STAGE_CASES[case]
+    inp = make()
+    opts = binding.make_opts(**kw)
+    d, new_ws, outs, run, _ = _stage_setup(inp, opts)
+    o_ref, h_ref = outs()
+    binding.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], cu_seqlens=d["cu_seqlens"],
+                      scale=inp["scale"], opts=opts, cu_seqlens_host=d["cu_host"], out=o_ref,
+                      final_state_out=h_ref, workspace=new_ws())
+    o, hT = outs()
+    run(range(binding.GDN_NUM_STAGES), new_ws(), o, hT)
+    assert torch.equal(o, o_ref) and torch.equal(hT, h_ref), case
+    assert_parity(compare_pairs(inp, o, hT), TOL[inp["spec"].dtype], "stages " + case)
+
+
+@pytest.mark.parametrize("case", ["dense_split", "dense_tree", "packed_split"])
+def test_segment_regions_carry_everything_the_next_stage_needs(case):
+    """A second workspace that ran only the stages before the merge, given the S*/M
+    region of the first (as a sequence split across GPUs would receive it), finishes
+    with the first's result; so does one given only the segment-start region before
+    the last stage."""
+    make, kw = STAGE_CASES[case]
+    inp = make()
+    opts = binding.make_opts(**kw)
+    d, new_ws, outs, run, region = _stage_setup(inp, opts)
+    S = binding
+    wa = new_ws()
+    o_ref, h_ref = outs()
+    run(range(S.GDN_NUM_STAGES), wa, o_ref, h_ref)
+    for reg, before, after in [(S.GDN_REGION_SEGMENT_MAPS, [S.GDN_STAGE_INVERSE, S.GDN_STAGE_GATE_SCAN],
+                                [S.GDN_STAGE_CP_MERGE, S.GDN_STAGE_FORWARD]),
+                               (S.GDN_REGION_SEGMENT_STARTS, [S.GDN_STAGE_INVERSE, S.GDN_STAGE_GATE_SCAN],
+                                [S.GDN_STAGE_FORWARD])]:
+        off, n = region(reg)
+        assert n > 0
+        wb = new_ws()
+        wb.fill_(0xA5)   # nothing of the first workspace leaks in
+        o, hT = outs()
+        run(before, wb, o, hT)
+        wb[off:off + n].copy_(wa[off:off + n])
+        run(after, wb, o, hT)
+        assert torch.equal(o, o_ref) and torch.equal(hT, h_ref), (case, reg)
