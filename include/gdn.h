@@ -145,6 +145,9 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
  * stage that the plan does not need (the split stages when no sequence is split,
  * the gate scan under force_correction) enqueues nothing and returns GDN_OK.
  * GDN_STAGE_INVERSE also builds the packed-sequence tables the later stages read.
+ * Each stage reads what the earlier stages of the same pass wrote into the
+ * workspace: running a stage on a workspace where they have not run (or ran with
+ * other arguments) is undefined, and with packed sequences can index out of range.
  * Errors as gdn_chunk_fwd; an unknown stage is GDN_ERR_ARG.
  */
 int gdn_chunk_fwd_stage(int stage, const void* q, const void* k, const void* v, const float* g,
