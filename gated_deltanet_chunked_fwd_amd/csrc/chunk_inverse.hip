@@ -280,7 +280,7 @@ hipError_t launch_chunk_inverse(const Problem& p, void* t_out, float* csum, bool
     return hipSuccess;
   }
   const int64_t blocks = p.total_chunks * ((p.H + 3) / 4);
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (blocks > kMaxDispatchItems / 256) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks);
   if (p.qkv_bf16) {
     if (p.dk == 128)

@@ -241,16 +241,23 @@ __global__ __launch_bounds__(64 * MergeCfg<DK>::NW) void cp_merge_kernel(Problem
 
 // ev: start recorded from the first kernel's dispatch, stop from the last one's.
 template <int DK>
-static void launch_merge_dk(const Problem& p, const FwdPlan& plan, int max_steps, hipStream_t s,
+static hipError_t launch_merge_dk(const Problem& p, const FwdPlan& plan, int max_steps, hipStream_t s,
                             KernelEvents ev) {
   const dim3 nt(64 * MergeCfg<DK>::NW);
   const int64_t nh = (int64_t)p.N * p.H;
   const int ncb = p.dv / 16;
   auto grid = [&](int64_t units, int cbs) { return dim3((unsigned)((units + 7) / 8 * 8 * cbs)); };
+  {   // the widest launch (the group maps, or the whole chain) must fit a dispatch
+    int G = 1;
+    while ((int64_t)G * G < max_steps) ++G;
+    const int64_t maxg = max_steps > kMergeTreeMinSteps ? (max_steps + G - 1) / G : 1;
+    if ((nh * maxg + 7) / 8 * 8 > kMaxDispatchItems / ((int64_t)(DK + p.dv) / 16 * nt.x))
+      return hipErrorInvalidConfiguration;
+  }
   if (max_steps <= kMergeTreeMinSteps) {
     hipExtLaunchKernelGGL(cp_merge_kernel<DK, kRun>, grid(nh, ncb), nt, 0, s, ev.start, ev.stop, 0, p, plan,
                           max(max_steps, 1), 1, 0);
-    return;
+    return hipGetLastError();
   }
   int G = 1;
   while ((int64_t)G * G < max_steps) ++G;   // G = ceil(sqrt(steps))
@@ -261,6 +268,7 @@ static void launch_merge_dk(const Problem& p, const FwdPlan& plan, int max_steps
                         G, 1, 1);
   hipExtLaunchKernelGGL(cp_merge_kernel<DK, kRun>, grid(nh * maxg, ncb), nt, 0, s, nullptr, ev.stop, 0, p,
                         plan, G, maxg, 1);
+  return hipGetLastError();
 }
 
 hipError_t launch_cp_merge(const Problem& p, const FwdPlan& plan, int max_steps, hipStream_t s,
@@ -269,9 +277,8 @@ hipError_t launch_cp_merge(const Problem& p, const FwdPlan& plan, int max_steps,
     ev.record_empty(s);
     return hipSuccess;
   }
-  if (p.dk == 128) launch_merge_dk<128>(p, plan, max_steps, s, ev);
-  else launch_merge_dk<64>(p, plan, max_steps, s, ev);
-  return hipGetLastError();
+  return p.dk == 128 ? launch_merge_dk<128>(p, plan, max_steps, s, ev)
+                     : launch_merge_dk<64>(p, plan, max_steps, s, ev);
 }
 
 }  // namespace gdn

@@ -693,10 +693,12 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
 
 // 1-D grid of ceil(units / 8) * 8 * column blocks (see the decode in the kernel).
 template <typename E, int DK, int PASS>
-static void launch_dk(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev) {
+static hipError_t launch_dk(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev) {
   // pass 1 also runs dk transition-matrix columns after the dv value columns
   const int cols = PASS == kPass1 ? p.dv + DK : p.dv;
   const int64_t groups = (plan.units + 7) / 8;
+  if (groups * 8 > kMaxDispatchItems / (4 * cols))   // 4 threads per column in either shape
+    return hipErrorInvalidConfiguration;
   if constexpr (sizeof(E) == 2) {
     // 128 columns per workgroup as 8 waves x 16 columns: two waves per SIMD.  Pass 1
     // always takes 64-column workgroups: both shapes reach the same throughput per CU,
@@ -707,19 +709,20 @@ static void launch_dk(const Problem& p, const FwdPlan& plan, hipStream_t s, Kern
       const int ncb = cols / 128;
       hipExtLaunchKernelGGL(fused_forward_kernel<E, DK, 16, 8, PASS>, dim3((unsigned)(groups * 8 * ncb)),
                             dim3(512), 0, s, ev.start, ev.stop, 0, p, plan);
-      return;
+      return hipGetLastError();
     }
   }
   // 64 columns per workgroup as 4 waves x 16 columns (fp32 tiles only fit LDS this way)
   const int ncb = cols / 64;
   hipExtLaunchKernelGGL(fused_forward_kernel<E, DK, 16, 4, PASS>, dim3((unsigned)(groups * 8 * ncb)),
                         dim3(256), 0, s, ev.start, ev.stop, 0, p, plan);
+  return hipGetLastError();
 }
 
 template <typename E, int DK>
-static void launch_pass(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev) {
-  if (plan.mode == kPass1) launch_dk<E, DK, kPass1>(p, plan, s, ev);
-  else launch_dk<E, DK, kPass3>(p, plan, s, ev);
+static hipError_t launch_pass(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev) {
+  if (plan.mode == kPass1) return launch_dk<E, DK, kPass1>(p, plan, s, ev);
+  return launch_dk<E, DK, kPass3>(p, plan, s, ev);
 }
 
 hipError_t launch_fused_forward(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev) {
@@ -727,14 +730,8 @@ hipError_t launch_fused_forward(const Problem& p, const FwdPlan& plan, hipStream
     ev.record_empty(s);
     return hipSuccess;
   }
-  if (p.qkv_bf16) {
-    if (p.dk == 128) launch_pass<bf16, 128>(p, plan, s, ev);
-    else launch_pass<bf16, 64>(p, plan, s, ev);
-  } else {
-    if (p.dk == 128) launch_pass<float, 128>(p, plan, s, ev);
-    else launch_pass<float, 64>(p, plan, s, ev);
-  }
-  return hipGetLastError();
+  if (p.qkv_bf16) return p.dk == 128 ? launch_pass<bf16, 128>(p, plan, s, ev) : launch_pass<bf16, 64>(p, plan, s, ev);
+  return p.dk == 128 ? launch_pass<float, 128>(p, plan, s, ev) : launch_pass<float, 64>(p, plan, s, ev);
 }
 
 }  // namespace gdn

@@ -124,7 +124,7 @@ hipError_t launch_plan_tables(const int32_t* cu, int N, int seg_chunks, int32_t*
 hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s) {
   if (p.total_chunks == 0) return hipSuccess;
   const int64_t blocks = p.total_chunks * ((p.H + 3) / 4);
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (blocks > kMaxDispatchItems / 256) return hipErrorInvalidConfiguration;
   chunk_gate_sums_kernel<<<(unsigned)blocks, 256, 0, s>>>(p, csum);
   return hipGetLastError();
 }
@@ -135,6 +135,7 @@ hipError_t launch_gate_scan(const Problem& p, const float* csum, int64_t max_chu
     ev.record_empty(s);
     return hipSuccess;
   }
+  if ((int64_t)p.N * p.H > kMaxDispatchItems / 1024) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)(p.N * p.H));
   if (max_chunks > 512)
     hipExtLaunchKernelGGL(gate_window_max_kernel<1024>, grid, dim3(1024), 0, s, ev.start, ev.stop, 0, csum,

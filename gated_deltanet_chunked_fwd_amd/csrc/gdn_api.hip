@@ -374,6 +374,29 @@ int check_inputs(const void* k, const float* g, const void* beta, const int32_t*
 }
 
 
+// Every launch of the plan fits the dispatch limits: an AQL dispatch counts work-items
+// per grid dimension in 32 bits, so a grid beyond 2^32 - 1 work-items would wrap and
+// silently drop work.  Each bound below is the launch's own grid (pass 1 and pass 3
+// run 4 threads per value column in either block shape).
+bool grids_fit(const gdn_shape* s, const Plan& P) {
+  auto fits = [](int64_t groups, int64_t items_each) {
+    return groups >= 0 && (items_each == 0 || groups <= gdn::kMaxDispatchItems / items_each);
+  };
+  const int64_t H = s->H, nh = s->N * s->H;
+  if (!fits(P.total_chunks * ((H + 3) / 4), 256)) return false;                  // K1
+  const int64_t unit_groups = (P.total_segs * H + 7) / 8;
+  if (!fits(unit_groups * 8, s->dv * 4)) return false;                           // pass 3
+  if (!P.split) return true;
+  if (!fits(nh, P.max_chunks > 512 ? 1024 : 256)) return false;                   // gate scan
+  if (!fits(unit_groups * 8, (s->dv + s->dk) * 4)) return false;                  // pass 1
+  const int64_t merge_threads = s->dk / 16 * 64;
+  const int64_t steps = (P.max_chunks + P.seg_chunks - 1) / P.seg_chunks - 1;
+  int64_t G = 1;
+  while (G * G < steps) ++G;
+  const int64_t maxg = steps > gdn::kMergeTreeMinSteps ? (steps + G - 1) / G : 1;
+  return fits((nh * maxg + 7) / 8 * 8, (s->dk + s->dv) / 16 * merge_threads);   // merge
+}
+
 // Runs stages [first, last] of the forward pass (GDN_STAGE_*, launch order) on one
 // workspace; gdn_chunk_fwd is all of them.  Every call validates all arguments and
 // plans the same way, so a caller that runs the stages one by one, in order, on one
@@ -396,6 +419,7 @@ int run_stages(int first, int last, const void* q, const void* k, const void* v,
     return GDN_ERR_ARG;
   if (!std::isfinite(scale)) return GDN_ERR_ARG;
   const Plan P = make_plan(shape, opts);
+  if (!grids_fit(shape, P)) return GDN_ERR_UNSUPPORTED;
   const Layout L = layout(shape, P);
   if (workspace_bytes < L.total || (L.total > 0 && !workspace) || !aligned(workspace, kAlign))
     return GDN_ERR_WORKSPACE;
@@ -563,6 +587,7 @@ int gdn_chunk_inverse(const void* k, const float* g, const void* beta, const int
   if (rc != GDN_OK) return rc;
   const int64_t nch = gdn_total_chunks(shape);
   if (nch > 0 && (!t_out || !aligned(t_out, 16))) return GDN_ERR_ARG;
+  if (nch * ((shape->H + 3) / 4) > gdn::kMaxDispatchItems / 256) return GDN_ERR_UNSUPPORTED;
   gdn::Problem p = make_problem(nullptr, k, nullptr, g, beta, nullptr, cu_seqlens, 1.f, nullptr,
                                 nullptr, shape, nch);
   if (cu_seqlens) {
@@ -602,6 +627,11 @@ int gdn_gate_scan(const float* g, const int32_t* cu_seqlens, const gdn_shape* sh
   gdn_gate_scan_workspace_bytes(shape, &need);
   if (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)) return GDN_ERR_WORKSPACE;
   const Plan P = make_plan(shape, opts);
+  // chunk gate sums (256 threads per 4 heads of a chunk), the scan (256 or 1024 per
+  // sequence-head) and the finalisation (one thread per sequence-head) must fit a dispatch
+  if (P.total_chunks * ((shape->H + 3) / 4) > gdn::kMaxDispatchItems / 256 ||
+      shape->N * shape->H > gdn::kMaxDispatchItems / 1024)
+    return GDN_ERR_UNSUPPORTED;
   char* ws = static_cast<char*>(workspace);
   const size_t off_best = align_up((size_t)(shape->N + 1) * sizeof(int32_t));
   const size_t off_csum = off_best + align_up((size_t)shape->N * shape->H * kWindowMaxCap *

@@ -47,6 +47,8 @@ struct CpBuffers {
 
 // Merge chains of more steps than this run as a two-level tree (cp_merge.hip).
 constexpr int kMergeTreeMinSteps = 16;
+// An AQL dispatch counts the work-items of a grid dimension in 32 bits.
+constexpr int64_t kMaxDispatchItems = 0xFFFFFFFFLL;
 
 // Work description for one launch of the fused forward kernel.  A work unit is
 // (sequence, head, segment); the kernel grid covers units x column blocks.

@@ -47,7 +47,8 @@ extern "C" {
 enum {
   GDN_OK = 0,
   GDN_ERR_ARG = -1,          /* null pointer, bad dimension, misalignment, bad cu_seqlens */
-  GDN_ERR_UNSUPPORTED = -2,  /* dk/dv not in {64,128}, dtype combination not built */
+  GDN_ERR_UNSUPPORTED = -2,  /* dk/dv not in {64,128}, dtype combination not built, or a
+                                problem whose launch grids would exceed 2^32 - 1 work-items */
   GDN_ERR_WORKSPACE = -3,    /* workspace missing or smaller than gdn_chunk_fwd_workspace_bytes */
   GDN_ERR_HIP = -4           /* a kernel launch failed (hipGetLastError) */
 };

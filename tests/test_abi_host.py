@@ -173,3 +173,20 @@ def test_workspace_regions():
             fake, ctypes.c_size_t(1 << 40), None]
     for bad in (-1, B.GDN_NUM_STAGES):
         assert B.lib().gdn_chunk_fwd_stage(bad, *args) == B.GDN_ERR_ARG
+
+
+def test_oversized_launch_grids_rejected_before_any_launch():
+    """2^20 one-token packed sequences x 128 heads: the unsplit forward would need
+    2^27 units x 512 threads, beyond a dispatch's 2^32 - 1 work-items; the call must
+    fail with GDN_ERR_UNSUPPORTED before anything is enqueued (fake pointers: any
+    launch would fault, validation must stop it first)."""
+    N, H = 1 << 20, 128
+    cu = (ctypes.c_int32 * (N + 1))(*range(N + 1))
+    s = shape(T=N, N=N, H=H, cu_seqlens_host=ctypes.cast(cu, ctypes.POINTER(ctypes.c_int32)))
+    fake = ctypes.c_void_p(4096)
+    opts = B.make_opts(no_split=1)
+    args = [fake] * 5 + [None, fake, ctypes.c_float(0.1), fake, None, ctypes.byref(s), ctypes.byref(opts),
+            fake, ctypes.c_size_t(1 << 62), None]
+    assert B.lib().gdn_chunk_fwd(*args) == B.GDN_ERR_UNSUPPORTED
+    small = shape(T=N, N=N, H=2, cu_seqlens_host=ctypes.cast(cu, ctypes.POINTER(ctypes.c_int32)))
+    assert ws_bytes(small)[0] == B.GDN_OK   # the same sequences with few heads are fine
