@@ -1,0 +1,79 @@
+"""Seeded random sweep of the forward's configuration space against the fp64 oracle.
+
+Each case draws, from its own seed: dense or packed input (packed lengths include
+empty and sub-chunk sequences), dk and dv in {64, 128}, bf16 or fp32 storage (bf16 or
+fp32 beta), a gate distribution per head (sigmoid gates, strong uniform gates or none
+at all), an initial state or none, whether the final state is requested, and the
+options (planner or a forced segment length, forced correction, the window cap,
+64-column value blocks, no split).  Every (sequence, head) pair is compared with the
+oracle: relative L2 per pair within 1e-2 (bf16 storage) or 1e-5 (fp32).  The inputs
+come from the seeded generators in synth; nothing here is shared with the HIP path
+but those inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_chunked_fwd_amd import binding, synth
+from tests.gpu_util import TOL, assert_parity, compare_pairs, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+CASES = 24
+
+
+def draw_case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    rng.random()
+    dtype = "f32" if seed % 3 == 0 else "bf16"   # a third of the cases in fp32
+    beta_dtype = dtype if rng.random() < 0.8 else ("f32" if dtype == "bf16" else "bf16")
+    dk, dv = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
+    H = int(rng.integers(1, 5))
+    packed = rng.random() < 0.5
+    if packed:
+        n = int(rng.integers(1, 7))
+        lens = [int(x) for x in rng.choice([0, 1, 17, 63, 64, 65, 200, 640, 1100, 1600], size=n)]
+        if sum(lens) == 0:
+            lens[0] = 129
+        B, T = 1, sum(lens)
+    else:
+        B, T = int(rng.integers(1, 4)), int(rng.choice([1, 65, 300, 777, 1300, 2100]))
+        lens = None
+    gate = str(rng.choice(["sigmoid", "uniform", "zero"], p=[0.5, 0.3, 0.2]))
+    zero_heads = tuple(int(h) for h in range(H) if rng.random() < 0.3)
+    h0_std = float(rng.choice([0.0, 0.05])) or None
+    spec = synth.Spec("random%d" % seed, B=B, T=T, H=H, dk=dk, dv=dv, dtype=dtype, beta_dtype=beta_dtype,
+                      gate=gate, zero_gate_heads=zero_heads, h0_std=None if packed else h0_std,
+                      seed=2000 + seed)
+    inp = synth.generate(spec)
+    if packed:
+        inp["cu_seqlens"] = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+        inp["N"] = len(lens)
+        if h0_std:
+            g = torch.Generator().manual_seed(3000 + seed)
+            inp["h0"] = (torch.randn(len(lens), H, dk, dv, generator=g) * h0_std).float()
+    opts = dict(
+        no_split=int(rng.random() < 0.1),
+        force_segment_chunks=int(rng.choice([0, 1, 1, 2, 2, 3, 5])),
+        force_correction=int(rng.random() < 0.3),
+        window_max_chunks=int(rng.choice([0, 1, 4, 16])),
+        value_block=int(rng.choice([0, 0, 64])),
+    )
+    if seed % 4 == 3:   # one-chunk segments: long merge chains (the two-level tree)
+        opts.update(no_split=0, force_segment_chunks=1)
+    final = bool(rng.random() < 0.8)
+    return inp, opts, final
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_random_configuration(seed):
+    inp, kw, final = draw_case(seed)
+    sp = inp["spec"]
+    label = "case %d: B=%d T=%d H=%d dk=%d dv=%d %s beta %s gate %s zero %s packed %s h0 %s final %s opts %s" % (
+        seed, sp.B, sp.T, sp.H, sp.dk, sp.dv, sp.dtype, sp.beta_dtype, sp.gate, sp.zero_gate_heads,
+        None if inp["cu_seqlens"] is None else inp["cu_seqlens"].tolist(), inp["h0"] is not None, final, kw)
+    print(label, flush=True)
+    o, hT = run_gpu(inp, opts=binding.make_opts(**kw), output_final_state=final)
+    assert (hT is None) == (not final)
+    errs = compare_pairs(inp, o, hT)
+    assert_parity(errs, TOL[sp.dtype], label)
