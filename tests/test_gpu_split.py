@@ -9,7 +9,7 @@ import torch
 
 from gated_deltanet_chunked_fwd_amd import binding, synth
 from oracle import gate
-from tests.gpu_util import TOL, assert_parity, compare_pairs, run_gpu, to_dev
+from tests.gpu_util import TOL, assert_parity, compare_pairs, rel_l2, run_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -228,3 +228,49 @@ def test_segment_regions_carry_everything_the_next_stage_needs(case):
         wb[off:off + n].copy_(wa[off:off + n])
         run(after, wb, o, hT)
         assert torch.equal(o, o_ref) and torch.equal(hT, h_ref), (case, reg)
+
+
+@pytest.mark.parametrize("case", ["dense_bf16", "dense_tree_f32", "packed_bf16"])
+def test_segment_starts_stage_parity(case):
+    """Stage parity of pass 1 and the merge: with every head on the correction path,
+    the segment starts the merge writes (workspace region GDN_REGION_SEGMENT_STARTS,
+    slot = global segment * H + head, K-major) equal the chunked oracle's
+    h_start(j+1) = M_j h_start(j) + S*_j, segment by segment (relative L2 within the
+    storage dtype's tolerance)."""
+    from oracle import chunked
+    L = 2
+    if case == "dense_bf16":
+        inp = synth.generate(spec(B=2, T=64 * 9 + 5, H=2, seed=91, h0_std=0.05))
+    elif case == "dense_tree_f32":
+        inp = synth.generate(spec(B=1, T=64 * 40 + 9, H=2, dk=64, dv=64, dtype="f32", seed=92))
+    else:
+        inp = _packed([64 * 7 + 3, 0, 64 * 5, 30], H=2, seed=93)
+    sp = inp["spec"]
+    opts = binding.make_opts(force_segment_chunks=L, force_correction=1)
+    d, new_ws, outs, run, region = _stage_setup(inp, opts)
+    ws = new_ws()
+    o, hT = outs()
+    run([binding.GDN_STAGE_INVERSE, binding.GDN_STAGE_GATE_SCAN, binding.GDN_STAGE_CP_PASS1,
+         binding.GDN_STAGE_CP_MERGE], ws, o, hT)
+    off, n = region(binding.GDN_REGION_SEGMENT_STARTS)
+    H, dk, dv = sp.H, sp.dk, sp.dv
+    starts = ws[off:off + n].view(torch.float32).reshape(-1, H, dk, dv).cpu().double().numpy()
+    cu = None if inp["cu_seqlens"] is None else inp["cu_seqlens"].numpy()
+    _, _, info = chunked.cp_forward(*(synth.as_f64(inp[x]) for x in ("q", "k", "v", "g", "beta")),
+                                    h0=synth.as_f64(inp["h0"]), cu_seqlens=cu, scale=inp["scale"],
+                                    seg_chunks=L)
+    lens = ([sp.T] * sp.B if cu is None else list(np.diff(cu)))
+    base, worst, checked = 0, 0.0, 0
+    for nseq, ln in enumerate(lens):
+        nch = (int(ln) + 63) // 64
+        segs = max(1, (nch + L - 1) // L)
+        for h in range(H):
+            ref = info[(nseq, h)]["h_start"]
+            for j in range(1, len(ref)):   # segment 0 starts from h0, which the merge does not form
+                e = rel_l2(starts[base + j, h], ref[j])
+                worst = max(worst, e)
+                checked += 1
+        base += segs
+    assert base == starts.shape[0]
+    print("%s: %d segment starts, worst rel L2 %.3e" % (case, checked, worst), flush=True)
+    assert checked > 0 and worst <= TOL[sp.dtype]
