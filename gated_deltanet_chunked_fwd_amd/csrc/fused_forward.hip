@@ -101,7 +101,11 @@ struct ChunkRegs {
   // applied); rows past the chunk end read the chunk's first row instead (masked
   // to zero in store()).  The loads go out in four parts spread over the step
   // (PART 0: g, beta, K; 1: Q; 2: V; 3: T): issuing a whole chunk at once fills the
-  // CU's vector-memory queue and stalls the waves that issue last.
+  // CU's vector-memory queue and stalls the waves that issue last.  Q and V carry the
+  // nontemporal hint (streamed, not kept in the caches): no other workgroup reads a
+  // chunk's Q, only the next segment's lookback reads its V, and the cache space
+  // they leave stays with K and T, which K1 has just written or read (measured 0-4%
+  // faster per call, never slower; the hint on K or T, or on the O stores, was not).
   template <int PART>
   __device__ __forceinline__ void load(const E* qb, const E* kb, const E* vb, const E* ts,
                                        const float* gb, const void* betab, bool beta_bf16,
@@ -120,7 +124,7 @@ struct ChunkRegs {
         const int r = (tid + NTH * j) / VPRK;
         const uint32_t o = (full || r < len_) ? of.k[j] : (uint32_t)((tid + NTH * j) % VPRK) * 16u;
         if constexpr (PART == 0) k[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(kb) + o);
-        else q[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(qb) + o);
+        else q[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(qb) + o));
       }
     }
     // V is loaded even when it is not used (vzero: masked at store time), so every
@@ -131,7 +135,7 @@ struct ChunkRegs {
       for (int j = 0; j < NV; ++j) {
         const int r = (tid + NTH * j) / VPRV;
         const uint32_t o = (full || r < len_) ? of.v[j] : (uint32_t)((tid + NTH * j) % VPRV) * 16u;
-        v[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(vb) + o);
+        v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(vb) + o));
       }
     }
     if constexpr (PART == 3) {
