@@ -272,6 +272,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
   if (plan.seg_off) {
     n = seq_of_chunk(sg, plan.seg_off, p.N, 0);
     seg = (int)(sg - plan.seg_off[n]);
+  } else if (p.cu) {   // packed without segment tables: one segment per sequence
+    n = (int)sg;
+    seg = 0;
   } else {
     const int64_t nch_all = (p.T + kChunk - 1) / kChunk;
     const int64_t segs = max((int64_t)1, (nch_all + plan.seg_chunks - 1) / plan.seg_chunks);

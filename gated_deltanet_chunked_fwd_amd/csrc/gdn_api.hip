@@ -234,7 +234,10 @@ Plan plan_uncached(const gdn_shape* s, const gdn_opts* o) {
     }
   }
   P.split = L < P.max_chunks;
-  P.seg_chunks = (int)std::min<int64_t>(L, INT_MAX / 2);
+  // An unsplit plan carries the one-segment value even when a segment length was
+  // forced: the kernels' decode without segment tables derives segments per sequence
+  // from it (packed input has none; its T spans all sequences).
+  P.seg_chunks = P.split ? (int)L : INT_MAX / 2;
   if (P.split) {
     for (int64_t n = 0; n < s->N; ++n)  // an empty sequence still owns one unit (its final state)
       P.total_segs += std::max<int64_t>(1, (seq_chunks(s, n) + L - 1) / L);

@@ -131,6 +131,23 @@ def test_plan_cache_follows_packed_lengths_and_options():
     assert [plan_L(s) for s in reversed(shapes)] == list(reversed(first))
 
 
+
+@pytest.mark.parametrize("L", [2, 3, 5, 100])
+def test_forced_segment_length_without_a_split_plans_one_segment(L):
+    """Packed lengths whose longest sequence has 2 chunks while the packed T spans 5:
+    a forced segment length >= 2 splits nothing, and the plan must then carry the
+    same one-segment value as no_split (the kernels' decode without segment tables
+    divides by it; a value of 2 there made them read 3 segments of one sequence)."""
+    cu = (ctypes.c_int32 * 7)(0, 65, 128, 192, 193, 194, 258)
+    s = shape(T=258, N=6, H=1, cu_seqlens_host=ctypes.cast(cu, ctypes.POINTER(ctypes.c_int32)))
+    unsplit = plan_L(s, B.make_opts(no_split=1))
+    assert unsplit >= 5
+    assert plan_L(s, B.make_opts(force_segment_chunks=L)) == unsplit
+    assert plan_L(s, B.make_opts(force_segment_chunks=L, force_correction=1)) == unsplit
+    assert plan_L(s, B.make_opts(force_segment_chunks=1)) == 1
+    dense = shape(T=64 * 5, H=1)
+    assert plan_L(dense, B.make_opts(force_segment_chunks=5)) == plan_L(dense, B.make_opts(no_split=1))
+
 def region(s, r, opts=None):
     off, n = ctypes.c_size_t(0), ctypes.c_size_t(0)
     rc = B.lib().gdn_chunk_fwd_workspace_region(ctypes.byref(s), None if opts is None else ctypes.byref(opts),

@@ -57,6 +57,18 @@ def test_split_parity_packed(corr):
     assert_parity(compare_pairs(inp, o, hT), TOL["bf16"], "packed corr=%d" % corr)
 
 
+
+@pytest.mark.parametrize("seg", [2, 3, 8])
+@pytest.mark.parametrize("corr", [0, 1])
+def test_packed_forced_segment_length_that_splits_nothing(seg, corr):
+    """Packed sequences of at most 2 chunks over a packed T of 5 chunks, with a forced
+    segment length >= 2: no sequence splits, and every sequence is one segment that
+    starts from its own initial state (regression: the plan once kept the forced
+    length, and the output kernel then read 3 segments of one sequence)."""
+    inp = _packed([65, 63, 64, 1, 1, 64], H=2, seed=397)
+    o, hT = run_gpu(inp, opts=binding.make_opts(force_segment_chunks=seg, force_correction=corr))
+    assert_parity(compare_pairs(inp, o, hT), TOL["bf16"], "packed unsplit seg=%d corr=%d" % (seg, corr))
+
 @pytest.mark.parametrize("seg", [1, 2])
 def test_split_tree_merge(seg):
     """Merge chains longer than 16 steps run as a two-level tree (group maps
