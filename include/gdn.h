@@ -225,8 +225,10 @@ int gdn_gate_scan(const float* g, const int32_t* cu_seqlens, const gdn_shape* sh
                   size_t workspace_bytes, hipStream_t stream);
 int gdn_gate_scan_workspace_bytes(const gdn_shape* shape, size_t* bytes);
 
-/* Segment length (chunks) the planner picks for gdn_chunk_fwd, or a negative status;
- * a value >= the longest sequence's chunk count means no sequence is split. */
+/* Segment length (chunks) the planner picks for gdn_chunk_fwd, or a negative status.
+ * When no sequence is split (no_split, a forced length at or above the longest
+ * sequence's chunk count, or the planner's own choice) the value is 1073741823
+ * (INT_MAX / 2), so every sequence is one segment. */
 int64_t gdn_plan_segment_chunks(const gdn_shape* shape, const gdn_opts* opts);
 
 /* Total number of chunks (sum over sequences of ceil(len/64)), or a negative status. */

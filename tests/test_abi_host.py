@@ -148,6 +148,35 @@ def test_forced_segment_length_without_a_split_plans_one_segment(L):
     dense = shape(T=64 * 5, H=1)
     assert plan_L(dense, B.make_opts(force_segment_chunks=5)) == plan_L(dense, B.make_opts(no_split=1))
 
+
+@pytest.mark.parametrize("seed", range(6))
+def test_unsplit_plans_report_the_one_segment_value(seed):
+    """Random packed and dense shapes with random forced lengths: a plan that splits
+    nothing (value at or above the longest sequence's chunk count) reports exactly
+    the one-segment value, and a forced length below it is kept as given."""
+    import numpy as np
+    rng = np.random.default_rng(500 + seed)
+    one = 1073741823
+    for _ in range(60):
+        if rng.random() < 0.6:
+            lens = [int(x) for x in rng.choice([0, 1, 40, 64, 65, 130, 700, 2000], size=int(rng.integers(1, 9)))]
+            if sum(lens) == 0:
+                lens[0] = 65
+            cu = (ctypes.c_int32 * (len(lens) + 1))(0, *np.cumsum(lens).tolist())
+            s = shape(T=sum(lens), N=len(lens), H=int(rng.integers(1, 5)),
+                      cu_seqlens_host=ctypes.cast(cu, ctypes.POINTER(ctypes.c_int32)))
+            longest = max((n + 63) // 64 for n in lens)
+        else:
+            T = int(rng.integers(1, 64 * 40))
+            Bn = int(rng.integers(1, 4))
+            s = shape(T=T, B=Bn, N=Bn, H=int(rng.integers(1, 5)))
+            longest = (T + 63) // 64
+        L = int(rng.integers(1, 50))
+        got = plan_L(s, B.make_opts(force_segment_chunks=L, force_correction=int(rng.random() < 0.5)))
+        assert got == (L if L < longest else one), (L, longest, got)
+        assert plan_L(s, B.make_opts(no_split=1)) == one
+        assert plan_L(s) == one or 1 <= plan_L(s) < longest
+
 def region(s, r, opts=None):
     off, n = ctypes.c_size_t(0), ctypes.c_size_t(0)
     rc = B.lib().gdn_chunk_fwd_workspace_region(ctypes.byref(s), None if opts is None else ctypes.byref(opts),
