@@ -9,6 +9,10 @@ options (planner or a forced segment length, forced correction, the window cap,
 oracle: relative L2 per pair within 1e-2 (bf16 storage) or 1e-5 (fp32).  The inputs
 come from the seeded generators in synth; nothing here is shared with the HIP path
 but those inputs.
+
+A second draw (draw_large_case) takes longer dense and packed inputs with the
+planner's own split choices (no forced segment length), so the planner's decisions
+are checked at realistic sizes.
 """
 import numpy as np
 import pytest
@@ -77,3 +81,43 @@ def test_random_configuration(seed):
     assert (hT is None) == (not final)
     errs = compare_pairs(inp, o, hT)
     assert_parity(errs, TOL[sp.dtype], label)
+
+
+LARGE_CASES = 6
+
+
+def draw_large_case(seed):
+    rng = np.random.default_rng(90000 + seed)
+    H = int(rng.integers(1, 9))
+    dk, dv = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
+    packed = rng.random() < 0.5
+    if packed:
+        lens = [int(x) for x in rng.integers(0, 6000, size=int(rng.integers(1, 13)))]
+        if sum(lens) == 0:
+            lens[0] = 300
+        B, T = 1, sum(lens)
+    else:
+        B, T = int(rng.integers(1, 3)), int(rng.integers(1000, 20000))
+    gate = str(rng.choice(["sigmoid", "uniform", "zero"], p=[0.5, 0.3, 0.2]))
+    zero_heads = tuple(int(h) for h in range(H) if rng.random() < 0.3)
+    dtype = "bf16" if rng.random() < 0.8 else "f32"
+    spec = synth.Spec("large%d" % seed, B=B, T=T, H=H, dk=dk, dv=dv, dtype=dtype, gate=gate,
+                      zero_gate_heads=zero_heads, h0_std=None if packed else 0.05, seed=95000 + seed)
+    inp = synth.generate(spec)
+    if packed:
+        inp["cu_seqlens"] = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+        inp["N"] = len(lens)
+    opts = dict(force_correction=int(rng.random() < 0.2), window_max_chunks=int(rng.choice([0, 0, 4, 16])))
+    return inp, opts
+
+
+@pytest.mark.parametrize("seed", range(LARGE_CASES))
+def test_random_large_configuration(seed):
+    inp, kw = draw_large_case(seed)
+    sp = inp["spec"]
+    label = "large case %d: B=%d T=%d H=%d dk=%d dv=%d %s gate %s zero %s packed %s opts %s" % (
+        seed, sp.B, sp.T, sp.H, sp.dk, sp.dv, sp.dtype, sp.gate, sp.zero_gate_heads,
+        None if inp["cu_seqlens"] is None else inp["cu_seqlens"].tolist(), kw)
+    print(label, flush=True)
+    o, hT = run_gpu(inp, opts=binding.make_opts(**kw), output_final_state=True)
+    assert_parity(compare_pairs(inp, o, hT), TOL[sp.dtype], label)
