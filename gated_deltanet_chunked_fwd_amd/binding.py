@@ -64,6 +64,99 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _need(cond, what):
+    if not cond:
+        raise ValueError(what)
+
+
+def _check_tensor(t, name, dtypes, shape, device, require_cuda):
+    _need(isinstance(t, torch.Tensor), "%s must be a torch.Tensor" % name)
+    if require_cuda:
+        _need(t.is_cuda, "%s must be a device tensor" % name)
+    if device is not None:
+        _need(t.device == device, "%s is on %s, expected %s" % (name, t.device, device))
+    _need(t.dtype in dtypes, "%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    _need(tuple(t.shape) == tuple(shape), "%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    _need(t.is_contiguous(), "%s must be contiguous" % name)
+
+
+def check_forward_args(q, k, v, g, beta, initial_state=None, cu_seqlens=None, cu_seqlens_host=None,
+                       out=None, final_state_out=None, workspace=None, require_cuda=True):
+    """Checks every tensor argument of chunk_fwd against the layouts of include/gdn.h
+    (the library reinterprets raw pointers, so a wrong dtype or shape would be read
+    past its end) and raises ValueError on the first mismatch.  Returns cu_seqlens as
+    the int32 device tensor the library reads (an int64 cu_seqlens, FLA's convention,
+    is converted)."""
+    fp = (torch.bfloat16, torch.float32)
+    _need(isinstance(q, torch.Tensor) and q.dim() == 4, "q must be a 4-D tensor [B, T, H, dk]")
+    B, T, H, dk = q.shape
+    dev = q.device
+    _check_tensor(q, "q", fp, (B, T, H, dk), None, require_cuda)
+    _check_tensor(k, "k", (q.dtype,), (B, T, H, dk), dev, require_cuda)
+    _need(isinstance(v, torch.Tensor) and v.dim() == 4, "v must be a 4-D tensor [B, T, H, dv]")
+    _check_tensor(v, "v", (q.dtype,), (B, T, H, v.shape[-1]), dev, require_cuda)
+    dv = v.shape[-1]
+    _check_tensor(g, "g", (torch.float32,), (B, T, H), dev, require_cuda)
+    _check_tensor(beta, "beta", fp, (B, T, H), dev, require_cuda)
+    N = B
+    if cu_seqlens is not None:
+        _need(B == 1, "packed sequences (cu_seqlens) need B == 1")
+        _need(isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.dim() == 1 and cu_seqlens.numel() >= 2,
+              "cu_seqlens must be a 1-D tensor of N + 1 offsets")
+        N = cu_seqlens.numel() - 1
+        _check_tensor(cu_seqlens, "cu_seqlens", (torch.int32, torch.int64), (N + 1,), dev, require_cuda)
+        if cu_seqlens_host is not None:
+            _need(isinstance(cu_seqlens_host, torch.Tensor) and not cu_seqlens_host.is_cuda and
+                  tuple(cu_seqlens_host.shape) == (N + 1,) and
+                  cu_seqlens_host.dtype in (torch.int32, torch.int64),
+                  "cu_seqlens_host must be a host int32/int64 tensor of N + 1 offsets")
+            _need(int(cu_seqlens_host[-1]) == T and int(cu_seqlens_host[0]) == 0,
+                  "cu_seqlens_host must start at 0 and end at T")
+        if cu_seqlens.dtype == torch.int64:
+            cu_seqlens = cu_seqlens.to(torch.int32)
+    else:
+        _need(cu_seqlens_host is None, "cu_seqlens_host given without cu_seqlens")
+    if initial_state is not None:
+        _check_tensor(initial_state, "initial_state", (torch.float32,), (N, H, dk, dv), dev, require_cuda)
+    if out is not None:
+        _check_tensor(out, "out", (q.dtype,), (B, T, H, dv), dev, require_cuda)
+    if final_state_out is not None:
+        _check_tensor(final_state_out, "final_state_out", (torch.float32,), (N, H, dk, dv), dev,
+                      require_cuda)
+    if workspace is not None:
+        _need(isinstance(workspace, torch.Tensor) and workspace.dtype == torch.uint8 and
+              workspace.dim() == 1 and workspace.is_contiguous() and workspace.device == dev,
+              "workspace must be a contiguous 1-D uint8 tensor on the inputs' device")
+    return cu_seqlens
+
+
+def check_gate_args(g, cu_seqlens=None, require_cuda=True):
+    """Checks the gate scan's arguments (g fp32 [B, T, H]); returns int32 cu_seqlens."""
+    _need(isinstance(g, torch.Tensor) and g.dim() == 3, "g must be a 3-D tensor [B, T, H]")
+    B, T, H = g.shape
+    _check_tensor(g, "g", (torch.float32,), (B, T, H), None, require_cuda)
+    if cu_seqlens is not None:
+        _need(B == 1, "packed sequences (cu_seqlens) need B == 1")
+        _need(isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.dim() == 1 and cu_seqlens.numel() >= 2,
+              "cu_seqlens must be a 1-D tensor of N + 1 offsets")
+        _check_tensor(cu_seqlens, "cu_seqlens", (torch.int32, torch.int64), (cu_seqlens.numel(),), g.device,
+                      require_cuda)
+        if cu_seqlens.dtype == torch.int64:
+            cu_seqlens = cu_seqlens.to(torch.int32)
+    return cu_seqlens
+
+
+def check_inverse_args(k, g, beta, cu_seqlens=None, require_cuda=True):
+    """Checks gdn_chunk_inverse's arguments (k [B, T, H, dk] bf16/fp32, g fp32 and beta
+    bf16/fp32 [B, T, H]); returns int32 cu_seqlens."""
+    _need(isinstance(k, torch.Tensor) and k.dim() == 4, "k must be a 4-D tensor [B, T, H, dk]")
+    B, T, H, dk = k.shape
+    _check_tensor(k, "k", (torch.bfloat16, torch.float32), (B, T, H, dk), None, require_cuda)
+    _check_tensor(g, "g", (torch.float32,), (B, T, H), k.device, require_cuda)
+    _check_tensor(beta, "beta", (torch.bfloat16, torch.float32), (B, T, H), k.device, require_cuda)
+    return check_gate_args(g, cu_seqlens, require_cuda)
+
+
 class _Shape:
     """Builds a GdnShape and keeps the host cu_seqlens buffer alive."""
 
@@ -104,9 +197,8 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=None,
     initial_state / final_state [N,H,dk,dv] fp32; cu_seqlens int32 [N+1] on the device
     (B == 1).  ``cu_seqlens_host`` avoids a device-to-host copy of cu_seqlens.
     """
-    for t in (q, k, v, g, beta):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("inputs must be contiguous device tensors")
+    cu_seqlens = check_forward_args(q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host,
+                                    out, final_state_out, workspace)
     sh = _Shape(q, v, beta, cu_seqlens, cu_seqlens_host)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -164,6 +256,7 @@ def workspace_region(q, v, beta, region, cu_seqlens=None, cu_seqlens_host=None, 
 
 def chunk_inverse(k, g, beta, cu_seqlens=None, cu_seqlens_host=None):
     """Step 1 alone: returns T [total_chunks, H, 64, 64] in k's dtype."""
+    cu_seqlens = check_inverse_args(k, g, beta, cu_seqlens)
     sh = _Shape(k, k, beta, cu_seqlens, cu_seqlens_host)
     nch = lib().gdn_total_chunks(sh.ref())
     if nch < 0:
@@ -186,6 +279,7 @@ def chunk_inverse(k, g, beta, cu_seqlens=None, cu_seqlens_host=None):
 
 def gate_scan(g, cu_seqlens=None, cu_seqlens_host=None, opts: Optional[GdnOpts] = None):
     """The gate scan alone: int32 [N, H] lookback windows (0 = none)."""
+    cu_seqlens = check_gate_args(g, cu_seqlens)
     B, T, H = g.shape
     fake_q = torch.empty((B, T, H, 64), dtype=torch.bfloat16, device="meta")
     sh = _Shape(fake_q, fake_q, g, cu_seqlens, cu_seqlens_host)

@@ -8,7 +8,10 @@ none of the method's arithmetic.
 
 Contents
   token      -- Oracle A: fp64 token-by-token recurrence (plain C via ctypes, plus a
-                numpy twin used to check the C build on tiny inputs).
+                numpy twin used to check the C build on tiny inputs), and the
+                magnitude scale*|S_t||q_t| of every output's inner product (the
+                scale an output's rounding error is judged against when that inner
+                product cancels).
   chunked    -- Oracle B: fp64 chunk-by-chunk WY form written from the pages' four
                 steps, its algebraic variants, the sequence-parallel correction
                 (wrong-start state S*, correction matrix M, merge) and the
@@ -20,7 +23,7 @@ Every function cites the passage of the pages it follows.  The pages are three
 web articles on FlashQLA; the primary one is the AICon talk transcript
 "Qwen系列模型线性注意力高性能优化实践" (tokendh.com).
 """
-from .token import token_recurrence, token_recurrence_numpy  # noqa: F401
+from .token import output_magnitude_numpy, token_recurrence, token_recurrence_numpy  # noqa: F401
 from .chunked import (  # noqa: F401
     chunk_inverse,
     chunked_forward,

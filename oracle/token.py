@@ -119,3 +119,35 @@ def token_recurrence_numpy(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=Non
                 o[t, h] = scale * S @ qf[t, h]
             hT[n, h] = S.T
     return o.reshape(v.shape), hT
+
+
+def output_magnitude_numpy(q, k, v, g, beta, h0=None, cu_seqlens=None, scale=None):
+    """Magnitude of every output's defining sum, m_t = scale * |S_t| |q_t| (absolute
+    values taken elementwise, S_t the post-update state of the same recurrence).
+
+    Each output o_t[j] = scale * sum_i S_t[j, i] q_t[i] is an inner product; a floating
+    point evaluation of it errs by at most a small multiple of the unit roundoff times
+    scale * sum_i |S_t[j, i] q_t[i]| = m_t[j], whatever |o_t[j]| is.  m_t is therefore the
+    scale against which an output's error is judged when the sum cancels (an
+    ill-conditioned inner product).  Same layouts as token_recurrence_numpy; slow, for
+    small inputs.  Returns m with the shape of v.
+    """
+    q, k, v, g, beta = map(_as_f64, (q, k, v, g, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    cu = _offsets(B, T, cu_seqlens)
+    N = len(cu) - 1
+    if scale is None:
+        scale = dk ** -0.5
+    qf, kf, vf = q.reshape(-1, H, dk), k.reshape(-1, H, dk), v.reshape(-1, H, dv)
+    gf, bf = g.reshape(-1, H), beta.reshape(-1, H)
+    m = np.zeros((B * T, H, dv))
+    for n in range(N):
+        for h in range(H):
+            S = np.zeros((dv, dk)) if h0 is None else _as_f64(h0)[n, h].T.copy()
+            for t in range(cu[n], cu[n + 1]):
+                kt, vt = kf[t, h], vf[t, h]
+                S = np.exp(gf[t, h]) * S
+                S = S + bf[t, h] * np.outer(vt - S @ kt, kt)
+                m[t, h] = abs(scale) * np.abs(S) @ np.abs(qf[t, h])
+    return m.reshape(v.shape)

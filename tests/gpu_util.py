@@ -80,3 +80,30 @@ def assert_parity(errs, tol, label=""):
         label, worst_o, worst_h, tol, [(n, h, "%.2e" % a, "%.2e" % b) for n, h, a, b in errs[:8]])
     print(msg, flush=True)
     assert worst_o <= tol and worst_h <= tol, msg
+
+
+def compare_pairs_magnitude(inp, o_gpu, pairs=None):
+    """Per-(sequence, head) output error judged against the magnitude of each output's
+    inner product: ||o - o_ref||_2 / ||m||_2 with m_t = scale |S_t| |q_t| from the
+    oracle (token.output_magnitude_numpy).  A floating point inner product errs by a
+    multiple of the unit roundoff times m, whatever |o| is, so this criterion stays
+    meaningful where o_t's inner product cancels.  Small inputs only (numpy oracle)."""
+    spec = inp["spec"]
+    bounds = seq_bounds(inp)
+    if pairs is None:
+        pairs = [(n, h) for n in range(len(bounds)) for h in range(spec.H)]
+    og = o_gpu.detach().to("cpu").to(torch.float64).numpy()
+    errs = []
+    for (n, h) in pairs:
+        b, s, e = bounds[n]
+        if e == s:
+            errs.append((n, h, 0.0, 0.0))
+            continue
+        o_ref, _ = oracle_pair(inp, n, h)
+        sl = lambda t: synth.as_f64(t[b:b + 1, s:e, h:h + 1])  # noqa: E731
+        h0 = None if inp.get("h0") is None else synth.as_f64(inp["h0"][n:n + 1, h:h + 1])
+        m = token.output_magnitude_numpy(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["g"]),
+                                         sl(inp["beta"]), h0, scale=inp["scale"])[0, :, 0]
+        errs.append((n, h, float(np.linalg.norm(og[b, s:e, h] - o_ref) / max(np.linalg.norm(m), 1e-300)),
+                     float(np.linalg.norm(o_ref) / max(np.linalg.norm(m), 1e-300))))
+    return errs

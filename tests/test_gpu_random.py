@@ -19,7 +19,7 @@ import pytest
 import torch
 
 from gated_deltanet_chunked_fwd_amd import binding, synth
-from tests.gpu_util import TOL, assert_parity, compare_pairs, run_gpu
+from tests.gpu_util import TOL, assert_parity, compare_pairs, compare_pairs_magnitude, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -121,3 +121,26 @@ def test_random_large_configuration(seed):
     print(label, flush=True)
     o, hT = run_gpu(inp, opts=binding.make_opts(**kw), output_final_state=True)
     assert_parity(compare_pairs(inp, o, hT), TOL[sp.dtype], label)
+
+
+def test_fp32_ill_conditioned_single_token_case():
+    """Seed 3609 of the sweep's draw: B = 3, T = 1, dk = 128, dv = 64, fp32.  Each
+    output is one fp32 inner product o = scale beta (k . q) v whose terms cancel (for
+    one pair sum |k_i q_i| / |k . q| is several hundred), so its relative L2 error says
+    nothing about the kernel: no fp32 evaluation order of such a sum meets 1e-5
+    relative.  The output is judged instead against the magnitude of its inner product
+    (tests.gpu_util.compare_pairs_magnitude: ||o - o_ref|| / ||scale |S||q| || <= 1e-5);
+    the final state, a plain product beta v k^T, keeps the 1e-5 relative bar."""
+    inp, kw, _ = draw_case(3609)
+    sp = inp["spec"]
+    assert (sp.dtype, sp.B, sp.T, sp.dk, sp.dv) == ("f32", 3, 1, 128, 64)
+    print("case 3609: B=%d T=%d H=%d dk=%d dv=%d %s opts %s" % (sp.B, sp.T, sp.H, sp.dk, sp.dv,
+                                                                  sp.dtype, kw), flush=True)
+    o, hT = run_gpu(inp, opts=binding.make_opts(**kw), output_final_state=True)
+    errs = compare_pairs_magnitude(inp, o)
+    # the case is the ill-conditioned one: some pair's |o| is far below its magnitude
+    assert min(e[3] for e in errs) < 0.05, errs
+    worst = max(e[2] for e in errs)
+    print("  worst magnitude-relative error %.3e over %d pairs" % (worst, len(errs)), flush=True)
+    assert worst <= TOL["f32"], errs
+    assert max(e[3] for e in compare_pairs(inp, o, hT)) <= TOL["f32"]

@@ -348,6 +348,110 @@ def test_window_decision_hand_cases():
     assert gate.window_chunks(np.full(64 * 40, -0.01), log_eps=le, w_max=16) == 0
 
 
+def test_window_decision_all_packed_hand_case():
+    """window_chunks_all on packed and dense [B, T, H] gates: per-(sequence, head)
+    answers worked by hand from constant per-head gates, so a sequence boundary off
+    by one token, a transposed head index or a partial last chunk summed as full
+    changes an answer.  log(2^-24) = -16.64; a full chunk of g = c sums to 64c."""
+    le = math.log(2.0 ** -24)
+    lens = [64 * 20, 64 * 3 + 10, 64, 0, 70]
+    H = 2
+    per_seq = [(-0.05, -0.3), (-0.3, 0.0), (-0.3, -0.05), (-0.3, -0.3), (-0.3, -0.2)]
+    g = np.concatenate([np.tile(np.array(c, dtype=float), (n, 1)) for n, c in zip(lens, per_seq)])
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    got = gate.window_chunks_all(g[None], cu_seqlens=cu, log_eps=le)
+    expect = np.array([
+        [6, 1],   # 20 chunks: -3.2 per chunk needs 6 (5 give -16.0); -19.2 needs 1
+        [2, 0],   # 3 full chunks and one of 10 tokens (-3.0): W = 1 fails on it, W = 2 holds
+        [1, 0],   # one chunk: -19.2 qualifies; -3.2 cannot (no run longer than 1 chunk)
+        [0, 0],   # empty sequence: no window
+        [2, 0],   # 64 + 6 tokens: last chunk -1.8 (head 0) / -1.2 (head 1); head 1's two
+    ])            # chunks sum to -14.0 > -16.64
+    assert got.tolist() == expect.tolist(), got
+    # dense [B, T, H]: two rows of 64 * 4 tokens with swapped per-head gates
+    gd = np.stack([np.tile([-0.3, -0.05], (256, 1)), np.tile([-0.05, -0.3], (256, 1))])
+    assert gate.window_chunks_all(gd, log_eps=le).tolist() == [[1, 0], [0, 1]]
+
+
+# ---------------------------------------------------------------- output magnitude
+
+
+def test_output_magnitude_closed_forms():
+    """m_t = scale |S_t| |q_t|: (a) one token from a zero state, S_1 = beta v k^T, so
+    m[j] = scale beta |v_j| sum_i |k_i q_i| (signed k and q); (b) with nonnegative
+    k, q, v on that token every term of the inner product is >= 0, so m == o;
+    (c) beta = 0, g = 0 from h0: m = scale |h0|^T |q| per token."""
+    rng = np.random.default_rng(21)
+    dk, dv = 8, 5
+    k = rng.standard_normal((1, 1, 1, dk))
+    k /= np.linalg.norm(k)
+    q = rng.standard_normal((1, 1, 1, dk))
+    v = rng.standard_normal((1, 1, 1, dv))
+    b = np.full((1, 1, 1), 0.7)
+    z = np.zeros((1, 1, 1))
+    m = token.output_magnitude_numpy(q, k, v, z, b, scale=0.5)
+    expect = 0.5 * 0.7 * np.abs(v[0, 0, 0]) * np.sum(np.abs(k * q))
+    assert np.allclose(m[0, 0, 0], expect, rtol=1e-14, atol=0)
+    ka, qa, va = np.abs(k), np.abs(q), np.abs(v)
+    o, _ = token.token_recurrence(qa, ka, va, z, b, None, scale=0.5)
+    m = token.output_magnitude_numpy(qa, ka, va, z, b, scale=0.5)
+    assert np.allclose(m, o, rtol=1e-14, atol=0)
+    T = 6
+    h0 = rng.standard_normal((1, 1, dk, dv))
+    qs = rng.standard_normal((1, T, 1, dk))
+    m = token.output_magnitude_numpy(qs, rng.standard_normal((1, T, 1, dk)),
+                                     rng.standard_normal((1, T, 1, dv)), np.zeros((1, T, 1)),
+                                     np.zeros((1, T, 1)), h0, scale=0.25)
+    assert np.allclose(m[0, :, 0], 0.25 * np.abs(qs[0, :, 0]) @ np.abs(h0[0, 0]), rtol=1e-14, atol=0)
+
+
+def test_output_magnitude_bounds_output():
+    """|o_t| <= m_t elementwise (triangle inequality) on a random gated packed case,
+    with equality nowhere forced; and m is invariant under q -> -q."""
+    rng = np.random.default_rng(22)
+    q, k, v, g, beta, h0 = rand_inputs(rng, 1, 90, 2, 8, 6, h0=True, N=3)
+    cu = [0, 30, 31, 90]
+    o, _ = token.token_recurrence(q, k, v, g, beta, h0, cu_seqlens=cu, scale=0.4)
+    m = token.output_magnitude_numpy(q, k, v, g, beta, h0, cu_seqlens=cu, scale=0.4)
+    assert np.all(np.abs(o) <= m * (1 + 1e-12) + 1e-300)
+    m2 = token.output_magnitude_numpy(-q, k, v, g, beta, h0, cu_seqlens=cu, scale=0.4)
+    assert np.array_equal(m, m2)
+
+
+# ---------------------------------------------------------------- FLA interface convention
+
+
+def test_layout_orientation_and_gate_convention_match_fla_reference():
+    """The pages say the API follows FLA's chunk_gated_delta_rule.  An FLA-convention
+    reference ships with transformers (Qwen3-Next's torch_recurrent_gated_delta_rule:
+    inputs [B, T, H, D], g = log alpha per token, beta per token, state [B, H, dk, dv],
+    scale dk^-1/2, fp32).  Oracle A on the same fp32-rounded inputs must agree with it
+    to fp32 rounding: this pins the token-major layout, the K-major state orientation
+    and the log-gate convention against an implementation written by others."""
+    os.environ.setdefault("HF_HUB_OFFLINE", "1")
+    torch = pytest.importorskip("torch")
+    mod = pytest.importorskip("transformers.models.qwen3_next.modeling_qwen3_next")
+    ref = mod.torch_recurrent_gated_delta_rule
+    rng = np.random.default_rng(23)
+    B, T, H, dk, dv = 2, 45, 3, 16, 8
+    q, k, v, g, beta, h0 = rand_inputs(rng, B, T, H, dk, dv, h0=True)
+    q, k, v, g, beta, h0 = (a.astype(np.float32).astype(np.float64) for a in (q, k, v, g, beta, h0))
+    tt = lambda a: torch.from_numpy(a).float()  # noqa: E731
+    o_ref, s_ref = ref(tt(q), tt(k), tt(v), tt(g), tt(beta), tt(h0), True)
+    o, hT = token.token_recurrence(q, k, v, g, beta, h0, scale=dk ** -0.5)
+    assert o_ref.shape == o.shape and s_ref.shape == hT.shape
+    assert rel(o, o_ref.double().numpy()) < 1e-5
+    assert rel(hT, s_ref.double().numpy()) < 1e-5
+    # and a transposed state would not agree (dk != dv makes the shapes differ; with
+    # dk == dv the transposed final state is far off)
+    q2, k2, v2, g2, b2, h2 = rand_inputs(rng, 1, 20, 1, 8, 8, h0=True)
+    q2, k2, v2, g2, b2, h2 = (a.astype(np.float32).astype(np.float64) for a in (q2, k2, v2, g2, b2, h2))
+    _, s2 = ref(tt(q2), tt(k2), tt(v2), tt(g2), tt(b2), tt(h2), True)
+    _, hT2 = token.token_recurrence(q2, k2, v2, g2, b2, h2, scale=8 ** -0.5)
+    assert rel(hT2, s2.double().numpy()) < 1e-5
+    assert rel(np.swapaxes(hT2, -1, -2), s2.double().numpy()) > 1e-2
+
+
 def _load_worked_example():
     path = os.path.join(os.path.dirname(__file__), "golden", "worked_example_dk2.txt")
     toks, final = [], None
