@@ -4,10 +4,13 @@ host-only tools (the sanitizer driver of the tests) share it."""
 import ctypes
 
 GDN_OK, GDN_ERR_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_ERR_HIP = 0, -1, -2, -3, -4
+GDN_ERR_SCRATCH = -5
+GDN_NOALLOC_SCRATCH_BYTES = 64 << 20   # include/gdn.h
 GDN_BF16, GDN_F32 = 1, 2
 
 # Symbols declared in include/gdn.h (checked by the CPU test of the boundary).
 EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_stage",
+           "gdn_chunk_fwd_noalloc",
            "gdn_chunk_fwd_workspace_region", "gdn_chunk_inverse",
            "gdn_gate_scan", "gdn_gate_scan_workspace_bytes", "gdn_plan_segment_chunks",
            "gdn_total_chunks", "gdn_status_str")
@@ -44,6 +47,9 @@ def declare(lib):
     lib.gdn_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, shp, opt,
                                   vp, sz, vp]
     lib.gdn_chunk_fwd.restype = ctypes.c_int
+    lib.gdn_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, shp,
+                                          opt, vp]
+    lib.gdn_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.gdn_chunk_fwd_stage.argtypes = [ctypes.c_int] + lib.gdn_chunk_fwd.argtypes
     lib.gdn_chunk_fwd_stage.restype = ctypes.c_int
     lib.gdn_chunk_fwd_workspace_region.argtypes = [shp, opt, ctypes.c_int, ctypes.POINTER(sz),

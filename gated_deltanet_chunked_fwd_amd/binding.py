@@ -15,8 +15,8 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgdn.so")
 
-from .abi import (EXPORTS, GDN_BF16, GDN_ERR_ARG, GDN_ERR_HIP, GDN_ERR_UNSUPPORTED,  # noqa: F401
-                  GDN_ERR_WORKSPACE, GDN_F32, GDN_NUM_REGIONS, GDN_NUM_STAGES, GDN_OK,
+from .abi import (EXPORTS, GDN_BF16, GDN_ERR_ARG, GDN_ERR_HIP, GDN_ERR_SCRATCH,  # noqa: F401
+                  GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_NOALLOC_SCRATCH_BYTES, GDN_F32, GDN_NUM_REGIONS, GDN_NUM_STAGES, GDN_OK,
                   GDN_REGION_CHUNK_INVERSE, GDN_REGION_SEGMENT_MAPS, GDN_REGION_SEGMENT_STARTS,
                   GDN_REGION_WINDOWS, GDN_STAGE_CP_MERGE, GDN_STAGE_CP_PASS1, GDN_STAGE_FORWARD,
                   GDN_STAGE_GATE_SCAN, GDN_STAGE_INVERSE, STAGE_NAMES, GdnOpts, GdnShape, declare,
@@ -228,6 +228,29 @@ def chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=None,
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_chunk_fwd" if stage is None else "gdn_chunk_fwd_stage")
     return o, fs
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, out, final_state_out=None, initial_state=None,
+                      cu_seqlens=None, scale=None, opts: Optional[GdnOpts] = None,
+                      cu_seqlens_host=None):
+    """chunk_fwd through gdn_chunk_fwd_noalloc: the library takes its scratch from its
+    built-in device array (GDN_NOALLOC_SCRATCH_BYTES per GPU) and allocates nothing;
+    the caller passes the outputs (``out``, and ``final_state_out`` or None).  Calls that
+    may overlap on one GPU share that array and must be serialised (one stream is
+    enough).  Returns ``(out, final_state_out)``."""
+    cu_seqlens = check_forward_args(q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host,
+                                    out, final_state_out)
+    _need(out is not None, "chunk_fwd_noalloc needs out=")
+    sh = _Shape(q, v, beta, cu_seqlens, cu_seqlens_host)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    rc = lib().gdn_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                     _ptr(cu_seqlens), ctypes.c_float(scale), _ptr(out),
+                                     _ptr(final_state_out), sh.ref(),
+                                     None if opts is None else ctypes.byref(opts), _stream(q.device))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_chunk_fwd_noalloc")
+    return out, final_state_out
 
 
 def chunk_fwd_stage(stage, q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=None,

@@ -44,6 +44,33 @@ constexpr int64_t kPlanModelMaxUnits = 1 << 16;   // larger plans use the closed
 constexpr float kWindowMargin = 1e-3f;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+}  // namespace
+
+// Scratch of the allocation-free entry point (gdn_chunk_fwd_noalloc): a file-scope
+// device array, one copy per GPU the library runs on, held until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host that name is a
+// stand-in, not a device address): it uses the address hipGetSymbolAddress returns,
+// taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of this device's `scratch` (nullptr if the query fails).  The first
+// call on a device makes the query; later calls return the cached address.
+void* scratch_address() {
+  static std::atomic<void*> cache[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+  cache[dev].store(q, std::memory_order_release);   // same value from any racing thread
+  return q;
+}
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Compute units of the current device, queried once per device.
@@ -534,6 +561,21 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g, c
                     final_state, shape, opts, workspace, workspace_bytes, stream);
 }
 
+int gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g,
+                          const void* beta, const float* initial_state,
+                          const int32_t* cu_seqlens, float scale, void* o, float* final_state,
+                          const gdn_shape* shape, const gdn_opts* opts, hipStream_t stream) {
+  int rc = validate_shape(shape);
+  if (rc == GDN_OK) rc = validate_opts(opts);
+  if (rc != GDN_OK) return rc;
+  const size_t need = layout(shape, make_plan(shape, opts)).total;
+  if (need > (size_t)GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_SCRATCH;
+  void* ws = scratch_address();
+  if (!ws) return GDN_ERR_HIP;
+  return run_stages(0, GDN_NUM_STAGES - 1, q, k, v, g, beta, initial_state, cu_seqlens, scale, o,
+                    final_state, shape, opts, ws, (size_t)GDN_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 int gdn_chunk_fwd_stage(int stage, const void* q, const void* k, const void* v, const float* g,
                         const void* beta, const float* initial_state, const int32_t* cu_seqlens,
                         float scale, void* o, float* final_state, const gdn_shape* shape,
@@ -664,6 +706,7 @@ const char* gdn_status_str(int status) {
     case GDN_ERR_UNSUPPORTED: return "unsupported configuration";
     case GDN_ERR_WORKSPACE: return "workspace missing or too small";
     case GDN_ERR_HIP: return "HIP launch failed";
+    case GDN_ERR_SCRATCH: return "problem needs more than the built-in scratch of gdn_chunk_fwd_noalloc";
     default: return "unknown status";
   }
 }

@@ -50,7 +50,9 @@ enum {
   GDN_ERR_UNSUPPORTED = -2,  /* dk/dv not in {64,128}, dtype combination not built, or a
                                 problem whose launch grids would exceed 2^32 - 1 work-items */
   GDN_ERR_WORKSPACE = -3,    /* workspace missing or smaller than gdn_chunk_fwd_workspace_bytes */
-  GDN_ERR_HIP = -4           /* a kernel launch failed (hipGetLastError) */
+  GDN_ERR_HIP = -4,          /* a kernel launch failed (hipGetLastError) */
+  GDN_ERR_SCRATCH = -5       /* gdn_chunk_fwd_noalloc: the problem's workspace exceeds
+                                GDN_NOALLOC_SCRATCH_BYTES */
 };
 
 /* ---- element types ----------------------------------------------------------- */
@@ -133,6 +135,33 @@ int gdn_chunk_fwd(const void* q, const void* k, const void* v, const float* g,
                   float scale, void* o, float* final_state, const gdn_shape* shape,
                   const gdn_opts* opts, void* workspace, size_t workspace_bytes,
                   hipStream_t stream);
+
+/*
+ * gdn_chunk_fwd without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The caller passes inputs and
+ * outputs exactly as for gdn_chunk_fwd; the scratch the kernels need (what
+ * gdn_chunk_fwd_workspace_bytes() reports) comes from a device array built into the
+ * library, GDN_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held from library load
+ * until the process ends.  Its address is looked up once per device (on the first
+ * call made with that device current).  The call makes no hipMalloc or hipFree.
+ *
+ * Limits and sharing:
+ *   * a problem whose workspace exceeds GDN_NOALLOC_SCRATCH_BYTES is rejected with
+ *     GDN_ERR_SCRATCH before anything is enqueued;
+ *   * every call on one GPU uses that GPU's one array: calls that may overlap on one
+ *     GPU (different streams, or different host threads without ordering) race and
+ *     must be serialised by the caller; calls on one stream are ordered and safe;
+ *   * the array keeps the last call's contents; nothing the kernels read from it
+ *     needs to start at zero (every region is written by an earlier kernel of the
+ *     same call before it is read).
+ * Other arguments, results and errors as gdn_chunk_fwd.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+int gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* g,
+                          const void* beta, const float* initial_state,
+                          const int32_t* cu_seqlens, float scale, void* o, float* final_state,
+                          const gdn_shape* shape, const gdn_opts* opts, hipStream_t stream);
 
 /*
  * One stage of gdn_chunk_fwd (the two-level API of the pages: the API section

@@ -236,3 +236,17 @@ def test_oversized_launch_grids_rejected_before_any_launch():
     assert B.lib().gdn_chunk_fwd(*args) == B.GDN_ERR_UNSUPPORTED
     small = shape(T=N, N=N, H=2, cu_seqlens_host=ctypes.cast(cu, ctypes.POINTER(ctypes.c_int32)))
     assert ws_bytes(small)[0] == B.GDN_OK   # the same sequences with few heads are fine
+
+
+def test_noalloc_rejects_problem_beyond_scratch_before_any_launch():
+    """gdn_chunk_fwd_noalloc refuses a problem whose workspace exceeds the built-in
+    scratch (GDN_ERR_SCRATCH) before it touches a pointer or the device."""
+    lib = B.lib()
+    s = shape(B=1, T=1 << 20, H=16, N=1)
+    need = ctypes.c_size_t(0)
+    assert lib.gdn_chunk_fwd_workspace_bytes(ctypes.byref(s), None, ctypes.byref(need)) == B.GDN_OK
+    assert need.value > B.GDN_NOALLOC_SCRATCH_BYTES
+    rc = lib.gdn_chunk_fwd_noalloc(None, None, None, None, None, None, None, ctypes.c_float(1.0), None, None,
+                                   ctypes.byref(s), None, None)
+    assert rc == B.GDN_ERR_SCRATCH
+    assert "scratch" in lib.gdn_status_str(rc).decode()
