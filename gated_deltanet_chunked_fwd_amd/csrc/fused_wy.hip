@@ -1,0 +1,643 @@
+// Steps 1-4 of the chunked WY form in one pass on gfx950 (bf16 storage): per
+// (sequence, head, segment, 32 value columns) one workgroup walks the chunks with
+// the state in registers, forms each chunk's inverse itself, and writes only O and
+// the final state.  Neither the inverse T nor W, U or S ever reaches HBM.
+//
+// FlashQLA talk transcript (tokendh.com): chunked-WY section (step 1, the chunk's
+// K K^T and its inverse; steps 2-4, the projections, the chunk-serial state
+// recurrence and the output); pain-points section (no W/U/S round trip through
+// HBM); algebraic-rewrites section (Gamma in log space; the forward merge "form V
+// minus S first, then apply gamma").  With h = S^T the state at chunk start, G the
+// chunk-local cumsum of g, gamma = exp(G), Gamma_rs = exp(G_r - G_s) (r >= s),
+// d = exp(G_last - G):
+//
+//   A  = strict_lower(diag(beta) K K^T * Gamma),  T = (I + A)^{-1}        (step 1)
+//   V' = V - diag(gamma) K h,   U = T diag(beta) V'                        (step 2)
+//   O  = scale (diag(gamma) Q h + ((Q K^T) * Gamma) U)                     (step 4)
+//   h <- gamma_last h + K^T (diag(d) U)                                    (step 3)
+//
+// Roles.  Only the last three lines depend on h; step 1 and P = scale (Q K^T) *
+// Gamma do not, so they are formed ahead of the recurrence by other waves:
+//   * NCH = BV / 16 "chain" waves own 16 value columns each (all dk rows of h in
+//     fp32 accumulator tiles, tile order, gdn_device.h) and run, per chunk, only
+//     X = K h, Y = Q h, V', U, O and the state update, from operands staged in LDS;
+//   * NP = 3 "prep" waves own every NP-th chunk.  A prep wave loads its chunk's K and
+//     Q rows from HBM straight into MFMA operand registers (plus V, g, beta), scans
+//     the gates, forms the gated Gram matrix, inverts it (16 x 16 diagonal blocks by
+//     forward substitution in fp32, the rest by two doubling levels of MFMA
+//     products) and forms P; then, in the step before the chain needs the chunk, it
+//     writes K, Q, V, T, P and the gate tables into one of two LDS buffer sets.
+// One workgroup barrier per chunk step: during step i the chain reads buffer set
+// i % 2 (K: ring slot i % 3) while the prep wave that owns chunk i + 1 writes set
+// (i + 1) % 2.  A prep
+// wave with chunk j issues its loads in step j - NP - 1, forms step 1 in step
+// j - NP, P in step j - NP + 1 and writes in step j - 1.  The first NP + 1 steps
+// only prepare (the chain waits at their barriers).
+#include <type_traits>
+
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+
+namespace {
+
+template <int DK, int BV>
+struct WyCfg {
+  static constexpr int NCH = BV / 16;          // chain waves (16 value columns each)
+  static constexpr int NP = 5;                 // prep waves
+  static constexpr int NW = NCH + NP;
+  static constexpr int NT = 64 * NW;
+  static constexpr int NKS = DK / 32;          // contraction steps over dk
+  static constexpr int NKT = DK / 16;          // dk tiles of the state
+  // LDS row strides (elements): rows feeding 16-byte fragment reads and 8-byte
+  // transpose reads are 8 (mod 32) dwords apart (conflict-free on gfx950's LDS)
+  static constexpr int KS = DK + 16;           // sK, sQ: tile-order rows
+  static constexpr int CS = kChunk + 16;       // sT, sP: tile-order rows
+  static constexpr int VS = BV + 16;           // sV: natural rows
+  static constexpr int VPR = BV / 8;           // 16-byte pieces per V row
+  static constexpr int NVP = kChunk * VPR / 64;  // V pieces per prep lane
+  // fp32 scratch of step 1: per prep wave G and beta; shared by the prep waves (only
+  // one of them inverts in any step) the diagonal A blocks (row-major, block stride
+  // ABS) and the diagonal T blocks (column-major, column stride TCS)
+  static constexpr int ABS = 260, TCS = 20, TBS = 16 * TCS;
+  static constexpr int INV = 4 * ABS + 4 * TBS;
+};
+
+// The ten 16 x 16 blocks (a, b), b <= a, of a lower-triangular 64 x 64 chunk matrix.
+__device__ __forceinline__ void lower_block(int i, int& a, int& b) {
+  a = i < 1 ? 0 : i < 3 ? 1 : i < 6 ? 2 : 3;
+  b = i - (a * (a + 1)) / 2;
+}
+
+// Orders this wave's LDS accesses across its lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// D(X^T), D(Y), acc -> acc + D(X Y) for 16 x 16 blocks held in accumulator layout:
+// slot e of lane (r, q) is X^T[4q+e][r] and Y[4q+e][r]; one bf16 16x16x16 MFMA on
+// the operands rounded to bf16 (T leaves as bf16, a rounding of the same size).
+__device__ __forceinline__ f32x4 mm16(const f32x4& xt, const f32x4& y, f32x4 acc) {
+  const i16x4 a = __builtin_bit_cast(i16x4, pack_bf16x4(xt));
+  const i16x4 b = __builtin_bit_cast(i16x4, pack_bf16x4(y));
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+}
+
+// One chunk held by a prep wave from its loads to its LDS writes.
+template <int DK, int BV>
+struct PrepChunk {
+  using Cfg = WyCfg<DK, BV>;
+  bf16x8 kf[4][Cfg::NKS];   // K rows 16a + r, columns 32s + 8q .. +7 (lane (r, q))
+  bf16x8 qf[4][Cfg::NKS];   // Q, same layout
+  u32x4 vp[Cfg::NVP];       // V pieces: piece lane + 64 j is row / VPR, 8 columns
+  float g, b;               // gate and beta of row = lane (zero past the chunk end)
+  f32x4 gd[4], go[6];       // Gram tiles: D(K_a K_a^T) and D(K_b K_a^T) for b < a (order of lower_block)
+  uint2 tb[10];             // T blocks, bf16, lane (r, q): row 16a + r, columns 16b + 4q .. +3
+  uint2 pb[10];             // P blocks, same layout (query rows, key columns)
+};
+
+}  // namespace
+
+template <int DK, int BV>
+__global__ __launch_bounds__(64 * (BV / 16 + 5), 1) void fused_wy_kernel(Problem p, FwdPlan plan) {
+  using Cfg = WyCfg<DK, BV>;
+  static_assert(Cfg::NT == 64 * (BV / 16 + 5), "launch bounds");
+  using M = Mma<bf16>;
+  using frag = bf16x8;
+  constexpr int NCH = Cfg::NCH, NP = Cfg::NP, NKS = Cfg::NKS, NKT = Cfg::NKT;
+  constexpr int KS = Cfg::KS, CS = Cfg::CS, VS = Cfg::VS;
+
+  __shared__ __align__(16) bf16 sK[3][kChunk * KS];   // ring of three: chunk i in slot i % 3
+  __shared__ __align__(16) bf16 sQ[2][kChunk * KS];
+  __shared__ __align__(16) bf16 sV[2][kChunk * VS];
+  __shared__ __align__(16) bf16 sT[2][kChunk * CS];
+  __shared__ __align__(16) bf16 sP[2][kChunk * CS];
+  __shared__ __align__(16) float sGam[2][kChunk], sGamS[2][kChunk], sDec[2][kChunk], sBet[2][kChunk];
+  __shared__ float sGC[2];
+  __shared__ __align__(16) float sGB[NP][2 * kChunk];
+  __shared__ __align__(16) float sInv[Cfg::INV];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, q = lane >> 4;
+  const int H = p.H, dv = p.dv;
+
+  // ---- unit decode (XCD-aware: the column blocks of one unit share id mod 8, so they
+  //      run on one XCD and share its L2 for K, Q, g, beta)
+  const int64_t bid = blockIdx.x;
+  const int ncb = dv / BV;
+  const int64_t rest = bid >> 3;
+  const int cb = (int)(rest % ncb);
+  const int64_t unit = (rest / ncb) * 8 + (bid & 7);
+  if (unit >= plan.units) return;
+  const int col0 = cb * BV;
+  const int h = (int)(unit % H);
+  const int64_t sg = plan.seg_order ? plan.seg_order[unit / H] : unit / H;
+  int n, seg;
+  if (plan.seg_off) {
+    n = seq_of_chunk(sg, plan.seg_off, p.N, 0);
+    seg = (int)(sg - plan.seg_off[n]);
+  } else if (p.cu) {   // packed without segment tables: one segment per sequence
+    n = (int)sg;
+    seg = 0;
+  } else {
+    const int64_t nch_all = (p.T + kChunk - 1) / kChunk;
+    const int64_t segs = max((int64_t)1, (nch_all + plan.seg_chunks - 1) / plan.seg_chunks);
+    n = (int)(sg / segs);
+    seg = (int)(sg - (int64_t)n * segs);
+  }
+  const SeqInfo si = seq_info(n, p.cu, p.chunk_off, p.T);
+  const int nch = (si.len + kChunk - 1) / kChunk;
+  const int c_begin = seg * plan.seg_chunks;
+  const int c_end = min(nch, c_begin + plan.seg_chunks);
+  const int nh = n * H + h;
+  const bool last_seg = c_end >= nch;
+  const int W = (plan.cp.best && !plan.cp.force_correction)
+                    ? window_of(plan.cp.best, nh, nch, plan.cp.wmax, plan.cp.thr) : 0;
+  // start state and chunk range: [c_start, c_end) is run, O is written from c_out
+  enum { kZero, kH0, kBuf };
+  int init = kZero, c_start = c_begin;
+  const int c_out = c_begin;
+  if (seg == 0) {
+    init = p.h0 ? kH0 : kZero;
+  } else if (W > 0) {
+    c_start = c_begin - W;
+    if (c_start <= 0) { c_start = 0; init = p.h0 ? kH0 : kZero; }
+  } else {
+    init = kBuf;
+  }
+  const int nrun = max(0, c_end - c_start);
+
+  // blocks (0, 1) and (2, 3) of T and P are zero and never written again
+  for (int e = tid; e < 2 * 2 * 16 * 16; e += Cfg::NT) {
+    const int buf = e >> 9, blk = (e >> 8) & 1, rr = (e >> 4) & 15, cc = e & 15;
+    const int row = tord(32 * blk + rr), col = 32 * blk + 16 + cc;
+    sT[buf][row * CS + col] = (bf16)0.f;
+    sP[buf][row * CS + col] = (bf16)0.f;
+  }
+
+  const int row_qk = H * DK, row_v = H * dv;   // element strides between tokens
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  if (wave < NCH) {
+    // =========================== chain wave ===========================
+    const int wcol = wave * 16;                // wave's first column inside the block
+    f32x4 hs[NKT];
+    {
+      const float* src = init == kH0 ? p.h0 + (int64_t)nh * DK * dv
+                                     : (init == kBuf ? plan.cp.hstart + (sg * H + h) * DK * dv : nullptr);
+#pragma unroll
+      for (int t = 0; t < NKT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          hs[t][i] = src ? src[(int64_t)prow(t, 4 * q + i) * dv + col0 + wcol + r16] : 0.f;
+    }
+    bf16* Ob = reinterpret_cast<bf16*>(p.o) + si.tok0 * row_v + (int64_t)h * dv + col0 + wcol;
+    // One chunk step; EMIT (compile-time): whether the chunk produces O (lookback
+    // chunks do not: no Q product, no O), so each variant is straight-line code.
+    auto chain_step = [&](auto emit_tag, int i) {
+      constexpr bool EMIT = decltype(emit_tag)::value;
+      const int b = i & 1;
+      const bf16* cK = sK[i % 3];
+      const bf16* cQ = sQ[b];
+      const bf16* cV = sV[b];
+      const bf16* cT = sT[b];
+      const bf16* cP = sP[b];
+      const int c = c_start + i;
+      const int len = min(kChunk, si.len - c * kChunk);
+      auto rows4 = [&](const float* v, int u) { return *reinterpret_cast<const f32x4*>(v + prow(u, 4 * q)); };
+      // ---- X = K h and Y^T = h^T Q^T (transposed: a lane holds four consecutive value
+      //      columns of one query row, the layout of the O store)
+      f32x4 X[4], Yp[4];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        frag aK[4], aQ[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          aK[u] = lds_frag(cK, KS, 16 * u + r16, 32 * ks, q);
+          if constexpr (EMIT) aQ[u] = lds_frag(cQ, KS, 16 * u + r16, 32 * ks, q);
+        }
+        const frag hb = M::pack(hs[2 * ks], hs[2 * ks + 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          X[u] = M::run(aK[u], hb, ks == 0 ? zero4 : X[u]);
+          if constexpr (EMIT) Yp[u] = M::run(hb, aQ[u], ks == 0 ? zero4 : Yp[u]);
+        }
+      }
+      // ---- V' = diag(beta) (V - diag(gamma) X), in place; V read in accumulator layout
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 vv = col_read4(cV, VS, prow(u, 4 * q), wcol + r16, wcol + 4 * (r16 & 3));
+        X[u] = rows4(sBet[b], u) * (vv - rows4(sGam[b], u) * X[u]);
+      }
+      // ---- U = T V' (T lower triangular: row tiles 0, 1 need contraction step 0 only)
+      frag wb[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) wb[ks] = M::pack(X[2 * ks], X[2 * ks + 1]);
+      f32x4 U[4];
+      {
+        frag aT[6];   // (u, s): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int ks = 0; ks <= (u >> 1); ++ks) aT[u < 2 ? u : 2 * u - 2 + ks] = lds_frag(cT, CS, 16 * u + r16, 32 * ks, q);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int ks = 0; ks <= (u >> 1); ++ks)
+            U[u] = M::run(aT[u < 2 ? u : 2 * u - 2 + ks], wb[ks], ks == 0 ? zero4 : U[u]);
+      }
+      frag ubp[2], ubd[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if constexpr (EMIT) ubp[ks] = M::pack(U[2 * ks], U[2 * ks + 1]);
+        ubd[ks] = M::pack(U[2 * ks] * rows4(sDec[b], 2 * ks), U[2 * ks + 1] * rows4(sDec[b], 2 * ks + 1));
+      }
+      // ---- O = scale diag(gamma) Q h + P U, stored 16 bytes per lane
+      if constexpr (EMIT) {
+        frag aP[6];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int ks = 0; ks <= (u >> 1); ++ks) aP[u < 2 ? u : 2 * u - 2 + ks] = lds_frag(cP, CS, 16 * u + r16, 32 * ks, q);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Yp[u] = Yp[u] * sGamS[b][prow(u, r16)];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int ks = 0; ks <= (u >> 1); ++ks) Yp[u] = M::run(ubp[ks], aP[u < 2 ? u : 2 * u - 2 + ks], Yp[u]);
+        bf16* ob = Ob + (int64_t)c * kChunk * row_v;
+        // for the tile pair (u, u+1), v_permlane16_swap hands lane group q^1 the other
+        // group's four columns: an even group then holds eight consecutive columns of
+        // tile u's row, an odd group those of tile u+1's row
+#pragma unroll
+        for (int u = 0; u < 4; u += 2) {
+          const int row = (q & 1) ? prow(u + 1, r16) : prow(u, r16);
+          const uint2 a = pack_bf16x4(Yp[u]), bb = pack_bf16x4(Yp[u + 1]);
+          const auto sx = __builtin_amdgcn_permlane16_swap(a.x, bb.x, false, false);
+          const auto sy = __builtin_amdgcn_permlane16_swap(a.y, bb.y, false, false);
+          const u32x4 v = {sx[0], sy[0], sx[1], sy[1]};
+          if (row < len) *reinterpret_cast<u32x4*>(ob + row * row_v + 8 * (q >> 1)) = v;
+        }
+      }
+      // ---- h <- gamma_last h + K^T (diag(d) U); K^T fragments by LDS transpose reads
+      const float gC = sGC[b];
+#pragma unroll
+      for (int t0 = 0; t0 < NKT; t0 += 2) {
+        frag aKt[2][2];
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const int t = t0 + dt;
+          const int own = prow(t, r16), supply = prow(t, 4 * (r16 & 3));
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+            aKt[dt][ks] = col_frag(cK, KS, 32 * ks + 4 * q, 32 * ks + 16 + 4 * q, own, supply);
+        }
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) hs[t0 + dt] *= gC;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) hs[t0 + dt] = M::run(aKt[dt][ks], ubd[ks], hs[t0 + dt]);
+      }
+    };
+    // the prep waves fill the first buffer sets during NP + 1 steps
+    for (int s = -NP - 1; s < 0; ++s) __syncthreads();
+    __builtin_amdgcn_s_setprio(1);
+    for (int i = 0; i < nrun; ++i) {
+      if (c_start + i >= c_out) chain_step(std::true_type{}, i);
+      else chain_step(std::false_type{}, i);
+      __syncthreads();
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if (last_seg && p.hT) {
+      float* dst = p.hT + (int64_t)nh * DK * dv + col0 + wcol;
+#pragma unroll
+      for (int t = 0; t < NKT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(int64_t)prow(t, 4 * q + i) * dv + r16] = hs[t][i];
+    }
+  } else {
+    // =========================== prep wave ===========================
+    const int pw = wave - NCH;                 // owns chunks c_start + i, i = pw (mod NP)
+    float* sG = sGB[pw];                       // chunk-local cumulative gate, per row
+    float* sB = sG + kChunk;                   // beta, per row
+    float* sAd = sInv;                         // diagonal A blocks, row-major, stride 16
+    float* sTd = sInv + 4 * Cfg::ABS;          // diagonal T blocks, column-major, stride TCS
+    const bf16* Kb = reinterpret_cast<const bf16*>(p.k) + si.tok0 * row_qk + (int64_t)h * DK;
+    const bf16* Qb = reinterpret_cast<const bf16*>(p.q) + si.tok0 * row_qk + (int64_t)h * DK;
+    const bf16* Vb = reinterpret_cast<const bf16*>(p.v) + si.tok0 * row_v + (int64_t)h * dv + col0;
+    const float* Gb = p.g + si.tok0 * H + h;
+    const int bsz = p.beta_bf16 ? 2 : 4;
+    const char* Bb = reinterpret_cast<const char*>(p.beta) + (si.tok0 * H + h) * bsz;
+    PrepChunk<DK, BV> R;
+
+    // ---- loads of chunk i (relative to c_start): rows past the chunk end read as zero
+    auto load = [&](int i) {
+      const int c = c_start + i;
+      const int len = min(kChunk, si.len - c * kChunk);
+      const bool withq = c >= c_out;
+      const int64_t t0 = (int64_t)c * kChunk;
+      const bf16* kc = Kb + t0 * row_qk;
+      const bf16* qc = Qb + t0 * row_qk;
+      const frag zf = {};
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int row = 16 * a + r16;
+        const bool ok = row < len;
+        const uint32_t off = (uint32_t)(row * row_qk + 8 * q) * 2u;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          R.kf[a][ks] = ok ? *reinterpret_cast<const frag*>(reinterpret_cast<const char*>(kc) + off + 64u * ks) : zf;
+          R.qf[a][ks] = (ok && withq)
+                            ? *reinterpret_cast<const frag*>(reinterpret_cast<const char*>(qc) + off + 64u * ks)
+                            : zf;
+        }
+      }
+      {
+        const bf16* vc = Vb + t0 * row_v;
+#pragma unroll
+        for (int j = 0; j < Cfg::NVP; ++j) {
+          const int idx = lane + 64 * j, row = idx / Cfg::VPR, cv = (idx % Cfg::VPR) * 8;
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          R.vp[j] = row < len ? *reinterpret_cast<const u32x4*>(vc + (int64_t)row * row_v + cv) : z;
+        }
+      }
+      R.g = lane < len ? Gb[(t0 + lane) * H] : 0.f;
+      if (lane < len) {
+        const int64_t bi = (t0 + lane) * H;
+        R.b = p.beta_bf16 ? (float)reinterpret_cast<const bf16*>(Bb)[bi] : reinterpret_cast<const float*>(Bb)[bi];
+      } else {
+        R.b = 0.f;
+      }
+    };
+
+    // ---- Q of chunk i again, for its LDS write (the first copy dies after P, so the
+    //      inverse runs without it; this one comes from L2)
+    auto load_q = [&](int i) {
+      const int c = c_start + i;
+      const int len = min(kChunk, si.len - c * kChunk);
+      const bf16* qc = Qb + (int64_t)c * kChunk * row_qk;
+      const frag zf = {};
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int row = 16 * a + r16;
+        const uint32_t off = (uint32_t)(row * row_qk + 8 * q) * 2u;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          R.qf[a][ks] = row < len ? *reinterpret_cast<const frag*>(reinterpret_cast<const char*>(qc) + off + 64u * ks) : zf;
+      }
+    };
+
+    // ---- gates and the Gram tiles of K K^T (first half of step 1)
+    auto gates_gram = [&]() {
+      const float G = wave_inclusive_scan_dpp(R.g);
+      sG[lane] = G;
+      sB[lane] = R.b;
+#pragma unroll
+      for (int k = 0; k < 10; ++k) {
+        int a, b;
+        lower_block(k, a, b);
+        f32x4 acc = zero4;
+        // diagonal: K_a K_a^T; off-diagonal transposed: K_b K_a^T
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) acc = M::run(R.kf[b][ks], R.kf[a][ks], acc);
+        if (a == b) R.gd[a] = acc;
+        else R.go[(a * (a - 1)) / 2 + b] = acc;
+      }
+    };
+
+    // ---- gated, masked A and T = (I + A)^{-1} (second half of step 1)
+    auto inverse = [&]() {
+      auto go = [&](int a, int b) -> const f32x4& { return R.go[(a * (a - 1)) / 2 + b]; };
+      wave_lds_sync();
+      // gate and mask: A[m][k] = beta_m exp(G_m - G_k) (K K^T)[m][k], k < m
+      float Gc[4], Bc[4];
+      f32x4 Gr[4], Br[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        Gc[a] = sG[16 * a + r16];
+        Bc[a] = sB[16 * a + r16];
+        Gr[a] = *reinterpret_cast<const f32x4*>(sG + 16 * a + 4 * q);
+        Br[a] = *reinterpret_cast<const f32x4*>(sB + 16 * a + 4 * q);
+      }
+      f32x4 At[4][4];   // At[a][b] = D(A_ab^T), b < a
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 4 * q + i;
+          sAd[a * Cfg::ABS + m * 16 + r16] = r16 < m ? Br[a][i] * fast_exp(Gr[a][i] - Gc[a]) * R.gd[a][i] : 0.f;
+        }
+#pragma unroll
+        for (int b = 0; b < a; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) At[a][b][i] = Bc[a] * fast_exp(Gc[a] - Gr[b][i]) * go(a, b)[i];
+      }
+      wave_lds_sync();
+      // T_bb = (I + A_bb)^{-1}: lane (r, q) solves column r of block q
+      {
+        const float* arow = sAd + q * Cfg::ABS;
+        float x[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          float acc = (m == r16) ? 1.f : 0.f;
+#pragma unroll
+          for (int j = 0; j < (m + 3) / 4; ++j) {
+            const f32x4 a4 = *reinterpret_cast<const f32x4*>(arow + m * 16 + 4 * j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (4 * j + e < m) acc -= a4[e] * x[4 * j + e];
+          }
+          x[m] = acc;
+        }
+        float* tcol = sTd + q * Cfg::TBS + r16 * Cfg::TCS;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 v = {x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]};
+          *reinterpret_cast<f32x4*>(tcol + 4 * j) = v;
+        }
+      }
+      wave_lds_sync();
+      f32x4 Td[4], TdT[4];   // D(T_aa), D(T_aa^T)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        Td[a] = *reinterpret_cast<const f32x4*>(sTd + a * Cfg::TBS + r16 * Cfg::TCS + 4 * q);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) TdT[a][i] = sTd[a * Cfg::TBS + (4 * q + i) * Cfg::TCS + r16];
+      }
+      // doubling levels: T_10 = -T_11 A_10 T_00, T_32 = -T_33 A_32 T_22, then the
+      // lower-left 32 x 32 quadrant from the two diagonal quadrants
+      const f32x4 R10 = mm16(At[1][0], Td[0], zero4);
+      const f32x4 T10 = -mm16(TdT[1], R10, zero4);
+      const f32x4 T10T = -mm16(R10, TdT[1], zero4);
+      const f32x4 R32 = mm16(At[3][2], Td[2], zero4);
+      const f32x4 T32T = -mm16(R32, TdT[3], zero4);
+      const f32x4 R20 = mm16(At[2][1], T10, mm16(At[2][0], Td[0], zero4));
+      const f32x4 R21 = mm16(At[2][1], Td[1], zero4);
+      const f32x4 R30 = mm16(At[3][1], T10, mm16(At[3][0], Td[0], zero4));
+      const f32x4 R31 = mm16(At[3][1], Td[1], zero4);
+      const f32x4 T20T = -mm16(R20, TdT[2], zero4);
+      const f32x4 T21T = -mm16(R21, TdT[2], zero4);
+      const f32x4 T30T = -mm16(R30, TdT[3], mm16(R20, T32T, zero4));
+      const f32x4 T31T = -mm16(R31, TdT[3], mm16(R21, T32T, zero4));
+      // blocks in lower_block order: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
+      R.tb[0] = pack_bf16x4(TdT[0]);
+      R.tb[1] = pack_bf16x4(T10T);
+      R.tb[2] = pack_bf16x4(TdT[1]);
+      R.tb[3] = pack_bf16x4(T20T);
+      R.tb[4] = pack_bf16x4(T21T);
+      R.tb[5] = pack_bf16x4(TdT[2]);
+      R.tb[6] = pack_bf16x4(T30T);
+      R.tb[7] = pack_bf16x4(T31T);
+      R.tb[8] = pack_bf16x4(T32T);
+      R.tb[9] = pack_bf16x4(TdT[3]);
+    };
+
+    // ---- P = scale (Q K^T) * Gamma, lower blocks; lane (r, q) of block (a, b): query
+    //      16a + r, keys 16b + 4q .. +3 (computed as K_b Q_a^T)
+    auto pstep = [&]() {
+#pragma unroll
+      for (int i = 0; i < 10; ++i) {
+        int a, b;
+        lower_block(i, a, b);
+        f32x4 acc = zero4;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) acc = M::run(R.kf[b][ks], R.qf[a][ks], acc);
+        const int qrow = 16 * a + r16, key0 = 16 * b + 4 * q;
+        const float Gq = sG[qrow];
+        const f32x4 Gk = *reinterpret_cast<const f32x4*>(sG + key0);
+        f32x4 pv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[e] = key0 + e <= qrow ? p.scale * acc[e] * fast_exp(Gq - Gk[e]) : 0.f;
+        R.pb[i] = pack_bf16x4(pv);
+      }
+    };
+
+    // ---- K of chunk i into its ring slot i % 3 (free from step i - 2 on: the chain
+    //      read it last for chunk i - 3), written before the inverse to free registers
+    auto write_k = [&](int i) {
+      bf16* dst = sK[i % 3];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int lr = tord(16 * a + r16);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) *reinterpret_cast<frag*>(dst + lr * KS + 32 * ks + 8 * q) = R.kf[a][ks];
+      }
+    };
+    // ---- the rest of what the chain reads for chunk i, into buffer set i % 2
+    auto write = [&](int i) {
+      const int b = i & 1;
+      const bool withq = c_start + i >= c_out;
+      if (withq) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int lr = tord(16 * a + r16);
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) *reinterpret_cast<frag*>(sQ[b] + lr * KS + 32 * ks + 8 * q) = R.qf[a][ks];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < Cfg::NVP; ++j) {
+        const int idx = lane + 64 * j, row = idx / Cfg::VPR, cv = (idx % Cfg::VPR) * 8;
+        *reinterpret_cast<u32x4*>(sV[b] + row * VS + cv) = R.vp[j];
+      }
+#pragma unroll
+      for (int k = 0; k < 10; ++k) {
+        int a, bb;
+        lower_block(k, a, bb);
+        const int off = tord(16 * a + r16) * CS + 16 * bb + 4 * q;
+        *reinterpret_cast<uint2*>(sT[b] + off) = R.tb[k];
+        if (withq) *reinterpret_cast<uint2*>(sP[b] + off) = R.pb[k];
+      }
+      const float G = sG[lane];
+      const float Glast = sG[kChunk - 1];   // rows past the chunk end repeat the last real G
+      const float gam = fast_exp(G);
+      sGam[b][lane] = gam;
+      sGamS[b][lane] = gam * p.scale;
+      sDec[b][lane] = fast_exp(Glast - G);
+      sBet[b][lane] = sB[lane];
+      if (lane == 0) sGC[b] = fast_exp(Glast);
+    };
+
+    // Step schedule (step s: the chain computes chunk s; s < 0: preparation only).
+    // This wave owns chunks i = pw, pw + NP, ...: it issues chunk i's loads in step
+    // i - NP - 1 (right after writing its previous chunk), lets them land during step
+    // i - 5, forms the gates and the Gram tiles in step i - 4, P in step i - 3 (after
+    // which Q is dead), the inverse in step i - 2 and writes everything in step i - 1.
+    // Each step has exactly one prep wave in each phase, so the inverse's scratch is
+    // shared.  Written as one straight pass per owned chunk so that the compiler sees
+    // which registers each phase holds.  Every wave executes one barrier per step,
+    // nrun + NP + 1 in all.
+    static_assert(NP == 5, "one pass of the loop below is the NP = 5 steps of one owned chunk");
+    int s = -NP - 1;
+    for (; s < pw - NP - 1; ++s) __syncthreads();
+    if (nrun > 0) load(min(pw, nrun - 1));
+    __syncthreads();
+    ++s;
+    for (int i = pw; i < nrun; i += NP) {
+      __syncthreads();   // s == i - 5: the loads land
+      ++s;
+      gates_gram();      // s == i - 4
+      __syncthreads();
+      ++s;
+      if (c_start + i >= c_out) {   // s == i - 3
+        pstep();
+      } else {
+#pragma unroll
+        for (int k = 0; k < 10; ++k) R.pb[k] = make_uint2(0u, 0u);
+      }
+      __syncthreads();
+      ++s;
+      write_k(i);        // s == i - 2
+      inverse();
+      if (c_start + i >= c_out) {
+        load_q(i);
+      } else {   // a lookback chunk writes no Q; defining it here ends the first copy's life
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) R.qf[a][ks] = frag{};
+      }
+      __syncthreads();
+      ++s;
+      write(i);          // s == i - 1
+      load(min(i + NP, nrun - 1));   // past the end: reloads the last chunk (unused); always
+                                     // defined, so the old registers die at the write
+      __syncthreads();
+      ++s;
+    }
+    for (; s < nrun; ++s) __syncthreads();
+  }
+}
+
+// 1-D grid of ceil(units / 8) * 8 * (dv / BV) workgroups (see the decode in the kernel).
+template <int DK>
+static hipError_t launch_wy_dk(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev) {
+  constexpr int BV = 32;
+  using Cfg = WyCfg<DK, BV>;
+  const int ncb = p.dv / BV;
+  const int64_t groups = (plan.units + 7) / 8;
+  if (groups * 8 * ncb > kMaxDispatchItems / Cfg::NT) return hipErrorInvalidConfiguration;
+  hipExtLaunchKernelGGL(fused_wy_kernel<DK, BV>, dim3((unsigned)(groups * 8 * ncb)), dim3(Cfg::NT), 0, s,
+                        ev.start, ev.stop, 0, p, plan);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_wy(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev) {
+  if (plan.units == 0) {
+    ev.record_empty(s);
+    return hipSuccess;
+  }
+  if (!p.qkv_bf16) return hipErrorInvalidValue;
+  return p.dk == 128 ? launch_wy_dk<128>(p, plan, s, ev) : launch_wy_dk<64>(p, plan, s, ev);
+}
+
+}  // namespace gdn

@@ -122,7 +122,8 @@ int validate_shape(const gdn_shape* s) {
 
 int validate_opts(const gdn_opts* o) {
   if (!o) return GDN_OK;
-  if (o->value_block != 0 && o->value_block != 64 && o->value_block != 128) return GDN_ERR_ARG;
+  if (o->value_block != 0 && o->value_block != 32 && o->value_block != 64 && o->value_block != 128)
+    return GDN_ERR_ARG;
   if (o->force_segment_chunks < 0 || o->window_max_chunks < 0 ||
       o->window_max_chunks > kWindowMaxCap)
     return GDN_ERR_ARG;
@@ -143,6 +144,9 @@ struct Plan {
   int64_t total_segs = 0;
   int value_block = 128;
   int pass1_block = 64;
+  // one-pass kernel (fused_wy.hip, bf16): the chunk inverse is formed inside the forward
+  // pass; K1 and the T buffer are needed only when a split plan runs pass 1
+  bool wy = false;
   int wmax = kWindowMaxCap;
   float log_eps = 0.f;
 };
@@ -218,7 +222,8 @@ Plan plan_uncached(const gdn_shape* s, const gdn_opts* o) {
     P.max_chunks = std::max(P.max_chunks, c);
   }
   const int vb_req = o ? o->value_block : 0;
-  P.value_block = (s->qkv_dtype == GDN_BF16 && s->dv % 128 == 0 && vb_req != 64) ? 128 : 64;
+  P.wy = s->qkv_dtype == GDN_BF16 && vb_req == 32;
+  P.value_block = P.wy ? 32 : (s->qkv_dtype == GDN_BF16 && s->dv % 128 == 0 && vb_req != 64) ? 128 : 64;
   P.pass1_block = vb_req == 128 ? 128 : 64;
   P.wmax = (o && o->window_max_chunks > 0) ? o->window_max_chunks : kWindowMaxCap;
   P.log_eps = (o && o->window_log_eps != 0.f) ? o->window_log_eps : (float)std::log(0x1p-24);
@@ -226,6 +231,8 @@ Plan plan_uncached(const gdn_shape* s, const gdn_opts* o) {
   if (!(o && o->no_split) && P.max_chunks > 1) {
     if (o && o->force_segment_chunks > 0) {
       L = o->force_segment_chunks;
+    } else if (P.wy) {
+      // one-pass plans run unsplit unless a segment length is forced
     } else {
       // T auto-CP: cost(L) = lambda1 * (pass-3 makespan in chunk steps) + lambda2 *
       // (merge steps of the longest sequence); the makespan is simulated (see
@@ -340,6 +347,10 @@ Plan make_plan(const gdn_shape* s, const gdn_opts* o) {
   return P;
 }
 
+// Whether the chunk-inverse kernel runs: always on the two-pass path; on the one-pass
+// path only for split plans (pass 1 and the gate scan read its T and chunk gate sums).
+bool runs_k1(const Plan& P) { return !P.wy || P.split; }
+
 struct Layout {
   size_t tmat = 0, chunk_off = 0, seg_off = 0, seg_order = 0, best = 0, csum = 0, sstar = 0, mcorr = 0,
          hstart = 0;
@@ -353,7 +364,7 @@ Layout layout(const gdn_shape* s, const Plan& P) {
   const size_t esz = s->qkv_dtype == GDN_BF16 ? 2 : 4;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
-  L.tmat = take((size_t)P.total_chunks * s->H * kChunk * kChunk * esz);
+  L.tmat = take(runs_k1(P) ? (size_t)P.total_chunks * s->H * kChunk * kChunk * esz : 0);
   L.chunk_off = take((size_t)(s->N + 1) * sizeof(int32_t));
   L.seg_off = take((size_t)(s->N + 1) * sizeof(int32_t));
   if (s->cu_seqlens_host && P.split && s->N <= gdn::kSegOrderMaxSeqs) {
@@ -416,6 +427,7 @@ bool grids_fit(const gdn_shape* s, const Plan& P) {
   if (!fits(P.total_chunks * ((H + 3) / 4), 256)) return false;                  // K1
   const int64_t unit_groups = (P.total_segs * H + 7) / 8;
   if (!fits(unit_groups * 8, s->dv * 4)) return false;                           // pass 3
+  if (P.wy && !fits(unit_groups * 8, s->dv / 32 * 448)) return false;            // one pass
   if (!P.split) return true;
   if (!fits(nh, P.max_chunks > 512 ? 1024 : 256)) return false;                   // gate scan
   if (!fits(unit_groups * 8, (s->dv + s->dk) * 4)) return false;                  // pass 1
@@ -473,9 +485,12 @@ int run_stages(int first, int last, const void* q, const void* k, const void* v,
   void* tmat = ws + L.tmat;
   float* csum = P.split ? reinterpret_cast<float*>(ws + L.csum) : nullptr;
   if (runs(GDN_STAGE_INVERSE)) {
-    if (gdn::launch_chunk_inverse(p, tmat, csum, false, stream,
-                                  stage_events(opts, GDN_STAGE_INVERSE)) != hipSuccess)
+    if (!runs_k1(P)) {
+      stage_events(opts, GDN_STAGE_INVERSE).record_empty(stream);
+    } else if (gdn::launch_chunk_inverse(p, tmat, csum, false, stream,
+                                         stage_events(opts, GDN_STAGE_INVERSE)) != hipSuccess) {
       return GDN_ERR_HIP;
+    }
   }
 
   gdn::FwdPlan plan;
@@ -518,7 +533,8 @@ int run_stages(int first, int last, const void* q, const void* k, const void* v,
     }
   }
   if (runs(GDN_STAGE_FORWARD)) {
-    if (gdn::launch_fused_forward(p, plan, stream, stage_events(opts, GDN_STAGE_FORWARD)) !=
+    const gdn::KernelEvents ev = stage_events(opts, GDN_STAGE_FORWARD);
+    if ((P.wy ? gdn::launch_fused_wy(p, plan, stream, ev) : gdn::launch_fused_forward(p, plan, stream, ev)) !=
         hipSuccess)
       return GDN_ERR_HIP;
   }
@@ -601,7 +617,7 @@ int gdn_chunk_fwd_workspace_region(const gdn_shape* shape, const gdn_opts* opts,
   switch (region) {
     case GDN_REGION_CHUNK_INVERSE:
       *offset = L.tmat;
-      *bytes = (size_t)P.total_chunks * shape->H * kChunk * kChunk * esz;
+      *bytes = runs_k1(P) ? (size_t)P.total_chunks * shape->H * kChunk * kChunk * esz : 0;
       break;
     case GDN_REGION_WINDOWS:
       *offset = L.best;

@@ -101,6 +101,9 @@ hipError_t launch_cp_merge(const Problem& p, const FwdPlan& plan, int max_steps,
 // forward never reads it).
 hipError_t launch_chunk_inverse(const Problem& p, void* t_out, float* csum, bool full,
                                 hipStream_t s, KernelEvents ev = {});
+// One pass, bf16 only: steps 1-4 with the inverse formed in the kernel (fused_wy.hip);
+// kPass3 plans only, 32 value columns per workgroup.
+hipError_t launch_fused_wy(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev = {});
 hipError_t launch_fused_forward(const Problem& p, const FwdPlan& plan, hipStream_t s,
                                 KernelEvents ev = {});
 

@@ -85,7 +85,7 @@ typedef struct gdn_opts {
   int32_t window_max_chunks;    /* longest lookback window in chunks, 1..16; 0 -> 16 */
   float lambda1_us;             /* planner: cost of one chunk step; 0 -> built in */
   float lambda2_us;             /* planner: cost of one merge step; 0 -> built in */
-  int32_t value_block;          /* value columns per workgroup of the fused kernel: 64 or
+  int32_t value_block;          /* value columns per workgroup of the fused kernel: 32, 64 or
                                    128; 0 -> planner's choice */
   /* Optional timing hook: NULL, or an array of 2 * GDN_NUM_STAGES events created by
    * the caller (hipEventCreate).  For every stage that runs, stage_events[2*s] and
