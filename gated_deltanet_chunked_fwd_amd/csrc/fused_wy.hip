@@ -21,18 +21,17 @@
 //   * NCH = BV / 16 "chain" waves own 16 value columns each (all dk rows of h in
 //     fp32 accumulator tiles, tile order, gdn_device.h) and run, per chunk, only
 //     X = K h, Y = Q h, V', U, O and the state update, from operands staged in LDS;
-//   * NP = 3 "prep" waves own every NP-th chunk.  A prep wave loads its chunk's K and
-//     Q rows from HBM straight into MFMA operand registers (plus V, g, beta), scans
-//     the gates, forms the gated Gram matrix, inverts it (16 x 16 diagonal blocks by
-//     forward substitution in fp32, the rest by two doubling levels of MFMA
-//     products) and forms P; then, in the step before the chain needs the chunk, it
-//     writes K, Q, V, T, P and the gate tables into one of two LDS buffer sets.
-// One workgroup barrier per chunk step: during step i the chain reads buffer set
-// i % 2 (K: ring slot i % 3) while the prep wave that owns chunk i + 1 writes set
-// (i + 1) % 2.  A prep
-// wave with chunk j issues its loads in step j - NP - 1, forms step 1 in step
-// j - NP, P in step j - NP + 1 and writes in step j - 1.  The first NP + 1 steps
-// only prepare (the chain waits at their barriers).
+//   * NP = 6 "prep" waves own every NP-th chunk.  A prep wave loads its chunk's rows
+//     from HBM straight into MFMA operand registers, scans the gates, forms the
+//     gated Gram matrix and its inverse (16 x 16 diagonal blocks by forward
+//     substitution in fp32, the rest by two doubling levels of MFMA products) and
+//     P, and stages K, Q, V, T, P and the gate tables in LDS for the chain.
+// One workgroup barrier per chunk step.  During step i the chain computes chunk i
+// from LDS buffer set i % 2 (K: ring slot i % 3); the prep wave that owns chunk
+// i + 1 writes set (i + 1) % 2 and the one that owns chunk i + 2 writes K into slot
+// (i + 2) % 3.  A prep wave spreads one chunk over NP steps, one phase per step
+// (see the schedule at the prep loop); each step has exactly one prep wave in each
+// phase.  The first NP + 1 steps only prepare (the chain waits at their barriers).
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -45,7 +44,7 @@ namespace {
 template <int DK, int BV>
 struct WyCfg {
   static constexpr int NCH = BV / 16;          // chain waves (16 value columns each)
-  static constexpr int NP = 5;                 // prep waves
+  static constexpr int NP = 6;                 // prep waves
   static constexpr int NW = NCH + NP;
   static constexpr int NT = 64 * NW;
   static constexpr int NKS = DK / 32;          // contraction steps over dk
@@ -57,8 +56,8 @@ struct WyCfg {
   static constexpr int VS = BV + 16;           // sV: natural rows
   static constexpr int VPR = BV / 8;           // 16-byte pieces per V row
   static constexpr int NVP = kChunk * VPR / 64;  // V pieces per prep lane
-  // fp32 scratch of step 1: per prep wave G and beta; shared by the prep waves (only
-  // one of them inverts in any step) the diagonal A blocks (row-major, block stride
+  // fp32 scratch of the diagonal-block substitution, shared by the prep waves (one of
+  // them substitutes in any step): the diagonal A blocks (row-major, block stride
   // ABS) and the diagonal T blocks (column-major, column stride TCS)
   static constexpr int ABS = 260, TCS = 20, TBS = 16 * TCS;
   static constexpr int INV = 4 * ABS + 4 * TBS;
@@ -86,15 +85,26 @@ __device__ __forceinline__ f32x4 mm16(const f32x4& xt, const f32x4& y, f32x4 acc
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
 }
 
-// One chunk held by a prep wave from its loads to its LDS writes.
+// An opaque zero (an instruction the compiler cannot see through): per-lane indices
+// offset by it are recomputed inside a loop instead of being hoisted and spilled.
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
+// One chunk held by a prep wave from its first loads to its last LDS write.
 template <int DK, int BV>
 struct PrepChunk {
   using Cfg = WyCfg<DK, BV>;
   bf16x8 kf[4][Cfg::NKS];   // K rows 16a + r, columns 32s + 8q .. +7 (lane (r, q))
   bf16x8 qf[4][Cfg::NKS];   // Q, same layout
   u32x4 vp[Cfg::NVP];       // V pieces: piece lane + 64 j is row / VPR, 8 columns
-  float g, b;               // gate and beta of row = lane (zero past the chunk end)
-  f32x4 gd[4], go[6];       // Gram tiles: D(K_a K_a^T) and D(K_b K_a^T) for b < a (order of lower_block)
+  float g, b;               // gate and beta of row = lane (as loaded; masked in gates_gram)
+  int len;                  // rows of the chunk
+  f32x4 ad[4];              // D(A_aa): diagonal blocks of A, slot i = A[16a+4q+i][16a+r]
+  f32x4 at[6];              // D(A_ab^T), b < a (order of lower_block without the diagonal)
+  f32x4 td[4], tdt[4];      // D(T_aa), D(T_aa^T)
   uint2 tb[10];             // T blocks, bf16, lane (r, q): row 16a + r, columns 16b + 4q .. +3
   uint2 pb[10];             // P blocks, same layout (query rows, key columns)
 };
@@ -102,9 +112,9 @@ struct PrepChunk {
 }  // namespace
 
 template <int DK, int BV>
-__global__ __launch_bounds__(64 * (BV / 16 + 5), 1) void fused_wy_kernel(Problem p, FwdPlan plan) {
+__global__ __launch_bounds__(64 * (BV / 16 + 6), 1) void fused_wy_kernel(Problem p, FwdPlan plan) {
   using Cfg = WyCfg<DK, BV>;
-  static_assert(Cfg::NT == 64 * (BV / 16 + 5), "launch bounds");
+  static_assert(Cfg::NT == 64 * (BV / 16 + 6), "launch bounds");
   using M = Mma<bf16>;
   using frag = bf16x8;
   constexpr int NCH = Cfg::NCH, NP = Cfg::NP, NKS = Cfg::NKS, NKT = Cfg::NKT;
@@ -196,6 +206,8 @@ __global__ __launch_bounds__(64 * (BV / 16 + 5), 1) void fused_wy_kernel(Problem
           hs[t][i] = src ? src[(int64_t)prow(t, 4 * q + i) * dv + col0 + wcol + r16] : 0.f;
     }
     bf16* Ob = reinterpret_cast<bf16*>(p.o) + si.tok0 * row_v + (int64_t)h * dv + col0 + wcol;
+    // per-lane indices, re-derived at every step from an opaque zero
+    int cr16 = r16, cq = q;
     // One chunk step; EMIT (compile-time): whether the chunk produces O (lookback
     // chunks do not: no Q product, no O), so each variant is straight-line code.
     auto chain_step = [&](auto emit_tag, int i) {
@@ -208,30 +220,32 @@ __global__ __launch_bounds__(64 * (BV / 16 + 5), 1) void fused_wy_kernel(Problem
       const bf16* cP = sP[b];
       const int c = c_start + i;
       const int len = min(kChunk, si.len - c * kChunk);
-      auto rows4 = [&](const float* v, int u) { return *reinterpret_cast<const f32x4*>(v + prow(u, 4 * q)); };
+      auto rows4 = [&](const float* v, int u) { return *reinterpret_cast<const f32x4*>(v + prow(u, 4 * cq)); };
       // ---- X = K h and Y^T = h^T Q^T (transposed: a lane holds four consecutive value
-      //      columns of one query row, the layout of the O store)
+      //      columns of one query row, the layout of the O store); every K and Q
+      //      fragment read is issued before the first product
+      frag aK[NKS][4], aQ[NKS][4];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          aK[ks][u] = lds_frag(cK, KS, 16 * u + cr16, 32 * ks, cq);
+          if constexpr (EMIT) aQ[ks][u] = lds_frag(cQ, KS, 16 * u + cr16, 32 * ks, cq);
+        }
       f32x4 X[4], Yp[4];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        frag aK[4], aQ[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          aK[u] = lds_frag(cK, KS, 16 * u + r16, 32 * ks, q);
-          if constexpr (EMIT) aQ[u] = lds_frag(cQ, KS, 16 * u + r16, 32 * ks, q);
-        }
         const frag hb = M::pack(hs[2 * ks], hs[2 * ks + 1]);
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          X[u] = M::run(aK[u], hb, ks == 0 ? zero4 : X[u]);
-          if constexpr (EMIT) Yp[u] = M::run(hb, aQ[u], ks == 0 ? zero4 : Yp[u]);
+          X[u] = M::run(aK[ks][u], hb, ks == 0 ? zero4 : X[u]);
+          if constexpr (EMIT) Yp[u] = M::run(hb, aQ[ks][u], ks == 0 ? zero4 : Yp[u]);
         }
       }
       // ---- V' = diag(beta) (V - diag(gamma) X), in place; V read in accumulator layout
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const f32x4 vv = col_read4(cV, VS, prow(u, 4 * q), wcol + r16, wcol + 4 * (r16 & 3));
+        const f32x4 vv = col_read4(cV, VS, prow(u, 4 * cq), wcol + cr16, wcol + 4 * (cr16 & 3));
         X[u] = rows4(sBet[b], u) * (vv - rows4(sGam[b], u) * X[u]);
       }
       // ---- U = T V' (T lower triangular: row tiles 0, 1 need contraction step 0 only)
@@ -244,8 +258,7 @@ __global__ __launch_bounds__(64 * (BV / 16 + 5), 1) void fused_wy_kernel(Problem
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int ks = 0; ks <= (u >> 1); ++ks) aT[u < 2 ? u : 2 * u - 2 + ks] = lds_frag(cT, CS, 16 * u + r16, 32 * ks, q);
-        __builtin_amdgcn_sched_barrier(0);
+          for (int ks = 0; ks <= (u >> 1); ++ks) aT[u < 2 ? u : 2 * u - 2 + ks] = lds_frag(cT, CS, 16 * u + cr16, 32 * ks, cq);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -258,16 +271,35 @@ __global__ __launch_bounds__(64 * (BV / 16 + 5), 1) void fused_wy_kernel(Problem
         if constexpr (EMIT) ubp[ks] = M::pack(U[2 * ks], U[2 * ks + 1]);
         ubd[ks] = M::pack(U[2 * ks] * rows4(sDec[b], 2 * ks), U[2 * ks + 1] * rows4(sDec[b], 2 * ks + 1));
       }
+      // ---- h <- gamma_last h + K^T (diag(d) U); K^T fragments by LDS transpose reads
+      const float gC = sGC[b];
+#pragma unroll
+      for (int t0 = 0; t0 < NKT; t0 += 2) {
+        frag aKt[2][2];
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const int t = t0 + dt;
+          const int own = prow(t, cr16), supply = prow(t, 4 * (cr16 & 3));
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+            aKt[dt][ks] = col_frag(cK, KS, 32 * ks + 4 * cq, 32 * ks + 16 + 4 * cq, own, supply);
+        }
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) hs[t0 + dt] *= gC;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) hs[t0 + dt] = M::run(aKt[dt][ks], ubd[ks], hs[t0 + dt]);
+      }
       // ---- O = scale diag(gamma) Q h + P U, stored 16 bytes per lane
       if constexpr (EMIT) {
         frag aP[6];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int ks = 0; ks <= (u >> 1); ++ks) aP[u < 2 ? u : 2 * u - 2 + ks] = lds_frag(cP, CS, 16 * u + r16, 32 * ks, q);
+          for (int ks = 0; ks <= (u >> 1); ++ks) aP[u < 2 ? u : 2 * u - 2 + ks] = lds_frag(cP, CS, 16 * u + cr16, 32 * ks, cq);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) Yp[u] = Yp[u] * sGamS[b][prow(u, r16)];
-        __builtin_amdgcn_sched_barrier(0);
+        for (int u = 0; u < 4; ++u) Yp[u] = Yp[u] * sGamS[b][prow(u, cr16)];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -278,40 +310,22 @@ __global__ __launch_bounds__(64 * (BV / 16 + 5), 1) void fused_wy_kernel(Problem
         // tile u's row, an odd group those of tile u+1's row
 #pragma unroll
         for (int u = 0; u < 4; u += 2) {
-          const int row = (q & 1) ? prow(u + 1, r16) : prow(u, r16);
+          const int row = (cq & 1) ? prow(u + 1, cr16) : prow(u, cr16);
           const uint2 a = pack_bf16x4(Yp[u]), bb = pack_bf16x4(Yp[u + 1]);
           const auto sx = __builtin_amdgcn_permlane16_swap(a.x, bb.x, false, false);
           const auto sy = __builtin_amdgcn_permlane16_swap(a.y, bb.y, false, false);
           const u32x4 v = {sx[0], sy[0], sx[1], sy[1]};
-          if (row < len) *reinterpret_cast<u32x4*>(ob + row * row_v + 8 * (q >> 1)) = v;
+          if (row < len) *reinterpret_cast<u32x4*>(ob + row * row_v + 8 * (cq >> 1)) = v;
         }
-      }
-      // ---- h <- gamma_last h + K^T (diag(d) U); K^T fragments by LDS transpose reads
-      const float gC = sGC[b];
-#pragma unroll
-      for (int t0 = 0; t0 < NKT; t0 += 2) {
-        frag aKt[2][2];
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const int t = t0 + dt;
-          const int own = prow(t, r16), supply = prow(t, 4 * (r16 & 3));
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-            aKt[dt][ks] = col_frag(cK, KS, 32 * ks + 4 * q, 32 * ks + 16 + 4 * q, own, supply);
-        }
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) hs[t0 + dt] *= gC;
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) hs[t0 + dt] = M::run(aKt[dt][ks], ubd[ks], hs[t0 + dt]);
       }
     };
     // the prep waves fill the first buffer sets during NP + 1 steps
     for (int s = -NP - 1; s < 0; ++s) __syncthreads();
     __builtin_amdgcn_s_setprio(1);
     for (int i = 0; i < nrun; ++i) {
+      const int z = opaque_zero();
+      cr16 = r16 + z;
+      cq = q + z;
       if (c_start + i >= c_out) chain_step(std::true_type{}, i);
       else chain_step(std::false_type{}, i);
       __syncthreads();
@@ -338,117 +352,116 @@ __global__ __launch_bounds__(64 * (BV / 16 + 5), 1) void fused_wy_kernel(Problem
     const int bsz = p.beta_bf16 ? 2 : 4;
     const char* Bb = reinterpret_cast<const char*>(p.beta) + (si.tok0 * H + h) * bsz;
     PrepChunk<DK, BV> R;
+    // per-lane indices used below, re-derived at every pass of the step loop from an
+    // opaque zero: their address arithmetic stays inside the loop (a few VALU
+    // operations) instead of being hoisted out and spilled to scratch
+    int lr16 = r16, lq = q, llane = lane;
 
-    // ---- loads of chunk i (relative to c_start): rows past the chunk end read as zero
-    auto load = [&](int i) {
+    // Rows past a partial chunk's end read the chunk's last row instead (always inside
+    // the sequence) and are left as they are: their beta and g are zeroed in
+    // gates_gram, which zeroes every contribution of such a row (A's rows, V', U), and
+    // their O rows are never stored.  No value is selected right after its load, so
+    // issuing a batch never waits for it.
+    auto row_off = [&](int a, int len) { return (uint32_t)(min(16 * a + lr16, len - 1) * row_qk + 8 * lq) * 2u; };
+    // ---- K, g and beta of chunk i (for step 1)
+    auto load_kgb = [&](int i) {
       const int c = c_start + i;
       const int len = min(kChunk, si.len - c * kChunk);
-      const bool withq = c >= c_out;
+      R.len = len;
       const int64_t t0 = (int64_t)c * kChunk;
-      const bf16* kc = Kb + t0 * row_qk;
-      const bf16* qc = Qb + t0 * row_qk;
-      const frag zf = {};
+      const char* kc = reinterpret_cast<const char*>(Kb + t0 * row_qk);
+      const int64_t ti = (t0 + min(llane, len - 1)) * H;
+      R.g = Gb[ti];
+      R.b = p.beta_bf16 ? (float)reinterpret_cast<const bf16*>(Bb)[ti] : reinterpret_cast<const float*>(Bb)[ti];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const int row = 16 * a + r16;
-        const bool ok = row < len;
-        const uint32_t off = (uint32_t)(row * row_qk + 8 * q) * 2u;
+        const uint32_t off = row_off(a, len);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) R.kf[a][ks] = *reinterpret_cast<const frag*>(kc + off + 64u * ks);
+      }
+    };
+    // ---- K again, Q and V of chunk i (for P and the LDS writes)
+    auto load_kqv = [&](int i) {
+      const int c = c_start + i;
+      const int len = R.len;
+      const int64_t t0 = (int64_t)c * kChunk;
+      const char* kc = reinterpret_cast<const char*>(Kb + t0 * row_qk);
+      const char* qc = reinterpret_cast<const char*>(Qb + t0 * row_qk);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const uint32_t off = row_off(a, len);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          R.kf[a][ks] = ok ? *reinterpret_cast<const frag*>(reinterpret_cast<const char*>(kc) + off + 64u * ks) : zf;
-          R.qf[a][ks] = (ok && withq)
-                            ? *reinterpret_cast<const frag*>(reinterpret_cast<const char*>(qc) + off + 64u * ks)
-                            : zf;
+          R.kf[a][ks] = *reinterpret_cast<const frag*>(kc + off + 64u * ks);
+          R.qf[a][ks] = *reinterpret_cast<const frag*>(qc + off + 64u * ks);
         }
       }
-      {
-        const bf16* vc = Vb + t0 * row_v;
+      const char* vc = reinterpret_cast<const char*>(Vb + t0 * row_v);
 #pragma unroll
-        for (int j = 0; j < Cfg::NVP; ++j) {
-          const int idx = lane + 64 * j, row = idx / Cfg::VPR, cv = (idx % Cfg::VPR) * 8;
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          R.vp[j] = row < len ? *reinterpret_cast<const u32x4*>(vc + (int64_t)row * row_v + cv) : z;
-        }
-      }
-      R.g = lane < len ? Gb[(t0 + lane) * H] : 0.f;
-      if (lane < len) {
-        const int64_t bi = (t0 + lane) * H;
-        R.b = p.beta_bf16 ? (float)reinterpret_cast<const bf16*>(Bb)[bi] : reinterpret_cast<const float*>(Bb)[bi];
-      } else {
-        R.b = 0.f;
+      for (int j = 0; j < Cfg::NVP; ++j) {
+        const int idx = llane + 64 * j, row = min(idx / Cfg::VPR, len - 1), cv = (idx % Cfg::VPR) * 8;
+        R.vp[j] = *reinterpret_cast<const u32x4*>(vc + (uint32_t)(row * row_v + cv) * 2u);
       }
     };
 
-    // ---- Q of chunk i again, for its LDS write (the first copy dies after P, so the
-    //      inverse runs without it; this one comes from L2)
-    auto load_q = [&](int i) {
-      const int c = c_start + i;
-      const int len = min(kChunk, si.len - c * kChunk);
-      const bf16* qc = Qb + (int64_t)c * kChunk * row_qk;
-      const frag zf = {};
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int row = 16 * a + r16;
-        const uint32_t off = (uint32_t)(row * row_qk + 8 * q) * 2u;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-          R.qf[a][ks] = row < len ? *reinterpret_cast<const frag*>(reinterpret_cast<const char*>(qc) + off + 64u * ks) : zf;
-      }
-    };
-
-    // ---- gates and the Gram tiles of K K^T (first half of step 1)
+    // ---- gates, the Gram tiles of K K^T, and A = strict_lower(diag(beta) K K^T * Gamma)
+    //      in registers: diagonal blocks D(A_aa), off-diagonal blocks transposed D(A_ab^T)
     auto gates_gram = [&]() {
-      const float G = wave_inclusive_scan_dpp(R.g);
-      sG[lane] = G;
-      sB[lane] = R.b;
+      const bool real = llane < R.len;   // rows past the chunk end: g = 0, beta = 0
+      const float G = wave_inclusive_scan_dpp(real ? R.g : 0.f);
+      sG[llane] = G;
+      sB[llane] = real ? R.b : 0.f;
+      f32x4 gd[4], go[6];   // D(K_a K_a^T), D(K_b K_a^T) for b < a
 #pragma unroll
       for (int k = 0; k < 10; ++k) {
         int a, b;
         lower_block(k, a, b);
         f32x4 acc = zero4;
-        // diagonal: K_a K_a^T; off-diagonal transposed: K_b K_a^T
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) acc = M::run(R.kf[b][ks], R.kf[a][ks], acc);
-        if (a == b) R.gd[a] = acc;
-        else R.go[(a * (a - 1)) / 2 + b] = acc;
+        if (a == b) gd[a] = acc;
+        else go[(a * (a - 1)) / 2 + b] = acc;
       }
-    };
-
-    // ---- gated, masked A and T = (I + A)^{-1} (second half of step 1)
-    auto inverse = [&]() {
-      auto go = [&](int a, int b) -> const f32x4& { return R.go[(a * (a - 1)) / 2 + b]; };
       wave_lds_sync();
-      // gate and mask: A[m][k] = beta_m exp(G_m - G_k) (K K^T)[m][k], k < m
       float Gc[4], Bc[4];
       f32x4 Gr[4], Br[4];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        Gc[a] = sG[16 * a + r16];
-        Bc[a] = sB[16 * a + r16];
-        Gr[a] = *reinterpret_cast<const f32x4*>(sG + 16 * a + 4 * q);
-        Br[a] = *reinterpret_cast<const f32x4*>(sB + 16 * a + 4 * q);
+        Gc[a] = sG[16 * a + lr16];
+        Bc[a] = sB[16 * a + lr16];
+        Gr[a] = *reinterpret_cast<const f32x4*>(sG + 16 * a + 4 * lq);
+        Br[a] = *reinterpret_cast<const f32x4*>(sB + 16 * a + 4 * lq);
       }
-      f32x4 At[4][4];   // At[a][b] = D(A_ab^T), b < a
+      // A[m][k] = beta_m exp(G_m - G_k) (K K^T)[m][k], k < m
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int m = 4 * q + i;
-          sAd[a * Cfg::ABS + m * 16 + r16] = r16 < m ? Br[a][i] * fast_exp(Gr[a][i] - Gc[a]) * R.gd[a][i] : 0.f;
+          const int m = 4 * lq + i;
+          R.ad[a][i] = lr16 < m ? Br[a][i] * fast_exp(Gr[a][i] - Gc[a]) * gd[a][i] : 0.f;
         }
 #pragma unroll
         for (int b = 0; b < a; ++b)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) At[a][b][i] = Bc[a] * fast_exp(Gc[a] - Gr[b][i]) * go(a, b)[i];
+          for (int i = 0; i < 4; ++i)
+            R.at[(a * (a - 1)) / 2 + b][i] = Bc[a] * fast_exp(Gc[a] - Gr[b][i]) * go[(a * (a - 1)) / 2 + b][i];
       }
+    };
+
+    // ---- T_bb = (I + A_bb)^{-1} for the four diagonal blocks, in fp32: lane (r, q)
+    //      solves column r of block q by forward substitution on the shared scratch
+    auto solve_diag = [&]() {
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sAd[a * Cfg::ABS + (4 * lq + i) * 16 + lr16] = R.ad[a][i];
       wave_lds_sync();
-      // T_bb = (I + A_bb)^{-1}: lane (r, q) solves column r of block q
       {
-        const float* arow = sAd + q * Cfg::ABS;
+        const float* arow = sAd + lq * Cfg::ABS;
         float x[16];
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
-          float acc = (m == r16) ? 1.f : 0.f;
+          float acc = (m == lr16) ? 1.f : 0.f;
 #pragma unroll
           for (int j = 0; j < (m + 3) / 4; ++j) {
             const f32x4 a4 = *reinterpret_cast<const f32x4*>(arow + m * 16 + 4 * j);
@@ -458,7 +471,7 @@ __global__ __launch_bounds__(64 * (BV / 16 + 5), 1) void fused_wy_kernel(Problem
           }
           x[m] = acc;
         }
-        float* tcol = sTd + q * Cfg::TBS + r16 * Cfg::TCS;
+        float* tcol = sTd + lq * Cfg::TBS + lr16 * Cfg::TCS;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const f32x4 v = {x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]};
@@ -466,151 +479,159 @@ __global__ __launch_bounds__(64 * (BV / 16 + 5), 1) void fused_wy_kernel(Problem
         }
       }
       wave_lds_sync();
-      f32x4 Td[4], TdT[4];   // D(T_aa), D(T_aa^T)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        Td[a] = *reinterpret_cast<const f32x4*>(sTd + a * Cfg::TBS + r16 * Cfg::TCS + 4 * q);
+        R.td[a] = *reinterpret_cast<const f32x4*>(sTd + a * Cfg::TBS + lr16 * Cfg::TCS + 4 * lq);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) TdT[a][i] = sTd[a * Cfg::TBS + (4 * q + i) * Cfg::TCS + r16];
+        for (int i = 0; i < 4; ++i) R.tdt[a][i] = sTd[a * Cfg::TBS + (4 * lq + i) * Cfg::TCS + lr16];
       }
-      // doubling levels: T_10 = -T_11 A_10 T_00, T_32 = -T_33 A_32 T_22, then the
-      // lower-left 32 x 32 quadrant from the two diagonal quadrants
-      const f32x4 R10 = mm16(At[1][0], Td[0], zero4);
-      const f32x4 T10 = -mm16(TdT[1], R10, zero4);
-      const f32x4 T10T = -mm16(R10, TdT[1], zero4);
-      const f32x4 R32 = mm16(At[3][2], Td[2], zero4);
-      const f32x4 T32T = -mm16(R32, TdT[3], zero4);
-      const f32x4 R20 = mm16(At[2][1], T10, mm16(At[2][0], Td[0], zero4));
-      const f32x4 R21 = mm16(At[2][1], Td[1], zero4);
-      const f32x4 R30 = mm16(At[3][1], T10, mm16(At[3][0], Td[0], zero4));
-      const f32x4 R31 = mm16(At[3][1], Td[1], zero4);
-      const f32x4 T20T = -mm16(R20, TdT[2], zero4);
-      const f32x4 T21T = -mm16(R21, TdT[2], zero4);
-      const f32x4 T30T = -mm16(R30, TdT[3], mm16(R20, T32T, zero4));
-      const f32x4 T31T = -mm16(R31, TdT[3], mm16(R21, T32T, zero4));
-      // blocks in lower_block order: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
-      R.tb[0] = pack_bf16x4(TdT[0]);
+    };
+
+    // ---- the off-diagonal blocks by two doubling levels: T_10 = -T_11 A_10 T_00,
+    //      T_32 = -T_33 A_32 T_22, then the lower-left 32 x 32 quadrant from the two
+    //      diagonal quadrants; T leaves as bf16 in the LDS-write layout
+    auto doubling = [&]() {
+      auto at = [&](int a, int b) -> const f32x4& { return R.at[(a * (a - 1)) / 2 + b]; };
+      const f32x4 R10 = mm16(at(1, 0), R.td[0], zero4);
+      const f32x4 T10 = -mm16(R.tdt[1], R10, zero4);
+      const f32x4 T10T = -mm16(R10, R.tdt[1], zero4);
+      const f32x4 R32 = mm16(at(3, 2), R.td[2], zero4);
+      const f32x4 T32T = -mm16(R32, R.tdt[3], zero4);
+      const f32x4 R20 = mm16(at(2, 1), T10, mm16(at(2, 0), R.td[0], zero4));
+      const f32x4 R21 = mm16(at(2, 1), R.td[1], zero4);
+      const f32x4 R30 = mm16(at(3, 1), T10, mm16(at(3, 0), R.td[0], zero4));
+      const f32x4 R31 = mm16(at(3, 1), R.td[1], zero4);
+      const f32x4 T20T = -mm16(R20, R.tdt[2], zero4);
+      const f32x4 T21T = -mm16(R21, R.tdt[2], zero4);
+      const f32x4 T30T = -mm16(R30, R.tdt[3], mm16(R20, T32T, zero4));
+      const f32x4 T31T = -mm16(R31, R.tdt[3], mm16(R21, T32T, zero4));
+      // lower_block order: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
+      R.tb[0] = pack_bf16x4(R.tdt[0]);
       R.tb[1] = pack_bf16x4(T10T);
-      R.tb[2] = pack_bf16x4(TdT[1]);
+      R.tb[2] = pack_bf16x4(R.tdt[1]);
       R.tb[3] = pack_bf16x4(T20T);
       R.tb[4] = pack_bf16x4(T21T);
-      R.tb[5] = pack_bf16x4(TdT[2]);
+      R.tb[5] = pack_bf16x4(R.tdt[2]);
       R.tb[6] = pack_bf16x4(T30T);
       R.tb[7] = pack_bf16x4(T31T);
       R.tb[8] = pack_bf16x4(T32T);
-      R.tb[9] = pack_bf16x4(TdT[3]);
-    };
-
-    // ---- P = scale (Q K^T) * Gamma, lower blocks; lane (r, q) of block (a, b): query
-    //      16a + r, keys 16b + 4q .. +3 (computed as K_b Q_a^T)
-    auto pstep = [&]() {
-#pragma unroll
-      for (int i = 0; i < 10; ++i) {
-        int a, b;
-        lower_block(i, a, b);
-        f32x4 acc = zero4;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) acc = M::run(R.kf[b][ks], R.qf[a][ks], acc);
-        const int qrow = 16 * a + r16, key0 = 16 * b + 4 * q;
-        const float Gq = sG[qrow];
-        const f32x4 Gk = *reinterpret_cast<const f32x4*>(sG + key0);
-        f32x4 pv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pv[e] = key0 + e <= qrow ? p.scale * acc[e] * fast_exp(Gq - Gk[e]) : 0.f;
-        R.pb[i] = pack_bf16x4(pv);
-      }
+      R.tb[9] = pack_bf16x4(R.tdt[3]);
     };
 
     // ---- K of chunk i into its ring slot i % 3 (free from step i - 2 on: the chain
-    //      read it last for chunk i - 3), written before the inverse to free registers
-    auto write_k = [&](int i) {
+    //      read it last for chunk i - 3), then P = scale (Q K^T) * Gamma, lower blocks;
+    //      lane (r, q) of block (a, b): query 16a + r, keys 16b + 4q .. +3 (as K_b Q_a^T)
+    auto write_k_p = [&](int i, bool withq) {
       bf16* dst = sK[i % 3];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const int lr = tord(16 * a + r16);
+        const int lr = tord(16 * a + lr16);
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) *reinterpret_cast<frag*>(dst + lr * KS + 32 * ks + 8 * q) = R.kf[a][ks];
+        for (int ks = 0; ks < NKS; ++ks) *reinterpret_cast<frag*>(dst + lr * KS + 32 * ks + 8 * lq) = R.kf[a][ks];
+      }
+      if (withq) {
+#pragma unroll
+        for (int k = 0; k < 10; ++k) {
+          int a, b;
+          lower_block(k, a, b);
+          f32x4 acc = zero4;
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) acc = M::run(R.kf[b][ks], R.qf[a][ks], acc);
+          const int qrow = 16 * a + lr16, key0 = 16 * b + 4 * lq;
+          const float Gq = sG[qrow];
+          const f32x4 Gk = *reinterpret_cast<const f32x4*>(sG + key0);
+          f32x4 pv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pv[e] = key0 + e <= qrow ? p.scale * acc[e] * fast_exp(Gq - Gk[e]) : 0.f;
+          R.pb[k] = pack_bf16x4(pv);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 10; ++k) R.pb[k] = make_uint2(0u, 0u);
       }
     };
-    // ---- the rest of what the chain reads for chunk i, into buffer set i % 2
-    auto write = [&](int i) {
+
+    // ---- Q, V, T, P and the gate tables of chunk i, into buffer set i % 2
+    auto write = [&](int i, bool withq) {
       const int b = i & 1;
-      const bool withq = c_start + i >= c_out;
       if (withq) {
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
-          const int lr = tord(16 * a + r16);
+          const int lr = tord(16 * a + lr16);
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) *reinterpret_cast<frag*>(sQ[b] + lr * KS + 32 * ks + 8 * q) = R.qf[a][ks];
+          for (int ks = 0; ks < NKS; ++ks) *reinterpret_cast<frag*>(sQ[b] + lr * KS + 32 * ks + 8 * lq) = R.qf[a][ks];
         }
       }
 #pragma unroll
       for (int j = 0; j < Cfg::NVP; ++j) {
-        const int idx = lane + 64 * j, row = idx / Cfg::VPR, cv = (idx % Cfg::VPR) * 8;
+        const int idx = llane + 64 * j, row = idx / Cfg::VPR, cv = (idx % Cfg::VPR) * 8;
         *reinterpret_cast<u32x4*>(sV[b] + row * VS + cv) = R.vp[j];
       }
 #pragma unroll
       for (int k = 0; k < 10; ++k) {
         int a, bb;
         lower_block(k, a, bb);
-        const int off = tord(16 * a + r16) * CS + 16 * bb + 4 * q;
+        const int off = tord(16 * a + lr16) * CS + 16 * bb + 4 * lq;
         *reinterpret_cast<uint2*>(sT[b] + off) = R.tb[k];
         if (withq) *reinterpret_cast<uint2*>(sP[b] + off) = R.pb[k];
       }
-      const float G = sG[lane];
+      const float G = sG[llane];
       const float Glast = sG[kChunk - 1];   // rows past the chunk end repeat the last real G
       const float gam = fast_exp(G);
-      sGam[b][lane] = gam;
-      sGamS[b][lane] = gam * p.scale;
-      sDec[b][lane] = fast_exp(Glast - G);
-      sBet[b][lane] = sB[lane];
-      if (lane == 0) sGC[b] = fast_exp(Glast);
+      sGam[b][llane] = gam;
+      sGamS[b][llane] = gam * p.scale;
+      sDec[b][llane] = fast_exp(Glast - G);
+      sBet[b][llane] = sB[llane];
+      if (llane == 0) sGC[b] = fast_exp(Glast);
     };
 
     // Step schedule (step s: the chain computes chunk s; s < 0: preparation only).
-    // This wave owns chunks i = pw, pw + NP, ...: it issues chunk i's loads in step
-    // i - NP - 1 (right after writing its previous chunk), lets them land during step
-    // i - 5, forms the gates and the Gram tiles in step i - 4, P in step i - 3 (after
-    // which Q is dead), the inverse in step i - 2 and writes everything in step i - 1.
-    // Each step has exactly one prep wave in each phase, so the inverse's scratch is
-    // shared.  Written as one straight pass per owned chunk so that the compiler sees
-    // which registers each phase holds.  Every wave executes one barrier per step,
-    // nrun + NP + 1 in all.
-    static_assert(NP == 5, "one pass of the loop below is the NP = 5 steps of one owned chunk");
+    // This wave owns chunks i = pw, pw + NP, ...; for chunk i:
+    //   step i - 7: K, g, beta loads issued (right after the previous chunk's writes)
+    //   step i - 6: they land
+    //   step i - 5: gates, Gram tiles, A in registers
+    //   step i - 4: diagonal-block substitution (the shared scratch)
+    //   step i - 3: doubling -> T; K, Q and V loads issued
+    //   step i - 2: K into its ring slot; P
+    //   step i - 1: Q, V, T, P and the gate tables into buffer set i % 2; K, g, beta
+    //               loads of chunk i + NP issued
+    // Written as one straight pass per owned chunk so that the compiler sees which
+    // registers each phase holds; loads past the last chunk reload the last chunk
+    // (unused), so every phase defines the same registers.  Every wave executes one
+    // barrier per step, nrun + NP + 1 in all.
+    static_assert(NP == 6, "one pass of the loop below is the NP = 6 steps of one owned chunk");
+    auto refresh_lanes = [&]() {
+      const int z = opaque_zero();
+      lr16 = r16 + z;
+      lq = q + z;
+      llane = lane + z;
+    };
     int s = -NP - 1;
     for (; s < pw - NP - 1; ++s) __syncthreads();
-    if (nrun > 0) load(min(pw, nrun - 1));
+    refresh_lanes();
+    if (nrun > 0) load_kgb(min(pw, nrun - 1));
     __syncthreads();
     ++s;
     for (int i = pw; i < nrun; i += NP) {
-      __syncthreads();   // s == i - 5: the loads land
+      const bool withq = c_start + i >= c_out;
+      refresh_lanes();
+      __syncthreads();     // s == i - 6: the loads land
       ++s;
-      gates_gram();      // s == i - 4
+      gates_gram();        // s == i - 5
       __syncthreads();
       ++s;
-      if (c_start + i >= c_out) {   // s == i - 3
-        pstep();
-      } else {
-#pragma unroll
-        for (int k = 0; k < 10; ++k) R.pb[k] = make_uint2(0u, 0u);
-      }
+      solve_diag();        // s == i - 4
       __syncthreads();
       ++s;
-      write_k(i);        // s == i - 2
-      inverse();
-      if (c_start + i >= c_out) {
-        load_q(i);
-      } else {   // a lookback chunk writes no Q; defining it here ends the first copy's life
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) R.qf[a][ks] = frag{};
-      }
+      doubling();          // s == i - 3
+      load_kqv(i);
       __syncthreads();
       ++s;
-      write(i);          // s == i - 1
-      load(min(i + NP, nrun - 1));   // past the end: reloads the last chunk (unused); always
-                                     // defined, so the old registers die at the write
+      write_k_p(i, withq); // s == i - 2
+      __syncthreads();
+      ++s;
+      write(i, withq);     // s == i - 1
+      load_kgb(min(i + NP, nrun - 1));
       __syncthreads();
       ++s;
     }

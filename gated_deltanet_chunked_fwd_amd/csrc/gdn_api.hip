@@ -427,7 +427,7 @@ bool grids_fit(const gdn_shape* s, const Plan& P) {
   if (!fits(P.total_chunks * ((H + 3) / 4), 256)) return false;                  // K1
   const int64_t unit_groups = (P.total_segs * H + 7) / 8;
   if (!fits(unit_groups * 8, s->dv * 4)) return false;                           // pass 3
-  if (P.wy && !fits(unit_groups * 8, s->dv / 32 * 448)) return false;            // one pass
+  if (P.wy && !fits(unit_groups * 8, s->dv / 32 * 512)) return false;            // one pass
   if (!P.split) return true;
   if (!fits(nh, P.max_chunks > 512 ? 1024 : 256)) return false;                   // gate scan
   if (!fits(unit_groups * 8, (s->dv + s->dk) * 4)) return false;                  // pass 1
