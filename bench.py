@@ -19,13 +19,17 @@ hipEventDisableSystemFence (no cache writeback when they complete).  For context
 path.ms_per_step_evicted_caches_median is the median of up to 10 calls that each
 start after a cache eviction (each includes one start marker, a few microseconds).
 
-Roofline (dominant kernel = the stage with the largest mean time):
+Roofline (dominant kernel = the stage with the largest mean time; for the forward
+stage that is fused_wy, the one-pass kernel, or fused_forward, the two-kernel
+path's forward, whichever the plan runs):
   achieved = algorithmic bytes of that kernel per launch (stage_bytes(): for the
   pass that writes o, bytes per token-head = 2*(dk+dv)*e_qkv + e_g + e_beta plus
   the fp32 states) / its live mean duration; peak = 8000 GB/s.
 traffic = HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE (from
-profiles/traffic_fused_forward.json) if those counters were taken on the current
-kernel source, else null.
+profiles/traffic_<kernel>.json) if those counters were taken on the current kernel
+source, workload and segment length, else null.
+roofline.whole_call: the same algorithmic bytes over the whole call (every launch,
+ms_per_step), the figure the one-GPU target is stated on.
 
 path.copy_gbs_context: read + write GB/s of a plain 512 MiB device copy on the same
 stream, as context for what the HBM roofline allows in practice.
@@ -62,6 +66,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-split", type=int, default=0)
     ap.add_argument("--value-block", type=int, default=0)
+    ap.add_argument("--one-pass", type=int, default=0, help="1: one-pass forward, -1: two-kernel path, 0: planner")
     ap.add_argument("--segment-chunks", type=int, default=0, help="force the split length (0: planner)")
     ap.add_argument("--batch", type=int, default=0,
                     help="override the workload's batch size B (dense workloads; occupancy sweeps)")
@@ -201,10 +206,11 @@ def source_sha(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
 
-def traffic_for(kernel_src, workload, seg_chunks):
-    """HBM bytes per launch from committed rocprofv3 counters, if they were taken on
-    this exact kernel source, workload and segment length; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic_fused_forward.json")
+def traffic_for(kernel, kernel_src, workload, seg_chunks):
+    """HBM bytes per launch of `kernel` from committed rocprofv3 counters
+    (profiles/traffic_<kernel>.json), if they were taken on this exact kernel source,
+    workload and segment length; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % kernel)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -270,10 +276,10 @@ def main():
     hT = torch.empty((N, spec.H, spec.dk, spec.dv), dtype=torch.float32, device=dev)
     hip = Hip()
     stage_ev = hip.events(2 * binding.GDN_NUM_STAGES)
-    opts_all = binding.make_opts(no_split=args.no_split, value_block=args.value_block,
+    opts_all = binding.make_opts(no_split=args.no_split, value_block=args.value_block, one_pass=args.one_pass,
                                  force_segment_chunks=args.segment_chunks,
                                  stage_events=ctypes.cast(stage_ev, ctypes.c_void_p))
-    opts = binding.make_opts(no_split=args.no_split, value_block=args.value_block,
+    opts = binding.make_opts(no_split=args.no_split, value_block=args.value_block, one_pass=args.one_pass,
                              force_segment_chunks=args.segment_chunks)
     ws = torch.empty(max(binding.workspace_bytes(d["q"], d["v"], d["beta"], d["cu_seqlens"],
                                                  inp["cu_seqlens"], opts), 1),
@@ -288,6 +294,7 @@ def main():
         flush.fill_(i & 0xFF)
         flush_rd.sum()
     seg_chunks = binding.plan_segment_chunks(d["q"], d["v"], d["beta"], inp["cu_seqlens"], opts)
+    one_pass = binding.plan_one_pass(d["q"], d["v"], d["beta"], inp["cu_seqlens"], opts)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
     def step(o_=None):
@@ -334,7 +341,7 @@ def main():
             arr[2 * prev_idx + 1] = ev_prev_stop
         else:
             arr[2 * dom_idx] = ev_dom_start
-        o_ = binding.make_opts(no_split=args.no_split, value_block=args.value_block,
+        o_ = binding.make_opts(no_split=args.no_split, value_block=args.value_block, one_pass=args.one_pass,
                                force_segment_chunks=args.segment_chunks,
                                stage_events=ctypes.cast(arr, ctypes.c_void_p))
         o_._keep = arr
@@ -391,8 +398,10 @@ def main():
     flops = algorithmic_flops(spec)
     copy_gbs = copy_bandwidth(hip, stream, torch)
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    ksrc = os.path.join(ROOT, "gated_deltanet_chunked_fwd_amd", "csrc", "fused_forward.hip")
-    traffic = traffic_for(ksrc, spec.name, seg_chunks) if dom == "fused_forward" else None
+    kernel = ("fused_wy" if one_pass else "fused_forward") if dom == "fused_forward" else dom
+    ksrc = os.path.join(ROOT, "gated_deltanet_chunked_fwd_amd", "csrc", kernel + ".hip")
+    traffic = traffic_for(kernel, ksrc, spec.name, seg_chunks) if dom == "fused_forward" else None
+    call_achieved = alg_bytes / (ms * 1e-3) / 1e9
     mfma_peak = BF16_PEAK_TFLOPS if spec.dtype == "bf16" else F32_PEAK_TFLOPS
     rec = {
         "metric": METRIC,
@@ -410,10 +419,12 @@ def main():
         "config": {"workload": spec.name, "B": spec.B, "T": spec.T, "H": spec.H, "dk": spec.dk,
                    "dv": spec.dv, "chunk": 64, "initial_state": has_h0,
                    "final_state": True, "split_allowed": not args.no_split,
-                   "segment_chunks": seg_chunks, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                   "segment_chunks": seg_chunks, "one_pass": one_pass, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes": dom_bytes, "kernel_ms": dom_ms},
+                     "algorithmic_bytes": dom_bytes, "kernel_ms": dom_ms,
+                     "whole_call": {"achieved": call_achieved, "frac": call_achieved / HBM_PEAK_GBS,
+                                    "ms": ms, "algorithmic_bytes": alg_bytes}},
         "path": {"hbm_frac": alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                  "mfma_frac": flops / (ms * 1e-3) / 1e12 / mfma_peak,
                  "algorithmic_flops": flops,

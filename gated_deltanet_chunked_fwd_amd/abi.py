@@ -12,7 +12,7 @@ GDN_BF16, GDN_F32 = 1, 2
 EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_stage",
            "gdn_chunk_fwd_noalloc",
            "gdn_chunk_fwd_workspace_region", "gdn_chunk_inverse",
-           "gdn_gate_scan", "gdn_gate_scan_workspace_bytes", "gdn_plan_segment_chunks",
+           "gdn_gate_scan", "gdn_gate_scan_workspace_bytes", "gdn_plan_segment_chunks", "gdn_plan_one_pass",
            "gdn_total_chunks", "gdn_status_str")
 
 
@@ -28,7 +28,7 @@ class GdnOpts(ctypes.Structure):
                 ("force_correction", ctypes.c_int32), ("window_log_eps", ctypes.c_float),
                 ("window_max_chunks", ctypes.c_int32), ("lambda1_us", ctypes.c_float),
                 ("lambda2_us", ctypes.c_float), ("value_block", ctypes.c_int32),
-                ("stage_events", ctypes.c_void_p)]
+                ("one_pass", ctypes.c_int32), ("stage_events", ctypes.c_void_p)]
 
 
 GDN_STAGE_INVERSE, GDN_STAGE_GATE_SCAN, GDN_STAGE_CP_PASS1, GDN_STAGE_CP_MERGE = 0, 1, 2, 3
@@ -63,6 +63,8 @@ def declare(lib):
     lib.gdn_gate_scan_workspace_bytes.restype = ctypes.c_int
     lib.gdn_plan_segment_chunks.argtypes = [shp, opt]
     lib.gdn_plan_segment_chunks.restype = ctypes.c_int64
+    lib.gdn_plan_one_pass.argtypes = [shp, opt]
+    lib.gdn_plan_one_pass.restype = ctypes.c_int
     lib.gdn_total_chunks.argtypes = [shp]
     lib.gdn_total_chunks.restype = ctypes.c_int64
     lib.gdn_status_str.argtypes = [ctypes.c_int]
@@ -72,6 +74,7 @@ def declare(lib):
 
 def make_opts(no_split=0, force_segment_chunks=0, force_correction=0, window_log_eps=0.0,
               window_max_chunks=0, lambda1_us=0.0, lambda2_us=0.0, value_block=0,
-              stage_events=None) -> GdnOpts:
+              one_pass=0, stage_events=None) -> GdnOpts:
     return GdnOpts(no_split, force_segment_chunks, force_correction, window_log_eps,
-                   window_max_chunks, lambda1_us, lambda2_us, value_block, stage_events)
+                   window_max_chunks, lambda1_us, lambda2_us, value_block, one_pass,
+                   stage_events)

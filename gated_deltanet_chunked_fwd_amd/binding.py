@@ -332,3 +332,13 @@ def plan_segment_chunks(q, v, beta, cu_seqlens_host=None, opts: Optional[GdnOpts
     if r < 0:
         raise GdnError(int(r), "gdn_plan_segment_chunks")
     return int(r)
+
+
+def plan_one_pass(q, v, beta, cu_seqlens_host=None, opts: Optional[GdnOpts] = None) -> bool:
+    """Whether gdn_chunk_fwd runs the one-pass forward (chunk inverses formed inside the
+    forward kernel) for these inputs and options."""
+    sh = _Shape(q, v, beta, cu_seqlens_host, cu_seqlens_host)
+    r = lib().gdn_plan_one_pass(sh.ref(), None if opts is None else ctypes.byref(opts))
+    if r < 0:
+        raise GdnError(int(r), "gdn_plan_one_pass")
+    return bool(r)

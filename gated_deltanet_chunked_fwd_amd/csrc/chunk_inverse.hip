@@ -92,7 +92,8 @@ __device__ __forceinline__ typename Mma<E>::frag load_frag(const E* src, bool ok
 // forward never reads it.
 template <typename E, int DK>
 __global__ __launch_bounds__(256) void chunk_inverse_kernel(Problem p, E* __restrict__ tout,
-                                                             float* __restrict__ csum, int full) {
+                                                             float* __restrict__ csum, int full,
+                                                             HeadFilter only) {
   using Cfg = InvCfg<E, DK>;
   using M = Mma<E>;
   using frag = typename M::frag;
@@ -112,6 +113,9 @@ __global__ __launch_bounds__(256) void chunk_inverse_kernel(Problem p, E* __rest
   const int c = (int)(cg - si.chunk0);
   const int64_t r0 = si.tok0 + (int64_t)c * kChunk;
   const int len = min(kChunk, si.len - c * kChunk);
+  // heads with an admissible lookback window never read T (only corrected heads do)
+  if (only.best && window_of(only.best, n * p.H + h, (si.len + kChunk - 1) / kChunk, only.wmax, only.thr) > 0)
+    return;   // whole wave
 
   float* sG = lds + wave * Cfg::PER_WAVE;   // chunk-local cumulative gate, per row
   float* sB = sG + kChunk;                  // beta, per row
@@ -274,7 +278,7 @@ hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hi
 }
 
 hipError_t launch_chunk_inverse(const Problem& p, void* t_out, float* csum, bool full, hipStream_t s,
-                                KernelEvents ev) {
+                                KernelEvents ev, HeadFilter only) {
   if (p.total_chunks == 0) {
     ev.record_empty(s);
     return hipSuccess;
@@ -285,17 +289,17 @@ hipError_t launch_chunk_inverse(const Problem& p, void* t_out, float* csum, bool
   if (p.qkv_bf16) {
     if (p.dk == 128)
       hipExtLaunchKernelGGL(chunk_inverse_kernel<bf16, 128>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, p,
-                            (bf16*)t_out, csum, full ? 1 : 0);
+                            (bf16*)t_out, csum, full ? 1 : 0, only);
     else
       hipExtLaunchKernelGGL(chunk_inverse_kernel<bf16, 64>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, p,
-                            (bf16*)t_out, csum, full ? 1 : 0);
+                            (bf16*)t_out, csum, full ? 1 : 0, only);
   } else {
     if (p.dk == 128)
       hipExtLaunchKernelGGL(chunk_inverse_kernel<float, 128>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, p,
-                            (float*)t_out, csum, full ? 1 : 0);
+                            (float*)t_out, csum, full ? 1 : 0, only);
     else
       hipExtLaunchKernelGGL(chunk_inverse_kernel<float, 64>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, p,
-                            (float*)t_out, csum, full ? 1 : 0);
+                            (float*)t_out, csum, full ? 1 : 0, only);
   }
   return hipGetLastError();
 }

@@ -1,7 +1,7 @@
 // Steps 1-4 of the chunked WY form in one pass on gfx950 (bf16 storage): per
-// (sequence, head, segment, 32 value columns) one workgroup walks the chunks with
-// the state in registers, forms each chunk's inverse itself, and writes only O and
-// the final state.  Neither the inverse T nor W, U or S ever reaches HBM.
+// (sequence, head, segment) one workgroup walks the chunks with the state of all
+// value columns in registers, forms each chunk's inverse itself, and writes only O
+// and the final state.  Neither the inverse T nor W, U or S ever reaches HBM.
 //
 // FlashQLA talk transcript (tokendh.com): chunked-WY section (step 1, the chunk's
 // K K^T and its inverse; steps 2-4, the projections, the chunk-serial state
@@ -18,20 +18,22 @@
 //
 // Roles.  Only the last three lines depend on h; step 1 and P = scale (Q K^T) *
 // Gamma do not, so they are formed ahead of the recurrence by other waves:
-//   * NCH = BV / 16 "chain" waves own 16 value columns each (all dk rows of h in
-//     fp32 accumulator tiles, tile order, gdn_device.h) and run, per chunk, only
-//     X = K h, Y = Q h, V', U, O and the state update, from operands staged in LDS;
-//   * NP = 6 "prep" waves own every NP-th chunk.  A prep wave loads its chunk's rows
-//     from HBM straight into MFMA operand registers, scans the gates, forms the
-//     gated Gram matrix and its inverse (16 x 16 diagonal blocks by forward
+//   * NCH = 4 "chain" waves own CW = BV / 4 value columns each (all dk rows of h
+//     in fp32 accumulator tiles, tile order, gdn_device.h) and run, per chunk, only
+//     X = K h, Y = Q h, V', U, O and the state update.  Every K, Q, K^T, T and P
+//     fragment a chain wave reads from LDS feeds CW / 16 MFMAs (one per 16-column
+//     tile).  Each chain wave also stages its own V columns: loaded from HBM one
+//     step ahead, written to its private LDS columns at the start of the step.
+//   * NP = 4 "prep" waves own every fourth chunk.  A prep wave loads its chunk's
+//     rows from HBM straight into MFMA operand registers, scans the gates, forms
+//     the gated Gram matrix and its inverse (16 x 16 diagonal blocks by forward
 //     substitution in fp32, the rest by two doubling levels of MFMA products) and
-//     P, and stages K, Q, V, T, P and the gate tables in LDS for the chain.
+//     P, and stages K, Q, T, P and the gate tables in LDS for the chain.
 // One workgroup barrier per chunk step.  During step i the chain computes chunk i
-// from LDS buffer set i % 2 (K: ring slot i % 3); the prep wave that owns chunk
-// i + 1 writes set (i + 1) % 2 and the one that owns chunk i + 2 writes K into slot
-// (i + 2) % 3.  A prep wave spreads one chunk over NP steps, one phase per step
-// (see the schedule at the prep loop); each step has exactly one prep wave in each
-// phase.  The first NP + 1 steps only prepare (the chain waits at their barriers).
+// from LDS buffer set i % 2 (K: ring slot i % 3).  A prep wave spreads one chunk
+// over four steps, one phase per step (see the schedule at the prep loop); each
+// step has exactly one prep wave in each phase.  The first NP + 1 steps only
+// prepare (the chain waits at their barriers).
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -43,8 +45,10 @@ namespace {
 
 template <int DK, int BV>
 struct WyCfg {
-  static constexpr int NCH = BV / 16;          // chain waves (16 value columns each)
-  static constexpr int NP = 6;                 // prep waves
+  static constexpr int NCH = 4;                // chain waves
+  static constexpr int CW = BV / NCH;          // value columns per chain wave (16 or 32)
+  static constexpr int NCT = CW / 16;          // 16-column tiles per chain wave
+  static constexpr int NP = 4;                 // prep waves
   static constexpr int NW = NCH + NP;
   static constexpr int NT = 64 * NW;
   static constexpr int NKS = DK / 32;          // contraction steps over dk
@@ -52,10 +56,13 @@ struct WyCfg {
   // LDS row strides (elements): rows feeding 16-byte fragment reads and 8-byte
   // transpose reads are 8 (mod 32) dwords apart (conflict-free on gfx950's LDS)
   static constexpr int KS = DK + 16;           // sK, sQ: tile-order rows
-  static constexpr int CS = kChunk + 16;       // sT, sP: tile-order rows
   static constexpr int VS = BV + 16;           // sV: natural rows
-  static constexpr int VPR = BV / 8;           // 16-byte pieces per V row
-  static constexpr int NVP = kChunk * VPR / 64;  // V pieces per prep lane
+  static constexpr int VPR = CW / 8;           // 16-byte pieces per row of a chain wave's V
+  static constexpr int NVP = kChunk * VPR / 64;  // V pieces per chain lane
+  // T and P: the six 16 x 32 operand fragments of a lower-triangular 64 x 64 matrix
+  // (tri_frag), each stored as 64 lanes x 8 elements in lane order
+  static constexpr int FR = 512;
+  static constexpr int TF = 6;
   // fp32 scratch of the diagonal-block substitution, shared by the prep waves (one of
   // them substitutes in any step): the diagonal A blocks (row-major, block stride
   // ABS) and the diagonal T blocks (column-major, column stride TCS)
@@ -63,10 +70,29 @@ struct WyCfg {
   static constexpr int INV = 4 * ABS + 4 * TBS;
 };
 
+// Word 3 of a raw (unswizzled, stride 0) buffer resource on gfx9-family GPUs: 32-bit
+// data format; accesses at or past the resource's byte size are dropped (stores) or
+// read as zero (loads).
+constexpr int kRawBufferFlags = 0x00020000;
+
 // The ten 16 x 16 blocks (a, b), b <= a, of a lower-triangular 64 x 64 chunk matrix.
 __device__ __forceinline__ void lower_block(int i, int& a, int& b) {
   a = i < 1 ? 0 : i < 3 ? 1 : i < 6 ? 2 : 3;
   b = i - (a * (a + 1)) / 2;
+}
+
+// Operand fragments of a lower-triangular chunk matrix whose rows are in tile order
+// (row slot 16 u + r) and whose columns are natural: fragment (u, s) covers row
+// tile u and columns 32 s .. 32 s + 31; tiles 0 and 1 need s = 0 only.
+__device__ __forceinline__ constexpr int tri_frag(int u, int s) { return u < 2 ? u : 2 * u - 2 + s; }
+
+// Element offset, in the fragment-ordered storage, of the four entries that lane
+// (r, q) holds of block (a, b) (row 16 a + r, columns 16 b + 4 q .. +3).
+__device__ __forceinline__ int tri_offset(int a, int b, int r, int q) {
+  const int slot = tord(16 * a + r);
+  const int u = slot >> 4, rr = slot & 15;
+  const int fq = 2 * (b & 1) + (q >> 1);
+  return tri_frag(u, b >> 1) * 512 + (16 * fq + rr) * 8 + 4 * (q & 1);
 }
 
 // Orders this wave's LDS accesses across its lanes.
@@ -94,13 +120,12 @@ __device__ __forceinline__ int opaque_zero() {
 }
 
 // One chunk held by a prep wave from its first loads to its last LDS write.
-template <int DK, int BV>
+template <int DK>
 struct PrepChunk {
-  using Cfg = WyCfg<DK, BV>;
-  bf16x8 kf[4][Cfg::NKS];   // K rows 16a + r, columns 32s + 8q .. +7 (lane (r, q))
-  bf16x8 qf[4][Cfg::NKS];   // Q, same layout
-  u32x4 vp[Cfg::NVP];       // V pieces: piece lane + 64 j is row / VPR, 8 columns
-  float g, b;               // gate and beta of row = lane (as loaded; masked in gates_gram)
+  bf16x8 kf[4][DK / 32];    // K rows 16a + r, columns 32s + 8q .. +7 (lane (r, q))
+  bf16x8 qf[4][DK / 32];    // Q, same layout
+  float g;                  // gate of row = lane, as loaded (masked in gates_gram)
+  uint32_t braw;            // beta of row = lane, raw storage bits (bf16 or fp32)
   int len;                  // rows of the chunk
   f32x4 ad[4];              // D(A_aa): diagonal blocks of A, slot i = A[16a+4q+i][16a+r]
   f32x4 at[6];              // D(A_ab^T), b < a (order of lower_block without the diagonal)
@@ -112,19 +137,19 @@ struct PrepChunk {
 }  // namespace
 
 template <int DK, int BV>
-__global__ __launch_bounds__(64 * (BV / 16 + 6), 1) void fused_wy_kernel(Problem p, FwdPlan plan) {
+__global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan plan) {
   using Cfg = WyCfg<DK, BV>;
-  static_assert(Cfg::NT == 64 * (BV / 16 + 6), "launch bounds");
+  static_assert(Cfg::NT == 512, "launch bounds");
   using M = Mma<bf16>;
   using frag = bf16x8;
-  constexpr int NCH = Cfg::NCH, NP = Cfg::NP, NKS = Cfg::NKS, NKT = Cfg::NKT;
-  constexpr int KS = Cfg::KS, CS = Cfg::CS, VS = Cfg::VS;
+  constexpr int NCH = Cfg::NCH, NP = Cfg::NP, NKS = Cfg::NKS, NKT = Cfg::NKT, NCT = Cfg::NCT;
+  constexpr int KS = Cfg::KS, VS = Cfg::VS, FR = Cfg::FR;
 
   __shared__ __align__(16) bf16 sK[3][kChunk * KS];   // ring of three: chunk i in slot i % 3
   __shared__ __align__(16) bf16 sQ[2][kChunk * KS];
-  __shared__ __align__(16) bf16 sV[2][kChunk * VS];
-  __shared__ __align__(16) bf16 sT[2][kChunk * CS];
-  __shared__ __align__(16) bf16 sP[2][kChunk * CS];
+  __shared__ __align__(16) bf16 sV[kChunk * VS];      // each chain wave: its own columns
+  __shared__ __align__(16) bf16 sT[2][Cfg::TF * FR];
+  __shared__ __align__(16) bf16 sP[2][Cfg::TF * FR];
   __shared__ __align__(16) float sGam[2][kChunk], sGamS[2][kChunk], sDec[2][kChunk], sBet[2][kChunk];
   __shared__ float sGC[2];
   __shared__ __align__(16) float sGB[NP][2 * kChunk];
@@ -181,12 +206,11 @@ __global__ __launch_bounds__(64 * (BV / 16 + 6), 1) void fused_wy_kernel(Problem
   }
   const int nrun = max(0, c_end - c_start);
 
-  // blocks (0, 1) and (2, 3) of T and P are zero and never written again
-  for (int e = tid; e < 2 * 2 * 16 * 16; e += Cfg::NT) {
-    const int buf = e >> 9, blk = (e >> 8) & 1, rr = (e >> 4) & 15, cc = e & 15;
-    const int row = tord(32 * blk + rr), col = 32 * blk + 16 + cc;
-    sT[buf][row * CS + col] = (bf16)0.f;
-    sP[buf][row * CS + col] = (bf16)0.f;
+  // T and P blocks above the diagonal are zero and never written
+  for (int e = tid; e < 2 * Cfg::TF * FR / 8; e += Cfg::NT) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4*>(&sT[0][0])[e] = z;
+    reinterpret_cast<u32x4*>(&sP[0][0])[e] = z;
   }
 
   const int row_qk = H * DK, row_v = H * dv;   // element strides between tokens
@@ -194,141 +218,248 @@ __global__ __launch_bounds__(64 * (BV / 16 + 6), 1) void fused_wy_kernel(Problem
 
   if (wave < NCH) {
     // =========================== chain wave ===========================
-    const int wcol = wave * 16;                // wave's first column inside the block
-    f32x4 hs[NKT];
+    const int wcol = wave * Cfg::CW;           // wave's first column inside the block
+    f32x4 hs[NKT][NCT];
     {
       const float* src = init == kH0 ? p.h0 + (int64_t)nh * DK * dv
                                      : (init == kBuf ? plan.cp.hstart + (sg * H + h) * DK * dv : nullptr);
 #pragma unroll
       for (int t = 0; t < NKT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          hs[t][i] = src ? src[(int64_t)prow(t, 4 * q + i) * dv + col0 + wcol + r16] : 0.f;
+        for (int j = 0; j < NCT; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            hs[t][j][i] = src ? src[(int64_t)prow(t, 4 * q + i) * dv + col0 + wcol + 16 * j + r16] : 0.f;
     }
     bf16* Ob = reinterpret_cast<bf16*>(p.o) + si.tok0 * row_v + (int64_t)h * dv + col0 + wcol;
+    const bf16* Vb = reinterpret_cast<const bf16*>(p.v) + si.tok0 * row_v + (int64_t)h * dv + col0 + wcol;
     // per-lane indices, re-derived at every step from an opaque zero
-    int cr16 = r16, cq = q;
+    int cr16 = r16, cq = q, clane = lane;
+    // this wave's V columns of chunk i, loaded one step ahead (rows past a partial
+    // chunk's end read its last row: their beta is zero, so they contribute nothing)
+    u32x4 vr[Cfg::NVP];
+    auto load_v = [&](int i) {
+      const int c = c_start + i;
+      const int len = min(kChunk, si.len - c * kChunk);
+      const char* vc = reinterpret_cast<const char*>(Vb + (int64_t)c * kChunk * row_v);
+#pragma unroll
+      for (int j = 0; j < Cfg::NVP; ++j) {
+        const int idx = clane + 64 * j, row = min(idx / Cfg::VPR, len - 1), cv = (idx % Cfg::VPR) * 8;
+        vr[j] = *reinterpret_cast<const u32x4*>(vc + (uint32_t)(row * row_v + cv) * 2u);
+      }
+    };
     // One chunk step; EMIT (compile-time): whether the chunk produces O (lookback
     // chunks do not: no Q product, no O), so each variant is straight-line code.
-    auto chain_step = [&](auto emit_tag, int i) {
+    // O of chunk i leaves through the V columns: at the end of the step each lane puts
+    // its packed O pieces into this wave's V columns (free once V' is formed), and at
+    // the top of the next step, after the V loads have landed, reads them back and
+    // stores them.  The O stores therefore go out after the wait for the V loads, and
+    // that wait (vmcnt counts loads and stores, which may complete out of order, so
+    // any outstanding store makes it wait for everything) only ever covers stores a
+    // step old.  The buffer resource ends after row len - 1: the hardware drops the
+    // stores of rows past a partial chunk's end, so no store sits behind a branch.
+    auto o_slot = [&](int u, int j) {
+      const int row = (cq & 1) ? prow(u + 1, cr16) : prow(u, cr16);
+      return row * VS + wcol + 16 * j + 8 * (cq >> 1);
+    };
+    auto flush_o = [&](int i) {
+      const int c = c_start + i;
+      const int len = min(kChunk, si.len - c * kChunk);
+      const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+          Ob + (int64_t)c * kChunk * row_v, (short)0, len * row_v * 2, kRawBufferFlags);
+#pragma unroll
+      for (int u = 0; u < 4; u += 2) {
+        const int row = (cq & 1) ? prow(u + 1, cr16) : prow(u, cr16);
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(sV + o_slot(u, j));
+          __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, (row * row_v + 16 * j + 8 * (cq >> 1)) * 2, 0, 0);
+        }
+      }
+    };
+    // FLUSH (compile-time): the previous step produced O that is still to be stored.
+    auto chain_step = [&](auto emit_tag, auto flush_tag, int i) {
       constexpr bool EMIT = decltype(emit_tag)::value;
+      if constexpr (decltype(flush_tag)::value) flush_o(i - 1);
       const int b = i & 1;
       const bf16* cK = sK[i % 3];
       const bf16* cQ = sQ[b];
-      const bf16* cV = sV[b];
       const bf16* cT = sT[b];
       const bf16* cP = sP[b];
       const int c = c_start + i;
       const int len = min(kChunk, si.len - c * kChunk);
       auto rows4 = [&](const float* v, int u) { return *reinterpret_cast<const f32x4*>(v + prow(u, 4 * cq)); };
+      // ---- this chunk's V columns into LDS (the next chunk's loads go out once the
+      //      X and Y fragments are dead)
+#pragma unroll
+      for (int j = 0; j < Cfg::NVP; ++j) {
+        const int idx = clane + 64 * j, row = idx / Cfg::VPR, cv = (idx % Cfg::VPR) * 8;
+        *reinterpret_cast<u32x4*>(sV + row * VS + wcol + cv) = vr[j];
+      }
       // ---- X = K h and Y^T = h^T Q^T (transposed: a lane holds four consecutive value
-      //      columns of one query row, the layout of the O store); every K and Q
-      //      fragment read is issued before the first product
-      frag aK[NKS][4], aQ[NKS][4];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          aK[ks][u] = lds_frag(cK, KS, 16 * u + cr16, 32 * ks, cq);
-          if constexpr (EMIT) aQ[ks][u] = lds_frag(cQ, KS, 16 * u + cr16, 32 * ks, cq);
-        }
-      f32x4 X[4], Yp[4];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const frag hb = M::pack(hs[2 * ks], hs[2 * ks + 1]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          X[u] = M::run(aK[ks][u], hb, ks == 0 ? zero4 : X[u]);
-          if constexpr (EMIT) Yp[u] = M::run(hb, aQ[ks][u], ks == 0 ? zero4 : Yp[u]);
-        }
-      }
-      // ---- V' = diag(beta) (V - diag(gamma) X), in place; V read in accumulator layout
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const f32x4 vv = col_read4(cV, VS, prow(u, 4 * cq), wcol + cr16, wcol + 4 * (cr16 & 3));
-        X[u] = rows4(sBet[b], u) * (vv - rows4(sGam[b], u) * X[u]);
-      }
-      // ---- U = T V' (T lower triangular: row tiles 0, 1 need contraction step 0 only)
-      frag wb[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) wb[ks] = M::pack(X[2 * ks], X[2 * ks + 1]);
-      f32x4 U[4];
+      //      columns of one query row, the layout of the O store).  Every K and Q
+      //      fragment feeds one MFMA per column tile.  Software-pipelined over the
+      //      contraction steps: step ks + 1's fragments are read while step ks's
+      //      products run, and the scheduling barriers keep it at that (two steps of
+      //      fragments live, not all of them).
+      f32x4 X[4][NCT], Yp[4][NCT];
       {
-        frag aT[6];   // (u, s): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+        frag fk[2][4], fq[2][4];
+        auto read = [&](int ks) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+          for (int u = 0; u < 4; ++u) {
+            fk[ks & 1][u] = lds_frag(cK, KS, 16 * u + cr16, 32 * ks, cq);
+            if constexpr (EMIT) fq[ks & 1][u] = lds_frag(cQ, KS, 16 * u + cr16, 32 * ks, cq);
+          }
+        };
+        read(0);
 #pragma unroll
-          for (int ks = 0; ks <= (u >> 1); ++ks) aT[u < 2 ? u : 2 * u - 2 + ks] = lds_frag(cT, CS, 16 * u + cr16, 32 * ks, cq);
+        for (int ks = 0; ks < NKS; ++ks) {
+          if (ks + 1 < NKS) read(ks + 1);
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+          for (int j = 0; j < NCT; ++j) {
+            const frag hb = M::pack(hs[2 * ks][j], hs[2 * ks + 1][j]);
 #pragma unroll
-          for (int ks = 0; ks <= (u >> 1); ++ks)
-            U[u] = M::run(aT[u < 2 ? u : 2 * u - 2 + ks], wb[ks], ks == 0 ? zero4 : U[u]);
-      }
-      frag ubp[2], ubd[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if constexpr (EMIT) ubp[ks] = M::pack(U[2 * ks], U[2 * ks + 1]);
-        ubd[ks] = M::pack(U[2 * ks] * rows4(sDec[b], 2 * ks), U[2 * ks + 1] * rows4(sDec[b], 2 * ks + 1));
-      }
-      // ---- h <- gamma_last h + K^T (diag(d) U); K^T fragments by LDS transpose reads
-      const float gC = sGC[b];
-#pragma unroll
-      for (int t0 = 0; t0 < NKT; t0 += 2) {
-        frag aKt[2][2];
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const int t = t0 + dt;
-          const int own = prow(t, cr16), supply = prow(t, 4 * (cr16 & 3));
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-            aKt[dt][ks] = col_frag(cK, KS, 32 * ks + 4 * cq, 32 * ks + 16 + 4 * cq, own, supply);
+            for (int u = 0; u < 4; ++u) {
+              X[u][j] = M::run(fk[ks & 1][u], hb, ks == 0 ? zero4 : X[u][j]);
+              if constexpr (EMIT) Yp[u][j] = M::run(hb, fq[ks & 1][u], ks == 0 ? zero4 : Yp[u][j]);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
+      }
+      load_v(min(i + 1, nrun - 1));
+      // ---- V' = diag(beta) (V - diag(gamma) X), in place; V read in accumulator layout
+      wave_lds_sync();
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) hs[t0 + dt] *= gC;
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
+        for (int j = 0; j < NCT; ++j) {
+          const int col = wcol + 16 * j;
+          const f32x4 vv = col_read4(sV, VS, prow(u, 4 * cq), col + cr16, col + 4 * (cr16 & 3));
+          X[u][j] = rows4(sBet[b], u) * (vv - rows4(sGam[b], u) * X[u][j]);
+        }
+      // ---- U = T V' (T lower triangular: row tiles 0, 1 need contraction step 0 only)
+      f32x4 U[4][NCT];
+      {
+        frag aT[6];
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) hs[t0 + dt] = M::run(aKt[dt][ks], ubd[ks], hs[t0 + dt]);
+        for (int f = 0; f < 6; ++f) aT[f] = *reinterpret_cast<const frag*>(cT + f * FR + 8 * clane);
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) {
+          frag wb[2];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) wb[ks] = M::pack(X[2 * ks][j], X[2 * ks + 1][j]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int ks = 0; ks <= (u >> 1); ++ks)
+              U[u][j] = M::run(aT[tri_frag(u, ks)], wb[ks], ks == 0 ? zero4 : U[u][j]);
+        }
+      }
+      frag ubp[2][NCT], ubd[2][NCT];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) {
+          if constexpr (EMIT) ubp[ks][j] = M::pack(U[2 * ks][j], U[2 * ks + 1][j]);
+          ubd[ks][j] = M::pack(U[2 * ks][j] * rows4(sDec[b], 2 * ks), U[2 * ks + 1][j] * rows4(sDec[b], 2 * ks + 1));
+        }
+      // ---- h <- gamma_last h + K^T (diag(d) U); K^T fragments by LDS transpose reads,
+      //      pipelined over pairs of dk tiles like the X and Y products
+      const float gC = sGC[b];
+      {
+        frag kt[2][2][2];   // [buffer][tile of the pair][contraction step]
+        auto read = [&](int t0) {
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt) {
+            const int t = t0 + dt;
+            const int own = prow(t, cr16), supply = prow(t, 4 * (cr16 & 3));
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+              kt[(t0 >> 1) & 1][dt][ks] = col_frag(cK, KS, 32 * ks + 4 * cq, 32 * ks + 16 + 4 * cq, own, supply);
+          }
+        };
+        read(0);
+#pragma unroll
+        for (int t0 = 0; t0 < NKT; t0 += 2) {
+          if (t0 + 2 < NKT) read(t0 + 2);
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int j = 0; j < NCT; ++j) {
+              hs[t0 + dt][j] *= gC;
+#pragma unroll
+              for (int ks = 0; ks < 2; ++ks)
+                hs[t0 + dt][j] = M::run(kt[(t0 >> 1) & 1][dt][ks], ubd[ks][j], hs[t0 + dt][j]);
+            }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       // ---- O = scale diag(gamma) Q h + P U, stored 16 bytes per lane
       if constexpr (EMIT) {
         frag aP[6];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int f = 0; f < 6; ++f) aP[f] = *reinterpret_cast<const frag*>(cP + f * FR + 8 * clane);
 #pragma unroll
-          for (int ks = 0; ks <= (u >> 1); ++ks) aP[u < 2 ? u : 2 * u - 2 + ks] = lds_frag(cP, CS, 16 * u + cr16, 32 * ks, cq);
+        for (int u = 0; u < 4; ++u) {
+          const float gs = sGamS[b][prow(u, cr16)];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) Yp[u] = Yp[u] * sGamS[b][prow(u, cr16)];
+          for (int j = 0; j < NCT; ++j) {
+            Yp[u][j] = Yp[u][j] * gs;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int ks = 0; ks <= (u >> 1); ++ks) Yp[u] = M::run(ubp[ks], aP[u < 2 ? u : 2 * u - 2 + ks], Yp[u]);
-        bf16* ob = Ob + (int64_t)c * kChunk * row_v;
+            for (int ks = 0; ks <= (u >> 1); ++ks) Yp[u][j] = M::run(ubp[ks][j], aP[tri_frag(u, ks)], Yp[u][j]);
+          }
+        }
         // for the tile pair (u, u+1), v_permlane16_swap hands lane group q^1 the other
         // group's four columns: an even group then holds eight consecutive columns of
         // tile u's row, an odd group those of tile u+1's row
 #pragma unroll
-        for (int u = 0; u < 4; u += 2) {
-          const int row = (cq & 1) ? prow(u + 1, cr16) : prow(u, cr16);
-          const uint2 a = pack_bf16x4(Yp[u]), bb = pack_bf16x4(Yp[u + 1]);
-          const auto sx = __builtin_amdgcn_permlane16_swap(a.x, bb.x, false, false);
-          const auto sy = __builtin_amdgcn_permlane16_swap(a.y, bb.y, false, false);
-          const u32x4 v = {sx[0], sy[0], sx[1], sy[1]};
-          if (row < len) *reinterpret_cast<u32x4*>(ob + row * row_v + 8 * (cq >> 1)) = v;
-        }
+        for (int u = 0; u < 4; u += 2)
+#pragma unroll
+          for (int j = 0; j < NCT; ++j) {
+            const uint2 a = pack_bf16x4(Yp[u][j]), bb = pack_bf16x4(Yp[u + 1][j]);
+            const auto sx = __builtin_amdgcn_permlane16_swap(a.x, bb.x, false, false);
+            const auto sy = __builtin_amdgcn_permlane16_swap(a.y, bb.y, false, false);
+            const u32x4 v = {sx[0], sy[0], sx[1], sy[1]};
+            *reinterpret_cast<u32x4*>(sV + o_slot(u, j)) = v;
+          }
       }
     };
     // the prep waves fill the first buffer sets during NP + 1 steps
+    if (nrun > 0) load_v(0);
     for (int s = -NP - 1; s < 0; ++s) __syncthreads();
     __builtin_amdgcn_s_setprio(1);
-    for (int i = 0; i < nrun; ++i) {
+    auto refresh_lanes = [&]() {
       const int z = opaque_zero();
       cr16 = r16 + z;
       cq = q + z;
-      if (c_start + i >= c_out) chain_step(std::true_type{}, i);
-      else chain_step(std::false_type{}, i);
+      clane = lane + z;
+    };
+    // lookback chunks (no O) come first; one loop per variant keeps each loop body
+    // straight-line for the register allocator.  The first output step (nothing to
+    // store yet) is peeled; the last one's O is stored after the loop.
+    const int nlook = min(nrun, c_out - c_start);
+    int i = 0;
+    for (; i < nlook; ++i) {
+      refresh_lanes();
+      chain_step(std::false_type{}, std::false_type{}, i);
       __syncthreads();
+    }
+    if (i < nrun) {
+      refresh_lanes();
+      chain_step(std::true_type{}, std::false_type{}, i);
+      __syncthreads();
+      ++i;
+    }
+    for (; i < nrun; ++i) {
+      refresh_lanes();
+      chain_step(std::true_type{}, std::true_type{}, i);
+      __syncthreads();
+    }
+    if (nrun > nlook) {
+      refresh_lanes();
+      flush_o(nrun - 1);
     }
     __builtin_amdgcn_s_setprio(0);
     if (last_seg && p.hT) {
@@ -336,7 +467,9 @@ __global__ __launch_bounds__(64 * (BV / 16 + 6), 1) void fused_wy_kernel(Problem
 #pragma unroll
       for (int t = 0; t < NKT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(int64_t)prow(t, 4 * q + i) * dv + r16] = hs[t][i];
+        for (int j = 0; j < NCT; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[(int64_t)prow(t, 4 * q + i) * dv + 16 * j + r16] = hs[t][j][i];
     }
   } else {
     // =========================== prep wave ===========================
@@ -347,11 +480,10 @@ __global__ __launch_bounds__(64 * (BV / 16 + 6), 1) void fused_wy_kernel(Problem
     float* sTd = sInv + 4 * Cfg::ABS;          // diagonal T blocks, column-major, stride TCS
     const bf16* Kb = reinterpret_cast<const bf16*>(p.k) + si.tok0 * row_qk + (int64_t)h * DK;
     const bf16* Qb = reinterpret_cast<const bf16*>(p.q) + si.tok0 * row_qk + (int64_t)h * DK;
-    const bf16* Vb = reinterpret_cast<const bf16*>(p.v) + si.tok0 * row_v + (int64_t)h * dv + col0;
     const float* Gb = p.g + si.tok0 * H + h;
     const int bsz = p.beta_bf16 ? 2 : 4;
     const char* Bb = reinterpret_cast<const char*>(p.beta) + (si.tok0 * H + h) * bsz;
-    PrepChunk<DK, BV> R;
+    PrepChunk<DK> R;
     // per-lane indices used below, re-derived at every pass of the step loop from an
     // opaque zero: their address arithmetic stays inside the loop (a few VALU
     // operations) instead of being hoisted out and spilled to scratch
@@ -360,8 +492,8 @@ __global__ __launch_bounds__(64 * (BV / 16 + 6), 1) void fused_wy_kernel(Problem
     // Rows past a partial chunk's end read the chunk's last row instead (always inside
     // the sequence) and are left as they are: their beta and g are zeroed in
     // gates_gram, which zeroes every contribution of such a row (A's rows, V', U), and
-    // their O rows are never stored.  No value is selected right after its load, so
-    // issuing a batch never waits for it.
+    // their O rows are never stored.  Nothing is computed from a loaded value until a
+    // later phase, so issuing a batch of loads never waits for it.
     auto row_off = [&](int a, int len) { return (uint32_t)(min(16 * a + lr16, len - 1) * row_qk + 8 * lq) * 2u; };
     // ---- K, g and beta of chunk i (for step 1)
     auto load_kgb = [&](int i) {
@@ -372,7 +504,8 @@ __global__ __launch_bounds__(64 * (BV / 16 + 6), 1) void fused_wy_kernel(Problem
       const char* kc = reinterpret_cast<const char*>(Kb + t0 * row_qk);
       const int64_t ti = (t0 + min(llane, len - 1)) * H;
       R.g = Gb[ti];
-      R.b = p.beta_bf16 ? (float)reinterpret_cast<const bf16*>(Bb)[ti] : reinterpret_cast<const float*>(Bb)[ti];
+      if (p.beta_bf16) R.braw = reinterpret_cast<const uint16_t*>(Bb)[ti];
+      else R.braw = reinterpret_cast<const uint32_t*>(Bb)[ti];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const uint32_t off = row_off(a, len);
@@ -380,8 +513,8 @@ __global__ __launch_bounds__(64 * (BV / 16 + 6), 1) void fused_wy_kernel(Problem
         for (int ks = 0; ks < NKS; ++ks) R.kf[a][ks] = *reinterpret_cast<const frag*>(kc + off + 64u * ks);
       }
     };
-    // ---- K again, Q and V of chunk i (for P and the LDS writes)
-    auto load_kqv = [&](int i) {
+    // ---- K again and Q of chunk i (for P and the LDS writes)
+    auto load_kq = [&](int i) {
       const int c = c_start + i;
       const int len = R.len;
       const int64_t t0 = (int64_t)c * kChunk;
@@ -396,21 +529,16 @@ __global__ __launch_bounds__(64 * (BV / 16 + 6), 1) void fused_wy_kernel(Problem
           R.qf[a][ks] = *reinterpret_cast<const frag*>(qc + off + 64u * ks);
         }
       }
-      const char* vc = reinterpret_cast<const char*>(Vb + t0 * row_v);
-#pragma unroll
-      for (int j = 0; j < Cfg::NVP; ++j) {
-        const int idx = llane + 64 * j, row = min(idx / Cfg::VPR, len - 1), cv = (idx % Cfg::VPR) * 8;
-        R.vp[j] = *reinterpret_cast<const u32x4*>(vc + (uint32_t)(row * row_v + cv) * 2u);
-      }
     };
 
     // ---- gates, the Gram tiles of K K^T, and A = strict_lower(diag(beta) K K^T * Gamma)
     //      in registers: diagonal blocks D(A_aa), off-diagonal blocks transposed D(A_ab^T)
     auto gates_gram = [&]() {
       const bool real = llane < R.len;   // rows past the chunk end: g = 0, beta = 0
+      const float bv = p.beta_bf16 ? __uint_as_float(R.braw << 16) : __uint_as_float(R.braw);
       const float G = wave_inclusive_scan_dpp(real ? R.g : 0.f);
       sG[llane] = G;
-      sB[llane] = real ? R.b : 0.f;
+      sB[llane] = real ? bv : 0.f;
       f32x4 gd[4], go[6];   // D(K_a K_a^T), D(K_b K_a^T) for b < a
 #pragma unroll
       for (int k = 0; k < 10; ++k) {
@@ -518,17 +646,9 @@ __global__ __launch_bounds__(64 * (BV / 16 + 6), 1) void fused_wy_kernel(Problem
       R.tb[9] = pack_bf16x4(R.tdt[3]);
     };
 
-    // ---- K of chunk i into its ring slot i % 3 (free from step i - 2 on: the chain
-    //      read it last for chunk i - 3), then P = scale (Q K^T) * Gamma, lower blocks;
-    //      lane (r, q) of block (a, b): query 16a + r, keys 16b + 4q .. +3 (as K_b Q_a^T)
-    auto write_k_p = [&](int i, bool withq) {
-      bf16* dst = sK[i % 3];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int lr = tord(16 * a + lr16);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) *reinterpret_cast<frag*>(dst + lr * KS + 32 * ks + 8 * lq) = R.kf[a][ks];
-      }
+    // ---- P = scale (Q K^T) * Gamma, lower blocks; lane (r, q) of block (a, b): query
+    //      16a + r, keys 16b + 4q .. +3 (as K_b Q_a^T)
+    auto p_tiles = [&](bool withq) {
       if (withq) {
 #pragma unroll
         for (int k = 0; k < 10; ++k) {
@@ -551,7 +671,19 @@ __global__ __launch_bounds__(64 * (BV / 16 + 6), 1) void fused_wy_kernel(Problem
       }
     };
 
-    // ---- Q, V, T, P and the gate tables of chunk i, into buffer set i % 2
+    // ---- K of chunk i into its ring slot i % 3 (free from step i - 2 on: the chain
+    //      read it last for chunk i - 3)
+    auto write_k = [&](int i) {
+      bf16* dst = sK[i % 3];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int lr = tord(16 * a + lr16);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) *reinterpret_cast<frag*>(dst + lr * KS + 32 * ks + 8 * lq) = R.kf[a][ks];
+      }
+    };
+
+    // ---- Q, T, P and the gate tables of chunk i, into buffer set i % 2
     auto write = [&](int i, bool withq) {
       const int b = i & 1;
       if (withq) {
@@ -563,15 +695,10 @@ __global__ __launch_bounds__(64 * (BV / 16 + 6), 1) void fused_wy_kernel(Problem
         }
       }
 #pragma unroll
-      for (int j = 0; j < Cfg::NVP; ++j) {
-        const int idx = llane + 64 * j, row = idx / Cfg::VPR, cv = (idx % Cfg::VPR) * 8;
-        *reinterpret_cast<u32x4*>(sV[b] + row * VS + cv) = R.vp[j];
-      }
-#pragma unroll
       for (int k = 0; k < 10; ++k) {
         int a, bb;
         lower_block(k, a, bb);
-        const int off = tord(16 * a + lr16) * CS + 16 * bb + 4 * lq;
+        const int off = tri_offset(a, bb, lr16, lq);
         *reinterpret_cast<uint2*>(sT[b] + off) = R.tb[k];
         if (withq) *reinterpret_cast<uint2*>(sP[b] + off) = R.pb[k];
       }
@@ -587,19 +714,16 @@ __global__ __launch_bounds__(64 * (BV / 16 + 6), 1) void fused_wy_kernel(Problem
 
     // Step schedule (step s: the chain computes chunk s; s < 0: preparation only).
     // This wave owns chunks i = pw, pw + NP, ...; for chunk i:
-    //   step i - 7: K, g, beta loads issued (right after the previous chunk's writes)
-    //   step i - 6: they land
-    //   step i - 5: gates, Gram tiles, A in registers
-    //   step i - 4: diagonal-block substitution (the shared scratch)
-    //   step i - 3: doubling -> T; K, Q and V loads issued
-    //   step i - 2: K into its ring slot; P
-    //   step i - 1: Q, V, T, P and the gate tables into buffer set i % 2; K, g, beta
-    //               loads of chunk i + NP issued
+    //   step i - 5: K, g, beta loads issued (for i = pw; later chunks: at step i - 6)
+    //   step i - 4: gates, Gram tiles, A in registers; K and Q loads issued
+    //   step i - 3: diagonal-block substitution (the shared scratch), doubling -> T
+    //   step i - 2: P; K into its ring slot; K, g, beta loads of chunk i + NP issued
+    //   step i - 1: Q, T, P and the gate tables into buffer set i % 2
     // Written as one straight pass per owned chunk so that the compiler sees which
     // registers each phase holds; loads past the last chunk reload the last chunk
     // (unused), so every phase defines the same registers.  Every wave executes one
     // barrier per step, nrun + NP + 1 in all.
-    static_assert(NP == 6, "one pass of the loop below is the NP = 6 steps of one owned chunk");
+    static_assert(NP == 4, "one pass of the loop below is the NP = 4 steps of one owned chunk");
     auto refresh_lanes = [&]() {
       const int z = opaque_zero();
       lr16 = r16 + z;
@@ -615,23 +739,20 @@ __global__ __launch_bounds__(64 * (BV / 16 + 6), 1) void fused_wy_kernel(Problem
     for (int i = pw; i < nrun; i += NP) {
       const bool withq = c_start + i >= c_out;
       refresh_lanes();
-      __syncthreads();     // s == i - 6: the loads land
-      ++s;
-      gates_gram();        // s == i - 5
+      gates_gram();        // s == i - 4
+      load_kq(i);
       __syncthreads();
       ++s;
-      solve_diag();        // s == i - 4
+      solve_diag();        // s == i - 3
+      doubling();
       __syncthreads();
       ++s;
-      doubling();          // s == i - 3
-      load_kqv(i);
-      __syncthreads();
-      ++s;
-      write_k_p(i, withq); // s == i - 2
+      p_tiles(withq);      // s == i - 2
+      write_k(i);
+      load_kgb(min(i + NP, nrun - 1));
       __syncthreads();
       ++s;
       write(i, withq);     // s == i - 1
-      load_kgb(min(i + NP, nrun - 1));
       __syncthreads();
       ++s;
     }
@@ -639,10 +760,10 @@ __global__ __launch_bounds__(64 * (BV / 16 + 6), 1) void fused_wy_kernel(Problem
   }
 }
 
-// 1-D grid of ceil(units / 8) * 8 * (dv / BV) workgroups (see the decode in the kernel).
-template <int DK>
+// 1-D grid of ceil(units / 8) * 8 workgroups (see the decode in the kernel); one
+// workgroup covers all dv value columns.
+template <int DK, int BV>
 static hipError_t launch_wy_dk(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev) {
-  constexpr int BV = 32;
   using Cfg = WyCfg<DK, BV>;
   const int ncb = p.dv / BV;
   const int64_t groups = (plan.units + 7) / 8;
@@ -658,7 +779,9 @@ hipError_t launch_fused_wy(const Problem& p, const FwdPlan& plan, hipStream_t s,
     return hipSuccess;
   }
   if (!p.qkv_bf16) return hipErrorInvalidValue;
-  return p.dk == 128 ? launch_wy_dk<128>(p, plan, s, ev) : launch_wy_dk<64>(p, plan, s, ev);
+  if (p.dk == 128)
+    return p.dv == 128 ? launch_wy_dk<128, 128>(p, plan, s, ev) : launch_wy_dk<128, 64>(p, plan, s, ev);
+  return p.dv == 128 ? launch_wy_dk<64, 128>(p, plan, s, ev) : launch_wy_dk<64, 64>(p, plan, s, ev);
 }
 
 }  // namespace gdn

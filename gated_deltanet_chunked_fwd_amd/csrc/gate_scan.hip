@@ -121,11 +121,15 @@ hipError_t launch_plan_tables(const int32_t* cu, int N, int seg_chunks, int32_t*
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s) {
-  if (p.total_chunks == 0) return hipSuccess;
+hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s, KernelEvents ev) {
+  if (p.total_chunks == 0) {
+    ev.record_empty(s);
+    return hipSuccess;
+  }
   const int64_t blocks = p.total_chunks * ((p.H + 3) / 4);
   if (blocks > kMaxDispatchItems / 256) return hipErrorInvalidConfiguration;
-  chunk_gate_sums_kernel<<<(unsigned)blocks, 256, 0, s>>>(p, csum);
+  hipExtLaunchKernelGGL(chunk_gate_sums_kernel, dim3((unsigned)blocks), dim3(256), 0, s, ev.start, ev.stop, 0,
+                        p, csum);
   return hipGetLastError();
 }
 

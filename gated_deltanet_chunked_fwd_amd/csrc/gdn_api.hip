@@ -122,8 +122,8 @@ int validate_shape(const gdn_shape* s) {
 
 int validate_opts(const gdn_opts* o) {
   if (!o) return GDN_OK;
-  if (o->value_block != 0 && o->value_block != 32 && o->value_block != 64 && o->value_block != 128)
-    return GDN_ERR_ARG;
+  if (o->value_block != 0 && o->value_block != 64 && o->value_block != 128) return GDN_ERR_ARG;
+  if (o->one_pass < -1 || o->one_pass > 1) return GDN_ERR_ARG;
   if (o->force_segment_chunks < 0 || o->window_max_chunks < 0 ||
       o->window_max_chunks > kWindowMaxCap)
     return GDN_ERR_ARG;
@@ -222,8 +222,9 @@ Plan plan_uncached(const gdn_shape* s, const gdn_opts* o) {
     P.max_chunks = std::max(P.max_chunks, c);
   }
   const int vb_req = o ? o->value_block : 0;
-  P.wy = s->qkv_dtype == GDN_BF16 && vb_req == 32;
-  P.value_block = P.wy ? 32 : (s->qkv_dtype == GDN_BF16 && s->dv % 128 == 0 && vb_req != 64) ? 128 : 64;
+  const int one_pass = o ? o->one_pass : 0;
+  P.wy = s->qkv_dtype == GDN_BF16 && (one_pass == 1 || (one_pass == 0 && vb_req == 0));
+  P.value_block = P.wy ? (int)s->dv : (s->qkv_dtype == GDN_BF16 && s->dv % 128 == 0 && vb_req != 64) ? 128 : 64;
   P.pass1_block = vb_req == 128 ? 128 : 64;
   P.wmax = (o && o->window_max_chunks > 0) ? o->window_max_chunks : kWindowMaxCap;
   P.log_eps = (o && o->window_log_eps != 0.f) ? o->window_log_eps : (float)std::log(0x1p-24);
@@ -231,8 +232,6 @@ Plan plan_uncached(const gdn_shape* s, const gdn_opts* o) {
   if (!(o && o->no_split) && P.max_chunks > 1) {
     if (o && o->force_segment_chunks > 0) {
       L = o->force_segment_chunks;
-    } else if (P.wy) {
-      // one-pass plans run unsplit unless a segment length is forced
     } else {
       // T auto-CP: cost(L) = lambda1 * (pass-3 makespan in chunk steps) + lambda2 *
       // (merge steps of the longest sequence); the makespan is simulated (see
@@ -289,7 +288,7 @@ Plan plan_uncached(const gdn_shape* s, const gdn_opts* o) {
 struct PlanKey {
   int64_t dims[6] = {0, 0, 0, 0, 0, 0};
   int32_t dtypes[2] = {0, 0};
-  int32_t no_split = 0, force_segment_chunks = 0, window_max_chunks = 0, value_block = 0;
+  int32_t no_split = 0, force_segment_chunks = 0, window_max_chunks = 0, value_block = 0, one_pass = 0;
   float window_log_eps = 0.f, lambda1_us = 0.f, lambda2_us = 0.f;
   int cus = 0;
   bool packed = false;
@@ -306,6 +305,7 @@ struct PlanKey {
     force_segment_chunks = r.force_segment_chunks;
     window_max_chunks = r.window_max_chunks;
     value_block = r.value_block;
+    one_pass = r.one_pass;
     window_log_eps = r.window_log_eps;
     lambda1_us = r.lambda1_us;
     lambda2_us = r.lambda2_us;
@@ -319,6 +319,7 @@ struct PlanKey {
            dtypes[1] == k.dtypes[1] && no_split == k.no_split &&
            force_segment_chunks == k.force_segment_chunks &&
            window_max_chunks == k.window_max_chunks && value_block == k.value_block &&
+           one_pass == k.one_pass &&
            window_log_eps == k.window_log_eps && lambda1_us == k.lambda1_us &&
            lambda2_us == k.lambda2_us && cus == k.cus && packed == k.packed && cu == k.cu;
   }
@@ -427,7 +428,7 @@ bool grids_fit(const gdn_shape* s, const Plan& P) {
   if (!fits(P.total_chunks * ((H + 3) / 4), 256)) return false;                  // K1
   const int64_t unit_groups = (P.total_segs * H + 7) / 8;
   if (!fits(unit_groups * 8, s->dv * 4)) return false;                           // pass 3
-  if (P.wy && !fits(unit_groups * 8, s->dv / 32 * 512)) return false;            // one pass
+  if (P.wy && !fits(unit_groups * 8, 512)) return false;                          // one pass
   if (!P.split) return true;
   if (!fits(nh, P.max_chunks > 512 ? 1024 : 256)) return false;                   // gate scan
   if (!fits(unit_groups * 8, (s->dv + s->dk) * 4)) return false;                  // pass 1
@@ -484,13 +485,18 @@ int run_stages(int first, int last, const void* q, const void* k, const void* v,
 
   void* tmat = ws + L.tmat;
   float* csum = P.split ? reinterpret_cast<float*>(ws + L.csum) : nullptr;
+  const bool forced = opts && opts->force_correction;
+  // One-pass plans read no T; a split one runs the chunk inverse only for the heads
+  // that take pass 1 (no admissible window), so it goes after the gate scan: the
+  // inverse stage then forms the chunk gate sums alone.
+  const bool k1_after_scan = P.wy && P.split && !forced;
   if (runs(GDN_STAGE_INVERSE)) {
-    if (!runs_k1(P)) {
-      stage_events(opts, GDN_STAGE_INVERSE).record_empty(stream);
-    } else if (gdn::launch_chunk_inverse(p, tmat, csum, false, stream,
-                                         stage_events(opts, GDN_STAGE_INVERSE)) != hipSuccess) {
-      return GDN_ERR_HIP;
-    }
+    const gdn::KernelEvents ev = stage_events(opts, GDN_STAGE_INVERSE);
+    hipError_t e = hipSuccess;
+    if (!runs_k1(P)) ev.record_empty(stream);
+    else if (k1_after_scan) e = gdn::launch_chunk_gate_sums(p, csum, stream, ev);
+    else e = gdn::launch_chunk_inverse(p, tmat, csum, false, stream, ev);
+    if (e != hipSuccess) return GDN_ERR_HIP;
   }
 
   gdn::FwdPlan plan;
@@ -507,7 +513,7 @@ int run_stages(int first, int last, const void* q, const void* k, const void* v,
     plan.cp.best = best;
     plan.cp.wmax = P.wmax;
     plan.cp.thr = P.log_eps - kWindowMargin;
-    plan.cp.force_correction = opts ? opts->force_correction : 0;
+    plan.cp.force_correction = forced ? 1 : 0;
     plan.cp.sstar = reinterpret_cast<float*>(ws + L.sstar);
     plan.cp.mcorr = ws + L.mcorr;
     plan.cp.hstart = reinterpret_cast<float*>(ws + L.hstart);
@@ -521,9 +527,18 @@ int run_stages(int first, int last, const void* q, const void* k, const void* v,
     if (runs(GDN_STAGE_CP_PASS1)) {
       gdn::FwdPlan p1 = plan;
       p1.mode = gdn::kPass1;
-      if (gdn::launch_fused_forward(p, p1, stream, stage_events(opts, GDN_STAGE_CP_PASS1)) !=
-          hipSuccess)
-        return GDN_ERR_HIP;
+      gdn::KernelEvents ev = stage_events(opts, GDN_STAGE_CP_PASS1);
+      if (k1_after_scan) {
+        gdn::HeadFilter only;
+        only.best = best;
+        only.wmax = P.wmax;
+        only.thr = plan.cp.thr;
+        if (gdn::launch_chunk_inverse(p, tmat, nullptr, false, stream, gdn::KernelEvents{ev.start, nullptr},
+                                      only) != hipSuccess)
+          return GDN_ERR_HIP;
+        ev.start = nullptr;
+      }
+      if (gdn::launch_fused_forward(p, p1, stream, ev) != hipSuccess) return GDN_ERR_HIP;
     }
     if (runs(GDN_STAGE_CP_MERGE)) {
       const int max_steps = (int)((P.max_chunks + P.seg_chunks - 1) / P.seg_chunks - 1);
@@ -558,6 +573,13 @@ int64_t gdn_plan_segment_chunks(const gdn_shape* shape, const gdn_opts* opts) {
   if (rc == GDN_OK) rc = validate_opts(opts);
   if (rc != GDN_OK) return rc;
   return make_plan(shape, opts).seg_chunks;
+}
+
+int gdn_plan_one_pass(const gdn_shape* shape, const gdn_opts* opts) {
+  int rc = validate_shape(shape);
+  if (rc == GDN_OK) rc = validate_opts(opts);
+  if (rc != GDN_OK) return rc;
+  return make_plan(shape, opts).wy ? 1 : 0;
 }
 
 int gdn_chunk_fwd_workspace_bytes(const gdn_shape* shape, const gdn_opts* opts, size_t* bytes) {

@@ -77,7 +77,6 @@ hipError_t launch_plan_tables(const int32_t* cu, int N, int seg_chunks, int32_t*
                               int32_t* seg_off, int32_t* seg_order, hipStream_t s);
 // Packed inputs of at most this many sequences get a longest-first segment order.
 constexpr int kSegOrderMaxSeqs = 1024;
-hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s);
 // Optional start / stop events of a single-kernel launch, recorded from the kernel's
 // own dispatch (hipExtLaunchKernel): timing a stage this way adds no packets to the
 // stream, where a separate event record costs a few microseconds of idle GPU.
@@ -89,6 +88,7 @@ struct KernelEvents {
     if (stop) (void)hipEventRecord(stop, s);
   }
 };
+hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s, KernelEvents ev = {});
 hipError_t launch_gate_scan(const Problem& p, const float* csum, int64_t max_chunks, int wmax,
                             uint32_t* best, hipStream_t s, KernelEvents ev = {});
 hipError_t launch_gate_finalize(const Problem& p, const uint32_t* best, int wmax, float thr,
@@ -96,11 +96,18 @@ hipError_t launch_gate_finalize(const Problem& p, const uint32_t* best, int wmax
 // max_steps: the most segment boundaries of any sequence (segments - 1).
 hipError_t launch_cp_merge(const Problem& p, const FwdPlan& plan, int max_steps, hipStream_t s,
                            KernelEvents ev = {});
+// Restricts the chunk inverse to the heads without an admissible lookback window
+// (window_of(best, ...) == 0); best == nullptr: every head.
+struct HeadFilter {
+  const uint32_t* best = nullptr;
+  int wmax = 0;
+  float thr = 0.f;
+};
 // csum (nullable): [total_chunks, H] per-chunk gate sums, written on the side.
 // full = false: T's zero upper-right 32 x 32 quadrant is left unwritten (the fused
 // forward never reads it).
 hipError_t launch_chunk_inverse(const Problem& p, void* t_out, float* csum, bool full,
-                                hipStream_t s, KernelEvents ev = {});
+                                hipStream_t s, KernelEvents ev = {}, HeadFilter only = {});
 // One pass, bf16 only: steps 1-4 with the inverse formed in the kernel (fused_wy.hip);
 // kPass3 plans only, 32 value columns per workgroup.
 hipError_t launch_fused_wy(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev = {});

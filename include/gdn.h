@@ -85,8 +85,13 @@ typedef struct gdn_opts {
   int32_t window_max_chunks;    /* longest lookback window in chunks, 1..16; 0 -> 16 */
   float lambda1_us;             /* planner: cost of one chunk step; 0 -> built in */
   float lambda2_us;             /* planner: cost of one merge step; 0 -> built in */
-  int32_t value_block;          /* value columns per workgroup of the fused kernel: 32, 64 or
-                                   128; 0 -> planner's choice */
+  int32_t value_block;          /* two-kernel path: value columns per workgroup of the fused
+                                   forward, 64 or 128; 0 -> planner's choice */
+  /* 1: the one-pass forward (bf16 only; each workgroup forms its chunks' inverses
+   *    itself and covers all dv value columns), -1: never (the chunk inverse runs
+   *    as its own kernel and the fused forward reads it), 0: planner (bf16 -> one
+   *    pass, fp32 -> two kernels). */
+  int32_t one_pass;
   /* Optional timing hook: NULL, or an array of 2 * GDN_NUM_STAGES events created by
    * the caller (hipEventCreate).  For every stage that runs, stage_events[2*s] and
    * stage_events[2*s+1] are recorded on `stream` from the dispatch of the stage's
@@ -259,6 +264,11 @@ int gdn_gate_scan_workspace_bytes(const gdn_shape* shape, size_t* bytes);
  * sequence's chunk count, or the planner's own choice) the value is 1073741823
  * (INT_MAX / 2), so every sequence is one segment. */
 int64_t gdn_plan_segment_chunks(const gdn_shape* shape, const gdn_opts* opts);
+
+/* 1 if gdn_chunk_fwd runs the one-pass forward for this problem and options (the
+ * chunk inverses formed inside the forward kernel), 0 if it runs the chunk inverse
+ * and the fused forward as separate kernels, or a negative status. */
+int gdn_plan_one_pass(const gdn_shape* shape, const gdn_opts* opts);
 
 /* Total number of chunks (sum over sequences of ceil(len/64)), or a negative status. */
 int64_t gdn_total_chunks(const gdn_shape* shape);

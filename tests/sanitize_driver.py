@@ -46,7 +46,7 @@ def abi(path):
         s = shape(**kw)
         o = A.make_opts(no_split=int(rng.random() < 0.1), force_segment_chunks=int(rng.choice([0, 0, 1, 3, 16])),
                         force_correction=int(rng.random() < 0.2), window_max_chunks=int(rng.choice([0, 1, 16])),
-                        value_block=int(rng.choice([0, 64, 128])), lambda1_us=float(rng.choice([0.0, 1.0])),
+                        value_block=int(rng.choice([0, 64, 128])), one_pass=int(rng.choice([-1, 0, 1])), lambda1_us=float(rng.choice([0.0, 1.0])),
                         lambda2_us=float(rng.choice([0.0, 5.0])))
         for opts in (None, ctypes.byref(o)):
             nb = ctypes.c_size_t(0)
@@ -89,7 +89,7 @@ def abi(path):
         nb = ctypes.c_size_t(0)
         assert lib.gdn_chunk_fwd_workspace_bytes(ctypes.byref(s2), None, ctypes.byref(nb)) < 0
         assert lib.gdn_plan_segment_chunks(ctypes.byref(s2), None) < 0
-    for opts in [A.make_opts(value_block=96), A.make_opts(force_segment_chunks=-2),
+    for opts in [A.make_opts(value_block=96), A.make_opts(value_block=32), A.make_opts(one_pass=2), A.make_opts(force_segment_chunks=-2),
                  A.make_opts(window_max_chunks=17), A.make_opts(window_log_eps=1.0),
                  A.make_opts(lambda1_us=-1.0)]:
         assert lib.gdn_plan_segment_chunks(ctypes.byref(s), ctypes.byref(opts)) < 0

@@ -34,18 +34,40 @@ def shape(**kw):
     return B.GdnShape(**d)
 
 
-def ws_bytes(s):
+def ws_bytes(s, opts=None):
     n = ctypes.c_size_t(0)
-    rc = B.lib().gdn_chunk_fwd_workspace_bytes(ctypes.byref(s), None, ctypes.byref(n))
+    rc = B.lib().gdn_chunk_fwd_workspace_bytes(ctypes.byref(s), None if opts is None else ctypes.byref(opts),
+                                               ctypes.byref(n))
     return rc, n.value
 
 
 def test_workspace_query():
-    rc, n = ws_bytes(shape())
+    two_kernel = B.make_opts(one_pass=-1)
+    rc, n = ws_bytes(shape(), two_kernel)
     assert rc == B.GDN_OK
     assert n >= 2 * 2 * 64 * 64 * 2  # two chunks x two heads of bf16 T
     rc32, n32 = ws_bytes(shape(qkv_dtype=B.GDN_F32))
     assert rc32 == B.GDN_OK and n32 > n
+    # the one-pass forward (the bf16 default) keeps no T, so an unsplit plan needs less
+    rc1, n1 = ws_bytes(shape())
+    assert rc1 == B.GDN_OK and n1 < 2 * 2 * 64 * 64 * 2
+
+
+def test_plan_one_pass_query():
+    lib = B.lib()
+    assert lib.gdn_plan_one_pass(ctypes.byref(shape()), None) == 1
+    assert lib.gdn_plan_one_pass(ctypes.byref(shape(qkv_dtype=B.GDN_F32, beta_dtype=B.GDN_F32)), None) == 0
+    for kw, want in [(dict(one_pass=-1), 0), (dict(one_pass=1), 1), (dict(value_block=64), 0),
+                     (dict(value_block=128), 0), (dict(one_pass=1, value_block=64), 1)]:
+        o = B.make_opts(**kw)
+        assert lib.gdn_plan_one_pass(ctypes.byref(shape()), ctypes.byref(o)) == want, kw
+    # fp32 has no one-pass kernel: forcing it still plans two kernels
+    o = B.make_opts(one_pass=1)
+    assert lib.gdn_plan_one_pass(ctypes.byref(shape(qkv_dtype=B.GDN_F32, beta_dtype=B.GDN_F32)),
+                                 ctypes.byref(o)) == 0
+    for bad in [dict(one_pass=2), dict(one_pass=-2), dict(value_block=32)]:
+        o = B.make_opts(**bad)
+        assert lib.gdn_plan_one_pass(ctypes.byref(shape()), ctypes.byref(o)) == B.GDN_ERR_ARG, bad
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -62,6 +62,7 @@ def draw_case(seed):
         force_correction=int(rng.random() < 0.3),
         window_max_chunks=int(rng.choice([0, 1, 4, 16])),
         value_block=int(rng.choice([0, 0, 64])),
+        one_pass=int(rng.choice([0, 0, 1, -1])),
     )
     if seed % 4 == 3:   # one-chunk segments: long merge chains (the two-level tree)
         opts.update(no_split=0, force_segment_chunks=1)

@@ -1,4 +1,4 @@
-"""GPU parity of the one-pass forward (value_block = 32: the chunk inverse and P are
+"""GPU parity of the one-pass forward (one_pass = 1: the chunk inverse and P are
 formed inside the fused kernel, fused_wy.hip) against the fp64 oracle, per (sequence,
 head) relative L2 on o and on the final state.  Covers ragged last chunks, every
 dk / dv combination, packed input with empty and sub-chunk sequences, initial and
@@ -24,7 +24,7 @@ def spec(**kw):
 
 
 def wy_opts(**kw):
-    return binding.make_opts(value_block=32, **kw)
+    return binding.make_opts(one_pass=1, **kw)
 
 
 CASES = [
