@@ -296,6 +296,9 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
         const int idx = clane + 64 * j, row = idx / Cfg::VPR, cv = (idx % Cfg::VPR) * 8;
         *reinterpret_cast<u32x4*>(sV + row * VS + wcol + cv) = vr[j];
       }
+      wave_lds_sync();
+      i16x4 vraw[4][NCT];   // V in accumulator layout, read during the last X/Y step
+      frag aT[6];           // T fragments, read there too
       // ---- X = K h and Y^T = h^T Q^T (transposed: a lane holds four consecutive value
       //      columns of one query row, the layout of the O store).  Every K and Q
       //      fragment feeds one MFMA per column tile.  Software-pipelined over the
@@ -316,6 +319,17 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           if (ks + 1 < NKS) read(ks + 1);
+          if (ks + 1 == NKS) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+              for (int j = 0; j < NCT; ++j) {
+                const int col = wcol + 16 * j;
+                vraw[u][j] = col_read4_raw(sV, VS, prow(u, 4 * cq), col + cr16, col + 4 * (cr16 & 3));
+              }
+#pragma unroll
+            for (int f = 0; f < 6; ++f) aT[f] = *reinterpret_cast<const frag*>(cT + f * FR + 8 * clane);
+          }
 #pragma unroll
           for (int j = 0; j < NCT; ++j) {
             const frag hb = M::pack(hs[2 * ks][j], hs[2 * ks + 1][j]);
@@ -329,22 +343,36 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
         }
       }
       load_v(min(i + 1, nrun - 1));
-      // ---- V' = diag(beta) (V - diag(gamma) X), in place; V read in accumulator layout
-      wave_lds_sync();
+      // ---- V' = diag(beta) (V - diag(gamma) X), in place
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 bet = rows4(sBet[b], u), gam = rows4(sGam[b], u);
 #pragma unroll
         for (int j = 0; j < NCT; ++j) {
-          const int col = wcol + 16 * j;
-          const f32x4 vv = col_read4(sV, VS, prow(u, 4 * cq), col + cr16, col + 4 * (cr16 & 3));
-          X[u][j] = rows4(sBet[b], u) * (vv - rows4(sGam[b], u) * X[u][j]);
+          f32x4 vv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vv[e] = __uint_as_float(((uint32_t)(uint16_t)vraw[u][j][e]) << 16);
+          X[u][j] = bet * (vv - gam * X[u][j]);
         }
+      }
+      // ---- K^T fragments of the state update (LDS transpose reads), pipelined over pairs
+      //      of dk tiles; the first pair is read here, ahead of U
+      frag kt[2][2][2];   // [buffer][tile of the pair][contraction step]
+      frag aP[6];         // P fragments (output chunks), read during the last pair
+      auto read_kt = [&](int t0) {
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const int t = t0 + dt;
+          const int own = prow(t, cr16), supply = prow(t, 4 * (cr16 & 3));
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+            kt[(t0 >> 1) & 1][dt][ks] = col_frag(cK, KS, 32 * ks + 4 * cq, 32 * ks + 16 + 4 * cq, own, supply);
+        }
+      };
+      read_kt(0);
       // ---- U = T V' (T lower triangular: row tiles 0, 1 need contraction step 0 only)
       f32x4 U[4][NCT];
       {
-        frag aT[6];
-#pragma unroll
-        for (int f = 0; f < 6; ++f) aT[f] = *reinterpret_cast<const frag*>(cT + f * FR + 8 * clane);
 #pragma unroll
         for (int j = 0; j < NCT; ++j) {
           frag wb[2];
@@ -365,25 +393,18 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
           if constexpr (EMIT) ubp[ks][j] = M::pack(U[2 * ks][j], U[2 * ks + 1][j]);
           ubd[ks][j] = M::pack(U[2 * ks][j] * rows4(sDec[b], 2 * ks), U[2 * ks + 1][j] * rows4(sDec[b], 2 * ks + 1));
         }
-      // ---- h <- gamma_last h + K^T (diag(d) U); K^T fragments by LDS transpose reads,
-      //      pipelined over pairs of dk tiles like the X and Y products
+      // ---- h <- gamma_last h + K^T (diag(d) U)
       const float gC = sGC[b];
       {
-        frag kt[2][2][2];   // [buffer][tile of the pair][contraction step]
-        auto read = [&](int t0) {
-#pragma unroll
-          for (int dt = 0; dt < 2; ++dt) {
-            const int t = t0 + dt;
-            const int own = prow(t, cr16), supply = prow(t, 4 * (cr16 & 3));
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-              kt[(t0 >> 1) & 1][dt][ks] = col_frag(cK, KS, 32 * ks + 4 * cq, 32 * ks + 16 + 4 * cq, own, supply);
-          }
-        };
-        read(0);
 #pragma unroll
         for (int t0 = 0; t0 < NKT; t0 += 2) {
-          if (t0 + 2 < NKT) read(t0 + 2);
+          if (t0 + 2 < NKT) read_kt(t0 + 2);
+          if constexpr (EMIT) {
+            if (t0 + 2 == NKT) {
+#pragma unroll
+              for (int f = 0; f < 6; ++f) aP[f] = *reinterpret_cast<const frag*>(cP + f * FR + 8 * clane);
+            }
+          }
 #pragma unroll
           for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -398,9 +419,6 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
       }
       // ---- O = scale diag(gamma) Q h + P U, stored 16 bytes per lane
       if constexpr (EMIT) {
-        frag aP[6];
-#pragma unroll
-        for (int f = 0; f < 6; ++f) aP[f] = *reinterpret_cast<const frag*>(cP + f * FR + 8 * clane);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const float gs = sGamS[b][prow(u, cr16)];
@@ -714,7 +732,7 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
 
     // Step schedule (step s: the chain computes chunk s; s < 0: preparation only).
     // This wave owns chunks i = pw, pw + NP, ...; for chunk i:
-    //   step i - 5: K, g, beta loads issued (for i = pw; later chunks: at step i - 6)
+    //   K, g, beta loads issued at step i - 6 (first owned chunk: at the start)
     //   step i - 4: gates, Gram tiles, A in registers; K and Q loads issued
     //   step i - 3: diagonal-block substitution (the shared scratch), doubling -> T
     //   step i - 2: P; K into its ring slot; K, g, beta loads of chunk i + NP issued
@@ -730,12 +748,12 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
       lq = q + z;
       llane = lane + z;
     };
+    // every prep wave issues its first chunk's loads at once: only chunk 0 waits for
+    // them in the preparation steps
     int s = -NP - 1;
-    for (; s < pw - NP - 1; ++s) __syncthreads();
     refresh_lanes();
     if (nrun > 0) load_kgb(min(pw, nrun - 1));
-    __syncthreads();
-    ++s;
+    for (; s < pw - NP; ++s) __syncthreads();
     for (int i = pw; i < nrun; i += NP) {
       const bool withq = c_start + i >= c_out;
       refresh_lanes();
