@@ -474,8 +474,9 @@ int run_stages(int first, int last, const void* q, const void* k, const void* v,
   int32_t* seg_off = reinterpret_cast<int32_t*>(ws + L.seg_off);
   int32_t* seg_order = reinterpret_cast<int32_t*>(ws + L.seg_order);
   uint32_t* best = reinterpret_cast<uint32_t*>(ws + L.best);
-  // the packed-sequence tables live in the workspace: built with step 1, read by every stage
-  if (cu_seqlens && runs(GDN_STAGE_INVERSE)) {
+  // the packed-sequence tables live in the workspace and are rebuilt by every call (a
+  // single stage too), so no kernel indexes by workspace contents it did not write
+  if (cu_seqlens) {
     if (gdn::launch_plan_tables(cu_seqlens, p.N, P.seg_chunks, chunk_off,
                                 P.split ? seg_off : nullptr, L.has_seg_order ? seg_order : nullptr,
                                 stream) != hipSuccess)

@@ -179,10 +179,18 @@ int gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const flo
  * elsewhere, the workspace regions below (gdn_chunk_fwd_workspace_region).  A
  * stage that the plan does not need (the split stages when no sequence is split,
  * the gate scan under force_correction) enqueues nothing and returns GDN_OK.
- * GDN_STAGE_INVERSE also builds the packed-sequence tables the later stages read.
- * Each stage reads what the earlier stages of the same pass wrote into the
- * workspace: running a stage on a workspace where they have not run (or ran with
- * other arguments) is undefined, and with packed sequences can index out of range.
+ * Under a one-pass plan (gdn_plan_one_pass) no stage forms T for the forward pass:
+ * an unsplit plan's GDN_STAGE_INVERSE enqueues nothing; a split plan's forms only
+ * the chunk gate sums, and its GDN_STAGE_CP_PASS1 first forms T for the heads
+ * without an admissible lookback window (the only ones pass 1 reads it for).
+ * With packed sequences every stage call first rebuilds, from cu_seqlens, the
+ * chunk and segment tables it indexes by (one small launch; gdn_chunk_fwd builds
+ * them once), so no stage indexes by anything a caller or an earlier stage left in
+ * the workspace: window lengths read back are clamped to the sequence, and every
+ * other workspace byte a stage reads is a value.  Each stage reads what the earlier
+ * stages of the same pass wrote into the workspace: running a stage on a workspace
+ * where they have not run (or ran with other arguments) gives unspecified output
+ * values (never an access outside the buffers the arguments describe).
  * Errors as gdn_chunk_fwd; an unknown stage is GDN_ERR_ARG.
  */
 int gdn_chunk_fwd_stage(int stage, const void* q, const void* k, const void* v, const float* g,
