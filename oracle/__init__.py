@@ -17,6 +17,10 @@ Contents
                 (wrong-start state S*, correction matrix M, merge) and the
                 window-lookback start.
   gate       -- brute-force window-length decision for strongly decaying heads.
+  backward   -- fp64 gradients of <dO, O> + <dhT, hT> with respect to q, k, v, g, beta
+                and the initial state: the token-by-token adjoint of the recurrence,
+                and separately the chunk-by-chunk backward of the WY form (with the
+                DA + DA^T merge of the pages' algebraic-rewrites section).
   build      -- compiles the C part with gcc.
 
 Every function cites the passage of the pages it follows.  The pages are three
@@ -32,3 +36,4 @@ from .chunked import (  # noqa: F401
     segment_transition,
 )
 from .gate import window_chunks, window_chunks_all  # noqa: F401
+from .backward import chunked_backward, token_backward_numpy  # noqa: F401
