@@ -10,6 +10,7 @@ GDN_BF16, GDN_F32 = 1, 2
 
 # Symbols declared in include/gdn.h (checked by the CPU test of the boundary).
 EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_stage",
+           "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes",
            "gdn_chunk_fwd_noalloc",
            "gdn_chunk_fwd_workspace_region", "gdn_chunk_inverse",
            "gdn_gate_scan", "gdn_gate_scan_workspace_bytes", "gdn_plan_segment_chunks", "gdn_plan_one_pass",
@@ -63,6 +64,11 @@ def declare(lib):
     lib.gdn_gate_scan_workspace_bytes.restype = ctypes.c_int
     lib.gdn_plan_segment_chunks.argtypes = [shp, opt]
     lib.gdn_plan_segment_chunks.restype = ctypes.c_int64
+    lib.gdn_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp,
+                                  vp, vp, shp, vp, sz, vp]
+    lib.gdn_chunk_bwd.restype = ctypes.c_int
+    lib.gdn_chunk_bwd_workspace_bytes.argtypes = [shp, ctypes.POINTER(sz)]
+    lib.gdn_chunk_bwd_workspace_bytes.restype = ctypes.c_int
     lib.gdn_plan_one_pass.argtypes = [shp, opt]
     lib.gdn_plan_one_pass.restype = ctypes.c_int
     lib.gdn_total_chunks.argtypes = [shp]

@@ -738,6 +738,86 @@ int gdn_gate_scan(const float* g, const int32_t* cu_seqlens, const gdn_shape* sh
   return GDN_OK;
 }
 
+// Backward workspace: packed chunk offsets, the chunk-start states, and the
+// workgroups' fp32 shares of dq, dk, dbeta and dg.
+struct BwdLayout {
+  size_t chunk_off = 0, hchk = 0, dq_p = 0, dk_p = 0, dbeta_p = 0, dg_p = 0, total = 0;
+};
+BwdLayout bwd_layout(const gdn_shape* s) {
+  BwdLayout L;
+  int64_t chunks = 0;
+  for (int64_t n = 0; n < s->N; ++n) chunks += seq_chunks(s, n);
+  const int64_t tot = s->B * s->T, nblk = s->dv / gdn::kBwdColumnBlock;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes); return o; };
+  L.chunk_off = take(s->cu_seqlens_host ? (size_t)(s->N + 1) * sizeof(int32_t) : 0);
+  L.hchk = take((size_t)chunks * s->H * s->dk * s->dv * sizeof(float));
+  L.dq_p = take((size_t)nblk * tot * s->H * s->dk * sizeof(float));
+  L.dk_p = take((size_t)nblk * tot * s->H * s->dk * sizeof(float));
+  L.dbeta_p = take((size_t)nblk * tot * s->H * sizeof(float));
+  L.dg_p = take((size_t)nblk * tot * s->H * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+int gdn_chunk_bwd_workspace_bytes(const gdn_shape* shape, size_t* bytes) {
+  int rc = validate_shape(shape);
+  if (rc != GDN_OK) return rc;
+  if (!bytes) return GDN_ERR_ARG;
+  *bytes = bwd_layout(shape).total;
+  return GDN_OK;
+}
+
+int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, float scale,
+                  const void* d_o, const float* d_final_state, void* dq, void* dk, void* dv,
+                  float* dg, void* dbeta, float* d_initial_state, const gdn_shape* shape,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = validate_shape(shape);
+  if (rc == GDN_OK) rc = check_inputs(k, g, beta, cu_seqlens, shape);
+  if (rc != GDN_OK) return rc;
+  if (!std::isfinite(scale)) return GDN_ERR_ARG;
+  if (shape->T > 0 && (!q || !v || !d_o || !dq || !dk || !dv || !dg || !dbeta)) return GDN_ERR_ARG;
+  const int eb = shape->beta_dtype == GDN_BF16 ? 2 : 4;
+  if ((q && !aligned(q, 16)) || (v && !aligned(v, 16)) || (d_o && !aligned(d_o, 16)) ||
+      (dq && !aligned(dq, 16)) || (dk && !aligned(dk, 16)) || (dv && !aligned(dv, 16)) ||
+      (dg && !aligned(dg, 4)) || (dbeta && !aligned(dbeta, eb)) ||
+      (initial_state && !aligned(initial_state, 16)) || (d_final_state && !aligned(d_final_state, 16)) ||
+      (d_initial_state && !aligned(d_initial_state, 16)))
+    return GDN_ERR_ARG;
+  const BwdLayout L = bwd_layout(shape);
+  if (workspace_bytes < L.total || (L.total > 0 && !workspace) || !aligned(workspace, kAlign))
+    return GDN_ERR_WORKSPACE;
+  const int64_t nblk = shape->dv / gdn::kBwdColumnBlock;
+  if (shape->N * shape->H * nblk > gdn::kMaxDispatchItems / 256) return GDN_ERR_UNSUPPORTED;
+  const int64_t total_chunks = gdn_total_chunks(shape);
+  char* ws = static_cast<char*>(workspace);
+  gdn::Problem p = make_problem(q, k, v, g, beta, initial_state, cu_seqlens, scale, nullptr, nullptr,
+                                shape, total_chunks);
+  if (cu_seqlens) {
+    int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + L.chunk_off);
+    if (gdn::launch_chunk_offsets(cu_seqlens, p.N, chunk_off, stream) != hipSuccess) return GDN_ERR_HIP;
+    p.chunk_off = chunk_off;
+  }
+  gdn::BwdArgs a;
+  a.d_o = d_o;
+  a.dhT = d_final_state;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dg = dg;
+  a.dbeta = dbeta;
+  a.dh0 = d_initial_state;
+  a.hchk = reinterpret_cast<float*>(ws + L.hchk);
+  a.dq_p = reinterpret_cast<float*>(ws + L.dq_p);
+  a.dk_p = reinterpret_cast<float*>(ws + L.dk_p);
+  a.dbeta_p = reinterpret_cast<float*>(ws + L.dbeta_p);
+  a.dg_p = reinterpret_cast<float*>(ws + L.dg_p);
+  a.total_tokens = shape->B * shape->T;
+  if (gdn::launch_chunk_bwd(p, a, stream) != hipSuccess) return GDN_ERR_HIP;
+  return GDN_OK;
+}
+
 const char* gdn_status_str(int status) {
   switch (status) {
     case GDN_OK: return "ok";

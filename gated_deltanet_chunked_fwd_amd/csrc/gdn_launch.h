@@ -114,4 +114,27 @@ hipError_t launch_fused_wy(const Problem& p, const FwdPlan& plan, hipStream_t s,
 hipError_t launch_fused_forward(const Problem& p, const FwdPlan& plan, hipStream_t s,
                                 KernelEvents ev = {});
 
+// Backward (chunk_bwd.hip): gradients of <dO, O> + <dhT, hT>.  Workgroup shares of
+// dq, dk (fp32 [blocks, tokens, H, dk]) and dbeta, dg (fp32 [blocks, tokens, H]) are
+// summed by the second kernel; hchk holds the state at every chunk start
+// ([total_chunks, H, dk, dv] fp32).  dhT and dh0 may be null.
+struct BwdArgs {
+  const void* d_o;
+  const float* dhT;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;
+  void* dbeta;
+  float* dh0;
+  float* hchk;
+  float* dq_p;
+  float* dk_p;
+  float* dbeta_p;
+  float* dg_p;
+  int64_t total_tokens;
+};
+constexpr int kBwdColumnBlock = 32;   // value columns per backward workgroup
+hipError_t launch_chunk_bwd(const Problem& p, const BwdArgs& a, hipStream_t s, KernelEvents ev = {});
+
 }  // namespace gdn

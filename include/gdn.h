@@ -267,6 +267,33 @@ int gdn_gate_scan(const float* g, const int32_t* cu_seqlens, const gdn_shape* sh
                   size_t workspace_bytes, hipStream_t stream);
 int gdn_gate_scan_workspace_bytes(const gdn_shape* shape, size_t* bytes);
 
+/*
+ * Backward of gdn_chunk_fwd: the gradients of L = <d_o, o> + <d_final_state,
+ * final_state> with respect to q, k, v, g, beta and initial_state, for the forward
+ * that gdn_chunk_fwd computes on the same arguments (FlashQLA talk transcript:
+ * results and timeline sections, a backward of the forward's chunk structure;
+ * algebraic-rewrites section, the K K^T gradient entering K as (dA + dA^T) K).
+ * The forward is recomputed inside (the state at every chunk start is kept in the
+ * workspace), so nothing from a forward call is needed.
+ *   q, k, v, g, beta, initial_state, cu_seqlens, scale   as gdn_chunk_fwd
+ *   d_o             device, [B,T,H,dv], dtype shape->qkv_dtype: gradient of o
+ *   d_final_state   device, [N,H,dk,dv] fp32: gradient of the final state, or NULL (zero)
+ *   dq, dk          device, [B,T,H,dk], dtype shape->qkv_dtype, fully overwritten
+ *   dv              device, [B,T,H,dv], dtype shape->qkv_dtype, fully overwritten
+ *   dg              device, [B,T,H] fp32 (gradient of the log gate), fully overwritten
+ *   dbeta           device, [B,T,H], dtype shape->beta_dtype, fully overwritten
+ *   d_initial_state device, [N,H,dk,dv] fp32, fully overwritten; or NULL (not written)
+ *   workspace       device scratch of at least gdn_chunk_bwd_workspace_bytes()
+ * Arithmetic is fp32 throughout (bf16 inputs converted on load, outputs rounded
+ * once).  Errors as gdn_chunk_fwd.
+ */
+int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const void* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, float scale,
+                  const void* d_o, const float* d_final_state, void* dq, void* dk, void* dv,
+                  float* dg, void* dbeta, float* d_initial_state, const gdn_shape* shape,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+int gdn_chunk_bwd_workspace_bytes(const gdn_shape* shape, size_t* bytes);
+
 /* Segment length (chunks) the planner picks for gdn_chunk_fwd, or a negative status.
  * When no sequence is split (no_split, a forced length at or above the longest
  * sequence's chunk count, or the planner's own choice) the value is 1073741823

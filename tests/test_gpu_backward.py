@@ -1,0 +1,109 @@
+"""GPU parity of the backward (gdn_chunk_bwd, chunk_bwd.hip) against the fp64 backward
+oracle (oracle/backward.py, chunk form, itself pinned against the token adjoint,
+finite differences and exact rational derivatives): per (sequence, head), the
+relative L2 error of dq, dk, dv, dg, dbeta and d_initial_state, under the forward's
+tolerances (1e-2 for bf16 storage, 1e-5 for fp32).  Covers the fp32 tiny workload,
+bf16 with every dk / dv combination, ragged last chunks, packed input with empty
+and one-token sequences, initial-state and final-state gradients present or absent,
+strong and absent decay, and fp32 beta with bf16 q/k/v."""
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_chunked_fwd_amd import binding, synth
+from oracle.backward import chunked_backward
+from tests.gpu_util import TOL, rel_l2, seq_bounds, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+
+
+def _grads_in(inp, seed, with_dhT):
+    """Seeded output gradients: do in the dtype of v (as a caller passes it), dhT fp32."""
+    spec = inp["spec"]
+    gen = torch.Generator().manual_seed(9000 + seed)
+    do = torch.randn(inp["v"].shape, generator=gen).to(inp["v"].dtype)
+    N = len(seq_bounds(inp))
+    dhT = torch.randn((N, spec.H, spec.dk, spec.dv), generator=gen).float() if with_dhT else None
+    return do, dhT
+
+
+def _run_and_compare(inp, seed, with_dhT=True):
+    spec = inp["spec"]
+    do, dhT = _grads_in(inp, seed, with_dhT)
+    d = to_dev(inp)
+    got = binding.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do.cuda(), d["h0"],
+                            None if dhT is None else dhT.cuda(), cu_seqlens=d["cu_seqlens"],
+                            scale=inp["scale"], cu_seqlens_host=d["cu_host"])
+    torch.cuda.synchronize()
+    got = [x.detach().cpu().double().numpy() for x in got]
+    f64 = synth.as_f64
+    ref = chunked_backward(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["g"]), f64(inp["beta"]),
+                           f64(do), None if dhT is None else f64(dhT), None if inp.get("h0") is None else f64(inp["h0"]),
+                           None if inp.get("cu_seqlens") is None else inp["cu_seqlens"].numpy())
+    worst = {k: 0.0 for k in NAMES}
+    for n, (b, s, e) in enumerate(seq_bounds(inp)):
+        for h in range(spec.H):
+            for i, name in enumerate(NAMES):
+                if name == "dh0":
+                    a, r = got[i][n, h], ref[i][n, h]
+                elif e > s:
+                    a, r = got[i][b, s:e, h], ref[i][b, s:e, h]
+                else:
+                    continue
+                worst[name] = max(worst[name], rel_l2(a, r))
+    return worst
+
+
+def _assert(worst, tol, label):
+    msg = "%s worst rel L2 %s (tol %.0e)" % (label, {k: "%.2e" % v for k, v in worst.items()}, tol)
+    print(msg, flush=True)
+    assert max(worst.values()) <= tol, msg
+
+
+def spec(**kw):
+    base = dict(name="bwd", B=1, T=200, H=2, dk=128, dv=128, dtype="bf16", seed=0)
+    base.update(kw)
+    return synth.Spec(**base)
+
+
+CASES = [
+    ("f32_tiny_workload", None),
+    ("bf16_d128_ragged_h0", dict(B=2, T=200, H=2, h0_std=0.05, seed=61)),
+    ("bf16_dk64_dv128", dict(B=1, T=150, H=2, dk=64, dv=128, seed=62)),
+    ("bf16_dk128_dv64", dict(B=1, T=130, H=2, dk=128, dv=64, seed=63)),
+    ("bf16_d64_one_chunk", dict(B=2, T=64, H=1, dk=64, dv=64, seed=64)),
+    ("bf16_strong_gate", dict(B=1, T=260, H=2, gate="uniform", seed=65)),
+    ("bf16_no_decay", dict(B=1, T=200, H=1, gate="zero", seed=66)),
+    ("bf16_beta_f32", dict(B=1, T=100, H=2, beta_dtype="f32", seed=67)),
+    ("f32_d128_h0", dict(B=1, T=140, H=2, dtype="f32", h0_std=0.05, seed=68)),
+]
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=[c[0] for c in CASES])
+def test_backward_parity(name, kw):
+    sp = synth.workload(1) if kw is None else spec(name=name, **kw)
+    print("backward case %s: %s" % (name, sp), flush=True)
+    inp = synth.generate(sp)
+    worst = _run_and_compare(inp, seed=sum(map(ord, name)) % 1000)
+    _assert(worst, TOL[sp.dtype], "backward " + name)
+
+
+def test_backward_without_final_state_gradient():
+    inp = synth.generate(spec(name="bwd_nodhT", B=1, T=120, H=2, dk=64, dv=64, dtype="f32", seed=69))
+    worst = _run_and_compare(inp, seed=5, with_dhT=False)
+    _assert(worst, TOL["f32"], "backward without dhT")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_packed_with_empty_and_tiny(dtype):
+    lengths = [130, 0, 1, 64, 77]
+    inp = synth.generate(spec(name="bwd_packed", B=1, T=int(sum(lengths)), H=2, dk=64, dv=64, dtype=dtype,
+                              seed=70))
+    inp["cu_seqlens"] = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
+    inp["N"] = len(lengths)
+    g = torch.Generator().manual_seed(71)
+    inp["h0"] = (torch.randn(len(lengths), 2, 64, 64, generator=g) * 0.05).float()
+    worst = _run_and_compare(inp, seed=6)
+    _assert(worst, TOL[dtype], "backward packed " + dtype)
