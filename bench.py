@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--segment-chunks", type=int, default=0, help="force the split length (0: planner)")
     ap.add_argument("--batch", type=int, default=0,
                     help="override the workload's batch size B (dense workloads; occupancy sweeps)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (gdn_chunk_bwd) on the workload instead of the forward")
     ap.add_argument("--copy-reference", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB (the known-size kernel that "
                          "scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings) and exit")
@@ -245,6 +247,78 @@ def cpu_baseline(inp, spec, min_seconds=10.0):
                       "in %.1f s" % (tokens, spec.H, passes, dt)}
 
 
+def backward_bytes(spec, n_seqs, has_h0):
+    """Compulsory HBM bytes of the backward: q, k, v, dO, g, beta in; dq, dk, dv, dg,
+    dbeta out; the fp32 final-state gradient in and the initial-state gradient out
+    (plus the initial state in, when there is one)."""
+    e = 2 if spec.dtype == "bf16" else 4
+    eb = 2 if (spec.beta_dtype or spec.dtype) == "bf16" else 4
+    th = spec.B * spec.T * spec.H
+    per = (2 * spec.dk + 2 * spec.dv) * e + 4 + eb + (2 * spec.dk + spec.dv) * e + 4 + eb
+    states = n_seqs * spec.H * spec.dk * spec.dv * 4 * (3 if has_h0 else 2)
+    return th * per + states
+
+
+def bench_backward(args):
+    """One JSON line for gdn_chunk_bwd on the workload: K back-to-back calls after one
+    cache eviction, bracketed by device synchronisations and one event pair; the
+    roofline is the backward's algorithmic bytes over that mean time."""
+    import torch
+
+    from gated_deltanet_chunked_fwd_amd import binding, synth
+
+    spec = synth.WORKLOADS[args.workload]
+    inp = synth.generate(spec)
+    dev = torch.device("cuda:0")
+    d = {k: (None if inp[k] is None else inp[k].to(dev).contiguous())
+         for k in ("q", "k", "v", "g", "beta", "h0", "cu_seqlens")}
+    N = inp["N"]
+    gen = torch.Generator().manual_seed(1234)
+    do = torch.randn(inp["v"].shape, generator=gen).to(inp["v"].dtype).to(dev)
+    dhT = torch.randn((N, spec.H, spec.dk, spec.dv), generator=gen).float().to(dev)
+    nbytes = ctypes.c_size_t(0)
+    sh = binding._Shape(d["q"], d["v"], d["beta"], d["cu_seqlens"], inp["cu_seqlens"])
+    if binding.lib().gdn_chunk_bwd_workspace_bytes(sh.ref(), ctypes.byref(nbytes)) != 0:
+        raise RuntimeError("gdn_chunk_bwd_workspace_bytes failed")
+    ws = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        return binding.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do, d["h0"], dhT,
+                                 cu_seqlens=d["cu_seqlens"], scale=inp["scale"],
+                                 cu_seqlens_host=inp["cu_seqlens"], workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    hip = Hip()
+    ev = hip.events(2)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    if not args.no_flush:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        flush.fill_(1)
+        del flush
+    torch.cuda.synchronize()
+    hip.record(ev[0], stream)
+    for _ in range(args.steps):
+        step()
+    hip.record(ev[1], stream)
+    torch.cuda.synchronize()
+    ms = hip.elapsed(ev[0], ev[1]) / args.steps
+    alg = backward_bytes(spec, N, d["h0"] is not None)
+    achieved = alg / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": "GDN bwd chunked: ms & tokens/s; % of HBM roofline",
+        "value": spec.B * spec.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype, "data": "synthetic (seeded)",
+        "config": {"workload": spec.name, "B": spec.B, "T": spec.T, "H": spec.H, "dk": spec.dk,
+                   "dv": spec.dv, "pass": "backward", "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "chunk_bwd_kernel + bwd_reduce_kernel (whole call)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": alg},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_reference:
@@ -255,6 +329,9 @@ def main():
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d, WORLD_SIZE %d requested)" % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
+    if args.backward:
+        bench_backward(args)
+        return
 
     import torch
 

@@ -789,7 +789,7 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
   if (workspace_bytes < L.total || (L.total > 0 && !workspace) || !aligned(workspace, kAlign))
     return GDN_ERR_WORKSPACE;
   const int64_t nblk = shape->dv / gdn::kBwdColumnBlock;
-  if (shape->N * shape->H * nblk > gdn::kMaxDispatchItems / 256) return GDN_ERR_UNSUPPORTED;
+  if (shape->N * shape->H * nblk > gdn::kMaxDispatchItems / 1024) return GDN_ERR_UNSUPPORTED;
   const int64_t total_chunks = gdn_total_chunks(shape);
   char* ws = static_cast<char*>(workspace);
   gdn::Problem p = make_problem(q, k, v, g, beta, initial_state, cu_seqlens, scale, nullptr, nullptr,

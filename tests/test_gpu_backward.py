@@ -107,3 +107,11 @@ def test_backward_packed_with_empty_and_tiny(dtype):
     inp["h0"] = (torch.randn(len(lengths), 2, 64, 64, generator=g) * 0.05).float()
     worst = _run_and_compare(inp, seed=6)
     _assert(worst, TOL[dtype], "backward packed " + dtype)
+
+
+def test_backward_qwen_like_full_size_every_pair():
+    """The backward at the Qwen-like workload's full size (B=4, T=4096, H=16, d=128),
+    every (sequence, head) pair against the fp64 chunk-form oracle."""
+    inp = synth.generate(synth.WORKLOADS[2])
+    worst = _run_and_compare(inp, seed=2)
+    _assert(worst, TOL["bf16"], "backward qwen_like full size")
