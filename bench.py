@@ -469,8 +469,12 @@ def main():
     lengths = ([spec.T] * spec.B if cu_host is None
                else [int(cu_host[i + 1] - cu_host[i]) for i in range(N)])
     windows = None
+    corrected = 0.0
     if seg_chunks < max((n + 63) // 64 for n in lengths):
         windows = binding.gate_scan(d["g"], d["cu_seqlens"], cu_host).cpu().tolist()
+        flat = [w for row in windows for w in row]
+        corrected = sum(1 for w in flat if w == 0) / max(1, len(flat))
+    model_us = binding.plan_predict_us(d["q"], d["v"], d["beta"], cu_host, opts, corrected)
     dom_bytes = stage_bytes(dom, spec, lengths, seg_chunks, windows, has_h0, True)
     flops = algorithmic_flops(spec)
     copy_gbs = copy_bandwidth(hip, stream, torch)
@@ -510,6 +514,7 @@ def main():
                  "ms_per_step_evicted_caches_median":
                      sorted(cold_ms)[len(cold_ms) // 2] if cold_ms else None,
                  "dominant_ms_min": min(dom_ms_list),
+                 "model_ms": model_us * 1e-3, "model_corrected_fraction": corrected,
                  "wall_s_timed_region": wall,
                  "host_ms_per_call": host_ms},
     }

@@ -13,7 +13,7 @@ EXPORTS = ("gdn_chunk_fwd", "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd_stag
            "gdn_chunk_bwd", "gdn_chunk_bwd_workspace_bytes",
            "gdn_chunk_fwd_noalloc",
            "gdn_chunk_fwd_workspace_region", "gdn_chunk_inverse",
-           "gdn_gate_scan", "gdn_gate_scan_workspace_bytes", "gdn_plan_segment_chunks", "gdn_plan_one_pass",
+           "gdn_gate_scan", "gdn_gate_scan_workspace_bytes", "gdn_plan_segment_chunks", "gdn_plan_one_pass", "gdn_plan_predict_us",
            "gdn_total_chunks", "gdn_status_str")
 
 
@@ -69,6 +69,8 @@ def declare(lib):
     lib.gdn_chunk_bwd.restype = ctypes.c_int
     lib.gdn_chunk_bwd_workspace_bytes.argtypes = [shp, ctypes.POINTER(sz)]
     lib.gdn_chunk_bwd_workspace_bytes.restype = ctypes.c_int
+    lib.gdn_plan_predict_us.argtypes = [shp, opt, ctypes.c_double, ctypes.POINTER(ctypes.c_double)]
+    lib.gdn_plan_predict_us.restype = ctypes.c_int
     lib.gdn_plan_one_pass.argtypes = [shp, opt]
     lib.gdn_plan_one_pass.restype = ctypes.c_int
     lib.gdn_total_chunks.argtypes = [shp]

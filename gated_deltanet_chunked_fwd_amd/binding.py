@@ -374,3 +374,16 @@ def chunk_bwd(q, k, v, g, beta, do, initial_state=None, d_final_state=None, cu_s
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_chunk_bwd")
     return dq, dkk, dvv, dg, db, dh0
+
+
+def plan_predict_us(q, v, beta, cu_seqlens_host=None, opts: Optional[GdnOpts] = None,
+                    corrected_fraction=0.0) -> float:
+    """The planner's modelled time (microseconds) of one chunk_fwd call for these inputs,
+    with the given share of (sequence, head) pairs that take no lookback window."""
+    sh = _Shape(q, v, beta, cu_seqlens_host, cu_seqlens_host)
+    us = ctypes.c_double(0.0)
+    rc = lib().gdn_plan_predict_us(sh.ref(), None if opts is None else ctypes.byref(opts),
+                                   ctypes.c_double(corrected_fraction), ctypes.byref(us))
+    if rc != GDN_OK:
+        raise GdnError(rc, "gdn_plan_predict_us")
+    return float(us.value)

@@ -32,13 +32,37 @@ using gdn::kChunk;
 using gdn::kWindowMaxCap;
 
 constexpr size_t kAlign = 256;
-// Planner costs, measured on MI355X (workload timestamps): one chunk step of the fused
-// kernel per workgroup, one merge step, and in chunk steps a workgroup's start-up and
-// the lookback a segment after the first usually walks (about 4.5 chunks of 0.7 step).
+// Per-kernel cost model of one call, in microseconds, fitted on MI355X to the five
+// workloads and to forced segment lengths on them (bench stage times):
+//   forward   kFwdFixedUs + step(busy) * makespan, the makespan in chunk steps from the
+//             simulated schedule (pass3_makespan: a unit's chunks, its start-up
+//             kStartSteps, kLookbackSteps for a segment after the first).  One-pass
+//             step(busy) = kStepBaseUs + kStepPerBusyUs * busy workgroups (HBM and L2
+//             contention: 3.1 us at 64 busy, 3.9 us at 256); two-kernel path: λ1.
+//   K1        two-kernel path only: kK1FixedUs + kK1PerChunkHeadUs per chunk-head.
+//   split     kSplitFixedUs + kSplitPerChunkHeadUs per chunk-head: the gate sums, the
+//             gate scan and the launches of the correction stages (on a window-only
+//             problem they find nothing to do, but their grids still scale with the
+//             chunk-heads); packed input adds the table launch, kPackedTablesUs.
+//   corrected heads (no admissible window), per call: their chunk inverse
+//             (kK1FixedUs + kCorrK1PerChunkHeadUs per chunk-head), pass 1
+//             (kPass1FixedUs + kPass1StepUs * L per round of workgroups) and the merge
+//             (short chain: kMergeFixedUs + λ2 per step; tree: kTreeFixedUs +
+//             kTreeSqrtUs * sqrt(steps)), which take the place of kCorrReplacesUs of
+//             the empty correction launches.
+// λ1 and λ2 are the per-call overrides gdn_opts.lambda1_us / lambda2_us.
 constexpr float kLambda1Us = 3.8f;
 constexpr float kLambda2Us = 0.75f;
-constexpr double kStartSteps = 2.0;
+constexpr double kStartSteps = 2.2;
 constexpr double kLookbackSteps = 3.2;
+constexpr double kFwdFixedUs = 4.5;
+constexpr double kStepBaseUs = 2.88, kStepPerBusyUs = 0.0039;
+constexpr double kStepF32Us = 5.5;               // two-kernel step on fp32 inputs
+constexpr double kK1FixedUs = 10.0, kK1PerChunkHeadUs = 0.004, kCorrK1PerChunkHeadUs = 0.007;
+constexpr double kSplitFixedUs = 11.4, kSplitPerChunkHeadUs = 0.0021, kPackedTablesUs = 4.0;
+constexpr double kCorrReplacesUs = 8.0;
+constexpr double kPass1FixedUs = 3.0, kPass1StepUs = 2.0;
+constexpr double kMergeFixedUs = 7.0, kTreeFixedUs = 35.4, kTreeSqrtUs = 3.18;
 constexpr int kMinSegmentChunks = 8;
 constexpr int64_t kPlanModelMaxUnits = 1 << 16;   // larger plans use the closed form
 constexpr float kWindowMargin = 1e-3f;
@@ -214,6 +238,45 @@ double pass3_makespan(const gdn_shape* s, int64_t L, int64_t cus, int ncb) {
   return m;
 }
 
+// The modelled time of one call (see the constants above) with segment length L
+// (L >= the longest sequence's chunks: no split) and a fraction `corr` of the
+// (sequence, head) pairs without an admissible window.
+double call_us(const gdn_shape* s, const Plan& P, const gdn_opts* o, int64_t L, int64_t cus,
+               double corr) {
+  const bool split = L < P.max_chunks;
+  const int ncb = (int)(s->dv / P.value_block);
+  int64_t segs = 0, longest_steps = 0;
+  for (int64_t n = 0; n < s->N; ++n) {
+    const int64_t nch = seq_chunks(s, n);
+    const int64_t sg = split ? std::max<int64_t>(1, (nch + L - 1) / L) : 1;
+    segs += sg;
+    longest_steps = std::max(longest_steps, sg - 1);
+  }
+  const double units = (double)segs * s->H * ncb;
+  const double busy = std::min<double>(units, (double)cus);
+  const double l1 = (o && o->lambda1_us > 0.f) ? o->lambda1_us : -1.0;
+  const double l2 = (o && o->lambda2_us > 0.f) ? o->lambda2_us : kLambda2Us;
+  double step = P.wy ? kStepBaseUs + kStepPerBusyUs * busy
+                     : (s->qkv_dtype == GDN_BF16 ? kLambda1Us : kStepF32Us);
+  if (l1 > 0) step = l1;
+  double t = kFwdFixedUs + step * pass3_makespan(s, split ? L : INT_MAX / 2, cus, ncb);
+  const double chunk_heads = (double)P.total_chunks * s->H;
+  if (!P.wy) t += kK1FixedUs + kK1PerChunkHeadUs * chunk_heads;
+  if (s->cu_seqlens_host) t += kPackedTablesUs;
+  if (!split) return t;
+  t += kSplitFixedUs + kSplitPerChunkHeadUs * chunk_heads;
+  if (corr > 0 && longest_steps > 0) {
+    t -= kCorrReplacesUs;
+    if (P.wy) t += kK1FixedUs + kCorrK1PerChunkHeadUs * corr * chunk_heads;
+    const double p1_wgs = corr * (double)(segs - s->N) * s->H * ((s->dv + s->dk) / P.pass1_block);
+    const double rounds = std::max(1.0, std::ceil(p1_wgs / (double)cus));
+    t += kPass1FixedUs + kPass1StepUs * (double)L * rounds;
+    t += longest_steps > gdn::kMergeTreeMinSteps ? kTreeFixedUs + kTreeSqrtUs * std::sqrt((double)longest_steps)
+                                                 : kMergeFixedUs + l2 * (double)longest_steps;
+  }
+  return t;
+}
+
 Plan plan_uncached(const gdn_shape* s, const gdn_opts* o) {
   Plan P;
   for (int64_t n = 0; n < s->N; ++n) {
@@ -233,18 +296,14 @@ Plan plan_uncached(const gdn_shape* s, const gdn_opts* o) {
     if (o && o->force_segment_chunks > 0) {
       L = o->force_segment_chunks;
     } else {
-      // T auto-CP: cost(L) = lambda1 * (pass-3 makespan in chunk steps) + lambda2 *
-      // (merge steps of the longest sequence); the makespan is simulated (see
-      // pass3_makespan), so unequal sequence lengths are scheduled as they will run.
-      // Candidates from kMinSegmentChunks up; no split (L = max_chunks) competes too.
-      const int ncb = (int)(s->dv / P.value_block);
+      // T auto-CP: the split length minimises the modelled call (call_us above, every
+      // head assumed to take a lookback window unless the correction is forced: the
+      // gates are on the device); no split (L = max_chunks) competes too.  The
+      // makespan is simulated (see pass3_makespan), so unequal sequence lengths are
+      // scheduled as they will run.
       const int64_t cus = device_cus();
-      const double l1 = (o && o->lambda1_us > 0.f) ? o->lambda1_us : kLambda1Us;
-      const double l2 = (o && o->lambda2_us > 0.f) ? o->lambda2_us : kLambda2Us;
-      auto cost = [&](int64_t cand) {
-        const int64_t steps = (P.max_chunks + cand - 1) / cand - 1;
-        return l1 * pass3_makespan(s, cand, cus, ncb) + l2 * (double)steps;
-      };
+      const double corr = (o && o->force_correction) ? 1.0 : 0.0;
+      auto cost = [&](int64_t cand) { return call_us(s, P, o, cand, cus, corr); };
       // candidates: a ladder of round lengths (ratio about 1.25 to 1.5) and the lengths
       // that cut the longest sequence into 2..8 equal segments
       std::vector<int64_t> cands;
@@ -574,6 +633,18 @@ int64_t gdn_plan_segment_chunks(const gdn_shape* shape, const gdn_opts* opts) {
   if (rc == GDN_OK) rc = validate_opts(opts);
   if (rc != GDN_OK) return rc;
   return make_plan(shape, opts).seg_chunks;
+}
+
+int gdn_plan_predict_us(const gdn_shape* shape, const gdn_opts* opts, double corrected_fraction,
+                        double* us) {
+  int rc = validate_shape(shape);
+  if (rc == GDN_OK) rc = validate_opts(opts);
+  if (rc != GDN_OK) return rc;
+  if (!us || !(corrected_fraction >= 0.0 && corrected_fraction <= 1.0)) return GDN_ERR_ARG;
+  const Plan P = make_plan(shape, opts);
+  const double corr = (opts && opts->force_correction) ? 1.0 : corrected_fraction;
+  *us = call_us(shape, P, opts, P.split ? P.seg_chunks : std::max<int64_t>(P.max_chunks, 1), device_cus(), corr);
+  return GDN_OK;
 }
 
 int gdn_plan_one_pass(const gdn_shape* shape, const gdn_opts* opts) {

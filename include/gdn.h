@@ -300,6 +300,15 @@ int gdn_chunk_bwd_workspace_bytes(const gdn_shape* shape, size_t* bytes);
  * (INT_MAX / 2), so every sequence is one segment. */
 int64_t gdn_plan_segment_chunks(const gdn_shape* shape, const gdn_opts* opts);
 
+/* The planner's modelled time of one gdn_chunk_fwd call, in microseconds, for the
+ * plan it picks (FlashQLA talk transcript, auto-CP section: a cost model decides the
+ * split; here per kernel, fitted on MI355X).  corrected_fraction in [0, 1] is the
+ * share of (sequence, head) pairs without an admissible lookback window (they run
+ * pass 1 and the merge; force_correction makes it 1); the planner itself, which
+ * cannot see the gates, picks the plan with 0.  Uses the current device's CU count. */
+int gdn_plan_predict_us(const gdn_shape* shape, const gdn_opts* opts, double corrected_fraction,
+                        double* us);
+
 /* 1 if gdn_chunk_fwd runs the one-pass forward for this problem and options (the
  * chunk inverses formed inside the forward kernel), 0 if it runs the chunk inverse
  * and the fused forward as separate kernels, or a negative status. */
