@@ -12,7 +12,7 @@
 // d = exp(G_last - G):
 //
 //   A  = strict_lower(diag(beta) K K^T * Gamma),  T = (I + A)^{-1}        (step 1)
-//   V' = V - diag(gamma) K h,   U = T diag(beta) V'                        (step 2)
+//   V' = V - diag(gamma) K h,   U = (T diag(beta)) V'                      (step 2)
 //   O  = scale (diag(gamma) Q h + ((Q K^T) * Gamma) U)                     (step 4)
 //   h <- gamma_last h + K^T (diag(d) U)                                    (step 3)
 //
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
   __shared__ __align__(16) bf16 sV[kChunk * VS];      // each chain wave: its own columns
   __shared__ __align__(16) bf16 sT[2][Cfg::TF * FR];
   __shared__ __align__(16) bf16 sP[2][Cfg::TF * FR];
-  __shared__ __align__(16) float sGam[2][kChunk], sGamS[2][kChunk], sDec[2][kChunk], sBet[2][kChunk];
+  __shared__ __align__(16) float sGam[2][kChunk], sGamS[2][kChunk], sDec[2][kChunk];
   __shared__ float sGC[2];
   __shared__ __align__(16) float sGB[NP][2 * kChunk];
   __shared__ __align__(16) float sInv[Cfg::INV];
@@ -286,8 +286,6 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
       const bf16* cQ = sQ[b];
       const bf16* cT = sT[b];
       const bf16* cP = sP[b];
-      const int c = c_start + i;
-      const int len = min(kChunk, si.len - c * kChunk);
       auto rows4 = [&](const float* v, int u) { return *reinterpret_cast<const f32x4*>(v + prow(u, 4 * cq)); };
       // ---- this chunk's V columns into LDS (the next chunk's loads go out once the
       //      X and Y fragments are dead)
@@ -299,6 +297,7 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
       wave_lds_sync();
       i16x4 vraw[4][NCT];   // V in accumulator layout, read during the last X/Y step
       frag aT[6];           // T fragments, read there too
+      f32x4 gamr[4];        // gamma of this lane's rows, read there too
       // ---- X = K h and Y^T = h^T Q^T (transposed: a lane holds four consecutive value
       //      columns of one query row, the layout of the O store).  Every K and Q
       //      fragment feeds one MFMA per column tile.  Software-pipelined over the
@@ -329,6 +328,8 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
               }
 #pragma unroll
             for (int f = 0; f < 6; ++f) aT[f] = *reinterpret_cast<const frag*>(cT + f * FR + 8 * clane);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) gamr[u] = rows4(sGam[b], u);
           }
 #pragma unroll
           for (int j = 0; j < NCT; ++j) {
@@ -343,22 +344,22 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
         }
       }
       load_v(min(i + 1, nrun - 1));
-      // ---- V' = diag(beta) (V - diag(gamma) X), in place
+      // ---- V - diag(gamma) X, in place (diag(beta) is folded into the stored T)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const f32x4 bet = rows4(sBet[b], u), gam = rows4(sGam[b], u);
 #pragma unroll
         for (int j = 0; j < NCT; ++j) {
           f32x4 vv;
 #pragma unroll
           for (int e = 0; e < 4; ++e) vv[e] = __uint_as_float(((uint32_t)(uint16_t)vraw[u][j][e]) << 16);
-          X[u][j] = bet * (vv - gam * X[u][j]);
+          X[u][j] = vv - gamr[u] * X[u][j];
         }
       }
       // ---- K^T fragments of the state update (LDS transpose reads), pipelined over pairs
       //      of dk tiles; the first pair is read here, ahead of U
       frag kt[2][2][2];   // [buffer][tile of the pair][contraction step]
       frag aP[6];         // P fragments (output chunks), read during the last pair
+      float gsr[4];       // gamma * scale of this lane's query rows, read there too
       auto read_kt = [&](int t0) {
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
@@ -370,6 +371,9 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
         }
       };
       read_kt(0);
+      f32x4 decr[4];   // exp(G_last - G) of this lane's rows
+#pragma unroll
+      for (int u = 0; u < 4; ++u) decr[u] = rows4(sDec[b], u);
       // ---- U = T V' (T lower triangular: row tiles 0, 1 need contraction step 0 only)
       f32x4 U[4][NCT];
       {
@@ -391,7 +395,7 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
 #pragma unroll
         for (int j = 0; j < NCT; ++j) {
           if constexpr (EMIT) ubp[ks][j] = M::pack(U[2 * ks][j], U[2 * ks + 1][j]);
-          ubd[ks][j] = M::pack(U[2 * ks][j] * rows4(sDec[b], 2 * ks), U[2 * ks + 1][j] * rows4(sDec[b], 2 * ks + 1));
+          ubd[ks][j] = M::pack(U[2 * ks][j] * decr[2 * ks], U[2 * ks + 1][j] * decr[2 * ks + 1]);
         }
       // ---- h <- gamma_last h + K^T (diag(d) U)
       const float gC = sGC[b];
@@ -403,6 +407,8 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
             if (t0 + 2 == NKT) {
 #pragma unroll
               for (int f = 0; f < 6; ++f) aP[f] = *reinterpret_cast<const frag*>(cP + f * FR + 8 * clane);
+#pragma unroll
+              for (int u = 0; u < 4; ++u) gsr[u] = sGamS[b][prow(u, cr16)];
             }
           }
 #pragma unroll
@@ -421,10 +427,9 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
       if constexpr (EMIT) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float gs = sGamS[b][prow(u, cr16)];
 #pragma unroll
           for (int j = 0; j < NCT; ++j) {
-            Yp[u][j] = Yp[u][j] * gs;
+            Yp[u][j] = Yp[u][j] * gsr[u];
 #pragma unroll
             for (int ks = 0; ks <= (u >> 1); ++ks) Yp[u][j] = M::run(ubp[ks][j], aP[tri_frag(u, ks)], Yp[u][j]);
           }
@@ -531,21 +536,19 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
         for (int ks = 0; ks < NKS; ++ks) R.kf[a][ks] = *reinterpret_cast<const frag*>(kc + off + 64u * ks);
       }
     };
-    // ---- K again and Q of chunk i (for P and the LDS writes)
-    auto load_kq = [&](int i) {
+    // ---- Q of chunk i (for P and the LDS write).  A lookback chunk produces no
+    //      output and needs no Q: it re-reads its own K rows instead (just loaded, so
+    //      served by the cache), which keeps the load count of every phase fixed.
+    auto load_kq = [&](int i, bool withq) {
       const int c = c_start + i;
       const int len = R.len;
       const int64_t t0 = (int64_t)c * kChunk;
-      const char* kc = reinterpret_cast<const char*>(Kb + t0 * row_qk);
-      const char* qc = reinterpret_cast<const char*>(Qb + t0 * row_qk);
+      const char* qc = reinterpret_cast<const char*>((withq ? Qb : Kb) + t0 * row_qk);
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const uint32_t off = row_off(a, len);
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          R.kf[a][ks] = *reinterpret_cast<const frag*>(kc + off + 64u * ks);
-          R.qf[a][ks] = *reinterpret_cast<const frag*>(qc + off + 64u * ks);
-        }
+        for (int ks = 0; ks < NKS; ++ks) R.qf[a][ks] = *reinterpret_cast<const frag*>(qc + off + 64u * ks);
       }
     };
 
@@ -651,17 +654,22 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
       const f32x4 T21T = -mm16(R21, R.tdt[2], zero4);
       const f32x4 T30T = -mm16(R30, R.tdt[3], mm16(R20, T32T, zero4));
       const f32x4 T31T = -mm16(R31, R.tdt[3], mm16(R21, T32T, zero4));
+      // T diag(beta) leaves for the chain: block (a, b) scaled by beta of its columns
+      // 16 b + 4 q .. +3 (zero on rows past a partial chunk's end).
       // lower_block order: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
-      R.tb[0] = pack_bf16x4(R.tdt[0]);
-      R.tb[1] = pack_bf16x4(T10T);
-      R.tb[2] = pack_bf16x4(R.tdt[1]);
-      R.tb[3] = pack_bf16x4(T20T);
-      R.tb[4] = pack_bf16x4(T21T);
-      R.tb[5] = pack_bf16x4(R.tdt[2]);
-      R.tb[6] = pack_bf16x4(T30T);
-      R.tb[7] = pack_bf16x4(T31T);
-      R.tb[8] = pack_bf16x4(T32T);
-      R.tb[9] = pack_bf16x4(R.tdt[3]);
+      f32x4 bc[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bc[c] = *reinterpret_cast<const f32x4*>(sB + 16 * c + 4 * lq);
+      R.tb[0] = pack_bf16x4(R.tdt[0] * bc[0]);
+      R.tb[1] = pack_bf16x4(T10T * bc[0]);
+      R.tb[2] = pack_bf16x4(R.tdt[1] * bc[1]);
+      R.tb[3] = pack_bf16x4(T20T * bc[0]);
+      R.tb[4] = pack_bf16x4(T21T * bc[1]);
+      R.tb[5] = pack_bf16x4(R.tdt[2] * bc[2]);
+      R.tb[6] = pack_bf16x4(T30T * bc[0]);
+      R.tb[7] = pack_bf16x4(T31T * bc[1]);
+      R.tb[8] = pack_bf16x4(T32T * bc[2]);
+      R.tb[9] = pack_bf16x4(R.tdt[3] * bc[3]);
     };
 
     // ---- P = scale (Q K^T) * Gamma, lower blocks; lane (r, q) of block (a, b): query
@@ -726,7 +734,6 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
       sGam[b][llane] = gam;
       sGamS[b][llane] = gam * p.scale;
       sDec[b][llane] = fast_exp(Glast - G);
-      sBet[b][llane] = sB[llane];
       if (llane == 0) sGC[b] = fast_exp(Glast);
     };
 
@@ -758,7 +765,7 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
       const bool withq = c_start + i >= c_out;
       refresh_lanes();
       gates_gram();        // s == i - 4
-      load_kq(i);
+      load_kq(i, withq);
       __syncthreads();
       ++s;
       solve_diag();        // s == i - 3

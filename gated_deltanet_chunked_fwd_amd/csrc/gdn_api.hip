@@ -814,7 +814,7 @@ int gdn_gate_scan(const float* g, const int32_t* cu_seqlens, const gdn_shape* sh
 struct BwdLayout {
   size_t chunk_off = 0, hchk = 0, dq_p = 0, dk_p = 0, dbeta_p = 0, dg_p = 0, total = 0;
 };
-BwdLayout bwd_layout(const gdn_shape* s) {
+static BwdLayout bwd_layout(const gdn_shape* s) {
   BwdLayout L;
   int64_t chunks = 0;
   for (int64_t n = 0; n < s->N; ++n) chunks += seq_chunks(s, n);
