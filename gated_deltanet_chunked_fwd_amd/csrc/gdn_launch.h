@@ -45,8 +45,10 @@ struct CpBuffers {
   float* gvec;              // segment): composed map A (as mcorr) and offset b (as sstar)
 };
 
-// Merge chains of more steps than this run as a two-level tree (cp_merge.hip).
-constexpr int kMergeTreeMinSteps = 16;
+// Merge chains of more steps than this run as a two-level tree (cp_merge.hip): about
+// where the tree's three launches (35 us + 3.2 us * sqrt(steps) on MI355X) beat one
+// serial launch (7 us + 0.75 us per step).
+constexpr int kMergeTreeMinSteps = 72;
 // An AQL dispatch counts the work-items of a grid dimension in 32 bits.
 constexpr int64_t kMaxDispatchItems = 0xFFFFFFFFLL;
 

@@ -71,19 +71,19 @@ def test_packed_forced_segment_length_that_splits_nothing(seg, corr):
 
 @pytest.mark.parametrize("seg", [1, 2])
 def test_split_tree_merge(seg):
-    """Merge chains longer than 16 steps run as a two-level tree (group maps
-    composed in parallel, a chain over groups, then each group's own steps): 40 and
-    20 steps, with an uneven last group for seg=1."""
-    inp = synth.generate(spec(B=1, T=64 * 40 + 9, H=2, seed=75 + seg, zero_gate_heads=(0,),
+    """Merge chains longer than 72 steps run as a two-level tree (group maps
+    composed in parallel, a chain over groups, then each group's own steps): 100
+    steps for seg=1 (groups of 10); seg=2 gives a 50-step serial chain."""
+    inp = synth.generate(spec(B=1, T=64 * 100 + 9, H=2, seed=75 + seg, zero_gate_heads=(0,),
                               h0_std=0.05))
     o, hT = run_gpu(inp, opts=binding.make_opts(force_segment_chunks=seg, force_correction=1))
     assert_parity(compare_pairs(inp, o, hT), TOL["bf16"], "tree merge seg=%d" % seg)
 
 
 def test_split_tree_merge_packed():
-    """Tree merge with sequences of different step counts (29, 16, 2, 0 steps, and
-    an empty sequence): every sequence uses the same group length."""
-    inp = _packed([64 * 30, 64 * 17 - 5, 64 * 3, 0, 50], H=2, seed=78, zero_heads=(0, 1))
+    """Tree merge with sequences of different step counts (79, 16, 2, 0 steps, and
+    an empty sequence): every sequence uses the same group length (9)."""
+    inp = _packed([64 * 80, 64 * 17 - 5, 64 * 3, 0, 50], H=2, seed=78, zero_heads=(0, 1))
     o, hT = run_gpu(inp, opts=binding.make_opts(force_segment_chunks=1))
     assert_parity(compare_pairs(inp, o, hT), TOL["bf16"], "tree merge packed")
 
@@ -187,7 +187,7 @@ def _stage_setup(inp, opts):
 STAGE_CASES = {
     "dense_split": (lambda: synth.generate(spec(seed=81, h0_std=0.05)),
                     dict(force_segment_chunks=3)),
-    "dense_tree": (lambda: synth.generate(spec(T=64 * 40 + 9, seed=82)), dict(force_segment_chunks=2)),
+    "dense_tree": (lambda: synth.generate(spec(T=64 * 80 + 9, seed=82)), dict(force_segment_chunks=1)),
     "packed_split": (lambda: _packed([64 * 9 + 7, 40, 0, 64 * 3, 64 * 6 + 1, 0], H=2, seed=83),
                      dict(force_segment_chunks=2)),
     "unsplit_f32": (lambda: synth.generate(spec(H=2, dk=64, dv=64, dtype="f32", seed=84)), dict(no_split=1)),
@@ -250,11 +250,11 @@ def test_segment_starts_stage_parity(case):
     h_start(j+1) = M_j h_start(j) + S*_j, segment by segment (relative L2 within the
     storage dtype's tolerance)."""
     from oracle import chunked
-    L = 2
+    L = 1 if case == "dense_tree_f32" else 2   # 80 merge steps: the tree
     if case == "dense_bf16":
         inp = synth.generate(spec(B=2, T=64 * 9 + 5, H=2, seed=91, h0_std=0.05))
     elif case == "dense_tree_f32":
-        inp = synth.generate(spec(B=1, T=64 * 40 + 9, H=2, dk=64, dv=64, dtype="f32", seed=92))
+        inp = synth.generate(spec(B=1, T=64 * 80 + 9, H=2, dk=64, dv=64, dtype="f32", seed=92))
     else:
         inp = _packed([64 * 7 + 3, 0, 64 * 5, 30], H=2, seed=93)
     sp = inp["spec"]
