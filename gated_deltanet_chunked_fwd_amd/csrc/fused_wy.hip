@@ -161,16 +161,18 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
   const int H = p.H, dv = p.dv;
 
   // ---- unit decode (XCD-aware: the column blocks of one unit share id mod 8, so they
-  //      run on one XCD and share its L2 for K, Q, g, beta)
-  const int64_t bid = blockIdx.x;
-  const int ncb = dv / BV;
-  const int64_t rest = bid >> 3;
+  //      run on one XCD and share its L2 for K, Q, g, beta).  A launch has fewer than
+  //      2^32 / 512 workgroups, so 32-bit arithmetic covers every index here.
+  const uint32_t bid = blockIdx.x;
+  const uint32_t ncb = (uint32_t)(dv / BV);
+  const uint32_t rest = bid >> 3;
   const int cb = (int)(rest % ncb);
-  const int64_t unit = (rest / ncb) * 8 + (bid & 7);
-  if (unit >= plan.units) return;
+  const uint32_t unit = (rest / ncb) * 8u + (bid & 7u);
+  if ((int64_t)unit >= plan.units) return;
   const int col0 = cb * BV;
-  const int h = (int)(unit % H);
-  const int64_t sg = plan.seg_order ? plan.seg_order[unit / H] : unit / H;
+  const int h = (int)(unit % (uint32_t)H);
+  const uint32_t sgu = unit / (uint32_t)H;
+  const int64_t sg = plan.seg_order ? (int64_t)plan.seg_order[sgu] : (int64_t)sgu;
   int n, seg;
   if (plan.seg_off) {
     n = seq_of_chunk(sg, plan.seg_off, p.N, 0);
@@ -179,10 +181,11 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
     n = (int)sg;
     seg = 0;
   } else {
-    const int64_t nch_all = (p.T + kChunk - 1) / kChunk;
-    const int64_t segs = max((int64_t)1, (nch_all + plan.seg_chunks - 1) / plan.seg_chunks);
-    n = (int)(sg / segs);
-    seg = (int)(sg - (int64_t)n * segs);
+    const uint32_t nch_all = (uint32_t)((p.T + kChunk - 1) / kChunk);
+    const uint32_t sc = (uint32_t)plan.seg_chunks;
+    const uint32_t segs = max(1u, (nch_all + sc - 1) / sc);
+    n = (int)((uint32_t)sg / segs);
+    seg = (int)((uint32_t)sg - (uint32_t)n * segs);
   }
   const SeqInfo si = seq_info(n, p.cu, p.chunk_off, p.T);
   const int nch = (si.len + kChunk - 1) / kChunk;

@@ -290,7 +290,10 @@ Plan plan_uncached(const gdn_shape* s, const gdn_opts* o) {
   P.value_block = P.wy ? (int)s->dv : (s->qkv_dtype == GDN_BF16 && s->dv % 128 == 0 && vb_req != 64) ? 128 : 64;
   P.pass1_block = vb_req == 128 ? 128 : 64;
   P.wmax = (o && o->window_max_chunks > 0) ? o->window_max_chunks : kWindowMaxCap;
-  P.log_eps = (o && o->window_log_eps != 0.f) ? o->window_log_eps : (float)std::log(0x1p-24);
+  // default window tolerance: 2^-16 for bf16 storage (256 times below its unit
+  // roundoff 2^-8), 2^-24 for fp32 (its unit roundoff)
+  P.log_eps = (o && o->window_log_eps != 0.f) ? o->window_log_eps
+             : (float)std::log(s->qkv_dtype == GDN_BF16 ? 0x1p-16 : 0x1p-24);
   int64_t L = INT_MAX / 2;
   if (!(o && o->no_split) && P.max_chunks > 1) {
     if (o && o->force_segment_chunks > 0) {

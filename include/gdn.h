@@ -81,7 +81,8 @@ typedef struct gdn_opts {
   int32_t force_segment_chunks; /* >0: split into segments of this many chunks; 0: planner */
   int32_t force_correction;     /* 1: every split head uses the wrong-start correction
                                    (S*, M and the merge) instead of window-lookback starts */
-  float window_log_eps;         /* log of the window tolerance; 0 -> log(2^-24) */
+  float window_log_eps;         /* log of the window tolerance; 0 -> log(2^-16) for bf16
+                                   q/k/v, log(2^-24) for fp32 */
   int32_t window_max_chunks;    /* longest lookback window in chunks, 1..16; 0 -> 16 */
   float lambda1_us;             /* planner: cost of one chunk step; 0 -> built in */
   float lambda2_us;             /* planner: cost of one merge step; 0 -> built in */
