@@ -38,7 +38,7 @@ constexpr size_t kAlign = 256;
 //             simulated schedule (pass3_makespan: a unit's chunks, its start-up
 //             kStartSteps, kLookbackSteps for a segment after the first).  One-pass
 //             step(busy) = kStepBaseUs + kStepPerBusyUs * busy workgroups (HBM and L2
-//             contention: 3.1 us at 64 busy, 3.9 us at 256); two-kernel path: λ1.
+//             contention: 2.7 us at 64 busy, 3.7 us at 256); two-kernel path: λ1.
 //   K1        two-kernel path only: kK1FixedUs + kK1PerChunkHeadUs per chunk-head.
 //   split     kSplitFixedUs + kSplitPerChunkHeadUs per chunk-head: the gate sums, the
 //             gate scan and the launches of the correction stages (on a window-only
@@ -54,9 +54,9 @@ constexpr size_t kAlign = 256;
 constexpr float kLambda1Us = 3.8f;
 constexpr float kLambda2Us = 0.75f;
 constexpr double kStartSteps = 2.2;
-constexpr double kLookbackSteps = 3.2;
+constexpr double kLookbackSteps = 2.7;
 constexpr double kFwdFixedUs = 4.5;
-constexpr double kStepBaseUs = 2.88, kStepPerBusyUs = 0.0039;
+constexpr double kStepBaseUs = 2.42, kStepPerBusyUs = 0.0050;
 constexpr double kStepF32Us = 5.5;               // two-kernel step on fp32 inputs
 constexpr double kK1FixedUs = 10.0, kK1PerChunkHeadUs = 0.004, kCorrK1PerChunkHeadUs = 0.007;
 constexpr double kSplitFixedUs = 11.4, kSplitPerChunkHeadUs = 0.0021, kPackedTablesUs = 4.0;

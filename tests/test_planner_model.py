@@ -51,7 +51,7 @@ def test_chosen_length_minimises_the_model():
 # Whole-call times measured on MI355X (bench.py, 10 back-to-back calls after a warm-up,
 # default plan), and the share of (sequence, head) pairs without a lookback window
 # (workload 4: head 3 has no decay).
-MEASURED_US = {1: (47.3, 0.0), 2: (107.8, 0.0), 3: (365.4, 0.0), 4: (302.1, 0.25), 5: (312.1, 0.0)}
+MEASURED_US = {1: (46.7, 0.0), 2: (99.1, 0.0), 3: (342.6, 0.0), 4: (294.5, 0.25), 5: (291.4, 0.0)}
 
 
 @pytest.mark.parametrize("w", sorted(MEASURED_US))
