@@ -100,6 +100,7 @@ __global__ __launch_bounds__(256) void chunk_inverse_kernel(Problem p, E* __rest
   constexpr int NS = Cfg::NS, OS = Cfg::OS, ABS = Cfg::ABS, TCS = Cfg::TCS, TBS = Cfg::TBS;
   __shared__ __align__(16) float lds[4 * Cfg::PER_WAVE];
 
+  if (only.ncorr && *only.ncorr == 0u) return;   // no head takes the correction
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, q = lane >> 4;

@@ -57,6 +57,7 @@ __global__ __launch_bounds__(64 * MergeCfg<DK>::NW) void cp_merge_kernel(Problem
   __shared__ __align__(16) bf16 sHi[2][16 * HS];
   __shared__ __align__(16) bf16 sLo[2][16 * HS];
 
+  if (plan.cp.ncorr && *plan.cp.ncorr == 0u) return;   // no head takes the correction
   // XCD-aware decode of the 1-D grid: workgroup b runs on XCD b % 8; the column
   // blocks of unit u all go to XCD u % 8
   const int dv = p.dv;

@@ -237,6 +237,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
     sG = sGb[b]; sGam = sGamb[b]; sGamS = sGamSb[b]; sDec = sDecb[b]; sBet = sBetb[b];
   };
 
+  if constexpr (PASS == kPass1) {
+    if (plan.cp.ncorr && *plan.cp.ncorr == 0u) return;   // no head takes the correction
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar table reads
   const int r16 = lane & 15, q = lane >> 4;

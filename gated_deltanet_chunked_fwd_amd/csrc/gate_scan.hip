@@ -28,8 +28,10 @@ namespace gdn {
 
 // Per (chunk, head): the sum of the chunk's gates, as the last entry of the
 // chunk-local inclusive wave scan (one wave per chunk-head, lane = chunk row).
-__global__ __launch_bounds__(256) void chunk_gate_sums_kernel(Problem p, float* __restrict__ csum) {
+__global__ __launch_bounds__(256) void chunk_gate_sums_kernel(Problem p, float* __restrict__ csum,
+                                                              uint32_t* __restrict__ ncorr_zero) {
   const int lane = threadIdx.x & 63;
+  if (ncorr_zero && blockIdx.x == 0 && threadIdx.x == 0) *ncorr_zero = 0u;
   const int HG = (p.H + 3) / 4;
   const int64_t cg = blockIdx.x / HG;
   const int h = (int)(blockIdx.x % HG) * 4 + (threadIdx.x >> 6);
@@ -50,7 +52,8 @@ __global__ __launch_bounds__(NT) void gate_window_max_kernel(const float* __rest
                                                                        const int32_t* __restrict__ cu,
                                                                        const int32_t* __restrict__ chunk_off,
                                                                        int64_t T, int N, int H, int wmax,
-                                                                       uint32_t* __restrict__ best) {
+                                                                       uint32_t* __restrict__ best, float thr,
+                                                                       uint32_t* __restrict__ ncorr) {
   __shared__ float sums[NT + kWindowMaxCap];
   __shared__ float red[NT / 64 * kWindowMaxCap];
   const int nh = blockIdx.x, n = nh / H, h = nh % H;
@@ -60,6 +63,10 @@ __global__ __launch_bounds__(NT) void gate_window_max_kernel(const float* __rest
   const int w = threadIdx.x;   // thread w holds the maximum for runs of w + 1 chunks
   if (w < kWindowMaxCap)       // 0 = no run of that length
     best[nh * kWindowMaxCap + w] = (w < wmax && v > -INFINITY) ? ordered_bits(v) : 0u;
+  if (ncorr && w < 64) {       // wave 0: count the pair if no length is admissible (window_of)
+    const bool ok = w < kWindowMaxCap && w < min(wmax, nch) && v > -INFINITY && v <= thr;
+    if (__ballot(ok) == 0ull && w == 0 && nch > 1) atomicAdd(ncorr, 1u);
+  }
 }
 
 // Packed input: the chunk / segment offset tables, and (split plans) the order in
@@ -121,7 +128,8 @@ hipError_t launch_plan_tables(const int32_t* cu, int N, int seg_chunks, int32_t*
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s, KernelEvents ev) {
+hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s, KernelEvents ev,
+                                  uint32_t* ncorr_zero) {
   if (p.total_chunks == 0) {
     ev.record_empty(s);
     return hipSuccess;
@@ -129,12 +137,12 @@ hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s, 
   const int64_t blocks = p.total_chunks * ((p.H + 3) / 4);
   if (blocks > kMaxDispatchItems / 256) return hipErrorInvalidConfiguration;
   hipExtLaunchKernelGGL(chunk_gate_sums_kernel, dim3((unsigned)blocks), dim3(256), 0, s, ev.start, ev.stop, 0,
-                        p, csum);
+                        p, csum, ncorr_zero);
   return hipGetLastError();
 }
 
 hipError_t launch_gate_scan(const Problem& p, const float* csum, int64_t max_chunks, int wmax,
-                            uint32_t* best, hipStream_t s, KernelEvents ev) {
+                            uint32_t* best, hipStream_t s, KernelEvents ev, float thr, uint32_t* ncorr) {
   if (p.N == 0) {
     ev.record_empty(s);
     return hipSuccess;
@@ -143,10 +151,10 @@ hipError_t launch_gate_scan(const Problem& p, const float* csum, int64_t max_chu
   const dim3 grid((unsigned)(p.N * p.H));
   if (max_chunks > 512)
     hipExtLaunchKernelGGL(gate_window_max_kernel<1024>, grid, dim3(1024), 0, s, ev.start, ev.stop, 0, csum,
-                          p.cu, p.chunk_off, p.T, p.N, p.H, wmax, best);
+                          p.cu, p.chunk_off, p.T, p.N, p.H, wmax, best, thr, ncorr);
   else
     hipExtLaunchKernelGGL(gate_window_max_kernel<256>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, csum,
-                          p.cu, p.chunk_off, p.T, p.N, p.H, wmax, best);
+                          p.cu, p.chunk_off, p.T, p.N, p.H, wmax, best, thr, ncorr);
   return hipGetLastError();
 }
 

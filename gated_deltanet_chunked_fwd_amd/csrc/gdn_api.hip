@@ -417,7 +417,7 @@ bool runs_k1(const Plan& P) { return !P.wy || P.split; }
 struct Layout {
   size_t tmat = 0, chunk_off = 0, seg_off = 0, seg_order = 0, best = 0, csum = 0, sstar = 0, mcorr = 0,
          hstart = 0;
-  size_t gmat = 0, gvec = 0;
+  size_t gmat = 0, gvec = 0, ncorr = 0;
   bool has_seg_order = false;
   size_t total = 0;
 };
@@ -436,6 +436,7 @@ Layout layout(const gdn_shape* s, const Plan& P) {
   }
   L.best = take((size_t)s->N * s->H * kWindowMaxCap * sizeof(uint32_t));
   if (P.split) {
+    L.ncorr = take(sizeof(uint32_t));
     L.csum = take((size_t)P.total_chunks * s->H * sizeof(float));
     const size_t slots = (size_t)P.total_segs * s->H;
     L.sstar = take(slots * s->dk * s->dv * sizeof(float));
@@ -553,11 +554,14 @@ int run_stages(int first, int last, const void* q, const void* k, const void* v,
   // that take pass 1 (no admissible window), so it goes after the gate scan: the
   // inverse stage then forms the chunk gate sums alone.
   const bool k1_after_scan = P.wy && P.split && !forced;
+  // count of heads without a window (one-pass split plans): zeroed with the gate sums,
+  // added to by the gate scan, read first by every correction launch
+  uint32_t* ncorr = k1_after_scan ? reinterpret_cast<uint32_t*>(ws + L.ncorr) : nullptr;
   if (runs(GDN_STAGE_INVERSE)) {
     const gdn::KernelEvents ev = stage_events(opts, GDN_STAGE_INVERSE);
     hipError_t e = hipSuccess;
     if (!runs_k1(P)) ev.record_empty(stream);
-    else if (k1_after_scan) e = gdn::launch_chunk_gate_sums(p, csum, stream, ev);
+    else if (k1_after_scan) e = gdn::launch_chunk_gate_sums(p, csum, stream, ev, ncorr);
     else e = gdn::launch_chunk_inverse(p, tmat, csum, false, stream, ev);
     if (e != hipSuccess) return GDN_ERR_HIP;
   }
@@ -582,9 +586,10 @@ int run_stages(int first, int last, const void* q, const void* k, const void* v,
     plan.cp.hstart = reinterpret_cast<float*>(ws + L.hstart);
     plan.cp.gmat = L.gmat ? ws + L.gmat : nullptr;
     plan.cp.gvec = L.gvec ? reinterpret_cast<float*>(ws + L.gvec) : nullptr;
+    plan.cp.ncorr = ncorr;
     if (!plan.cp.force_correction && runs(GDN_STAGE_GATE_SCAN)) {
       if (gdn::launch_gate_scan(p, csum, P.max_chunks, P.wmax, best, stream,
-                                stage_events(opts, GDN_STAGE_GATE_SCAN)) != hipSuccess)
+                                stage_events(opts, GDN_STAGE_GATE_SCAN), plan.cp.thr, ncorr) != hipSuccess)
         return GDN_ERR_HIP;
     }
     if (runs(GDN_STAGE_CP_PASS1)) {
@@ -596,6 +601,7 @@ int run_stages(int first, int last, const void* q, const void* k, const void* v,
         only.best = best;
         only.wmax = P.wmax;
         only.thr = plan.cp.thr;
+        only.ncorr = ncorr;
         if (gdn::launch_chunk_inverse(p, tmat, nullptr, false, stream, gdn::KernelEvents{ev.start, nullptr},
                                       only) != hipSuccess)
           return GDN_ERR_HIP;

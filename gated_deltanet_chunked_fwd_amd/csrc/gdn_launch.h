@@ -43,6 +43,10 @@ struct CpBuffers {
   float* hstart;            // [total_segs, H, dk, dv] true segment start states
   void* gmat;               // long merge chains, per group of steps (slot of the group's first
   float* gvec;              // segment): composed map A (as mcorr) and offset b (as sstar)
+  // (nullable) count of (sequence, head) pairs without an admissible window, written
+  // by the gate scan: when it is zero the correction launches (restricted chunk
+  // inverse, pass 1, merge) return at once instead of finding that per unit
+  const uint32_t* ncorr;
 };
 
 // Merge chains of more steps than this run as a two-level tree (cp_merge.hip): about
@@ -90,9 +94,15 @@ struct KernelEvents {
     if (stop) (void)hipEventRecord(stop, s);
   }
 };
-hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s, KernelEvents ev = {});
+// ncorr_zero (nullable): the gate scan's counter of heads without a window, set to
+// zero here (the scan that follows adds to it).
+hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s, KernelEvents ev = {},
+                                  uint32_t* ncorr_zero = nullptr);
+// ncorr (nullable): adds 1 for every (sequence, head) of more than one chunk with no
+// admissible window under thr (the decision window_of() takes).
 hipError_t launch_gate_scan(const Problem& p, const float* csum, int64_t max_chunks, int wmax,
-                            uint32_t* best, hipStream_t s, KernelEvents ev = {});
+                            uint32_t* best, hipStream_t s, KernelEvents ev = {}, float thr = 0.f,
+                            uint32_t* ncorr = nullptr);
 hipError_t launch_gate_finalize(const Problem& p, const uint32_t* best, int wmax, float thr,
                                 int32_t* out, hipStream_t s);
 // max_steps: the most segment boundaries of any sequence (segments - 1).
@@ -104,6 +114,7 @@ struct HeadFilter {
   const uint32_t* best = nullptr;
   int wmax = 0;
   float thr = 0.f;
+  const uint32_t* ncorr = nullptr;   // as CpBuffers::ncorr
 };
 // csum (nullable): [total_chunks, H] per-chunk gate sums, written on the side.
 // full = false: T's zero upper-right 32 x 32 quadrant is left unwritten (the fused
