@@ -38,12 +38,12 @@ constexpr size_t kAlign = 256;
 //             simulated schedule (pass3_makespan: a unit's chunks, its start-up
 //             kStartSteps, kLookbackSteps for a segment after the first).  One-pass
 //             step(busy) = kStepBaseUs + kStepPerBusyUs * busy workgroups (HBM and L2
-//             contention: 2.7 us at 64 busy, 3.7 us at 256); two-kernel path: λ1.
+//             contention: 2.7 us at 64 busy, 3.8 us at 256); two-kernel path: λ1.
 //   K1        two-kernel path only: kK1FixedUs + kK1PerChunkHeadUs per chunk-head.
 //   split     kSplitFixedUs + kSplitPerChunkHeadUs per chunk-head: the gate sums, the
 //             gate scan and the launches of the correction stages (on a window-only
-//             problem they find nothing to do, but their grids still scale with the
-//             chunk-heads); packed input adds the table launch, kPackedTablesUs.
+//             problem they read the gate scan's count and return at once); packed
+//             input adds the table launch, kPackedTablesUs.
 //   corrected heads (no admissible window), per call: their chunk inverse
 //             (kK1FixedUs + kCorrK1PerChunkHeadUs per chunk-head), pass 1
 //             (kPass1FixedUs + kPass1StepUs * L per round of workgroups) and the merge
@@ -54,12 +54,12 @@ constexpr size_t kAlign = 256;
 constexpr float kLambda1Us = 3.8f;
 constexpr float kLambda2Us = 0.75f;
 constexpr double kStartSteps = 2.2;
-constexpr double kLookbackSteps = 2.7;
+constexpr double kLookbackSteps = 1.0;
 constexpr double kFwdFixedUs = 4.5;
-constexpr double kStepBaseUs = 2.42, kStepPerBusyUs = 0.0050;
+constexpr double kStepBaseUs = 2.37, kStepPerBusyUs = 0.0055;
 constexpr double kStepF32Us = 5.5;               // two-kernel step on fp32 inputs
 constexpr double kK1FixedUs = 10.0, kK1PerChunkHeadUs = 0.004, kCorrK1PerChunkHeadUs = 0.007;
-constexpr double kSplitFixedUs = 11.4, kSplitPerChunkHeadUs = 0.0021, kPackedTablesUs = 4.0;
+constexpr double kSplitFixedUs = 17.5, kSplitPerChunkHeadUs = 0.0, kPackedTablesUs = 4.0;
 constexpr double kCorrReplacesUs = 8.0;
 constexpr double kPass1FixedUs = 3.0, kPass1StepUs = 2.0;
 constexpr double kMergeFixedUs = 7.0, kTreeFixedUs = 35.4, kTreeSqrtUs = 3.18;
