@@ -40,7 +40,9 @@ struct MergeCfg {
   static constexpr int NW = DK / 16;     // waves, one 16-row tile each
   static constexpr int NKS = DK / 32;    // contraction steps
   static constexpr int HS = DK + 8;      // row stride of the bf16 state copies
-  static constexpr int NSET = DK == 128 ? 4 : 6;   // operand sets in flight (registers permitting)
+  // operand sets in flight: at DK = 128 (8 waves, 256 registers) four sets spill 60
+  // registers and two run the 63-step chain of the long workload 12 us faster
+  static constexpr int NSET = DK == 128 ? 2 : 6;
 };
 
 // kRun: steps of one group from its start (or the whole chain from h0);
