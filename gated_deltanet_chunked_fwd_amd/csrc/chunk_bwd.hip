@@ -28,11 +28,13 @@
 // the chunks in reverse, recomputing each chunk's intermediates from its checkpoint.
 // dV and dh0 of its columns are final; dQ, dK, dbeta and dg are sums over all value
 // columns, so each workgroup writes its share in fp32 and a second kernel adds the
-// shares.  Arithmetic is plain fp32 (inputs converted on load), one thread per output
-// element of each product, the chunk's matrices in LDS and K, Q, V, dO read from
-// global memory (L1/L2 resident within a chunk).  1024 threads per workgroup: the
-// products' inner loops wait on those reads, and 16 waves hide 2.5x more of the
-// latency than 4 (Qwen-like shape: 90 ms with 256 threads, 54 with 512, 36 with 1024).
+// shares.  Arithmetic is plain fp32 (inputs converted on load), the chunk's matrices
+// in LDS, K, Q, V and dO read from global memory (L1/L2 resident within a chunk) as
+// runs of eight consecutive elements (one 16-byte load for bf16): every product
+// gives each thread a run of eight outputs, or eight contraction terms, per load.
+// P = (Q K^T) * Gamma is formed once per chunk, so no exponential sits in an inner
+// loop.  1024 threads per workgroup: the inner loops wait on those reads, and 16
+// waves hide more of the latency than 4.
 #include <algorithm>
 
 #include "gdn_device.h"
@@ -43,22 +45,48 @@ namespace gdn {
 namespace {
 
 constexpr int kBwdCols = kBwdColumnBlock;  // value columns per workgroup
-constexpr int kBwdThreads = 1024;
+constexpr int kBwdThreads = 512;
 constexpr int NS = kChunk + 1;            // row stride (floats) of chunk x chunk LDS matrices
 constexpr int CS = kBwdCols + 1;          // row stride of chunk x 32 and dk x 32 LDS matrices
 
 template <typename E>
 __device__ __forceinline__ float ldf(const E* p, int64_t i) { return (float)p[i]; }
 
+// Eight consecutive elements as fp32 (p 16-byte aligned for bf16, 32-byte for fp32).
+__device__ __forceinline__ void ld8(const bf16* p, float* o) {
+  const uint4 r = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(w[i] << 16);
+    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void ld8(const float* p, float* o) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+  o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+
+// Sum over the 16 consecutive lanes of a row group (a row's partial sums).
+__device__ __forceinline__ float row16_sum(float x) {
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
 }  // namespace
 
 template <typename E, int DK>
 __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdArgs a) {
+  static_assert(kBwdCols == 32 && DK % 8 == 0, "thread mappings below");
+  constexpr int D8 = DK / 8;             // runs of eight along dk
   __shared__ float sKK[kChunk * NS], sT[kChunk * NS], sQK[kChunk * NS], sM[kChunk * NS];
-  __shared__ float sKh[kChunk * CS], sQh[kChunk * CS], sVp[kChunk * CS], sU[kChunk * CS];
+  __shared__ float sKh[kChunk * CS], sVp[kChunk * CS], sU[kChunk * CS];
   __shared__ float sdU[kChunk * CS], sdR[kChunk * CS];
   __shared__ float sH[DK * CS], sdH[DK * CS];
-  __shared__ float sG[kChunk], sGam[kChunk], sD[kChunk], sBet[kChunk], sdG[kChunk], sDD[kChunk];
+  __shared__ float sG[kChunk], sGam[kChunk], sD[kChunk], sBet[kChunk], sdG[kChunk], sDD[kChunk], sQhY[kChunk];
   __shared__ float sRed[kBwdThreads / 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -78,11 +106,13 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
   const float scale = p.scale;
   const int64_t tot = a.total_tokens;
 
-  auto Kv = [&](int i, int d) { return ldf(Kg, (int64_t)i * rqk + d); };
-  auto Qv = [&](int i, int d) { return ldf(Qg, (int64_t)i * rqk + d); };
+  auto Krow = [&](int i) { return Kg + (int64_t)i * rqk; };
+  auto Qrow = [&](int i) { return Qg + (int64_t)i * rqk; };
+  auto DOrow = [&](int i) { return DOg + (int64_t)i * rv; };
   auto gam_ij = [&](int i, int j) { return expf(sG[i] - sG[j]); };   // j <= i
 
-  // ---- the chunk's gates, K K^T (lower), K h, A -> T, V', U (the forward quantities)
+  // ---- the chunk's gates, K K^T (lower), P = (Q K^T) * Gamma (lower, backward only),
+  //      K h, A -> T, V', U (the forward quantities)
   auto recompute = [&](int t0, int len, bool for_backward) {
     if (wave == 0) {
       float gv = 0.f, bv = 0.f;
@@ -103,48 +133,86 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
     for (int e = tid; e < len * len; e += kBwdThreads) {
       const int i = e / len, j = e % len;
       if (j <= i) {
+        const E* ki = Krow(t0 + i);
+        const E* kj = Krow(t0 + j);
+        const E* qi = Qrow(t0 + i);
         float acc = 0.f, accq = 0.f;
-        for (int d = 0; d < DK; ++d) {
-          const float kj = Kv(t0 + j, d);
-          acc += Kv(t0 + i, d) * kj;
-          if (for_backward) accq += Qv(t0 + i, d) * kj;
+#pragma unroll 2
+        for (int d = 0; d < DK; d += 8) {
+          float x[8], y[8], z[8];
+          ld8(ki + d, x);
+          ld8(kj + d, y);
+          if (for_backward) ld8(qi + d, z);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            acc += x[u] * y[u];
+            if (for_backward) accq += z[u] * y[u];
+          }
         }
         sKK[i * NS + j] = acc;
-        if (for_backward) sQK[i * NS + j] = accq;
+        if (for_backward) sQK[i * NS + j] = accq * gam_ij(i, j);
       }
     }
     for (int e = tid; e < len * kBwdCols; e += kBwdThreads) {
       const int i = e / kBwdCols, j = e % kBwdCols;
-      float acc = 0.f, accq = 0.f;
-      for (int d = 0; d < DK; ++d) {
-        const float hv = sH[d * CS + j];
-        acc += Kv(t0 + i, d) * hv;
-        if (for_backward) accq += Qv(t0 + i, d) * hv;
+      const E* ki = Krow(t0 + i);
+      float acc = 0.f;
+#pragma unroll 2
+      for (int d = 0; d < DK; d += 8) {
+        float x[8];
+        ld8(ki + d, x);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += x[u] * sH[(d + u) * CS + j];
       }
       sKh[i * CS + j] = acc;
-      if (for_backward) sQh[i * CS + j] = accq;
     }
     __syncthreads();
-    // A (strict lower) into sM, then T = (I + A)^{-1}: thread j solves column j
-    for (int e = tid; e < len * len; e += kBwdThreads) {
-      const int i = e / len, j = e % len;
-      sM[i * NS + j] = j < i ? sBet[i] * gam_ij(i, j) * sKK[i * NS + j] : 0.f;
+    // A (strict lower; zero elsewhere over the whole 64 x 64, rows past a partial
+    // chunk's end included) into sM
+    for (int e = tid; e < kChunk * kChunk; e += kBwdThreads) {
+      const int i = e / kChunk, j = e % kChunk;
+      sM[i * NS + j] = (j < i && i < len) ? sBet[i] * gam_ij(i, j) * sKK[i * NS + j] : 0.f;
     }
     for (int e = tid; e < len * kBwdCols; e += kBwdThreads) {
       const int i = e / kBwdCols, j = e % kBwdCols;
       sVp[i * CS + j] = ldf(Vg, (int64_t)(t0 + i) * rv + j) - sGam[i] * sKh[i * CS + j];
     }
     __syncthreads();
-    if (tid < len) {
-      const int j = tid;
-      for (int i = 0; i < len; ++i) {
-        float x = i == j ? 1.f : 0.f;
-        if (i > j)
-          for (int m = j; m < i; ++m) x -= sM[i * NS + m] * sT[m * NS + j];
-        sT[i * NS + j] = x;
+    // T = (I + A)^{-1} by 16 x 16 blocks: the diagonal blocks by forward substitution
+    // (one thread per (block, column)), then the blocks below the diagonal, by
+    // distance from it: T_ab = -T_aa X, X = sum_{k=b}^{a-1} A_ak T_kb (sdU as scratch)
+    if (tid < kChunk) {
+      const int o = 16 * (tid >> 4), c = tid & 15;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = r == c ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < r; ++m)
+          if (m >= c) v -= sM[(o + r) * NS + o + m] * x[m];
+        x[r] = r >= c ? v : 0.f;
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sT[(o + r) * NS + o + c] = x[r];
     }
     __syncthreads();
+    for (int dist = 1; dist < 4; ++dist) {
+      const int nb = 4 - dist;   // blocks (a, a - dist), a = dist .. 3
+      for (int e = tid; e < nb * 256; e += kBwdThreads) {
+        const int a16 = 16 * (dist + e / 256), r = (e >> 4) & 15, c = e & 15, b16 = a16 - 16 * dist;
+        float acc = 0.f;
+        for (int m = b16; m < a16; ++m) acc += sM[(a16 + r) * NS + m] * sT[m * NS + b16 + c];
+        sdU[(a16 + r) * CS + c] = acc;
+      }
+      __syncthreads();
+      for (int e = tid; e < nb * 256; e += kBwdThreads) {
+        const int a16 = 16 * (dist + e / 256), r = (e >> 4) & 15, c = e & 15, b16 = a16 - 16 * dist;
+        float acc = 0.f;
+        for (int m = 0; m <= r; ++m) acc += sT[(a16 + r) * NS + a16 + m] * sdU[(a16 + m) * CS + c];
+        sT[(a16 + r) * NS + b16 + c] = -acc;
+      }
+      __syncthreads();
+    }
     for (int e = tid; e < len * kBwdCols; e += kBwdThreads) {
       const int i = e / kBwdCols, j = e % kBwdCols;
       float acc = 0.f;
@@ -171,11 +239,20 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
     }
     recompute(t0, len, false);
     const float gn = expf(sG[len - 1]);
-    for (int e = tid; e < DK * kBwdCols; e += kBwdThreads) {
-      const int i = e / kBwdCols, j = e % kBwdCols;
-      float acc = 0.f;
-      for (int m = 0; m < len; ++m) acc += sD[m] * Kv(t0 + m, i) * sU[m * CS + j];
-      sH[i * CS + j] = gn * sH[i * CS + j] + acc;
+    // h <- gamma_n h + K^T diag(d) U: a thread owns rows i8 .. i8 + 7 of one column
+    for (int e = tid; e < D8 * kBwdCols; e += kBwdThreads) {
+      const int i8 = (e / kBwdCols) * 8, j = e % kBwdCols;
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+      for (int m = 0; m < len; ++m) {
+        float x[8];
+        ld8(Krow(t0 + m) + i8, x);
+        const float du = sD[m] * sU[m * CS + j];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] += x[u] * du;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sH[(i8 + u) * CS + j] = gn * sH[(i8 + u) * CS + j] + acc[u];
     }
     __syncthreads();
   }
@@ -196,26 +273,43 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
     __syncthreads();
     recompute(t0, len, true);
     const float gn = expf(sG[len - 1]);
-    auto dY = [&](int i, int j) { return scale * ldf(DOg, (int64_t)(t0 + i) * rv + j); };
     // K dh' (into sdR for now) and dd_i = sum_j U_ij (K dh')_ij
     for (int e = tid; e < len * kBwdCols; e += kBwdThreads) {
       const int i = e / kBwdCols, j = e % kBwdCols;
+      const E* ki = Krow(t0 + i);
       float acc = 0.f;
-      for (int d = 0; d < DK; ++d) acc += Kv(t0 + i, d) * sdH[d * CS + j];
+#pragma unroll 2
+      for (int d = 0; d < DK; d += 8) {
+        float x[8];
+        ld8(ki + d, x);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += x[u] * sdH[(d + u) * CS + j];
+      }
       sdR[i * CS + j] = acc;
     }
     __syncthreads();
-    if (tid < len) {
-      float acc = 0.f;
-      for (int j = 0; j < kBwdCols; ++j) acc += sU[tid * CS + j] * sdR[tid * CS + j];
-      sDD[tid] = acc;
+    // (16 lanes per row: the rows' reductions below are all split this way)
+    for (int e = tid; e < len * 16; e += kBwdThreads) {
+      const int i = e >> 4, pp = e & 15;
+      const float acc = row16_sum(sU[i * CS + pp] * sdR[i * CS + pp] + sU[i * CS + pp + 16] * sdR[i * CS + pp + 16]);
+      if (pp == 0) sDD[i] = acc;
     }
-    // dU = diag(d) K dh' + P^T dY,  P_mi = QK_mi Gamma_mi (i <= m)
-    for (int e = tid; e < len * kBwdCols; e += kBwdThreads) {
-      const int i = e / kBwdCols, j = e % kBwdCols;
-      float acc = sD[i] * sdR[i * CS + j];
-      for (int m = i; m < len; ++m) acc += sQK[m * NS + i] * gam_ij(m, i) * dY(m, j);
-      sdU[i * CS + j] = acc;
+    // dU = diag(d) K dh' + P^T dY: a thread owns columns j8 .. j8 + 7 of one row
+    for (int e = tid; e < len * (kBwdCols / 8); e += kBwdThreads) {
+      const int i = e / (kBwdCols / 8), j8 = (e % (kBwdCols / 8)) * 8;
+      float acc[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] = sD[i] * sdR[i * CS + j8 + u];
+#pragma unroll 2
+      for (int m = i; m < len; ++m) {
+        float o[8];
+        ld8(DOrow(t0 + m) + j8, o);
+        const float pm = scale * sQK[m * NS + i];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] += pm * o[u];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sdU[i * CS + j8 + u] = acc[u];
     }
     __syncthreads();
     // dR = T^T dU;  dP = lower(dY U^T) into sM
@@ -228,23 +322,32 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
     for (int e = tid; e < len * len; e += kBwdThreads) {
       const int i = e / len, j = e % len;
       float acc = 0.f;
-      if (j <= i)
-        for (int k2 = 0; k2 < kBwdCols; ++k2) acc += dY(i, k2) * sU[j * CS + k2];
+      if (j <= i) {
+#pragma unroll 2
+        for (int k8 = 0; k8 < kBwdCols; k8 += 8) {
+          float o[8];
+          ld8(DOrow(t0 + i) + k8, o);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) acc += o[u] * sU[j * CS + k8 + u];
+        }
+        acc *= scale;
+      }
       sM[i * NS + j] = acc;
     }
     __syncthreads();
-    // dV = diag(beta) dR; the Gamma gradient of P: E_ij = dP_ij QK_ij Gamma_ij
+    // dV = diag(beta) dR; the Gamma gradient of P: E_ij = dP_ij P_ij
     E* dVg = reinterpret_cast<E*>(a.dv) + si.tok0 * rv + (int64_t)h * dv + col0;
     for (int e = tid; e < len * kBwdCols; e += kBwdThreads) {
       const int i = e / kBwdCols, j = e % kBwdCols;
       dVg[(int64_t)(t0 + i) * rv + j] = (E)(sBet[i] * sdR[i * CS + j]);
     }
-    if (tid < len) {
-      const int i = tid;
+    for (int e = tid; e < len * 16; e += kBwdThreads) {
+      const int i = e >> 4, pp = e & 15;
       float r = 0.f, cs = 0.f;
-      for (int j = 0; j <= i; ++j) r += sM[i * NS + j] * sQK[i * NS + j] * gam_ij(i, j);
-      for (int m = i; m < len; ++m) cs += sM[m * NS + i] * sQK[m * NS + i] * gam_ij(m, i);
-      sdG[i] = r - cs;
+      for (int j = pp; j <= i; j += 16) r += sM[i * NS + j] * sQK[i * NS + j];
+      for (int m = i + pp; m < len; m += 16) cs += sM[m * NS + i] * sQK[m * NS + i];
+      const float v = row16_sum(r - cs);
+      if (pp == 0) sdG[i] = v;
     }
     __syncthreads();
     // sQK <- dP * Gamma (lower);  then dA = strict_lower(-dR U^T) into sM
@@ -262,19 +365,18 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
     }
     __syncthreads();
     // dbeta share: rowsum(dR * V') + sum_j dA_ij KK_ij Gamma_ij; the Gamma gradient of A
-    if (tid < len) {
-      const int i = tid;
-      float db = 0.f;
-      for (int j = 0; j < kBwdCols; ++j) db += sdR[i * CS + j] * sVp[i * CS + j];
-      float r = 0.f, cs = 0.f;
-      for (int j = 0; j < i; ++j) {
-        const float t = sM[i * NS + j] * sKK[i * NS + j] * gam_ij(i, j);
-        db += t;
-        r += sBet[i] * t;
+    for (int e = tid; e < len * 16; e += kBwdThreads) {
+      const int i = e >> 4, pp = e & 15;
+      float db = sdR[i * CS + pp] * sVp[i * CS + pp] + sdR[i * CS + pp + 16] * sVp[i * CS + pp + 16];
+      float t = 0.f, cs = 0.f;
+      for (int j = pp; j < i; j += 16) t += sM[i * NS + j] * sKK[i * NS + j] * gam_ij(i, j);
+      for (int m = i + 1 + pp; m < len; m += 16) cs += sBet[m] * sM[m * NS + i] * sKK[m * NS + i] * gam_ij(m, i);
+      db = row16_sum(db + t);
+      const float dgA = row16_sum(sBet[i] * t - cs);
+      if (pp == 0) {
+        sdG[i] += dgA;
+        a.dbeta_p[((int64_t)blk * tot + si.tok0 + t0 + i) * H + h] = db;
       }
-      for (int m = i + 1; m < len; ++m) cs += sBet[m] * sM[m * NS + i] * sKK[m * NS + i] * gam_ij(m, i);
-      sdG[i] += r - cs;
-      a.dbeta_p[((int64_t)blk * tot + si.tok0 + t0 + i) * H + h] = db;
     }
     __syncthreads();
     // sKK <- dB = diag(beta) dA * Gamma (strict lower; zero elsewhere)
@@ -283,27 +385,59 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
       sKK[i * NS + j] = j < i ? sBet[i] * sM[i * NS + j] * gam_ij(i, j) : 0.f;
     }
     __syncthreads();
-    // shares of dQ and dK (the K K^T gradient enters as (dB + dB^T) K, merged)
-    for (int e = tid; e < len * DK; e += kBwdThreads) {
-      const int i = e / DK, d = e % DK;
-      float dq = 0.f, dk = 0.f, hdy = 0.f, udh = 0.f, rvh = 0.f;
+    // shares of dQ and dK (the K K^T gradient enters as (dB + dB^T) K, merged); a
+    // thread owns columns d8 .. d8 + 7 of one row.  The Y = Q h part of gamma's
+    // gradient, sum_j (Q h)_ij dY_ij = sum_d Q_id (dY h^T)_id, is summed on the side.
+    for (int e = tid; e < len * D8; e += kBwdThreads) {
+      const int i = e / D8, d8 = (e % D8) * 8;
+      float hdy[8], udh[8], rvh[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) hdy[u] = udh[u] = rvh[u] = 0.f;
+#pragma unroll 2
       for (int j = 0; j < kBwdCols; ++j) {
-        const float hv = sH[d * CS + j];
-        hdy += dY(i, j) * hv;
-        udh += sU[i * CS + j] * sdH[d * CS + j];
-        rvh += sBet[i] * sdR[i * CS + j] * hv;
+        const float dy = scale * ldf(DOg, (int64_t)(t0 + i) * rv + j);
+        const float uu = sU[i * CS + j], rr = sBet[i] * sdR[i * CS + j];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float hv = sH[(d8 + u) * CS + j];
+          hdy[u] += dy * hv;
+          udh[u] += uu * sdH[(d8 + u) * CS + j];
+          rvh[u] += rr * hv;
+        }
       }
-      dq = sGam[i] * hdy;
-      dk = sD[i] * udh - sGam[i] * rvh;
+      float dq[8], dk[8], qi[8];
+      ld8(Qrow(t0 + i) + d8, qi);
+      float qhy = 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        qhy += qi[u] * hdy[u];
+        dq[u] = sGam[i] * hdy[u];
+        dk[u] = sD[i] * udh[u] - sGam[i] * rvh[u];
+      }
+#pragma unroll 1
       for (int m = 0; m < len; ++m) {
-        const float km = Kv(t0 + m, d);
-        if (m <= i) dq += sQK[i * NS + m] * km;
-        if (m >= i) dk += sQK[m * NS + i] * Qv(t0 + m, d);
-        dk += (sKK[i * NS + m] + sKK[m * NS + i]) * km;
+        float km[8], qm[8];
+        ld8(Krow(t0 + m) + d8, km);
+        ld8(Qrow(t0 + m) + d8, qm);
+        const float pq = sQK[i * NS + m];                      // zero for m > i
+        const float pk = m >= i ? sQK[m * NS + i] : 0.f;
+        const float bb = sKK[i * NS + m] + sKK[m * NS + i];    // dB strict lower, zero elsewhere
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          dq[u] += pq * km[u];
+          dk[u] += pk * qm[u] + bb * km[u];
+        }
       }
-      const int64_t o = (((int64_t)blk * tot + si.tok0 + t0 + i) * H + h) * DK + d;
-      a.dq_p[o] = dq;
-      a.dk_p[o] = dk;
+      const int64_t o = (((int64_t)blk * tot + si.tok0 + t0 + i) * H + h) * DK + d8;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        a.dq_p[o + u] = dq[u];
+        a.dk_p[o + u] = dk[u];
+      }
+      // the D8 threads of row i are consecutive lanes of one wave
+#pragma unroll
+      for (int off = D8 / 2; off >= 1; off >>= 1) qhy += __shfl_xor(qhy, off, 64);
+      if (d8 == 0) sQhY[i] = qhy;
     }
     // gamma_n's gradient: <h, dh'> over this block's columns (workgroup reduction)
     float part = 0.f;
@@ -313,35 +447,43 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
     }
     for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
     if (lane == 0) sRed[wave] = part;
+    __syncthreads();
     // the gamma and d gradients into dG
-    if (tid < len) {
-      const int i = tid;
-      float dgam = 0.f;
-      for (int j = 0; j < kBwdCols; ++j)
-        dgam += sQh[i * CS + j] * dY(i, j) - sBet[i] * sdR[i * CS + j] * sKh[i * CS + j];
-      sdG[i] += dgam * sGam[i] - sDD[i] * sD[i];
+    for (int e = tid; e < len * 16; e += kBwdThreads) {
+      const int i = e >> 4, pp = e & 15;
+      const float rk = sdR[i * CS + pp] * sKh[i * CS + pp] + sdR[i * CS + pp + 16] * sKh[i * CS + pp + 16];
+      const float dgam = sQhY[i] - sBet[i] * row16_sum(rk);
+      if (pp == 0) sdG[i] += dgam * sGam[i] - sDD[i] * sD[i];
     }
     __syncthreads();
-    if (tid == 0) {
-      float dgn = 0.f, ddd = 0.f;
-      for (int w = 0; w < kBwdThreads / 64; ++w) dgn += sRed[w];
-      for (int m = 0; m < len; ++m) ddd += sDD[m] * sD[m];
-      sdG[len - 1] += ddd + dgn * gn;
+    // gamma_n's and d's gradients into the last row, then dg = reverse cumsum of dG
+    if (wave == 0) {
+      float x = (lane < len ? sDD[lane] * sD[lane] : 0.f) + (lane < kBwdThreads / 64 ? sRed[lane] * gn : 0.f);
+      for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+      const float gv = lane < len ? sdG[lane] + (lane == len - 1 ? x : 0.f) : 0.f;
+      const float pre = wave_inclusive_scan(gv);
+      const float total = __shfl(pre, 63, 64);
+      if (lane < len) a.dg_p[((int64_t)blk * tot + si.tok0 + t0 + lane) * H + h] = total - pre + gv;
     }
-    __syncthreads();
-    // dg share = reverse cumsum of dG over the chunk
-    if (tid < len) {
-      float acc = 0.f;
-      for (int m = tid; m < len; ++m) acc += sdG[m];
-      a.dg_p[((int64_t)blk * tot + si.tok0 + t0 + tid) * H + h] = acc;
-    }
-    // dh = gamma_n dh' + Q^T diag(gamma) dY - K^T diag(gamma beta) dR (in place)
-    for (int e = tid; e < DK * kBwdCols; e += kBwdThreads) {
-      const int i = e / kBwdCols, j = e % kBwdCols;
-      float acc = gn * sdH[i * CS + j];
-      for (int m = 0; m < len; ++m)
-        acc += sGam[m] * (Qv(t0 + m, i) * dY(m, j) - Kv(t0 + m, i) * sBet[m] * sdR[m * CS + j]);
-      sdH[i * CS + j] = acc;
+    // dh = gamma_n dh' + Q^T diag(gamma) dY - K^T diag(gamma beta) dR (in place): a
+    // thread owns rows i8 .. i8 + 7 of one column
+    for (int e = tid; e < D8 * kBwdCols; e += kBwdThreads) {
+      const int i8 = (e / kBwdCols) * 8, j = e % kBwdCols;
+      float acc[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] = gn * sdH[(i8 + u) * CS + j];
+#pragma unroll 1
+      for (int m = 0; m < len; ++m) {
+        float qv[8], kv[8];
+        ld8(Qrow(t0 + m) + i8, qv);
+        ld8(Krow(t0 + m) + i8, kv);
+        const float ay = sGam[m] * scale * ldf(DOg, (int64_t)(t0 + m) * rv + j);
+        const float ar = sGam[m] * sBet[m] * sdR[m * CS + j];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] += qv[u] * ay - kv[u] * ar;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sdH[(i8 + u) * CS + j] = acc[u];
     }
     __syncthreads();
   }
