@@ -82,12 +82,19 @@ template <typename E, int DK>
 __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdArgs a) {
   static_assert(kBwdCols == 32 && DK % 8 == 0, "thread mappings below");
   constexpr int D8 = DK / 8;             // runs of eight along dk
+  // bf16 inputs: the chunk's K and dO rows are staged in LDS (16-byte rows padding
+  // keeps the row-strided reads of K K^T off a single bank group)
+  constexpr bool kStage = sizeof(E) == 2;
+  constexpr int KSS = DK + 8, DOS = kBwdCols + 8;
   __shared__ float sKK[kChunk * NS], sT[kChunk * NS], sQK[kChunk * NS], sM[kChunk * NS];
-  __shared__ float sKh[kChunk * CS], sVp[kChunk * CS], sU[kChunk * CS];
+  __shared__ float sVp[kChunk * CS], sU[kChunk * CS];
   __shared__ float sdU[kChunk * CS], sdR[kChunk * CS];
   __shared__ float sH[DK * CS], sdH[DK * CS];
-  __shared__ float sG[kChunk], sGam[kChunk], sD[kChunk], sBet[kChunk], sdG[kChunk], sDD[kChunk], sQhY[kChunk];
+  __shared__ float sG[kChunk], sGam[kChunk], sD[kChunk], sBet[kChunk], sdG[kChunk], sDD[kChunk], sQhY[kChunk],
+      sKhR[kChunk];
   __shared__ float sRed[kBwdThreads / 64];
+  __shared__ __align__(16) E sKs[kStage ? kChunk * KSS : 8];
+  __shared__ __align__(16) E sDOs[kStage ? kChunk * DOS : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk = p.dv / kBwdCols;
@@ -110,10 +117,46 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
   auto Qrow = [&](int i) { return Qg + (int64_t)i * rqk; };
   auto DOrow = [&](int i) { return DOg + (int64_t)i * rv; };
   auto gam_ij = [&](int i, int j) { return expf(sG[i] - sG[j]); };   // j <= i
+  int ct0 = 0;   // first token of the chunk being processed
+  // eight K elements of chunk row i from dk column d; eight dO elements of row i from
+  // value column c; one dO element (dO, not yet scaled)
+  auto kld8 = [&](int i, int d, float* o) {
+    if constexpr (kStage) ld8(sKs + i * KSS + d, o);
+    else ld8(Krow(ct0 + i) + d, o);
+  };
+  auto dold8 = [&](int i, int c, float* o) {
+    if constexpr (kStage) ld8(sDOs + i * DOS + c, o);
+    else ld8(DOrow(ct0 + i) + c, o);
+  };
+  auto dos = [&](int i, int c) {
+    if constexpr (kStage) return (float)sDOs[i * DOS + c];
+    else return ldf(DOg, (int64_t)(ct0 + i) * rv + c);
+  };
+  // the chunk's K rows (and dO rows) into LDS; rows past a partial chunk's end are zero
+  auto stage = [&](int t0, int len, bool with_do) {
+    if constexpr (kStage) {
+      for (int e = tid; e < kChunk * D8; e += kBwdThreads) {
+        const int i = e / D8, d8 = (e % D8) * 8;
+        uint4 v = {0u, 0u, 0u, 0u};
+        if (i < len) v = *reinterpret_cast<const uint4*>(Krow(t0 + i) + d8);
+        *reinterpret_cast<uint4*>(sKs + i * KSS + d8) = v;
+      }
+      if (with_do) {
+        for (int e = tid; e < kChunk * (kBwdCols / 8); e += kBwdThreads) {
+          const int i = e / (kBwdCols / 8), c8 = (e % (kBwdCols / 8)) * 8;
+          uint4 v = {0u, 0u, 0u, 0u};
+          if (i < len) v = *reinterpret_cast<const uint4*>(DOrow(t0 + i) + c8);
+          *reinterpret_cast<uint4*>(sDOs + i * DOS + c8) = v;
+        }
+      }
+    }
+  };
 
   // ---- the chunk's gates, K K^T (lower), P = (Q K^T) * Gamma (lower, backward only),
   //      K h, A -> T, V', U (the forward quantities)
   auto recompute = [&](int t0, int len, bool for_backward) {
+    ct0 = t0;
+    stage(t0, len, for_backward);
     if (wave == 0) {
       float gv = 0.f, bv = 0.f;
       if (lane < len) {
@@ -133,15 +176,13 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
     for (int e = tid; e < len * len; e += kBwdThreads) {
       const int i = e / len, j = e % len;
       if (j <= i) {
-        const E* ki = Krow(t0 + i);
-        const E* kj = Krow(t0 + j);
         const E* qi = Qrow(t0 + i);
         float acc = 0.f, accq = 0.f;
 #pragma unroll 2
         for (int d = 0; d < DK; d += 8) {
           float x[8], y[8], z[8];
-          ld8(ki + d, x);
-          ld8(kj + d, y);
+          kld8(i, d, x);
+          kld8(j, d, y);
           if (for_backward) ld8(qi + d, z);
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
@@ -153,18 +194,18 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
         if (for_backward) sQK[i * NS + j] = accq * gam_ij(i, j);
       }
     }
+    // V' = V - diag(gamma) K h
     for (int e = tid; e < len * kBwdCols; e += kBwdThreads) {
       const int i = e / kBwdCols, j = e % kBwdCols;
-      const E* ki = Krow(t0 + i);
       float acc = 0.f;
 #pragma unroll 2
       for (int d = 0; d < DK; d += 8) {
         float x[8];
-        ld8(ki + d, x);
+        kld8(i, d, x);
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc += x[u] * sH[(d + u) * CS + j];
       }
-      sKh[i * CS + j] = acc;
+      sVp[i * CS + j] = ldf(Vg, (int64_t)(t0 + i) * rv + j) - expf(sG[i]) * acc;
     }
     __syncthreads();
     // A (strict lower; zero elsewhere over the whole 64 x 64, rows past a partial
@@ -172,10 +213,6 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
     for (int e = tid; e < kChunk * kChunk; e += kBwdThreads) {
       const int i = e / kChunk, j = e % kChunk;
       sM[i * NS + j] = (j < i && i < len) ? sBet[i] * gam_ij(i, j) * sKK[i * NS + j] : 0.f;
-    }
-    for (int e = tid; e < len * kBwdCols; e += kBwdThreads) {
-      const int i = e / kBwdCols, j = e % kBwdCols;
-      sVp[i * CS + j] = ldf(Vg, (int64_t)(t0 + i) * rv + j) - sGam[i] * sKh[i * CS + j];
     }
     __syncthreads();
     // T = (I + A)^{-1} by 16 x 16 blocks: the diagonal blocks by forward substitution
@@ -246,7 +283,7 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
 #pragma unroll 2
       for (int m = 0; m < len; ++m) {
         float x[8];
-        ld8(Krow(t0 + m) + i8, x);
+        kld8(m, i8, x);
         const float du = sD[m] * sU[m * CS + j];
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc[u] += x[u] * du;
@@ -276,12 +313,11 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
     // K dh' (into sdR for now) and dd_i = sum_j U_ij (K dh')_ij
     for (int e = tid; e < len * kBwdCols; e += kBwdThreads) {
       const int i = e / kBwdCols, j = e % kBwdCols;
-      const E* ki = Krow(t0 + i);
       float acc = 0.f;
 #pragma unroll 2
       for (int d = 0; d < DK; d += 8) {
         float x[8];
-        ld8(ki + d, x);
+        kld8(i, d, x);
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc += x[u] * sdH[(d + u) * CS + j];
       }
@@ -303,7 +339,7 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
 #pragma unroll 2
       for (int m = i; m < len; ++m) {
         float o[8];
-        ld8(DOrow(t0 + m) + j8, o);
+        dold8(m, j8, o);
         const float pm = scale * sQK[m * NS + i];
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc[u] += pm * o[u];
@@ -326,7 +362,7 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
 #pragma unroll 2
         for (int k8 = 0; k8 < kBwdCols; k8 += 8) {
           float o[8];
-          ld8(DOrow(t0 + i) + k8, o);
+          dold8(i, k8, o);
 #pragma unroll
           for (int u = 0; u < 8; ++u) acc += o[u] * sU[j * CS + k8 + u];
         }
@@ -395,7 +431,7 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
       for (int u = 0; u < 8; ++u) hdy[u] = udh[u] = rvh[u] = 0.f;
 #pragma unroll 2
       for (int j = 0; j < kBwdCols; ++j) {
-        const float dy = scale * ldf(DOg, (int64_t)(t0 + i) * rv + j);
+        const float dy = scale * dos(i, j);
         const float uu = sU[i * CS + j], rr = sBet[i] * sdR[i * CS + j];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -405,19 +441,21 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
           rvh[u] += rr * hv;
         }
       }
-      float dq[8], dk[8], qi[8];
+      float dq[8], dk[8], qi[8], ki[8];
       ld8(Qrow(t0 + i) + d8, qi);
-      float qhy = 0.f;
+      kld8(i, d8, ki);
+      float qhy = 0.f, khr = 0.f;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         qhy += qi[u] * hdy[u];
+        khr += ki[u] * rvh[u];
         dq[u] = sGam[i] * hdy[u];
         dk[u] = sD[i] * udh[u] - sGam[i] * rvh[u];
       }
 #pragma unroll 1
       for (int m = 0; m < len; ++m) {
         float km[8], qm[8];
-        ld8(Krow(t0 + m) + d8, km);
+        kld8(m, d8, km);
         ld8(Qrow(t0 + m) + d8, qm);
         const float pq = sQK[i * NS + m];                      // zero for m > i
         const float pk = m >= i ? sQK[m * NS + i] : 0.f;
@@ -436,8 +474,14 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
       }
       // the D8 threads of row i are consecutive lanes of one wave
 #pragma unroll
-      for (int off = D8 / 2; off >= 1; off >>= 1) qhy += __shfl_xor(qhy, off, 64);
-      if (d8 == 0) sQhY[i] = qhy;
+      for (int off = D8 / 2; off >= 1; off >>= 1) {
+        qhy += __shfl_xor(qhy, off, 64);
+        khr += __shfl_xor(khr, off, 64);
+      }
+      if (d8 == 0) {
+        sQhY[i] = qhy;
+        sKhR[i] = khr;
+      }
     }
     // gamma_n's gradient: <h, dh'> over this block's columns (workgroup reduction)
     float part = 0.f;
@@ -449,12 +493,9 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
     if (lane == 0) sRed[wave] = part;
     __syncthreads();
     // the gamma and d gradients into dG
-    for (int e = tid; e < len * 16; e += kBwdThreads) {
-      const int i = e >> 4, pp = e & 15;
-      const float rk = sdR[i * CS + pp] * sKh[i * CS + pp] + sdR[i * CS + pp + 16] * sKh[i * CS + pp + 16];
-      const float dgam = sQhY[i] - sBet[i] * row16_sum(rk);
-      if (pp == 0) sdG[i] += dgam * sGam[i] - sDD[i] * sD[i];
-    }
+    // (the K h part of gamma's gradient, beta_i sum_j dR_ij (K h)_ij =
+    // sum_d K_id (beta_i dR h^T)_id, was summed with the dK shares)
+    if (tid < len) sdG[tid] += (sQhY[tid] - sKhR[tid]) * sGam[tid] - sDD[tid] * sD[tid];
     __syncthreads();
     // gamma_n's and d's gradients into the last row, then dg = reverse cumsum of dG
     if (wave == 0) {
@@ -476,8 +517,8 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
       for (int m = 0; m < len; ++m) {
         float qv[8], kv[8];
         ld8(Qrow(t0 + m) + i8, qv);
-        ld8(Krow(t0 + m) + i8, kv);
-        const float ay = sGam[m] * scale * ldf(DOg, (int64_t)(t0 + m) * rv + j);
+        kld8(m, i8, kv);
+        const float ay = sGam[m] * scale * dos(m, j);
         const float ar = sGam[m] * sBet[m] * sdR[m * CS + j];
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc[u] += qv[u] * ay - kv[u] * ar;
