@@ -183,7 +183,11 @@ int gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const flo
  * Under a one-pass plan (gdn_plan_one_pass) no stage forms T for the forward pass:
  * an unsplit plan's GDN_STAGE_INVERSE enqueues nothing; a split plan's forms only
  * the chunk gate sums, and its GDN_STAGE_CP_PASS1 first forms T for the heads
- * without an admissible lookback window (the only ones pass 1 reads it for).
+ * without an admissible lookback window (the only ones pass 1 reads it for).  A
+ * split one-pass plan also keeps in the workspace a count of the (sequence, head)
+ * pairs without a window: GDN_STAGE_INVERSE zeroes it, GDN_STAGE_GATE_SCAN adds to
+ * it, and GDN_STAGE_CP_PASS1 and GDN_STAGE_CP_MERGE do nothing when it is zero (a
+ * workspace that receives regions from elsewhere runs those two stages first).
  * With packed sequences every stage call first rebuilds, from cu_seqlens, the
  * chunk and segment tables it indexes by (one small launch; gdn_chunk_fwd builds
  * them once), so no stage indexes by anything a caller or an earlier stage left in
