@@ -35,5 +35,5 @@ from .chunked import (  # noqa: F401
     window_forward,
     segment_transition,
 )
-from .gate import window_chunks, window_chunks_all  # noqa: F401
+from .gate import segment_windows, window_chunks, window_chunks_all  # noqa: F401
 from .backward import chunked_backward, token_backward_numpy  # noqa: F401

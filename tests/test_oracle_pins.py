@@ -373,6 +373,58 @@ def test_window_decision_all_packed_hand_case():
     assert gate.window_chunks_all(gd, log_eps=le).tolist() == [[1, 0], [0, 1]]
 
 
+def _chunks(sums, H=1):
+    """Gates [1, 64 * len(sums), H] whose chunk c sums to sums[c] (every token of a
+    chunk equal), the same on every head unless sums is a list of per-head lists."""
+    cols = sums if H > 1 else [sums]
+    g = np.stack([np.repeat(np.asarray(c, dtype=float) / 64.0, 64) for c in cols], axis=-1)
+    return g[None]
+
+
+def test_segment_windows_hand_cases():
+    """Per-segment windows worked by hand (log(2^-24) = -16.64): a segment start st
+    takes the smallest W whose W chunks before st sum to <= log eps, or W = st (the
+    window reaches the sequence start); a head with a start that has none takes the
+    correction (all its entries 0)."""
+    le = math.log(2.0 ** -24)
+    # -3.2 per chunk: 6 chunks needed (5 give -16.0); starts 8, 16, 24, 32
+    assert gate.segment_windows(_chunks([-3.2] * 40), 8, log_eps=le)[:, 0].tolist() == [0, 6, 6, 6, 6]
+    # L = 4: the start at chunk 4 reaches the sequence start with W = 4 (exact)
+    assert gate.segment_windows(_chunks([-3.2] * 16), 4, log_eps=le)[:, 0].tolist() == [0, 4, 6, 6]
+    # no decay: starts at 8 and 16 reach the sequence start (W = st <= 16) ...
+    assert gate.segment_windows(_chunks([0.0] * 24), 8, log_eps=le)[:, 0].tolist() == [0, 8, 16]
+    # ... but a start at 24 cannot: the whole head takes the correction
+    assert gate.segment_windows(_chunks([0.0] * 40), 8, log_eps=le)[:, 0].tolist() == [0, 0, 0, 0, 0]
+    # a weak stretch (chunks 10..13 without decay) inside the second segment only
+    # lengthens the window of the start right after it; the whole-sequence rule
+    # (window_chunks) needs 8 for every start
+    sums = [-5.0] * 32
+    sums[10:14] = [0.0] * 4
+    got = gate.segment_windows(_chunks(sums), 8, log_eps=le)[:, 0].tolist()
+    assert got == [0, 4, 8, 4], got
+    assert gate.window_chunks(np.repeat(np.asarray(sums) / 64.0, 64), log_eps=le) == 8
+    # w_max caps the search
+    assert gate.segment_windows(_chunks([-3.2] * 40), 8, log_eps=le, w_max=5)[:, 0].tolist() == [0, 0, 0, 0, 0]
+
+
+def test_segment_windows_packed_numbering_and_heads():
+    """Packed sequences (segments numbered over the sequences in order, empty and
+    one-segment sequences keep one row) and two heads with different gates."""
+    le = math.log(2.0 ** -24)
+    lens = [64 * 20, 64 * 3, 0, 64 * 9 + 5]
+    per_head = (-0.05, -0.3)   # per token: -3.2 / -19.2 per full chunk
+    g = np.concatenate([np.tile(np.array(per_head), (n, 1)) for n in lens])[None]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    got = gate.segment_windows(g, 8, cu_seqlens=cu, log_eps=le)
+    expect = [
+        [0, 0], [6, 1], [6, 1],   # 20 chunks: starts 8 and 16
+        [0, 0],                    # 3 chunks: one segment
+        [0, 0],                    # empty: one segment
+        [0, 0], [6, 1],            # 10 chunks (the last partial): start 8
+    ]
+    assert got.tolist() == expect, got.tolist()
+
+
 # ---------------------------------------------------------------- output magnitude
 
 
