@@ -34,7 +34,7 @@ class GdnOpts(ctypes.Structure):
 
 GDN_STAGE_INVERSE, GDN_STAGE_GATE_SCAN, GDN_STAGE_CP_PASS1, GDN_STAGE_CP_MERGE = 0, 1, 2, 3
 GDN_STAGE_FORWARD, GDN_NUM_STAGES = 4, 5
-GDN_REGION_CHUNK_INVERSE, GDN_REGION_WINDOWS, GDN_REGION_SEGMENT_MAPS = 0, 1, 2
+GDN_REGION_CHUNK_INVERSE, GDN_REGION_SEGMENT_WINDOWS, GDN_REGION_SEGMENT_MAPS = 0, 1, 2
 GDN_REGION_SEGMENT_STARTS, GDN_NUM_REGIONS = 3, 4
 STAGE_NAMES = ("chunk_inverse", "gate_scan", "cp_pass1", "cp_merge", "fused_forward")
 

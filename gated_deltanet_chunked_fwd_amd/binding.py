@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libgdn.so")
 from .abi import (EXPORTS, GDN_BF16, GDN_ERR_ARG, GDN_ERR_HIP, GDN_ERR_SCRATCH,  # noqa: F401
                   GDN_ERR_UNSUPPORTED, GDN_ERR_WORKSPACE, GDN_NOALLOC_SCRATCH_BYTES, GDN_F32, GDN_NUM_REGIONS, GDN_NUM_STAGES, GDN_OK,
                   GDN_REGION_CHUNK_INVERSE, GDN_REGION_SEGMENT_MAPS, GDN_REGION_SEGMENT_STARTS,
-                  GDN_REGION_WINDOWS, GDN_STAGE_CP_MERGE, GDN_STAGE_CP_PASS1, GDN_STAGE_FORWARD,
+                  GDN_REGION_SEGMENT_WINDOWS, GDN_STAGE_CP_MERGE, GDN_STAGE_CP_PASS1, GDN_STAGE_FORWARD,
                   GDN_STAGE_GATE_SCAN, GDN_STAGE_INVERSE, STAGE_NAMES, GdnOpts, GdnShape, declare,
                   make_opts)
 

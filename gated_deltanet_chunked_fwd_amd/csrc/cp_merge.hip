@@ -76,11 +76,10 @@ __global__ __launch_bounds__(64 * MergeCfg<DK>::NW) void cp_merge_kernel(Problem
   const int L = plan.seg_chunks;
   const int segs = (nch + L - 1) / L;
   if (segs < 2) return;
-  if (!plan.cp.force_correction && window_of(plan.cp.best, nh, nch, plan.cp.wmax, plan.cp.thr) > 0)
-    return;
   const int64_t sg0 =
       plan.seg_off ? plan.seg_off[n]
                    : (int64_t)n * max((int64_t)1, ((p.T + kChunk - 1) / kChunk + L - 1) / L);
+  if (!plan.cp.force_correction && plan.cp.seg_win[(sg0 + 1) * H + h] > 0) return;   // window head
   const int steps = segs - 1;
   const int ngroups = (steps + G - 1) / G;
   if (g >= ngroups) return;

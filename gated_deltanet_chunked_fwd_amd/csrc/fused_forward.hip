@@ -257,16 +257,31 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
   const int col0 = cb * BV;                // first value column of the workgroup
   const int wcol = wave * NCW;             // wave's first column inside the block
 
-  // Pass 1 numbers its units head-major, so the few heads that need it (all of
-  // their units run full segments) still spread over all XCDs; pass 3 numbers them
-  // segment-major, in the plan's segment order when there is one (packed input:
-  // longest segments first), so units dispatched together have similar lengths.
-  const int64_t nseg = plan.units / H;     // segments over all sequences
+  // Pass 1 takes the gate scan's work list when there is one: only units that run
+  // are dispatched, ahead of none that exit (exiting workgroups dispatched first
+  // leave the working ones packed two to a CU where one each would fit), and a
+  // pair's segments, one run of the list, spread over all XCDs.  Without it pass 1
+  // numbers every (segment, head) head-major, to the same spreading end.  Pass 3
+  // numbers them segment-major, in the plan's segment order when there is one
+  // (packed input: longest segments first), so units dispatched together have
+  // similar lengths.
   int h;
   int64_t sg;                              // global segment index
   if constexpr (PASS == kPass1) {
-    h = (int)(unit / nseg);
-    sg = unit - (int64_t)h * nseg;
+    if (plan.cp.p1_slots) {   // (entries read back are clamped to the slots)
+      if (unit >= (int64_t)plan.cp.ncorr[1]) return;
+      const int64_t segs_all =
+          plan.seg_off ? (int64_t)plan.seg_off[p.N]
+                       : (int64_t)p.N * max((int64_t)1, ((p.T + kChunk - 1) / kChunk + plan.seg_chunks - 1) /
+                                                            plan.seg_chunks);
+      const int64_t slot = min(max((int64_t)plan.cp.p1_slots[unit], (int64_t)0), segs_all * H - 1);
+      h = (int)(slot % H);
+      sg = slot / H;
+    } else {
+      const int64_t nseg = plan.units / H;   // segments over all sequences
+      h = (int)(unit / nseg);
+      sg = unit - (int64_t)h * nseg;
+    }
   } else {
     h = (int)(unit % H);
     sg = plan.seg_order ? plan.seg_order[unit / H] : unit / H;   // longest segments first
@@ -290,15 +305,21 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
   const int c_end = min(nch, c_begin + plan.seg_chunks);
   const int nh = n * H + h;
   const bool last_seg = c_end >= nch;
-  const int W = (plan.cp.best && !plan.cp.force_correction)
-                    ? window_of(plan.cp.best, nh, nch, plan.cp.wmax, plan.cp.thr) : 0;
+  // (clamped: a window read from a workspace the gate scan did not fill stays inside
+  // the segment's sequence)
+  const int W = (plan.cp.seg_win && !plan.cp.force_correction)
+                    ? min(max(plan.cp.seg_win[sg * H + h], 0), c_begin) : 0;
 
   // start state and the chunk range: [c_start, c_end) is run, O is written from c_out
   enum { kZero, kH0, kBuf, kEye };
   int init = kZero, c_start = c_begin, c_out = c_begin;
   bool mcols = false;   // pass 1: this block carries the transition-matrix columns
   if constexpr (PASS == kPass1) {
-    if (W > 0 || last_seg) return;     // window heads and last segments need no pass 1
+    // last segments and window heads need no pass 1; a head's windows are all set or
+    // all zero, and its second segment (there is one: this is not the last) holds one
+    if (last_seg) return;
+    if (plan.cp.seg_win && !plan.cp.force_correction && plan.cp.seg_win[(sg - seg + 1) * H + h] > 0)
+      return;
     mcols = col0 >= dv;
     init = mcols ? kEye : kZero;
     c_out = c_end;

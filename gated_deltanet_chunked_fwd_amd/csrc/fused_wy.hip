@@ -193,8 +193,10 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
   const int c_end = min(nch, c_begin + plan.seg_chunks);
   const int nh = n * H + h;
   const bool last_seg = c_end >= nch;
-  const int W = (plan.cp.best && !plan.cp.force_correction)
-                    ? window_of(plan.cp.best, nh, nch, plan.cp.wmax, plan.cp.thr) : 0;
+  // (clamped: a window read from a workspace the gate scan did not fill stays inside
+  // the segment's sequence)
+  const int W = (plan.cp.seg_win && !plan.cp.force_correction)
+                    ? min(max(plan.cp.seg_win[sg * H + h], 0), c_begin) : 0;
   // start state and chunk range: [c_start, c_end) is run, O is written from c_out
   enum { kZero, kH0, kBuf };
   int init = kZero, c_start = c_begin;

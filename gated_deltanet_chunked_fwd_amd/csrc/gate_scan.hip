@@ -1,6 +1,7 @@
-// Gate scan on gfx950: per (sequence, head), the largest gate sum over every run
-// of W consecutive chunks (W = 1..wmax), from which the window-lookback length
-// is decided.
+// Gate scan on gfx950: the window-lookback lengths.  The forward pass takes one per
+// segment start (the W chunks right before it); the stand-alone entry point one per
+// (sequence, head), from the largest gate sum over every run of W consecutive chunks
+// (W = 1..wmax).
 //
 // FlashQLA talk transcript (tokendh.com), sliding-window section: with alpha < 1
 // and ||I - beta k k^T|| <= 1 a state's influence decays by alpha per token, so a
@@ -9,18 +10,18 @@
 // cumsum) to pick the heads that may start a segment from a lookback window.
 //
 // Decision: the error of starting W chunks early from a zero state is at most
-// ||S_old|| exp(sum of g over those chunks), so W is admissible iff every run of W
-// consecutive chunks has gate sum <= log_eps - margin (margin 1e-3 absorbs the
-// fp32 summation error).  The smallest admissible W <= wmax is used; 0 = none.
+// ||S_old|| exp(sum of g over those chunks), so a start may use W if the W chunks
+// before it have gate sum <= log_eps - margin (margin 1e-3 absorbs the fp32
+// summation error), and a head may use W at every start if every run of W
+// consecutive chunks does.  The smallest such W <= wmax is used; 0 = none.
 //
 // The chunk gate sums come from the chunk-inverse kernel, which forms the chunk's
 // cumulative gate anyway (or, for the stand-alone entry point, from
 // chunk_gate_sums_kernel with the same wave scan, so both give identical sums).
-// gate_window_max: one block per (sequence, head) forms
-// the maximum run sum per W (block_run_max) and stores it in best[nh][W] (floats as
-// order-preserving uints; 0 = no such run, so no reset is needed).  window_of()
-// turns best[] into W wherever it is needed; gate_window_finalize writes it out for
-// the stand-alone entry point.
+// gate_window_max: one block per (sequence, head) forms the segment windows (forward
+// pass) or the maximum run sum per W (block_run_max) into best[nh][W] (floats as
+// order-preserving uints; 0 = no such run, so no reset is needed), which
+// gate_window_finalize turns into W for the stand-alone entry point (window_of).
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -31,7 +32,7 @@ namespace gdn {
 __global__ __launch_bounds__(256) void chunk_gate_sums_kernel(Problem p, float* __restrict__ csum,
                                                               uint32_t* __restrict__ ncorr_zero) {
   const int lane = threadIdx.x & 63;
-  if (ncorr_zero && blockIdx.x == 0 && threadIdx.x == 0) *ncorr_zero = 0u;
+  if (ncorr_zero && blockIdx.x == 0 && threadIdx.x < 2) ncorr_zero[threadIdx.x] = 0u;
   const int HG = (p.H + 3) / 4;
   const int64_t cg = blockIdx.x / HG;
   const int h = (int)(blockIdx.x % HG) * 4 + (threadIdx.x >> 6);
@@ -53,20 +54,65 @@ __global__ __launch_bounds__(NT) void gate_window_max_kernel(const float* __rest
                                                                        const int32_t* __restrict__ chunk_off,
                                                                        int64_t T, int N, int H, int wmax,
                                                                        uint32_t* __restrict__ best, float thr,
-                                                                       uint32_t* __restrict__ ncorr) {
+                                                                       uint32_t* __restrict__ ncorr, int seg_chunks,
+                                                                       const int32_t* __restrict__ seg_off,
+                                                                       int32_t* __restrict__ seg_win,
+                                                                       int32_t* __restrict__ p1_slots, int64_t p1_cap) {
   __shared__ float sums[NT + kWindowMaxCap];
   __shared__ float red[NT / 64 * kWindowMaxCap];
   const int nh = blockIdx.x, n = nh / H, h = nh % H;
   const SeqInfo si = seq_info(n, cu, chunk_off, T);
   const int nch = (si.len + kChunk - 1) / kChunk;
-  const float v = block_run_max<NT>(csum, si.chunk0, nch, H, h, wmax, sums, NT + kWindowMaxCap, red);
-  const int w = threadIdx.x;   // thread w holds the maximum for runs of w + 1 chunks
-  if (w < kWindowMaxCap)       // 0 = no run of that length
-    best[nh * kWindowMaxCap + w] = (w < wmax && v > -INFINITY) ? ordered_bits(v) : 0u;
-  if (ncorr && w < 64) {       // wave 0: count the pair if no length is admissible (window_of)
-    const bool ok = w < kWindowMaxCap && w < min(wmax, nch) && v > -INFINITY && v <= thr;
-    if (__ballot(ok) == 0ull && w == 0 && nch > 1) atomicAdd(ncorr, 1u);
+  // per-segment windows, first: the W chunks right before a segment start bound the
+  // error of starting it from zero W chunks early (one thread per start)
+  const int L = seg_chunks;
+  const int segs = seg_win ? max(1, (nch + L - 1) / L) : 0;
+  const int64_t sb = seg_off ? (int64_t)seg_off[n] : (int64_t)n * segs;   // dense: equal lengths
+  int miss = 0;
+  for (int j = 1 + (int)threadIdx.x; j < segs; j += NT) {
+    const int st = j * L, lim = min(wmax, st);
+    float c[kWindowMaxCap];   // the (up to) 16 chunk sums before the start, loaded at once
+#pragma unroll
+    for (int k = 0; k < kWindowMaxCap; ++k)   // index kept inside the sequence
+      c[k] = csum[(si.chunk0 + max(st - 1 - k, 0)) * H + h];
+    int W = 0;
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 1; k <= kWindowMaxCap; ++k) {
+      acc += k <= lim ? c[k - 1] : 0.f;
+      if (W == 0 && k <= lim && (k == st || acc <= thr)) W = k;
+    }
+    seg_win[(sb + j) * H + h] = W;
+    miss |= W == 0;
   }
+  // a pair with a start that has no window takes the correction: no slot keeps a
+  // window, and its segments but the last are pass-1 units, a run of segs - 1 list
+  // entries reserved here (so the atomic's round trip overlaps a maximum scan)
+  const bool corr = seg_win && __syncthreads_or(miss);
+  uint32_t base = 0;
+  if (corr) {
+    for (int j = (int)threadIdx.x; j < segs; j += NT) seg_win[(sb + j) * H + h] = 0;
+    if (threadIdx.x == 0 && ncorr) {
+      atomicAdd(ncorr, 1u);
+      if (p1_slots) base = atomicAdd(ncorr + 1, (uint32_t)(segs - 1));
+    }
+  } else if (seg_win && threadIdx.x == 0) {
+    seg_win[sb * H + h] = 0;
+  }
+
+  if (best) {
+    const float v = block_run_max<NT>(csum, si.chunk0, nch, H, h, wmax, sums, NT + kWindowMaxCap, red);
+    const int w = threadIdx.x;   // thread w holds the maximum for runs of w + 1 chunks
+    if (w < kWindowMaxCap)       // 0 = no run of that length
+      best[nh * kWindowMaxCap + w] = (w < wmax && v > -INFINITY) ? ordered_bits(v) : 0u;
+  }
+  if (!corr || !p1_slots || !ncorr) return;
+  __shared__ uint32_t sbase;
+  if (threadIdx.x == 0) sbase = base;
+  __syncthreads();
+  // (bounded: a count an earlier scan left unreset can run past the list)
+  for (int j = (int)threadIdx.x; j + 1 < segs; j += NT)
+    if ((int64_t)sbase + j < p1_cap) p1_slots[sbase + j] = (int32_t)((sb + j) * H + h);
 }
 
 // Packed input: the chunk / segment offset tables, and (split plans) the order in
@@ -142,19 +188,23 @@ hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s, 
 }
 
 hipError_t launch_gate_scan(const Problem& p, const float* csum, int64_t max_chunks, int wmax,
-                            uint32_t* best, hipStream_t s, KernelEvents ev, float thr, uint32_t* ncorr) {
+                            uint32_t* best, hipStream_t s, KernelEvents ev, float thr, uint32_t* ncorr,
+                            int seg_chunks, const int32_t* seg_off, int32_t* seg_win, int32_t* p1_slots,
+                            int64_t p1_cap) {
   if (p.N == 0) {
     ev.record_empty(s);
     return hipSuccess;
   }
   if ((int64_t)p.N * p.H > kMaxDispatchItems / 1024) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)(p.N * p.H));
-  if (max_chunks > 512)
+  if (best && max_chunks > 512)   // (segment windows alone: a pass of 256 starts is plenty)
     hipExtLaunchKernelGGL(gate_window_max_kernel<1024>, grid, dim3(1024), 0, s, ev.start, ev.stop, 0, csum,
-                          p.cu, p.chunk_off, p.T, p.N, p.H, wmax, best, thr, ncorr);
+                          p.cu, p.chunk_off, p.T, p.N, p.H, wmax, best, thr, ncorr, seg_chunks, seg_off,
+                          seg_win, p1_slots, p1_cap);
   else
     hipExtLaunchKernelGGL(gate_window_max_kernel<256>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, csum,
-                          p.cu, p.chunk_off, p.T, p.N, p.H, wmax, best, thr, ncorr);
+                          p.cu, p.chunk_off, p.T, p.N, p.H, wmax, best, thr, ncorr, seg_chunks, seg_off,
+                          seg_win, p1_slots, p1_cap);
   return hipGetLastError();
 }
 

@@ -415,9 +415,8 @@ Plan make_plan(const gdn_shape* s, const gdn_opts* o) {
 bool runs_k1(const Plan& P) { return !P.wy || P.split; }
 
 struct Layout {
-  size_t tmat = 0, chunk_off = 0, seg_off = 0, seg_order = 0, best = 0, csum = 0, sstar = 0, mcorr = 0,
-         hstart = 0;
-  size_t gmat = 0, gvec = 0, ncorr = 0;
+  size_t tmat = 0, chunk_off = 0, seg_off = 0, seg_order = 0, csum = 0, sstar = 0, mcorr = 0, hstart = 0;
+  size_t gmat = 0, gvec = 0, ncorr = 0, seg_win = 0, p1_slots = 0;
   bool has_seg_order = false;
   size_t total = 0;
 };
@@ -434,9 +433,10 @@ Layout layout(const gdn_shape* s, const Plan& P) {
     L.seg_order = take((size_t)P.total_segs * sizeof(int32_t));
     L.has_seg_order = true;
   }
-  L.best = take((size_t)s->N * s->H * kWindowMaxCap * sizeof(uint32_t));
   if (P.split) {
-    L.ncorr = take(sizeof(uint32_t));
+    L.ncorr = take(2 * sizeof(uint32_t));
+    L.seg_win = take((size_t)P.total_segs * s->H * sizeof(int32_t));
+    L.p1_slots = take((size_t)(P.total_segs - s->N) * s->H * sizeof(int32_t));
     L.csum = take((size_t)P.total_chunks * s->H * sizeof(float));
     const size_t slots = (size_t)P.total_segs * s->H;
     L.sstar = take(slots * s->dk * s->dv * sizeof(float));
@@ -536,7 +536,6 @@ int run_stages(int first, int last, const void* q, const void* k, const void* v,
   int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + L.chunk_off);
   int32_t* seg_off = reinterpret_cast<int32_t*>(ws + L.seg_off);
   int32_t* seg_order = reinterpret_cast<int32_t*>(ws + L.seg_order);
-  uint32_t* best = reinterpret_cast<uint32_t*>(ws + L.best);
   // the packed-sequence tables live in the workspace and are rebuilt by every call (a
   // single stage too), so no kernel indexes by workspace contents it did not write
   if (cu_seqlens) {
@@ -554,8 +553,9 @@ int run_stages(int first, int last, const void* q, const void* k, const void* v,
   // that take pass 1 (no admissible window), so it goes after the gate scan: the
   // inverse stage then forms the chunk gate sums alone.
   const bool k1_after_scan = P.wy && P.split && !forced;
-  // count of heads without a window (one-pass split plans): zeroed with the gate sums,
-  // added to by the gate scan, read first by every correction launch
+  // counts of the heads without a window and of pass 1's units (one-pass split plans):
+  // zeroed with the gate sums, added to by the gate scan, read first by every
+  // correction launch
   uint32_t* ncorr = k1_after_scan ? reinterpret_cast<uint32_t*>(ws + L.ncorr) : nullptr;
   if (runs(GDN_STAGE_INVERSE)) {
     const gdn::KernelEvents ev = stage_events(opts, GDN_STAGE_INVERSE);
@@ -577,9 +577,6 @@ int run_stages(int first, int last, const void* q, const void* k, const void* v,
   plan.mode = gdn::kPass3;
   plan.cp = gdn::CpBuffers{};
   if (P.split) {
-    plan.cp.best = best;
-    plan.cp.wmax = P.wmax;
-    plan.cp.thr = P.log_eps - kWindowMargin;
     plan.cp.force_correction = forced ? 1 : 0;
     plan.cp.sstar = reinterpret_cast<float*>(ws + L.sstar);
     plan.cp.mcorr = ws + L.mcorr;
@@ -587,20 +584,29 @@ int run_stages(int first, int last, const void* q, const void* k, const void* v,
     plan.cp.gmat = L.gmat ? ws + L.gmat : nullptr;
     plan.cp.gvec = L.gvec ? reinterpret_cast<float*>(ws + L.gvec) : nullptr;
     plan.cp.ncorr = ncorr;
+    int32_t* seg_win = reinterpret_cast<int32_t*>(ws + L.seg_win);
+    plan.cp.seg_win = seg_win;
+    int32_t* p1_slots = ncorr ? reinterpret_cast<int32_t*>(ws + L.p1_slots) : nullptr;
+    plan.cp.p1_slots = p1_slots;
     if (!plan.cp.force_correction && runs(GDN_STAGE_GATE_SCAN)) {
-      if (gdn::launch_gate_scan(p, csum, P.max_chunks, P.wmax, best, stream,
-                                stage_events(opts, GDN_STAGE_GATE_SCAN), plan.cp.thr, ncorr) != hipSuccess)
+      if (gdn::launch_gate_scan(p, csum, P.max_chunks, P.wmax, nullptr, stream,
+                                stage_events(opts, GDN_STAGE_GATE_SCAN), P.log_eps - kWindowMargin, ncorr,
+                                P.seg_chunks,
+                                cu_seqlens ? seg_off : nullptr, seg_win, p1_slots,
+                                (P.total_segs - p.N) * p.H) != hipSuccess)
         return GDN_ERR_HIP;
     }
     if (runs(GDN_STAGE_CP_PASS1)) {
       gdn::FwdPlan p1 = plan;
       p1.mode = gdn::kPass1;
+      if (p1_slots) p1.units = (P.total_segs - p.N) * p.H;   // the list's capacity
       gdn::KernelEvents ev = stage_events(opts, GDN_STAGE_CP_PASS1);
       if (k1_after_scan) {
         gdn::HeadFilter only;
-        only.best = best;
-        only.wmax = P.wmax;
-        only.thr = plan.cp.thr;
+        only.p1_slots = p1_slots;
+        only.p1_cap = p1.units;
+        only.seg_off = cu_seqlens ? seg_off : nullptr;
+        only.seg_chunks = P.seg_chunks;
         only.ncorr = ncorr;
         if (gdn::launch_chunk_inverse(p, tmat, nullptr, false, stream, gdn::KernelEvents{ev.start, nullptr},
                                       only) != hipSuccess)
@@ -722,9 +728,11 @@ int gdn_chunk_fwd_workspace_region(const gdn_shape* shape, const gdn_opts* opts,
       *offset = L.tmat;
       *bytes = runs_k1(P) ? (size_t)P.total_chunks * shape->H * kChunk * kChunk * esz : 0;
       break;
-    case GDN_REGION_WINDOWS:
-      *offset = L.best;
-      *bytes = (size_t)shape->N * shape->H * kWindowMaxCap * sizeof(uint32_t);
+    case GDN_REGION_SEGMENT_WINDOWS:
+      if (P.split) {
+        *offset = L.seg_win;
+        *bytes = slots * sizeof(int32_t);
+      }
       break;
     case GDN_REGION_SEGMENT_MAPS:
       if (P.split) {

@@ -31,9 +31,6 @@ constexpr int kWindowMaxCap = 16;  // longest lookback window the gate scan can 
 
 // Sequence-split state shared by the split passes (all null when no split).
 struct CpBuffers {
-  const uint32_t* best;     // [N*H][kWindowMaxCap] gate-scan maxima (order-preserving bits)
-  int wmax;                 // longest admissible window (chunks)
-  float thr;                // window threshold: log_eps - margin
   int force_correction;     // 1: every split head uses the wrong-start correction
   float* sstar;             // [total_segs, H] x [dk x dv] fp32 wrong-start (zero-start) segment
                             // end states, each in accumulator-tile order (sfrag_offset)
@@ -43,10 +40,19 @@ struct CpBuffers {
   float* hstart;            // [total_segs, H, dk, dv] true segment start states
   void* gmat;               // long merge chains, per group of steps (slot of the group's first
   float* gvec;              // segment): composed map A (as mcorr) and offset b (as sstar)
-  // (nullable) count of (sequence, head) pairs without an admissible window, written
-  // by the gate scan: when it is zero the correction launches (restricted chunk
-  // inverse, pass 1, merge) return at once instead of finding that per unit
+  // (nullable) two counters written by the gate scan: [0] the (sequence, head) pairs
+  // without an admissible window (when it is zero the correction launches, the
+  // restricted chunk inverse, pass 1 and the merge, return at once instead of finding
+  // that per unit) and [1] the entries of p1_slots
   const uint32_t* ncorr;
+  // (nullable, needs ncorr) pass 1's work list: the slots s * H + h of the segments,
+  // all but each sequence's last, of the pairs without a window, one run per pair in
+  // the order the gate scan's workgroups finished (the order changes no result)
+  const int32_t* p1_slots;
+  // per (segment, head) slot s * H + h: the lookback window, in chunks, of the
+  // segment's start (gate scan); 0 for first segments and for every slot of a
+  // (sequence, head) that takes the correction
+  const int32_t* seg_win;
 };
 
 // Merge chains of more steps than this run as a two-level tree (cp_merge.hip): about
@@ -63,7 +69,8 @@ constexpr int64_t kMaxDispatchItems = 0xFFFFFFFFLL;
 //           (correction heads); the last segment writes the final state.
 //   kPass1: correction heads only, all but the last segment: run the segment from
 //           a zero state (value columns -> sstar) and, with V = 0, from the
-//           identity (extra dk columns -> mcorr); no O.
+//           identity (extra dk columns -> mcorr); no O.  With cp.p1_slots a unit is
+//           an entry of that list (units: its capacity), else every (segment, head).
 enum { kPass3 = 0, kPass1 = 1 };
 struct FwdPlan {
   const void* Tmat;          // chunk inverses [total_chunks, H, 64, 64]
@@ -94,27 +101,35 @@ struct KernelEvents {
     if (stop) (void)hipEventRecord(stop, s);
   }
 };
-// ncorr_zero (nullable): the gate scan's counter of heads without a window, set to
-// zero here (the scan that follows adds to it).
+// ncorr_zero (nullable): the gate scan's two counters (CpBuffers::ncorr), set to zero
+// here (the scan that follows adds to them).
 hipError_t launch_chunk_gate_sums(const Problem& p, float* csum, hipStream_t s, KernelEvents ev = {},
                                   uint32_t* ncorr_zero = nullptr);
-// ncorr (nullable): adds 1 for every (sequence, head) of more than one chunk with no
-// admissible window under thr (the decision window_of() takes).
+// best (nullable): the per-(sequence, head) maxima of run sums for W = 1..wmax.
+// seg_win (nullable): per (segment, head) windows of a plan that cuts sequences into
+// segments of seg_chunks chunks (seg_off: packed segment offsets, else dense); a
+// segment start takes the smallest W <= min(wmax, its chunk index) whose W chunks
+// before it sum to <= thr, or W = its chunk index (the sequence start); a
+// (sequence, head) with a start that has none gets 0 in every slot, adds 1 to
+// ncorr[0] (nullable) and, with p1_slots (nullable, needs ncorr), appends the slots
+// of its segments but the last to p1_slots (p1_cap entries), counted in ncorr[1].
 hipError_t launch_gate_scan(const Problem& p, const float* csum, int64_t max_chunks, int wmax,
                             uint32_t* best, hipStream_t s, KernelEvents ev = {}, float thr = 0.f,
-                            uint32_t* ncorr = nullptr);
+                            uint32_t* ncorr = nullptr, int seg_chunks = 0, const int32_t* seg_off = nullptr,
+                            int32_t* seg_win = nullptr, int32_t* p1_slots = nullptr, int64_t p1_cap = 0);
 hipError_t launch_gate_finalize(const Problem& p, const uint32_t* best, int wmax, float thr,
                                 int32_t* out, hipStream_t s);
 // max_steps: the most segment boundaries of any sequence (segments - 1).
 hipError_t launch_cp_merge(const Problem& p, const FwdPlan& plan, int max_steps, hipStream_t s,
                            KernelEvents ev = {});
-// Restricts the chunk inverse to the heads without an admissible lookback window
-// (window_of(best, ...) == 0); best == nullptr: every head.
+// The chunk inverse restricted to pass 1's work list (CpBuffers::p1_slots): the
+// chunks of the listed segments only, ncorr[1] entries, at most p1_cap.
 struct HeadFilter {
-  const uint32_t* best = nullptr;
-  int wmax = 0;
-  float thr = 0.f;
-  const uint32_t* ncorr = nullptr;   // as CpBuffers::ncorr
+  const int32_t* p1_slots = nullptr;  // null: every chunk-head
+  int64_t p1_cap = 0;
+  const int32_t* seg_off = nullptr;   // packed split plans: per-sequence segment offsets
+  int seg_chunks = 0;
+  const uint32_t* ncorr = nullptr;    // as CpBuffers::ncorr
 };
 // csum (nullable): [total_chunks, H] per-chunk gate sums, written on the side.
 // full = false: T's zero upper-right 32 x 32 quadrant is left unwritten (the fused

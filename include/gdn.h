@@ -182,17 +182,21 @@ int gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const flo
  * the gate scan under force_correction) enqueues nothing and returns GDN_OK.
  * Under a one-pass plan (gdn_plan_one_pass) no stage forms T for the forward pass:
  * an unsplit plan's GDN_STAGE_INVERSE enqueues nothing; a split plan's forms only
- * the chunk gate sums, and its GDN_STAGE_CP_PASS1 first forms T for the heads
- * without an admissible lookback window (the only ones pass 1 reads it for).  A
+ * the chunk gate sums, and its GDN_STAGE_CP_PASS1 first forms T for the chunks of
+ * pass 1's units (below: the only ones pass 1 reads it for).  A
  * split one-pass plan also keeps in the workspace a count of the (sequence, head)
- * pairs without a window: GDN_STAGE_INVERSE zeroes it, GDN_STAGE_GATE_SCAN adds to
- * it, and GDN_STAGE_CP_PASS1 and GDN_STAGE_CP_MERGE do nothing when it is zero (a
- * workspace that receives regions from elsewhere runs those two stages first).
+ * pairs without a window and a list of pass 1's units (the segments of those pairs
+ * but each sequence's last) with its length: GDN_STAGE_INVERSE zeroes both counts,
+ * GDN_STAGE_GATE_SCAN adds to them and writes the list, GDN_STAGE_CP_PASS1 runs the
+ * listed units, and GDN_STAGE_CP_PASS1 and GDN_STAGE_CP_MERGE do nothing when the
+ * pair count is zero (a workspace that receives regions from elsewhere runs those
+ * two stages first).
  * With packed sequences every stage call first rebuilds, from cu_seqlens, the
  * chunk and segment tables it indexes by (one small launch; gdn_chunk_fwd builds
  * them once), so no stage indexes by anything a caller or an earlier stage left in
- * the workspace: window lengths read back are clamped to the sequence, and every
- * other workspace byte a stage reads is a value.  Each stage reads what the earlier
+ * the workspace: window lengths read back are clamped to the sequence, list entries
+ * to the slots and the list's length to its capacity, and every other workspace
+ * byte a stage reads is a value.  Each stage reads what the earlier
  * stages of the same pass wrote into the workspace: running a stage on a workspace
  * where they have not run (or ran with other arguments) gives unspecified output
  * values (never an access outside the buffers the arguments describe).
@@ -212,10 +216,18 @@ enum {
   GDN_REGION_CHUNK_INVERSE = 0,  /* T of every chunk-head: [total_chunks, H, 64, 64] in
                                     shape->qkv_dtype, as gdn_chunk_inverse writes it, except
                                     that the (zero) upper-right 32 x 32 quadrant is not
-                                    written (written by GDN_STAGE_INVERSE) */
-  GDN_REGION_WINDOWS = 1,        /* per (sequence, head): 16 uint32, the largest gate sum
-                                    over runs of 1..16 chunks in an order-preserving encoding
-                                    (GDN_STAGE_GATE_SCAN) */
+                                    written (GDN_STAGE_INVERSE; under a one-pass plan empty
+                                    when nothing is split, else written by
+                                    GDN_STAGE_CP_PASS1 for the chunks of its units only) */
+  GDN_REGION_SEGMENT_WINDOWS = 1, /* per slot int32: the lookback window, in chunks, of the
+                                    segment's start: the smallest W <= min(window_max_chunks,
+                                    the start's chunk index) whose W chunks before the start
+                                    have a gate sum <= window_log_eps - 1e-3 (fp32 sums), or
+                                    W = the start's chunk index (the window reaches the
+                                    sequence start, where the state is exact); 0 for first
+                                    segments and for every slot of a (sequence, head) with a
+                                    start that has none, which takes the correction
+                                    (GDN_STAGE_GATE_SCAN; read by every later stage) */
   GDN_REGION_SEGMENT_MAPS = 2,   /* per slot the affine map of its segment: the wrong-start
                                     end state S* (dk * dv fp32 per slot, all slots), then,
                                     at a 256-byte aligned offset, the transition M (2 * dk *

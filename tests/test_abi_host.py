@@ -216,7 +216,7 @@ def test_workspace_regions():
     total = ctypes.c_size_t(0)
     assert B.lib().gdn_chunk_fwd_workspace_bytes(ctypes.byref(s), ctypes.byref(split), ctypes.byref(total)) == 0
     chunks, segs = 15, 5
-    want = {B.GDN_REGION_CHUNK_INVERSE: chunks * H * 64 * 64 * 2, B.GDN_REGION_WINDOWS: H * 16 * 4,
+    want = {B.GDN_REGION_CHUNK_INVERSE: chunks * H * 64 * 64 * 2, B.GDN_REGION_SEGMENT_WINDOWS: segs * H * 4,
             B.GDN_REGION_SEGMENT_STARTS: segs * H * d * d * 4}
     spans = []
     for r in range(B.GDN_NUM_REGIONS):
@@ -232,7 +232,7 @@ def test_workspace_regions():
     spans.sort()
     assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
     unsplit = B.make_opts(no_split=1)
-    for r in (B.GDN_REGION_SEGMENT_MAPS, B.GDN_REGION_SEGMENT_STARTS):
+    for r in (B.GDN_REGION_SEGMENT_WINDOWS, B.GDN_REGION_SEGMENT_MAPS, B.GDN_REGION_SEGMENT_STARTS):
         assert region(s, r, unsplit) == (B.GDN_OK, 0, 0)
     assert region(s, B.GDN_NUM_REGIONS)[0] == B.GDN_ERR_ARG
     assert region(s, -1)[0] == B.GDN_ERR_ARG

@@ -184,6 +184,68 @@ def _stage_setup(inp, opts):
     return d, new_ws, outs, run, region
 
 
+SEGWIN_CASES = {
+    "sigmoid_L8": (lambda: synth.generate(spec(B=2, T=64 * 40 + 9, H=4, seed=86, zero_gate_heads=())), 8),
+    "uniform_L3": (lambda: synth.generate(spec(B=1, T=64 * 30, H=3, gate="uniform", seed=87, zero_gate_heads=())), 3),
+    "mixed_L8": (lambda: synth.generate(spec(B=1, T=64 * 40, H=4, seed=88, zero_gate_heads=(2,))), 8),
+    "zero_short_L8": (lambda: synth.generate(spec(B=1, T=64 * 24, H=2, seed=89, gate="zero", zero_gate_heads=())), 8),
+    "packed_L4": (lambda: _packed([64 * 20 + 7, 64 * 3, 0, 64 * 9 + 5, 40], H=3, seed=90, zero_heads=(1,)), 4),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SEGWIN_CASES))
+def test_segment_windows_stage(case):
+    """The per-segment windows the gate scan writes (GDN_REGION_SEGMENT_WINDOWS)
+    against the fp64 per-segment rule of oracle/gate.py: every GPU window is
+    admissible in fp64 (its chunks sum to <= log eps, or it reaches the sequence
+    start) and minimal up to the 1e-3 margin band; a pair the GPU sends to the
+    correction has a start with no window below the band; decisions outside the
+    band equal the oracle's."""
+    make, L = SEGWIN_CASES[case]
+    inp = make()
+    opts = binding.make_opts(force_segment_chunks=L)
+    d, new_ws, outs, run, region = _stage_setup(inp, opts)
+    ws = new_ws()
+    o, hT = outs()
+    run([binding.GDN_STAGE_INVERSE, binding.GDN_STAGE_GATE_SCAN], ws, o, hT)
+    off, n = region(binding.GDN_REGION_SEGMENT_WINDOWS)
+    H = inp["spec"].H
+    got = ws[off:off + n].view(torch.int32).reshape(-1, H).cpu().numpy()
+    le = math.log(2.0 ** -16)          # bf16 default tolerance
+    g64 = synth.as_f64(inp["g"])
+    cu = None if inp.get("cu_seqlens") is None else inp["cu_seqlens"].numpy()
+    ref = gate.segment_windows(g64, L, cu_seqlens=cu, log_eps=le - 1e-3)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    B, T, _ = g64.shape
+    cuv = np.arange(B + 1) * T if cu is None else cu
+    gf = g64.reshape(-1, H)
+    row = 0
+    for s_ in range(len(cuv) - 1):
+        nch = (cuv[s_ + 1] - cuv[s_] + 63) // 64
+        segs = max(1, (nch + L - 1) // L)
+        for h in range(H):
+            sums = gate.chunk_sums(gf[cuv[s_]:cuv[s_ + 1], h])
+            col = got[row:row + segs, h]
+            assert col[0] == 0, (s_, h)
+            if segs > 1 and (col[1:] == 0).all():     # correction: some start has no window
+                assert any(j * L > 16 and all(sums[j * L - w:j * L].sum() > le - 2e-3 for w in range(1, 17))
+                           for j in range(1, segs)), (s_, h)
+            else:
+                for j in range(1, segs):
+                    st, W = j * L, int(col[j])
+                    assert 1 <= W <= min(16, st), (s_, h, j, W)
+                    assert W == st or sums[st - W:st].sum() <= le, (s_, h, j, W)
+                    for w in range(1, W):
+                        assert sums[st - w:st].sum() > le - 2e-3, (s_, h, j, w)
+            near = any(abs(sums[j * L - w:j * L].sum() - (le - 1e-3)) < 1e-3
+                       for j in range(1, segs) for w in range(1, min(16, j * L) + 1))
+            if not near:
+                assert (col == ref[row:row + segs, h]).all(), (s_, h, col.tolist(), ref[row:row + segs, h].tolist())
+        row += segs
+    assert row == got.shape[0]
+    print("segment windows", case, got.T.tolist())
+
+
 STAGE_CASES = {
     "dense_split": (lambda: synth.generate(spec(seed=81, h0_std=0.05)),
                     dict(force_segment_chunks=3)),
