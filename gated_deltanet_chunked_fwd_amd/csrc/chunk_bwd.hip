@@ -22,19 +22,21 @@
 //   dh   = gamma_n dh' + Q^T diag(gamma) dY - K^T diag(gamma) dV
 //   dG   from the Gamma, gamma, d and gamma_n terms; dg = reverse cumsum of dG.
 //
-// Mapping: one workgroup per (sequence, head, 32 value columns).  The state columns
-// are independent in the forward, so each workgroup runs the forward over its
-// sequence first (the state at every chunk start goes to a checkpoint buffer), then
-// the chunks in reverse, recomputing each chunk's intermediates from its checkpoint.
+// Mapping: one workgroup per (sequence, head, 32 value columns), walking the chunks
+// in reverse and recomputing each chunk's intermediates from the state at its start.
+// Those states come from the forward's checkpoint pass (fused_forward.hip, kCkpt:
+// the fused forward's MFMA recurrence over whole sequences, storing the state at
+// every chunk start), which runs first.
 // dV and dh0 of its columns are final; dQ, dK, dbeta and dg are sums over all value
 // columns, so each workgroup writes its share in fp32 and a second kernel adds the
 // shares.  Arithmetic is plain fp32 (inputs converted on load), the chunk's matrices
-// in LDS, K, Q, V and dO read from global memory (L1/L2 resident within a chunk) as
-// runs of eight consecutive elements (one 16-byte load for bf16): every product
-// gives each thread a run of eight outputs, or eight contraction terms, per load.
-// P = (Q K^T) * Gamma is formed once per chunk, so no exponential sits in an inner
-// loop.  1024 threads per workgroup: the inner loops wait on those reads, and 16
-// waves hide more of the latency than 4.
+// in LDS (and, for bf16 inputs, the chunk's K and dO rows), Q and V read from global
+// memory (L1/L2 resident within a chunk); operands come as runs of eight consecutive
+// elements (one 16-byte load for bf16): every product gives each thread a run of
+// eight outputs, or eight contraction terms, per load.  P = (Q K^T) * Gamma is formed
+// once per chunk, so no exponential sits in an inner loop.  512 threads (eight waves,
+// two per SIMD) per workgroup: 1024 spilled registers once the loops took runs of
+// eight.
 #include <algorithm>
 
 #include "gdn_device.h"
@@ -152,11 +154,11 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
     }
   };
 
-  // ---- the chunk's gates, K K^T (lower), P = (Q K^T) * Gamma (lower, backward only),
+  // ---- the chunk's gates, K K^T (lower), P = (Q K^T) * Gamma (lower),
   //      K h, A -> T, V', U (the forward quantities)
-  auto recompute = [&](int t0, int len, bool for_backward) {
+  auto recompute = [&](int t0, int len) {
     ct0 = t0;
-    stage(t0, len, for_backward);
+    stage(t0, len, true);
     if (wave == 0) {
       float gv = 0.f, bv = 0.f;
       if (lane < len) {
@@ -183,15 +185,15 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
           float x[8], y[8], z[8];
           kld8(i, d, x);
           kld8(j, d, y);
-          if (for_backward) ld8(qi + d, z);
+          ld8(qi + d, z);
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
             acc += x[u] * y[u];
-            if (for_backward) accq += z[u] * y[u];
+            accq += z[u] * y[u];
           }
         }
         sKK[i * NS + j] = acc;
-        if (for_backward) sQK[i * NS + j] = accq * gam_ij(i, j);
+        sQK[i * NS + j] = accq * gam_ij(i, j);
       }
     }
     // V' = V - diag(gamma) K h
@@ -259,40 +261,9 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
     __syncthreads();
   };
 
-  auto chk = [&](int c) { return a.hchk + (((si.chunk0 + c) * H + h) * (int64_t)DK) * dv + col0; };
-
-  // ================= forward sweep: the state at every chunk start =================
-  for (int e = tid; e < DK * kBwdCols; e += kBwdThreads) {
-    const int i = e / kBwdCols, j = e % kBwdCols;
-    sH[i * CS + j] = p.h0 ? p.h0[((int64_t)nh * DK + i) * dv + col0 + j] : 0.f;
-  }
-  __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    const int t0 = c * kChunk, len = min(kChunk, si.len - t0);
-    float* hc = chk(c);
-    for (int e = tid; e < DK * kBwdCols; e += kBwdThreads) {
-      const int i = e / kBwdCols, j = e % kBwdCols;
-      hc[(int64_t)i * dv + j] = sH[i * CS + j];
-    }
-    recompute(t0, len, false);
-    const float gn = expf(sG[len - 1]);
-    // h <- gamma_n h + K^T diag(d) U: a thread owns rows i8 .. i8 + 7 of one column
-    for (int e = tid; e < D8 * kBwdCols; e += kBwdThreads) {
-      const int i8 = (e / kBwdCols) * 8, j = e % kBwdCols;
-      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-      for (int m = 0; m < len; ++m) {
-        float x[8];
-        kld8(m, i8, x);
-        const float du = sD[m] * sU[m * CS + j];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc[u] += x[u] * du;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) sH[(i8 + u) * CS + j] = gn * sH[(i8 + u) * CS + j] + acc[u];
-    }
-    __syncthreads();
-  }
+  // the state at every chunk start: the forward's checkpoint pass wrote it
+  // (fused_forward.hip, kCkpt; layout ckpt_offset)
+  auto chk = [&](int c) { return a.hchk + ((si.chunk0 + c) * H + h) * (int64_t)DK * dv; };
 
   // ================= reverse sweep =================
   for (int e = tid; e < DK * kBwdCols; e += kBwdThreads) {
@@ -303,12 +274,14 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
   for (int c = nch - 1; c >= 0; --c) {
     const int t0 = c * kChunk, len = min(kChunk, si.len - t0);
     const float* hc = chk(c);
-    for (int e = tid; e < DK * kBwdCols; e += kBwdThreads) {
-      const int i = e / kBwdCols, j = e % kBwdCols;
-      sH[i * CS + j] = hc[(int64_t)i * dv + j];
+    for (int e = tid; e < DK / 4 * kBwdCols; e += kBwdThreads) {   // four rows of a column
+      const int i4 = (e / kBwdCols) * 4, j = e % kBwdCols;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(hc + ckpt_offset(i4, col0 + j, dv));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sH[(i4 + u) * CS + j] = x[u];
     }
     __syncthreads();
-    recompute(t0, len, true);
+    recompute(t0, len);
     const float gn = expf(sG[len - 1]);
     // K dh' (into sdR for now) and dd_i = sum_j U_ij (K dh')_ij
     for (int e = tid; e < len * kBwdCols; e += kBwdThreads) {

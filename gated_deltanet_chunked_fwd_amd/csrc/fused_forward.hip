@@ -59,7 +59,8 @@ struct FwdCfg {
 // Nothing touches the loaded registers until store(): masking of rows past the
 // chunk end (zero there; beta = g = 0) and the beta conversion happen at store
 // time, so no wait for the loads is forced before the chunk's compute.
-// WITH_Q: pass 1 produces no output, so it neither loads nor stages Q.
+// WITH_Q: pass 1 and the checkpoint pass produce no output, so they neither load nor
+// stage Q.
 template <typename E, int DK, int BV, int NTH, bool WITH_Q>
 struct ChunkRegs {
   static constexpr int EPV = 16 / (int)sizeof(E);
@@ -205,8 +206,8 @@ __device__ __forceinline__ void p_pair(int i, int& qt, int& kt) {
   else { qt = 2 + ((i - 4) >> 2); kt = (i - 4) & 3; }
 }
 
-// PASS (kPass3 / kPass1) is a template parameter so that each pass compiles to
-// its own straight-line code and shows up as its own kernel in profiles.
+// PASS (kPass3 / kPass1 / kCkpt) is a template parameter so that each pass compiles
+// to its own straight-line code and shows up as its own kernel in profiles.
 template <typename E, int DK, int NCW, int NW, int PASS>
 __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) == 4)) ? 1 : 2) void fused_forward_kernel(Problem p,
                                                                                       FwdPlan plan) {
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
 
   // Prefetch depth: the global loads of chunk c + PF are issued while chunk c is
   // computed, from PF register sets used in turn.  Pass 1 has the registers for two.
-  constexpr int PF = (PASS == kPass1) ? 2 : 1;
+  constexpr int PF = (PASS != kPass3) ? 2 : 1;
   using Stage = ChunkRegs<E, DK, BV, Cfg::NT, PASS == kPass3>;
   Stage pf[PF];
   typename Stage::Offsets offs;
@@ -631,6 +632,15 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
   auto chunk = [&](auto q_tag, Stage& ld, Stage& sg, int c) {
     constexpr bool LOADQ = decltype(q_tag)::value;
     const int len = min(kChunk, si.len - c * kChunk);
+    if constexpr (PASS == kCkpt) {   // the state at this chunk's start
+      float* dst = plan.ckpt + ((si.chunk0 + c) * H + h) * (int64_t)DK * dv;
+#pragma unroll
+      for (int t = 0; t < NKT; ++t)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          *reinterpret_cast<f32x4*>(dst + ckpt_offset(prow(t, 4 * q), col0 + wcol + ct * 16 + r16, dv)) =
+              hs[t][ct];
+    }
     if constexpr (NB == 1) {
       gC = stage(std::true_type{}, ld, c, 0);
       __syncthreads();
@@ -710,7 +720,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
       for (int ct = 0; ct < NCT; ++ct)
         *reinterpret_cast<f32x4*>(dst + sfrag_offset<DK>(prow(t, 4 * q), col0 + wcol + ct * 16 + r16)) =
             hs[t][ct];
-  } else if (last_seg && p.hT) {
+  } else if (PASS == kPass3 && last_seg && p.hT) {
     float* dst = p.hT + (int64_t)nh * DK * dv + col0;
 #pragma unroll
     for (int t = 0; t < NKT; ++t)
@@ -753,6 +763,7 @@ static hipError_t launch_dk(const Problem& p, const FwdPlan& plan, hipStream_t s
 template <typename E, int DK>
 static hipError_t launch_pass(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev) {
   if (plan.mode == kPass1) return launch_dk<E, DK, kPass1>(p, plan, s, ev);
+  if (plan.mode == kCkpt) return launch_dk<E, DK, kCkpt>(p, plan, s, ev);
   return launch_dk<E, DK, kPass3>(p, plan, s, ev);
 }
 

@@ -576,6 +576,7 @@ int run_stages(int first, int last, const void* q, const void* k, const void* v,
   plan.pass1_block = P.pass1_block;
   plan.mode = gdn::kPass3;
   plan.cp = gdn::CpBuffers{};
+  plan.ckpt = nullptr;
   if (P.split) {
     plan.cp.force_correction = forced ? 1 : 0;
     plan.cp.sstar = reinterpret_cast<float*>(ws + L.sstar);
@@ -826,19 +827,25 @@ int gdn_gate_scan(const float* g, const int32_t* cu_seqlens, const gdn_shape* sh
   return GDN_OK;
 }
 
-// Backward workspace: packed chunk offsets, the chunk-start states, and the
-// workgroups' fp32 shares of dq, dk, dbeta and dg.
+// Backward workspace: packed chunk offsets, the chunk inverses and chunk-start states
+// of the checkpoint pass, and the workgroups' fp32 shares of dq, dk, dbeta and dg.
 struct BwdLayout {
-  size_t chunk_off = 0, hchk = 0, dq_p = 0, dk_p = 0, dbeta_p = 0, dg_p = 0, total = 0;
+  size_t chunk_off = 0, tmat = 0, hchk = 0, dq_p = 0, dk_p = 0, dbeta_p = 0, dg_p = 0, total = 0;
+  int max_chunks = 0;
 };
 static BwdLayout bwd_layout(const gdn_shape* s) {
   BwdLayout L;
   int64_t chunks = 0;
-  for (int64_t n = 0; n < s->N; ++n) chunks += seq_chunks(s, n);
+  for (int64_t n = 0; n < s->N; ++n) {
+    chunks += seq_chunks(s, n);
+    L.max_chunks = std::max(L.max_chunks, (int)seq_chunks(s, n));
+  }
   const int64_t tot = s->B * s->T, nblk = s->dv / gdn::kBwdColumnBlock;
+  const size_t esz = s->qkv_dtype == GDN_BF16 ? 2 : 4;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes); return o; };
   L.chunk_off = take(s->cu_seqlens_host ? (size_t)(s->N + 1) * sizeof(int32_t) : 0);
+  L.tmat = take((size_t)chunks * s->H * kChunk * kChunk * esz);
   L.hchk = take((size_t)chunks * s->H * s->dk * s->dv * sizeof(float));
   L.dq_p = take((size_t)nblk * tot * s->H * s->dk * sizeof(float));
   L.dk_p = take((size_t)nblk * tot * s->H * s->dk * sizeof(float));
@@ -902,6 +909,24 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
   a.dbeta_p = reinterpret_cast<float*>(ws + L.dbeta_p);
   a.dg_p = reinterpret_cast<float*>(ws + L.dg_p);
   a.total_tokens = shape->B * shape->T;
+  if (total_chunks > 0) {
+    // the state at every chunk start, by the forward's own recurrence: the chunk
+    // inverses, then the checkpoint pass over whole sequences (one segment each)
+    void* tmat = ws + L.tmat;
+    if (gdn::launch_chunk_inverse(p, tmat, nullptr, false, stream) != hipSuccess) return GDN_ERR_HIP;
+    gdn::FwdPlan ck;
+    ck.Tmat = tmat;
+    ck.seg_chunks = std::max(1, L.max_chunks);
+    ck.seg_off = nullptr;
+    ck.seg_order = nullptr;
+    ck.units = p.N * (int64_t)p.H;
+    ck.value_block = 64;
+    ck.pass1_block = 64;
+    ck.mode = gdn::kCkpt;
+    ck.cp = gdn::CpBuffers{};
+    ck.ckpt = a.hchk;
+    if (gdn::launch_fused_forward(p, ck, stream) != hipSuccess) return GDN_ERR_HIP;
+  }
   if (gdn::launch_chunk_bwd(p, a, stream) != hipSuccess) return GDN_ERR_HIP;
   return GDN_OK;
 }

@@ -71,7 +71,16 @@ constexpr int64_t kMaxDispatchItems = 0xFFFFFFFFLL;
 //           a zero state (value columns -> sstar) and, with V = 0, from the
 //           identity (extra dk columns -> mcorr); no O.  With cp.p1_slots a unit is
 //           an entry of that list (units: its capacity), else every (segment, head).
-enum { kPass3 = 0, kPass1 = 1 };
+//   kCkpt:  the backward's checkpoints: every sequence as one segment from h0 (or
+//           0), value columns only, no O; the state at the start of every chunk goes
+//           to ckpt (below).
+enum { kPass3 = 0, kPass1 = 1, kCkpt = 2 };
+// Checkpoint layout: per (chunk, head) a dk x dv fp32 state, rows in groups of four
+// interleaved by column, element (r, c) at ((r / 4) * dv + c) * 4 + r % 4 (four
+// consecutive rows of one column are one 16-byte store).
+__host__ __device__ constexpr int64_t ckpt_offset(int r, int c, int dv) {
+  return ((int64_t)(r >> 2) * dv + c) * 4 + (r & 3);
+}
 struct FwdPlan {
   const void* Tmat;          // chunk inverses [total_chunks, H, 64, 64]
   int seg_chunks;            // chunks per segment (>= max chunks of any sequence: one segment)
@@ -80,8 +89,9 @@ struct FwdPlan {
   int64_t units;             // number of (sequence, head, segment) units
   int value_block;           // value columns per workgroup: 64, 128, or 0 (widest that fits)
   int pass1_block;           // pass-1 columns per workgroup: 128 (if requested), else 64
-  int mode;                  // kPass3 or kPass1
+  int mode;                  // kPass3, kPass1 or kCkpt
   CpBuffers cp;
+  float* ckpt;               // kCkpt: [total_chunks, H] x (dk x dv, ckpt_offset) fp32
 };
 
 hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hipStream_t s);
@@ -145,7 +155,8 @@ hipError_t launch_fused_forward(const Problem& p, const FwdPlan& plan, hipStream
 // Backward (chunk_bwd.hip): gradients of <dO, O> + <dhT, hT>.  Workgroup shares of
 // dq, dk (fp32 [blocks, tokens, H, dk]) and dbeta, dg (fp32 [blocks, tokens, H]) are
 // summed by the second kernel; hchk holds the state at every chunk start
-// ([total_chunks, H, dk, dv] fp32).  dhT and dh0 may be null.
+// ([total_chunks, H] x dk x dv fp32 in ckpt_offset order, written by the forward's
+// kCkpt pass before the backward kernel runs).  dhT and dh0 may be null.
 struct BwdArgs {
   const void* d_o;
   const float* dhT;

@@ -290,8 +290,10 @@ int gdn_gate_scan_workspace_bytes(const gdn_shape* shape, size_t* bytes);
  * that gdn_chunk_fwd computes on the same arguments (FlashQLA talk transcript:
  * results and timeline sections, a backward of the forward's chunk structure;
  * algebraic-rewrites section, the K K^T gradient entering K as (dA + dA^T) K).
- * The forward is recomputed inside (the state at every chunk start is kept in the
- * workspace), so nothing from a forward call is needed.
+ * The forward is recomputed inside, so nothing from a forward call is needed: the
+ * chunk inverses and the forward's own recurrence over whole sequences (no split)
+ * put the state at every chunk start in the workspace, and the backward kernel
+ * walks the chunks in reverse from those states.
  *   q, k, v, g, beta, initial_state, cu_seqlens, scale   as gdn_chunk_fwd
  *   d_o             device, [B,T,H,dv], dtype shape->qkv_dtype: gradient of o
  *   d_final_state   device, [N,H,dk,dv] fp32: gradient of the final state, or NULL (zero)
@@ -301,8 +303,9 @@ int gdn_gate_scan_workspace_bytes(const gdn_shape* shape, size_t* bytes);
  *   dbeta           device, [B,T,H], dtype shape->beta_dtype, fully overwritten
  *   d_initial_state device, [N,H,dk,dv] fp32, fully overwritten; or NULL (not written)
  *   workspace       device scratch of at least gdn_chunk_bwd_workspace_bytes()
- * Arithmetic is fp32 throughout (bf16 inputs converted on load, outputs rounded
- * once).  Errors as gdn_chunk_fwd.
+ * The chunk-start states carry the forward's precision (bf16 MFMA operands on bf16
+ * inputs, fp32 on fp32); the backward's own arithmetic is fp32 throughout (bf16
+ * inputs converted on load, outputs rounded once).  Errors as gdn_chunk_fwd.
  */
 int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const void* beta,
                   const float* initial_state, const int32_t* cu_seqlens, float scale,

@@ -193,6 +193,33 @@ SEGWIN_CASES = {
 }
 
 
+SUMS_CASES = dict(SEGWIN_CASES)
+SUMS_CASES["odd_heads_L5"] = (lambda: synth.generate(spec(B=2, T=64 * 21 + 30, H=33, seed=91, zero_gate_heads=(4,))), 5)
+SUMS_CASES["head_blocks_L4"] = (lambda: _packed([64 * 13 + 3, 64 * 2, 64 * 9], H=80, seed=92, zero_heads=(70,)), 4)
+
+
+@pytest.mark.parametrize("case", sorted(SUMS_CASES))
+def test_segment_windows_same_on_both_paths(case):
+    """The one-pass path forms the chunk gate sums in a kernel of their own, the
+    two-kernel path in the chunk inverse; both take the same wave scan over the same
+    values, so the windows they decide are equal bit for bit (head counts that are
+    odd and above one gate-sum block of 64 heads included)."""
+    make, L = SUMS_CASES[case]
+    inp = make()
+    got = []
+    for one_pass in (1, -1):
+        opts = binding.make_opts(force_segment_chunks=L, one_pass=one_pass)
+        d, new_ws, outs, run, region = _stage_setup(inp, opts)
+        ws = new_ws()
+        o, hT = outs()
+        print("case %s one_pass=%d" % (case, one_pass), flush=True)
+        run([binding.GDN_STAGE_INVERSE, binding.GDN_STAGE_GATE_SCAN], ws, o, hT)
+        off, n = region(binding.GDN_REGION_SEGMENT_WINDOWS)
+        got.append(ws[off:off + n].view(torch.int32).cpu())
+    assert got[0].numel() > 0
+    assert torch.equal(got[0], got[1])
+
+
 @pytest.mark.parametrize("case", sorted(SEGWIN_CASES))
 def test_segment_windows_stage(case):
     """The per-segment windows the gate scan writes (GDN_REGION_SEGMENT_WINDOWS)
