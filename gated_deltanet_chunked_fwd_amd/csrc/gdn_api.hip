@@ -38,7 +38,7 @@ constexpr size_t kAlign = 256;
 //             simulated schedule (pass3_makespan: a unit's chunks, its start-up
 //             kStartSteps, kLookbackSteps for a segment after the first).  One-pass
 //             step(busy) = kStepBaseUs + kStepPerBusyUs * busy workgroups (HBM and L2
-//             contention: 2.7 us at 64 busy, 3.8 us at 256); two-kernel path: λ1.
+//             contention: 2.7 us at 64 busy, 3.7 us at 256); two-kernel path: λ1.
 //   K1        two-kernel path only: kK1FixedUs + kK1PerChunkHeadUs per chunk-head.
 //   split     kSplitFixedUs + kSplitPerChunkHeadUs per chunk-head: the gate sums, the
 //             gate scan and the launches of the correction stages (on a window-only
@@ -56,7 +56,7 @@ constexpr float kLambda2Us = 0.75f;
 constexpr double kStartSteps = 2.2;
 constexpr double kLookbackSteps = 1.0;
 constexpr double kFwdFixedUs = 4.5;
-constexpr double kStepBaseUs = 2.37, kStepPerBusyUs = 0.0055;
+constexpr double kStepBaseUs = 2.33, kStepPerBusyUs = 0.0055;
 constexpr double kStepF32Us = 5.5;               // two-kernel step on fp32 inputs
 constexpr double kK1FixedUs = 10.0, kK1PerChunkHeadUs = 0.004, kCorrK1PerChunkHeadUs = 0.007;
 constexpr double kSplitFixedUs = 17.5, kSplitPerChunkHeadUs = 0.0, kPackedTablesUs = 4.0;
