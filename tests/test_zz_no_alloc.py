@@ -2,9 +2,10 @@
 
 Both run the same plan and kernels; the only difference is where the scratch lives
 (the library's built-in device array instead of a caller workspace), so the outputs
-must be bitwise equal, and they must match the fp64 oracle within the bf16 bar.  Two
-calls in a row on the built-in array, the second on a smaller input (the array keeps
-the first call's contents), each followed by the workspace call it is compared with."""
+must be bitwise equal, and they must match the fp64 oracle within the bf16 bar.  Calls
+in a row on the built-in array, each on a smaller input than the one before (the array
+keeps the earlier calls' contents), each followed by the workspace call it is compared
+with."""
 import ctypes
 
 import numpy as np
@@ -32,15 +33,20 @@ def run_both(inp, opts):
     return o, hT, o_ref, h_ref
 
 
-def test_noalloc_matches_workspace_call_twice_second_smaller():
+def test_noalloc_matches_workspace_call_in_a_row_each_smaller():
     big = synth.generate(synth.Spec("noalloc_big", B=2, T=1500, H=4, dk=128, dv=128, h0_std=0.05, seed=71))
+    mid = synth.generate(synth.Spec("noalloc_mid", B=1, T=1200, H=3, dk=128, dv=128, zero_gate_heads=(1,),
+                                    seed=73))
     small = synth.generate(synth.Spec("noalloc_small", B=1, T=300, H=2, dk=64, dv=128, seed=72))
     lens = [100, 0, 150, 50]
     small["cu_seqlens"] = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
     small["N"] = len(lens)
-    # first call: a split plan (segment maps, merge and starts live in the scratch);
-    # second call: smaller, packed, unsplit
+    # first call: a split plan, every head corrected (segment maps, merge and starts
+    # live in the scratch); second: smaller, split, one head without a window (the gate
+    # scan's counters and pass 1's work list live there too); third: smaller, packed,
+    # unsplit
     for inp, opts in ((big, binding.make_opts(force_segment_chunks=4, force_correction=1)),
+                      (mid, binding.make_opts(force_segment_chunks=4)),
                       (small, binding.make_opts())):
         sp = inp["spec"]
         print("noalloc %s: B=%d T=%d H=%d dk=%d dv=%d" % (sp.name, sp.B, sp.T, sp.H, sp.dk, sp.dv), flush=True)
