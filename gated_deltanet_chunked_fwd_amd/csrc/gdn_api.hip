@@ -44,7 +44,7 @@ constexpr size_t kAlign = 256;
 //             gate scan and the launches of the correction stages (on a window-only
 //             problem they read the gate scan's count and return at once); packed
 //             input adds the table launch, kPackedTablesUs.
-//   corrected heads (no admissible window), per call: their chunk inverse
+//   corrected heads (a segment start without a window), per call: their chunk inverse
 //             (kK1FixedUs + kCorrK1PerChunkHeadUs per chunk-head), pass 1
 //             (kPass1FixedUs + kPass1StepUs * L per round of workgroups) and the merge
 //             (short chain: kMergeFixedUs + λ2 per step; tree: kTreeFixedUs +
@@ -240,7 +240,7 @@ double pass3_makespan(const gdn_shape* s, int64_t L, int64_t cus, int ncb) {
 
 // The modelled time of one call (see the constants above) with segment length L
 // (L >= the longest sequence's chunks: no split) and a fraction `corr` of the
-// (sequence, head) pairs without an admissible window.
+// (sequence, head) pairs that take the correction (a segment start without a window).
 double call_us(const gdn_shape* s, const Plan& P, const gdn_opts* o, int64_t L, int64_t cus,
                double corr) {
   const bool split = L < P.max_chunks;
@@ -549,9 +549,9 @@ int run_stages(int first, int last, const void* q, const void* k, const void* v,
   void* tmat = ws + L.tmat;
   float* csum = P.split ? reinterpret_cast<float*>(ws + L.csum) : nullptr;
   const bool forced = opts && opts->force_correction;
-  // One-pass plans read no T; a split one runs the chunk inverse only for the heads
-  // that take pass 1 (no admissible window), so it goes after the gate scan: the
-  // inverse stage then forms the chunk gate sums alone.
+  // One-pass plans read no T; a split one runs the chunk inverse only for pass 1's
+  // listed segments (of the pairs with a start that has no window), so it goes after
+  // the gate scan: the inverse stage then forms the chunk gate sums alone.
   const bool k1_after_scan = P.wy && P.split && !forced;
   // counts of the heads without a window and of pass 1's units (one-pass split plans):
   // zeroed with the gate sums, added to by the gate scan, read first by every

@@ -185,7 +185,7 @@ int gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const flo
  * the chunk gate sums, and its GDN_STAGE_CP_PASS1 first forms T for the chunks of
  * pass 1's units (below: the only ones pass 1 reads it for).  A
  * split one-pass plan also keeps in the workspace a count of the (sequence, head)
- * pairs without a window and a list of pass 1's units (the segments of those pairs
+ * pairs that take the correction and a list of pass 1's units (the segments of those pairs
  * but each sequence's last) with its length: GDN_STAGE_INVERSE zeroes both counts,
  * GDN_STAGE_GATE_SCAN adds to them and writes the list, GDN_STAGE_CP_PASS1 runs the
  * listed units, and GDN_STAGE_CP_PASS1 and GDN_STAGE_CP_MERGE do nothing when the
@@ -323,9 +323,10 @@ int64_t gdn_plan_segment_chunks(const gdn_shape* shape, const gdn_opts* opts);
 /* The planner's modelled time of one gdn_chunk_fwd call, in microseconds, for the
  * plan it picks (FlashQLA talk transcript, auto-CP section: a cost model decides the
  * split; here per kernel, fitted on MI355X).  corrected_fraction in [0, 1] is the
- * share of (sequence, head) pairs without an admissible lookback window (they run
- * pass 1 and the merge; force_correction makes it 1); the planner itself, which
- * cannot see the gates, picks the plan with 0.  Uses the current device's CU count. */
+ * share of (sequence, head) pairs that take the correction (a segment start without a
+ * lookback window; they run pass 1 and the merge; force_correction makes it 1); the
+ * planner itself, which cannot see the gates, picks the plan with 0.  Uses the
+ * current device's CU count. */
 int gdn_plan_predict_us(const gdn_shape* shape, const gdn_opts* opts, double corrected_fraction,
                         double* us);
 
