@@ -278,14 +278,15 @@ def bench_backward(args):
     dhT = torch.randn((N, spec.H, spec.dk, spec.dv), generator=gen).float().to(dev)
     nbytes = ctypes.c_size_t(0)
     sh = binding._Shape(d["q"], d["v"], d["beta"], d["cu_seqlens"], inp["cu_seqlens"])
-    if binding.lib().gdn_chunk_bwd_workspace_bytes(sh.ref(), ctypes.byref(nbytes)) != 0:
+    opts = binding.make_opts(no_split=args.no_split, force_segment_chunks=args.segment_chunks)
+    if binding.lib().gdn_chunk_bwd_workspace_bytes(sh.ref(), ctypes.byref(opts), ctypes.byref(nbytes)) != 0:
         raise RuntimeError("gdn_chunk_bwd_workspace_bytes failed")
     ws = torch.empty(max(int(nbytes.value), 1), dtype=torch.uint8, device=dev)
 
     def step():
         return binding.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do, d["h0"], dhT,
                                  cu_seqlens=d["cu_seqlens"], scale=inp["scale"],
-                                 cu_seqlens_host=inp["cu_seqlens"], workspace=ws)
+                                 cu_seqlens_host=inp["cu_seqlens"], workspace=ws, opts=opts)
 
     for _ in range(args.warmup):
         step()
@@ -311,8 +312,9 @@ def bench_backward(args):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": spec.dtype, "data": "synthetic (seeded)",
         "config": {"workload": spec.name, "B": spec.B, "T": spec.T, "H": spec.H, "dk": spec.dk,
-                   "dv": spec.dv, "pass": "backward", "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "chunk_bwd_kernel + bwd_reduce_kernel (whole call)",
+                   "dv": spec.dv, "pass": "backward", "split_allowed": not args.no_split,
+                   "segment_chunks": args.segment_chunks or None, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "the whole backward call",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": alg},
     }

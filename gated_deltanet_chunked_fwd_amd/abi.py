@@ -65,9 +65,9 @@ def declare(lib):
     lib.gdn_plan_segment_chunks.argtypes = [shp, opt]
     lib.gdn_plan_segment_chunks.restype = ctypes.c_int64
     lib.gdn_chunk_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp,
-                                  vp, vp, shp, vp, sz, vp]
+                                  vp, vp, shp, opt, vp, sz, vp]
     lib.gdn_chunk_bwd.restype = ctypes.c_int
-    lib.gdn_chunk_bwd_workspace_bytes.argtypes = [shp, ctypes.POINTER(sz)]
+    lib.gdn_chunk_bwd_workspace_bytes.argtypes = [shp, opt, ctypes.POINTER(sz)]
     lib.gdn_chunk_bwd_workspace_bytes.restype = ctypes.c_int
     lib.gdn_plan_predict_us.argtypes = [shp, opt, ctypes.c_double, ctypes.POINTER(ctypes.c_double)]
     lib.gdn_plan_predict_us.restype = ctypes.c_int

@@ -345,11 +345,12 @@ def plan_one_pass(q, v, beta, cu_seqlens_host=None, opts: Optional[GdnOpts] = No
 
 
 def chunk_bwd(q, k, v, g, beta, do, initial_state=None, d_final_state=None, cu_seqlens=None, scale=None,
-              cu_seqlens_host=None, want_d_initial_state=True, workspace=None):
+              cu_seqlens_host=None, want_d_initial_state=True, workspace=None, opts: Optional[GdnOpts] = None):
     """Backward of chunk_fwd: the gradients of <do, o> + <d_final_state, final_state>.
     Returns ``(dq, dk, dv, dg, dbeta, d_initial_state)`` (the last None unless wanted);
     dq, dk, dv in q's dtype, dg fp32, dbeta in beta's dtype, d_initial_state fp32
-    [N, H, dk, dv].  d_final_state None means zero."""
+    [N, H, dk, dv].  d_final_state None means zero.  opts: the split of the reverse
+    sweep (force_segment_chunks, no_split)."""
     cu_seqlens = check_forward_args(q, k, v, g, beta, initial_state, cu_seqlens, cu_seqlens_host,
                                     None, d_final_state, None)
     _check_tensor(do, "do", (q.dtype,), tuple(v.shape), q.device, True)
@@ -362,14 +363,15 @@ def chunk_bwd(q, k, v, g, beta, do, initial_state=None, d_final_state=None, cu_s
     dg, db = torch.empty_like(g), torch.empty_like(beta)
     dh0 = torch.empty((sh.N, H, dk, dv), dtype=torch.float32, device=q.device) if want_d_initial_state else None
     n = ctypes.c_size_t(0)
-    rc = lib().gdn_chunk_bwd_workspace_bytes(sh.ref(), ctypes.byref(n))
+    oref = None if opts is None else ctypes.byref(opts)
+    rc = lib().gdn_chunk_bwd_workspace_bytes(sh.ref(), oref, ctypes.byref(n))
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_chunk_bwd_workspace_bytes")
     if workspace is None or workspace.numel() < n.value:
         workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=q.device)
     rc = lib().gdn_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
                              _ptr(cu_seqlens), ctypes.c_float(scale), _ptr(do), _ptr(d_final_state),
-                             _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dg), _ptr(db), _ptr(dh0), sh.ref(),
+                             _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(dg), _ptr(db), _ptr(dh0), sh.ref(), oref,
                              _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(q.device))
     if rc != GDN_OK:
         raise GdnError(rc, "gdn_chunk_bwd")

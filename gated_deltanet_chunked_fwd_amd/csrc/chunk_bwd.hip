@@ -101,11 +101,37 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk = p.dv / kBwdCols;
   const int blk = (int)(blockIdx.x % nblk);
-  const int64_t nh = blockIdx.x / nblk;
-  if (nh >= (int64_t)p.N * p.H) return;   // whole workgroup
-  const int n = (int)(nh / p.H), h = (int)(nh % p.H);
+  const int64_t unit = blockIdx.x / nblk;
+  if (unit >= a.units) return;   // whole workgroup
+  // the unit: (sequence, head), or with a split (segment, head), segments numbered as
+  // in the forward's split; [c_lo, c_hi) are its chunks
+  int n, h, seg = 0, S = 1;
+  int64_t sg0 = 0;
+  if (a.seg_chunks > 0) {
+    h = (int)(unit % p.H);
+    const int64_t sg = unit / p.H;
+    if (a.seg_off) {
+      n = seq_of_chunk(sg, a.seg_off, p.N, 0);
+      sg0 = a.seg_off[n];
+      S = (int)(a.seg_off[n + 1] - sg0);
+    } else {
+      const int64_t segs = max((int64_t)1, ((p.T + kChunk - 1) / kChunk + a.seg_chunks - 1) / a.seg_chunks);
+      n = (int)(sg / segs);
+      sg0 = (int64_t)n * segs;
+      S = (int)segs;
+    }
+    seg = (int)(sg - sg0);
+  } else {
+    n = (int)(unit / p.H);
+    h = (int)(unit % p.H);
+  }
+  const bool chain = a.mode == kBwdChain;
+  if (chain && seg == 0) return;   // the merge needs no offset of a first segment
+  const int64_t nh = (int64_t)n * p.H + h;
   const SeqInfo si = seq_info(n, p.cu, p.chunk_off, p.T);
   const int nch = (si.len + kChunk - 1) / kChunk;
+  const int c_lo = a.seg_chunks > 0 ? min(nch, seg * a.seg_chunks) : 0;
+  const int c_hi = a.seg_chunks > 0 ? min(nch, (seg + 1) * a.seg_chunks) : nch;
   const int H = p.H, dv = p.dv, col0 = blk * kBwdCols;
   const int64_t rqk = (int64_t)H * DK, rv = (int64_t)H * dv;
   const E* Qg = reinterpret_cast<const E*>(p.q) + si.tok0 * rqk + (int64_t)h * DK;
@@ -196,8 +222,8 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
         sQK[i * NS + j] = accq * gam_ij(i, j);
       }
     }
-    // V' = V - diag(gamma) K h
-    for (int e = tid; e < len * kBwdCols; e += kBwdThreads) {
+    // V' = V - diag(gamma) K h (the chain pass needs neither V' nor U)
+    for (int e = tid; e < (chain ? 0 : len * kBwdCols); e += kBwdThreads) {
       const int i = e / kBwdCols, j = e % kBwdCols;
       float acc = 0.f;
 #pragma unroll 2
@@ -252,7 +278,7 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
       }
       __syncthreads();
     }
-    for (int e = tid; e < len * kBwdCols; e += kBwdThreads) {
+    for (int e = tid; e < (chain ? 0 : len * kBwdCols); e += kBwdThreads) {
       const int i = e / kBwdCols, j = e % kBwdCols;
       float acc = 0.f;
       for (int m = 0; m <= i; ++m) acc += sT[i * NS + m] * sBet[m] * sVp[m * CS + j];
@@ -266,15 +292,24 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
   auto chk = [&](int c) { return a.hchk + ((si.chunk0 + c) * H + h) * (int64_t)DK * dv; };
 
   // ================= reverse sweep =================
+  // the state gradient after the unit's last chunk: dhT for a sequence's last segment
+  // (or a whole sequence), the merge's result for the other segments, zero in the
+  // chain pass
+  const int64_t gslot = bwd_slot(sg0, S, seg) * H + h;
   for (int e = tid; e < DK * kBwdCols; e += kBwdThreads) {
     const int i = e / kBwdCols, j = e % kBwdCols;
-    sdH[i * CS + j] = a.dhT ? a.dhT[((int64_t)nh * DK + i) * dv + col0 + j] : 0.f;
+    float x = 0.f;
+    if (!chain) {
+      if (seg == S - 1) x = a.dhT ? a.dhT[((int64_t)nh * DK + i) * dv + col0 + j] : 0.f;
+      else x = a.seg_g[(gslot * DK + i) * dv + col0 + j];
+    }
+    sdH[i * CS + j] = x;
   }
   __syncthreads();
-  for (int c = nch - 1; c >= 0; --c) {
+  for (int c = c_hi - 1; c >= c_lo; --c) {
     const int t0 = c * kChunk, len = min(kChunk, si.len - t0);
     const float* hc = chk(c);
-    for (int e = tid; e < DK / 4 * kBwdCols; e += kBwdThreads) {   // four rows of a column
+    for (int e = tid; e < (chain ? 0 : DK / 4 * kBwdCols); e += kBwdThreads) {   // four rows of a column
       const int i4 = (e / kBwdCols) * 4, j = e % kBwdCols;
       const f32x4 x = *reinterpret_cast<const f32x4*>(hc + ckpt_offset(i4, col0 + j, dv));
 #pragma unroll
@@ -298,7 +333,7 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
     }
     __syncthreads();
     // (16 lanes per row: the rows' reductions below are all split this way)
-    for (int e = tid; e < len * 16; e += kBwdThreads) {
+    for (int e = tid; e < (chain ? 0 : len * 16); e += kBwdThreads) {
       const int i = e >> 4, pp = e & 15;
       const float acc = row16_sum(sU[i * CS + pp] * sdR[i * CS + pp] + sU[i * CS + pp + 16] * sdR[i * CS + pp + 16]);
       if (pp == 0) sDD[i] = acc;
@@ -328,156 +363,160 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
       for (int m = i; m < len; ++m) acc += sT[m * NS + i] * sdU[m * CS + j];
       sdR[i * CS + j] = acc;
     }
-    for (int e = tid; e < len * len; e += kBwdThreads) {
-      const int i = e / len, j = e % len;
-      float acc = 0.f;
-      if (j <= i) {
+    if (chain) {
+      __syncthreads();   // dR, read by the state-gradient update below
+    } else {
+      for (int e = tid; e < len * len; e += kBwdThreads) {
+        const int i = e / len, j = e % len;
+        float acc = 0.f;
+        if (j <= i) {
 #pragma unroll 2
-        for (int k8 = 0; k8 < kBwdCols; k8 += 8) {
-          float o[8];
-          dold8(i, k8, o);
+          for (int k8 = 0; k8 < kBwdCols; k8 += 8) {
+            float o[8];
+            dold8(i, k8, o);
 #pragma unroll
-          for (int u = 0; u < 8; ++u) acc += o[u] * sU[j * CS + k8 + u];
+            for (int u = 0; u < 8; ++u) acc += o[u] * sU[j * CS + k8 + u];
+          }
+          acc *= scale;
         }
-        acc *= scale;
+        sM[i * NS + j] = acc;
       }
-      sM[i * NS + j] = acc;
-    }
-    __syncthreads();
-    // dV = diag(beta) dR; the Gamma gradient of P: E_ij = dP_ij P_ij
-    E* dVg = reinterpret_cast<E*>(a.dv) + si.tok0 * rv + (int64_t)h * dv + col0;
-    for (int e = tid; e < len * kBwdCols; e += kBwdThreads) {
-      const int i = e / kBwdCols, j = e % kBwdCols;
-      dVg[(int64_t)(t0 + i) * rv + j] = (E)(sBet[i] * sdR[i * CS + j]);
-    }
-    for (int e = tid; e < len * 16; e += kBwdThreads) {
-      const int i = e >> 4, pp = e & 15;
-      float r = 0.f, cs = 0.f;
-      for (int j = pp; j <= i; j += 16) r += sM[i * NS + j] * sQK[i * NS + j];
-      for (int m = i + pp; m < len; m += 16) cs += sM[m * NS + i] * sQK[m * NS + i];
-      const float v = row16_sum(r - cs);
-      if (pp == 0) sdG[i] = v;
-    }
-    __syncthreads();
-    // sQK <- dP * Gamma (lower);  then dA = strict_lower(-dR U^T) into sM
-    for (int e = tid; e < len * len; e += kBwdThreads) {
-      const int i = e / len, j = e % len;
-      sQK[i * NS + j] = j <= i ? sM[i * NS + j] * gam_ij(i, j) : 0.f;
-    }
-    __syncthreads();
-    for (int e = tid; e < len * len; e += kBwdThreads) {
-      const int i = e / len, j = e % len;
-      float acc = 0.f;
-      if (j < i)
-        for (int k2 = 0; k2 < kBwdCols; ++k2) acc -= sdR[i * CS + k2] * sU[j * CS + k2];
-      sM[i * NS + j] = acc;
-    }
-    __syncthreads();
-    // dbeta share: rowsum(dR * V') + sum_j dA_ij KK_ij Gamma_ij; the Gamma gradient of A
-    for (int e = tid; e < len * 16; e += kBwdThreads) {
-      const int i = e >> 4, pp = e & 15;
-      float db = sdR[i * CS + pp] * sVp[i * CS + pp] + sdR[i * CS + pp + 16] * sVp[i * CS + pp + 16];
-      float t = 0.f, cs = 0.f;
-      for (int j = pp; j < i; j += 16) t += sM[i * NS + j] * sKK[i * NS + j] * gam_ij(i, j);
-      for (int m = i + 1 + pp; m < len; m += 16) cs += sBet[m] * sM[m * NS + i] * sKK[m * NS + i] * gam_ij(m, i);
-      db = row16_sum(db + t);
-      const float dgA = row16_sum(sBet[i] * t - cs);
-      if (pp == 0) {
-        sdG[i] += dgA;
-        a.dbeta_p[((int64_t)blk * tot + si.tok0 + t0 + i) * H + h] = db;
+      __syncthreads();
+      // dV = diag(beta) dR; the Gamma gradient of P: E_ij = dP_ij P_ij
+      E* dVg = reinterpret_cast<E*>(a.dv) + si.tok0 * rv + (int64_t)h * dv + col0;
+      for (int e = tid; e < len * kBwdCols; e += kBwdThreads) {
+        const int i = e / kBwdCols, j = e % kBwdCols;
+        dVg[(int64_t)(t0 + i) * rv + j] = (E)(sBet[i] * sdR[i * CS + j]);
       }
-    }
-    __syncthreads();
-    // sKK <- dB = diag(beta) dA * Gamma (strict lower; zero elsewhere)
-    for (int e = tid; e < len * len; e += kBwdThreads) {
-      const int i = e / len, j = e % len;
-      sKK[i * NS + j] = j < i ? sBet[i] * sM[i * NS + j] * gam_ij(i, j) : 0.f;
-    }
-    __syncthreads();
-    // shares of dQ and dK (the K K^T gradient enters as (dB + dB^T) K, merged); a
-    // thread owns columns d8 .. d8 + 7 of one row.  The Y = Q h part of gamma's
-    // gradient, sum_j (Q h)_ij dY_ij = sum_d Q_id (dY h^T)_id, is summed on the side.
-    for (int e = tid; e < len * D8; e += kBwdThreads) {
-      const int i = e / D8, d8 = (e % D8) * 8;
-      float hdy[8], udh[8], rvh[8];
+      for (int e = tid; e < len * 16; e += kBwdThreads) {
+        const int i = e >> 4, pp = e & 15;
+        float r = 0.f, cs = 0.f;
+        for (int j = pp; j <= i; j += 16) r += sM[i * NS + j] * sQK[i * NS + j];
+        for (int m = i + pp; m < len; m += 16) cs += sM[m * NS + i] * sQK[m * NS + i];
+        const float v = row16_sum(r - cs);
+        if (pp == 0) sdG[i] = v;
+      }
+      __syncthreads();
+      // sQK <- dP * Gamma (lower);  then dA = strict_lower(-dR U^T) into sM
+      for (int e = tid; e < len * len; e += kBwdThreads) {
+        const int i = e / len, j = e % len;
+        sQK[i * NS + j] = j <= i ? sM[i * NS + j] * gam_ij(i, j) : 0.f;
+      }
+      __syncthreads();
+      for (int e = tid; e < len * len; e += kBwdThreads) {
+        const int i = e / len, j = e % len;
+        float acc = 0.f;
+        if (j < i)
+          for (int k2 = 0; k2 < kBwdCols; ++k2) acc -= sdR[i * CS + k2] * sU[j * CS + k2];
+        sM[i * NS + j] = acc;
+      }
+      __syncthreads();
+      // dbeta share: rowsum(dR * V') + sum_j dA_ij KK_ij Gamma_ij; the Gamma gradient of A
+      for (int e = tid; e < len * 16; e += kBwdThreads) {
+        const int i = e >> 4, pp = e & 15;
+        float db = sdR[i * CS + pp] * sVp[i * CS + pp] + sdR[i * CS + pp + 16] * sVp[i * CS + pp + 16];
+        float t = 0.f, cs = 0.f;
+        for (int j = pp; j < i; j += 16) t += sM[i * NS + j] * sKK[i * NS + j] * gam_ij(i, j);
+        for (int m = i + 1 + pp; m < len; m += 16) cs += sBet[m] * sM[m * NS + i] * sKK[m * NS + i] * gam_ij(m, i);
+        db = row16_sum(db + t);
+        const float dgA = row16_sum(sBet[i] * t - cs);
+        if (pp == 0) {
+          sdG[i] += dgA;
+          a.dbeta_p[((int64_t)blk * tot + si.tok0 + t0 + i) * H + h] = db;
+        }
+      }
+      __syncthreads();
+      // sKK <- dB = diag(beta) dA * Gamma (strict lower; zero elsewhere)
+      for (int e = tid; e < len * len; e += kBwdThreads) {
+        const int i = e / len, j = e % len;
+        sKK[i * NS + j] = j < i ? sBet[i] * sM[i * NS + j] * gam_ij(i, j) : 0.f;
+      }
+      __syncthreads();
+      // shares of dQ and dK (the K K^T gradient enters as (dB + dB^T) K, merged); a
+      // thread owns columns d8 .. d8 + 7 of one row.  The Y = Q h part of gamma's
+      // gradient, sum_j (Q h)_ij dY_ij = sum_d Q_id (dY h^T)_id, is summed on the side.
+      for (int e = tid; e < len * D8; e += kBwdThreads) {
+        const int i = e / D8, d8 = (e % D8) * 8;
+        float hdy[8], udh[8], rvh[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) hdy[u] = udh[u] = rvh[u] = 0.f;
+        for (int u = 0; u < 8; ++u) hdy[u] = udh[u] = rvh[u] = 0.f;
 #pragma unroll 2
-      for (int j = 0; j < kBwdCols; ++j) {
-        const float dy = scale * dos(i, j);
-        const float uu = sU[i * CS + j], rr = sBet[i] * sdR[i * CS + j];
+        for (int j = 0; j < kBwdCols; ++j) {
+          const float dy = scale * dos(i, j);
+          const float uu = sU[i * CS + j], rr = sBet[i] * sdR[i * CS + j];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const float hv = sH[(d8 + u) * CS + j];
+            hdy[u] += dy * hv;
+            udh[u] += uu * sdH[(d8 + u) * CS + j];
+            rvh[u] += rr * hv;
+          }
+        }
+        float dq[8], dk[8], qi[8], ki[8];
+        ld8(Qrow(t0 + i) + d8, qi);
+        kld8(i, d8, ki);
+        float qhy = 0.f, khr = 0.f;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const float hv = sH[(d8 + u) * CS + j];
-          hdy[u] += dy * hv;
-          udh[u] += uu * sdH[(d8 + u) * CS + j];
-          rvh[u] += rr * hv;
+          qhy += qi[u] * hdy[u];
+          khr += ki[u] * rvh[u];
+          dq[u] = sGam[i] * hdy[u];
+          dk[u] = sD[i] * udh[u] - sGam[i] * rvh[u];
         }
-      }
-      float dq[8], dk[8], qi[8], ki[8];
-      ld8(Qrow(t0 + i) + d8, qi);
-      kld8(i, d8, ki);
-      float qhy = 0.f, khr = 0.f;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        qhy += qi[u] * hdy[u];
-        khr += ki[u] * rvh[u];
-        dq[u] = sGam[i] * hdy[u];
-        dk[u] = sD[i] * udh[u] - sGam[i] * rvh[u];
-      }
 #pragma unroll 1
-      for (int m = 0; m < len; ++m) {
-        float km[8], qm[8];
-        kld8(m, d8, km);
-        ld8(Qrow(t0 + m) + d8, qm);
-        const float pq = sQK[i * NS + m];                      // zero for m > i
-        const float pk = m >= i ? sQK[m * NS + i] : 0.f;
-        const float bb = sKK[i * NS + m] + sKK[m * NS + i];    // dB strict lower, zero elsewhere
+        for (int m = 0; m < len; ++m) {
+          float km[8], qm[8];
+          kld8(m, d8, km);
+          ld8(Qrow(t0 + m) + d8, qm);
+          const float pq = sQK[i * NS + m];                      // zero for m > i
+          const float pk = m >= i ? sQK[m * NS + i] : 0.f;
+          const float bb = sKK[i * NS + m] + sKK[m * NS + i];    // dB strict lower, zero elsewhere
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            dq[u] += pq * km[u];
+            dk[u] += pk * qm[u] + bb * km[u];
+          }
+        }
+        const int64_t o = (((int64_t)blk * tot + si.tok0 + t0 + i) * H + h) * DK + d8;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          dq[u] += pq * km[u];
-          dk[u] += pk * qm[u] + bb * km[u];
+          a.dq_p[o + u] = dq[u];
+          a.dk_p[o + u] = dk[u];
+        }
+        // the D8 threads of row i are consecutive lanes of one wave
+#pragma unroll
+        for (int off = D8 / 2; off >= 1; off >>= 1) {
+          qhy += __shfl_xor(qhy, off, 64);
+          khr += __shfl_xor(khr, off, 64);
+        }
+        if (d8 == 0) {
+          sQhY[i] = qhy;
+          sKhR[i] = khr;
         }
       }
-      const int64_t o = (((int64_t)blk * tot + si.tok0 + t0 + i) * H + h) * DK + d8;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        a.dq_p[o + u] = dq[u];
-        a.dk_p[o + u] = dk[u];
+      // gamma_n's gradient: <h, dh'> over this block's columns (workgroup reduction)
+      float part = 0.f;
+      for (int e = tid; e < DK * kBwdCols; e += kBwdThreads) {
+        const int i = e / kBwdCols, j = e % kBwdCols;
+        part += sH[i * CS + j] * sdH[i * CS + j];
       }
-      // the D8 threads of row i are consecutive lanes of one wave
-#pragma unroll
-      for (int off = D8 / 2; off >= 1; off >>= 1) {
-        qhy += __shfl_xor(qhy, off, 64);
-        khr += __shfl_xor(khr, off, 64);
+      for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+      if (lane == 0) sRed[wave] = part;
+      __syncthreads();
+      // the gamma and d gradients into dG
+      // (the K h part of gamma's gradient, beta_i sum_j dR_ij (K h)_ij =
+      // sum_d K_id (beta_i dR h^T)_id, was summed with the dK shares)
+      if (tid < len) sdG[tid] += (sQhY[tid] - sKhR[tid]) * sGam[tid] - sDD[tid] * sD[tid];
+      __syncthreads();
+      // gamma_n's and d's gradients into the last row, then dg = reverse cumsum of dG
+      if (wave == 0) {
+        float x = (lane < len ? sDD[lane] * sD[lane] : 0.f) + (lane < kBwdThreads / 64 ? sRed[lane] * gn : 0.f);
+        for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+        const float gv = lane < len ? sdG[lane] + (lane == len - 1 ? x : 0.f) : 0.f;
+        const float pre = wave_inclusive_scan(gv);
+        const float total = __shfl(pre, 63, 64);
+        if (lane < len) a.dg_p[((int64_t)blk * tot + si.tok0 + t0 + lane) * H + h] = total - pre + gv;
       }
-      if (d8 == 0) {
-        sQhY[i] = qhy;
-        sKhR[i] = khr;
-      }
-    }
-    // gamma_n's gradient: <h, dh'> over this block's columns (workgroup reduction)
-    float part = 0.f;
-    for (int e = tid; e < DK * kBwdCols; e += kBwdThreads) {
-      const int i = e / kBwdCols, j = e % kBwdCols;
-      part += sH[i * CS + j] * sdH[i * CS + j];
-    }
-    for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-    if (lane == 0) sRed[wave] = part;
-    __syncthreads();
-    // the gamma and d gradients into dG
-    // (the K h part of gamma's gradient, beta_i sum_j dR_ij (K h)_ij =
-    // sum_d K_id (beta_i dR h^T)_id, was summed with the dK shares)
-    if (tid < len) sdG[tid] += (sQhY[tid] - sKhR[tid]) * sGam[tid] - sDD[tid] * sD[tid];
-    __syncthreads();
-    // gamma_n's and d's gradients into the last row, then dg = reverse cumsum of dG
-    if (wave == 0) {
-      float x = (lane < len ? sDD[lane] * sD[lane] : 0.f) + (lane < kBwdThreads / 64 ? sRed[lane] * gn : 0.f);
-      for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-      const float gv = lane < len ? sdG[lane] + (lane == len - 1 ? x : 0.f) : 0.f;
-      const float pre = wave_inclusive_scan(gv);
-      const float total = __shfl(pre, 63, 64);
-      if (lane < len) a.dg_p[((int64_t)blk * tot + si.tok0 + t0 + lane) * H + h] = total - pre + gv;
     }
     // dh = gamma_n dh' + Q^T diag(gamma) dY - K^T diag(gamma beta) dR (in place): a
     // thread owns rows i8 .. i8 + 7 of one column
@@ -501,7 +540,15 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
     }
     __syncthreads();
   }
-  if (a.dh0) {
+  if (chain) {
+    // the state gradient at the segment's start from a zero one at its end: the merge's
+    // offset for this segment (accumulator-tile order, as the forward's S*)
+    float* dst = a.seg_b + gslot * (int64_t)DK * dv;
+    for (int e = tid; e < DK * kBwdCols; e += kBwdThreads) {
+      const int i = e / kBwdCols, j = e % kBwdCols;
+      dst[sfrag_offset<DK>(i, col0 + j)] = sdH[i * CS + j];
+    }
+  } else if (a.dh0 && seg == 0) {
     for (int e = tid; e < DK * kBwdCols; e += kBwdThreads) {
       const int i = e / kBwdCols, j = e % kBwdCols;
       a.dh0[((int64_t)nh * DK + i) * dv + col0 + j] = sdH[i * CS + j];
@@ -536,11 +583,12 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a, int64_t tot,
 template <typename E, int DK>
 static hipError_t launch_bwd_dk(const Problem& p, const BwdArgs& a, hipStream_t s, KernelEvents ev) {
   const int nblk = p.dv / kBwdCols;
-  const int64_t wgs = (int64_t)p.N * p.H * nblk;
+  const int64_t wgs = a.units * nblk;
   if (wgs > kMaxDispatchItems / kBwdThreads) return hipErrorInvalidConfiguration;
-  hipExtLaunchKernelGGL(chunk_bwd_kernel<E, DK>, dim3((unsigned)wgs), dim3(kBwdThreads), 0, s, ev.start, nullptr,
-                        0, p, a);
+  hipExtLaunchKernelGGL(chunk_bwd_kernel<E, DK>, dim3((unsigned)wgs), dim3(kBwdThreads), 0, s, ev.start,
+                        a.mode == kBwdChain ? ev.stop : nullptr, 0, p, a);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  if (a.mode == kBwdChain) return hipSuccess;   // no shares to add
   const int64_t n_qk = a.total_tokens * p.H * DK;
   const int64_t blocks = std::min<int64_t>((n_qk + 255) / 256, 65536);
   if (p.beta_bf16)
@@ -553,7 +601,7 @@ static hipError_t launch_bwd_dk(const Problem& p, const BwdArgs& a, hipStream_t 
 }
 
 hipError_t launch_chunk_bwd(const Problem& p, const BwdArgs& a, hipStream_t s, KernelEvents ev) {
-  if (a.total_tokens == 0 && (int64_t)p.N * p.H == 0) {
+  if (a.units == 0) {
     ev.record_empty(s);
     return hipSuccess;
   }

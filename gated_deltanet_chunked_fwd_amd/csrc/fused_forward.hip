@@ -250,12 +250,15 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
   // K, T (and shared V) reads are served by one XCD's L2.  Padding ids past the last
   // unit exit at once.
   const int64_t bid = blockIdx.x;
-  const int ncb = ((PASS == kPass1) ? dv + DK : dv) / BV;   // column blocks per unit
+  // column blocks per unit: pass 1 also runs dk identity columns after the dv value
+  // columns (the backward's maps: the identity columns alone)
+  const bool bwd_maps = PASS == kPass1 && plan.bwd_maps;
+  const int ncb = ((PASS == kPass1) ? (bwd_maps ? DK : dv + DK) : dv) / BV;
   const int64_t rest = bid >> 3;
   const int cb = (int)(rest % ncb);
   const int64_t unit = (rest / ncb) * 8 + (bid & 7);
   if (unit >= plan.units) return;
-  const int col0 = cb * BV;                // first value column of the workgroup
+  const int col0 = (bwd_maps ? dv : 0) + cb * BV;   // first (value or identity) column
   const int wcol = wave * NCW;             // wave's first column inside the block
 
   // Pass 1 takes the gate scan's work list when there is one: only units that run
@@ -316,11 +319,15 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
   int init = kZero, c_start = c_begin, c_out = c_begin;
   bool mcols = false;   // pass 1: this block carries the transition-matrix columns
   if constexpr (PASS == kPass1) {
-    // last segments and window heads need no pass 1; a head's windows are all set or
-    // all zero, and its second segment (there is one: this is not the last) holds one
-    if (last_seg) return;
-    if (plan.cp.seg_win && !plan.cp.force_correction && plan.cp.seg_win[(sg - seg + 1) * H + h] > 0)
-      return;
+    if (bwd_maps) {
+      if (seg == 0) return;   // the backward's merge needs no map of a first segment
+    } else {
+      // last segments and window heads need no pass 1; a head's windows are all set or
+      // all zero, and its second segment (there is one: this is not the last) holds one
+      if (last_seg) return;
+      if (plan.cp.seg_win && !plan.cp.force_correction && plan.cp.seg_win[(sg - seg + 1) * H + h] > 0)
+        return;
+    }
     mcols = col0 >= dv;
     init = mcols ? kEye : kZero;
     c_out = c_end;
@@ -691,7 +698,15 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
   //      M (pass 1 identity columns) as bf16 high and low parts for the merge's MFMAs,
   //      in the merge's operand order (mfrag_offset)
   if (PASS == kPass1 && mcols) {
-    const int64_t slot = sg * H + h;
+    // the backward's maps: the transpose, at the segment's backward slot
+    int64_t slot = sg * H + h;
+    if (bwd_maps) {
+      const int64_t sg0 = sg - seg;
+      const int S = plan.seg_off ? (int)(plan.seg_off[n + 1] - plan.seg_off[n])
+                                 : (int)max((int64_t)1, ((p.T + kChunk - 1) / kChunk + plan.seg_chunks - 1) /
+                                                            plan.seg_chunks);
+      slot = bwd_slot(sg0, S, seg) * H + h;
+    }
     bf16* mhi = reinterpret_cast<bf16*>(plan.cp.mcorr) + slot * 2 * DK * DK;
     bf16* mlo = mhi + DK * DK;
     const int mc = col0 - dv + wcol + r16;
@@ -703,7 +718,8 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
         for (int i = 0; i < 4; ++i) {
           const float x = hs[t][ct][i];
           const bf16 hi = (bf16)x;
-          const int64_t at = mfrag_offset<DK>(prow(t, 4 * q + i), mc + ct * 16);
+          const int r = prow(t, 4 * q + i), c = mc + ct * 16;
+          const int64_t at = bwd_maps ? mfrag_offset<DK>(c, r) : mfrag_offset<DK>(r, c);
           mhi[at] = hi;
           mlo[at] = (bf16)(x - (float)hi);
         }
@@ -735,8 +751,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
 // 1-D grid of ceil(units / 8) * 8 * column blocks (see the decode in the kernel).
 template <typename E, int DK, int PASS>
 static hipError_t launch_dk(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev) {
-  // pass 1 also runs dk transition-matrix columns after the dv value columns
-  const int cols = PASS == kPass1 ? p.dv + DK : p.dv;
+  // pass 1 also runs dk transition-matrix columns after the dv value columns (the
+  // backward's maps: those alone)
+  const int cols = PASS == kPass1 ? (plan.bwd_maps ? DK : p.dv + DK) : p.dv;
   const int64_t groups = (plan.units + 7) / 8;
   if (groups * 8 > kMaxDispatchItems / (4 * cols))   // 4 threads per column in either shape
     return hipErrorInvalidConfiguration;

@@ -577,6 +577,7 @@ int run_stages(int first, int last, const void* q, const void* k, const void* v,
   plan.mode = gdn::kPass3;
   plan.cp = gdn::CpBuffers{};
   plan.ckpt = nullptr;
+  plan.bwd_maps = 0;
   if (P.split) {
     plan.cp.force_correction = forced ? 1 : 0;
     plan.cp.sstar = reinterpret_cast<float*>(ws + L.sstar);
@@ -827,18 +828,48 @@ int gdn_gate_scan(const float* g, const int32_t* cu_seqlens, const gdn_shape* sh
   return GDN_OK;
 }
 
+// The backward's split of the reverse sweep (the state-gradient chain is serial per
+// sequence like the forward's state chain, so a (sequence, head, 32 value columns)
+// workgroup per CU leaves most of the chip idle when there are few of them): segments
+// of L chunks, each run from the true state gradient at its end, which a merge over
+// the segments' maps finds.  A pass costs each segment twice its chunks (pass 1 and
+// the full pass), so it pays once there are enough segments per sequence: at least
+// kBwdMinSegments, L at least kBwdMinSegChunks, and as many segments as keep every CU
+// busy.  no_split and force_segment_chunks as for the forward.
+constexpr int kBwdMinSegments = 4, kBwdMinSegChunks = 8;
+static int64_t bwd_segment_chunks(const gdn_shape* s, const gdn_opts* o, int64_t max_chunks) {
+  if (max_chunks <= 1 || (o && o->no_split)) return std::max<int64_t>(1, max_chunks);
+  if (o && o->force_segment_chunks > 0) return std::min<int64_t>(o->force_segment_chunks, max_chunks);
+  const int64_t units = s->N * s->H * (s->dv / gdn::kBwdColumnBlock);
+  const int64_t segs = device_cus() / std::max<int64_t>(1, units);
+  if (segs < kBwdMinSegments || max_chunks < kBwdMinSegments * kBwdMinSegChunks) return max_chunks;
+  return std::max<int64_t>(kBwdMinSegChunks, (max_chunks + segs - 1) / segs);
+}
+
 // Backward workspace: packed chunk offsets, the chunk inverses and chunk-start states
-// of the checkpoint pass, and the workgroups' fp32 shares of dq, dk, dbeta and dg.
+// of the checkpoint pass, the workgroups' fp32 shares of dq, dk, dbeta and dg, and
+// with a split the segment offsets, the segments' transposed maps, offsets and end
+// state gradients (and the merge's group maps for long chains).
 struct BwdLayout {
   size_t chunk_off = 0, tmat = 0, hchk = 0, dq_p = 0, dk_p = 0, dbeta_p = 0, dg_p = 0, total = 0;
+  size_t seg_off = 0, seg_b = 0, seg_m = 0, seg_g = 0, gmat = 0, gvec = 0;
   int max_chunks = 0;
+  int64_t seg_chunks = 0, total_segs = 0, max_steps = 0;
+  bool split = false;
 };
-static BwdLayout bwd_layout(const gdn_shape* s) {
+static BwdLayout bwd_layout(const gdn_shape* s, const gdn_opts* o) {
   BwdLayout L;
   int64_t chunks = 0;
   for (int64_t n = 0; n < s->N; ++n) {
     chunks += seq_chunks(s, n);
     L.max_chunks = std::max(L.max_chunks, (int)seq_chunks(s, n));
+  }
+  L.seg_chunks = bwd_segment_chunks(s, o, L.max_chunks);
+  L.split = L.seg_chunks < L.max_chunks;
+  for (int64_t n = 0; n < s->N; ++n) {
+    const int64_t sg = L.split ? std::max<int64_t>(1, (seq_chunks(s, n) + L.seg_chunks - 1) / L.seg_chunks) : 1;
+    L.total_segs += sg;
+    L.max_steps = std::max(L.max_steps, sg - 1);
   }
   const int64_t tot = s->B * s->T, nblk = s->dv / gdn::kBwdColumnBlock;
   const size_t esz = s->qkv_dtype == GDN_BF16 ? 2 : 4;
@@ -851,15 +882,27 @@ static BwdLayout bwd_layout(const gdn_shape* s) {
   L.dk_p = take((size_t)nblk * tot * s->H * s->dk * sizeof(float));
   L.dbeta_p = take((size_t)nblk * tot * s->H * sizeof(float));
   L.dg_p = take((size_t)nblk * tot * s->H * sizeof(float));
+  if (L.split) {
+    const size_t slots = (size_t)L.total_segs * s->H;
+    L.seg_off = take(s->cu_seqlens_host ? (size_t)(s->N + 1) * sizeof(int32_t) : 0);
+    L.seg_b = take(slots * s->dk * s->dv * sizeof(float));
+    L.seg_m = take(slots * 2 * s->dk * s->dk * sizeof(uint16_t));
+    L.seg_g = take(slots * s->dk * s->dv * sizeof(float));
+    if (L.max_steps > gdn::kMergeTreeMinSteps) {
+      L.gmat = take(slots * 2 * s->dk * s->dk * sizeof(uint16_t));
+      L.gvec = take(slots * s->dk * s->dv * sizeof(float));
+    }
+  }
   L.total = off;
   return L;
 }
 
-int gdn_chunk_bwd_workspace_bytes(const gdn_shape* shape, size_t* bytes) {
+int gdn_chunk_bwd_workspace_bytes(const gdn_shape* shape, const gdn_opts* opts, size_t* bytes) {
   int rc = validate_shape(shape);
+  if (rc == GDN_OK) rc = validate_opts(opts);
   if (rc != GDN_OK) return rc;
   if (!bytes) return GDN_ERR_ARG;
-  *bytes = bwd_layout(shape).total;
+  *bytes = bwd_layout(shape, opts).total;
   return GDN_OK;
 }
 
@@ -867,8 +910,9 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
                   const float* initial_state, const int32_t* cu_seqlens, float scale,
                   const void* d_o, const float* d_final_state, void* dq, void* dk, void* dv,
                   float* dg, void* dbeta, float* d_initial_state, const gdn_shape* shape,
-                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                  const gdn_opts* opts, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int rc = validate_shape(shape);
+  if (rc == GDN_OK) rc = validate_opts(opts);
   if (rc == GDN_OK) rc = check_inputs(k, g, beta, cu_seqlens, shape);
   if (rc != GDN_OK) return rc;
   if (!std::isfinite(scale)) return GDN_ERR_ARG;
@@ -880,18 +924,21 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
       (initial_state && !aligned(initial_state, 16)) || (d_final_state && !aligned(d_final_state, 16)) ||
       (d_initial_state && !aligned(d_initial_state, 16)))
     return GDN_ERR_ARG;
-  const BwdLayout L = bwd_layout(shape);
+  const BwdLayout L = bwd_layout(shape, opts);
   if (workspace_bytes < L.total || (L.total > 0 && !workspace) || !aligned(workspace, kAlign))
     return GDN_ERR_WORKSPACE;
   const int64_t nblk = shape->dv / gdn::kBwdColumnBlock;
-  if (shape->N * shape->H * nblk > gdn::kMaxDispatchItems / 1024) return GDN_ERR_UNSUPPORTED;
+  if (L.total_segs * shape->H * nblk > gdn::kMaxDispatchItems / 1024) return GDN_ERR_UNSUPPORTED;
   const int64_t total_chunks = gdn_total_chunks(shape);
   char* ws = static_cast<char*>(workspace);
   gdn::Problem p = make_problem(q, k, v, g, beta, initial_state, cu_seqlens, scale, nullptr, nullptr,
                                 shape, total_chunks);
+  int32_t* seg_off = L.split && cu_seqlens ? reinterpret_cast<int32_t*>(ws + L.seg_off) : nullptr;
   if (cu_seqlens) {
     int32_t* chunk_off = reinterpret_cast<int32_t*>(ws + L.chunk_off);
-    if (gdn::launch_chunk_offsets(cu_seqlens, p.N, chunk_off, stream) != hipSuccess) return GDN_ERR_HIP;
+    if (gdn::launch_plan_tables(cu_seqlens, p.N, (int)L.seg_chunks, chunk_off, seg_off, nullptr, stream) !=
+        hipSuccess)
+      return GDN_ERR_HIP;
     p.chunk_off = chunk_off;
   }
   gdn::BwdArgs a;
@@ -909,10 +956,16 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
   a.dbeta_p = reinterpret_cast<float*>(ws + L.dbeta_p);
   a.dg_p = reinterpret_cast<float*>(ws + L.dg_p);
   a.total_tokens = shape->B * shape->T;
+  a.seg_chunks = L.split ? (int)L.seg_chunks : 0;
+  a.seg_off = seg_off;
+  a.units = (L.split ? L.total_segs : shape->N) * shape->H;
+  a.mode = gdn::kBwdFull;
+  a.seg_b = L.split ? reinterpret_cast<float*>(ws + L.seg_b) : nullptr;
+  a.seg_g = L.split ? reinterpret_cast<const float*>(ws + L.seg_g) : nullptr;
+  void* tmat = ws + L.tmat;
   if (total_chunks > 0) {
     // the state at every chunk start, by the forward's own recurrence: the chunk
     // inverses, then the checkpoint pass over whole sequences (one segment each)
-    void* tmat = ws + L.tmat;
     if (gdn::launch_chunk_inverse(p, tmat, nullptr, false, stream) != hipSuccess) return GDN_ERR_HIP;
     gdn::FwdPlan ck;
     ck.Tmat = tmat;
@@ -925,7 +978,40 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
     ck.mode = gdn::kCkpt;
     ck.cp = gdn::CpBuffers{};
     ck.ckpt = a.hchk;
+    ck.bwd_maps = 0;
     if (gdn::launch_fused_forward(p, ck, stream) != hipSuccess) return GDN_ERR_HIP;
+  }
+  if (L.split) {
+    // the state gradient at every segment's end: the transposed segment maps (the
+    // forward's pass 1 on the identity columns), the offsets (the backward from a zero
+    // gradient at each segment's end), and the merge over the segments last to first
+    // from dhT
+    gdn::FwdPlan mp;
+    mp.Tmat = tmat;
+    mp.seg_chunks = (int)L.seg_chunks;
+    mp.seg_off = seg_off;
+    mp.seg_order = nullptr;
+    mp.units = L.total_segs * shape->H;
+    mp.value_block = 64;
+    mp.pass1_block = 64;
+    mp.mode = gdn::kPass1;
+    mp.cp = gdn::CpBuffers{};
+    mp.cp.force_correction = 1;
+    mp.cp.mcorr = ws + L.seg_m;
+    mp.cp.sstar = a.seg_b;
+    mp.cp.hstart = reinterpret_cast<float*>(ws + L.seg_g);
+    mp.cp.gmat = L.gmat ? ws + L.gmat : nullptr;
+    mp.cp.gvec = L.gvec ? reinterpret_cast<float*>(ws + L.gvec) : nullptr;
+    mp.ckpt = nullptr;
+    mp.bwd_maps = 1;
+    if (gdn::launch_fused_forward(p, mp, stream) != hipSuccess) return GDN_ERR_HIP;
+    gdn::BwdArgs ch = a;
+    ch.mode = gdn::kBwdChain;
+    if (gdn::launch_chunk_bwd(p, ch, stream) != hipSuccess) return GDN_ERR_HIP;
+    gdn::Problem pm = p;
+    pm.h0 = d_final_state;   // the merge's chain starts from the gradient of the final state
+    mp.bwd_maps = 0;
+    if (gdn::launch_cp_merge(pm, mp, (int)L.max_steps, stream) != hipSuccess) return GDN_ERR_HIP;
   }
   if (gdn::launch_chunk_bwd(p, a, stream) != hipSuccess) return GDN_ERR_HIP;
   return GDN_OK;

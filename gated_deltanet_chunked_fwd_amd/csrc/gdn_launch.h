@@ -92,7 +92,17 @@ struct FwdPlan {
   int mode;                  // kPass3, kPass1 or kCkpt
   CpBuffers cp;
   float* ckpt;               // kCkpt: [total_chunks, H] x (dk x dv, ckpt_offset) fp32
+  // kPass1 for the backward's split: identity columns only, every segment but each
+  // sequence's first, the transpose of the segment's transition M stored (as cp.mcorr)
+  // at the backward's slot of the segment (bwd_slot)
+  int bwd_maps;
 };
+
+// The backward's split runs a sequence's segments last to first through the merge, so
+// segment seg of a sequence with S segments starting at global index sg0 uses slot
+// sg0 + S - 1 - seg (the merge's step k reads the maps and offsets of slot sg0 + k and
+// writes the state of slot sg0 + k + 1).
+__host__ __device__ constexpr int64_t bwd_slot(int64_t sg0, int S, int seg) { return sg0 + (S - 1 - seg); }
 
 hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hipStream_t s);
 // seg_order (nullable, needs seg_off): pass 3's segment order, longest first.
@@ -157,6 +167,13 @@ hipError_t launch_fused_forward(const Problem& p, const FwdPlan& plan, hipStream
 // summed by the second kernel; hchk holds the state at every chunk start
 // ([total_chunks, H] x dk x dv fp32 in ckpt_offset order, written by the forward's
 // kCkpt pass before the backward kernel runs).  dhT and dh0 may be null.
+//   kBwdFull:  the gradients; with a split, each segment starts from the state
+//              gradient at its end (seg_g, the merge's output; dhT for a sequence's
+//              last segment) and only a first segment writes dh0.
+//   kBwdChain: the split's pass 1: every segment but a sequence's first, from a zero
+//              state gradient, only the state-gradient chain (no checkpoint, no
+//              gradient written); the gradient at the segment's start goes to seg_b.
+enum { kBwdFull = 0, kBwdChain = 1 };
 struct BwdArgs {
   const void* d_o;
   const float* dhT;
@@ -172,6 +189,15 @@ struct BwdArgs {
   float* dbeta_p;
   float* dg_p;
   int64_t total_tokens;
+  // the split of the reverse sweep: seg_chunks = 0 walks every sequence whole; else a
+  // unit is (segment, head), segments numbered as in the forward's split (seg_off for
+  // packed input, else the same count for every sequence), units = segments x H
+  int seg_chunks;
+  const int32_t* seg_off;
+  int64_t units;
+  int mode;                  // kBwdFull or kBwdChain
+  float* seg_b;              // kBwdChain: per bwd_slot, dk x dv fp32 (sfrag_offset order)
+  const float* seg_g;        // kBwdFull with a split: per bwd_slot, [dk, dv] fp32 (natural)
 };
 constexpr int kBwdColumnBlock = 32;   // value columns per backward workgroup
 hipError_t launch_chunk_bwd(const Problem& p, const BwdArgs& a, hipStream_t s, KernelEvents ev = {});

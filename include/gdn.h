@@ -293,7 +293,14 @@ int gdn_gate_scan_workspace_bytes(const gdn_shape* shape, size_t* bytes);
  * The forward is recomputed inside, so nothing from a forward call is needed: the
  * chunk inverses and the forward's own recurrence over whole sequences (no split)
  * put the state at every chunk start in the workspace, and the backward kernel
- * walks the chunks in reverse from those states.
+ * walks the chunks in reverse from those states.  The reverse walk is serial per
+ * sequence, so when (sequence, head, 32 value columns) workgroups would leave most
+ * CUs idle it is split into segments (FlashQLA talk transcript: timeline section, the
+ * backward's own intra-GPU sequence parallelism): the state gradient's map over a
+ * segment is the transpose of the forward's transition M, so the forward's pass 1
+ * forms the transposed maps, a pass from a zero gradient at each segment's end the
+ * offsets, the merge the true gradient at every segment's end (from d_final_state,
+ * segments last to first), and each segment then runs the full backward from it.
  *   q, k, v, g, beta, initial_state, cu_seqlens, scale   as gdn_chunk_fwd
  *   d_o             device, [B,T,H,dv], dtype shape->qkv_dtype: gradient of o
  *   d_final_state   device, [N,H,dk,dv] fp32: gradient of the final state, or NULL (zero)
@@ -302,7 +309,12 @@ int gdn_gate_scan_workspace_bytes(const gdn_shape* shape, size_t* bytes);
  *   dg              device, [B,T,H] fp32 (gradient of the log gate), fully overwritten
  *   dbeta           device, [B,T,H], dtype shape->beta_dtype, fully overwritten
  *   d_initial_state device, [N,H,dk,dv] fp32, fully overwritten; or NULL (not written)
- *   workspace       device scratch of at least gdn_chunk_bwd_workspace_bytes()
+ *   opts            NULL or options: force_segment_chunks (> 0: the split's segment
+ *                   length in chunks) and no_split as for gdn_chunk_fwd; the rest is
+ *                   ignored.  Default: split when each sequence gets at least four
+ *                   segments of at least eight chunks and the units still fit the CUs.
+ *   workspace       device scratch of at least gdn_chunk_bwd_workspace_bytes() for the
+ *                   same shape and options
  * The chunk-start states carry the forward's precision (bf16 MFMA operands on bf16
  * inputs, fp32 on fp32); the backward's own arithmetic is fp32 throughout (bf16
  * inputs converted on load, outputs rounded once).  Errors as gdn_chunk_fwd.
@@ -311,8 +323,8 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
                   const float* initial_state, const int32_t* cu_seqlens, float scale,
                   const void* d_o, const float* d_final_state, void* dq, void* dk, void* dv,
                   float* dg, void* dbeta, float* d_initial_state, const gdn_shape* shape,
-                  void* workspace, size_t workspace_bytes, hipStream_t stream);
-int gdn_chunk_bwd_workspace_bytes(const gdn_shape* shape, size_t* bytes);
+                  const gdn_opts* opts, void* workspace, size_t workspace_bytes, hipStream_t stream);
+int gdn_chunk_bwd_workspace_bytes(const gdn_shape* shape, const gdn_opts* opts, size_t* bytes);
 
 /* Segment length (chunks) the planner picks for gdn_chunk_fwd, or a negative status.
  * When no sequence is split (no_split, a forced length at or above the longest

@@ -5,7 +5,13 @@ relative L2 error of dq, dk, dv, dg, dbeta and d_initial_state, under the forwar
 tolerances (1e-2 for bf16 storage, 1e-5 for fp32).  Covers the fp32 tiny workload,
 bf16 with every dk / dv combination, ragged last chunks, packed input with empty
 and one-token sequences, initial-state and final-state gradients present or absent,
-strong and absent decay, and fp32 beta with bf16 q/k/v."""
+strong and absent decay, and fp32 beta with bf16 q/k/v.  The split of the reverse
+sweep (segments run from the state gradient at their end, found by a merge over the
+segments' transposed maps) is checked the same way: forced segment lengths on dense
+and packed input, bf16 and fp32, with and without the final-state gradient, a chain
+long enough for the merge's two-level tree, and the planner's own split."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -29,13 +35,13 @@ def _grads_in(inp, seed, with_dhT):
     return do, dhT
 
 
-def _run_and_compare(inp, seed, with_dhT=True):
+def _run_and_compare(inp, seed, with_dhT=True, opts=None):
     spec = inp["spec"]
     do, dhT = _grads_in(inp, seed, with_dhT)
     d = to_dev(inp)
     got = binding.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do.cuda(), d["h0"],
                             None if dhT is None else dhT.cuda(), cu_seqlens=d["cu_seqlens"],
-                            scale=inp["scale"], cu_seqlens_host=d["cu_host"])
+                            scale=inp["scale"], cu_seqlens_host=d["cu_host"], opts=opts)
     torch.cuda.synchronize()
     got = [x.detach().cpu().double().numpy() for x in got]
     f64 = synth.as_f64
@@ -115,3 +121,56 @@ def test_backward_qwen_like_full_size_every_pair():
     inp = synth.generate(synth.WORKLOADS[2])
     worst = _run_and_compare(inp, seed=2)
     _assert(worst, TOL["bf16"], "backward qwen_like full size")
+
+
+SPLIT_CASES = [
+    # name, spec overrides, segment length in chunks, final-state gradient
+    ("bf16_d128_L4_h0", dict(B=1, T=64 * 24 + 37, H=2, h0_std=0.05, seed=81), 4, True),
+    ("f32_d64_L3", dict(B=2, T=64 * 12 + 5, H=1, dk=64, dv=64, dtype="f32", h0_std=0.05, seed=82), 3, True),
+    ("bf16_dk64_dv128_L2_no_dhT", dict(B=1, T=64 * 9 + 40, H=2, dk=64, dv=128, seed=83), 2, False),
+    ("bf16_no_decay_L3", dict(B=1, T=64 * 10, H=1, gate="zero", seed=84), 3, True),
+    ("f32_tree_L1", dict(B=1, T=64 * 80 + 9, H=1, dk=64, dv=64, dtype="f32", seed=85), 1, True),
+]
+
+
+@pytest.mark.parametrize("name,kw,L,with_dhT", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_backward_split_parity(name, kw, L, with_dhT):
+    sp = spec(name=name, **kw)
+    print("backward split case %s: L=%d %s" % (name, L, sp), flush=True)
+    inp = synth.generate(sp)
+    worst = _run_and_compare(inp, seed=sum(map(ord, name)) % 1000, with_dhT=with_dhT,
+                             opts=binding.make_opts(force_segment_chunks=L))
+    _assert(worst, TOL[sp.dtype], "backward split " + name)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_split_packed(dtype):
+    lengths = [64 * 9 + 10, 0, 30, 64 * 5, 64 * 13 + 63]
+    inp = synth.generate(spec(name="bwd_split_packed", B=1, T=int(sum(lengths)), H=2, dk=64, dv=64, dtype=dtype,
+                              seed=86))
+    inp["cu_seqlens"] = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32))
+    inp["N"] = len(lengths)
+    g = torch.Generator().manual_seed(87)
+    inp["h0"] = (torch.randn(len(lengths), 2, 64, 64, generator=g) * 0.05).float()
+    print("backward split packed %s: lengths %s, L=2" % (dtype, lengths), flush=True)
+    worst = _run_and_compare(inp, seed=7, opts=binding.make_opts(force_segment_chunks=2))
+    _assert(worst, TOL[dtype], "backward split packed " + dtype)
+
+
+def test_backward_planner_splits_long_few_heads():
+    """One sequence, one head: 2 workgroups unsplit, so the planner cuts the 40 chunks
+    into segments (checked through the workspace size, which grows by the split's
+    buffers) and the result still matches the oracle."""
+    sp = spec(name="bwd_planner_split", B=1, T=64 * 40, H=1, dk=64, dv=64, seed=88)
+    inp = synth.generate(sp)
+    d = to_dev(inp)
+    sizes = []
+    for o in (None, binding.make_opts(no_split=1)):
+        n = ctypes.c_size_t(0)
+        sh = binding._Shape(d["q"], d["v"], d["beta"], None, None)
+        assert binding.lib().gdn_chunk_bwd_workspace_bytes(sh.ref(), None if o is None else ctypes.byref(o),
+                                                           ctypes.byref(n)) == 0
+        sizes.append(n.value)
+    assert sizes[0] > sizes[1], sizes
+    worst = _run_and_compare(inp, seed=8)
+    _assert(worst, TOL["bf16"], "backward planner split")
