@@ -70,3 +70,21 @@ def test_predict_rejects_bad_fraction():
     for bad in (-0.1, 1.5, float("nan")):
         with pytest.raises(binding.GdnError):
             binding.plan_predict_us(q, q, beta, None, None, bad)
+
+
+# Whole calls on a (B*H, T) grid (dense bf16, dk = dv = 128, H = min(B*H, 16), log gates
+# log-sigmoid of N(3, 1) logits, so every head takes lookback windows: corrected
+# fraction 0), measured on
+# MI355X at the default plan (20 back-to-back calls, median of three runs).
+GRID_MEASURED_US = {(1, 4, 2048): 49.4, (1, 4, 8192): 50.4, (1, 4, 32768): 58.2,
+                    (1, 16, 2048): 51.6, (1, 16, 8192): 59.7, (1, 16, 32768): 165.1,
+                    (4, 16, 2048): 57.6, (4, 16, 8192): 159.6, (4, 16, 32768): 530.6,
+                    (16, 16, 2048): 136.5, (16, 16, 8192): 511.2, (16, 16, 32768): 1990.3}
+
+
+@pytest.mark.parametrize("B,H,T", sorted(GRID_MEASURED_US))
+def test_model_tracks_the_measured_grid(B, H, T):
+    q, beta = _meta(B, T, H)
+    pred = binding.plan_predict_us(q, q, beta)
+    meas = GRID_MEASURED_US[(B, H, T)]
+    assert abs(pred / meas - 1.0) <= 0.12, (B, H, T, pred, meas)
