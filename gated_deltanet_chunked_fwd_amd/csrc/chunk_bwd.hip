@@ -1,5 +1,6 @@
-// Backward of the chunked GDN forward on gfx950: gradients of <dO, O> + <dhT, hT>
-// with respect to q, k, v, g, beta and the initial state.
+// Backward of the chunked GDN forward on gfx950 for fp32 q / k / v (bf16 inputs take
+// the MFMA kernels of chunk_bwd_mfma.hip): gradients of <dO, O> + <dhT, hT> with
+// respect to q, k, v, g, beta and the initial state.
 //
 // FlashQLA talk transcript (tokendh.com): results and timeline sections (the
 // backward keeps the forward's structure); algebraic-rewrites section (the K K^T
@@ -29,11 +30,10 @@
 // every chunk start), which runs first.
 // dV and dh0 of its columns are final; dQ, dK, dbeta and dg are sums over all value
 // columns, so each workgroup writes its share in fp32 and a second kernel adds the
-// shares.  Arithmetic is plain fp32 (inputs converted on load), the chunk's matrices
-// in LDS (and, for bf16 inputs, the chunk's K and dO rows), Q and V read from global
-// memory (L1/L2 resident within a chunk); operands come as runs of eight consecutive
-// elements (one 16-byte load for bf16): every product gives each thread a run of
-// eight outputs, or eight contraction terms, per load.  P = (Q K^T) * Gamma is formed
+// shares.  Arithmetic is plain fp32, the chunk's matrices in LDS, K, Q, V and dO
+// read from global memory (L1/L2 resident within a chunk); operands come as runs of
+// eight consecutive elements: every product gives each thread a run of eight
+// outputs, or eight contraction terms, per load.  P = (Q K^T) * Gamma is formed
 // once per chunk, so no exponential sits in an inner loop.  512 threads (eight waves,
 // two per SIMD) per workgroup: 1024 spilled registers once the loops took runs of
 // eight.
@@ -84,10 +84,6 @@ template <typename E, int DK>
 __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdArgs a) {
   static_assert(kBwdCols == 32 && DK % 8 == 0, "thread mappings below");
   constexpr int D8 = DK / 8;             // runs of eight along dk
-  // bf16 inputs: the chunk's K and dO rows are staged in LDS (16-byte rows padding
-  // keeps the row-strided reads of K K^T off a single bank group)
-  constexpr bool kStage = sizeof(E) == 2;
-  constexpr int KSS = DK + 8, DOS = kBwdCols + 8;
   __shared__ float sKK[kChunk * NS], sT[kChunk * NS], sQK[kChunk * NS], sM[kChunk * NS];
   __shared__ float sVp[kChunk * CS], sU[kChunk * CS];
   __shared__ float sdU[kChunk * CS], sdR[kChunk * CS];
@@ -95,8 +91,6 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
   __shared__ float sG[kChunk], sGam[kChunk], sD[kChunk], sBet[kChunk], sdG[kChunk], sDD[kChunk], sQhY[kChunk],
       sKhR[kChunk];
   __shared__ float sRed[kBwdThreads / 64];
-  __shared__ __align__(16) E sKs[kStage ? kChunk * KSS : 8];
-  __shared__ __align__(16) E sDOs[kStage ? kChunk * DOS : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk = p.dv / kBwdCols;
@@ -148,43 +142,15 @@ __global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(Problem p, BwdAr
   int ct0 = 0;   // first token of the chunk being processed
   // eight K elements of chunk row i from dk column d; eight dO elements of row i from
   // value column c; one dO element (dO, not yet scaled)
-  auto kld8 = [&](int i, int d, float* o) {
-    if constexpr (kStage) ld8(sKs + i * KSS + d, o);
-    else ld8(Krow(ct0 + i) + d, o);
-  };
-  auto dold8 = [&](int i, int c, float* o) {
-    if constexpr (kStage) ld8(sDOs + i * DOS + c, o);
-    else ld8(DOrow(ct0 + i) + c, o);
-  };
-  auto dos = [&](int i, int c) {
-    if constexpr (kStage) return (float)sDOs[i * DOS + c];
-    else return ldf(DOg, (int64_t)(ct0 + i) * rv + c);
-  };
-  // the chunk's K rows (and dO rows) into LDS; rows past a partial chunk's end are zero
-  auto stage = [&](int t0, int len, bool with_do) {
-    if constexpr (kStage) {
-      for (int e = tid; e < kChunk * D8; e += kBwdThreads) {
-        const int i = e / D8, d8 = (e % D8) * 8;
-        uint4 v = {0u, 0u, 0u, 0u};
-        if (i < len) v = *reinterpret_cast<const uint4*>(Krow(t0 + i) + d8);
-        *reinterpret_cast<uint4*>(sKs + i * KSS + d8) = v;
-      }
-      if (with_do) {
-        for (int e = tid; e < kChunk * (kBwdCols / 8); e += kBwdThreads) {
-          const int i = e / (kBwdCols / 8), c8 = (e % (kBwdCols / 8)) * 8;
-          uint4 v = {0u, 0u, 0u, 0u};
-          if (i < len) v = *reinterpret_cast<const uint4*>(DOrow(t0 + i) + c8);
-          *reinterpret_cast<uint4*>(sDOs + i * DOS + c8) = v;
-        }
-      }
-    }
-  };
+  auto kld8 = [&](int i, int d, float* o) { ld8(Krow(ct0 + i) + d, o); };
+  auto dold8 = [&](int i, int c, float* o) { ld8(DOrow(ct0 + i) + c, o); };
+  auto dos = [&](int i, int c) { return ldf(DOg, (int64_t)(ct0 + i) * rv + c); };
+
 
   // ---- the chunk's gates, K K^T (lower), P = (Q K^T) * Gamma (lower),
   //      K h, A -> T, V', U (the forward quantities)
   auto recompute = [&](int t0, int len) {
     ct0 = t0;
-    stage(t0, len, true);
     if (wave == 0) {
       float gv = 0.f, bv = 0.f;
       if (lane < len) {
@@ -605,9 +571,7 @@ hipError_t launch_chunk_bwd(const Problem& p, const BwdArgs& a, hipStream_t s, K
     ev.record_empty(s);
     return hipSuccess;
   }
-  if (p.dv % kBwdCols != 0) return hipErrorInvalidValue;
-  if (p.qkv_bf16)
-    return p.dk == 128 ? launch_bwd_dk<bf16, 128>(p, a, s, ev) : launch_bwd_dk<bf16, 64>(p, a, s, ev);
+  if (p.dv % kBwdCols != 0 || p.qkv_bf16) return hipErrorInvalidValue;   // bf16: chunk_bwd_mfma.hip
   return p.dk == 128 ? launch_bwd_dk<float, 128>(p, a, s, ev) : launch_bwd_dk<float, 64>(p, a, s, ev);
 }
 

@@ -546,12 +546,18 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
         const f32x4 vv = col_read4(sV, VS, prow(u, 4 * q), cb + r16, cb + 4 * (r16 & 3));
         X[u][ct] = rows4(sBet, u) * (vv - rows4(sGam, u) * X[u][ct]);
       }
-    // ---- U = T W (T lower triangular: row tiles 0,1 need contraction step 0 only)
-    frag wb[2][NCT];
+    // ---- U = T W (T lower triangular: row tiles 0,1 need contraction step 0 only).
+    //      The checkpoint pass (bf16) carries W, and d U below, as bf16 hi + lo pairs:
+    //      the backward's gate gradient is sensitive to the states' rounding.
+    constexpr bool SPLIT = PASS == kCkpt && sizeof(E) == 2;
+    frag wb[2][NCT], wl[2][NCT];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) wb[s][ct] = M::pack(X[2 * s][ct], X[2 * s + 1][ct]);
+      for (int ct = 0; ct < NCT; ++ct) {
+        wb[s][ct] = M::pack(X[2 * s][ct], X[2 * s + 1][ct]);
+        if constexpr (SPLIT) wl[s][ct] = pack_residual(X[2 * s][ct], X[2 * s + 1][ct]);
+      }
     f32x4 U[4][NCT];
     {
       frag aT[6];   // T fragments (u, s): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
@@ -566,18 +572,22 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
 #pragma unroll
         for (int s = 0; s <= (u >> 1); ++s)
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct)
+          for (int ct = 0; ct < NCT; ++ct) {
             U[u][ct] = M::run(aT[u < 2 ? u : 2 * u - 2 + s], wb[s][ct], s == 0 ? zero4 : U[u][ct]);
+            if constexpr (SPLIT) U[u][ct] = M::run(aT[u < 2 ? u : 2 * u - 2 + s], wl[s][ct], U[u][ct]);
+          }
     }
       __builtin_amdgcn_s_setprio(0);
     load_part(P3{});
-    frag ubd[2][NCT];
+    frag ubd[2][NCT], ubl[2][NCT];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         if constexpr (EMIT) ubp[s][ct] = M::pack(U[2 * s][ct], U[2 * s + 1][ct]);
-        ubd[s][ct] = M::pack(U[2 * s][ct] * rows4(sDec, 2 * s), U[2 * s + 1][ct] * rows4(sDec, 2 * s + 1));
+        const f32x4 dlo = U[2 * s][ct] * rows4(sDec, 2 * s), dhi = U[2 * s + 1][ct] * rows4(sDec, 2 * s + 1);
+        ubd[s][ct] = M::pack(dlo, dhi);
+        if constexpr (SPLIT) ubl[s][ct] = pack_residual(dlo, dhi);
       }
     // ---- h <- gamma_last h + K^T (diag(d) U); K^T fragments by LDS transpose reads,
     //      two dk tiles' fragments read as a batch ahead of their MFMAs
@@ -603,7 +613,10 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && (PASS == kPass3 || sizeof(E) =
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) hs[t0 + dt][ct] = M::run(aKt[dt][s], ubd[s][ct], hs[t0 + dt][ct]);
+          for (int ct = 0; ct < NCT; ++ct) {
+            hs[t0 + dt][ct] = M::run(aKt[dt][s], ubd[s][ct], hs[t0 + dt][ct]);
+            if constexpr (SPLIT) hs[t0 + dt][ct] = M::run(aKt[dt][s], ubl[s][ct], hs[t0 + dt][ct]);
+          }
     }
       __builtin_amdgcn_s_setprio(0);
   };

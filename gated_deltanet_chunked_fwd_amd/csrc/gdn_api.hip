@@ -851,11 +851,12 @@ static int64_t bwd_segment_chunks(const gdn_shape* s, const gdn_opts* o, int64_t
 // with a split the segment offsets, the segments' transposed maps, offsets and end
 // state gradients (and the merge's group maps for long chains).
 struct BwdLayout {
-  size_t chunk_off = 0, tmat = 0, hchk = 0, dq_p = 0, dk_p = 0, dbeta_p = 0, dg_p = 0, total = 0;
+  size_t chunk_off = 0, tmat = 0, hchk = 0, dhchk = 0, dq_p = 0, dk_p = 0, dbeta_p = 0, dg_p = 0, total = 0;
   size_t seg_off = 0, seg_b = 0, seg_m = 0, seg_g = 0, gmat = 0, gvec = 0;
   int max_chunks = 0;
   int64_t seg_chunks = 0, total_segs = 0, max_steps = 0;
   bool split = false;
+  bool mfma = false;   // bf16 q / k / v: the MFMA chain and per-chunk kernels
 };
 static BwdLayout bwd_layout(const gdn_shape* s, const gdn_opts* o) {
   BwdLayout L;
@@ -878,10 +879,15 @@ static BwdLayout bwd_layout(const gdn_shape* s, const gdn_opts* o) {
   L.chunk_off = take(s->cu_seqlens_host ? (size_t)(s->N + 1) * sizeof(int32_t) : 0);
   L.tmat = take((size_t)chunks * s->H * kChunk * kChunk * esz);
   L.hchk = take((size_t)chunks * s->H * s->dk * s->dv * sizeof(float));
-  L.dq_p = take((size_t)nblk * tot * s->H * s->dk * sizeof(float));
-  L.dk_p = take((size_t)nblk * tot * s->H * s->dk * sizeof(float));
-  L.dbeta_p = take((size_t)nblk * tot * s->H * sizeof(float));
-  L.dg_p = take((size_t)nblk * tot * s->H * sizeof(float));
+  L.mfma = s->qkv_dtype == GDN_BF16;
+  if (L.mfma) {
+    L.dhchk = take((size_t)chunks * s->H * s->dk * s->dv * sizeof(float));
+  } else {
+    L.dq_p = take((size_t)nblk * tot * s->H * s->dk * sizeof(float));
+    L.dk_p = take((size_t)nblk * tot * s->H * s->dk * sizeof(float));
+    L.dbeta_p = take((size_t)nblk * tot * s->H * sizeof(float));
+    L.dg_p = take((size_t)nblk * tot * s->H * sizeof(float));
+  }
   if (L.split) {
     const size_t slots = (size_t)L.total_segs * s->H;
     L.seg_off = take(s->cu_seqlens_host ? (size_t)(s->N + 1) * sizeof(int32_t) : 0);
@@ -930,6 +936,7 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
   const int64_t nblk = shape->dv / gdn::kBwdColumnBlock;
   if (L.total_segs * shape->H * nblk > gdn::kMaxDispatchItems / 1024) return GDN_ERR_UNSUPPORTED;
   const int64_t total_chunks = gdn_total_chunks(shape);
+  if (L.mfma && total_chunks * shape->H > gdn::kMaxDispatchItems / 512) return GDN_ERR_UNSUPPORTED;
   char* ws = static_cast<char*>(workspace);
   gdn::Problem p = make_problem(q, k, v, g, beta, initial_state, cu_seqlens, scale, nullptr, nullptr,
                                 shape, total_chunks);
@@ -963,10 +970,13 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
   a.seg_b = L.split ? reinterpret_cast<float*>(ws + L.seg_b) : nullptr;
   a.seg_g = L.split ? reinterpret_cast<const float*>(ws + L.seg_g) : nullptr;
   void* tmat = ws + L.tmat;
+  a.tmat = tmat;
+  a.dhchk = L.mfma ? reinterpret_cast<float*>(ws + L.dhchk) : nullptr;
   if (total_chunks > 0) {
     // the state at every chunk start, by the forward's own recurrence: the chunk
-    // inverses, then the checkpoint pass over whole sequences (one segment each)
-    if (gdn::launch_chunk_inverse(p, tmat, nullptr, false, stream) != hipSuccess) return GDN_ERR_HIP;
+    // inverses (whole, for the MFMA backward's transposed reads), then the checkpoint
+    // pass over whole sequences (one segment each)
+    if (gdn::launch_chunk_inverse(p, tmat, nullptr, L.mfma, stream) != hipSuccess) return GDN_ERR_HIP;
     gdn::FwdPlan ck;
     ck.Tmat = tmat;
     ck.seg_chunks = std::max(1, L.max_chunks);
@@ -1007,13 +1017,19 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
     if (gdn::launch_fused_forward(p, mp, stream) != hipSuccess) return GDN_ERR_HIP;
     gdn::BwdArgs ch = a;
     ch.mode = gdn::kBwdChain;
-    if (gdn::launch_chunk_bwd(p, ch, stream) != hipSuccess) return GDN_ERR_HIP;
+    if ((L.mfma ? gdn::launch_bwd_dh(p, ch, stream) : gdn::launch_chunk_bwd(p, ch, stream)) != hipSuccess)
+      return GDN_ERR_HIP;
     gdn::Problem pm = p;
     pm.h0 = d_final_state;   // the merge's chain starts from the gradient of the final state
     mp.bwd_maps = 0;
     if (gdn::launch_cp_merge(pm, mp, (int)L.max_steps, stream) != hipSuccess) return GDN_ERR_HIP;
   }
-  if (gdn::launch_chunk_bwd(p, a, stream) != hipSuccess) return GDN_ERR_HIP;
+  if (L.mfma) {
+    if (gdn::launch_bwd_dh(p, a, stream) != hipSuccess) return GDN_ERR_HIP;
+    if (gdn::launch_bwd_grads(p, a, stream) != hipSuccess) return GDN_ERR_HIP;
+  } else if (gdn::launch_chunk_bwd(p, a, stream) != hipSuccess) {
+    return GDN_ERR_HIP;
+  }
   return GDN_OK;
 }
 

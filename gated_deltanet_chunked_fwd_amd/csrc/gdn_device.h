@@ -176,6 +176,18 @@ __device__ __forceinline__ f32x4 col_read4_storage(const float* M, int stride, i
   return col_read4(M, stride, row0, own_col, supply_col);
 }
 
+// The bf16 residuals x - bf16(x) of the eight values Mma<bf16>::pack(lo, hi) rounds:
+// an operand carried as the pair (pack, pack_residual) keeps about 16 significant
+// bits, at the cost of a second product.
+__device__ __forceinline__ bf16x8 pack_residual(const f32x4& lo, const f32x4& hi) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = (bf16)(lo[i] - (float)(bf16)lo[i]);
+    r[4 + i] = (bf16)(hi[i] - (float)(bf16)hi[i]);
+  }
+  return r;
+}
 // Four fp32 values as four bf16 (round to nearest even) in two dwords.
 __device__ __forceinline__ uint2 pack_bf16x4(const f32x4& v) {
   bf16x4 b;

@@ -198,8 +198,18 @@ struct BwdArgs {
   int mode;                  // kBwdFull or kBwdChain
   float* seg_b;              // kBwdChain: per bwd_slot, dk x dv fp32 (sfrag_offset order)
   const float* seg_g;        // kBwdFull with a split: per bwd_slot, [dk, dv] fp32 (natural)
+  // bf16 path (chunk_bwd_mfma.hip): the chunk inverses (K1, [total_chunks, H, 64, 64]
+  // bf16, the zero upper-right quadrant written) and the chain's checkpoints of the
+  // state gradient after every chunk ([total_chunks, H] x dk x dv fp32, ckpt_offset)
+  const void* tmat;
+  float* dhchk;
 };
 constexpr int kBwdColumnBlock = 32;   // value columns per backward workgroup
 hipError_t launch_chunk_bwd(const Problem& p, const BwdArgs& a, hipStream_t s, KernelEvents ev = {});
+// bf16 q / k / v (chunk_bwd_mfma.hip): the state-gradient chain (dv, the checkpoints
+// of dh', dh0; kBwdChain: only the segment offsets), then the gradients of every
+// (chunk, head) from hchk and dhchk (dq, dk, dbeta, dg).
+hipError_t launch_bwd_dh(const Problem& p, const BwdArgs& a, hipStream_t s, KernelEvents ev = {});
+hipError_t launch_bwd_grads(const Problem& p, const BwdArgs& a, hipStream_t s, KernelEvents ev = {});
 
 }  // namespace gdn

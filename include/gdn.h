@@ -292,10 +292,14 @@ int gdn_gate_scan_workspace_bytes(const gdn_shape* shape, size_t* bytes);
  * algebraic-rewrites section, the K K^T gradient entering K as (dA + dA^T) K).
  * The forward is recomputed inside, so nothing from a forward call is needed: the
  * chunk inverses and the forward's own recurrence over whole sequences (no split)
- * put the state at every chunk start in the workspace, and the backward kernel
- * walks the chunks in reverse from those states.  The reverse walk is serial per
- * sequence, so when (sequence, head, 32 value columns) workgroups would leave most
- * CUs idle it is split into segments (FlashQLA talk transcript: timeline section, the
+ * put the state at every chunk start in the workspace.  bf16 q / k / v: a chain
+ * kernel walks the chunks in reverse carrying only the state gradient (dv, and the
+ * state gradient after every chunk into the workspace), then every (chunk, head)
+ * forms dq, dk, dbeta and dg on its own from the two checkpoints, all products on
+ * bf16 MFMA with fp32 accumulation.  fp32: one kernel walks the chunks in reverse
+ * in plain fp32 and a second adds the value-column blocks' shares.  The reverse walk
+ * is serial per sequence, so when (sequence, head, 32 value columns) workgroups
+ * would leave most CUs idle it is split into segments (FlashQLA talk transcript: timeline section, the
  * backward's own intra-GPU sequence parallelism): the state gradient's map over a
  * segment is the transpose of the forward's transition M, so the forward's pass 1
  * forms the transposed maps, a pass from a zero gradient at each segment's end the
@@ -315,9 +319,11 @@ int gdn_gate_scan_workspace_bytes(const gdn_shape* shape, size_t* bytes);
  *                   segments of at least eight chunks and the units still fit the CUs.
  *   workspace       device scratch of at least gdn_chunk_bwd_workspace_bytes() for the
  *                   same shape and options
- * The chunk-start states carry the forward's precision (bf16 MFMA operands on bf16
- * inputs, fp32 on fp32); the backward's own arithmetic is fp32 throughout (bf16
- * inputs converted on load, outputs rounded once).  Errors as gdn_chunk_fwd.
+ * Precision: fp32 inputs, fp32 arithmetic throughout.  bf16 inputs, bf16 MFMA
+ * operands with fp32 accumulation as in the forward, except that the operands the
+ * gate gradient is most sensitive to (diag(beta) V' in U, in the chunk-start states'
+ * recurrence and in the per-chunk kernel, and d U in the states' update) are carried
+ * as bf16 hi + lo pairs.  Errors as gdn_chunk_fwd.
  */
 int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, const void* beta,
                   const float* initial_state, const int32_t* cu_seqlens, float scale,
