@@ -113,10 +113,20 @@ __device__ __forceinline__ BwdUnit bwd_unit(const Problem& p, const BwdArgs& a, 
   return u;
 }
 
+// Workgroup barrier for LDS data: this wave's LDS accesses complete, then s_barrier.
+// Unlike __syncthreads it does not wait for the wave's outstanding global stores (no
+// data written to global memory is read back inside these kernels).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 constexpr int kDhCols = 32;     // value columns per chain workgroup
 constexpr int kDhThreads = 256;
 constexpr int kGrThreads = 512;
-constexpr int kTS = 72;         // row stride (elements) of 64 x 64 LDS matrices
+constexpr int kTS = 80;         // row stride (elements) of 64 x 64 LDS matrices: rows
+                                // 8 (mod 32) dwords apart, as every LDS matrix here
 
 }  // namespace
 
@@ -218,12 +228,27 @@ __global__ __launch_bounds__(kDhThreads) void bwd_dh_kernel(Problem p, BwdArgs a
       pb = lane < len ? beta_at(p.beta, (si.tok0 + t0 + lane) * H + h, p.beta_bf16) : 0.f;
     }
   };
+  // dV of chunk c (16-byte stores of the rows inside the chunk) from sDV, and the
+  // checkpoint of the state gradient after chunk c from the registers
+  auto store_dv = [&](int c) {
+    const int len = min(kChunk, si.len - c * kChunk);
+    const int row = tid >> 2, cp = tid & 3;
+    if (row < len)
+      *reinterpret_cast<u32x4*>(DVg + ((int64_t)c * kChunk + row) * rv + cp * 8) =
+          *reinterpret_cast<const u32x4*>(sDV + row * VS + cp * 8);
+  };
+  auto store_ckpt = [&](int c) {
+    float* ck = a.dhchk + ((si.chunk0 + c) * H + h) * (int64_t)DK * dv;
+#pragma unroll
+    for (int tt = 0; tt < NRT; ++tt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        *reinterpret_cast<f32x4*>(ck + ckpt_offset(16 * (NRT * w + tt) + 4 * q, col0 + 16 * j + r, dv)) = dh[tt][j];
+  };
   if (c_hi > c_lo) load(c_hi - 1);
-  __syncthreads();
+  lds_barrier();
 
   for (int c = c_hi - 1; c >= c_lo; --c) {
-    const int len = min(kChunk, si.len - c * kChunk);
-    const int64_t t0 = (int64_t)c * kChunk;
     // ---- this chunk into LDS; the gates (wave 0); the next chunk's loads
 #pragma unroll
     for (int k = 0; k < NKP; ++k) {
@@ -246,7 +271,7 @@ __global__ __launch_bounds__(kDhThreads) void bwd_dh_kernel(Problem p, BwdArgs a
       sBet[lane] = pb;
     }
     if (c > c_lo) load(c - 1);
-    __syncthreads();
+    lds_barrier();
 
     // ---- P = (Q K^T) * Gamma (lower blocks); gamma * scale * dO; X' = K dh'
     for (int k = w; k < 10; k += 4) {
@@ -279,7 +304,7 @@ __global__ __launch_bounds__(kDhThreads) void bwd_dh_kernel(Problem p, BwdArgs a
       for (int ks = 0; ks < NKS; ++ks)
         X[j] = Mb::run(op_rows(sK, KS, 16 * w, 32 * ks), op_cols(sH, HS, 32 * ks, 16 * j), X[j]);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- dU = diag(d) X' + scale P^T dO (P^T is upper triangular)
 #pragma unroll
@@ -293,7 +318,7 @@ __global__ __launch_bounds__(kDhThreads) void bwd_dh_kernel(Problem p, BwdArgs a
         sDU[i * VS + 16 * j + r] = (bf16)(sD[i] * X[j][s] + p.scale * acc[s]);
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- dR = T^T dU, dV = diag(beta) dR
 #pragma unroll
@@ -309,20 +334,11 @@ __global__ __launch_bounds__(kDhThreads) void bwd_dh_kernel(Problem p, BwdArgs a
         sGV[i * VS + 16 * j + r] = (bf16)(-sGam[i] * dvv);
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     if (!chain) {
-      // dV (16-byte stores of rows inside the chunk) and the checkpoint of dh'
-      const int row = tid >> 2, cp = tid & 3;
-      if (row < len)
-        *reinterpret_cast<u32x4*>(DVg + (t0 + row) * rv + cp * 8) =
-            *reinterpret_cast<const u32x4*>(sDV + row * VS + cp * 8);
-      float* ck = a.dhchk + ((si.chunk0 + c) * H + h) * (int64_t)DK * dv;
-#pragma unroll
-      for (int tt = 0; tt < NRT; ++tt)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          *reinterpret_cast<f32x4*>(ck + ckpt_offset(16 * (NRT * w + tt) + 4 * q, col0 + 16 * j + r, dv)) = dh[tt][j];
+      store_dv(c);
+      store_ckpt(c);
     }
     // ---- dh <- gamma_n dh' + Q^T (gamma dY) - K^T (gamma dV)
     const float gn = fast_exp(sG[kChunk - 1]);
@@ -341,7 +357,7 @@ __global__ __launch_bounds__(kDhThreads) void bwd_dh_kernel(Problem p, BwdArgs a
 #pragma unroll
         for (int s = 0; s < 4; ++s) sH[(16 * t + 4 * q + s) * HS + 16 * j + r] = (bf16)acc[s];
       }
-    __syncthreads();
+    lds_barrier();
   }
 
   if (chain) {
@@ -377,13 +393,14 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
   constexpr int KS = DK + 16, VS = DV + 16, HS = DK + 16, TS = kTS;
   constexpr int NKS = DK / 32, NVS = DV / 32;
   constexpr int NJV = DV / 32, NJK = DK / 32;   // column tiles per wave: 64 x dv, 64 x dk results
-  constexpr int RF = (kChunk * VS > 2 * kChunk * TS) ? kChunk * VS : 2 * kChunk * TS;
-  constexpr int RG = (kChunk * VS > kChunk * TS) ? kChunk * VS : kChunk * TS;
+  constexpr int RF = (kChunk * VS > kChunk * TS) ? kChunk * VS : kChunk * TS;
+  constexpr int RG = RF;
+  static_assert(DV * HS >= kChunk * TS, "dB + dB^T fits the h^T region");
   constexpr int NHP = DK * DV / 4 / NT;         // 16-byte checkpoint pieces per thread
   static_assert(NHP * NT * 4 == DK * DV, "checkpoint pieces");
   __shared__ __align__(16) bf16 sK[kChunk * KS], sQ[kChunk * KS], sDO[kChunk * VS], sT[kChunk * TS];
-  __shared__ __align__(16) bf16 sH[DV * HS];   // h^T, then dh'^T: [value column][key]
-  __shared__ __align__(16) bf16 sF[RF];        // diag(beta) V', then dU, then (dP * Gamma | dB + dB^T)
+  __shared__ __align__(16) bf16 sH[DV * HS];   // h^T, then W's low half, then dh'^T, then dB + dB^T
+  __shared__ __align__(16) bf16 sF[RF];        // diag(beta) V', then dU, then dP * Gamma
   __shared__ __align__(16) bf16 sR[RG];        // P, then dR
   __shared__ __align__(16) bf16 sU[kChunk * VS];
   __shared__ float sG[kChunk], sGam[kChunk], sD[kChunk], sBet[kChunk];
@@ -435,10 +452,32 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
     const int rq = e / DV, cv = e % DV;
     *reinterpret_cast<uint2*>(sH + cv * HS + 4 * rq) = pack_bf16x4(x);
   };
+  // gamma_n <h, dh'> from both fp32 checkpoints (dh' is loaded again, as its bf16
+  // transpose, once h^T is dead)
+  float hd = 0.f;
 #pragma unroll
   for (int k = 0; k < NHP; ++k) {
     const int e = tid + NT * k;
-    ck_to_lds(*reinterpret_cast<const f32x4*>(hck + (int64_t)e * 4), e);
+    const f32x4 hx = *reinterpret_cast<const f32x4*>(hck + (int64_t)e * 4);
+    const f32x4 dx = *reinterpret_cast<const f32x4*>(dck + (int64_t)e * 4);
+    hd += hx[0] * dx[0] + hx[1] * dx[1] + hx[2] * dx[2] + hx[3] * dx[3];
+    ck_to_lds(hx, e);
+  }
+  // this lane's V elements (accumulator layout of its 64 x dv tiles) and dV rows (A
+  // operands of dK's dV h^T term), loaded with the rest
+  float vin[NJV][4];
+#pragma unroll
+  for (int jj = 0; jj < NJV; ++jj)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int i = 16 * u + 4 * q + s;
+      vin[jj][s] = i < len ? (float)Vg[i * rv + 16 * (half * NJV + jj) + r] : 0.f;
+    }
+  frag dvf[NVS];
+#pragma unroll
+  for (int ks = 0; ks < NVS; ++ks) {
+    const int row = 16 * u + r;
+    dvf[ks] = row < len ? *reinterpret_cast<const frag*>(DVg + row * rv + 32 * ks + 8 * q) : __builtin_bit_cast(frag, z4);
   }
   if (w == 0) {
     const float g = lane < len ? p.g[(t0 + lane) * H + h] : 0.f;
@@ -451,11 +490,11 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
   }
   sPG[w][lane] = 0.f;
   sPB[w][lane] = 0.f;
-  __syncthreads();
+  lds_barrier();
 
   float rg[4] = {0.f, 0.f, 0.f, 0.f};   // dG of rows 16 u + 4 q + s (this wave's column tiles)
   float rb[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta, the same rows
-  float gnp = 0.f;                      // this lane's share of dG at the last row (G_n)
+  float gnp = fast_exp(sG[kChunk - 1]) * hd;   // this lane's share of dG at the last row (G_n)
 
   // ---- (a) P = (Q K^T) * Gamma on this wave's lower blocks, into LDS (the blocks
   //      above are zero).  K K^T and Q K^T are formed again where dA and dP need them
@@ -490,18 +529,12 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
 #pragma unroll
   for (int jj = 0; jj < NJV; ++jj) {
     const int jt = half * NJV + jj;
-    f32x4 vv;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int i = 16 * u + 4 * q + s;
-      vv[s] = i < len ? (float)Vg[i * rv + 16 * jt + r] : 0.f;
-    }
     f32x4 acc = zero4;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
       acc = Mb::run(op_rows(sK, KS, 16 * u, 32 * ks), op_rows(sH, HS, 16 * jt, 32 * ks), acc);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) vp[jj][s] = vv[s] - sGam[16 * u + 4 * q + s] * acc[s];
+    for (int s = 0; s < 4; ++s) vp[jj][s] = vin[jj][s] - sGam[16 * u + 4 * q + s] * acc[s];
   }
   // ---- (c) dQ = diag(gamma) dY h^T and dK = -diag(gamma) dV h^T (first terms), with
   //      their gamma terms of dG: sum_d Q_id dQ_id + sum_d K_id dK_id
@@ -513,16 +546,12 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
   }
 #pragma unroll
   for (int ks = 0; ks < NVS; ++ks) {
-    // this lane's A rows of dO (LDS) and dV (the chain's output, global)
     const frag dof = op_rows(sDO, VS, 16 * u, 32 * ks);
-    const int row = 16 * u + r;
-    const frag dvf = row < len ? *reinterpret_cast<const frag*>(DVg + row * rv + 32 * ks + 8 * q)
-                               : __builtin_bit_cast(frag, z4);
 #pragma unroll
     for (int jj = 0; jj < NJK; ++jj) {
       const frag hb = op_cols(sH, HS, 32 * ks, 16 * (half * NJK + jj));
       dq[jj] = Mb::run(dof, hb, dq[jj]);
-      dk[jj] = Mb::run(dvf, hb, dk[jj]);
+      dk[jj] = Mb::run(dvf[ks], hb, dk[jj]);
     }
   }
 #pragma unroll
@@ -536,7 +565,11 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
       rg[s] += (float)sQ[i * KS + d] * dq[jj][s] + (float)sK[i * KS + d] * dk[jj][s];
     }
   }
-  __syncthreads();   // h^T read for the last time
+  // the chain's dh' (fp32, L2-resident since the load phase) for its bf16 transpose
+  f32x4 pdh[NHP];
+#pragma unroll
+  for (int k = 0; k < NHP; ++k) pdh[k] = *reinterpret_cast<const f32x4*>(dck + (int64_t)(tid + NT * k) * 4);
+  lds_barrier();   // h^T read for the last time
 
   // ---- W = diag(beta) V' into LDS as a bf16 hi + lo pair (lo in the h^T region, now
   //      free): the gate gradient is sensitive to U's rounding
@@ -552,10 +585,9 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
       sF[o] = hi;
       sWl[o] = (bf16)(x - (float)hi);
     }
-  __syncthreads();
+  lds_barrier();
 
-  // ---- (e) U = T diag(beta) V' (T lower triangular); the chain's dh'^T into LDS and
-  //      gamma_n <h, dh'> (the fp32 h pieces re-read from the cache)
+  // ---- (e) U = T diag(beta) V' (T lower triangular); the chain's dh'^T into LDS
   f32x4 Ut[NJV];
 #pragma unroll
   for (int jj = 0; jj < NJV; ++jj) {
@@ -570,21 +602,10 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
 #pragma unroll
     for (int s = 0; s < 4; ++s) sU[(16 * u + 4 * q + s) * VS + 16 * jt + r] = (bf16)acc[s];
   }
-  __syncthreads();   // W's low half read: the region takes dh'^T
-  {
-    const float gn = fast_exp(sG[kChunk - 1]);
-    float hd = 0.f;
+  lds_barrier();   // W's low half read: the region takes dh'^T
 #pragma unroll
-    for (int k = 0; k < NHP; ++k) {
-      const int e = tid + NT * k;
-      const f32x4 dx = *reinterpret_cast<const f32x4*>(dck + (int64_t)e * 4);
-      const f32x4 hx = *reinterpret_cast<const f32x4*>(hck + (int64_t)e * 4);
-      hd += hx[0] * dx[0] + hx[1] * dx[1] + hx[2] * dx[2] + hx[3] * dx[3];
-      ck_to_lds(dx, e);
-    }
-    gnp += gn * hd;
-  }
-  __syncthreads();
+  for (int k = 0; k < NHP; ++k) ck_to_lds(pdh[k], tid + NT * k);
+  lds_barrier();
 
   // ---- (f) X' = K dh', and the d terms of dG
   f32x4 X[NJV];
@@ -604,7 +625,7 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
       gnp += sD[i] * xu;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- (h) dU = diag(d) X' + scale P^T dO
 #pragma unroll
@@ -619,7 +640,7 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
       sF[i * VS + 16 * jt + r] = (bf16)(sD[i] * X[jj][s] + p.scale * acc[s]);
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- (i) dR = T^T dU, and the V' term of dbeta
 #pragma unroll
@@ -645,12 +666,12 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
 #pragma unroll
     for (int s = 0; s < 4; ++s) dk[jj][s] += sD[16 * u + 4 * q + s] * acc[s];
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- (k) dP = lower(dY U^T) and dA = strict_lower(-dR U^T) on this wave's blocks:
   //      the Gamma terms of dG, the A term of dbeta, dP * Gamma and dB + dB^T into LDS
   bf16* sDPG = sF;
-  bf16* sDBS = sF + kChunk * TS;
+  bf16* sDBS = sH;   // dh'^T was read for the last time in (j)
   for (int bi = 0; bi < nb; ++bi) {
     {
       int ba, bb;
@@ -694,7 +715,7 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
       if (q == 0) sPG[w][16 * bb + r] -= colc;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- (l) dQ += (dP * Gamma) K;  dK += (dP * Gamma)^T Q + (dB + dB^T) K; store
   bf16* dQg = reinterpret_cast<bf16*>(a.dq) + t0 * rqk + (int64_t)h * DK;
@@ -709,14 +730,6 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
       dk[jj] = Mb::run(op_rows(sDBS, TS, 16 * u, 32 * ks), op_cols(sK, KS, 32 * ks, 16 * dt), dk[jj]);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int i = 16 * u + 4 * q + s;
-      if (i < len) {
-        dQg[i * rqk + 16 * dt + r] = (bf16)dq[jj][s];
-        dKg[i * rqk + 16 * dt + r] = (bf16)dk[jj][s];
-      }
-    }
   }
   // ---- the row sums of this wave's tiles, then dG, dbeta and dg per row
 #pragma unroll
@@ -733,7 +746,7 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
     for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
     if (lane == 0) sPN[w] = t;
   }
-  __syncthreads();
+  lds_barrier();
   if (w == 0) {
     float dG = 0.f, db = 0.f;
 #pragma unroll
@@ -755,6 +768,17 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
       else reinterpret_cast<float*>(a.dbeta)[(t0 + lane) * H + h] = db;
     }
   }
+  // dq and dk last: no barrier waits for these stores
+#pragma unroll
+  for (int jj = 0; jj < NJK; ++jj)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int i = 16 * u + 4 * q + s, d = 16 * (half * NJK + jj) + r;
+      if (i < len) {
+        dQg[i * rqk + d] = (bf16)dq[jj][s];
+        dKg[i * rqk + d] = (bf16)dk[jj][s];
+      }
+    }
 }
 
 template <int DK>
