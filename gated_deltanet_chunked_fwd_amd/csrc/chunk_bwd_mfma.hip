@@ -147,6 +147,7 @@ __global__ __launch_bounds__(kDhThreads) void bwd_dh_kernel(Problem p, BwdArgs a
       sDV[kChunk * VS];
   __shared__ __align__(16) bf16 sH[DK * HS];
   __shared__ float sG[kChunk], sGam[kChunk], sD[kChunk], sBet[kChunk];
+  __shared__ float sHD[NT / 64];
 
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, q = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -200,8 +201,10 @@ __global__ __launch_bounds__(kDhThreads) void bwd_dh_kernel(Problem p, BwdArgs a
         sH[d * HS + c] = (bf16)x;
       }
 
-  // ---- one chunk's inputs, loaded into registers a chunk ahead
+  // ---- one chunk's inputs, loaded into registers a chunk ahead (the forward state at
+  //      the chunk's start, for gamma_n <h, dh'>, in the layout of this lane's dh')
   u32x4 pk[NKP], pq[NKP], po, pt[2];
+  f32x4 ph[NRT][2];
   float pg = 0.f, pb = 0.f;
   auto load = [&](int c) {
     const int len = min(kChunk, si.len - c * kChunk);
@@ -227,9 +230,20 @@ __global__ __launch_bounds__(kDhThreads) void bwd_dh_kernel(Problem p, BwdArgs a
       pg = lane < len ? Gg[(t0 + lane) * H] : 0.f;
       pb = lane < len ? beta_at(p.beta, (si.tok0 + t0 + lane) * H + h, p.beta_bf16) : 0.f;
     }
+    if (!chain) {
+      const float* hc = a.hchk + ((si.chunk0 + c) * H + h) * (int64_t)DK * dv;
+#pragma unroll
+      for (int tt = 0; tt < NRT; ++tt)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          ph[tt][j] = *reinterpret_cast<const f32x4*>(hc + ckpt_offset(16 * (NRT * w + tt) + 4 * q, col0 + 16 * j + r, dv));
+    }
   };
-  // dV of chunk c (16-byte stores of the rows inside the chunk) from sDV, and the
-  // checkpoint of the state gradient after chunk c from the registers
+  // dV of chunk c (16-byte stores of the rows inside the chunk) from sDV; the
+  // checkpoint of the state gradient after chunk c from the registers, as its bf16
+  // transpose (four keys of one value column per 8-byte store); this wave's share of
+  // gamma_n <h, dh'> into sHD (hd: this lane's <h, dh'> terms, formed at the top of the
+  // step; the workgroup's sum is written at the next step)
   auto store_dv = [&](int c) {
     const int len = min(kChunk, si.len - c * kChunk);
     const int row = tid >> 2, cp = tid & 3;
@@ -237,18 +251,32 @@ __global__ __launch_bounds__(kDhThreads) void bwd_dh_kernel(Problem p, BwdArgs a
       *reinterpret_cast<u32x4*>(DVg + ((int64_t)c * kChunk + row) * rv + cp * 8) =
           *reinterpret_cast<const u32x4*>(sDV + row * VS + cp * 8);
   };
-  auto store_ckpt = [&](int c) {
-    float* ck = a.dhchk + ((si.chunk0 + c) * H + h) * (int64_t)DK * dv;
+  auto store_ckpt = [&](int c, float hd) {
+    bf16* ck = reinterpret_cast<bf16*>(a.dhchk) + ((si.chunk0 + c) * H + h) * (int64_t)DK * dv;
 #pragma unroll
     for (int tt = 0; tt < NRT; ++tt)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        *reinterpret_cast<f32x4*>(ck + ckpt_offset(16 * (NRT * w + tt) + 4 * q, col0 + 16 * j + r, dv)) = dh[tt][j];
+        *reinterpret_cast<uint2*>(ck + (int64_t)(col0 + 16 * j + r) * DK + 16 * (NRT * w + tt) + 4 * q) =
+            pack_bf16x4(dh[tt][j]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) hd += __shfl_xor(hd, off, 64);
+    if (lane == 0) sHD[w] = fast_exp(sG[kChunk - 1]) * hd;
+  };
+  // the workgroup's gamma_n <h, dh'> of chunk c, once sHD is complete
+  auto store_gnh = [&](int c) {
+    if (tid == 0) {
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < NT / 64; ++k) s += sHD[k];
+      a.gnh[((si.chunk0 + c) * H + h) * nblk + blk] = s;
+    }
   };
   if (c_hi > c_lo) load(c_hi - 1);
   lds_barrier();
 
   for (int c = c_hi - 1; c >= c_lo; --c) {
+    if (!chain && c + 1 < c_hi) store_gnh(c + 1);
     // ---- this chunk into LDS; the gates (wave 0); the next chunk's loads
 #pragma unroll
     for (int k = 0; k < NKP; ++k) {
@@ -269,6 +297,16 @@ __global__ __launch_bounds__(kDhThreads) void bwd_dh_kernel(Problem p, BwdArgs a
       sGam[lane] = fast_exp(G);
       sD[lane] = fast_exp(Gn - G);
       sBet[lane] = pb;
+    }
+    // <h, dh'> of this chunk, before the next chunk's loads take ph
+    float hdc = 0.f;
+    if (!chain) {
+#pragma unroll
+      for (int tt = 0; tt < NRT; ++tt)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) hdc += ph[tt][j][i] * dh[tt][j][i];
     }
     if (c > c_lo) load(c - 1);
     lds_barrier();
@@ -338,7 +376,7 @@ __global__ __launch_bounds__(kDhThreads) void bwd_dh_kernel(Problem p, BwdArgs a
 
     if (!chain) {
       store_dv(c);
-      store_ckpt(c);
+      store_ckpt(c, hdc);
     }
     // ---- dh <- gamma_n dh' + Q^T (gamma dY) - K^T (gamma dV)
     const float gn = fast_exp(sG[kChunk - 1]);
@@ -360,6 +398,7 @@ __global__ __launch_bounds__(kDhThreads) void bwd_dh_kernel(Problem p, BwdArgs a
     lds_barrier();
   }
 
+  if (!chain && c_hi > c_lo) store_gnh(c_lo);
   if (chain) {
     // the state gradient at the segment's start from a zero one at its end: the merge's
     // offset for this segment (accumulator-tile order, as the forward's S*)
@@ -384,9 +423,9 @@ __global__ __launch_bounds__(kDhThreads) void bwd_dh_kernel(Problem p, BwdArgs a
 
 // ========================= 2. the gradients of every chunk =========================
 // Workgroup = (chunk, head), eight waves.  Wave w owns row tile u = w % 4 of the
-// 64 x dv and 64 x dk results, column tiles [NJ (w / 4), NJ (w / 4 + 1)), and one or
-// two of the ten lower 64 x 64 blocks (w and w + 8), the same tiles in every product
-// so that the row sums of dbeta and dG pair registers lane by lane.
+// 64 x dv and 64 x dk results, column tiles [NJ (w / 4), NJ (w / 4 + 1)), and the
+// lower 64 x 64 blocks w and w + 8, the same tiles in every product so that the row
+// sums of dbeta and dG pair registers lane by lane.
 template <int DK, int DV>
 __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArgs a) {
   constexpr int NT = kGrThreads, NW = NT / 64;
@@ -424,7 +463,7 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
   const bf16* DOg = reinterpret_cast<const bf16*>(a.d_o) + t0 * rv + (int64_t)h * DV;
   const bf16* DVg = reinterpret_cast<const bf16*>(a.dv) + t0 * rv + (int64_t)h * DV;
   const float* hck = a.hchk + (cg * H + h) * (int64_t)(DK * DV);
-  const float* dck = a.dhchk + (cg * H + h) * (int64_t)(DK * DV);
+  const bf16* dck = reinterpret_cast<const bf16*>(a.dhchk) + (cg * H + h) * (int64_t)(DK * DV);
   const bf16* Tc = reinterpret_cast<const bf16*>(a.tmat) + (cg * H + h) * (int64_t)(kChunk * kChunk);
   const u32x4 z4 = {0u, 0u, 0u, 0u};
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -443,8 +482,9 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
     *reinterpret_cast<u32x4*>(sDO + row * VS + cp * 8) =
         row < len ? *reinterpret_cast<const u32x4*>(DOg + row * rv + cp * 8) : z4;
   }
-  {
-    const int row = tid >> 3, cp = tid & 7;
+#pragma unroll
+  for (int k = 0; k < kChunk * kChunk / 8 / NT; ++k) {
+    const int idx = tid + NT * k, row = idx >> 3, cp = idx & 7;
     *reinterpret_cast<u32x4*>(sT + row * TS + cp * 8) = *reinterpret_cast<const u32x4*>(Tc + row * kChunk + cp * 8);
   }
   // checkpoint piece e holds keys 4 (e / DV) .. +3 of value column e % DV (ckpt_offset)
@@ -452,17 +492,15 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
     const int rq = e / DV, cv = e % DV;
     *reinterpret_cast<uint2*>(sH + cv * HS + 4 * rq) = pack_bf16x4(x);
   };
-  // gamma_n <h, dh'> from both fp32 checkpoints (dh' is loaded again, as its bf16
-  // transpose, once h^T is dead)
-  float hd = 0.f;
 #pragma unroll
   for (int k = 0; k < NHP; ++k) {
     const int e = tid + NT * k;
-    const f32x4 hx = *reinterpret_cast<const f32x4*>(hck + (int64_t)e * 4);
-    const f32x4 dx = *reinterpret_cast<const f32x4*>(dck + (int64_t)e * 4);
-    hd += hx[0] * dx[0] + hx[1] * dx[1] + hx[2] * dx[2] + hx[3] * dx[3];
-    ck_to_lds(hx, e);
+    ck_to_lds(*reinterpret_cast<const f32x4*>(hck + (int64_t)e * 4), e);
   }
+  // gamma_n <h, dh'>: the chain's partial sums, one per 32 value columns
+  float hd = 0.f;
+  if (tid == 0)
+    for (int b = 0; b < DV / kDhCols; ++b) hd += a.gnh[(cg * H + h) * (DV / kDhCols) + b];
   // this lane's V elements (accumulator layout of its 64 x dv tiles) and dV rows (A
   // operands of dK's dV h^T term), loaded with the rest
   float vin[NJV][4];
@@ -494,12 +532,12 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
 
   float rg[4] = {0.f, 0.f, 0.f, 0.f};   // dG of rows 16 u + 4 q + s (this wave's column tiles)
   float rb[4] = {0.f, 0.f, 0.f, 0.f};   // dbeta, the same rows
-  float gnp = fast_exp(sG[kChunk - 1]) * hd;   // this lane's share of dG at the last row (G_n)
+  float gnp = hd;                       // this lane's share of dG at the last row (G_n)
 
   // ---- (a) P = (Q K^T) * Gamma on this wave's lower blocks, into LDS (the blocks
   //      above are zero).  K K^T and Q K^T are formed again where dA and dP need them
   //      (fewer registers held through the products between).
-  const int nb = (w + 8 < 10) ? 2 : 1;
+
   auto gram = [&](int ba, int bb, f32x4& kk, f32x4& qk) {
     kk = zero4;
     qk = zero4;
@@ -510,9 +548,12 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
       qk = Mb::run(op_rows(sQ, KS, 16 * ba, 32 * ks), kb, qk);
     }
   };
-  for (int bi = 0; bi < nb; ++bi) {
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi) {
+    const int kb = w + NW * bi;
+    if (kb >= 10) break;
     int ba, bb;
-    tri_block(w + 8 * bi, ba, bb);
+    tri_block(kb, ba, bb);
     f32x4 qk = zero4;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
@@ -565,10 +606,6 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
       rg[s] += (float)sQ[i * KS + d] * dq[jj][s] + (float)sK[i * KS + d] * dk[jj][s];
     }
   }
-  // the chain's dh' (fp32, L2-resident since the load phase) for its bf16 transpose
-  f32x4 pdh[NHP];
-#pragma unroll
-  for (int k = 0; k < NHP; ++k) pdh[k] = *reinterpret_cast<const f32x4*>(dck + (int64_t)(tid + NT * k) * 4);
   lds_barrier();   // h^T read for the last time
 
   // ---- W = diag(beta) V' into LDS as a bf16 hi + lo pair (lo in the h^T region, now
@@ -603,8 +640,12 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
     for (int s = 0; s < 4; ++s) sU[(16 * u + 4 * q + s) * VS + 16 * jt + r] = (bf16)acc[s];
   }
   lds_barrier();   // W's low half read: the region takes dh'^T
+  // the chain's dh'^T (bf16 [value column][key]) into LDS
 #pragma unroll
-  for (int k = 0; k < NHP; ++k) ck_to_lds(pdh[k], tid + NT * k);
+  for (int k = 0; k < DV * DK / 8 / NT; ++k) {
+    const int idx = tid + NT * k, row = idx / (DK / 8), cp = idx % (DK / 8);
+    *reinterpret_cast<u32x4*>(sH + row * HS + cp * 8) = *reinterpret_cast<const u32x4*>(dck + (int64_t)idx * 8);
+  }
   lds_barrier();
 
   // ---- (f) X' = K dh', and the d terms of dG
@@ -672,10 +713,12 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
   //      the Gamma terms of dG, the A term of dbeta, dP * Gamma and dB + dB^T into LDS
   bf16* sDPG = sF;
   bf16* sDBS = sH;   // dh'^T was read for the last time in (j)
-  for (int bi = 0; bi < nb; ++bi) {
-    {
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi) {
+    const int kb = w + NW * bi;
+    if (kb < 10) {
       int ba, bb;
-      tri_block(w + 8 * bi, ba, bb);
+      tri_block(kb, ba, bb);
       f32x4 kk, qk;
       gram(ba, bb, kk, qk);
       f32x4 dp = zero4, da = zero4;

@@ -851,7 +851,7 @@ static int64_t bwd_segment_chunks(const gdn_shape* s, const gdn_opts* o, int64_t
 // with a split the segment offsets, the segments' transposed maps, offsets and end
 // state gradients (and the merge's group maps for long chains).
 struct BwdLayout {
-  size_t chunk_off = 0, tmat = 0, hchk = 0, dhchk = 0, dq_p = 0, dk_p = 0, dbeta_p = 0, dg_p = 0, total = 0;
+  size_t chunk_off = 0, tmat = 0, hchk = 0, dhchk = 0, gnh = 0, dq_p = 0, dk_p = 0, dbeta_p = 0, dg_p = 0, total = 0;
   size_t seg_off = 0, seg_b = 0, seg_m = 0, seg_g = 0, gmat = 0, gvec = 0;
   int max_chunks = 0;
   int64_t seg_chunks = 0, total_segs = 0, max_steps = 0;
@@ -881,7 +881,8 @@ static BwdLayout bwd_layout(const gdn_shape* s, const gdn_opts* o) {
   L.hchk = take((size_t)chunks * s->H * s->dk * s->dv * sizeof(float));
   L.mfma = s->qkv_dtype == GDN_BF16;
   if (L.mfma) {
-    L.dhchk = take((size_t)chunks * s->H * s->dk * s->dv * sizeof(float));
+    L.dhchk = take((size_t)chunks * s->H * s->dk * s->dv * sizeof(uint16_t));
+    L.gnh = take((size_t)chunks * s->H * nblk * sizeof(float));
   } else {
     L.dq_p = take((size_t)nblk * tot * s->H * s->dk * sizeof(float));
     L.dk_p = take((size_t)nblk * tot * s->H * s->dk * sizeof(float));
@@ -971,7 +972,8 @@ int gdn_chunk_bwd(const void* q, const void* k, const void* v, const float* g, c
   a.seg_g = L.split ? reinterpret_cast<const float*>(ws + L.seg_g) : nullptr;
   void* tmat = ws + L.tmat;
   a.tmat = tmat;
-  a.dhchk = L.mfma ? reinterpret_cast<float*>(ws + L.dhchk) : nullptr;
+  a.dhchk = L.mfma ? ws + L.dhchk : nullptr;
+  a.gnh = L.mfma ? reinterpret_cast<float*>(ws + L.gnh) : nullptr;
   if (total_chunks > 0) {
     // the state at every chunk start, by the forward's own recurrence: the chunk
     // inverses (whole, for the MFMA backward's transposed reads), then the checkpoint

@@ -199,10 +199,13 @@ struct BwdArgs {
   float* seg_b;              // kBwdChain: per bwd_slot, dk x dv fp32 (sfrag_offset order)
   const float* seg_g;        // kBwdFull with a split: per bwd_slot, [dk, dv] fp32 (natural)
   // bf16 path (chunk_bwd_mfma.hip): the chunk inverses (K1, [total_chunks, H, 64, 64]
-  // bf16, the zero upper-right quadrant written) and the chain's checkpoints of the
-  // state gradient after every chunk ([total_chunks, H] x dk x dv fp32, ckpt_offset)
+  // bf16, the zero upper-right quadrant written); the chain's checkpoints of the state
+  // gradient dh' after every chunk, as its bf16 transpose ([total_chunks, H, dv, dk]);
+  // and gamma_n <h, dh'> of every chunk in fp32, one partial sum per 32 value columns
+  // ([total_chunks, H, dv / 32])
   const void* tmat;
-  float* dhchk;
+  void* dhchk;
+  float* gnh;
 };
 constexpr int kBwdColumnBlock = 32;   // value columns per backward workgroup
 hipError_t launch_chunk_bwd(const Problem& p, const BwdArgs& a, hipStream_t s, KernelEvents ev = {});
