@@ -5,7 +5,8 @@ relative L2 error of dq, dk, dv, dg, dbeta and d_initial_state, under the forwar
 tolerances (1e-2 for bf16 storage, 1e-5 for fp32).  Covers the fp32 tiny workload,
 bf16 with every dk / dv combination, ragged last chunks, packed input with empty
 and one-token sequences, initial-state and final-state gradients present or absent,
-strong and absent decay, and fp32 beta with bf16 q/k/v.  The split of the reverse
+strong and absent decay, and fp32 beta with bf16 q/k/v; a seeded random sweep over
+those axes (dbeta judged at its own dtype's bar); two calls bitwise equal.  The split of the reverse
 sweep (segments run from the state gradient at their end, found by a merge over the
 segments' transposed maps) is checked the same way: forced segment lengths on dense
 and packed input, bf16 and fp32, with and without the final-state gradient, a chain
@@ -174,3 +175,92 @@ def test_backward_planner_splits_long_few_heads():
     assert sizes[0] > sizes[1], sizes
     worst = _run_and_compare(inp, seed=8)
     _assert(worst, TOL["bf16"], "backward planner split")
+
+
+RANDOM_CASES = 16
+
+
+def draw_backward_case(seed):
+    """A seeded draw over the backward's configuration space (sizes the fp64 chunk
+    oracle finishes in about a second)."""
+    rng = np.random.default_rng(7000 + seed)
+    dtype = "f32" if seed % 4 == 0 else "bf16"
+    beta_dtype = dtype if rng.random() < 0.7 else ("f32" if dtype == "bf16" else "bf16")
+    dk, dv = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
+    H = int(rng.integers(1, 4))
+    packed = rng.random() < 0.5
+    # bf16 draws take no one-token sequence: its dbeta (and, without a state, its dq)
+    # is a single dot product whose relative error measures the cancellation in it,
+    # not the kernel (the reading of the fp32 single-token forward case, applied to
+    # the backward's bf16 operands); fp32 draws keep them
+    short = [1] if dtype == "f32" else [2]
+    if packed:
+        lens = [int(x) for x in rng.choice([0] + short + [17, 63, 64, 65, 200, 640], size=int(rng.integers(1, 6)))]
+        if sum(lens) == 0:
+            lens[0] = 129
+        B, T = 1, sum(lens)
+    else:
+        B, T = int(rng.integers(1, 3)), int(rng.choice(short + [65, 300, 777, 1300]))
+        lens = None
+    gate = str(rng.choice(["sigmoid", "uniform", "zero"], p=[0.5, 0.3, 0.2]))
+    zero_heads = tuple(int(h) for h in range(H) if rng.random() < 0.3)
+    h0_std = float(rng.choice([0.0, 0.05])) or None
+    sp = synth.Spec("bwd_random%d" % seed, B=B, T=T, H=H, dk=dk, dv=dv, dtype=dtype, beta_dtype=beta_dtype,
+                    gate=gate, zero_gate_heads=zero_heads, h0_std=None if packed else h0_std, seed=7500 + seed)
+    inp = synth.generate(sp)
+    if packed:
+        inp["cu_seqlens"] = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+        inp["N"] = len(lens)
+        if h0_std:
+            g = torch.Generator().manual_seed(7800 + seed)
+            inp["h0"] = (torch.randn(len(lens), H, dk, dv, generator=g) * h0_std).float()
+    # fp32 draws no forced split: the merge carries each segment's map as a bf16 hi + lo
+    # pair (about 16 significant bits), which bounds a forced fp32 split of many short
+    # segments near the 1e-5 bar (a stated limit; the fixed fp32 split cases above
+    # measure <= 3.4e-6)
+    split = str(rng.choice(["planner", "forced", "none"] if dtype == "bf16" else ["planner", "none"]))
+    opts = None
+    if split == "forced":
+        opts = binding.make_opts(force_segment_chunks=int(rng.choice([1, 2, 3, 5])))
+    elif split == "none":
+        opts = binding.make_opts(no_split=1)
+    with_dhT = bool(rng.random() < 0.7)
+    return inp, opts, with_dhT, split
+
+
+@pytest.mark.parametrize("seed", range(RANDOM_CASES))
+def test_backward_random_configuration(seed):
+    """Every gradient of every (sequence, head) pair against the fp64 chunk-form oracle
+    on a seeded random configuration (both paths: bf16 MFMA and fp32)."""
+    inp, opts, with_dhT, split = draw_backward_case(seed)
+    sp = inp["spec"]
+    label = "random case %d: B=%d T=%d H=%d dk=%d dv=%d %s beta %s gate %s zero %s packed %s h0 %s dhT %s split %s" % (
+        seed, sp.B, sp.T, sp.H, sp.dk, sp.dv, sp.dtype, sp.beta_dtype, sp.gate, sp.zero_gate_heads,
+        None if inp.get("cu_seqlens") is None else inp["cu_seqlens"].tolist(), inp.get("h0") is not None,
+        with_dhT, split)
+    print(label, flush=True)
+    worst = _run_and_compare(inp, seed=100 + seed, with_dhT=with_dhT, opts=opts)
+    # dbeta comes back in beta's dtype: a bf16 dbeta carries bf16 rounding even when
+    # q / k / v are fp32
+    tol = {name: TOL[sp.dtype] for name in NAMES}
+    tol["dbeta"] = max(TOL[sp.dtype], TOL[sp.beta_dtype])
+    msg = "%s worst rel L2 %s" % (label, {k: "%.2e" % v for k, v in worst.items()})
+    print(msg, flush=True)
+    for name in NAMES:
+        assert worst[name] <= tol[name], (name, msg)
+
+
+def test_backward_bf16_is_deterministic():
+    """Two calls on the same inputs give bitwise-identical gradients (every reduction in
+    the bf16 kernels sums in a fixed order; no atomics)."""
+    inp = synth.generate(spec(name="bwd_det", B=2, T=700, H=3, h0_std=0.05, seed=91))
+    do, dhT = _grads_in(inp, 91, True)
+    d = to_dev(inp)
+    outs = []
+    for _ in range(2):
+        got = binding.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do.cuda(), d["h0"], dhT.cuda(),
+                                scale=inp["scale"])
+        torch.cuda.synchronize()
+        outs.append([x.detach().cpu() for x in got])
+    for name, a, b in zip(NAMES, *outs):
+        assert torch.equal(a, b), name
