@@ -92,51 +92,21 @@ __device__ __forceinline__ typename Mma<E>::frag load_frag(const E* src, bool ok
 // forward never reads it.
 template <typename E, int DK>
 __global__ __launch_bounds__(256) void chunk_inverse_kernel(Problem p, E* __restrict__ tout,
-                                                             float* __restrict__ csum, int full,
-                                                             HeadFilter only) {
+                                                             float* __restrict__ csum, int full) {
   using Cfg = InvCfg<E, DK>;
   using M = Mma<E>;
   using frag = typename M::frag;
   constexpr int NS = Cfg::NS, OS = Cfg::OS, ABS = Cfg::ABS, TCS = Cfg::TCS, TBS = Cfg::TBS;
   __shared__ __align__(16) float lds[4 * Cfg::PER_WAVE];
 
-  if (only.ncorr && *only.ncorr == 0u) return;   // no head takes the correction
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, q = lane >> 4;
-  int64_t cg;
-  int h, n;
-  if (only.p1_slots) {
-    // pass 1's work list: a workgroup takes 4 consecutive chunks (one per wave) of a
-    // listed segment; entries read back are clamped to the slots
-    const int L = only.seg_chunks, per = (L + 3) / 4;
-    const int64_t u = blockIdx.x / per;
-    if (u >= (int64_t)only.ncorr[1]) return;
-    const int64_t segs_d = max((int64_t)1, ((p.T + kChunk - 1) / kChunk + L - 1) / L);   // dense
-    const int64_t segs_all = only.seg_off ? (int64_t)only.seg_off[p.N] : (int64_t)p.N * segs_d;
-    const int64_t slot = min(max((int64_t)only.p1_slots[u], (int64_t)0), segs_all * p.H - 1);
-    h = (int)(slot % p.H);
-    const int64_t sg = slot / p.H;
-    int seg;
-    if (only.seg_off) {
-      n = seq_of_chunk(sg, only.seg_off, p.N, 0);
-      seg = (int)(sg - only.seg_off[n]);
-    } else {
-      n = (int)(sg / segs_d);
-      seg = (int)(sg - (int64_t)n * segs_d);
-    }
-    const SeqInfo sq = seq_info(n, p.cu, p.chunk_off, p.T);
-    const int nch = (sq.len + kChunk - 1) / kChunk;
-    const int c = seg * L + (int)(blockIdx.x % per) * 4 + wave;
-    if (c >= min(nch, (seg + 1) * L)) return;   // whole wave: no workgroup barrier follows
-    cg = sq.chunk0 + c;
-  } else {
-    const int HG = (p.H + 3) / 4;
-    cg = blockIdx.x / HG;
-    h = (int)(blockIdx.x % HG) * 4 + wave;
-    if (h >= p.H) return;   // whole wave: no workgroup barrier follows
-    n = seq_of_chunk(cg, p.chunk_off, p.N, p.T);
-  }
+  const int HG = (p.H + 3) / 4;
+  const int64_t cg = blockIdx.x / HG;
+  const int h = (int)(blockIdx.x % HG) * 4 + wave;
+  if (h >= p.H) return;   // whole wave: no workgroup barrier follows
+  const int n = seq_of_chunk(cg, p.chunk_off, p.N, p.T);
   const SeqInfo si = seq_info(n, p.cu, p.chunk_off, p.T);
   const int c = (int)(cg - si.chunk0);
   const int64_t r0 = si.tok0 + (int64_t)c * kChunk;
@@ -303,14 +273,8 @@ hipError_t launch_chunk_offsets(const int32_t* cu, int N, int32_t* chunk_off, hi
 }
 
 hipError_t launch_chunk_inverse(const Problem& p, void* t_out, float* csum, bool full, hipStream_t s,
-                                KernelEvents ev, HeadFilter only) {
-  if (p.total_chunks == 0) {
-    ev.record_empty(s);
-    return hipSuccess;
-  }
-  // (work list: its capacity times the workgroups of one segment)
-  const int64_t blocks = only.p1_slots ? only.p1_cap * ((only.seg_chunks + 3) / 4)
-                                       : p.total_chunks * ((p.H + 3) / 4);
+                                KernelEvents ev) {
+  const int64_t blocks = p.total_chunks * ((p.H + 3) / 4);
   if (blocks == 0) {
     ev.record_empty(s);
     return hipSuccess;
@@ -320,17 +284,17 @@ hipError_t launch_chunk_inverse(const Problem& p, void* t_out, float* csum, bool
   if (p.qkv_bf16) {
     if (p.dk == 128)
       hipExtLaunchKernelGGL(chunk_inverse_kernel<bf16, 128>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, p,
-                            (bf16*)t_out, csum, full ? 1 : 0, only);
+                            (bf16*)t_out, csum, full ? 1 : 0);
     else
       hipExtLaunchKernelGGL(chunk_inverse_kernel<bf16, 64>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, p,
-                            (bf16*)t_out, csum, full ? 1 : 0, only);
+                            (bf16*)t_out, csum, full ? 1 : 0);
   } else {
     if (p.dk == 128)
       hipExtLaunchKernelGGL(chunk_inverse_kernel<float, 128>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, p,
-                            (float*)t_out, csum, full ? 1 : 0, only);
+                            (float*)t_out, csum, full ? 1 : 0);
     else
       hipExtLaunchKernelGGL(chunk_inverse_kernel<float, 64>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, p,
-                            (float*)t_out, csum, full ? 1 : 0, only);
+                            (float*)t_out, csum, full ? 1 : 0);
   }
   return hipGetLastError();
 }

@@ -136,7 +136,11 @@ struct PrepChunk {
 
 }  // namespace
 
-template <int DK, int BV>
+// PASS: kPass3 (steps 1-4 with O) or kPass1 (the split's pass 1: a segment from a zero
+// state on the value columns -> S*, and with V = 0 from the identity on dk more columns
+// -> M; every chunk a lookback step, no Q, no O; the chunk inverses formed here as in
+// pass 3, so a split plan runs no separate chunk-inverse kernel).
+template <int DK, int BV, int PASS>
 __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan plan) {
   using Cfg = WyCfg<DK, BV>;
   static_assert(Cfg::NT == 512, "launch bounds");
@@ -155,6 +159,10 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
   __shared__ __align__(16) float sGB[NP][2 * kChunk];
   __shared__ __align__(16) float sInv[Cfg::INV];
 
+  constexpr bool P1 = PASS == kPass1;
+  if constexpr (P1) {
+    if (plan.cp.ncorr && *plan.cp.ncorr == 0u) return;   // no head takes the correction
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, q = lane >> 4;
@@ -162,17 +170,39 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
 
   // ---- unit decode (XCD-aware: the column blocks of one unit share id mod 8, so they
   //      run on one XCD and share its L2 for K, Q, g, beta).  A launch has fewer than
-  //      2^32 / 512 workgroups, so 32-bit arithmetic covers every index here.
+  //      2^32 / 512 workgroups, so 32-bit arithmetic covers every index here.  Pass 1
+  //      runs dk identity columns after the dv value columns, takes its units from the
+  //      gate scan's work list when there is one (so only units that run are
+  //      dispatched), else numbers every (segment, head) head-major.
   const uint32_t bid = blockIdx.x;
-  const uint32_t ncb = (uint32_t)(dv / BV);
+  const uint32_t ncb = (uint32_t)((P1 ? dv + DK : dv) / BV);
   const uint32_t rest = bid >> 3;
   const int cb = (int)(rest % ncb);
   const uint32_t unit = (rest / ncb) * 8u + (bid & 7u);
   if ((int64_t)unit >= plan.units) return;
   const int col0 = cb * BV;
-  const int h = (int)(unit % (uint32_t)H);
-  const uint32_t sgu = unit / (uint32_t)H;
-  const int64_t sg = plan.seg_order ? (int64_t)plan.seg_order[sgu] : (int64_t)sgu;
+  int h;
+  int64_t sg;
+  if constexpr (P1) {
+    if (plan.cp.p1_slots) {   // (entries read back are clamped to the slots)
+      if (unit >= plan.cp.ncorr[1]) return;
+      const int64_t segs_all =
+          plan.seg_off ? (int64_t)plan.seg_off[p.N]
+                       : (int64_t)p.N * max((int64_t)1, ((p.T + kChunk - 1) / kChunk + plan.seg_chunks - 1) /
+                                                            plan.seg_chunks);
+      const int64_t slot = min(max((int64_t)plan.cp.p1_slots[unit], (int64_t)0), segs_all * H - 1);
+      h = (int)(slot % H);
+      sg = slot / H;
+    } else {
+      const uint32_t nseg = (uint32_t)(plan.units / H);   // segments over all sequences
+      h = (int)(unit / nseg);
+      sg = (int64_t)(unit - (uint32_t)h * nseg);
+    }
+  } else {
+    h = (int)(unit % (uint32_t)H);
+    const uint32_t sgu = unit / (uint32_t)H;
+    sg = plan.seg_order ? (int64_t)plan.seg_order[sgu] : (int64_t)sgu;
+  }
   int n, seg;
   if (plan.seg_off) {
     n = seq_of_chunk(sg, plan.seg_off, p.N, 0);
@@ -198,10 +228,19 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
   const int W = (plan.cp.seg_win && !plan.cp.force_correction)
                     ? min(max(plan.cp.seg_win[sg * H + h], 0), c_begin) : 0;
   // start state and chunk range: [c_start, c_end) is run, O is written from c_out
-  enum { kZero, kH0, kBuf };
+  enum { kZero, kH0, kBuf, kEye };
   int init = kZero, c_start = c_begin;
-  const int c_out = c_begin;
-  if (seg == 0) {
+  int c_out = c_begin;
+  bool mcols = false;   // pass 1: this block carries the transition-matrix columns
+  if constexpr (P1) {
+    // last segments and window heads need no pass 1; a head's windows are all set or
+    // all zero, and its second segment (there is one: this is not the last) holds one
+    if (last_seg) return;
+    if (plan.cp.seg_win && !plan.cp.force_correction && plan.cp.seg_win[(sg - seg + 1) * H + h] > 0) return;
+    mcols = col0 >= dv;
+    init = mcols ? kEye : kZero;
+    c_out = c_end;
+  } else if (seg == 0) {
     init = p.h0 ? kH0 : kZero;
   } else if (W > 0) {
     c_start = c_begin - W;
@@ -225,6 +264,7 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
     // =========================== chain wave ===========================
     const int wcol = wave * Cfg::CW;           // wave's first column inside the block
     f32x4 hs[NKT][NCT];
+    const int mc = col0 - dv + wcol + r16;   // identity column (pass 1's matrix blocks)
     {
       const float* src = init == kH0 ? p.h0 + (int64_t)nh * DK * dv
                                      : (init == kBuf ? plan.cp.hstart + (sg * H + h) * DK * dv : nullptr);
@@ -234,7 +274,8 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
         for (int j = 0; j < NCT; ++j)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            hs[t][j][i] = src ? src[(int64_t)prow(t, 4 * q + i) * dv + col0 + wcol + 16 * j + r16] : 0.f;
+            hs[t][j][i] = src ? src[(int64_t)prow(t, 4 * q + i) * dv + col0 + wcol + 16 * j + r16]
+                              : (init == kEye && prow(t, 4 * q + i) == mc + 16 * j ? 1.f : 0.f);
     }
     bf16* Ob = reinterpret_cast<bf16*>(p.o) + si.tok0 * row_v + (int64_t)h * dv + col0 + wcol;
     const bf16* Vb = reinterpret_cast<const bf16*>(p.v) + si.tok0 * row_v + (int64_t)h * dv + col0 + wcol;
@@ -244,6 +285,11 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
     // chunk's end read its last row: their beta is zero, so they contribute nothing)
     u32x4 vr[Cfg::NVP];
     auto load_v = [&](int i) {
+      if (mcols) {   // V = 0 on the transition-matrix columns
+#pragma unroll
+        for (int j = 0; j < Cfg::NVP; ++j) vr[j] = u32x4{0u, 0u, 0u, 0u};
+        return;
+      }
       const int c = c_start + i;
       const int len = min(kChunk, si.len - c * kChunk);
       const char* vc = reinterpret_cast<const char*>(Vb + (int64_t)c * kChunk * row_v);
@@ -490,7 +536,34 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
       flush_o(nrun - 1);
     }
     __builtin_amdgcn_s_setprio(0);
-    if (last_seg && p.hT) {
+    if constexpr (P1) {
+      if (mcols) {
+        // M as bf16 high and low parts in the merge's operand order (mfrag_offset)
+        bf16* mhi = reinterpret_cast<bf16*>(plan.cp.mcorr) + (sg * H + h) * 2 * DK * DK;
+        bf16* mlo = mhi + DK * DK;
+#pragma unroll
+        for (int t = 0; t < NKT; ++t)
+#pragma unroll
+          for (int j = 0; j < NCT; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float x = hs[t][j][i];
+              const bf16 hi = (bf16)x;
+              const int64_t at = mfrag_offset<DK>(prow(t, 4 * q + i), mc + 16 * j);
+              mhi[at] = hi;
+              mlo[at] = (bf16)(x - (float)hi);
+            }
+      } else {
+        // S* as the merge's accumulator tiles (sfrag_offset): a lane's four rows of a
+        // tile are consecutive, one 16-byte store per tile
+        float* dst = plan.cp.sstar + (sg * H + h) * DK * dv;
+#pragma unroll
+        for (int t = 0; t < NKT; ++t)
+#pragma unroll
+          for (int j = 0; j < NCT; ++j)
+            *reinterpret_cast<f32x4*>(dst + sfrag_offset<DK>(prow(t, 4 * q), col0 + wcol + 16 * j + r16)) = hs[t][j];
+      }
+    } else if (last_seg && p.hT) {
       float* dst = p.hT + (int64_t)nh * DK * dv + col0 + wcol;
 #pragma unroll
       for (int t = 0; t < NKT; ++t)
@@ -790,17 +863,24 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
   }
 }
 
-// 1-D grid of ceil(units / 8) * 8 workgroups (see the decode in the kernel); one
-// workgroup covers all dv value columns.
-template <int DK, int BV>
+// 1-D grid of ceil(units / 8) * 8 workgroups per column block (see the decode in the
+// kernel); pass 3: one block of all dv value columns; pass 1: (dv + dk) / dv blocks.
+template <int DK, int BV, int PASS>
 static hipError_t launch_wy_dk(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev) {
   using Cfg = WyCfg<DK, BV>;
-  const int ncb = p.dv / BV;
+  const int ncb = (PASS == kPass1 ? p.dv + DK : p.dv) / BV;
   const int64_t groups = (plan.units + 7) / 8;
   if (groups * 8 * ncb > kMaxDispatchItems / Cfg::NT) return hipErrorInvalidConfiguration;
-  hipExtLaunchKernelGGL(fused_wy_kernel<DK, BV>, dim3((unsigned)(groups * 8 * ncb)), dim3(Cfg::NT), 0, s,
+  hipExtLaunchKernelGGL((fused_wy_kernel<DK, BV, PASS>), dim3((unsigned)(groups * 8 * ncb)), dim3(Cfg::NT), 0, s,
                         ev.start, ev.stop, 0, p, plan);
   return hipGetLastError();
+}
+
+template <int PASS>
+static hipError_t launch_wy_pass(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev) {
+  if (p.dk == 128)
+    return p.dv == 128 ? launch_wy_dk<128, 128, PASS>(p, plan, s, ev) : launch_wy_dk<128, 64, PASS>(p, plan, s, ev);
+  return p.dv == 128 ? launch_wy_dk<64, 128, PASS>(p, plan, s, ev) : launch_wy_dk<64, 64, PASS>(p, plan, s, ev);
 }
 
 hipError_t launch_fused_wy(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev) {
@@ -808,10 +888,8 @@ hipError_t launch_fused_wy(const Problem& p, const FwdPlan& plan, hipStream_t s,
     ev.record_empty(s);
     return hipSuccess;
   }
-  if (!p.qkv_bf16) return hipErrorInvalidValue;
-  if (p.dk == 128)
-    return p.dv == 128 ? launch_wy_dk<128, 128>(p, plan, s, ev) : launch_wy_dk<128, 64>(p, plan, s, ev);
-  return p.dv == 128 ? launch_wy_dk<64, 128>(p, plan, s, ev) : launch_wy_dk<64, 64>(p, plan, s, ev);
+  if (!p.qkv_bf16 || (plan.mode != kPass3 && plan.mode != kPass1)) return hipErrorInvalidValue;
+  return plan.mode == kPass1 ? launch_wy_pass<kPass1>(p, plan, s, ev) : launch_wy_pass<kPass3>(p, plan, s, ev);
 }
 
 }  // namespace gdn

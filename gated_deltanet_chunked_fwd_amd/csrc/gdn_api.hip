@@ -40,13 +40,14 @@ constexpr size_t kAlign = 256;
 //             step(busy) = kStepBaseUs + kStepPerBusyUs * busy workgroups (HBM and L2
 //             contention: 2.7 us at 64 busy, 3.7 us at 256); two-kernel path: λ1.
 //   K1        two-kernel path only: kK1FixedUs + kK1PerChunkHeadUs per chunk-head.
-//   split     kSplitFixedUs + kSplitPerChunkHeadUs per chunk-head: the gate sums, the
-//             gate scan and the launches of the correction stages (on a window-only
-//             problem they read the gate scan's count and return at once); packed
-//             input adds the table launch, kPackedTablesUs.
-//   corrected heads (a segment start without a window), per call: their chunk inverse
-//             (kK1FixedUs + kCorrK1PerChunkHeadUs per chunk-head), pass 1
-//             (kPass1FixedUs + kPass1StepUs * L per round of workgroups) and the merge
+//   split     kSplitFixedUs (one-pass: kSplitFixedWyUs) + kSplitPerChunkHeadUs per
+//             chunk-head: the gate sums, the gate scan and the launches of the
+//             correction stages (on a window-only problem they read the gate scan's
+//             count and return at once); packed input adds the table launch,
+//             kPackedTablesUs.
+//   corrected heads (a segment start without a window), per call: pass 1
+//             (kPass1FixedUs + kPass1StepUs * L per round of workgroups; one-pass
+//             plans form T inside pass 1, two-kernel plans read K1's) and the merge
 //             (short chain: kMergeFixedUs + λ2 per step; tree: kTreeFixedUs +
 //             kTreeSqrtUs * sqrt(steps)), which take the place of kCorrReplacesUs of
 //             the empty correction launches.
@@ -58,8 +59,8 @@ constexpr double kLookbackSteps = 1.0;
 constexpr double kFwdFixedUs = 4.5;
 constexpr double kStepBaseUs = 2.33, kStepPerBusyUs = 0.0055;
 constexpr double kStepF32Us = 5.5;               // two-kernel step on fp32 inputs
-constexpr double kK1FixedUs = 10.0, kK1PerChunkHeadUs = 0.004, kCorrK1PerChunkHeadUs = 0.007;
-constexpr double kSplitFixedUs = 17.5, kSplitPerChunkHeadUs = 0.0, kPackedTablesUs = 4.0;
+constexpr double kK1FixedUs = 10.0, kK1PerChunkHeadUs = 0.004;
+constexpr double kSplitFixedUs = 17.5, kSplitFixedWyUs = 12.5, kSplitPerChunkHeadUs = 0.0, kPackedTablesUs = 4.0;
 constexpr double kCorrReplacesUs = 8.0;
 constexpr double kPass1FixedUs = 3.0, kPass1StepUs = 2.0;
 constexpr double kMergeFixedUs = 7.0, kTreeFixedUs = 35.4, kTreeSqrtUs = 3.18;
@@ -264,11 +265,12 @@ double call_us(const gdn_shape* s, const Plan& P, const gdn_opts* o, int64_t L, 
   if (!P.wy) t += kK1FixedUs + kK1PerChunkHeadUs * chunk_heads;
   if (s->cu_seqlens_host) t += kPackedTablesUs;
   if (!split) return t;
-  t += kSplitFixedUs + kSplitPerChunkHeadUs * chunk_heads;
+  t += (P.wy ? kSplitFixedWyUs : kSplitFixedUs) + kSplitPerChunkHeadUs * chunk_heads;
   if (corr > 0 && longest_steps > 0) {
     t -= kCorrReplacesUs;
-    if (P.wy) t += kK1FixedUs + kCorrK1PerChunkHeadUs * corr * chunk_heads;
-    const double p1_wgs = corr * (double)(segs - s->N) * s->H * ((s->dv + s->dk) / P.pass1_block);
+    // pass 1's column blocks: dv wide in the one-pass kernel, pass1_block in the other
+    const int p1_block = P.wy ? s->dv : P.pass1_block;
+    const double p1_wgs = corr * (double)(segs - s->N) * s->H * ((s->dv + s->dk) / p1_block);
     const double rounds = std::max(1.0, std::ceil(p1_wgs / (double)cus));
     t += kPass1FixedUs + kPass1StepUs * (double)L * rounds;
     t += longest_steps > gdn::kMergeTreeMinSteps ? kTreeFixedUs + kTreeSqrtUs * std::sqrt((double)longest_steps)
@@ -410,9 +412,9 @@ Plan make_plan(const gdn_shape* s, const gdn_opts* o) {
   return P;
 }
 
-// Whether the chunk-inverse kernel runs: always on the two-pass path; on the one-pass
-// path only for split plans (pass 1 and the gate scan read its T and chunk gate sums).
-bool runs_k1(const Plan& P) { return !P.wy || P.split; }
+// Whether the chunk-inverse kernel runs: on the two-pass path only (the one-pass
+// kernel forms the inverses itself, in pass 3 and in pass 1).
+bool runs_k1(const Plan& P) { return !P.wy; }
 
 struct Layout {
   size_t tmat = 0, chunk_off = 0, seg_off = 0, seg_order = 0, csum = 0, sstar = 0, mcorr = 0, hstart = 0;
@@ -549,19 +551,18 @@ int run_stages(int first, int last, const void* q, const void* k, const void* v,
   void* tmat = ws + L.tmat;
   float* csum = P.split ? reinterpret_cast<float*>(ws + L.csum) : nullptr;
   const bool forced = opts && opts->force_correction;
-  // One-pass plans read no T; a split one runs the chunk inverse only for pass 1's
-  // listed segments (of the pairs with a start that has no window), so it goes after
-  // the gate scan: the inverse stage then forms the chunk gate sums alone.
-  const bool k1_after_scan = P.wy && P.split && !forced;
+  // One-pass plans read no T (the one-pass kernel forms it, in pass 3 and in pass 1):
+  // the inverse stage of a split one forms the chunk gate sums alone, for the scan.
+  const bool listed = P.wy && P.split && !forced;
   // counts of the heads without a window and of pass 1's units (one-pass split plans):
   // zeroed with the gate sums, added to by the gate scan, read first by every
   // correction launch
-  uint32_t* ncorr = k1_after_scan ? reinterpret_cast<uint32_t*>(ws + L.ncorr) : nullptr;
+  uint32_t* ncorr = listed ? reinterpret_cast<uint32_t*>(ws + L.ncorr) : nullptr;
   if (runs(GDN_STAGE_INVERSE)) {
     const gdn::KernelEvents ev = stage_events(opts, GDN_STAGE_INVERSE);
     hipError_t e = hipSuccess;
-    if (!runs_k1(P)) ev.record_empty(stream);
-    else if (k1_after_scan) e = gdn::launch_chunk_gate_sums(p, csum, stream, ev, ncorr);
+    if (listed) e = gdn::launch_chunk_gate_sums(p, csum, stream, ev, ncorr);
+    else if (!runs_k1(P)) ev.record_empty(stream);
     else e = gdn::launch_chunk_inverse(p, tmat, csum, false, stream, ev);
     if (e != hipSuccess) return GDN_ERR_HIP;
   }
@@ -602,20 +603,10 @@ int run_stages(int first, int last, const void* q, const void* k, const void* v,
       gdn::FwdPlan p1 = plan;
       p1.mode = gdn::kPass1;
       if (p1_slots) p1.units = (P.total_segs - p.N) * p.H;   // the list's capacity
-      gdn::KernelEvents ev = stage_events(opts, GDN_STAGE_CP_PASS1);
-      if (k1_after_scan) {
-        gdn::HeadFilter only;
-        only.p1_slots = p1_slots;
-        only.p1_cap = p1.units;
-        only.seg_off = cu_seqlens ? seg_off : nullptr;
-        only.seg_chunks = P.seg_chunks;
-        only.ncorr = ncorr;
-        if (gdn::launch_chunk_inverse(p, tmat, nullptr, false, stream, gdn::KernelEvents{ev.start, nullptr},
-                                      only) != hipSuccess)
-          return GDN_ERR_HIP;
-        ev.start = nullptr;
-      }
-      if (gdn::launch_fused_forward(p, p1, stream, ev) != hipSuccess) return GDN_ERR_HIP;
+      const gdn::KernelEvents ev = stage_events(opts, GDN_STAGE_CP_PASS1);
+      if ((P.wy ? gdn::launch_fused_wy(p, p1, stream, ev) : gdn::launch_fused_forward(p, p1, stream, ev)) !=
+          hipSuccess)
+        return GDN_ERR_HIP;
     }
     if (runs(GDN_STAGE_CP_MERGE)) {
       const int max_steps = (int)((P.max_chunks + P.seg_chunks - 1) / P.seg_chunks - 1);

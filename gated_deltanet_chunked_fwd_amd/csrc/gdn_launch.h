@@ -142,22 +142,14 @@ hipError_t launch_gate_finalize(const Problem& p, const uint32_t* best, int wmax
 // max_steps: the most segment boundaries of any sequence (segments - 1).
 hipError_t launch_cp_merge(const Problem& p, const FwdPlan& plan, int max_steps, hipStream_t s,
                            KernelEvents ev = {});
-// The chunk inverse restricted to pass 1's work list (CpBuffers::p1_slots): the
-// chunks of the listed segments only, ncorr[1] entries, at most p1_cap.
-struct HeadFilter {
-  const int32_t* p1_slots = nullptr;  // null: every chunk-head
-  int64_t p1_cap = 0;
-  const int32_t* seg_off = nullptr;   // packed split plans: per-sequence segment offsets
-  int seg_chunks = 0;
-  const uint32_t* ncorr = nullptr;    // as CpBuffers::ncorr
-};
 // csum (nullable): [total_chunks, H] per-chunk gate sums, written on the side.
 // full = false: T's zero upper-right 32 x 32 quadrant is left unwritten (the fused
 // forward never reads it).
 hipError_t launch_chunk_inverse(const Problem& p, void* t_out, float* csum, bool full,
-                                hipStream_t s, KernelEvents ev = {}, HeadFilter only = {});
-// One pass, bf16 only: steps 1-4 with the inverse formed in the kernel (fused_wy.hip);
-// kPass3 plans only, 32 value columns per workgroup.
+                                hipStream_t s, KernelEvents ev = {});
+// One pass, bf16 only (fused_wy.hip): the chunk inverse formed in the kernel; kPass3
+// (steps 1-4 with O) or kPass1 (the split's pass 1, S* and M; with cp.p1_slots a unit
+// is an entry of the work list).  A workgroup covers dv columns.
 hipError_t launch_fused_wy(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev = {});
 hipError_t launch_fused_forward(const Problem& p, const FwdPlan& plan, hipStream_t s,
                                 KernelEvents ev = {});

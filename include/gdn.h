@@ -180,10 +180,9 @@ int gdn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const flo
  * elsewhere, the workspace regions below (gdn_chunk_fwd_workspace_region).  A
  * stage that the plan does not need (the split stages when no sequence is split,
  * the gate scan under force_correction) enqueues nothing and returns GDN_OK.
- * Under a one-pass plan (gdn_plan_one_pass) no stage forms T for the forward pass:
- * an unsplit plan's GDN_STAGE_INVERSE enqueues nothing; a split plan's forms only
- * the chunk gate sums, and its GDN_STAGE_CP_PASS1 first forms T for the chunks of
- * pass 1's units (below: the only ones pass 1 reads it for).  A
+ * Under a one-pass plan (gdn_plan_one_pass) no stage writes T: the one-pass kernel
+ * forms it in pass 1 and in the forward itself.  An unsplit plan's GDN_STAGE_INVERSE
+ * enqueues nothing; a split plan's forms only the chunk gate sums.  A
  * split one-pass plan also keeps in the workspace a count of the (sequence, head)
  * pairs that take the correction and a list of pass 1's units (the segments of those pairs
  * but each sequence's last) with its length: GDN_STAGE_INVERSE zeroes both counts,
@@ -216,9 +215,8 @@ enum {
   GDN_REGION_CHUNK_INVERSE = 0,  /* T of every chunk-head: [total_chunks, H, 64, 64] in
                                     shape->qkv_dtype, as gdn_chunk_inverse writes it, except
                                     that the (zero) upper-right 32 x 32 quadrant is not
-                                    written (GDN_STAGE_INVERSE; under a one-pass plan empty
-                                    when nothing is split, else written by
-                                    GDN_STAGE_CP_PASS1 for the chunks of its units only) */
+                                    written (GDN_STAGE_INVERSE; empty under a one-pass
+                                    plan) */
   GDN_REGION_SEGMENT_WINDOWS = 1, /* per slot int32: the lookback window, in chunks, of the
                                     segment's start: the smallest W <= min(window_max_chunks,
                                     the start's chunk index) whose W chunks before the start

@@ -209,22 +209,28 @@ def region(s, r, opts=None):
 def test_workspace_regions():
     """The stage-connecting regions lie inside the workspace, 256-byte aligned and
     disjoint, with the sizes their layouts imply; the segment regions are empty when
-    nothing is split; unknown regions and stages are rejected before any launch."""
+    nothing is split, the chunk-inverse region on one-pass plans (the one-pass kernel
+    forms T itself, in pass 1 too); unknown regions and stages are rejected before any
+    launch."""
     T, H, d = 64 * 14 + 23, 3, 128
     s = shape(T=T, H=H, dk=d, dv=d)
     split = B.make_opts(force_segment_chunks=3)
     total = ctypes.c_size_t(0)
     assert B.lib().gdn_chunk_fwd_workspace_bytes(ctypes.byref(s), ctypes.byref(split), ctypes.byref(total)) == 0
     chunks, segs = 15, 5
-    want = {B.GDN_REGION_CHUNK_INVERSE: chunks * H * 64 * 64 * 2, B.GDN_REGION_SEGMENT_WINDOWS: segs * H * 4,
+    want = {B.GDN_REGION_CHUNK_INVERSE: 0, B.GDN_REGION_SEGMENT_WINDOWS: segs * H * 4,
             B.GDN_REGION_SEGMENT_STARTS: segs * H * d * d * 4}
     spans = []
     for r in range(B.GDN_NUM_REGIONS):
         rc, off, n = region(s, r, split)
-        assert rc == B.GDN_OK and off % 256 == 0 and 0 < n and off + n <= total.value
+        assert rc == B.GDN_OK and off % 256 == 0 and off + n <= total.value
+        assert (n == 0) == (r == B.GDN_REGION_CHUNK_INVERSE), r
         if r in want:
             assert n == want[r], r
-        spans.append((off, off + n))
+        if n:
+            spans.append((off, off + n))
+    two_kernel = B.make_opts(force_segment_chunks=3, one_pass=-1)
+    assert region(s, B.GDN_REGION_CHUNK_INVERSE, two_kernel)[2] == chunks * H * 64 * 64 * 2
     rc, off, n = region(s, B.GDN_REGION_SEGMENT_MAPS, split)
     # S* (fp32) then M (2 x bf16) per slot, M at the next 256-byte boundary
     smap = segs * H * d * d * 4
@@ -264,7 +270,7 @@ def test_noalloc_rejects_problem_beyond_scratch_before_any_launch():
     """gdn_chunk_fwd_noalloc refuses a problem whose workspace exceeds the built-in
     scratch (GDN_ERR_SCRATCH) before it touches a pointer or the device."""
     lib = B.lib()
-    s = shape(B=1, T=1 << 20, H=16, N=1)
+    s = shape(B=1, T=1 << 22, H=16, N=1)
     need = ctypes.c_size_t(0)
     assert lib.gdn_chunk_fwd_workspace_bytes(ctypes.byref(s), None, ctypes.byref(need)) == B.GDN_OK
     assert need.value > B.GDN_NOALLOC_SCRATCH_BYTES

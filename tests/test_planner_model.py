@@ -51,7 +51,7 @@ def test_chosen_length_minimises_the_model():
 # Whole-call times measured on MI355X (bench.py, 10 back-to-back calls after a warm-up,
 # default plan), and the share of (sequence, head) pairs without a lookback window
 # (workload 4: head 3 has no decay).
-MEASURED_US = {1: (44.8, 0.0), 2: (86.9, 0.0), 3: (328.1, 0.0), 4: (275.8, 0.25), 5: (288.8, 0.0)}
+MEASURED_US = {1: (44.7, 0.0), 2: (86.6, 0.0), 3: (323.5, 0.0), 4: (262.7, 0.25), 5: (287.7, 0.0)}
 
 
 @pytest.mark.parametrize("w", sorted(MEASURED_US))
@@ -76,10 +76,10 @@ def test_predict_rejects_bad_fraction():
 # log-sigmoid of N(3, 1) logits, so every head takes lookback windows: corrected
 # fraction 0), measured on
 # MI355X at the default plan (20 back-to-back calls, median of three runs).
-GRID_MEASURED_US = {(1, 4, 2048): 49.4, (1, 4, 8192): 50.4, (1, 4, 32768): 58.2,
-                    (1, 16, 2048): 51.6, (1, 16, 8192): 59.7, (1, 16, 32768): 165.1,
-                    (4, 16, 2048): 57.6, (4, 16, 8192): 159.6, (4, 16, 32768): 530.6,
-                    (16, 16, 2048): 136.5, (16, 16, 8192): 511.2, (16, 16, 32768): 1990.3}
+GRID_MEASURED_US = {(1, 4, 2048): 46.1, (1, 4, 8192): 47.8, (1, 4, 32768): 54.7,
+                    (1, 16, 2048): 48.1, (1, 16, 8192): 55.0, (1, 16, 32768): 155.5,
+                    (4, 16, 2048): 56.4, (4, 16, 8192): 151.4, (4, 16, 32768): 504.7,
+                    (16, 16, 2048): 134.8, (16, 16, 8192): 485.6, (16, 16, 32768): 1895.4}
 
 
 @pytest.mark.parametrize("B,H,T", sorted(GRID_MEASURED_US))

@@ -59,7 +59,7 @@ def test_noalloc_rejects_problem_beyond_scratch():
     """A problem whose workspace exceeds the built-in array is rejected before anything
     is enqueued (no pointer is touched: all are null here)."""
     lib = binding.lib()
-    s = binding.GdnShape(1, 1 << 20, 16, 128, 128, 1, binding.GDN_BF16, binding.GDN_BF16, None)
+    s = binding.GdnShape(1, 1 << 22, 16, 128, 128, 1, binding.GDN_BF16, binding.GDN_BF16, None)
     need = ctypes.c_size_t(0)
     assert lib.gdn_chunk_fwd_workspace_bytes(ctypes.byref(s), None, ctypes.byref(need)) == 0
     assert need.value > binding.GDN_NOALLOC_SCRATCH_BYTES
