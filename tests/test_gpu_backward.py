@@ -264,3 +264,23 @@ def test_backward_bf16_is_deterministic():
         outs.append([x.detach().cpu() for x in got])
     for name, a, b in zip(NAMES, *outs):
         assert torch.equal(a, b), name
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_backward_zero_length_passes_the_state_gradient_through(dtype):
+    """T = 0 (dense) and a packed batch of empty sequences: no chunk to differentiate,
+    so the initial-state gradient is the final-state gradient and every other gradient
+    is empty (both paths: the chain kernel runs with no chunk, nothing else launches)."""
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    H, d = 2, 64
+    for B, T, cu in ((3, 0, None), (1, 0, torch.zeros(4, dtype=torch.int32))):
+        N = B if cu is None else len(cu) - 1
+        q = torch.zeros((B, T, H, d), dtype=tdt, device="cuda")
+        g = torch.zeros((B, T, H), dtype=torch.float32, device="cuda")
+        beta = torch.zeros((B, T, H), dtype=tdt, device="cuda")
+        dhT = torch.randn((N, H, d, d), generator=torch.Generator().manual_seed(5)).cuda()
+        got = binding.chunk_bwd(q, q, q, g, beta, q, None, dhT, scale=0.125,
+                                cu_seqlens=None if cu is None else cu.cuda(), cu_seqlens_host=cu)
+        torch.cuda.synchronize()
+        assert all(x.numel() == 0 for x in got[:5])
+        assert torch.equal(got[5].cpu(), dhT.cpu())
