@@ -175,7 +175,9 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
   //      gate scan's work list when there is one (so only units that run are
   //      dispatched), else numbers every (segment, head) head-major.
   const uint32_t bid = blockIdx.x;
-  const uint32_t ncb = (uint32_t)((P1 ? dv + DK : dv) / BV);
+  // (dk < dv: the one matrix block is half used; its columns past dk stay zero and
+  // are not stored)
+  const uint32_t ncb = (uint32_t)((P1 ? dv + DK + BV - 1 : dv) / BV);
   const uint32_t rest = bid >> 3;
   const int cb = (int)(rest % ncb);
   const uint32_t unit = (rest / ncb) * 8u + (bid & 7u);
@@ -547,6 +549,7 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
           for (int j = 0; j < NCT; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
+              if (mc + 16 * j >= DK) continue;   // a half-used block's spare columns
               const float x = hs[t][j][i];
               const bf16 hi = (bf16)x;
               const int64_t at = mfrag_offset<DK>(prow(t, 4 * q + i), mc + 16 * j);
@@ -868,7 +871,7 @@ __global__ __launch_bounds__(512, 1) void fused_wy_kernel(Problem p, FwdPlan pla
 template <int DK, int BV, int PASS>
 static hipError_t launch_wy_dk(const Problem& p, const FwdPlan& plan, hipStream_t s, KernelEvents ev) {
   using Cfg = WyCfg<DK, BV>;
-  const int ncb = (PASS == kPass1 ? p.dv + DK : p.dv) / BV;
+  const int ncb = (PASS == kPass1 ? p.dv + DK + BV - 1 : p.dv) / BV;
   const int64_t groups = (plan.units + 7) / 8;
   if (groups * 8 * ncb > kMaxDispatchItems / Cfg::NT) return hipErrorInvalidConfiguration;
   hipExtLaunchKernelGGL((fused_wy_kernel<DK, BV, PASS>), dim3((unsigned)(groups * 8 * ncb)), dim3(Cfg::NT), 0, s,

@@ -375,3 +375,17 @@ def test_segment_starts_stage_parity(case):
     assert base == starts.shape[0]
     print("%s: %d segment starts, worst rel L2 %.3e" % (case, checked, worst), flush=True)
     assert checked > 0 and worst <= TOL[sp.dtype]
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 64), (64, 128), (64, 64)])
+@pytest.mark.parametrize("corr", [0, 1])
+def test_one_pass_pass1_column_blocks(dk, dv, corr):
+    """Pass 1 in the one-pass kernel: a unit's value block then its dk / dv
+    transition-matrix blocks (three blocks at dk = 128, dv = 64), from the gate scan's
+    work list (head 0 without decay) or every segment (forced correction)."""
+    inp = synth.generate(spec(B=2, T=64 * 9 + 5, H=2, dk=dk, dv=dv, seed=140 + dk + dv + corr,
+                              zero_gate_heads=(0,), h0_std=0.05))
+    opts = binding.make_opts(force_segment_chunks=2, force_correction=corr, one_pass=1)
+    assert binding.plan_one_pass(inp["q"], inp["v"], inp["beta"], None, opts)
+    o, hT = run_gpu(inp, opts=opts)
+    assert_parity(compare_pairs(inp, o, hT), TOL["bf16"], "one-pass pass 1 dk=%d dv=%d corr=%d" % (dk, dv, corr))
