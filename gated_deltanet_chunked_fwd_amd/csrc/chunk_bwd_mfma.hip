@@ -241,7 +241,8 @@ __global__ __launch_bounds__(kDhThreads) void bwd_dh_kernel(Problem p, BwdArgs a
   };
   // dV of chunk c (16-byte stores of the rows inside the chunk) from sDV; the
   // checkpoint of the state gradient after chunk c from the registers, as its bf16
-  // transpose (four keys of one value column per 8-byte store); this wave's share of
+  // transpose as a hi + lo pair (hi block, then lo block; four keys of one value column
+  // per 8-byte store); this wave's share of
   // gamma_n <h, dh'> into sHD (hd: this lane's <h, dh'> terms, formed at the top of the
   // step; the workgroup's sum is written at the next step)
   auto store_dv = [&](int c) {
@@ -252,13 +253,20 @@ __global__ __launch_bounds__(kDhThreads) void bwd_dh_kernel(Problem p, BwdArgs a
           *reinterpret_cast<const u32x4*>(sDV + row * VS + cp * 8);
   };
   auto store_ckpt = [&](int c, float hd) {
-    bf16* ck = reinterpret_cast<bf16*>(a.dhchk) + ((si.chunk0 + c) * H + h) * (int64_t)DK * dv;
+    bf16* ck = reinterpret_cast<bf16*>(a.dhchk) + ((si.chunk0 + c) * H + h) * (int64_t)2 * DK * dv;
 #pragma unroll
     for (int tt = 0; tt < NRT; ++tt)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        *reinterpret_cast<uint2*>(ck + (int64_t)(col0 + 16 * j + r) * DK + 16 * (NRT * w + tt) + 4 * q) =
-            pack_bf16x4(dh[tt][j]);
+      for (int j = 0; j < 2; ++j) {
+        const int64_t at = (int64_t)(col0 + 16 * j + r) * DK + 16 * (NRT * w + tt) + 4 * q;
+        const uint2 hi = pack_bf16x4(dh[tt][j]);
+        *reinterpret_cast<uint2*>(ck + at) = hi;
+        const bf16x4 hb = __builtin_bit_cast(bf16x4, hi);
+        f32x4 lo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lo[i] = dh[tt][j][i] - (float)hb[i];
+        *reinterpret_cast<uint2*>(ck + (int64_t)DK * dv + at) = pack_bf16x4(lo);
+      }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) hd += __shfl_xor(hd, off, 64);
     if (lane == 0) sHD[w] = fast_exp(sG[kChunk - 1]) * hd;
@@ -463,7 +471,8 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
   const bf16* DOg = reinterpret_cast<const bf16*>(a.d_o) + t0 * rv + (int64_t)h * DV;
   const bf16* DVg = reinterpret_cast<const bf16*>(a.dv) + t0 * rv + (int64_t)h * DV;
   const float* hck = a.hchk + (cg * H + h) * (int64_t)(DK * DV);
-  const bf16* dck = reinterpret_cast<const bf16*>(a.dhchk) + (cg * H + h) * (int64_t)(DK * DV);
+  const bf16* dck = reinterpret_cast<const bf16*>(a.dhchk) + (cg * H + h) * (int64_t)(2 * DK * DV);
+  const bf16* dcl = dck + (int64_t)DK * DV;   // dh'^T's low half (X' operands, read from global)
   const bf16* Tc = reinterpret_cast<const bf16*>(a.tmat) + (cg * H + h) * (int64_t)(kChunk * kChunk);
   const u32x4 z4 = {0u, 0u, 0u, 0u};
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -640,12 +649,19 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
     for (int s = 0; s < 4; ++s) sU[(16 * u + 4 * q + s) * VS + 16 * jt + r] = (bf16)acc[s];
   }
   lds_barrier();   // W's low half read: the region takes dh'^T
-  // the chain's dh'^T (bf16 [value column][key]) into LDS
+  // the chain's dh'^T (bf16 [value column][key]) into LDS; the low half's X' operands
+  // go out now, ahead of the barrier
 #pragma unroll
   for (int k = 0; k < DV * DK / 8 / NT; ++k) {
     const int idx = tid + NT * k, row = idx / (DK / 8), cp = idx % (DK / 8);
     *reinterpret_cast<u32x4*>(sH + row * HS + cp * 8) = *reinterpret_cast<const u32x4*>(dck + (int64_t)idx * 8);
   }
+  frag dlo[NJV][NKS];
+#pragma unroll
+  for (int jj = 0; jj < NJV; ++jj)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      dlo[jj][ks] = *reinterpret_cast<const frag*>(dcl + (int64_t)(16 * (half * NJV + jj) + r) * DK + 32 * ks + 8 * q);
   lds_barrier();
 
   // ---- (f) X' = K dh', and the d terms of dG
@@ -655,8 +671,11 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
     const int jt = half * NJV + jj;
     f32x4 acc = zero4;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      acc = Mb::run(op_rows(sK, KS, 16 * u, 32 * ks), op_rows(sH, HS, 16 * jt, 32 * ks), acc);
+    for (int ks = 0; ks < NKS; ++ks) {
+      const frag ka = op_rows(sK, KS, 16 * u, 32 * ks);
+      acc = Mb::run(ka, op_rows(sH, HS, 16 * jt, 32 * ks), acc);
+      acc = Mb::run(ka, dlo[jj][ks], acc);
+    }
     X[jj] = acc;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {

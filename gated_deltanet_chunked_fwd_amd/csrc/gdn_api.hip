@@ -872,7 +872,7 @@ static BwdLayout bwd_layout(const gdn_shape* s, const gdn_opts* o) {
   L.hchk = take((size_t)chunks * s->H * s->dk * s->dv * sizeof(float));
   L.mfma = s->qkv_dtype == GDN_BF16;
   if (L.mfma) {
-    L.dhchk = take((size_t)chunks * s->H * s->dk * s->dv * sizeof(uint16_t));
+    L.dhchk = take((size_t)chunks * s->H * 2 * s->dk * s->dv * sizeof(uint16_t));
     L.gnh = take((size_t)chunks * s->H * nblk * sizeof(float));
   } else {
     L.dq_p = take((size_t)nblk * tot * s->H * s->dk * sizeof(float));

@@ -192,7 +192,8 @@ struct BwdArgs {
   const float* seg_g;        // kBwdFull with a split: per bwd_slot, [dk, dv] fp32 (natural)
   // bf16 path (chunk_bwd_mfma.hip): the chunk inverses (K1, [total_chunks, H, 64, 64]
   // bf16, the zero upper-right quadrant written); the chain's checkpoints of the state
-  // gradient dh' after every chunk, as its bf16 transpose ([total_chunks, H, dv, dk]);
+  // gradient dh' after every chunk, as its bf16 transpose split hi + lo
+  // ([total_chunks, H] x {hi, lo} x [dv, dk]);
   // and gamma_n <h, dh'> of every chunk in fp32, one partial sum per 32 value columns
   // ([total_chunks, H, dv / 32])
   const void* tmat;
