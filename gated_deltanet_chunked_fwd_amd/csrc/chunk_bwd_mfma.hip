@@ -656,12 +656,15 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
     const int idx = tid + NT * k, row = idx / (DK / 8), cp = idx % (DK / 8);
     *reinterpret_cast<u32x4*>(sH + row * HS + cp * 8) = *reinterpret_cast<const u32x4*>(dck + (int64_t)idx * 8);
   }
-  frag dlo[NJV][NKS];
-#pragma unroll
-  for (int jj = 0; jj < NJV; ++jj)
+  // the low half's operands for one value tile at a time, double-buffered: the first
+  // tile's go out before the barrier, each next tile's before the current tile's MFMAs
+  auto load_dlo = [&](frag* dst, int jt) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
-      dlo[jj][ks] = *reinterpret_cast<const frag*>(dcl + (int64_t)(16 * (half * NJV + jj) + r) * DK + 32 * ks + 8 * q);
+      dst[ks] = *reinterpret_cast<const frag*>(dcl + (int64_t)(16 * jt + r) * DK + 32 * ks + 8 * q);
+  };
+  frag dlo[2][NKS];
+  load_dlo(dlo[0], half * NJV);
   lds_barrier();
 
   // ---- (f) X' = K dh', and the d terms of dG
@@ -669,12 +672,13 @@ __global__ __launch_bounds__(kGrThreads) void bwd_grads_kernel(Problem p, BwdArg
 #pragma unroll
   for (int jj = 0; jj < NJV; ++jj) {
     const int jt = half * NJV + jj;
+    if (jj + 1 < NJV) load_dlo(dlo[(jj + 1) & 1], jt + 1);
     f32x4 acc = zero4;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       const frag ka = op_rows(sK, KS, 16 * u, 32 * ks);
       acc = Mb::run(ka, op_rows(sH, HS, 16 * jt, 32 * ks), acc);
-      acc = Mb::run(ka, dlo[jj][ks], acc);
+      acc = Mb::run(ka, dlo[jj & 1][ks], acc);
     }
     X[jj] = acc;
 #pragma unroll
